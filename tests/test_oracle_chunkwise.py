@@ -1,0 +1,213 @@
+"""Pins of the fp64 chunkwise evaluator (and, through agreement, of the token recurrence).
+
+* chunkwise == token recurrence for many chunk sizes, tails, packed sequences,
+  initial states and gate strengths (scalar and per-channel gates);
+* the inverse: (I + A_raw) A = I by brute force, and A equals the exact 16 -> 32 -> 64
+  block-triangular merge written out from 06 . Flash Linear Attention section 4;
+* the FlashQLA rewrite identity Gamma (.) A' = A;
+* the derivation identity (I + A_raw) V' = diag(beta)(V - diag(gamma) K S);
+* store-before-update: the entering state of chunk i is the recurrence's state after i*C tokens;
+* context parallelism: affine fix-up == serial, and the X/Y/Z form == the direct S*/M form;
+* beta -> "no erase" reduces to gated linear attention (token loop written here).
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import chunkwise as cw
+from oracle.recurrent import gdn_recurrent
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _inputs(rng, T, H, Dk, Dv, gate="scalar", mu=-2.0, batch=1):
+    q = rng.standard_normal((batch, T, H, Dk))
+    k = rng.standard_normal((batch, T, H, Dk))
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((batch, T, H, Dv))
+    gs = (batch, T, H) if gate == "scalar" else (batch, T, H, Dk)
+    g = np.zeros(gs) if mu is None else -np.logaddexp(0, rng.standard_normal(gs) + mu)
+    beta = 1 / (1 + np.exp(-rng.standard_normal((batch, T, H))))
+    return q, k, v, g, beta
+
+
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+@pytest.mark.parametrize("C", [1, 16, 64, 100, 203])
+def test_chunkwise_equals_recurrence(gate, C):
+    rng = np.random.default_rng(10 + C)
+    T, H, D = 203, 2, 16
+    q, k, v, g, beta = _inputs(rng, T, H, D, D, gate)
+    h0 = 0.3 * rng.standard_normal((1, H, D, D))
+    o1, f1 = gdn_recurrent(q, k, v, g, beta, 0.25, h0=h0, gate=gate)
+    o2, f2 = cw.chunkwise_fwd(q, k, v, g, beta, 0.25, h0=h0, chunk_size=C, gate=gate)
+    np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(f2, f1, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("mu", [None, -7.0, 2.0])
+def test_chunkwise_equals_recurrence_gate_strengths(mu):
+    # g == 0 (no decay), weak decay (~ -1e-3 per token) and strong decay (~ -2 per token)
+    rng = np.random.default_rng(20)
+    q, k, v, g, beta = _inputs(rng, 300, 1, 32, 24, mu=mu)
+    h0 = rng.standard_normal((1, 1, 32, 24))
+    o1, f1 = gdn_recurrent(q, k, v, g, beta, 0.2, h0=h0)
+    o2, f2 = cw.chunkwise_fwd(q, k, v, g, beta, 0.2, h0=h0, chunk_size=64)
+    np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-11)
+    np.testing.assert_allclose(f2, f1, rtol=0, atol=1e-11)
+
+
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+def test_packed_ragged_sequences(gate):
+    rng = np.random.default_rng(30)
+    lens = [1, 63, 64, 65, 129, 7]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    q, k, v, g, beta = _inputs(rng, int(cu[-1]), 2, 16, 8, gate)
+    h0 = rng.standard_normal((len(lens), 2, 16, 8))
+    o1, f1 = gdn_recurrent(q, k, v, g, beta, 0.5, h0=h0, cu_seqlens=cu, gate=gate)
+    o2, f2 = cw.chunkwise_fwd(q, k, v, g, beta, 0.5, h0=h0, cu_seqlens=cu, chunk_size=64, gate=gate)
+    np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(f2, f1, rtol=0, atol=1e-12)
+
+
+def _records(gate="scalar", seed=40, T=64, D=32):
+    rng = np.random.default_rng(seed)
+    q, k, v, g, beta = _inputs(rng, T, 1, D, D, gate)
+    h0 = rng.standard_normal((1, 1, D, D))
+    _, _, recs = cw.chunkwise_fwd(q, k, v, g, beta, 0.3, h0=h0, chunk_size=64, gate=gate, return_records=True)
+    return (q, k, v, g, beta, h0), recs[(0, 0)]
+
+
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+def test_inverse_brute_force(gate):
+    _, recs = _records(gate)
+    for r in recs:
+        c = r["A"].shape[0]
+        np.testing.assert_allclose((np.eye(c) + r["A_raw"]) @ r["A"], np.eye(c), atol=1e-12)
+        np.testing.assert_allclose(r["A"] @ (np.eye(c) + r["A_raw"]), np.eye(c), atol=1e-12)
+        assert np.all(np.triu(r["A"], 1) == 0) and np.all(np.diag(r["A"]) == 1)
+
+
+def _schur_merge_inverse(L):
+    """(I + L)^{-1} by 16x16 forward substitution and exact block merges 16->32->64
+    (06 . Flash Linear Attention section 4: inv([[I+A00, 0], [A10, I+A11]]) has lower-left
+    block -A11^{-1} A10 A00^{-1})."""
+    def fwd_sub(Lb):  # row i absorbs the rows above it
+        n = Lb.shape[0]
+        X = np.eye(n)
+        for i in range(n):
+            for j in range(i):
+                X[i] -= Lb[i, j] * X[j]
+        return X
+
+    def merge(Ai00, Ai11, L10):
+        n0, n1 = Ai00.shape[0], Ai11.shape[0]
+        out = np.zeros((n0 + n1, n0 + n1))
+        out[:n0, :n0] = Ai00
+        out[n0:, n0:] = Ai11
+        out[n0:, :n0] = -Ai11 @ L10 @ Ai00
+        return out
+
+    blocks = [fwd_sub(L[i:i + 16, i:i + 16]) for i in range(0, 64, 16)]
+    b32 = [merge(blocks[0], blocks[1], L[16:32, 0:16]), merge(blocks[2], blocks[3], L[48:64, 32:48])]
+    return merge(b32[0], b32[1], L[32:64, 0:32])
+
+
+def test_inverse_equals_block_merge():
+    _, recs = _records("scalar", seed=41)
+    r = recs[0]
+    np.testing.assert_allclose(_schur_merge_inverse(r["A_raw"]), r["A"], atol=1e-12)
+
+
+def test_gamma_times_ungated_inverse():
+    # FlashQLA rewrite: (I + strictLower(diag(b)(Gamma (.) K K^T)))^{-1} == Gamma (.) (I + strictLower(diag(b) K K^T))^{-1}
+    (q, k, v, g, beta, h0), recs = _records("scalar", seed=42)
+    r = recs[0]
+    K, b = k[0, :, 0], beta[0, :, 0]
+    Ap = cw.unit_lower_inverse(np.tril(b[:, None] * (K @ K.T), -1))
+    np.testing.assert_allclose(r["Gamma"] * Ap, r["A"], atol=1e-12)
+
+
+def test_wy_derivation_identity():
+    # (I + A_raw) V' = diag(beta)(V - diag(gamma) K S_enter)  -- the recurrence unrolled inside a chunk
+    (q, k, v, g, beta, h0), recs = _records("scalar", seed=43)
+    r = recs[0]
+    K, V, b = k[0, :, 0], v[0, :, 0], beta[0, :, 0]
+    lhs = (np.eye(64) + r["A_raw"]) @ r["Vp"]
+    rhs = b[:, None] * (V - r["gamma"][:, None] * (K @ r["S_enter"]))
+    np.testing.assert_allclose(lhs, rhs, atol=1e-12)
+
+
+def test_golden_u_expansion():
+    d = json.load(open(os.path.join(GOLDEN, "wy_u_4x4.json")))
+    A, b, v = (np.array(d[x], dtype=float) for x in ("A", "beta", "v"))
+    # U = A diag(beta) V as the chunk evaluator forms it (A given, so no inverse involved)
+    np.testing.assert_array_equal(A @ (b[:, None] * v), np.array(d["expected_u"], dtype=float))
+
+
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+def test_store_before_update(gate):
+    rng = np.random.default_rng(50)
+    q, k, v, g, beta = _inputs(rng, 200, 1, 16, 16, gate)
+    h0 = rng.standard_normal((1, 1, 16, 16))
+    _, _, recs = cw.chunkwise_fwd(q, k, v, g, beta, 0.3, h0=h0, chunk_size=64, gate=gate, return_records=True)
+    recs = recs[(0, 0)]
+    np.testing.assert_array_equal(recs[0]["S_enter"], h0[0, 0])
+    for i in range(1, len(recs)):
+        t = 64 * i
+        _, fin = gdn_recurrent(q[:, :t], k[:, :t], v[:, :t], g[:, :t], beta[:, :t], 0.3, h0=h0, gate=gate)
+        np.testing.assert_allclose(recs[i]["S_enter"], fin[0, 0], atol=1e-12)
+
+
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+@pytest.mark.parametrize("seg", [1, 3, 4, 16])
+def test_cp_fixup_equals_serial(gate, seg):
+    rng = np.random.default_rng(60 + seg)
+    mu = -7.0  # weak decay, so the transition M carries real weight
+    q, k, v, g, beta = _inputs(rng, 64 * 9 + 23, 1, 16, 12, gate, mu=mu)
+    h0 = rng.standard_normal((1, 1, 16, 12))
+    o, fin, recs = cw.chunkwise_fwd(q, k, v, g, beta, 0.3, h0=h0, chunk_size=64, gate=gate, return_records=True)
+    recs = recs[(0, 0)]
+    maps = cw.cp_segment_maps(recs, seg)
+    starts, final = cw.cp_fixup(h0[0, 0], maps)
+    np.testing.assert_allclose(final, fin[0, 0], atol=1e-11)
+    for j, S in enumerate(starts):
+        np.testing.assert_allclose(S, recs[j * seg]["S_enter"], atol=1e-11)
+    # each segment run from its fixed-up start reproduces the serial outputs
+    Q, K, V = q[0, :, 0], k[0, :, 0], v[0, :, 0]
+    for j, S in enumerate(starts):
+        for r in recs[j * seg:(j + 1) * seg]:
+            s, e = r["start"], r["end"]
+            Vp, S_next = cw.state_step(S, r)
+            np.testing.assert_allclose(cw.chunk_output(Q[s:e], K[s:e], S, Vp, r, 0.3, gate), o[0, s:e, 0],
+                                       atol=1e-11)
+            S = S_next
+
+
+def test_cp_xyz_form_equals_direct_form():
+    rng = np.random.default_rng(70)
+    q, k, v, g, beta = _inputs(rng, 64 * 7 + 5, 1, 16, 12, mu=-7.0)
+    _, _, recs = cw.chunkwise_fwd(q, k, v, g, beta, 0.3, chunk_size=64, return_records=True)
+    direct = cw.cp_segment_maps(recs[(0, 0)], 3)
+    xyz = cw.cp_segment_maps_xyz(k[0, :, 0], v[0, :, 0], beta[0, :, 0], g[0, :, 0], 64, 3)
+    for (S1, M1), (S2, M2) in zip(direct, xyz):
+        np.testing.assert_allclose(S2, S1, atol=1e-11)
+        np.testing.assert_allclose(M2, M1, atol=1e-11)
+
+
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+def test_no_erase_reduces_to_gated_linear_attention(gate):
+    # Without the erase term the chunk machinery must give S_t = alpha_t S_{t-1} + beta_t k_t v_t^T.
+    rng = np.random.default_rng(80)
+    T, D = 150, 8
+    q, k, v, g, beta = _inputs(rng, T, 1, D, D, gate)
+    h0 = rng.standard_normal((1, 1, D, D))
+    o, fin = cw.chunkwise_fwd(q, k, v, g, beta, 0.6, h0=h0, chunk_size=64, gate=gate, erase=False)
+    S = h0[0, 0].copy()
+    for t in range(T):
+        a = np.exp(g[0, t, 0])
+        S = (a * S if gate == "scalar" else a[:, None] * S) + beta[0, t, 0] * np.outer(k[0, t, 0], v[0, t, 0])
+        np.testing.assert_allclose(o[0, t, 0], 0.6 * S.T @ q[0, t, 0], atol=1e-12)
+    np.testing.assert_allclose(fin[0, 0], S, atol=1e-12)
