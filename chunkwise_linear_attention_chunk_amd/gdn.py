@@ -1,0 +1,149 @@
+"""Thin ctypes binding of libgdn (include/gdn.h): argument marshalling only.
+
+Every step of the forward runs in the HIP kernels behind ``gdn_fwd``; PyTorch is
+used here for device memory (outputs and the workspace) and for the current
+stream.  There is no fallback: if ``libgdn.so`` has not been built, or a tensor
+is not on a GPU, the call raises.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP = range(5)
+DTYPE_F32, DTYPE_BF16 = 0, 1
+GATE_SCALAR, GATE_CHANNEL = 0, 1
+CP_MODES = {"auto": 0, "off": 1, "on": 2}
+EXPORTED = ("gdn_fwd", "gdn_fwd_workspace_bytes", "gdn_status_string", "gdn_last_error")
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(message)
+        self.status = status
+
+
+class FwdArgs(ctypes.Structure):
+    """Mirror of gdn_fwd_args."""
+    _fields_ = [
+        ("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H_qk", ctypes.c_int32), ("H_v", ctypes.c_int32),
+        ("D_k", ctypes.c_int32), ("D_v", ctypes.c_int32), ("chunk_size", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("gate_kind", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("g", ctypes.c_void_p),
+        ("beta", ctypes.c_void_p), ("h0", ctypes.c_void_p), ("cu_seqlens_dev", ctypes.c_void_p),
+        ("cu_seqlens_host", ctypes.c_void_p), ("N", ctypes.c_int32), ("o", ctypes.c_void_p),
+        ("final_state", ctypes.c_void_p), ("cp_mode", ctypes.c_int32), ("cp_segment_chunks", ctypes.c_int32),
+        ("o_dtype", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """Load libgdn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise GdnError(GDN_ERR_HIP, f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        L.gdn_fwd_workspace_bytes.argtypes = [ctypes.POINTER(FwdArgs)]
+        L.gdn_fwd_workspace_bytes.restype = ctypes.c_size_t
+        L.gdn_fwd.argtypes = [ctypes.POINTER(FwdArgs), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.gdn_fwd.restype = ctypes.c_int
+        L.gdn_status_string.argtypes = [ctypes.c_int]
+        L.gdn_status_string.restype = ctypes.c_char_p
+        L.gdn_last_error.argtypes = []
+        L.gdn_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(status):
+    if status != GDN_OK:
+        L = lib()
+        raise GdnError(status, f"{L.gdn_status_string(status).decode()}: {L.gdn_last_error().decode()}")
+
+
+def make_args(q, k, v, g, beta, scale=None, initial_state=None, cu_seqlens=None, cu_seqlens_cpu=None,
+              chunk_size=64, o=None, final_state=None, cp_mode="auto", cp_segment_chunks=0):
+    """Fill a gdn_fwd_args from tensors (shapes are read, nothing is computed)."""
+    if q.dim() != 4:
+        raise GdnError(GDN_ERR_INVALID_ARG, "q must be [B, T, H_qk, D_k]")
+    B, T, H_qk, D_k = q.shape
+    H_v, D_v = v.shape[2], v.shape[3]
+    dt = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}.get(q.dtype)
+    if dt is None:
+        raise GdnError(GDN_ERR_UNSUPPORTED, f"dtype {q.dtype} (supported: float32, bfloat16)")
+    gate = GATE_SCALAR if g.dim() == 3 else GATE_CHANNEL
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    a = FwdArgs()
+    a.B, a.T, a.H_qk, a.H_v, a.D_k, a.D_v = B, T, H_qk, H_v, D_k, D_v
+    a.chunk_size, a.dtype, a.gate_kind = chunk_size, dt, gate
+    a.scale = float(D_k ** -0.5 if scale is None else scale)
+    a.q, a.k, a.v, a.g, a.beta = (_ptr(t) for t in (q, k, v, g, beta))
+    a.h0 = _ptr(initial_state)
+    a.cu_seqlens_dev = _ptr(cu_seqlens)
+    a.cu_seqlens_host = _ptr(cu_seqlens_cpu)
+    a.N = N
+    a.o = _ptr(o)
+    a.final_state = _ptr(final_state)
+    a.cp_mode = CP_MODES[cp_mode] if isinstance(cp_mode, str) else int(cp_mode)
+    a.cp_segment_chunks = int(cp_segment_chunks)
+    a.o_dtype = dt if o is None else {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}[o.dtype]
+    return a
+
+
+def _require_gpu(name, t):
+    if t is not None and (not t.is_cuda or not t.is_contiguous()):
+        raise GdnError(GDN_ERR_INVALID_ARG, f"{name} must be a contiguous GPU tensor")
+
+
+def workspace_bytes(args):
+    return int(lib().gdn_fwd_workspace_bytes(ctypes.byref(args)))
+
+
+def fwd_raw(args, workspace, workspace_bytes_, stream):
+    """Call gdn_fwd with a prepared FwdArgs, a workspace pointer (int) and a stream handle (int)."""
+    _check(lib().gdn_fwd(ctypes.byref(args), ctypes.c_void_p(workspace), ctypes.c_size_t(workspace_bytes_),
+                         ctypes.c_void_p(stream)))
+
+
+def fwd(q, k, v, g, beta, scale=None, initial_state=None, cu_seqlens=None, chunk_size=64,
+        output_final_state=True, cp_mode="auto", cp_segment_chunks=0, workspace=None, out_dtype=None):
+    """Chunked-prefill forward of the gated delta rule on the GPU.
+
+    q, k: [B, T, H_qk, D_k]; v: [B, T, H_v, D_v]; g: [B, T, H_v] fp32 log-gates (or
+    [B, T, H_v, D_k] per-channel); beta: [B, T, H_v]; initial_state: [N, H_v, D_k, D_v] fp32;
+    cu_seqlens: [N + 1] int32 token offsets of packed sequences (B == 1).
+    out_dtype: dtype of o (default q's dtype; torch.float32 returns the unrounded fp32 result).
+    Returns (o [B, T, H_v, D_v], final_state [N, H_v, D_k, D_v] fp32 or None).
+    """
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("initial_state", initial_state)):
+        _require_gpu(name, t)
+    cu_dev = cu_host = None
+    if cu_seqlens is not None:
+        cu_host = cu_seqlens.detach().to("cpu", torch.int32).contiguous()
+        cu_dev = cu_seqlens if cu_seqlens.is_cuda else cu_host.to(q.device)
+        cu_dev = cu_dev.to(torch.int32).contiguous()
+    N = q.shape[0] if cu_seqlens is None else cu_host.numel() - 1
+    o = torch.empty(v.shape, dtype=q.dtype if out_dtype is None else out_dtype, device=q.device)
+    fs = (torch.empty((N, v.shape[2], k.shape[3], v.shape[3]), dtype=torch.float32, device=q.device)
+          if output_final_state else None)
+    a = make_args(q, k, v, g, beta, scale, initial_state, cu_dev, cu_host, chunk_size, o, fs, cp_mode,
+                  cp_segment_chunks)
+    nbytes = workspace_bytes(a)
+    if nbytes == 0 and q.numel() > 0:
+        _check(lib().gdn_fwd(ctypes.byref(a), None, 0, None))  # reports the validation error
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    fwd_raw(a, workspace.data_ptr(), workspace.numel(), stream)
+    return o, fs

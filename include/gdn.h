@@ -1,0 +1,113 @@
+/*
+ * libgdn -- chunked-prefill forward of the gated delta rule on MI355X (gfx950).
+ *
+ * The operation (FlashQLA announcement (Qwen), section "key problems of FLA GDN
+ * chunked prefill", the four-step forward for chunk i; GDN-in-FLA notes,
+ * forward Steps 1-5):
+ *
+ *   per sequence, per value head, per chunk of C = 64 tokens (the last chunk of a
+ *   sequence may be shorter), with g_c the chunk-local cumsum of the log-gates,
+ *   gamma = exp(g_c) and Gamma_ij = gamma_i / gamma_j:
+ *     A  = (I + strictLower(diag(beta)(Gamma (.) K K^T)))^{-1}
+ *     W  = A diag(beta) diag(gamma) K,      U = A diag(beta) V
+ *     V' = U - W S
+ *     S <- gamma_C S + K^T diag(gamma_C / gamma) V'        (gamma_C: last valid token)
+ *     O  = scale (diag(gamma) Q S + (Lower(Gamma) (.) Q K^T) V')   (mask includes the diagonal)
+ *
+ *   which equals, token by token, S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,
+ *   o_t = scale S_t^T q_t with alpha_t = exp(g_t) and the [D_k, D_v] state layout.
+ *
+ *   Per-channel gates (KDA; "KDA源码剖析之FLA", sections 3-5): the log-gate is a
+ *   [D_k] vector per token, the decay Diag(exp(gk_t)) is applied to the rows of S
+ *   before the read and the erase.
+ *
+ * Tensor layouts (row-major, contiguous, device memory):
+ *   q, k         [B, T, H_qk, D_k]   dtype
+ *   v            [B, T, H_v,  D_v]   dtype
+ *   g            [B, T, H_v]         fp32       (GDN_GATE_SCALAR, natural-log gate, <= 0 expected)
+ *   g            [B, T, H_v, D_k]    dtype      (GDN_GATE_CHANNEL)
+ *   beta         [B, T, H_v]         dtype
+ *   o            [B, T, H_v, D_v]    o_dtype    (written)
+ *   h0           [N, H_v, D_k, D_v]  fp32       (NULL: zero initial state)
+ *   final_state  [N, H_v, D_k, D_v]  fp32       (NULL: not written)
+ *   Value head h reads query/key head h / (H_v / H_qk).
+ *   Packed variable-length input: B == 1, cu_seqlens holds N + 1 token offsets
+ *   (cu[0] = 0, non-decreasing, cu[N] = T); chunks never straddle sequences.
+ *
+ * Ownership: the caller owns every buffer, including the workspace.  gdn_fwd
+ * allocates nothing, enqueues all work on `stream` (a hipStream_t; NULL is the
+ * null stream) and returns without synchronising.  Inputs must stay valid and
+ * outputs untouched until the enqueued work completes.
+ *
+ * Errors: all validation happens before any launch; on an error nothing is
+ * enqueued and no output is touched.  Faults inside kernels surface at the
+ * caller's next synchronisation, as for any HIP launch.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_INVALID_ARG = 1,  /* null required pointer, bad size, bad cu_seqlens, ... */
+    GDN_ERR_UNSUPPORTED = 2,  /* valid but not implemented (chunk size, head dim, dtype mix) */
+    GDN_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than gdn_fwd_workspace_bytes() */
+    GDN_ERR_HIP = 4           /* a HIP launch or query failed */
+} gdn_status;
+
+typedef enum { GDN_DTYPE_F32 = 0, GDN_DTYPE_BF16 = 1 } gdn_dtype;
+typedef enum { GDN_GATE_SCALAR = 0, GDN_GATE_CHANNEL = 1 } gdn_gate_kind;
+
+/* Context parallelism inside one GPU (FlashQLA announcement, the in-GPU CP
+ * pre-process and fix-up): split each sequence into segments of L chunks, run
+ * every segment from S = 0 together with its transition matrix M, fix up the
+ * segment start states serially, then run all segments in parallel. */
+typedef enum { GDN_CP_AUTO = 0, GDN_CP_OFF = 1, GDN_CP_ON = 2 } gdn_cp_mode;
+
+typedef struct {
+    int32_t B, T;             /* batch and tokens per batch row (T = total tokens when packed) */
+    int32_t H_qk, H_v;        /* query/key heads, value heads (H_v % H_qk == 0) */
+    int32_t D_k, D_v;         /* head dims: D_k == D_v in {64, 128} */
+    int32_t chunk_size;       /* must be 64 */
+    int32_t dtype;            /* gdn_dtype of q, k, v, beta, o (and a channel gate) */
+    int32_t gate_kind;        /* gdn_gate_kind */
+    float scale;              /* output scale, usually D_k^-1/2 */
+    const void *q, *k, *v, *g, *beta;
+    const float *h0;                  /* nullable */
+    const int32_t *cu_seqlens_dev;    /* nullable; [N + 1] device copy used by the kernels */
+    const int32_t *cu_seqlens_host;   /* required with cu_seqlens_dev; host copy used for planning */
+    int32_t N;                        /* sequences: N == B when not packed */
+    void *o;
+    float *final_state;               /* nullable */
+    int32_t cp_mode;                  /* gdn_cp_mode; AUTO decides from the shape */
+    int32_t cp_segment_chunks;        /* segment length L in chunks; 0 = choose */
+    int32_t o_dtype;                  /* gdn_dtype of o: equal to dtype, or GDN_DTYPE_F32 to receive
+                                         the fp32 result before it is rounded to a bf16 output */
+} gdn_fwd_args;
+
+/* Bytes of device workspace gdn_fwd needs for these arguments (0 on invalid
+ * arguments).  Depends on shapes, the packed lengths and the CP decision only. */
+size_t gdn_fwd_workspace_bytes(const gdn_fwd_args *a);
+
+/* Validate, plan and enqueue the forward on `stream` (a hipStream_t).  The
+ * workspace must be device memory of at least gdn_fwd_workspace_bytes(a)
+ * bytes, 256-byte aligned; its contents on entry do not matter. */
+gdn_status gdn_fwd(const gdn_fwd_args *a, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static, human-readable name of a status code. */
+const char *gdn_status_string(gdn_status s);
+
+/* Last validation message of this thread (empty when the last call succeeded). */
+const char *gdn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

@@ -1,0 +1,102 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerance: max|delta| <= 1e-4 * RMS for fp32 inputs and <= 2e-2 * RMS for bf16 inputs, on the
+output o and on the final state.  Small cases are compared in full; the full-size workloads
+are compared on sampled (sequence, head) pairs that the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+from chunkwise_linear_attention_chunk_amd import synth
+from parity_util import TOL, check, gpu_run
+
+pytestmark = pytest.mark.gpu
+
+
+def _w(name, **kw):
+    return synth.make_inputs(synth.workload(name, **kw))
+
+
+# --------------------------------------------------------------------------- fp32
+def test_tiny_fp32_workload():
+    x = _w("tiny_fp32")
+    check(x, TOL["fp32"], label="tiny_fp32")
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 200, 1000])
+def test_fp32_ragged_lengths_with_initial_state(T):
+    x = _w("tiny_fp32", T=T, B=2, h0=True, seed=T)
+    check(x, TOL["fp32"], label=f"fp32 T={T}")
+
+
+@pytest.mark.parametrize("mu", [None, -7.0, 2.0])
+def test_fp32_gate_strengths(mu):
+    # g == 0, weak decay (~1e-3 per token) and strong decay: the inter-chunk state matters
+    x = _w("tiny_fp32", T=640, H=3, h0=True, mu=mu, seed=5)
+    check(x, TOL["fp32"], label=f"fp32 mu={mu}")
+
+
+def test_fp32_head_dim_128_and_grouped_heads():
+    x = _w("tiny_fp32", T=333, H=4, H_qk=2, D=128, h0=True, seed=9)
+    check(x, TOL["fp32"], label="fp32 D=128 H_v=4 H_qk=2")
+
+
+def test_fp32_packed_ragged():
+    x = _w("tiny_fp32", n_seqs=7, lens=(1, 63, 64, 65, 129, 7, 300), H=2, h0=True, seed=3)
+    check(x, TOL["fp32"], label="fp32 packed")
+
+
+# --------------------------------------------------------------------------- bf16
+@pytest.mark.parametrize("T,mu", [(300, -2.0), (1000, -7.0), (777, None)])
+def test_bf16_small(T, mu):
+    x = _w("qwen3next_bf16", B=2, H=3, T=T, mu=mu, h0=True, seed=T)
+    check(x, TOL["bf16"], label=f"bf16 T={T} mu={mu}")
+
+
+def test_bf16_head_dim_64_grouped():
+    x = _w("qwen3next_bf16", B=1, H=4, H_qk=1, D=64, T=500, h0=True, seed=11)
+    check(x, TOL["bf16"], label="bf16 D=64 H_v=4 H_qk=1")
+
+
+def test_bf16_packed_ragged():
+    x = _w("varlen_bf16", n_seqs=8, lens=(0, 1, 63, 64, 65, 1000, 129, 7), H=3, seed=4)
+    check(x, TOL["bf16"], label="bf16 packed ragged")
+
+
+def test_qwen3next_workload_sampled():
+    x = _w("qwen3next_bf16")
+    check(x, TOL["bf16"], batches=[0, 3], heads=[0, 7, 15], label="qwen3next_bf16 (sampled)")
+
+
+def test_longctx_workload_sampled():
+    x = _w("longctx_bf16")
+    check(x, TOL["bf16"], heads=[0, 3], label="longctx_bf16 (sampled)")
+
+
+def test_varlen_workload_sampled():
+    x = _w("varlen_bf16")
+    lens = np.diff(x["cu_seqlens"].numpy())
+    seqs = [int(np.argmax(lens)), int(np.argmin(lens)), 5]
+    check(x, TOL["bf16"], heads=[0, 9], seqs=seqs, label="varlen_bf16 (sampled)")
+
+
+# --------------------------------------------------------------------------- properties
+def test_deterministic():
+    x = _w("qwen3next_bf16", B=1, H=4, T=700, h0=True, seed=21)
+    o1, f1 = gpu_run(x)
+    o2, f2 = gpu_run(x)
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
+
+
+def test_continuation():
+    # running T1 and then T2 from the final state equals running T1 + T2 (up to tolerance)
+    x = _w("tiny_fp32", T=512, h0=True, mu=-7.0, seed=31)
+    o_full, f_full = gpu_run(x)
+    cut = 200
+    part = lambda d, a, b: {**d, **{n: d[n][:, a:b].contiguous() for n in ("q", "k", "v", "g", "beta")}}
+    o1, f1 = gpu_run(part(x, 0, cut))
+    o2, f2 = gpu_run({**part(x, cut, 512), "h0": f1})
+    rms = o_full.double().pow(2).mean().sqrt()
+    assert (torch.cat([o1, o2], 1) - o_full).abs().max() <= 1e-4 * rms
+    assert (f2 - f_full).abs().max() <= 1e-4 * f_full.double().pow(2).mean().sqrt()
