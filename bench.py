@@ -1,0 +1,213 @@
+#!/usr/bin/env python3
+"""Benchmark of the gated-delta-rule chunked-prefill forward on one MI355X.
+
+One step = one gdn_fwd call (plan, kernel (a), [CP stages], kernels (b)+(d)) over the whole batch
+of the workload, with every input already resident in HBM.  Three input copies are rotated so
+the 256 MB last-level cache cannot hold a step's working set from the previous step.
+
+Prints one JSON line: tokens/s, per-stage times from HIP events recorded on the launch stream
+inside the timed region, the roofline of the dominant kernel (algorithmic bytes per launch /
+its mean duration), and the fp64 oracle timed on the host cores as a reported CPU baseline.
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GDN chunked-prefill fwd tokens/s at 1 GPU + % of MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
+KERNEL_SOURCES = {"chunk": "chunkwise_linear_attention_chunk_amd/csrc/gdn_chunk.hip",
+                  "intra": "chunkwise_linear_attention_chunk_amd/csrc/gdn_intra.hip"}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3next_bf16")
+    ap.add_argument("--copies", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: all host cores)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a 1 GiB device copy (calibrates the HBM byte counters)")
+    return ap.parse_args()
+
+
+def hip_runtime():
+    """The HIP runtime torch already loaded (one runtime per process)."""
+    maps = open("/proc/self/maps").read().splitlines()
+    paths = sorted({l.split()[-1] for l in maps if "libamdhip64" in l and l.split()[-1].startswith("/")})
+    if not paths:
+        raise RuntimeError("libamdhip64 is not loaded")
+    hip = ctypes.CDLL(paths[0])
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return hip
+
+
+def algorithmic_bytes(x, esz):
+    """Compulsory HBM bytes of one forward: inputs read once, outputs written once."""
+    q, v = x["q"], x["v"]
+    tokens = q.shape[0] * q.shape[1]
+    H_qk, D_k, H_v, D_v = q.shape[2], q.shape[3], v.shape[2], v.shape[3]
+    b = tokens * (2 * H_qk * D_k * esz + 2 * H_v * D_v * esz + H_v * esz)   # q, k, v, o, beta
+    b += x["g"].numel() * x["g"].element_size()                            # gate
+    state = x["n_seqs"] * H_v * D_k * D_v * 4
+    b += state + (state if x["h0"] is not None else 0)                     # final state, h0
+    return b
+
+
+def algorithmic_flops(x):
+    """6 d^2 + 5 C d + C^2 / 3 per token-head (d = head dim, C = 64), triangular halves counted."""
+    tokens = x["q"].shape[0] * x["q"].shape[1]
+    d, C = x["q"].shape[3], 64
+    return tokens * x["v"].shape[2] * (6 * d * d + 5 * C * d + C * C / 3)
+
+
+def source_hash(kernel):
+    with open(os.path.join(ROOT, KERNEL_SOURCES[kernel]), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, if taken on the current source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_sha256_16") != source_hash(kernel):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(x, threads):
+    from chunkwise_linear_attention_chunk_amd import synth
+    from oracle.recurrent import gdn_recurrent
+    f64 = synth.to_f64
+    args = [f64(x[n]) for n in ("q", "k", "v", "g", "beta")]
+    cu = None if x["cu_seqlens"] is None else x["cu_seqlens"].numpy()
+    nt = threads or os.cpu_count() or 1
+    t0 = time.perf_counter()
+    gdn_recurrent(*args, x["scale"], h0=f64(x["h0"]), cu_seqlens=cu, gate=x["gate"], n_threads=nt)
+    dt = time.perf_counter() - t0
+    return {"value": x["tokens"] / dt, "unit": "tokens/s", "cores": nt, "kind": "oracle",
+            "sample": f"the whole workload once ({x['tokens']} tokens x {x['v'].shape[2]} heads), "
+                      f"fp64 token recurrence, {dt:.2f} s wall"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {a.gpus}); "
+              "heads and sequences would shard across GPUs with no communication.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from chunkwise_linear_attention_chunk_amd import gdn, synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.init()
+    if a.copy_probe:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": src.numel() * 4, "copy_probe_bytes_written": dst.numel() * 4}))
+        return
+
+    w = synth.workload(a.workload)
+    x = synth.make_inputs(w)
+    esz = x["q"].element_size()
+    names = ("q", "k", "v", "g", "beta")
+    copies = []
+    for _ in range(max(1, a.copies)):
+        t = {n: x[n].to(dev) for n in names}
+        t["h0"] = None if x["h0"] is None else x["h0"].to(dev)
+        copies.append(t)
+    cu_host = None if x["cu_seqlens"] is None else x["cu_seqlens"].to(torch.int32)
+    cu_dev = None if cu_host is None else cu_host.to(dev)
+    o = torch.empty(x["v"].shape, dtype=x["q"].dtype, device=dev)
+    fs = torch.empty((x["n_seqs"],) + tuple(x["v"].shape[2:3]) + (x["q"].shape[3], x["v"].shape[3]),
+                     dtype=torch.float32, device=dev)
+    argv = [gdn.make_args(c["q"], c["k"], c["v"], c["g"], c["beta"], x["scale"], c["h0"], cu_dev, cu_host,
+                          64, o, fs) for c in copies]
+    nbytes = gdn.workspace_bytes(argv[0])
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    hip = hip_runtime()
+    n_ev = len(gdn.STAGES) + 1
+    events = []
+    for _ in range(a.steps):
+        arr = (ctypes.c_void_p * n_ev)()
+        for j in range(n_ev):
+            ev = ctypes.c_void_p()
+            if hip.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            arr[j] = ev.value
+        events.append(arr)
+
+    for i in range(a.warmup):
+        gdn.fwd_raw(argv[i % len(argv)], ws.data_ptr(), ws.numel(), stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ran = []
+    for i in range(a.steps):
+        ran.append(gdn.fwd_timed_raw(argv[i % len(argv)], ws.data_ptr(), ws.numel(), stream, events[i]))
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    stage_ms = {s: 0.0 for s in gdn.STAGES}
+    for arr, mask in zip(events, ran):
+        prev = 0  # last recorded boundary
+        for j, s in enumerate(gdn.STAGES):
+            if not (mask >> j) & 1:
+                continue
+            ms = ctypes.c_float()
+            if hip.hipEventElapsedTime(ctypes.byref(ms), arr[prev], arr[j + 1]) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            stage_ms[s] += ms.value / a.steps
+            prev = j + 1
+        for j in range(n_ev):
+            hip.hipEventDestroy(arr[j])
+    dominant = max(("intra", "chunk"), key=lambda s: stage_ms[s])
+    alg_bytes = algorithmic_bytes(x, esz)
+    if dominant == "intra":  # kernel (a) reads k, g, beta
+        k = x["k"]
+        alg_bytes_dom = k.numel() * esz + x["g"].numel() * x["g"].element_size() + x["beta"].numel() * esz
+    else:                    # kernels (b)+(d) read q, k, v, g, beta (+h0) and write o and the final state
+        alg_bytes_dom = alg_bytes
+    t_dom = stage_ms[dominant] * 1e-3
+    achieved = alg_bytes_dom / t_dom / 1e9
+    ms_step = elapsed / a.steps * 1e3
+    value = x["tokens"] * a.steps / elapsed
+    t_bound = max(alg_bytes / (HBM_PEAK_GBS * 1e9), algorithmic_flops(x) / (BF16_PEAK_TFLOPS * 1e12))
+    rec = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": {2: "bf16", 4: "f32"}[esz], "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B if not w.n_seqs else 1, "T_total": x["tokens"],
+                   "seqs": x["n_seqs"], "H_qk": w.hqk, "H_v": w.H, "d_k": w.D, "d_v": w.D,
+                   "chunk": 64, "gate": w.gate, "h0": w.h0, "input_copies": len(copies)},
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(dominant, w.name)},
+        "stage_ms": stage_ms,
+        "whole_op": {"alg_bytes": alg_bytes, "alg_flops": algorithmic_flops(x), "t_bound_ms": t_bound * 1e3,
+                     "roofline_frac": t_bound / (ms_step * 1e-3)},
+    }
+    if not a.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(x, a.cpu_threads)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -117,36 +117,69 @@ extern "C" size_t gdn_fwd_workspace_bytes(const gdn_fwd_args *a) {
     return pl.bytes;
 }
 
-extern "C" gdn_status gdn_fwd(const gdn_fwd_args *a, void *workspace, size_t workspace_bytes, void *stream) {
+namespace {
+
+gdn_status run_fwd(const gdn_fwd_args *a, void *workspace, size_t workspace_bytes, void *stream,
+                   void *const *events, uint32_t *stages_run) {
     Plan pl;
     const gdn_status st = validate_and_plan(a, &pl);
     if (st != GDN_OK) return st;
-    if (a->N == 0) return GDN_OK;
-    if (!workspace) return fail(GDN_ERR_WORKSPACE, "workspace is NULL (needs %zu bytes)", pl.bytes);
+    if (!workspace && pl.bytes) return fail(GDN_ERR_WORKSPACE, "workspace is NULL (needs %zu bytes)", pl.bytes);
     if (workspace_bytes < pl.bytes)
         return fail(GDN_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, pl.bytes);
     if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
         return fail(GDN_ERR_WORKSPACE, "workspace is not %zu-byte aligned", kAlign);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    uint32_t ran = 0;
+    // records the boundary after `stage` (or the start when stage < 0)
+    auto mark = [&](int stage) -> hipError_t {
+        if (stage >= 0) ran |= 1u << stage;
+        return events ? hipEventRecord(static_cast<hipEvent_t>(events[stage + 1]), s) : hipSuccess;
+    };
+    auto done = [&](gdn_status r) {
+        if (stages_run) *stages_run = ran;
+        return r;
+    };
+    hipError_t e = mark(-1);
+    if (e != hipSuccess) return done(fail(GDN_ERR_HIP, "event record: %s", hipGetErrorString(e)));
+    if (a->N == 0) return done(GDN_OK);
     char *ws = static_cast<char *>(workspace);
-    auto *seq = reinterpret_cast<gdn::SeqInfo *>(ws + pl.off_seq);
-    auto *chunks = reinterpret_cast<gdn::ChunkInfo *>(ws + pl.off_chunks);
-    auto *order = reinterpret_cast<int *>(ws + pl.off_order);
+    const bool packed = a->cu_seqlens_dev != nullptr;
+    gdn::SeqInfo *seq = packed ? reinterpret_cast<gdn::SeqInfo *>(ws + pl.off_seq) : nullptr;
+    gdn::ChunkInfo *chunks = packed ? reinterpret_cast<gdn::ChunkInfo *>(ws + pl.off_chunks) : nullptr;
+    int *order = packed ? reinterpret_cast<int *>(ws + pl.off_order) : nullptr;
 
-    gdn::PlanParams pp{a->cu_seqlens_dev, a->N, a->T, a->B * a->T, (int)pl.total_chunks, seq, chunks, order};
-    hipError_t e = gdn::launch_plan(pp, s);
-    if (e != hipSuccess) return fail(GDN_ERR_HIP, "plan launch: %s", hipGetErrorString(e));
+    if (packed) {
+        gdn::PlanParams pp{a->cu_seqlens_dev, a->N, a->T, a->B * a->T, (int)pl.total_chunks, seq, chunks, order};
+        e = gdn::launch_plan(pp, s);
+        if (e != hipSuccess) return done(fail(GDN_ERR_HIP, "plan launch: %s", hipGetErrorString(e)));
+        if ((e = mark(GDN_STAGE_PLAN)) != hipSuccess) return done(fail(GDN_ERR_HIP, "event: %s", hipGetErrorString(e)));
+    }
 
-    gdn::IntraParams ip{a->k, a->g, a->beta, chunks, (int)pl.total_chunks, a->H_qk, a->H_v, ws + pl.off_A};
+    gdn::IntraParams ip{a->k, a->g, a->beta, chunks, a->T, (int)pl.total_chunks, a->H_qk, a->H_v, ws + pl.off_A};
     e = gdn::launch_intra(a->dtype, a->D_k, ip, s);
-    if (e != hipSuccess) return fail(GDN_ERR_HIP, "intra launch: %s", hipGetErrorString(e));
+    if (e != hipSuccess) return done(fail(GDN_ERR_HIP, "intra launch: %s", hipGetErrorString(e)));
+    if ((e = mark(GDN_STAGE_INTRA)) != hipSuccess) return done(fail(GDN_ERR_HIP, "event: %s", hipGetErrorString(e)));
 
     gdn::ChunkParams cp{a->q, a->k, a->v, a->g, a->beta, ws + pl.off_A, a->h0, a->o, a->final_state,
-                        seq, order, a->N, a->H_qk, a->H_v, a->D_v, pl.n_slices, a->scale,
+                        seq, order, a->T, a->N, a->H_qk, a->H_v, a->D_v, pl.n_slices, a->scale,
                         a->o_dtype == GDN_DTYPE_F32 ? 1 : 0};
     e = gdn::launch_chunk(a->dtype, a->D_k, pl.BV, cp, s);
-    if (e != hipSuccess) return fail(GDN_ERR_HIP, "chunk launch: %s", hipGetErrorString(e));
-    return GDN_OK;
+    if (e != hipSuccess) return done(fail(GDN_ERR_HIP, "chunk launch: %s", hipGetErrorString(e)));
+    if ((e = mark(GDN_STAGE_CHUNK)) != hipSuccess) return done(fail(GDN_ERR_HIP, "event: %s", hipGetErrorString(e)));
+    return done(GDN_OK);
+}
+
+}  // namespace
+
+extern "C" gdn_status gdn_fwd(const gdn_fwd_args *a, void *workspace, size_t workspace_bytes, void *stream) {
+    return run_fwd(a, workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+extern "C" gdn_status gdn_fwd_timed(const gdn_fwd_args *a, void *workspace, size_t workspace_bytes, void *stream,
+                                    void *const *events, uint32_t *stages_run) {
+    if (!events) return fail(GDN_ERR_INVALID_ARG, "events is NULL");
+    return run_fwd(a, workspace, workspace_bytes, stream, events, stages_run);
 }
 
 extern "C" const char *gdn_status_string(gdn_status s) {

@@ -87,7 +87,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanParams p) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Register staging of one chunk's global tiles (loaded one chunk ahead).
+// Register staging of one chunk's global tiles (loaded one chunk ahead): vectors per thread.
 // ------------------------------------------------------------------------------------------
 template <typename T, int DK, int BV>
 struct Stage {
@@ -95,8 +95,6 @@ struct Stage {
     static constexpr int QV = 64 * DK / VEC / 256;                 // 16-byte vectors per thread (Q, K)
     static constexpr int AV = 64 * 64 / VEC / 256;                 // (A)
     static constexpr int VV = (64 * BV / VEC + 255) / 256;         // (V slice)
-    float4 q[QV], k[QV], a[AV], v[VV];
-    float g, b;
 };
 
 // LDS carve-up of the recurrence kernel (element offsets in T).
@@ -145,9 +143,9 @@ __global__ __launch_bounds__(256) void chunk_kernel(ChunkParams p) {
     const int bid = blockIdx.x, xcd = bid & 7, rr = bid >> 3;
     const int slice = rr % p.n_slices, unit = (rr / p.n_slices) * 8 + xcd;
     if (unit >= p.N * p.H_v) return;
-    const int n = p.order[unit / p.H_v], h = unit % p.H_v;
+    const int n = p.seq ? p.order[unit / p.H_v] : unit / p.H_v, h = unit % p.H_v;
     const int hq = h / (p.H_v / p.H_qk);
-    const SeqInfo si = p.seq[n];
+    const SeqInfo si = seq_info(p.seq, n, p.T);
     const int DV = p.D_v, c0 = slice * BV;
 
     const T *qb = static_cast<const T *>(p.q) + (int64_t)hq * DK;
@@ -159,28 +157,31 @@ __global__ __launch_bounds__(256) void chunk_kernel(ChunkParams p) {
     const int64_t o_off = (int64_t)h * DV + c0;
     const int64_t qk_stride = (int64_t)p.H_qk * DK, v_stride = (int64_t)p.H_v * DV;
 
-    auto load = [&](St &st, int c) {
+    // Loads are issued unconditionally from rows clamped into the chunk (every address stays in
+    // bounds) and the tail is masked when the data is staged, so no load sits behind a branch that
+    // would force a wait for it.
+    u32x4 rq[St::QV], rk[St::QV], ra[St::AV], rv[St::VV];
+    float rg, rb;
+    auto load = [&](int c) __attribute__((always_inline)) {
         const int tok = si.tok0 + c * kChunk;
-        const int nv = min(kChunk, si.len - c * kChunk);
+        const int last = min(kChunk, si.len - c * kChunk) - 1;
 #pragma unroll
         for (int i = 0; i < St::QV; ++i) {
-            const int idx = tid + 256 * i, row = idx / VPR, cv = idx - row * VPR;
-            const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-            st.q[i] = row < nv ? *reinterpret_cast<const float4 *>(qb + (tok + row) * qk_stride + cv * VEC) : z;
-            st.k[i] = row < nv ? *reinterpret_cast<const float4 *>(kb_ + (tok + row) * qk_stride + cv * VEC) : z;
+            const int idx = tid + 256 * i, row = min(idx / VPR, last), cv = idx % VPR;
+            rq[i] = *reinterpret_cast<const u32x4 *>(qb + (tok + row) * qk_stride + cv * VEC);
+            rk[i] = *reinterpret_cast<const u32x4 *>(kb_ + (tok + row) * qk_stride + cv * VEC);
         }
         const T *Ac = Ab + (int64_t)(si.chunk0 + c) * p.H_v * 4096;
 #pragma unroll
-        for (int i = 0; i < St::AV; ++i) st.a[i] = reinterpret_cast<const float4 *>(Ac)[tid + 256 * i];
+        for (int i = 0; i < St::AV; ++i) ra[i] = reinterpret_cast<const u32x4 *>(Ac)[tid + 256 * i];
 #pragma unroll
         for (int i = 0; i < St::VV; ++i) {
-            const int idx = tid + 256 * i, row = idx / VPV, cv = idx - row * VPV;
-            st.v[i] = (idx < 64 * VPV && row < nv)
-                          ? *reinterpret_cast<const float4 *>(vb + (tok + row) * v_stride + cv * VEC)
-                          : make_float4(0.f, 0.f, 0.f, 0.f);
+            const int idx = min(tid + 256 * i, 64 * VPV - 1), row = min(idx / VPV, last), cv = idx % VPV;
+            rv[i] = *reinterpret_cast<const u32x4 *>(vb + (tok + row) * v_stride + cv * VEC);
         }
-        st.g = lane < nv ? gb[(int64_t)(tok + lane) * p.H_v] : 0.f;
-        st.b = lane < nv ? to_f32(bb[(int64_t)(tok + lane) * p.H_v]) : 0.f;
+        const int tl = min(lane, last);
+        rg = gb[(int64_t)(tok + tl) * p.H_v];
+        rb = to_f32(bb[(int64_t)(tok + tl) * p.H_v]);
     };
 
     // ---- initial state (fp32 registers) and its matrix-core copy
@@ -206,39 +207,40 @@ __global__ __launch_bounds__(256) void chunk_kernel(ChunkParams p) {
         sPl[off] = from_f32<T>(0.f);
     }
 
-    St st;
-    if (si.nchunks > 0) load(st, 0);
+    if (si.nchunks > 0) load(0);
 
     for (int c = 0; c < si.nchunks; ++c) {
         const int nv = min(kChunk, si.len - c * kChunk);
         const int tokc = si.tok0 + c * kChunk;
         __syncthreads();  // the previous chunk is done with every LDS tile
 
-        // ---- stage chunk c
+        // ---- stage chunk c (rows past the chunk end become zero)
+        const u32x4 z4 = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int i = 0; i < St::QV; ++i) {
             const int idx = tid + 256 * i, row = idx / VPR, cv = idx - row * VPR;
-            *reinterpret_cast<float4 *>(sQ + row * KP + cv * VEC) = st.q[i];
-            *reinterpret_cast<float4 *>(sK + row * KP + cv * VEC) = st.k[i];
+            *reinterpret_cast<u32x4 *>(sQ + row * KP + cv * VEC) = row < nv ? rq[i] : z4;
+            *reinterpret_cast<u32x4 *>(sK + row * KP + cv * VEC) = row < nv ? rk[i] : z4;
         }
 #pragma unroll
         for (int i = 0; i < St::AV; ++i) {
             const int idx = tid + 256 * i, row = idx / (64 / VEC), cv = idx - row * (64 / VEC);
-            *reinterpret_cast<float4 *>(sA + row * TP + cv * VEC) = st.a[i];
+            *reinterpret_cast<u32x4 *>(sA + row * TP + cv * VEC) = ra[i];
         }
 #pragma unroll
         for (int i = 0; i < St::VV; ++i) {
             const int idx = tid + 256 * i;
-            if (idx < 64 * VPV) reinterpret_cast<float4 *>(sV)[idx] = st.v[i];
+            if (idx < 64 * VPV) reinterpret_cast<u32x4 *>(sV)[idx] = (idx / VPV) < nv ? rv[i] : z4;
         }
-        const float gl = wave_inclusive_scan(st.g) * kLog2e;  // lane t: log2 gamma_t
+        const float gv = lane < nv ? rg : 0.f, bv = lane < nv ? rb : 0.f;
+        const float gl = wave_inclusive_scan(gv) * kLog2e;    // lane t: log2 gamma_t
         const float glC = __shfl(gl, 63, 64);                  // tail tokens carry g = 0
         if (wave == 0) {
             sGl[lane] = gl;
-            sB[lane] = st.b;
+            sB[lane] = bv;
             sSc[lane] = exp2f(glC - gl);                       // gamma_C / gamma_t
         }
-        if (c + 1 < si.nchunks) load(st, c + 1);              // overlaps with the compute below
+        load(min(c + 1, si.nchunks - 1));                      // overlaps with the compute below
         __syncthreads();
 
         // ---- P = scale * Lower(Gamma) (.) Q K^T, built as P^T tiles (rows of P land contiguous)

@@ -22,6 +22,8 @@ typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // raw 16 bytes (a native vector, so
+                                                              // selects and copies stay in registers)
 
 constexpr float kLog2e = 1.4426950408889634f;
 

@@ -30,9 +30,22 @@ struct PlanParams {
     int *order;             // [N] sequences, longest first (ties by index)
 };
 
+// Batched (not packed) input has no tables: sequence n covers tokens [n T, n T + T).
+__device__ __forceinline__ SeqInfo seq_info(const SeqInfo *seq, int n, int T) {
+    if (seq) return seq[n];
+    const int nc = (T + kChunk - 1) / kChunk;
+    return SeqInfo{n * T, T, n * nc, nc};
+}
+__device__ __forceinline__ ChunkInfo chunk_info(const ChunkInfo *chunks, int ci, int T) {
+    if (chunks) return chunks[ci];
+    const int nc = (T + kChunk - 1) / kChunk, n = ci / nc, c = ci - n * nc;
+    return ChunkInfo{n * T + c * kChunk, min(kChunk, T - c * kChunk)};
+}
+
 struct IntraParams {
     const void *k, *g, *beta;
-    const ChunkInfo *chunks;
+    const ChunkInfo *chunks;  // nullptr: batched input of T tokens per sequence
+    int T;
     int n_chunks, H_qk, H_v;
     void *A;                // [n_chunks][H_v][64][64] in the input dtype
 };
@@ -43,8 +56,9 @@ struct ChunkParams {
     const float *h0;        // nullable [N][H_v][D_k][D_v]
     void *o;
     float *final_state;     // nullable
-    const SeqInfo *seq;
+    const SeqInfo *seq;     // nullptr: batched input of T tokens per sequence (order = identity)
     const int *order;
+    int T;
     int N, H_qk, H_v, D_v, n_slices;
     float scale;
     int o_f32;              // 1: o is fp32 (the unrounded result), 0: o has the input dtype

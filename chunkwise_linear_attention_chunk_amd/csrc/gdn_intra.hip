@@ -37,30 +37,36 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraParams p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, grp = lane >> 4;
     const int ci = blockIdx.x / p.H_v, h = blockIdx.x - ci * p.H_v;
     const int hq = h / (p.H_v / p.H_qk);
-    const ChunkInfo cinfo = p.chunks[ci];
+    const ChunkInfo cinfo = chunk_info(p.chunks, ci, p.T);
     const int t0 = cinfo.tok0, nv = cinfo.nv;
     const T *k = static_cast<const T *>(p.k);
     const float *g = static_cast<const float *>(p.g);
     const T *beta = static_cast<const T *>(p.beta);
 
     // ---- chunk-local inclusive cumsum of the log-gate (log2 units) and beta; tail rows are 0
+    // Loads are unconditional from rows clamped into the chunk (always in bounds); the tail is
+    // masked afterwards, so the loads are not serialised behind branches.
+    const int last = max(nv - 1, 0);
+    constexpr int VPR = DK / VEC;
+    constexpr int NV = 64 * VPR / 256;
+    u32x4 kv[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int idx = tid + 256 * i, row = min(idx / VPR, last), cv = idx % VPR;
+        kv[i] = *reinterpret_cast<const u32x4 *>(k + ((int64_t)(t0 + row) * p.H_qk + hq) * DK + cv * VEC);
+    }
     if (wave == 0) {
-        float gv = 0.f, bv = 0.f;
-        if (lane < nv) {
-            const int64_t idx = (int64_t)(t0 + lane) * p.H_v + h;
-            gv = g[idx];
-            bv = to_f32(beta[idx]);
-        }
+        const int64_t idx = (int64_t)(t0 + min(lane, last)) * p.H_v + h;
+        const float gv = lane < nv ? g[idx] : 0.f;
+        const float bv = lane < nv ? to_f32(beta[idx]) : 0.f;
         sGl[lane] = wave_inclusive_scan(gv) * kLog2e;
         sB[lane] = bv;
     }
     // ---- K tile [64][DK] (rows past the chunk end are zero)
-    constexpr int VPR = DK / VEC;
-    for (int idx = tid; idx < 64 * VPR; idx += 256) {
-        const int row = idx / VPR, cv = idx - row * VPR;
-        float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (row < nv) val = *reinterpret_cast<const float4 *>(k + ((int64_t)(t0 + row) * p.H_qk + hq) * DK + cv * VEC);
-        *reinterpret_cast<float4 *>(sK + row * KP + cv * VEC) = val;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int idx = tid + 256 * i, row = idx / VPR, cv = idx % VPR;
+        *reinterpret_cast<u32x4 *>(sK + row * KP + cv * VEC) = row < nv ? kv[i] : u32x4{0u, 0u, 0u, 0u};
     }
     __syncthreads();
 
@@ -153,7 +159,7 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraParams p) {
             const int col = c0 + e;
             vals[e] = from_f32<T>(col < row ? sX[row * LP + col] : (col == row ? 1.f : 0.f));
         }
-        *reinterpret_cast<float4 *>(A + row * 64 + c0) = *reinterpret_cast<const float4 *>(vals);
+        *reinterpret_cast<u32x4 *>(A + row * 64 + c0) = *reinterpret_cast<const u32x4 *>(vals);
     }
 }
 

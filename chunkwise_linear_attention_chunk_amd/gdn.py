@@ -17,7 +17,8 @@ GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP
 DTYPE_F32, DTYPE_BF16 = 0, 1
 GATE_SCALAR, GATE_CHANNEL = 0, 1
 CP_MODES = {"auto": 0, "off": 1, "on": 2}
-EXPORTED = ("gdn_fwd", "gdn_fwd_workspace_bytes", "gdn_status_string", "gdn_last_error")
+EXPORTED = ("gdn_fwd", "gdn_fwd_timed", "gdn_fwd_workspace_bytes", "gdn_status_string", "gdn_last_error")
+STAGES = ("plan", "intra", "cp_pre", "cp_fix", "chunk")  # order of gdn_fwd_timed's stages
 
 
 class GdnError(RuntimeError):
@@ -54,6 +55,9 @@ def lib():
         L.gdn_fwd_workspace_bytes.restype = ctypes.c_size_t
         L.gdn_fwd.argtypes = [ctypes.POINTER(FwdArgs), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         L.gdn_fwd.restype = ctypes.c_int
+        L.gdn_fwd_timed.argtypes = [ctypes.POINTER(FwdArgs), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.POINTER(ctypes.c_uint32)]
+        L.gdn_fwd_timed.restype = ctypes.c_int
         L.gdn_status_string.argtypes = [ctypes.c_int]
         L.gdn_status_string.restype = ctypes.c_char_p
         L.gdn_last_error.argtypes = []
@@ -114,6 +118,16 @@ def fwd_raw(args, workspace, workspace_bytes_, stream):
     """Call gdn_fwd with a prepared FwdArgs, a workspace pointer (int) and a stream handle (int)."""
     _check(lib().gdn_fwd(ctypes.byref(args), ctypes.c_void_p(workspace), ctypes.c_size_t(workspace_bytes_),
                          ctypes.c_void_p(stream)))
+
+
+def fwd_timed_raw(args, workspace, workspace_bytes_, stream, events):
+    """gdn_fwd_timed with events = a ctypes array of len(STAGES) + 1 hipEvent_t handles.
+
+    Returns the bit mask of the stages that ran (their events were recorded)."""
+    ran = ctypes.c_uint32(0)
+    _check(lib().gdn_fwd_timed(ctypes.byref(args), ctypes.c_void_p(workspace), ctypes.c_size_t(workspace_bytes_),
+                               ctypes.c_void_p(stream), ctypes.cast(events, ctypes.c_void_p), ctypes.byref(ran)))
+    return ran.value
 
 
 def fwd(q, k, v, g, beta, scale=None, initial_state=None, cu_seqlens=None, chunk_size=64,

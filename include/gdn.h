@@ -100,6 +100,24 @@ size_t gdn_fwd_workspace_bytes(const gdn_fwd_args *a);
  * bytes, 256-byte aligned; its contents on entry do not matter. */
 gdn_status gdn_fwd(const gdn_fwd_args *a, void *workspace, size_t workspace_bytes, void *stream);
 
+/* Stages of one forward, in launch order, for gdn_fwd_timed. */
+enum {
+    GDN_STAGE_PLAN = 0,      /* sequence / chunk tables */
+    GDN_STAGE_INTRA = 1,     /* kernel (a): gate cumsum, gated beta*K K^T, inverse */
+    GDN_STAGE_CP_PRE = 2,    /* in-GPU context parallelism: per-segment S* and M */
+    GDN_STAGE_CP_FIX = 3,    /* in-GPU context parallelism: serial fix-up of segment starts */
+    GDN_STAGE_CHUNK = 4,     /* kernels (b)+(d): state recurrence fused with the output */
+    GDN_N_STAGES = 5
+};
+
+/* Same as gdn_fwd, and also records caller-created hipEvent_t events on `stream` for
+ * measurement: events[0] before the first stage and events[i + 1] right after stage i, for the
+ * stages that run with these arguments (bit i of *stages_run is set for them); events of stages
+ * that do not run are not recorded, so a stage's duration is the time from the previous recorded
+ * event to its own.  events must hold GDN_N_STAGES + 1 valid events; stages_run may be NULL. */
+gdn_status gdn_fwd_timed(const gdn_fwd_args *a, void *workspace, size_t workspace_bytes, void *stream,
+                         void *const *events, uint32_t *stages_run);
+
 /* Static, human-readable name of a status code. */
 const char *gdn_status_string(gdn_status s);
 
