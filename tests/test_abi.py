@@ -1,0 +1,131 @@
+"""C-ABI checks that need no GPU: exported symbols, struct layout, argument validation, planning.
+
+Validation runs before any launch, so every error path here returns without touching HIP.
+"""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+from chunkwise_linear_attention_chunk_amd import gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported():
+    names = _declared_functions()
+    assert {"gdn_fwd", "gdn_fwd_timed", "gdn_fwd_workspace_bytes", "gdn_status_string", "gdn_last_error"} <= set(names)
+    lib = ctypes.CDLL(gdn.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} is declared in gdn.h but not exported"
+    assert set(gdn.EXPORTED) == set(names)
+
+
+def test_struct_layout_matches_header():
+    fields = [f[0] for f in gdn.FwdArgs._fields_]
+    src = "#include <stdio.h>\n#include <stddef.h>\n#include \"gdn.h\"\nint main(void){\n"
+    src += 'printf("%zu\\n", sizeof(gdn_fwd_args));\n'
+    src += "".join(f'printf("%zu\\n", offsetof(gdn_fwd_args, {f}));\n' for f in fields)
+    src += "return 0;}\n"
+    with tempfile.TemporaryDirectory() as d:
+        c, exe = os.path.join(d, "probe.c"), os.path.join(d, "probe")
+        open(c, "w").write(src)
+        subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), c, "-o", exe], check=True)
+        out = [int(x) for x in subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split()]
+    assert out[0] == ctypes.sizeof(gdn.FwdArgs)
+    for f, off in zip(fields, out[1:]):
+        assert getattr(gdn.FwdArgs, f).offset == off, f"field {f}: ctypes {getattr(gdn.FwdArgs, f).offset} vs C {off}"
+
+
+def test_status_strings():
+    lib = gdn.lib()
+    for code, name in enumerate(["GDN_OK", "GDN_ERR_INVALID_ARG", "GDN_ERR_UNSUPPORTED", "GDN_ERR_WORKSPACE",
+                                 "GDN_ERR_HIP"]):
+        assert lib.gdn_status_string(code).decode() == name
+
+
+def _args(**kw):
+    a = gdn.FwdArgs()
+    a.B, a.T, a.H_qk, a.H_v, a.D_k, a.D_v = 2, 300, 4, 8, 128, 128
+    a.chunk_size, a.dtype, a.gate_kind, a.scale, a.N = 64, gdn.DTYPE_BF16, gdn.GATE_SCALAR, 0.088, 2
+    a.o_dtype = gdn.DTYPE_BF16
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: every case fails validation or sizing first
+    a.q = a.k = a.v = a.g = a.beta = a.o = fake
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def _status(a, workspace=None, nbytes=0):
+    return gdn.lib().gdn_fwd(ctypes.byref(a), workspace, nbytes, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(chunk_size=48), gdn.GDN_ERR_INVALID_ARG, "power of two"),
+    (dict(chunk_size=32), gdn.GDN_ERR_UNSUPPORTED, "chunk_size"),
+    (dict(D_k=512, D_v=512), gdn.GDN_ERR_UNSUPPORTED, "D_k=512"),
+    (dict(D_k=96), gdn.GDN_ERR_UNSUPPORTED, "D_k=96"),
+    (dict(H_v=6), gdn.GDN_ERR_INVALID_ARG, "multiple"),
+    (dict(dtype=7), gdn.GDN_ERR_INVALID_ARG, "dtype"),
+    (dict(o_dtype=gdn.DTYPE_BF16, dtype=gdn.DTYPE_F32), gdn.GDN_ERR_INVALID_ARG, "o_dtype"),
+    (dict(N=3), gdn.GDN_ERR_INVALID_ARG, "N=3"),
+    (dict(q=None), gdn.GDN_ERR_INVALID_ARG, "required"),
+    (dict(B=-1), gdn.GDN_ERR_INVALID_ARG, "B=-1"),
+    (dict(cp_mode=9), gdn.GDN_ERR_INVALID_ARG, "cp_mode"),
+    (dict(scale=float("nan")), gdn.GDN_ERR_INVALID_ARG, "scale"),
+])
+def test_invalid_arguments_are_rejected_before_launch(kw, status, msg):
+    a = _args(**kw)
+    assert _status(a) == status
+    assert msg in gdn.lib().gdn_last_error().decode()
+    assert gdn.workspace_bytes(a) == 0
+
+
+def _packed(cu, **kw):
+    arr = (ctypes.c_int32 * len(cu))(*cu)
+    kw = {"T": cu[-1], **kw}
+    a = _args(B=1, N=len(cu) - 1, cu_seqlens_host=ctypes.cast(arr, ctypes.c_void_p),
+              cu_seqlens_dev=ctypes.c_void_p(0x2000), **kw)
+    return a, arr
+
+
+@pytest.mark.parametrize("cu,msg", [([1, 5, 9], "cu_seqlens[0]"), ([0, 9, 5], "decreases"), ([0, 4, 9], None)])
+def test_packed_sequence_validation(cu, msg):
+    a, keep = _packed(cu, T=8) if msg is None else _packed(cu)
+    assert _status(a) == gdn.GDN_ERR_INVALID_ARG
+    assert (msg or "!= T") in gdn.lib().gdn_last_error().decode()
+
+
+def test_packed_needs_single_batch_row_and_host_copy():
+    a, keep = _packed([0, 10, 20])
+    a.B = 2
+    assert _status(a) == gdn.GDN_ERR_INVALID_ARG
+    a, keep = _packed([0, 10, 20])
+    a.cu_seqlens_host = None
+    assert _status(a) == gdn.GDN_ERR_INVALID_ARG
+
+
+def test_workspace_size_and_checks():
+    a = _args()
+    n = gdn.workspace_bytes(a)
+    # A: ceil(300/64) = 5 chunks per sequence x 2 sequences x 8 heads x 64 x 64 bf16, plus small tables
+    assert n >= 10 * 8 * 64 * 64 * 2
+    assert n < 10 * 8 * 64 * 64 * 2 + 4096
+    assert _status(a, None, 0) == gdn.GDN_ERR_WORKSPACE
+    assert _status(a, ctypes.c_void_p(0x10000), n - 1) == gdn.GDN_ERR_WORKSPACE
+    assert _status(a, ctypes.c_void_p(0x10001), n) == gdn.GDN_ERR_WORKSPACE  # misaligned
+    assert "aligned" in gdn.lib().gdn_last_error().decode()
+    # packed lengths change the chunk count: ceil(1/64) + ceil(64/64) + ceil(65/64) = 4 chunks
+    p, keep = _packed([0, 1, 65, 130])
+    assert gdn.workspace_bytes(p) >= 4 * 8 * 64 * 64 * 2
+    assert gdn.workspace_bytes(p) < 4 * 8 * 64 * 64 * 2 + 4096
