@@ -95,8 +95,10 @@ gdn_status validate_and_plan(const gdn_fwd_args *a, Plan *pl) {
     pl->total_chunks = nch;
     if (nch * a->H_v > INT32_MAX) return fail(GDN_ERR_UNSUPPORTED, "too many chunk-heads");
 
+    // value columns per recurrence workgroup (16 per chain/output wave pair); GDN_BV overrides
+    // for experiments.  fp32 with D_k = 128 fits the LDS budget only with one pair.
     const int bv_env = env_int("GDN_BV", 0);
-    pl->BV = (a->dtype == GDN_DTYPE_F32) ? 16 : (bv_env == 16 ? 16 : 32);
+    pl->BV = (a->dtype == GDN_DTYPE_F32 && a->D_k == 128) ? 16 : (bv_env == 16 ? 16 : 32);
     pl->n_slices = a->D_v / pl->BV;
 
     const size_t esz = a->dtype == GDN_DTYPE_BF16 ? 2 : 4;

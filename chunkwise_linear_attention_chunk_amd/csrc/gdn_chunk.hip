@@ -87,66 +87,138 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanParams p) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Register staging of one chunk's global tiles (loaded one chunk ahead): vectors per thread.
+// Recurrence + output.  One workgroup per (sequence, value head, NSUB slices of 16 value columns);
+// per slice a chain wave (waves 0 .. NSUB-1) and an output wave (waves NSUB .. 2 NSUB-1).
+// Per chunk c, two phases separated by one workgroup barrier:
+//   phase 1  chain: hand S_c to the output wave; KS = K S_c; X = diag(beta)(V - diag(gamma) KS);
+//                   V' = A X; hand V' to the output wave; V'' = diag(gamma_C / gamma) V'
+//            output: P = scale Lower(Gamma) (.) Q K^T (registers)
+//   phase 2  chain: S_{c+1} = gamma_C S_c + K^T V''   (K^T read transposed from the K tile)
+//            output: O = scale diag(gamma) Q S_c + P V', stored
+// Accumulator tiles feed the next product directly (pi order, gdn_device.h).  Q, K, A and the V
+// slice of chunk c + 1 stream into the other LDS buffer with direct-to-LDS loads while chunk c
+// computes.  Rows past the end of a chunk are loaded from the last valid row (always in bounds);
+// they meet beta = 0 and g = 0, so X and V' vanish there, and their outputs are not stored.
 // ------------------------------------------------------------------------------------------
-template <typename T, int DK, int BV>
-struct Stage {
-    static constexpr int VEC = Vec16<T>::N;
-    static constexpr int QV = 64 * DK / VEC / 256;                 // 16-byte vectors per thread (Q, K)
-    static constexpr int AV = 64 * 64 / VEC / 256;                 // (A)
-    static constexpr int VV = (64 * BV / VEC + 255) / 256;         // (V slice)
-};
+// Per-token gate rows of one chunk, staged once by wave 0.
+enum { GL = 0, BETA = 64, SC = 128, GAM = 192, SGAM = 256, GROWS = 320 };  // log2 gamma, beta,
+                                                                        // gamma_C/gamma, gamma, scale*gamma
 
-// LDS carve-up of the recurrence kernel (element offsets in T).
-template <typename T, int DK, int BV>
-struct ChunkLds {
-    static constexpr int VEC = Vec16<T>::N;
-    static constexpr int KP = DK + VEC;   // row stride of [*, DK] tiles (padded against bank conflicts)
-    static constexpr int TP = 64 + VEC;   // row stride of [*, 64] tiles
+template <typename T, int DK, int NSUB, int NBUF>
+struct RecLds {
+    static constexpr int ESZ = (int)sizeof(T);
+    static constexpr int BV = 16 * NSUB;
+    static constexpr int KGPR = DK * ESZ / 16;     // 16-byte granules per Q/K row
+    static constexpr int AGPR = 64 * ESZ / 16;     // per A row
+    static constexpr int VGPR = BV * ESZ / 16;     // per V-slice row
+    static constexpr int KT = 64 * KGPR * 16, AT = 64 * AGPR * 16, VT = 64 * VGPR * 16;  // tile bytes
+    static constexpr int NKB = DK / 32;
     static constexpr int NS = Split<T>::parts;
-    static constexpr int Q = 0, K = Q + 64 * KP, A = K + 64 * KP;
-    static constexpr int P = A + 64 * TP;                 // NS x [64][TP]   scale * Lower(Gamma) (.) Q K^T
-    static constexpr int St = P + NS * 64 * TP;           // NS x [BV][KP]   S^T
-    static constexpr int Xt = St + NS * BV * KP;          // NS x [BV][TP]   X^T
-    static constexpr int V = Xt + NS * BV * TP;           // [64][BV]        V slice
-    static constexpr int VP_BYTES = 2 * NS * BV * TP;     // V'^T and V''^T = (diag(gamma_C/gamma) V')^T
-    static constexpr bool VP_IN_Q = VP_BYTES <= 64 * KP;  // alias them onto Q once Q is consumed
-    static constexpr int Vp = VP_IN_Q ? Q : V + 64 * BV;
-    static constexpr int END = VP_IN_Q ? V + 64 * BV : Vp + VP_BYTES;
-    static constexpr int BYTES = END * (int)sizeof(T);
+    // one tile buffer (byte offsets): K, Q, A, V slice of one chunk
+    static constexpr int K0 = 0, Q0 = KT, A0 = 2 * KT, V0 = 2 * KT + AT, TILES = 2 * KT + AT + VT;
+    static constexpr int SXN = NSUB * NKB * NS * 64;   // state fragments handed to the output waves
+    static constexpr int VXN = NSUB * 2 * NS * 64;     // V' fragments handed to the output waves
+    static constexpr int PXN = 6 * NS * 64;            // P fragments shared by the output waves
+    static constexpr int BYTES = NBUF * TILES + (SXN + VXN + PXN) * (int)sizeof(Frag<T>) + 2 * GROWS * 4;
+    static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
-template <typename T, int DK, int BV>
-__global__ __launch_bounds__(256) void chunk_kernel(ChunkParams p) {
-    using St = Stage<T, DK, BV>;
-    using L = ChunkLds<T, DK, BV>;
-    constexpr int VEC = St::VEC, KP = L::KP, TP = L::TP;
-    constexpr bool SPLIT = Split<T>::parts == 2;
-    constexpr int NT = BV / 16;    // value-column tiles
-    constexpr int MT = DK / 64;    // 16-row state tiles per wave
-    constexpr int VPR = DK / VEC;  // vectors per Q/K row
-    constexpr int VPV = BV / VEC;  // vectors per V-slice row
+// 8 consecutive elements (col multiple of 8) of a swizzled tile row.
+template <int GPR>
+__device__ __forceinline__ Frag<bf16> ld8_t(const unsigned char *tile, int row, int col) {
+    Frag<bf16> f;
+    f.v = *reinterpret_cast<const bf16x8 *>(tile + tile_off<GPR, 2>(row, col));
+    return f;
+}
+template <int GPR>
+__device__ __forceinline__ Frag<float> ld8_t_f(const unsigned char *tile, int row, int col) {
+    const float4 a = *reinterpret_cast<const float4 *>(tile + tile_off<GPR, 4>(row, col));
+    const float4 b = *reinterpret_cast<const float4 *>(tile + tile_off<GPR, 4>(row, col + 4));
+    Frag<float> f;
+    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+    return f;
+}
+template <typename T, int GPR>
+__device__ __forceinline__ Frag<T> ld8_tile(const unsigned char *tile, int row, int col) {
+    if constexpr (sizeof(T) == 2) return ld8_t<GPR>(tile, row, col);
+    else return ld8_t_f<GPR>(tile, row, col);
+}
+// pi-order operand of a swizzled tile row: elements [32kb + 4grp, +4) and [32kb + 16 + 4grp, +4).
+template <typename T, int GPR>
+__device__ __forceinline__ Frag<T> ldpi_tile(const unsigned char *tile, int row, int kb) {
+    const int grp = (threadIdx.x & 63) >> 4;
+    const int c0 = 32 * kb + 4 * grp, c1 = c0 + 16;
+    Frag<T> f;
+    if constexpr (sizeof(T) == 2) {
+        const bf16x4 a = *reinterpret_cast<const bf16x4 *>(tile + tile_off<GPR, 2>(row, c0));
+        const bf16x4 b = *reinterpret_cast<const bf16x4 *>(tile + tile_off<GPR, 2>(row, c1));
+        f.v = bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    } else {
+        const float4 a = *reinterpret_cast<const float4 *>(tile + tile_off<GPR, 4>(row, c0));
+        const float4 b = *reinterpret_cast<const float4 *>(tile + tile_off<GPR, 4>(row, c1));
+        f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+        f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+    }
+    return f;
+}
+// pi-order column operand of the K tile (the K^T operand of the state update): row d, tokens
+// 32kb + 4grp + r and 32kb + 16 + 4grp + r.
+template <typename T, int GPR>
+__device__ __forceinline__ Frag<T> ldpi_col_tile(const unsigned char *tile, int d0, int kb) {
+    const int lane = threadIdx.x & 63, grp = lane >> 4, j = lane & 15;
+    Frag<T> f;
+    if constexpr (sizeof(T) == 2) {
+        // transposed reads: lane j = 4e + q of the group points at K[t_e][d0 + 4q .. + 3]
+        const int e = j >> 2, q = j & 3;
+        const int t0 = 32 * kb + 4 * grp + e;
+        const bf16x4 a = lds_read_tr16(tile + tile_off<GPR, 2>(t0, d0 + 4 * q));
+        const bf16x4 b = lds_read_tr16(tile + tile_off<GPR, 2>(t0 + 16, d0 + 4 * q));
+        f.v = bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int t = 32 * kb + (e < 4 ? 4 * grp + e : 16 + 4 * grp + e - 4);
+            f.v[e] = *reinterpret_cast<const float *>(tile + tile_off<GPR, 4>(t, d0 + j));
+        }
+    }
+    return f;
+}
 
-    __shared__ __attribute__((aligned(16))) T smem[L::END];
-    __shared__ float sGl[64], sB[64], sSc[64];
-    T *sQ = smem + L::Q, *sK = smem + L::K, *sA = smem + L::A, *sV = smem + L::V;
-    T *sPh = smem + L::P, *sPl = sPh + (SPLIT ? 64 * TP : 0);
-    T *sSth = smem + L::St, *sStl = sSth + (SPLIT ? BV * KP : 0);
-    T *sXth = smem + L::Xt, *sXtl = sXth + (SPLIT ? BV * TP : 0);
-    T *sVph = smem + L::Vp, *sVpl = sVph + (SPLIT ? BV * TP : 0);          // V'^T
-    T *sVqh = sVph + L::NS * BV * TP, *sVql = sVqh + (SPLIT ? BV * TP : 0);  // V''^T
+template <typename T, int DK, int NSUB, int NBUF>
+__global__ __launch_bounds__(128 * NSUB) void chunk_kernel(ChunkParams p) {
+    using L = RecLds<T, DK, NSUB, NBUF>;
+    constexpr int NW = 2 * NSUB;                   // waves
+    constexpr int BV = L::BV, NKB = L::NKB, ESZ = L::ESZ;
+    constexpr int EPG = 16 / ESZ;                  // elements per granule
+    constexpr int MD = DK / 16;                    // 16-row state tiles
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, grp = lane >> 4;
+    // Separate LDS objects for the two tile buffers and for the exchange: the chunk loop is
+    // unrolled by two, so every LDS access names its buffer at compile time and the compiler can
+    // see that the direct-to-LDS loads into one buffer never alias the reads of the other (it
+    // would otherwise wait for the loads before every LDS access).
+    __shared__ __attribute__((aligned(16))) unsigned char tiles0[L::TILES];
+    __shared__ __attribute__((aligned(16))) unsigned char tiles1[NBUF == 2 ? L::TILES : 16];
+    __shared__ __attribute__((aligned(16))) Frag<T> sSx[L::SXN];
+    __shared__ __attribute__((aligned(16))) Frag<T> sVx[L::VXN];
+    __shared__ __attribute__((aligned(16))) Frag<T> sPx[L::PXN];
+    __shared__ float sG[2 * GROWS];
+
+    // the wave index is uniform across a wave: readfirstlane makes the role branches scalar
+    const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool chain = wave < NSUB;
+    const int sub = chain ? wave : wave - NSUB;
 
     // XCD-aware mapping: the slices of one (sequence, head) share blockIdx % 8, i.e. one XCD and
-    // its L2, so Q/K/A tiles fetched by one slice are L2 hits for the others.
+    // its L2, so Q/K/A fetched by one workgroup are L2 hits for the others.
     const int bid = blockIdx.x, xcd = bid & 7, rr = bid >> 3;
     const int slice = rr % p.n_slices, unit = (rr / p.n_slices) * 8 + xcd;
     if (unit >= p.N * p.H_v) return;
     const int n = p.seq ? p.order[unit / p.H_v] : unit / p.H_v, h = unit % p.H_v;
     const int hq = h / (p.H_v / p.H_qk);
     const SeqInfo si = seq_info(p.seq, n, p.T);
-    const int DV = p.D_v, c0 = slice * BV;
+    const int DV = p.D_v, c0 = slice * BV, col = c0 + 16 * sub + l16;  // this lane's value column
 
     const T *qb = static_cast<const T *>(p.q) + (int64_t)hq * DK;
     const T *kb_ = static_cast<const T *>(p.k) + (int64_t)hq * DK;
@@ -154,235 +226,258 @@ __global__ __launch_bounds__(256) void chunk_kernel(ChunkParams p) {
     const float *gb = static_cast<const float *>(p.g) + h;
     const T *bb = static_cast<const T *>(p.beta) + h;
     const T *Ab = static_cast<const T *>(p.A) + (int64_t)h * 4096;
-    const int64_t o_off = (int64_t)h * DV + c0;
     const int64_t qk_stride = (int64_t)p.H_qk * DK, v_stride = (int64_t)p.H_v * DV;
+    const int qks = (int)qk_stride, vs = (int)v_stride, hv = p.H_v;
+    const int nch = si.nchunks;
+    auto nvalid = [&](int c) { return min(kChunk, si.len - c * kChunk); };
 
-    // Loads are issued unconditionally from rows clamped into the chunk (every address stays in
-    // bounds) and the tail is masked when the data is staged, so no load sits behind a branch that
-    // would force a wait for it.
-    u32x4 rq[St::QV], rk[St::QV], ra[St::AV], rv[St::VV];
-    float rg, rb;
-    auto load = [&](int c) __attribute__((always_inline)) {
-        const int tok = si.tok0 + c * kChunk;
-        const int last = min(kChunk, si.len - c * kChunk) - 1;
-#pragma unroll
-        for (int i = 0; i < St::QV; ++i) {
-            const int idx = tid + 256 * i, row = min(idx / VPR, last), cv = idx % VPR;
-            rq[i] = *reinterpret_cast<const u32x4 *>(qb + (tok + row) * qk_stride + cv * VEC);
-            rk[i] = *reinterpret_cast<const u32x4 *>(kb_ + (tok + row) * qk_stride + cv * VEC);
-        }
+    // ---- direct-to-LDS loads of chunk c into a tile buffer; instruction i of a tile goes to wave i % NW
+    auto issue_loads = [&](int c, unsigned char *tb) __attribute__((always_inline)) {
+        const int64_t tok = si.tok0 + c * kChunk;
+        const int last = nvalid(c) - 1;
+        const T *kc = kb_ + tok * qk_stride, *qc = qb + tok * qk_stride, *vc = vb + tok * v_stride;
         const T *Ac = Ab + (int64_t)(si.chunk0 + c) * p.H_v * 4096;
 #pragma unroll
-        for (int i = 0; i < St::AV; ++i) ra[i] = reinterpret_cast<const u32x4 *>(Ac)[tid + 256 * i];
-#pragma unroll
-        for (int i = 0; i < St::VV; ++i) {
-            const int idx = min(tid + 256 * i, 64 * VPV - 1), row = min(idx / VPV, last), cv = idx % VPV;
-            rv[i] = *reinterpret_cast<const u32x4 *>(vb + (tok + row) * v_stride + cv * VEC);
+        for (int i = wave; i < L::KGPR; i += NW) {         // 64 * KGPR granules = KGPR instructions
+            const int pos = 64 * i + lane, row = pos / L::KGPR, g = pos % L::KGPR;
+            const int cv = g ^ tile_swz<L::KGPR>(row), rowc = min(row, last);
+            load_granule_to_lds(kc + rowc * qks + cv * EPG, tb + L::K0 + 1024 * i);
+            load_granule_to_lds(qc + rowc * qks + cv * EPG, tb + L::Q0 + 1024 * i);
         }
-        const int tl = min(lane, last);
-        rg = gb[(int64_t)(tok + tl) * p.H_v];
-        rb = to_f32(bb[(int64_t)(tok + tl) * p.H_v]);
+#pragma unroll
+        for (int i = wave; i < L::AGPR; i += NW) {
+            const int pos = 64 * i + lane, row = pos / L::AGPR, g = pos % L::AGPR;
+            const int cv = g ^ tile_swz<L::AGPR>(row);
+            load_granule_to_lds(Ac + row * 64 + cv * EPG, tb + L::A0 + 1024 * i);
+        }
+#pragma unroll
+        for (int i = wave; i < L::VGPR; i += NW) {
+            const int pos = 64 * i + lane, row = pos / L::VGPR, g = pos % L::VGPR;
+            const int cv = g ^ tile_swz<L::VGPR>(row), rowc = min(row, last);
+            load_granule_to_lds(vc + rowc * vs + cv * EPG, tb + L::V0 + 1024 * i);
+        }
+    };
+    float rg = 0.f;   // wave 0: gate and (raw) beta of token `lane` of the next chunk; converted
+    T rb = T(0.f);    // only when used, so the loads are not waited for here
+    auto load_gates = [&](int c) __attribute__((always_inline)) {
+        const int64_t tok = si.tok0 + c * kChunk;
+        const int tl = min(lane, nvalid(c) - 1);
+        rg = (gb + tok * hv)[tl * hv];
+        rb = (bb + tok * hv)[tl * hv];
     };
 
-    // ---- initial state (fp32 registers) and its matrix-core copy
-    const int drow0 = wave * (DK / 4);
-    f32x4 S[MT][NT];
+    // ---- chain state: S [DK][16] of this slice in fp32 accumulator tiles (rows 16m + 4grp + r)
+    f32x4 S[MD];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int m = 0; m < MD; ++m)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int d = drow0 + 16 * mt + 4 * grp + r, col = c0 + 16 * nt + l16;
-                S[mt][nt][r] = p.h0 ? p.h0[(((int64_t)n * p.H_v + h) * DK + d) * DV + col] : 0.f;
+        for (int r = 0; r < 4; ++r)
+            S[m][r] = (chain && p.h0) ? p.h0[(((int64_t)n * p.H_v + h) * DK + 16 * m + 4 * grp + r) * DV + col] : 0.f;
+
+    // ---- one chunk; B = tile buffer holding it (compile time)
+    auto step = [&]<int B>(int c) __attribute__((always_inline)) {
+        unsigned char *tcur = B == 0 ? tiles0 : tiles1;
+        unsigned char *tnext = B == 0 ? tiles1 : tiles0;
+        if constexpr (NBUF == 1) {
+            if (c > 0) {
+                __syncthreads();  // every wave is done with the single buffer
+                issue_loads(c, tiles0);
             }
-            const int off = (16 * nt + l16) * KP + drow0 + 16 * mt + 4 * grp;
-            st4_split(sSth + off, sStl + off, S[mt][nt]);
         }
-    // P's upper tiles inside the contraction blocks that are used: (0,1) and (2,3); never rewritten
-    for (int idx = tid; idx < 2 * 16 * 16; idx += 256) {
-        const int tsel = idx >> 8, e = idx & 255, rrow = e >> 4, ccol = e & 15;
-        const int off = (tsel ? 32 + rrow : rrow) * TP + (tsel ? 48 + ccol : 16 + ccol);
-        sPh[off] = from_f32<T>(0.f);
-        sPl[off] = from_f32<T>(0.f);
-    }
-
-    if (si.nchunks > 0) load(0);
-
-    for (int c = 0; c < si.nchunks; ++c) {
-        const int nv = min(kChunk, si.len - c * kChunk);
-        const int tokc = si.tok0 + c * kChunk;
-        __syncthreads();  // the previous chunk is done with every LDS tile
-
-        // ---- stage chunk c (rows past the chunk end become zero)
-        const u32x4 z4 = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int i = 0; i < St::QV; ++i) {
-            const int idx = tid + 256 * i, row = idx / VPR, cv = idx - row * VPR;
-            *reinterpret_cast<u32x4 *>(sQ + row * KP + cv * VEC) = row < nv ? rq[i] : z4;
-            *reinterpret_cast<u32x4 *>(sK + row * KP + cv * VEC) = row < nv ? rk[i] : z4;
-        }
-#pragma unroll
-        for (int i = 0; i < St::AV; ++i) {
-            const int idx = tid + 256 * i, row = idx / (64 / VEC), cv = idx - row * (64 / VEC);
-            *reinterpret_cast<u32x4 *>(sA + row * TP + cv * VEC) = ra[i];
-        }
-#pragma unroll
-        for (int i = 0; i < St::VV; ++i) {
-            const int idx = tid + 256 * i;
-            if (idx < 64 * VPV) reinterpret_cast<u32x4 *>(sV)[idx] = (idx / VPV) < nv ? rv[i] : z4;
-        }
-        const float gv = lane < nv ? rg : 0.f, bv = lane < nv ? rb : 0.f;
-        const float gl = wave_inclusive_scan(gv) * kLog2e;    // lane t: log2 gamma_t
-        const float glC = __shfl(gl, 63, 64);                  // tail tokens carry g = 0
+        const int nv = nvalid(c);
+        float *g3 = sG + B * GROWS;
         if (wave == 0) {
-            sGl[lane] = gl;
-            sB[lane] = bv;
-            sSc[lane] = exp2f(glC - gl);                       // gamma_C / gamma_t
+            const float gv = lane < nv ? rg : 0.f;                   // tail tokens carry g = 0
+            const float gl = wave_inclusive_scan(gv) * kLog2e;       // log2 gamma_t
+            const float glC = __shfl(gl, 63, 64);
+            const float gam = fast_exp2(gl);
+            g3[GL + lane] = gl;
+            g3[BETA + lane] = lane < nv ? to_f32(rb) : 0.f;
+            g3[SC + lane] = fast_exp2(glC - gl);                     // gamma_C / gamma_t
+            g3[GAM + lane] = gam;
+            g3[SGAM + lane] = p.scale * gam;
         }
-        load(min(c + 1, si.nchunks - 1));                      // overlaps with the compute below
-        __syncthreads();
-
-        // ---- P = scale * Lower(Gamma) (.) Q K^T, built as P^T tiles (rows of P land contiguous)
-        for (int t = wave; t < 10; t += 4) {
-            const int ti = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
-            const int tj = t - ti * (ti + 1) / 2;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        // vmcnt(0) (gfx9 encoding: vmcnt bits [3:0],[15:14] = 0; expcnt [6:4] and lgkmcnt [11:8]
+        // left at their maxima): this wave's direct-to-LDS loads of chunk c have landed
+        __builtin_amdgcn_s_waitcnt(0x0f70);
+        __syncthreads();  // tiles and gates of chunk c are visible
+        if constexpr (NBUF == 2) {
+            if (c + 1 < nch) issue_loads(c + 1, tnext);               // stream chunk c + 1 meanwhile
+        }
+        if (wave == 0) load_gates(min(c + 1, nch - 1));
+        const unsigned char *tK = tcur + L::K0, *tQ = tcur + L::Q0, *tA = tcur + L::A0, *tV = tcur + L::V0;
+        // =========================== phase 1 ===========================
+        Frag<T> Wh[2], Wl[2];          // chain: V'' (pi order over tokens)
+        if (chain) {
+            Frag<T> Sh[NKB], Sl[NKB];
 #pragma unroll
-            for (int kb = 0; kb < DK / 32; ++kb)
-                mma(acc, ld8(sK + (16 * tj + l16) * KP + 32 * kb + 8 * grp),
-                    ld8(sQ + (16 * ti + l16) * KP + 32 * kb + 8 * grp));
-            const int i = 16 * ti + l16;  // acc[r] = (Q K^T)[i][16 tj + 4 grp + r]
-            const float gli = sGl[i];
-            f32x4 pv;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int j = 16 * tj + 4 * grp + r;
-                pv[r] = (j <= i) ? p.scale * exp2f(gli - sGl[j]) * acc[r] : 0.f;
+            for (int kb = 0; kb < NKB; ++kb) {
+                float x[8];
+                pack_pi(S[2 * kb], S[2 * kb + 1], x);
+                split8(x, Sh[kb], Sl[kb]);
+                Frag<T> *dst = sSx + ((sub * NKB + kb) * L::NS) * 64 + lane;
+                dst[0] = Sh[kb];
+                if constexpr (L::NS == 2) dst[64] = Sl[kb];
             }
-            const int off = i * TP + 16 * tj + 4 * grp;
-            st4_split(sPh + off, sPl + off, pv);
-        }
-
-        // ---- K S and Q S for rows 16w .. 16w+15 (S carried as hi + lo)
-        f32x4 ks[NT], oacc[NT];
+            f32x4 ks[4];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            ks[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            oacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+            for (int m = 0; m < 4; ++m) {
+                ks[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < DK / 32; ++kb) {
-            const auto ak = ld8(sK + (16 * wave + l16) * KP + 32 * kb + 8 * grp);
-            const auto aq = ld8(sQ + (16 * wave + l16) * KP + 32 * kb + 8 * grp);
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const int off = (16 * nt + l16) * KP + 32 * kb + 8 * grp;
-                const auto bh = ld8(sSth + off);
-                mma(ks[nt], ak, bh);
-                mma(oacc[nt], aq, bh);
-                if constexpr (SPLIT) {
-                    const auto bl = ld8(sStl + off);
-                    mma(ks[nt], ak, bl);
-                    mma(oacc[nt], aq, bl);
-                }
+                for (int kb = 0; kb < NKB; ++kb) mma_x(ks[m], ldpi_tile<T, L::KGPR>(tK, 16 * m + l16, kb), Sh[kb], Sl[kb]);
             }
-        }
-        // ---- X = diag(beta)(V - diag(gamma) K S) -> X^T; O_inter = scale diag(gamma) Q S
+            f32x4 xx[4];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            f32x4 x;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * wave + 4 * grp + r;
-                const float gam = exp2f(sGl[i]);
-                x[r] = sB[i] * (to_f32(sV[i * BV + 16 * nt + l16]) - gam * ks[nt][r]);
-                oacc[nt][r] *= p.scale * gam;
-            }
-            const int off = (16 * nt + l16) * TP + 16 * wave + 4 * grp;
-            st4_split(sXth + off, sXtl + off, x);
-        }
-        __syncthreads();
-
-        // ---- V' = A X for rows 16w.. (A lower triangular: blocks past the diagonal skipped);
-        //      also V'' = diag(gamma_C / gamma) V' for the state update
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int kb = 0; kb <= (wave >> 1); ++kb) {
-                const auto a = ld8(sA + (16 * wave + l16) * TP + 32 * kb + 8 * grp);
-                const int off = (16 * nt + l16) * TP + 32 * kb + 8 * grp;
-                mma(acc, a, ld8(sXth + off));
-                if constexpr (SPLIT) mma(acc, a, ld8(sXtl + off));
-            }
-            const int off = (16 * nt + l16) * TP + 16 * wave + 4 * grp;
-            st4_split(sVph + off, sVpl + off, acc);
-            f32x4 accs;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) accs[r] = acc[r] * sSc[16 * wave + 4 * grp + r];
-            st4_split(sVqh + off, sVql + off, accs);
-        }
-        __syncthreads();
-
-        // ---- O = O_inter + P V' (rows 16w..), both factors carried as hi + lo
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            for (int kb = 0; kb <= (wave >> 1); ++kb) {
-                const int pa = (16 * wave + l16) * TP + 32 * kb + 8 * grp;
-                const int vo = (16 * nt + l16) * TP + 32 * kb + 8 * grp;
-                const auto ph = ld8(sPh + pa);
-                const auto vh = ld8(sVph + vo);
-                mma(oacc[nt], ph, vh);
-                if constexpr (SPLIT) {
-                    mma(oacc[nt], ph, ld8(sVpl + vo));
-                    mma(oacc[nt], ld8(sPl + pa), vh);
-                }
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * wave + 4 * grp + r;
-                if (i < nv) {
-                    const int64_t e = (int64_t)(tokc + i) * v_stride + o_off + 16 * nt + l16;
-                    if (p.o_f32) static_cast<float *>(p.o)[e] = oacc[nt][r];
-                    else static_cast<T *>(p.o)[e] = from_f32<T>(oacc[nt][r]);
-                }
-            }
-        }
-
-        // ---- S <- gamma_C S + K^T V''   (rows drow0 .. drow0 + DK/4; K columns read from the row tile)
-        const float gC = exp2f(glC);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            Frag<T> a[2];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) set_elem(a[kb], e, sK[(32 * kb + 8 * grp + e) * KP + drow0 + 16 * mt + l16]);
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                S[mt][nt] *= gC;
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const int vo = (16 * nt + l16) * TP + 32 * kb + 8 * grp;
-                    mma(S[mt][nt], a[kb], ld8(sVqh + vo));
-                    if constexpr (SPLIT) mma(S[mt][nt], a[kb], ld8(sVql + vo));
-                }
-                const int off = (16 * nt + l16) * KP + drow0 + 16 * mt + 4 * grp;
-                st4_split(sSth + off, sStl + off, S[mt][nt]);
-            }
-        }
-    }
-
-    if (p.final_state) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
+            for (int m = 0; m < 4; ++m)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int d = drow0 + 16 * mt + 4 * grp + r, col = c0 + 16 * nt + l16;
-                    p.final_state[(((int64_t)n * p.H_v + h) * DK + d) * DV + col] = S[mt][nt][r];
+                    const int i = 16 * m + 4 * grp + r;
+                    const float v = to_f32(*reinterpret_cast<const T *>(tV + tile_off<L::VGPR, ESZ>(i, 16 * sub + l16)));
+                    xx[m][r] = g3[BETA + i] * (v - g3[GAM + i] * ks[m][r]);
                 }
+            Frag<T> Xh[2], Xl[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                float x[8];
+                pack_pi(xx[2 * kb], xx[2 * kb + 1], x);
+                split8(x, Xh[kb], Xl[kb]);
+            }
+            f32x4 vp[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                vp[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb <= m / 2; ++kb) mma_x(vp[m], ldpi_tile<T, L::AGPR>(tA, 16 * m + l16, kb), Xh[kb], Xl[kb]);
+            }
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                float x[8];
+                pack_pi(vp[2 * kb], vp[2 * kb + 1], x);
+                Frag<T> vh, vl;
+                split8(x, vh, vl);
+                Frag<T> *dst = sVx + ((sub * 2 + kb) * L::NS) * 64 + lane;
+                dst[0] = vh;
+                if constexpr (L::NS == 2) dst[64] = vl;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int t = 32 * kb + (e < 4 ? 4 * grp + e : 16 + 4 * grp + e - 4);
+                    x[e] *= g3[SC + t];
+                }
+                split8(x, Wh[kb], Wl[kb]);
+            }
+        } else {
+            // P^T tiles: acc[r] = (Q K^T)[i = 16 ti + l16][j = 16 tj + 4 grp + r], grouped into the six
+            // pi-order fragments (ti, kb); the output waves share the work and the result through LDS.
+#pragma unroll
+            for (int f = 0; f < 6; ++f) {
+                constexpr int FTI[6] = {0, 1, 2, 2, 3, 3}, FKB[6] = {0, 0, 0, 1, 0, 1};
+                // balanced split of the ten tiles: owner of fragment f
+                constexpr int OWN2[6] = {1, 0, 0, 0, 1, 1};
+                const int owner = NSUB == 1 ? 0 : (NSUB == 2 ? OWN2[f] : f % NSUB);
+                if (sub != owner) continue;
+                const int ti = FTI[f], kb = FKB[f];
+                const float gli = g3[GL + 16 * ti + l16];
+                float x[8];
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const int tj = 2 * kb + half;
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                    if (tj <= ti) {
+#pragma unroll
+                        for (int kd = 0; kd < NKB; ++kd)
+                            mma(acc, ld8_tile<T, L::KGPR>(tK, 16 * tj + l16, 32 * kd + 8 * grp),
+                                ld8_tile<T, L::KGPR>(tQ, 16 * ti + l16, 32 * kd + 8 * grp));
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int j = 16 * tj + 4 * grp + r;
+                        const float v = p.scale * fast_exp2(gli - g3[GL + j]) * acc[r];
+                        x[4 * half + r] = tj < ti ? v : (tj == ti && 4 * grp + r <= l16) ? v : 0.f;
+                    }
+                }
+                Frag<T> ph, pl;
+                split8(x, ph, pl);
+                sPx[(f * L::NS) * 64 + lane] = ph;
+                if constexpr (L::NS == 2) sPx[(f * L::NS + 1) * 64 + lane] = pl;
+            }
+        }
+        lds_only_barrier();  // S_c and V' of chunk c are visible to the output waves
+
+        // =========================== phase 2 ===========================
+        if (chain) {
+            const float gC = g3[GAM + 63];
+#pragma unroll
+            for (int m = 0; m < MD; ++m) {
+                S[m] *= gC;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) mma_x(S[m], ldpi_col_tile<T, L::KGPR>(tK, 16 * m, kb), Wh[kb], Wl[kb]);
+            }
+        } else {
+            const Frag<T> *sxs = sSx + (sub * NKB * L::NS) * 64 + lane;
+            const Frag<T> *vxs = sVx + (sub * 2 * L::NS) * 64 + lane;
+            f32x4 o[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) o[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                Frag<T> sh = sxs[kb * L::NS * 64], sl;
+                if constexpr (L::NS == 2) sl = sxs[kb * L::NS * 64 + 64];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) mma_x(o[m], ldpi_tile<T, L::KGPR>(tQ, 16 * m + l16, kb), sh, sl);
+            }
+            Frag<T> Vh[2], Vl[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                Vh[kb] = vxs[kb * L::NS * 64];
+                if constexpr (L::NS == 2) Vl[kb] = vxs[kb * L::NS * 64 + 64];
+            }
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o[m][r] *= g3[SGAM + 16 * m + 4 * grp + r];
+#pragma unroll
+                for (int kb = 0; kb <= m / 2; ++kb) {
+                    const int f = m == 0 ? 0 : m == 1 ? 1 : m == 2 ? 2 + kb : 4 + kb;
+                    Frag<T> ph = sPx[(f * L::NS) * 64 + lane], pl;
+                    if constexpr (L::NS == 2) pl = sPx[(f * L::NS + 1) * 64 + lane];
+                    mma_xx(o[m], ph, pl, Vh[kb], Vl[kb]);
+                }
+            }
+            // buffer stores: the resource covers the chunk's valid rows only (rows past the end are
+            // dropped by the bounds check); row offsets are scalar, the lane offset is computed once
+            const int64_t ebase = (int64_t)(si.tok0 + c * kChunk) * v_stride + (int64_t)h * DV + c0;
+            const int oes = p.o_f32 ? 4 : ESZ;
+            const __amdgpu_buffer_rsrc_t ors = make_rsrc(static_cast<char *>(p.o) + ebase * oes,
+                                                         ((nv - 1) * vs + BV) * oes);
+            const int vlane = ((4 * grp) * vs + 16 * sub + l16) * oes;
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int soff = (16 * m + r) * vs * oes;
+                    if (p.o_f32) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o[m][r]), ors, vlane, soff, 0);
+                    else if constexpr (ESZ == 2)
+                        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (bf16)o[m][r]), ors, vlane, soff, 0);
+                    else __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o[m][r]), ors, vlane, soff, 0);
+                }
+        }
+    };
+
+    if (nch > 0) {
+        issue_loads(0, tiles0);
+        if (wave == 0) load_gates(0);
+    }
+    for (int c = 0; c < nch; c += 2) {
+        step.template operator()<0>(c);
+        if (c + 1 < nch) step.template operator()<NBUF == 2 ? 1 : 0>(c + 1);
+    }
+
+    if (chain && p.final_state) {
+#pragma unroll
+        for (int m = 0; m < MD; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                p.final_state[(((int64_t)n * p.H_v + h) * DK + 16 * m + 4 * grp + r) * DV + col] = S[m][r];
     }
 }
 
@@ -396,19 +491,20 @@ hipError_t launch_plan(const PlanParams &p, hipStream_t s) {
 hipError_t launch_chunk(int dtype, int D_k, int BV, const ChunkParams &p, hipStream_t s) {
     const int units = p.N * p.H_v;
     const unsigned groups = (unsigned)((units + 7) / 8);
-    const dim3 grid(groups * 8u * (unsigned)p.n_slices), block(256);
+    const dim3 grid(groups * 8u * (unsigned)p.n_slices);
     if (units == 0) return hipSuccess;
-#define GDN_CHUNK_CASE(DT, T_, DK_, BV_)                                                        \
-    if (dtype == DT && D_k == DK_ && BV == BV_) {                                               \
-        hipLaunchKernelGGL((chunk_kernel<T_, DK_, BV_>), grid, block, 0, s, p);                 \
-        return hipGetLastError();                                                               \
+#define GDN_CHUNK_CASE(DT, T_, DK_, NSUB_, NBUF_)                                                     \
+    if (dtype == DT && D_k == DK_ && BV == 16 * NSUB_) {                                              \
+        hipLaunchKernelGGL((chunk_kernel<T_, DK_, NSUB_, NBUF_>), grid, dim3(128 * NSUB_), 0, s, p);  \
+        return hipGetLastError();                                                                     \
     }
-    GDN_CHUNK_CASE(1, bf16, 128, 32)
-    GDN_CHUNK_CASE(1, bf16, 128, 16)
-    GDN_CHUNK_CASE(1, bf16, 64, 32)
-    GDN_CHUNK_CASE(1, bf16, 64, 16)
-    GDN_CHUNK_CASE(0, float, 128, 16)
-    GDN_CHUNK_CASE(0, float, 64, 16)
+    GDN_CHUNK_CASE(1, bf16, 128, 2, 2)
+    GDN_CHUNK_CASE(1, bf16, 128, 1, 2)
+    GDN_CHUNK_CASE(1, bf16, 64, 2, 2)
+    GDN_CHUNK_CASE(1, bf16, 64, 1, 2)
+    GDN_CHUNK_CASE(0, float, 128, 1, 1)
+    GDN_CHUNK_CASE(0, float, 64, 2, 2)
+    GDN_CHUNK_CASE(0, float, 64, 1, 2)
 #undef GDN_CHUNK_CASE
     return hipErrorInvalidValue;
 }

@@ -91,6 +91,124 @@ __device__ __forceinline__ void st4_split(float *hi, float *, const f32x4 &x) {
 __device__ __forceinline__ void set_elem(Frag<bf16> &f, int e, bf16 x) { f.v[e] = x; }
 __device__ __forceinline__ void set_elem(Frag<float> &f, int e, float x) { f.v[e] = x; }
 
+// ---- operands taken from accumulator registers ----------------------------------------------
+// A 32-wide contraction block made of two 16-row accumulator tiles C0 (rows 0..15) and C1
+// (rows 16..31) is, lane for lane, an operand fragment whose lane group grp holds contraction
+// indices {4grp..4grp+3} from C0 and {16+4grp..16+4grp+3} from C1 ("pi order").  The partner
+// operand is read from memory in the same pi order with ld_pi.
+
+// 2^x on the hardware transcendental unit (results below 2^-126 flush to zero, which the
+// decays here tolerate: such a factor multiplies a contribution that is already negligible).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// x -> hi (+ lo) fragments; fp32 keeps the value whole.  hi is x truncated to bf16 (its upper 16
+// bits), lo = bf16(x - hi) carries the next 8+ bits; together ~16 significant bits.
+__device__ __forceinline__ void split8(const float *x, Frag<bf16> &h, Frag<bf16> &l) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t bits = __float_as_uint(x[e]) & 0xffff0000u;
+        h.v[e] = __builtin_bit_cast(bf16, (unsigned short)(bits >> 16));
+        l.v[e] = (bf16)(x[e] - __uint_as_float(bits));
+    }
+}
+__device__ __forceinline__ void split8(const float *x, Frag<float> &h, Frag<float> &) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h.v[e] = x[e];
+}
+// Pack two accumulator tiles into the 8 pi-order values of this lane.
+__device__ __forceinline__ void pack_pi(const f32x4 &c0, const f32x4 &c1, float *x) {
+    x[0] = c0[0]; x[1] = c0[1]; x[2] = c0[2]; x[3] = c0[3];
+    x[4] = c1[0]; x[5] = c1[1]; x[6] = c1[2]; x[7] = c1[3];
+}
+
+// Row operand in pi order: elements [32kb + 4grp, +4) and [32kb + 16 + 4grp, +4) of `row`.
+__device__ __forceinline__ Frag<bf16> ld_pi(const bf16 *row, int kb) {
+    const int grp = (threadIdx.x & 63) >> 4;
+    const bf16x4 a = *reinterpret_cast<const bf16x4 *>(row + 32 * kb + 4 * grp);
+    const bf16x4 b = *reinterpret_cast<const bf16x4 *>(row + 32 * kb + 16 + 4 * grp);
+    Frag<bf16> f;
+    f.v = bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return f;
+}
+__device__ __forceinline__ Frag<float> ld_pi(const float *row, int kb) {
+    const int grp = (threadIdx.x & 63) >> 4;
+    const float4 a = *reinterpret_cast<const float4 *>(row + 32 * kb + 4 * grp);
+    const float4 b = *reinterpret_cast<const float4 *>(row + 32 * kb + 16 + 4 * grp);
+    Frag<float> f;
+    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+    return f;
+}
+// Column operand in pi order from a row-major tile: M[32kb + 4grp + r][col] and M[32kb+16+4grp+r][col].
+template <typename T>
+__device__ __forceinline__ Frag<T> ld_pi_col(const T *m, int ld, int col, int kb) {
+    const int grp = (threadIdx.x & 63) >> 4;
+    Frag<T> f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int t = 32 * kb + (e < 4 ? 4 * grp + e : 16 + 4 * grp + e - 4);
+        set_elem(f, e, m[t * ld + col]);
+    }
+    return f;
+}
+
+// acc += a * (bh + bl)            (one exact operand, one hi/lo pair)
+template <typename T>
+__device__ __forceinline__ void mma_x(f32x4 &acc, const Frag<T> &a, const Frag<T> &bh, const Frag<T> &bl) {
+    mma(acc, a, bh);
+    if constexpr (Split<T>::parts == 2) mma(acc, a, bl);
+}
+// acc += (ah + al) * (bh + bl)    (lo * lo dropped)
+template <typename T>
+__device__ __forceinline__ void mma_xx(f32x4 &acc, const Frag<T> &ah, const Frag<T> &al, const Frag<T> &bh,
+                                       const Frag<T> &bl) {
+    mma(acc, ah, bh);
+    if constexpr (Split<T>::parts == 2) {
+        mma(acc, ah, bl);
+        mma(acc, al, bh);
+    }
+}
+
+// ---- tiles loaded straight into LDS ----------------------------------------------------------
+// A tile of R rows of RB bytes is stored as 16-byte granules.  Granule (row, cv) sits at position
+// row * GPR + (cv ^ swz(row)) (GPR = RB / 16 granules per row).  The XOR spreads the 16 rows an
+// MFMA operand read touches over all 16 four-bank groups, so 16-byte row reads are conflict free.
+template <int GPR>
+__device__ __forceinline__ int tile_swz(int row) {
+    constexpr int DIV = GPR >= 16 ? 1 : 16 / GPR;
+    constexpr int MOD = GPR >= 16 ? 16 : GPR;
+    return (row / DIV) % MOD;
+}
+// Byte offset of element `col` of row `row` (elements of ESZ bytes).
+template <int GPR, int ESZ>
+__device__ __forceinline__ int tile_off(int row, int col) {
+    const int g = (col * ESZ) >> 4, within = (col * ESZ) & 15;
+    return (row * GPR + (g ^ tile_swz<GPR>(row))) * 16 + within;
+}
+typedef __attribute__((address_space(3))) void lds_void;
+// One wave instruction moves 64 granules of global memory into LDS positions lds + 16 * lane.
+__device__ __forceinline__ void load_granule_to_lds(const void *src, void *lds_base) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void *)lds_base, 16, 0, 0);
+}
+// Raw buffer resource over [base, base + bytes): out-of-range accesses are dropped (stores) or
+// read as zero (loads).  Word 3 is the gfx9 default descriptor format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
+}
+
+// Workgroup barrier that waits only for this wave's LDS operations (lgkmcnt), not for its
+// direct-to-LDS loads in flight into the other tile buffer: a fence would have to wait for those,
+// since they are LDS writes too.  The memory clobber keeps the compiler from moving memory
+// accesses across it.  Only for LDS data produced by ds_* instructions.
+__device__ __forceinline__ void lds_only_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Transposed LDS read (ds_read_b64_tr_b16): within each group of 16 lanes, lane j = 4e + q points at
+// 4 consecutive 16-bit elements M[t_e][d_q .. d_q + 3]; lane i = 4q + s then receives
+// M[t_0 .. t_3][d_q + s].  (Checked on gfx950 with an in-bounds probe.)
+__device__ __forceinline__ bf16x4 lds_read_tr16(const void *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4 *)(p));
+}
+
 // 16-byte vector of T: 8 bf16 or 4 fp32.
 template <typename T> struct Vec16 { static constexpr int N = 16 / sizeof(T); };
 
