@@ -34,6 +34,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen3next_bf16")
     ap.add_argument("--copies", type=int, default=3)
+    ap.add_argument("--cp", default="auto", choices=["auto", "off", "on"],
+                    help="in-GPU context parallelism (auto: on when too few (sequence, head) chains fill the chip)")
+    ap.add_argument("--cp-segment-chunks", type=int, default=0, help="CP segment length in chunks (0: automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: all host cores)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -139,7 +142,7 @@ def main():
     fs = torch.empty((x["n_seqs"],) + tuple(x["v"].shape[2:3]) + (x["q"].shape[3], x["v"].shape[3]),
                      dtype=torch.float32, device=dev)
     argv = [gdn.make_args(c["q"], c["k"], c["v"], c["g"], c["beta"], x["scale"], c["h0"], cu_dev, cu_host,
-                          64, o, fs) for c in copies]
+                          64, o, fs, a.cp, a.cp_segment_chunks) for c in copies]
     nbytes = gdn.workspace_bytes(argv[0])
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
@@ -197,7 +200,8 @@ def main():
         "vs_baseline": None, "dtype": {2: "bf16", 4: "f32"}[esz], "data": "synthetic",
         "config": {"workload": w.name, "B": w.B if not w.n_seqs else 1, "T_total": x["tokens"],
                    "seqs": x["n_seqs"], "H_qk": w.hqk, "H_v": w.H, "d_k": w.D, "d_v": w.D,
-                   "chunk": 64, "gate": w.gate, "h0": w.h0, "input_copies": len(copies)},
+                   "chunk": 64, "gate": w.gate, "h0": w.h0, "input_copies": len(copies),
+                   "cp": a.cp, "cp_ran": bool((ran[-1] >> gdn.STAGES.index("cp_pre")) & 1)},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(dominant, w.name)},
         "stage_ms": stage_ms,

@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <algorithm>
 #include <string>
 
 #include "../../include/gdn.h"
@@ -36,8 +37,27 @@ struct Plan {
     int64_t total_chunks = 0;
     int BV = 32;
     int n_slices = 0;
-    size_t off_A = 0, off_seq = 0, off_chunks = 0, off_order = 0, bytes = 0;
+    bool cp = false;          // in-GPU context parallelism
+    int seg_chunks = 0;       // segment length in chunks (one segment per sequence without CP)
+    int64_t total_segs = 0;
+    size_t off_A = 0, off_seq = 0, off_chunks = 0, off_segs = 0, off_order = 0;
+    size_t off_sstar = 0, off_m = 0, off_start = 0, bytes = 0;
 };
+
+constexpr int kNoSegments = 1 << 28;  // segment length meaning "the whole sequence"
+
+int64_t count_segments(const gdn_fwd_args *a, int sl) {
+    auto segs = [&](int64_t len) {
+        const int64_t nc = (len + gdn::kChunk - 1) / gdn::kChunk;
+        return std::max<int64_t>(1, (nc + sl - 1) / sl);
+    };
+    if (a->cu_seqlens_dev) {
+        int64_t t = 0;
+        for (int i = 0; i < a->N; ++i) t += segs(a->cu_seqlens_host[i + 1] - a->cu_seqlens_host[i]);
+        return t;
+    }
+    return (int64_t)a->B * segs(a->T);
+}
 
 int env_int(const char *name, int dflt) {
     const char *s = std::getenv(name);
@@ -101,12 +121,44 @@ gdn_status validate_and_plan(const gdn_fwd_args *a, Plan *pl) {
     pl->BV = (a->dtype == GDN_DTYPE_F32 && a->D_k == 128) ? 16 : (bv_env == 16 ? 16 : 32);
     pl->n_slices = a->D_v / pl->BV;
 
+    // ---- in-GPU context parallelism: split sequences into segments when too few
+    //      (sequence, head, slice) chains exist to fill the chip (FlashQLA page, auto-CP).
+    int64_t max_nc = 0;
+    if (packed) {
+        for (int i = 0; i < a->N; ++i)
+            max_nc = std::max<int64_t>(max_nc, (a->cu_seqlens_host[i + 1] - a->cu_seqlens_host[i] + 63) / 64);
+    } else {
+        max_nc = (a->T + 63) / 64;
+    }
+    const int64_t chains = (int64_t)a->N * a->H_v * pl->n_slices;
+    const int seg_env = env_int("GDN_CP_SEG", 0);
+    int sl = a->cp_segment_chunks > 0 ? a->cp_segment_chunks : seg_env;
+    if (sl <= 0) {
+        // enough segments for about two recurrence workgroups per CU, at least 4 chunks each
+        const int64_t want = std::max<int64_t>(1, (512 + chains - 1) / std::max<int64_t>(chains, 1));
+        sl = (int)std::max<int64_t>(4, (max_nc + want - 1) / want);
+    }
+    bool cp = false;
+    if (a->cp_mode == GDN_CP_ON) cp = true;
+    else if (a->cp_mode == GDN_CP_AUTO) cp = chains < 128 && max_nc >= 2 * (int64_t)sl;
+    pl->cp = cp;
+    pl->seg_chunks = cp ? sl : kNoSegments;
+    pl->total_segs = count_segments(a, pl->seg_chunks);
+    if (pl->total_segs * a->H_v > INT32_MAX / 64) return fail(GDN_ERR_UNSUPPORTED, "too many segments");
+
     const size_t esz = a->dtype == GDN_DTYPE_BF16 ? 2 : 4;
+    const size_t seg_heads = (size_t)pl->total_segs * a->H_v;
     size_t off = 0;
     pl->off_A = off;      off = align_up(off + (size_t)nch * a->H_v * 64 * 64 * esz);
     pl->off_seq = off;    off = align_up(off + (size_t)a->N * sizeof(gdn::SeqInfo));
     pl->off_chunks = off; off = align_up(off + (size_t)nch * sizeof(gdn::ChunkInfo));
-    pl->off_order = off;  off = align_up(off + (size_t)a->N * sizeof(int));
+    pl->off_segs = off;   off = align_up(off + (size_t)pl->total_segs * sizeof(gdn::SegInfo));
+    pl->off_order = off;  off = align_up(off + (size_t)pl->total_segs * sizeof(int));
+    if (cp) {
+        pl->off_sstar = off; off = align_up(off + seg_heads * a->D_k * a->D_v * sizeof(float));
+        pl->off_m = off;     off = align_up(off + seg_heads * a->D_k * a->D_k * sizeof(float));
+        pl->off_start = off; off = align_up(off + seg_heads * a->D_k * a->D_v * sizeof(float));
+    }
     pl->bytes = off;
     return GDN_OK;
 }
@@ -149,10 +201,12 @@ gdn_status run_fwd(const gdn_fwd_args *a, void *workspace, size_t workspace_byte
     const bool packed = a->cu_seqlens_dev != nullptr;
     gdn::SeqInfo *seq = packed ? reinterpret_cast<gdn::SeqInfo *>(ws + pl.off_seq) : nullptr;
     gdn::ChunkInfo *chunks = packed ? reinterpret_cast<gdn::ChunkInfo *>(ws + pl.off_chunks) : nullptr;
+    gdn::SegInfo *segs = packed ? reinterpret_cast<gdn::SegInfo *>(ws + pl.off_segs) : nullptr;
     int *order = packed ? reinterpret_cast<int *>(ws + pl.off_order) : nullptr;
 
     if (packed) {
-        gdn::PlanParams pp{a->cu_seqlens_dev, a->N, a->T, a->B * a->T, (int)pl.total_chunks, seq, chunks, order};
+        gdn::PlanParams pp{a->cu_seqlens_dev, a->N, a->T, a->B * a->T, (int)pl.total_chunks, pl.seg_chunks,
+                           (int)pl.total_segs, seq, chunks, segs, order};
         e = gdn::launch_plan(pp, s);
         if (e != hipSuccess) return done(fail(GDN_ERR_HIP, "plan launch: %s", hipGetErrorString(e)));
         if ((e = mark(GDN_STAGE_PLAN)) != hipSuccess) return done(fail(GDN_ERR_HIP, "event: %s", hipGetErrorString(e)));
@@ -163,9 +217,29 @@ gdn_status run_fwd(const gdn_fwd_args *a, void *workspace, size_t workspace_byte
     if (e != hipSuccess) return done(fail(GDN_ERR_HIP, "intra launch: %s", hipGetErrorString(e)));
     if ((e = mark(GDN_STAGE_INTRA)) != hipSuccess) return done(fail(GDN_ERR_HIP, "event: %s", hipGetErrorString(e)));
 
-    gdn::ChunkParams cp{a->q, a->k, a->v, a->g, a->beta, ws + pl.off_A, a->h0, a->o, a->final_state,
-                        seq, order, a->T, a->N, a->H_qk, a->H_v, a->D_v, pl.n_slices, a->scale,
-                        a->o_dtype == GDN_DTYPE_F32 ? 1 : 0};
+    gdn::ChunkParams cp{};
+    cp.q = a->q; cp.k = a->k; cp.v = a->v; cp.g = a->g; cp.beta = a->beta;
+    cp.A = ws + pl.off_A; cp.h0 = a->h0; cp.o = a->o; cp.final_state = a->final_state;
+    cp.seq = seq; cp.segs = segs; cp.order = order;
+    cp.T = a->T; cp.N = a->N; cp.H_qk = a->H_qk; cp.H_v = a->H_v; cp.D_v = a->D_v;
+    cp.seg_chunks = pl.seg_chunks; cp.total_segs = (int)pl.total_segs;
+    cp.scale = a->scale; cp.o_f32 = a->o_dtype == GDN_DTYPE_F32 ? 1 : 0;
+    if (pl.cp) {
+        cp.seg_sstar = reinterpret_cast<float *>(ws + pl.off_sstar);
+        cp.seg_m = reinterpret_cast<float *>(ws + pl.off_m);
+        cp.seg_start = reinterpret_cast<float *>(ws + pl.off_start);
+        gdn::ChunkParams pre = cp;
+        pre.n_slices = (a->D_v + a->D_k) / pl.BV;
+        e = gdn::launch_cp_pre(a->dtype, a->D_k, pl.BV, pre, s);
+        if (e != hipSuccess) return done(fail(GDN_ERR_HIP, "cp pre-process launch: %s", hipGetErrorString(e)));
+        if ((e = mark(GDN_STAGE_CP_PRE)) != hipSuccess) return done(fail(GDN_ERR_HIP, "event: %s", hipGetErrorString(e)));
+        gdn::FixParams fp{segs, seq, a->T, a->N, a->H_v, a->D_v, pl.seg_chunks, (int)pl.total_segs, a->h0, cp.seg_sstar, cp.seg_m,
+                          reinterpret_cast<float *>(ws + pl.off_start)};
+        e = gdn::launch_cp_fix(a->dtype, a->D_k, fp, s);
+        if (e != hipSuccess) return done(fail(GDN_ERR_HIP, "cp fix-up launch: %s", hipGetErrorString(e)));
+        if ((e = mark(GDN_STAGE_CP_FIX)) != hipSuccess) return done(fail(GDN_ERR_HIP, "event: %s", hipGetErrorString(e)));
+    }
+    cp.n_slices = pl.n_slices;
     e = gdn::launch_chunk(a->dtype, a->D_k, pl.BV, cp, s);
     if (e != hipSuccess) return done(fail(GDN_ERR_HIP, "chunk launch: %s", hipGetErrorString(e)));
     if ((e = mark(GDN_STAGE_CHUNK)) != hipSuccess) return done(fail(GDN_ERR_HIP, "event: %s", hipGetErrorString(e)));

@@ -24,15 +24,18 @@ namespace gdn {
 namespace {
 
 // ------------------------------------------------------------------------------------------
-// Plan: sequence table, chunk table and a longest-first order of the sequences.
+// Plan: sequence, chunk and segment tables, and a longest-first order of the segments.
 // One workgroup of 256 threads.
 // ------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void plan_kernel(PlanParams p) {
-    __shared__ int sScan[256];
+    __shared__ int sC[256], sS[256];
     const int tid = threadIdx.x;
-    // every chunk entry starts empty (nv = 0: the intra kernel then reads nothing)
+    // every chunk entry starts empty (nv = 0: the intra kernel then reads nothing), every segment
+    // entry empty and not last (it then writes no final state)
     for (int i = tid; i < p.total_chunks; i += 256) p.chunks[i] = ChunkInfo{0, 0};
-    int carry = 0;
+    for (int i = tid; i < p.total_segs; i += 256) p.segs[i] = SegInfo{0, 0, 0, 0, 0};
+    __syncthreads();
+    int carry_c = 0, carry_s = 0;
     for (int base = 0; base < p.N; base += 256) {
         const int n = base + tid;
         int tok0 = 0, len = 0;
@@ -44,22 +47,27 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanParams p) {
             tok0 = min(max(tok0, 0), p.total_tokens);
             len = min(max(len, 0), p.total_tokens - tok0);
         }
-        const int nc = (len + kChunk - 1) / kChunk;
-        sScan[tid] = nc;
+        const int nc = n < p.N ? ceil_div(len, kChunk) : 0;
+        const int ns = n < p.N ? max(1, ceil_div(nc, p.seg_chunks)) : 0;
+        sC[tid] = nc;
+        sS[tid] = ns;
         __syncthreads();
         for (int off = 1; off < 256; off <<= 1) {
-            const int y = tid >= off ? sScan[tid - off] : 0;
+            const int yc = tid >= off ? sC[tid - off] : 0, ys = tid >= off ? sS[tid - off] : 0;
             __syncthreads();
-            sScan[tid] += y;
+            sC[tid] += yc;
+            sS[tid] += ys;
             __syncthreads();
         }
         if (n < p.N) {
-            // never more chunks than the host sized the workspace and the intra grid for
-            const int chunk0 = min(carry + sScan[tid] - nc, p.total_chunks);
+            // never more chunks or segments than the host sized the workspace and grids for
+            const int chunk0 = min(carry_c + sC[tid] - nc, p.total_chunks);
             const int ncc = min(nc, p.total_chunks - chunk0);
-            p.seq[n] = SeqInfo{tok0, min(len, ncc * kChunk), chunk0, ncc};
+            const int seg0 = min(carry_s + sS[tid] - ns, p.total_segs);
+            p.seq[n] = SeqInfo{tok0, min(len, ncc * kChunk), chunk0, ncc, seg0};
         }
-        carry += sScan[255];
+        carry_c += sC[255];
+        carry_s += sS[255];
         __syncthreads();
     }
     __syncthreads();
@@ -69,20 +77,26 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanParams p) {
             const int rem = si.len - c * kChunk;
             p.chunks[si.chunk0 + c] = ChunkInfo{si.tok0 + c * kChunk, rem < kChunk ? rem : kChunk};
         }
+        const int ns = max(1, ceil_div(si.nchunks, p.seg_chunks));
+        for (int j = 0; j < ns && si.seg0 + j < p.total_segs; ++j) {
+            const int c0 = j * p.seg_chunks;
+            p.segs[si.seg0 + j] = SegInfo{n, j, c0, max(0, min(p.seg_chunks, si.nchunks - c0)), j == ns - 1 ? 1 : 0};
+        }
     }
-    // rank sort (longest first, ties by index); identity for the batched form and very many sequences
-    const bool sort = p.cu != nullptr && p.N <= 4096;
-    for (int n = tid; n < p.N; n += 256) {
-        int rank = n;
+    __syncthreads();
+    // rank sort of the segments (longest first, ties by index); identity past 1024 segments
+    const bool sort = p.total_segs <= 1024;
+    for (int g = tid; g < p.total_segs; g += 256) {
+        int rank = g;
         if (sort) {
-            const int len = p.seq[n].len;
+            const int len = p.segs[g].nchunks;
             rank = 0;
-            for (int m = 0; m < p.N; ++m) {
-                const int lm = p.seq[m].len;
-                rank += (lm > len) || (lm == len && m < n);
+            for (int m = 0; m < p.total_segs; ++m) {
+                const int lm = p.segs[m].nchunks;
+                rank += (lm > len) || (lm == len && m < g);
             }
         }
-        p.order[rank] = n;
+        p.order[rank] = g;
     }
 }
 
@@ -185,10 +199,16 @@ __device__ __forceinline__ Frag<T> ldpi_col_tile(const unsigned char *tile, int 
     return f;
 }
 
-template <typename T, int DK, int NSUB, int NBUF>
-__global__ __launch_bounds__(128 * NSUB) void chunk_kernel(ChunkParams p) {
+// MODE 0: main pass (chain + output waves) over one segment of a sequence, from h0 or from the
+//         segment's fixed-up start state; the last segment writes the final state.
+// MODE 1: context-parallel pre-process (chain waves only) over "virtual" columns: value columns
+//         (V as given, S = 0 at the segment start) give S*, identity columns (V = 0, S = I) give
+//         the segment's transition matrix M; both are written to the workspace.
+template <typename T, int DK, int NSUB, int NBUF, int MODE>
+__global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kernel(ChunkParams p) {
     using L = RecLds<T, DK, NSUB, NBUF>;
-    constexpr int NW = 2 * NSUB;                   // waves
+    constexpr bool OUT = MODE == 0;
+    constexpr int NW = OUT ? 2 * NSUB : NSUB;      // waves
     constexpr int BV = L::BV, NKB = L::NKB, ESZ = L::ESZ;
     constexpr int EPG = 16 / ESZ;                  // elements per granule
     constexpr int MD = DK / 16;                    // 16-row state tiles
@@ -199,9 +219,9 @@ __global__ __launch_bounds__(128 * NSUB) void chunk_kernel(ChunkParams p) {
     // would otherwise wait for the loads before every LDS access).
     __shared__ __attribute__((aligned(16))) unsigned char tiles0[L::TILES];
     __shared__ __attribute__((aligned(16))) unsigned char tiles1[NBUF == 2 ? L::TILES : 16];
-    __shared__ __attribute__((aligned(16))) Frag<T> sSx[L::SXN];
-    __shared__ __attribute__((aligned(16))) Frag<T> sVx[L::VXN];
-    __shared__ __attribute__((aligned(16))) Frag<T> sPx[L::PXN];
+    __shared__ __attribute__((aligned(16))) Frag<T> sSx[OUT ? L::SXN : 1];
+    __shared__ __attribute__((aligned(16))) Frag<T> sVx[OUT ? L::VXN : 1];
+    __shared__ __attribute__((aligned(16))) Frag<T> sPx[OUT ? L::PXN : 1];
     __shared__ float sG[2 * GROWS];
 
     // the wave index is uniform across a wave: readfirstlane makes the role branches scalar
@@ -210,39 +230,52 @@ __global__ __launch_bounds__(128 * NSUB) void chunk_kernel(ChunkParams p) {
     const bool chain = wave < NSUB;
     const int sub = chain ? wave : wave - NSUB;
 
-    // XCD-aware mapping: the slices of one (sequence, head) share blockIdx % 8, i.e. one XCD and
+    // XCD-aware mapping: the slices of one (segment, head) share blockIdx % 8, i.e. one XCD and
     // its L2, so Q/K/A fetched by one workgroup are L2 hits for the others.
     const int bid = blockIdx.x, xcd = bid & 7, rr = bid >> 3;
     const int slice = rr % p.n_slices, unit = (rr / p.n_slices) * 8 + xcd;
-    if (unit >= p.N * p.H_v) return;
-    const int n = p.seq ? p.order[unit / p.H_v] : unit / p.H_v, h = unit % p.H_v;
+    if (unit >= p.total_segs * p.H_v) return;
+    const int gsi = unit / p.H_v, h = unit % p.H_v;
+    const int gs = p.segs ? p.order[gsi] : gsi;
+    const SegInfo sg = seg_info(p.segs, gs, p.T, p.seg_chunks);
+    const int n = sg.n;
     const int hq = h / (p.H_v / p.H_qk);
     const SeqInfo si = seq_info(p.seq, n, p.T);
-    const int DV = p.D_v, c0 = slice * BV, col = c0 + 16 * sub + l16;  // this lane's value column
+    const int DV = p.D_v;
+    // pre-process: slices past the value columns are identity (M) columns
+    const bool mcols = !OUT && slice * BV >= DV;
+    if constexpr (!OUT) {
+        if (sg.last) return;                        // the last segment's maps are never needed
+        if (mcols && sg.j == 0 && !p.h0) return;    // M of the first segment multiplies h0 = 0
+    }
+    const int c0 = mcols ? slice * BV - DV : slice * BV;           // first column of this slice
+    const int col = c0 + 16 * sub + l16;                           // this lane's column
+    const int ccols = mcols ? DK : DV;                             // columns of the state matrix
 
     const T *qb = static_cast<const T *>(p.q) + (int64_t)hq * DK;
     const T *kb_ = static_cast<const T *>(p.k) + (int64_t)hq * DK;
-    const T *vb = static_cast<const T *>(p.v) + (int64_t)h * DV + c0;
+    const T *vb = static_cast<const T *>(p.v) + (int64_t)h * DV + (mcols ? 0 : c0);
     const float *gb = static_cast<const float *>(p.g) + h;
     const T *bb = static_cast<const T *>(p.beta) + h;
     const T *Ab = static_cast<const T *>(p.A) + (int64_t)h * 4096;
     const int64_t qk_stride = (int64_t)p.H_qk * DK, v_stride = (int64_t)p.H_v * DV;
     const int qks = (int)qk_stride, vs = (int)v_stride, hv = p.H_v;
-    const int nch = si.nchunks;
-    auto nvalid = [&](int c) { return min(kChunk, si.len - c * kChunk); };
+    const int nch = sg.nchunks;
+    // chunk c of the segment is chunk sg.c0 + c of the sequence
+    auto nvalid = [&](int c) { return min(kChunk, si.len - (sg.c0 + c) * kChunk); };
 
     // ---- direct-to-LDS loads of chunk c into a tile buffer; instruction i of a tile goes to wave i % NW
     auto issue_loads = [&](int c, unsigned char *tb) __attribute__((always_inline)) {
-        const int64_t tok = si.tok0 + c * kChunk;
+        const int64_t tok = si.tok0 + (int64_t)(sg.c0 + c) * kChunk;
         const int last = nvalid(c) - 1;
         const T *kc = kb_ + tok * qk_stride, *qc = qb + tok * qk_stride, *vc = vb + tok * v_stride;
-        const T *Ac = Ab + (int64_t)(si.chunk0 + c) * p.H_v * 4096;
+        const T *Ac = Ab + (int64_t)(si.chunk0 + sg.c0 + c) * p.H_v * 4096;
 #pragma unroll
         for (int i = wave; i < L::KGPR; i += NW) {         // 64 * KGPR granules = KGPR instructions
             const int pos = 64 * i + lane, row = pos / L::KGPR, g = pos % L::KGPR;
             const int cv = g ^ tile_swz<L::KGPR>(row), rowc = min(row, last);
             load_granule_to_lds(kc + rowc * qks + cv * EPG, tb + L::K0 + 1024 * i);
-            load_granule_to_lds(qc + rowc * qks + cv * EPG, tb + L::Q0 + 1024 * i);
+            if constexpr (OUT) load_granule_to_lds(qc + rowc * qks + cv * EPG, tb + L::Q0 + 1024 * i);
         }
 #pragma unroll
         for (int i = wave; i < L::AGPR; i += NW) {
@@ -250,29 +283,39 @@ __global__ __launch_bounds__(128 * NSUB) void chunk_kernel(ChunkParams p) {
             const int cv = g ^ tile_swz<L::AGPR>(row);
             load_granule_to_lds(Ac + row * 64 + cv * EPG, tb + L::A0 + 1024 * i);
         }
+        if (!mcols) {
 #pragma unroll
-        for (int i = wave; i < L::VGPR; i += NW) {
-            const int pos = 64 * i + lane, row = pos / L::VGPR, g = pos % L::VGPR;
-            const int cv = g ^ tile_swz<L::VGPR>(row), rowc = min(row, last);
-            load_granule_to_lds(vc + rowc * vs + cv * EPG, tb + L::V0 + 1024 * i);
+            for (int i = wave; i < L::VGPR; i += NW) {
+                const int pos = 64 * i + lane, row = pos / L::VGPR, g = pos % L::VGPR;
+                const int cv = g ^ tile_swz<L::VGPR>(row), rowc = min(row, last);
+                load_granule_to_lds(vc + rowc * vs + cv * EPG, tb + L::V0 + 1024 * i);
+            }
         }
     };
     float rg = 0.f;   // wave 0: gate and (raw) beta of token `lane` of the next chunk; converted
     T rb = T(0.f);    // only when used, so the loads are not waited for here
     auto load_gates = [&](int c) __attribute__((always_inline)) {
-        const int64_t tok = si.tok0 + c * kChunk;
+        const int64_t tok = si.tok0 + (int64_t)(sg.c0 + c) * kChunk;
         const int tl = min(lane, nvalid(c) - 1);
         rg = (gb + tok * hv)[tl * hv];
         rb = (bb + tok * hv)[tl * hv];
     };
 
     // ---- chain state: S [DK][16] of this slice in fp32 accumulator tiles (rows 16m + 4grp + r)
+    //      main pass: h0 (first segment) or the fixed-up start state; pre-process: 0 or identity
     f32x4 S[MD];
+    const float *s_init = nullptr;
+    if constexpr (OUT) {
+        s_init = sg.j == 0 ? (p.h0 ? p.h0 + ((int64_t)n * p.H_v + h) * DK * DV : nullptr)
+                           : p.seg_start + ((int64_t)gs * p.H_v + h) * DK * DV;
+    }
 #pragma unroll
     for (int m = 0; m < MD; ++m)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            S[m][r] = (chain && p.h0) ? p.h0[(((int64_t)n * p.H_v + h) * DK + 16 * m + 4 * grp + r) * DV + col] : 0.f;
+        for (int r = 0; r < 4; ++r) {
+            const int d = 16 * m + 4 * grp + r;
+            S[m][r] = (chain && s_init) ? s_init[d * DV + col] : (mcols && d == col) ? 1.f : 0.f;
+        }
 
     // ---- one chunk; B = tile buffer holding it (compile time)
     auto step = [&]<int B>(int c) __attribute__((always_inline)) {
@@ -315,9 +358,11 @@ __global__ __launch_bounds__(128 * NSUB) void chunk_kernel(ChunkParams p) {
                 float x[8];
                 pack_pi(S[2 * kb], S[2 * kb + 1], x);
                 split8(x, Sh[kb], Sl[kb]);
-                Frag<T> *dst = sSx + ((sub * NKB + kb) * L::NS) * 64 + lane;
-                dst[0] = Sh[kb];
-                if constexpr (L::NS == 2) dst[64] = Sl[kb];
+                if constexpr (OUT) {
+                    Frag<T> *dst = sSx + ((sub * NKB + kb) * L::NS) * 64 + lane;
+                    dst[0] = Sh[kb];
+                    if constexpr (L::NS == 2) dst[64] = Sl[kb];
+                }
             }
             f32x4 ks[4];
 #pragma unroll
@@ -332,7 +377,7 @@ __global__ __launch_bounds__(128 * NSUB) void chunk_kernel(ChunkParams p) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = 16 * m + 4 * grp + r;
-                    const float v = to_f32(*reinterpret_cast<const T *>(tV + tile_off<L::VGPR, ESZ>(i, 16 * sub + l16)));
+                    const float v = mcols ? 0.f : to_f32(*reinterpret_cast<const T *>(tV + tile_off<L::VGPR, ESZ>(i, 16 * sub + l16)));
                     xx[m][r] = g3[BETA + i] * (v - g3[GAM + i] * ks[m][r]);
                 }
             Frag<T> Xh[2], Xl[2];
@@ -355,9 +400,11 @@ __global__ __launch_bounds__(128 * NSUB) void chunk_kernel(ChunkParams p) {
                 pack_pi(vp[2 * kb], vp[2 * kb + 1], x);
                 Frag<T> vh, vl;
                 split8(x, vh, vl);
-                Frag<T> *dst = sVx + ((sub * 2 + kb) * L::NS) * 64 + lane;
-                dst[0] = vh;
-                if constexpr (L::NS == 2) dst[64] = vl;
+                if constexpr (OUT) {
+                    Frag<T> *dst = sVx + ((sub * 2 + kb) * L::NS) * 64 + lane;
+                    dst[0] = vh;
+                    if constexpr (L::NS == 2) dst[64] = vl;
+                }
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int t = 32 * kb + (e < 4 ? 4 * grp + e : 16 + 4 * grp + e - 4);
@@ -365,7 +412,7 @@ __global__ __launch_bounds__(128 * NSUB) void chunk_kernel(ChunkParams p) {
                 }
                 split8(x, Wh[kb], Wl[kb]);
             }
-        } else {
+        } else if constexpr (OUT) {
             // P^T tiles: acc[r] = (Q K^T)[i = 16 ti + l16][j = 16 tj + 4 grp + r], grouped into the six
             // pi-order fragments (ti, kb); the output waves share the work and the result through LDS.
 #pragma unroll
@@ -401,7 +448,7 @@ __global__ __launch_bounds__(128 * NSUB) void chunk_kernel(ChunkParams p) {
                 if constexpr (L::NS == 2) sPx[(f * L::NS + 1) * 64 + lane] = pl;
             }
         }
-        lds_only_barrier();  // S_c and V' of chunk c are visible to the output waves
+        if constexpr (OUT) lds_only_barrier();  // S_c and V' of chunk c are visible to the output waves
 
         // =========================== phase 2 ===========================
         if (chain) {
@@ -412,7 +459,7 @@ __global__ __launch_bounds__(128 * NSUB) void chunk_kernel(ChunkParams p) {
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) mma_x(S[m], ldpi_col_tile<T, L::KGPR>(tK, 16 * m, kb), Wh[kb], Wl[kb]);
             }
-        } else {
+        } else if constexpr (OUT) {
             const Frag<T> *sxs = sSx + (sub * NKB * L::NS) * 64 + lane;
             const Frag<T> *vxs = sVx + (sub * 2 * L::NS) * 64 + lane;
             f32x4 o[4];
@@ -445,7 +492,7 @@ __global__ __launch_bounds__(128 * NSUB) void chunk_kernel(ChunkParams p) {
             }
             // buffer stores: the resource covers the chunk's valid rows only (rows past the end are
             // dropped by the bounds check); row offsets are scalar, the lane offset is computed once
-            const int64_t ebase = (int64_t)(si.tok0 + c * kChunk) * v_stride + (int64_t)h * DV + c0;
+            const int64_t ebase = (int64_t)(si.tok0 + (sg.c0 + c) * kChunk) * v_stride + (int64_t)h * DV + c0;
             const int oes = p.o_f32 ? 4 : ESZ;
             const __amdgpu_buffer_rsrc_t ors = make_rsrc(static_cast<char *>(p.o) + ebase * oes,
                                                          ((nv - 1) * vs + BV) * oes);
@@ -472,12 +519,126 @@ __global__ __launch_bounds__(128 * NSUB) void chunk_kernel(ChunkParams p) {
         if (c + 1 < nch) step.template operator()<NBUF == 2 ? 1 : 0>(c + 1);
     }
 
-    if (chain && p.final_state) {
+    // ---- end of the segment: final state (main pass, last segment) or the segment's maps
+    float *s_end = nullptr;
+    if constexpr (OUT) {
+        if (sg.last && p.final_state) s_end = p.final_state + ((int64_t)n * p.H_v + h) * DK * DV;
+    } else {
+        s_end = (mcols ? p.seg_m : p.seg_sstar) + ((int64_t)gs * p.H_v + h) * DK * ccols;
+    }
+    if (chain && s_end) {
 #pragma unroll
         for (int m = 0; m < MD; ++m)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                p.final_state[(((int64_t)n * p.H_v + h) * DK + 16 * m + 4 * grp + r) * DV + col] = S[m][r];
+            for (int r = 0; r < 4; ++r) s_end[(16 * m + 4 * grp + r) * ccols + col] = S[m][r];
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Context-parallel fix-up (FlashQLA page, the S_{j,0} update of the CP pre-process): per
+// (sequence, value head, 16 value columns), serially over the sequence's segments,
+//   S_start(0) = h0 (or 0),   S_start(j + 1) = S*_j + M_j S_start(j),
+// writing S_start(j) for j >= 1.  Four waves each produce DK/64 16-row tiles of the product; the
+// new state goes through LDS to become the next step's operand.  M is prefetched one segment
+// ahead into registers and staged in LDS (hi + lo bf16 pairs, or fp32).
+// ------------------------------------------------------------------------------------------
+template <typename T, int DK>
+__global__ __launch_bounds__(256) void cp_fix_kernel(FixParams p) {
+    constexpr int NS = Split<T>::parts, MP = DK + 16 / (int)sizeof(T);  // padded row of M
+    constexpr int MT = DK / 64;                    // 16-row output tiles per wave
+    constexpr int NV = DK * DK / 4 / 256;          // float4 of M per thread
+    __shared__ __attribute__((aligned(16))) T sM[NS][DK * MP];
+    __shared__ __attribute__((aligned(16))) float sS[DK * 17];  // S_start [DK][16], padded
+    const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nsl = p.D_v / 16;
+    const int unit = blockIdx.x / nsl, slice = blockIdx.x - unit * nsl;
+    if (unit >= p.N * p.H_v) return;
+    const int n = unit / p.H_v, h = unit - n * p.H_v;
+    const SeqInfo si = seq_info(p.seq, n, p.T);
+    const int gs0 = p.seq ? si.seg0 : n * max(1, ceil_div(si.nchunks, p.seg_chunks));
+    // segments of this sequence (bounded by the planned count, so every index below is in range)
+    const int ns = min(max(1, ceil_div(si.nchunks, p.seg_chunks)), p.total_segs - gs0);
+    if (ns < 2) return;
+    const int c0 = slice * 16, DV = p.D_v;
+    const int64_t hstride = (int64_t)DK * DV;
+
+    // S_start(0): h0 or zero
+    for (int i = tid; i < DK * 16; i += 256) {
+        const int d = i >> 4, c = i & 15;
+        sS[d * 17 + c] = p.h0 ? p.h0[((int64_t)n * p.H_v + h) * hstride + d * DV + c0 + c] : 0.f;
+    }
+    float4 mreg[NV];
+    auto load_m = [&](int j) __attribute__((always_inline)) {
+        const float4 *src = reinterpret_cast<const float4 *>(p.seg_m + ((int64_t)(gs0 + j) * p.H_v + h) * DK * DK);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) mreg[i] = src[tid + 256 * i];
+    };
+    load_m(0);
+    for (int j = 0; j + 1 < ns; ++j) {
+        __syncthreads();  // the previous step is done with sM and sS
+        // stage M_j
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int e = 4 * (tid + 256 * i), row = e / DK, cc = e - row * DK;
+            const float x[4] = {mreg[i].x, mreg[i].y, mreg[i].z, mreg[i].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if constexpr (NS == 2) {
+                    const bf16 hi = (bf16)x[q];
+                    sM[0][row * MP + cc + q] = hi;
+                    sM[1][row * MP + cc + q] = (bf16)(x[q] - (float)hi);
+                } else {
+                    sM[0][row * MP + cc + q] = from_f32<T>(x[q]);
+                }
+            }
+        }
+        if (j + 2 < ns) load_m(j + 1);
+        __syncthreads();
+        // B operand: S_start(j) in pi order over d, as hi/lo fragments
+        Frag<T> Bh[DK / 32], Bl[DK / 32];
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb) {
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int d = 32 * kb + (e < 4 ? 4 * grp + e : 16 + 4 * grp + e - 4);
+                x[e] = sS[d * 17 + l16];
+            }
+            split8(x, Bh[kb], Bl[kb]);
+        }
+        // this wave's output tiles: rows 16 (wave * MT + t) ..
+        f32x4 acc[MT];
+        const float *sst = p.seg_sstar + ((int64_t)(gs0 + j) * p.H_v + h) * hstride;
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            const int m = wave * MT + t;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[t][r] = sst[(16 * m + 4 * grp + r) * DV + c0 + l16];
+            if (j == 0 && !p.h0) continue;  // S_start(0) = 0 (M_0 was not computed)
+#pragma unroll
+            for (int kb = 0; kb < DK / 32; ++kb) {
+                const Frag<T> ah = ld_pi(&sM[0][(16 * m + l16) * MP], kb);
+                if constexpr (NS == 2) {
+                    const Frag<T> al = ld_pi(&sM[1][(16 * m + l16) * MP], kb);
+                    mma_xx(acc[t], ah, al, Bh[kb], Bl[kb]);
+                } else {
+                    mma(acc[t], ah, Bh[kb]);
+                }
+            }
+        }
+        __syncthreads();  // every wave has read S_start(j)
+        float *dst = const_cast<float *>(p.seg_start) + ((int64_t)(gs0 + j + 1) * p.H_v + h) * hstride;
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            const int m = wave * MT + t;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int d = 16 * m + 4 * grp + r;
+                sS[d * 17 + l16] = acc[t][r];
+                dst[d * DV + c0 + l16] = acc[t][r];
+            }
+        }
     }
 }
 
@@ -488,15 +649,17 @@ hipError_t launch_plan(const PlanParams &p, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_chunk(int dtype, int D_k, int BV, const ChunkParams &p, hipStream_t s) {
-    const int units = p.N * p.H_v;
+template <int MODE>
+static hipError_t launch_rec(int dtype, int D_k, int BV, const ChunkParams &p, hipStream_t s) {
+    const int units = p.total_segs * p.H_v;
     const unsigned groups = (unsigned)((units + 7) / 8);
     const dim3 grid(groups * 8u * (unsigned)p.n_slices);
     if (units == 0) return hipSuccess;
-#define GDN_CHUNK_CASE(DT, T_, DK_, NSUB_, NBUF_)                                                     \
-    if (dtype == DT && D_k == DK_ && BV == 16 * NSUB_) {                                              \
-        hipLaunchKernelGGL((chunk_kernel<T_, DK_, NSUB_, NBUF_>), grid, dim3(128 * NSUB_), 0, s, p);  \
-        return hipGetLastError();                                                                     \
+#define GDN_CHUNK_CASE(DT, T_, DK_, NSUB_, NBUF_)                                                         \
+    if (dtype == DT && D_k == DK_ && BV == 16 * NSUB_) {                                                  \
+        hipLaunchKernelGGL((chunk_kernel<T_, DK_, NSUB_, NBUF_, MODE>), grid, dim3((MODE == 0 ? 128 : 64) * NSUB_), \
+                           0, s, p);                                                                      \
+        return hipGetLastError();                                                                         \
     }
     GDN_CHUNK_CASE(1, bf16, 128, 2, 2)
     GDN_CHUNK_CASE(1, bf16, 128, 1, 2)
@@ -507,6 +670,23 @@ hipError_t launch_chunk(int dtype, int D_k, int BV, const ChunkParams &p, hipStr
     GDN_CHUNK_CASE(0, float, 64, 1, 2)
 #undef GDN_CHUNK_CASE
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_chunk(int dtype, int D_k, int BV, const ChunkParams &p, hipStream_t s) {
+    return launch_rec<0>(dtype, D_k, BV, p, s);
+}
+hipError_t launch_cp_pre(int dtype, int D_k, int BV, const ChunkParams &p, hipStream_t s) {
+    return launch_rec<1>(dtype, D_k, BV, p, s);
+}
+hipError_t launch_cp_fix(int dtype, int D_k, const FixParams &p, hipStream_t s) {
+    const dim3 grid((unsigned)(p.N * p.H_v * (p.D_v / 16))), block(256);
+    if (p.N * p.H_v == 0) return hipSuccess;
+    if (dtype == 1 && D_k == 128) hipLaunchKernelGGL((cp_fix_kernel<bf16, 128>), grid, block, 0, s, p);
+    else if (dtype == 1 && D_k == 64) hipLaunchKernelGGL((cp_fix_kernel<bf16, 64>), grid, block, 0, s, p);
+    else if (dtype == 0 && D_k == 128) hipLaunchKernelGGL((cp_fix_kernel<float, 128>), grid, block, 0, s, p);
+    else if (dtype == 0 && D_k == 64) hipLaunchKernelGGL((cp_fix_kernel<float, 64>), grid, block, 0, s, p);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
 }
 
 }  // namespace gdn

@@ -14,10 +14,18 @@ struct SeqInfo {            // one per sequence
     int len;                // tokens
     int chunk0;             // global index of its first chunk
     int nchunks;            // ceil(len / 64)
+    int seg0;               // global index of its first segment
 };
 struct ChunkInfo {          // one per global chunk
     int tok0;               // first token of the chunk
     int nv;                 // valid tokens (1..64)
+};
+struct SegInfo {            // one per (sequence, segment of at most seg_chunks chunks)
+    int n;                  // sequence
+    int j;                  // segment index within the sequence
+    int c0;                 // first chunk of the segment within the sequence
+    int nchunks;            // chunks in the segment (0 only for an empty sequence)
+    int last;               // 1 for the last segment of its sequence
 };
 
 struct PlanParams {
@@ -25,16 +33,29 @@ struct PlanParams {
     int N, T;
     int total_tokens;       // B * T: sequence spans are clamped to [0, total_tokens)
     int total_chunks;       // chunk count the host planned from its copy of cu_seqlens
+    int seg_chunks;         // segment length in chunks
+    int total_segs;         // segment count the host planned
     SeqInfo *seq;           // [N]
     ChunkInfo *chunks;      // [total chunks]
-    int *order;             // [N] sequences, longest first (ties by index)
+    SegInfo *segs;          // [total segments]
+    int *order;             // [total segments] longest first (ties by index)
 };
+
+__device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Batched input: segment gs of sequences with nc chunks each, segments of sl chunks.
+__device__ __forceinline__ SegInfo seg_info(const SegInfo *segs, int gs, int T, int sl) {
+    if (segs) return segs[gs];
+    const int nc = ceil_div(T, kChunk), ns = max(1, ceil_div(nc, sl));
+    const int n = gs / ns, j = gs - n * ns, c0 = j * sl;
+    return SegInfo{n, j, c0, min(sl, nc - c0), j == ns - 1 ? 1 : 0};
+}
 
 // Batched (not packed) input has no tables: sequence n covers tokens [n T, n T + T).
 __device__ __forceinline__ SeqInfo seq_info(const SeqInfo *seq, int n, int T) {
     if (seq) return seq[n];
     const int nc = (T + kChunk - 1) / kChunk;
-    return SeqInfo{n * T, T, n * nc, nc};
+    return SeqInfo{n * T, T, n * nc, nc, 0};
 }
 __device__ __forceinline__ ChunkInfo chunk_info(const ChunkInfo *chunks, int ci, int T) {
     if (chunks) return chunks[ci];
@@ -57,15 +78,33 @@ struct ChunkParams {
     void *o;
     float *final_state;     // nullable
     const SeqInfo *seq;     // nullptr: batched input of T tokens per sequence (order = identity)
-    const int *order;
+    const SegInfo *segs;    // nullptr: batched input, segments derived from T and seg_chunks
+    const int *order;       // segment order (packed input)
     int T;
     int N, H_qk, H_v, D_v, n_slices;
+    int seg_chunks, total_segs;
     float scale;
     int o_f32;              // 1: o is fp32 (the unrounded result), 0: o has the input dtype
+    // context parallelism (workspace, fp32, [total_segs][H_v][D_k][cols]):
+    float *seg_sstar;       // pre-process output: S* of the segment (cols = D_v)
+    float *seg_m;           // pre-process output: transition M of the segment (cols = D_k)
+    const float *seg_start; // main pass input for segments j >= 1 (cols = D_v)
+};
+
+struct FixParams {
+    const SegInfo *segs;
+    const SeqInfo *seq;
+    int T, N, H_v, D_v, seg_chunks, total_segs;
+    const float *h0;        // nullable
+    const float *seg_sstar, *seg_m;
+    float *seg_start;
 };
 
 hipError_t launch_plan(const PlanParams &p, hipStream_t s);
 hipError_t launch_intra(int dtype, int D_k, const IntraParams &p, hipStream_t s);
 hipError_t launch_chunk(int dtype, int D_k, int BV, const ChunkParams &p, hipStream_t s);
+// mode 1: context-parallel pre-process (chain only over value and identity columns)
+hipError_t launch_cp_pre(int dtype, int D_k, int BV, const ChunkParams &p, hipStream_t s);
+hipError_t launch_cp_fix(int dtype, int D_k, const FixParams &p, hipStream_t s);
 
 }  // namespace gdn

@@ -129,3 +129,17 @@ def test_workspace_size_and_checks():
     p, keep = _packed([0, 1, 65, 130])
     assert gdn.workspace_bytes(p) >= 4 * 8 * 64 * 64 * 2
     assert gdn.workspace_bytes(p) < 4 * 8 * 64 * 64 * 2 + 4096
+
+
+def test_workspace_with_context_parallelism():
+    # CP on with 2-chunk segments: 5 chunks per sequence -> 3 segments each, 6 in all; per segment
+    # and head the workspace holds S* [128][128], M [128][128] and the start state [128][128] in fp32
+    base = gdn.workspace_bytes(_args(cp_mode=gdn.CP_MODES["off"]))
+    on = gdn.workspace_bytes(_args(cp_mode=gdn.CP_MODES["on"], cp_segment_chunks=2))
+    maps = 6 * 8 * 3 * 128 * 128 * 4
+    assert maps <= on - base < maps + 4096
+    # automatic choice: B*H_v = 4 with 1024 chunks splits the sequence; B*H_v = 64 does not
+    long = gdn.workspace_bytes(_args(B=1, N=1, T=65536, H_qk=4, H_v=4))
+    assert long > 1024 * 4 * 64 * 64 * 2 + 4 * 3 * 128 * 128 * 4
+    wide = gdn.workspace_bytes(_args(B=4, N=4, T=4096, H_qk=16, H_v=16))
+    assert wide < 4 * 64 * 16 * 64 * 64 * 2 + 4096

@@ -71,7 +71,7 @@ def test_qwen3next_workload_sampled():
 
 def test_longctx_workload_sampled():
     x = _w("longctx_bf16")
-    check(x, TOL["bf16"], heads=[0, 3], label="longctx_bf16 (sampled)")
+    check(x, TOL["bf16"], heads=[0, 3], label="longctx_bf16 serial (sampled)", cp_mode="off")
 
 
 def test_varlen_workload_sampled():
@@ -79,6 +79,56 @@ def test_varlen_workload_sampled():
     lens = np.diff(x["cu_seqlens"].numpy())
     seqs = [int(np.argmax(lens)), int(np.argmin(lens)), 5]
     check(x, TOL["bf16"], heads=[0, 9], seqs=seqs, label="varlen_bf16 (sampled)")
+
+
+# --------------------------------------------------------------------------- context parallelism
+# Sequences split into segments of L chunks: per-segment S* and M, serial fix-up of the segment
+# start states, then the main pass per segment (FlashQLA page, the CP pre-process).
+@pytest.mark.parametrize("L", [1, 2, 3, 7])
+def test_cp_bf16_segment_lengths(L):
+    x = _w("qwen3next_bf16", B=2, H=2, T=64 * 20 + 17, h0=True, seed=40 + L)
+    check(x, TOL["bf16"], label=f"bf16 CP L={L}", cp_mode="on", cp_segment_chunks=L)
+
+
+@pytest.mark.parametrize("L", [1, 3])
+def test_cp_without_initial_state(L):
+    # the first segment's M is never formed without h0: the fix-up must not use it
+    x = _w("qwen3next_bf16", B=1, H=2, T=64 * 9, mu=-7.0, seed=50 + L)
+    check(x, TOL["bf16"], label=f"bf16 CP no h0 L={L}", cp_mode="on", cp_segment_chunks=L)
+
+
+@pytest.mark.parametrize("L", [1, 4])
+def test_cp_fp32(L):
+    x = _w("tiny_fp32", B=2, T=64 * 11 + 5, h0=True, mu=-7.0, seed=60 + L)
+    check(x, TOL["fp32"], label=f"fp32 CP L={L}", cp_mode="on", cp_segment_chunks=L)
+    x = _w("tiny_fp32", T=64 * 6 + 40, H=4, H_qk=2, D=128, h0=True, seed=70 + L)
+    check(x, TOL["fp32"], label=f"fp32 D=128 CP L={L}", cp_mode="on", cp_segment_chunks=L)
+
+
+def test_cp_packed_ragged():
+    x = _w("varlen_bf16", n_seqs=8, lens=(0, 1, 63, 64, 65, 1000, 129, 700), H=3, h0=True, seed=80)
+    check(x, TOL["bf16"], label="bf16 packed CP L=2", cp_mode="on", cp_segment_chunks=2)
+
+
+def test_cp_bf16_head_dim_64():
+    x = _w("qwen3next_bf16", B=1, H=4, H_qk=1, D=64, T=900, h0=True, seed=90)
+    check(x, TOL["bf16"], label="bf16 D=64 CP L=3", cp_mode="on", cp_segment_chunks=3)
+
+
+def test_cp_matches_serial_pass():
+    # the two schedules compute the same quantities; they differ only by rounding order
+    x = _w("qwen3next_bf16", B=1, H=2, T=64 * 40, h0=True, mu=-7.0, seed=91)
+    o1, f1 = gpu_run(x, cp_mode="off", out_dtype=torch.float32)
+    o2, f2 = gpu_run(x, cp_mode="on", cp_segment_chunks=5, out_dtype=torch.float32)
+    rms_o, rms_f = o1.double().pow(2).mean().sqrt(), f1.double().pow(2).mean().sqrt()
+    assert (o1 - o2).abs().max() <= 1e-2 * rms_o
+    assert (f1 - f2).abs().max() <= 1e-2 * rms_f
+
+
+def test_longctx_workload_cp_auto_sampled():
+    # B*H = 4: the automatic choice splits the sequence into segments
+    x = _w("longctx_bf16")
+    check(x, TOL["bf16"], heads=[1, 2], label="longctx_bf16 CP auto (sampled)", cp_mode="auto")
 
 
 # --------------------------------------------------------------------------- properties
