@@ -41,7 +41,9 @@ struct Plan {
     int seg_chunks = 0;       // segment length in chunks (one segment per sequence without CP)
     int64_t total_segs = 0;
     size_t off_A = 0, off_seq = 0, off_chunks = 0, off_segs = 0, off_order = 0;
-    size_t off_sstar = 0, off_m = 0, off_start = 0, bytes = 0;
+    size_t off_sstar = 0, off_m = 0, off_start = 0;
+    size_t off_P = 0, off_kg = 0, off_kd = 0, off_qg = 0, off_dec = 0;  // per-channel gates
+    size_t bytes = 0;
 };
 
 constexpr int kNoSegments = 1 << 28;  // segment length meaning "the whole sequence"
@@ -80,7 +82,6 @@ gdn_status validate_and_plan(const gdn_fwd_args *a, Plan *pl) {
     if (a->dtype != GDN_DTYPE_F32 && a->dtype != GDN_DTYPE_BF16) return fail(GDN_ERR_INVALID_ARG, "bad dtype %d", a->dtype);
     if (a->gate_kind != GDN_GATE_SCALAR && a->gate_kind != GDN_GATE_CHANNEL)
         return fail(GDN_ERR_INVALID_ARG, "bad gate_kind %d", a->gate_kind);
-    if (a->gate_kind == GDN_GATE_CHANNEL) return fail(GDN_ERR_UNSUPPORTED, "per-channel gates are not built yet");
     if (!std::isfinite(a->scale)) return fail(GDN_ERR_INVALID_ARG, "scale is not finite");
     if (a->o_dtype != a->dtype && a->o_dtype != GDN_DTYPE_F32)
         return fail(GDN_ERR_INVALID_ARG, "o_dtype %d must equal dtype %d or be fp32", a->o_dtype, a->dtype);
@@ -118,7 +119,9 @@ gdn_status validate_and_plan(const gdn_fwd_args *a, Plan *pl) {
     // value columns per recurrence workgroup (16 per chain/output wave pair); GDN_BV overrides
     // for experiments.  fp32 with D_k = 128 fits the LDS budget only with one pair.
     const int bv_env = env_int("GDN_BV", 0);
-    pl->BV = (a->dtype == GDN_DTYPE_F32 && a->D_k == 128) ? 16 : (bv_env == 16 ? 16 : 32);
+    const bool channel = a->gate_kind == GDN_GATE_CHANNEL;
+    if (a->dtype == GDN_DTYPE_F32) pl->BV = (a->D_k == 128 || channel) ? 16 : 32;
+    else pl->BV = bv_env == 16 && !channel ? 16 : 32;
     pl->n_slices = a->D_v / pl->BV;
 
     // ---- in-GPU context parallelism: split sequences into segments when too few
@@ -154,6 +157,14 @@ gdn_status validate_and_plan(const gdn_fwd_args *a, Plan *pl) {
     pl->off_chunks = off; off = align_up(off + (size_t)nch * sizeof(gdn::ChunkInfo));
     pl->off_segs = off;   off = align_up(off + (size_t)pl->total_segs * sizeof(gdn::SegInfo));
     pl->off_order = off;  off = align_up(off + (size_t)pl->total_segs * sizeof(int));
+    if (channel) {
+        const size_t tiles = (size_t)nch * a->H_v;
+        pl->off_P = off;   off = align_up(off + tiles * (esz == 2 ? 2 : 1) * 64 * 64 * esz);
+        pl->off_kg = off;  off = align_up(off + tiles * 64 * a->D_k * esz);
+        pl->off_kd = off;  off = align_up(off + tiles * (esz == 2 ? 2 : 1) * 64 * a->D_k * esz);
+        pl->off_qg = off;  off = align_up(off + tiles * (esz == 2 ? 2 : 1) * 64 * a->D_k * esz);
+        pl->off_dec = off; off = align_up(off + tiles * a->D_k * sizeof(float));
+    }
     if (cp) {
         pl->off_sstar = off; off = align_up(off + seg_heads * a->D_k * a->D_v * sizeof(float));
         pl->off_m = off;     off = align_up(off + seg_heads * a->D_k * a->D_k * sizeof(float));
@@ -212,8 +223,16 @@ gdn_status run_fwd(const gdn_fwd_args *a, void *workspace, size_t workspace_byte
         if ((e = mark(GDN_STAGE_PLAN)) != hipSuccess) return done(fail(GDN_ERR_HIP, "event: %s", hipGetErrorString(e)));
     }
 
-    gdn::IntraParams ip{a->k, a->g, a->beta, chunks, a->T, (int)pl.total_chunks, a->H_qk, a->H_v, ws + pl.off_A};
-    e = gdn::launch_intra(a->dtype, a->D_k, ip, s);
+    const bool channel = a->gate_kind == GDN_GATE_CHANNEL;
+    if (channel) {
+        gdn::IntraKdaParams ip{a->q, a->k, a->g, a->beta, chunks, a->T, (int)pl.total_chunks, a->H_qk, a->H_v,
+                               a->scale, ws + pl.off_A, ws + pl.off_P, ws + pl.off_kg, ws + pl.off_kd,
+                               ws + pl.off_qg, reinterpret_cast<float *>(ws + pl.off_dec)};
+        e = gdn::launch_intra_kda(a->dtype, a->D_k, ip, s);
+    } else {
+        gdn::IntraParams ip{a->k, a->g, a->beta, chunks, a->T, (int)pl.total_chunks, a->H_qk, a->H_v, ws + pl.off_A};
+        e = gdn::launch_intra(a->dtype, a->D_k, ip, s);
+    }
     if (e != hipSuccess) return done(fail(GDN_ERR_HIP, "intra launch: %s", hipGetErrorString(e)));
     if ((e = mark(GDN_STAGE_INTRA)) != hipSuccess) return done(fail(GDN_ERR_HIP, "event: %s", hipGetErrorString(e)));
 
@@ -224,13 +243,17 @@ gdn_status run_fwd(const gdn_fwd_args *a, void *workspace, size_t workspace_byte
     cp.T = a->T; cp.N = a->N; cp.H_qk = a->H_qk; cp.H_v = a->H_v; cp.D_v = a->D_v;
     cp.seg_chunks = pl.seg_chunks; cp.total_segs = (int)pl.total_segs;
     cp.scale = a->scale; cp.o_f32 = a->o_dtype == GDN_DTYPE_F32 ? 1 : 0;
+    if (channel) {
+        cp.P = ws + pl.off_P; cp.kg = ws + pl.off_kg; cp.kd = ws + pl.off_kd; cp.qg = ws + pl.off_qg;
+        cp.decay = reinterpret_cast<const float *>(ws + pl.off_dec);
+    }
     if (pl.cp) {
         cp.seg_sstar = reinterpret_cast<float *>(ws + pl.off_sstar);
         cp.seg_m = reinterpret_cast<float *>(ws + pl.off_m);
         cp.seg_start = reinterpret_cast<float *>(ws + pl.off_start);
         gdn::ChunkParams pre = cp;
         pre.n_slices = (a->D_v + a->D_k) / pl.BV;
-        e = gdn::launch_cp_pre(a->dtype, a->D_k, pl.BV, pre, s);
+        e = gdn::launch_cp_pre(a->dtype, a->D_k, pl.BV, a->gate_kind, pre, s);
         if (e != hipSuccess) return done(fail(GDN_ERR_HIP, "cp pre-process launch: %s", hipGetErrorString(e)));
         if ((e = mark(GDN_STAGE_CP_PRE)) != hipSuccess) return done(fail(GDN_ERR_HIP, "event: %s", hipGetErrorString(e)));
         gdn::FixParams fp{segs, seq, a->T, a->N, a->H_v, a->D_v, pl.seg_chunks, (int)pl.total_segs, a->h0, cp.seg_sstar, cp.seg_m,
@@ -240,7 +263,7 @@ gdn_status run_fwd(const gdn_fwd_args *a, void *workspace, size_t workspace_byte
         if ((e = mark(GDN_STAGE_CP_FIX)) != hipSuccess) return done(fail(GDN_ERR_HIP, "event: %s", hipGetErrorString(e)));
     }
     cp.n_slices = pl.n_slices;
-    e = gdn::launch_chunk(a->dtype, a->D_k, pl.BV, cp, s);
+    e = gdn::launch_chunk(a->dtype, a->D_k, pl.BV, a->gate_kind, cp, s);
     if (e != hipSuccess) return done(fail(GDN_ERR_HIP, "chunk launch: %s", hipGetErrorString(e)));
     if ((e = mark(GDN_STAGE_CHUNK)) != hipSuccess) return done(fail(GDN_ERR_HIP, "event: %s", hipGetErrorString(e)));
     return done(GDN_OK);

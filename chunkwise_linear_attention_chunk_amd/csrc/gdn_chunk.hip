@@ -115,10 +115,11 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanParams p) {
 // they meet beta = 0 and g = 0, so X and V' vanish there, and their outputs are not stored.
 // ------------------------------------------------------------------------------------------
 // Per-token gate rows of one chunk, staged once by wave 0.
-enum { GL = 0, BETA = 64, SC = 128, GAM = 192, SGAM = 256, GROWS = 320 };  // log2 gamma, beta,
-                                                                        // gamma_C/gamma, gamma, scale*gamma
+// Scalar gate: log2 gamma, beta, gamma_C/gamma, gamma, scale*gamma.  Per-channel gate: beta and
+// the [D_k] chunk decay 2^G_C.
+enum { GL = 0, BETA = 64, SC = 128, GAM = 192, SGAM = 256, DEC = 320, GROWS = 448 };
 
-template <typename T, int DK, int NSUB, int NBUF>
+template <typename T, int DK, int NSUB, int NBUF, int GATE>
 struct RecLds {
     static constexpr int ESZ = (int)sizeof(T);
     static constexpr int BV = 16 * NSUB;
@@ -128,11 +129,15 @@ struct RecLds {
     static constexpr int KT = 64 * KGPR * 16, AT = 64 * AGPR * 16, VT = 64 * VGPR * 16;  // tile bytes
     static constexpr int NKB = DK / 32;
     static constexpr int NS = Split<T>::parts;
-    // one tile buffer (byte offsets): K, Q, A, V slice of one chunk
-    static constexpr int K0 = 0, Q0 = KT, A0 = 2 * KT, V0 = 2 * KT + AT, TILES = 2 * KT + AT + VT;
+    static constexpr bool CH = GATE == GDN_GATE_CHANNEL_K;
+    // one tile buffer (byte offsets): K, Q, A, V slice of one chunk.  With per-channel gates K is
+    // K 2^G and Q is Q 2^G (hi part), followed by K 2^(G_C - G) (hi, lo), Q 2^G's lo part and P (hi, lo)
+    static constexpr int K0 = 0, Q0 = KT, A0 = 2 * KT, V0 = 2 * KT + AT, KD0 = V0 + VT;
+    static constexpr int QL0 = KD0 + (CH ? NS * KT : 0), P0 = QL0 + (CH && NS == 2 ? KT : 0);
+    static constexpr int TILES = P0 + (CH ? NS * AT : 0);
     static constexpr int SXN = NSUB * NKB * NS * 64;   // state fragments handed to the output waves
     static constexpr int VXN = NSUB * 2 * NS * 64;     // V' fragments handed to the output waves
-    static constexpr int PXN = 6 * NS * 64;            // P fragments shared by the output waves
+    static constexpr int PXN = CH ? 1 : 6 * NS * 64;   // P fragments shared by the output waves
     static constexpr int BYTES = NBUF * TILES + (SXN + VXN + PXN) * (int)sizeof(Frag<T>) + 2 * GROWS * 4;
     static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
@@ -204,10 +209,11 @@ __device__ __forceinline__ Frag<T> ldpi_col_tile(const unsigned char *tile, int 
 // MODE 1: context-parallel pre-process (chain waves only) over "virtual" columns: value columns
 //         (V as given, S = 0 at the segment start) give S*, identity columns (V = 0, S = I) give
 //         the segment's transition matrix M; both are written to the workspace.
-template <typename T, int DK, int NSUB, int NBUF, int MODE>
+template <typename T, int DK, int NSUB, int NBUF, int MODE, int GATE>
 __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kernel(ChunkParams p) {
-    using L = RecLds<T, DK, NSUB, NBUF>;
+    using L = RecLds<T, DK, NSUB, NBUF, GATE>;
     constexpr bool OUT = MODE == 0;
+    constexpr bool CH = L::CH;
     constexpr int NW = OUT ? 2 * NSUB : NSUB;      // waves
     constexpr int BV = L::BV, NKB = L::NKB, ESZ = L::ESZ;
     constexpr int EPG = 16 / ESZ;                  // elements per granule
@@ -258,6 +264,12 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
     const float *gb = static_cast<const float *>(p.g) + h;
     const T *bb = static_cast<const T *>(p.beta) + h;
     const T *Ab = static_cast<const T *>(p.A) + (int64_t)h * 4096;
+    // per-channel gates: gated tiles [chunk][H_v][64][DK] and P [chunk][H_v][NS][64][64]
+    const T *kgb = static_cast<const T *>(p.kg) + (int64_t)h * 64 * DK;
+    const T *kdb = static_cast<const T *>(p.kd) + (int64_t)h * L::NS * 64 * DK;
+    const T *qgb = static_cast<const T *>(p.qg) + (int64_t)h * L::NS * 64 * DK;
+    const T *Pb = static_cast<const T *>(p.P) + (int64_t)h * L::NS * 4096;
+    const float *decb = p.decay + (int64_t)h * DK;
     const int64_t qk_stride = (int64_t)p.H_qk * DK, v_stride = (int64_t)p.H_v * DV;
     const int qks = (int)qk_stride, vs = (int)v_stride, hv = p.H_v;
     const int nch = sg.nchunks;
@@ -268,14 +280,38 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
     auto issue_loads = [&](int c, unsigned char *tb) __attribute__((always_inline)) {
         const int64_t tok = si.tok0 + (int64_t)(sg.c0 + c) * kChunk;
         const int last = nvalid(c) - 1;
-        const T *kc = kb_ + tok * qk_stride, *qc = qb + tok * qk_stride, *vc = vb + tok * v_stride;
-        const T *Ac = Ab + (int64_t)(si.chunk0 + sg.c0 + c) * p.H_v * 4096;
+        const int64_t gci = si.chunk0 + sg.c0 + c;   // global chunk index
+        const T *vc = vb + tok * v_stride;
+        const T *Ac = Ab + gci * p.H_v * 4096;
+        // K and Q rows: the inputs (row stride H_qk DK, clamped into the chunk), or the gated tiles
+        // (row stride DK, tail rows already zero)
+        const T *kc = CH ? kgb + gci * p.H_v * 64 * DK : kb_ + tok * qk_stride;
+        const T *qc = CH ? qgb + gci * p.H_v * L::NS * 64 * DK : qb + tok * qk_stride;
+        const T *kdc = kdb + gci * p.H_v * L::NS * 64 * DK;
+        const int kst = CH ? DK : qks;
 #pragma unroll
         for (int i = wave; i < L::KGPR; i += NW) {         // 64 * KGPR granules = KGPR instructions
             const int pos = 64 * i + lane, row = pos / L::KGPR, g = pos % L::KGPR;
-            const int cv = g ^ tile_swz<L::KGPR>(row), rowc = min(row, last);
-            load_granule_to_lds(kc + rowc * qks + cv * EPG, tb + L::K0 + 1024 * i);
-            if constexpr (OUT) load_granule_to_lds(qc + rowc * qks + cv * EPG, tb + L::Q0 + 1024 * i);
+            const int cv = g ^ tile_swz<L::KGPR>(row), rowc = CH ? row : min(row, last);
+            load_granule_to_lds(kc + rowc * kst + cv * EPG, tb + L::K0 + 1024 * i);
+            if constexpr (OUT) load_granule_to_lds(qc + rowc * kst + cv * EPG, tb + L::Q0 + 1024 * i);
+            if constexpr (CH) {
+                load_granule_to_lds(kdc + row * DK + cv * EPG, tb + L::KD0 + 1024 * i);
+                if constexpr (L::NS == 2) {
+                    load_granule_to_lds(kdc + 64 * DK + row * DK + cv * EPG, tb + L::KD0 + L::KT + 1024 * i);
+                    if constexpr (OUT) load_granule_to_lds(qc + 64 * DK + row * DK + cv * EPG, tb + L::QL0 + 1024 * i);
+                }
+            }
+        }
+        if constexpr (CH && OUT) {
+            const T *Pc = Pb + gci * p.H_v * L::NS * 4096;
+#pragma unroll
+            for (int i = wave; i < L::NS * L::AGPR; i += NW) {
+                const int part = i / L::AGPR, ii = i % L::AGPR;
+                const int pos = 64 * ii + lane, row = pos / L::AGPR, g = pos % L::AGPR;
+                const int cv = g ^ tile_swz<L::AGPR>(row);
+                load_granule_to_lds(Pc + part * 4096 + row * 64 + cv * EPG, tb + L::P0 + part * L::AT + 1024 * ii);
+            }
         }
 #pragma unroll
         for (int i = wave; i < L::AGPR; i += NW) {
@@ -294,10 +330,17 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
     };
     float rg = 0.f;   // wave 0: gate and (raw) beta of token `lane` of the next chunk; converted
     T rb = T(0.f);    // only when used, so the loads are not waited for here
+    float rdec[DK / 64];  // per-channel gates: the chunk decay of channels lane, lane + 64
     auto load_gates = [&](int c) __attribute__((always_inline)) {
         const int64_t tok = si.tok0 + (int64_t)(sg.c0 + c) * kChunk;
         const int tl = min(lane, nvalid(c) - 1);
-        rg = (gb + tok * hv)[tl * hv];
+        if constexpr (CH) {
+            const float *dc = decb + (si.chunk0 + sg.c0 + c) * (int64_t)p.H_v * DK;
+#pragma unroll
+            for (int u = 0; u < DK / 64; ++u) rdec[u] = dc[lane + 64 * u];
+        } else {
+            rg = (gb + tok * hv)[tl * hv];
+        }
         rb = (bb + tok * hv)[tl * hv];
     };
 
@@ -330,15 +373,20 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
         const int nv = nvalid(c);
         float *g3 = sG + B * GROWS;
         if (wave == 0) {
-            const float gv = lane < nv ? rg : 0.f;                   // tail tokens carry g = 0
-            const float gl = wave_inclusive_scan(gv) * kLog2e;       // log2 gamma_t
-            const float glC = __shfl(gl, 63, 64);
-            const float gam = fast_exp2(gl);
-            g3[GL + lane] = gl;
             g3[BETA + lane] = lane < nv ? to_f32(rb) : 0.f;
-            g3[SC + lane] = fast_exp2(glC - gl);                     // gamma_C / gamma_t
-            g3[GAM + lane] = gam;
-            g3[SGAM + lane] = p.scale * gam;
+            if constexpr (CH) {
+#pragma unroll
+                for (int u = 0; u < DK / 64; ++u) g3[DEC + lane + 64 * u] = rdec[u];
+            } else {
+                const float gv = lane < nv ? rg : 0.f;                   // tail tokens carry g = 0
+                const float gl = wave_inclusive_scan(gv) * kLog2e;       // log2 gamma_t
+                const float glC = __shfl(gl, 63, 64);
+                const float gam = fast_exp2(gl);
+                g3[GL + lane] = gl;
+                g3[SC + lane] = fast_exp2(glC - gl);                     // gamma_C / gamma_t
+                g3[GAM + lane] = gam;
+                g3[SGAM + lane] = p.scale * gam;
+            }
         }
         // vmcnt(0) (gfx9 encoding: vmcnt bits [3:0],[15:14] = 0; expcnt [6:4] and lgkmcnt [11:8]
         // left at their maxima): this wave's direct-to-LDS loads of chunk c have landed
@@ -349,6 +397,7 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
         }
         if (wave == 0) load_gates(min(c + 1, nch - 1));
         const unsigned char *tK = tcur + L::K0, *tQ = tcur + L::Q0, *tA = tcur + L::A0, *tV = tcur + L::V0;
+        const unsigned char *tKd = CH ? tcur + L::KD0 : tK, *tP = tcur + L::P0, *tQl = tcur + L::QL0;
         // =========================== phase 1 ===========================
         Frag<T> Wh[2], Wl[2];          // chain: V'' (pi order over tokens)
         if (chain) {
@@ -378,7 +427,7 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
                 for (int r = 0; r < 4; ++r) {
                     const int i = 16 * m + 4 * grp + r;
                     const float v = mcols ? 0.f : to_f32(*reinterpret_cast<const T *>(tV + tile_off<L::VGPR, ESZ>(i, 16 * sub + l16)));
-                    xx[m][r] = g3[BETA + i] * (v - g3[GAM + i] * ks[m][r]);
+                    xx[m][r] = CH ? g3[BETA + i] * (v - ks[m][r]) : g3[BETA + i] * (v - g3[GAM + i] * ks[m][r]);
                 }
             Frag<T> Xh[2], Xl[2];
 #pragma unroll
@@ -405,14 +454,16 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
                     dst[0] = vh;
                     if constexpr (L::NS == 2) dst[64] = vl;
                 }
+                if constexpr (!CH) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int t = 32 * kb + (e < 4 ? 4 * grp + e : 16 + 4 * grp + e - 4);
-                    x[e] *= g3[SC + t];
+                    for (int e = 0; e < 8; ++e) {
+                        const int t = 32 * kb + (e < 4 ? 4 * grp + e : 16 + 4 * grp + e - 4);
+                        x[e] *= g3[SC + t];
+                    }
                 }
                 split8(x, Wh[kb], Wl[kb]);
             }
-        } else if constexpr (OUT) {
+        } else if constexpr (OUT && !CH) {
             // P^T tiles: acc[r] = (Q K^T)[i = 16 ti + l16][j = 16 tj + 4 grp + r], grouped into the six
             // pi-order fragments (ti, kb); the output waves share the work and the result through LDS.
 #pragma unroll
@@ -455,9 +506,20 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
             const float gC = g3[GAM + 63];
 #pragma unroll
             for (int m = 0; m < MD; ++m) {
-                S[m] *= gC;
+                if constexpr (CH) {
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) mma_x(S[m], ldpi_col_tile<T, L::KGPR>(tK, 16 * m, kb), Wh[kb], Wl[kb]);
+                    for (int r = 0; r < 4; ++r) S[m][r] *= g3[DEC + 16 * m + 4 * grp + r];
+                } else {
+                    S[m] *= gC;
+                }
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    const Frag<T> kdh = ldpi_col_tile<T, L::KGPR>(tKd, 16 * m, kb);
+                    if constexpr (CH && L::NS == 2)
+                        mma_xx(S[m], kdh, ldpi_col_tile<T, L::KGPR>(tKd + L::KT, 16 * m, kb), Wh[kb], Wl[kb]);
+                    else
+                        mma_x(S[m], kdh, Wh[kb], Wl[kb]);
+                }
             }
         } else if constexpr (OUT) {
             const Frag<T> *sxs = sSx + (sub * NKB * L::NS) * 64 + lane;
@@ -470,7 +532,13 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
                 Frag<T> sh = sxs[kb * L::NS * 64], sl;
                 if constexpr (L::NS == 2) sl = sxs[kb * L::NS * 64 + 64];
 #pragma unroll
-                for (int m = 0; m < 4; ++m) mma_x(o[m], ldpi_tile<T, L::KGPR>(tQ, 16 * m + l16, kb), sh, sl);
+                for (int m = 0; m < 4; ++m) {
+                    const Frag<T> qh = ldpi_tile<T, L::KGPR>(tQ, 16 * m + l16, kb);
+                    if constexpr (CH && L::NS == 2)
+                        mma_xx(o[m], qh, ldpi_tile<T, L::KGPR>(tQl, 16 * m + l16, kb), sh, sl);
+                    else
+                        mma_x(o[m], qh, sh, sl);
+                }
             }
             Frag<T> Vh[2], Vl[2];
 #pragma unroll
@@ -481,12 +549,18 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) o[m][r] *= g3[SGAM + 16 * m + 4 * grp + r];
+                for (int r = 0; r < 4; ++r) o[m][r] *= CH ? p.scale : g3[SGAM + 16 * m + 4 * grp + r];
 #pragma unroll
                 for (int kb = 0; kb <= m / 2; ++kb) {
-                    const int f = m == 0 ? 0 : m == 1 ? 1 : m == 2 ? 2 + kb : 4 + kb;
-                    Frag<T> ph = sPx[(f * L::NS) * 64 + lane], pl;
-                    if constexpr (L::NS == 2) pl = sPx[(f * L::NS + 1) * 64 + lane];
+                    Frag<T> ph, pl;
+                    if constexpr (CH) {
+                        ph = ldpi_tile<T, L::AGPR>(tP, 16 * m + l16, kb);
+                        if constexpr (L::NS == 2) pl = ldpi_tile<T, L::AGPR>(tP + L::AT, 16 * m + l16, kb);
+                    } else {
+                        const int f = m == 0 ? 0 : m == 1 ? 1 : m == 2 ? 2 + kb : 4 + kb;
+                        ph = sPx[(f * L::NS) * 64 + lane];
+                        if constexpr (L::NS == 2) pl = sPx[(f * L::NS + 1) * 64 + lane];
+                    }
                     mma_xx(o[m], ph, pl, Vh[kb], Vl[kb]);
                 }
             }
@@ -649,7 +723,7 @@ hipError_t launch_plan(const PlanParams &p, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int MODE>
+template <int MODE, int GATE>
 static hipError_t launch_rec(int dtype, int D_k, int BV, const ChunkParams &p, hipStream_t s) {
     const int units = p.total_segs * p.H_v;
     const unsigned groups = (unsigned)((units + 7) / 8);
@@ -657,26 +731,36 @@ static hipError_t launch_rec(int dtype, int D_k, int BV, const ChunkParams &p, h
     if (units == 0) return hipSuccess;
 #define GDN_CHUNK_CASE(DT, T_, DK_, NSUB_, NBUF_)                                                         \
     if (dtype == DT && D_k == DK_ && BV == 16 * NSUB_) {                                                  \
-        hipLaunchKernelGGL((chunk_kernel<T_, DK_, NSUB_, NBUF_, MODE>), grid, dim3((MODE == 0 ? 128 : 64) * NSUB_), \
+        hipLaunchKernelGGL((chunk_kernel<T_, DK_, NSUB_, NBUF_, MODE, GATE>), grid, dim3((MODE == 0 ? 128 : 64) * NSUB_), \
                            0, s, p);                                                                      \
         return hipGetLastError();                                                                         \
     }
-    GDN_CHUNK_CASE(1, bf16, 128, 2, 2)
-    GDN_CHUNK_CASE(1, bf16, 128, 1, 2)
-    GDN_CHUNK_CASE(1, bf16, 64, 2, 2)
-    GDN_CHUNK_CASE(1, bf16, 64, 1, 2)
-    GDN_CHUNK_CASE(0, float, 128, 1, 1)
-    GDN_CHUNK_CASE(0, float, 64, 2, 2)
-    GDN_CHUNK_CASE(0, float, 64, 1, 2)
+    if constexpr (GATE == GDN_GATE_CHANNEL_K) {
+        // the gated and decayed K tiles and P take LDS: one tile buffer for D_k = 128
+        GDN_CHUNK_CASE(1, bf16, 128, 2, 1)
+        GDN_CHUNK_CASE(1, bf16, 64, 2, 2)
+        GDN_CHUNK_CASE(0, float, 128, 1, 1)
+        GDN_CHUNK_CASE(0, float, 64, 1, 1)
+    } else {
+        GDN_CHUNK_CASE(1, bf16, 128, 2, 2)
+        GDN_CHUNK_CASE(1, bf16, 128, 1, 2)
+        GDN_CHUNK_CASE(1, bf16, 64, 2, 2)
+        GDN_CHUNK_CASE(1, bf16, 64, 1, 2)
+        GDN_CHUNK_CASE(0, float, 128, 1, 1)
+        GDN_CHUNK_CASE(0, float, 64, 2, 2)
+        GDN_CHUNK_CASE(0, float, 64, 1, 2)
+    }
 #undef GDN_CHUNK_CASE
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_chunk(int dtype, int D_k, int BV, const ChunkParams &p, hipStream_t s) {
-    return launch_rec<0>(dtype, D_k, BV, p, s);
+hipError_t launch_chunk(int dtype, int D_k, int BV, int gate, const ChunkParams &p, hipStream_t s) {
+    return gate == GDN_GATE_CHANNEL_K ? launch_rec<0, GDN_GATE_CHANNEL_K>(dtype, D_k, BV, p, s)
+                                      : launch_rec<0, 0>(dtype, D_k, BV, p, s);
 }
-hipError_t launch_cp_pre(int dtype, int D_k, int BV, const ChunkParams &p, hipStream_t s) {
-    return launch_rec<1>(dtype, D_k, BV, p, s);
+hipError_t launch_cp_pre(int dtype, int D_k, int BV, int gate, const ChunkParams &p, hipStream_t s) {
+    return gate == GDN_GATE_CHANNEL_K ? launch_rec<1, GDN_GATE_CHANNEL_K>(dtype, D_k, BV, p, s)
+                                      : launch_rec<1, 0>(dtype, D_k, BV, p, s);
 }
 hipError_t launch_cp_fix(int dtype, int D_k, const FixParams &p, hipStream_t s) {
     const dim3 grid((unsigned)(p.N * p.H_v * (p.D_v / 16))), block(256);

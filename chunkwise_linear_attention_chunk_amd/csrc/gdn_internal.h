@@ -7,6 +7,7 @@
 namespace gdn {
 
 constexpr int kChunk = 64;  // tokens per chunk
+constexpr int GDN_GATE_CHANNEL_K = 1;  // gate kind of per-channel (KDA) gates, as in gdn.h
 
 // Device-side plan tables (built by the plan kernel from cu_seqlens or the batch shape).
 struct SeqInfo {            // one per sequence
@@ -71,6 +72,19 @@ struct IntraParams {
     void *A;                // [n_chunks][H_v][64][64] in the input dtype
 };
 
+struct IntraKdaParams {       // per-channel gates
+    const void *q, *k, *g, *beta;  // g: [tokens][H_v][D_k] in the input dtype
+    const ChunkInfo *chunks;
+    int T;
+    int n_chunks, H_qk, H_v;
+    float scale;
+    void *A;                // [n_chunks][H_v][64][64]
+    void *P;                // [n_chunks][H_v][parts][64][64]: scale (Lower(2^(G_i - G_j)) (.) Q K^T), hi (+ lo)
+    void *kg;               // [n_chunks][H_v][64][D_k]: K 2^G
+    void *kd, *qg;          // [n_chunks][H_v][parts][64][D_k]: K 2^(G_C - G), Q 2^G, hi (+ lo)
+    float *decay;           // [n_chunks][H_v][D_k]: 2^G_C
+};
+
 struct ChunkParams {
     const void *q, *k, *v, *g, *beta;
     const void *A;          // from the intra kernel
@@ -89,6 +103,9 @@ struct ChunkParams {
     float *seg_sstar;       // pre-process output: S* of the segment (cols = D_v)
     float *seg_m;           // pre-process output: transition M of the segment (cols = D_k)
     const float *seg_start; // main pass input for segments j >= 1 (cols = D_v)
+    // per-channel gates (from the per-chunk kernel): gated tiles, P and the chunk decay
+    const void *kg, *kd, *qg, *P;
+    const float *decay;
 };
 
 struct FixParams {
@@ -102,9 +119,10 @@ struct FixParams {
 
 hipError_t launch_plan(const PlanParams &p, hipStream_t s);
 hipError_t launch_intra(int dtype, int D_k, const IntraParams &p, hipStream_t s);
-hipError_t launch_chunk(int dtype, int D_k, int BV, const ChunkParams &p, hipStream_t s);
+hipError_t launch_intra_kda(int dtype, int D_k, const IntraKdaParams &p, hipStream_t s);
+hipError_t launch_chunk(int dtype, int D_k, int BV, int gate, const ChunkParams &p, hipStream_t s);
 // mode 1: context-parallel pre-process (chain only over value and identity columns)
-hipError_t launch_cp_pre(int dtype, int D_k, int BV, const ChunkParams &p, hipStream_t s);
+hipError_t launch_cp_pre(int dtype, int D_k, int BV, int gate, const ChunkParams &p, hipStream_t s);
 hipError_t launch_cp_fix(int dtype, int D_k, const FixParams &p, hipStream_t s);
 
 }  // namespace gdn

@@ -19,6 +19,92 @@ namespace gdn {
 
 namespace {
 
+// Exact inverse of the unit lower triangular I + L (L strictly lower, fp32 [64][LP] in LDS) into X
+// (same layout, strictly lower part only): forward substitution inside the four 16x16 diagonal
+// blocks (lane = column), then the block-triangular merges 16 -> 32 -> 64 on fp32 MFMA.  Called
+// by all 256 threads with L complete and visible; returns after a barrier, X complete.
+__device__ __forceinline__ void invert_unit_lower(const float *sL, float *sX) {
+    constexpr int LP = 64 + 4;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, grp = lane >> 4;
+    // ---- inverses of the four 16x16 diagonal blocks: lane c owns column c, row i absorbs rows < i
+    {
+        const float *L = sL + (16 * wave) * LP + 16 * wave;
+        const int c = l16;
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float s = (i == c) ? 1.f : 0.f;
+#pragma unroll
+            for (int j = 0; j < i; ++j) s -= L[i * LP + j] * x[j];
+            x[i] = s;
+        }
+        if (grp == 0) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sX[(16 * wave + i) * LP + 16 * wave + c] = x[i];
+        }
+    }
+    __syncthreads();
+
+    // ---- 16 -> 32: Ai[b+1][b] = -D_{b+1} L_{b+1,b} D_b for b = 0 (wave 0) and b = 2 (wave 1)
+    if (wave < 2) {
+        const int b = 2 * wave;
+        f32x4 tt = {0.f, 0.f, 0.f, 0.f}, oo = {0.f, 0.f, 0.f, 0.f};
+        mm16_f32_lds(tt, sL + 16 * (b + 1) * LP + 16 * b, LP, sX + 16 * b * LP + 16 * b, LP);
+        mm16_f32_regB(oo, sX + 16 * (b + 1) * LP + 16 * (b + 1), LP, tt);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sX[(16 * (b + 1) + 4 * grp + r) * LP + 16 * b + l16] = -oo[r];
+    }
+    __syncthreads();
+
+    // ---- 32 -> 64: lower-left 32x32 block = -Ai_BB L_BA Ai_AA; wave w builds tile (2 + w/2, w%2)
+    {
+        const int I = 2 + (wave >> 1), J = wave & 1;
+        auto Lt = [&](int a, int b) { return sL + 16 * a * LP + 16 * b; };
+        auto Xt = [&](int a, int b) { return sX + 16 * a * LP + 16 * b; };
+        // T[Ip][J] = L[Ip][0] AiAA[0][J] + L[Ip][1] AiAA[1][J]   (AiAA[0][1] = 0)
+        auto tcalc = [&](int Ip) {
+            f32x4 t = {0.f, 0.f, 0.f, 0.f};
+            if (J == 0) {
+                mm16_f32_lds(t, Lt(Ip, 0), LP, Xt(0, 0), LP);
+                mm16_f32_lds(t, Lt(Ip, 1), LP, Xt(1, 0), LP);
+            } else {
+                mm16_f32_lds(t, Lt(Ip, 1), LP, Xt(1, 1), LP);
+            }
+            return t;
+        };
+        const f32x4 T2 = tcalc(2);
+        f32x4 oo = {0.f, 0.f, 0.f, 0.f};
+        if (I == 2) {
+            mm16_f32_regB(oo, Xt(2, 2), LP, T2);
+        } else {
+            const f32x4 T3 = tcalc(3);
+            mm16_f32_regB(oo, Xt(3, 2), LP, T2);
+            mm16_f32_regB(oo, Xt(3, 3), LP, T3);
+        }
+        // the tiles written here (rows 32..63, cols 0..31) are read by no wave in this step
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sX[(16 * I + 4 * grp + r) * LP + 16 * J + l16] = -oo[r];
+    }
+    __syncthreads();
+}
+
+// Store X's strictly lower part as the unit lower triangular A = I + X (zero above the diagonal)
+// in the input dtype, [64][64] row-major at A.
+template <typename T>
+__device__ __forceinline__ void store_unit_lower(const float *sX, T *A) {
+    constexpr int VEC = Vec16<T>::N, LP = 64 + 4;
+    for (int idx = threadIdx.x; idx < 64 * 64 / VEC; idx += 256) {
+        const int row = idx / (64 / VEC), c0 = (idx - row * (64 / VEC)) * VEC;
+        T vals[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const int col = c0 + e;
+            vals[e] = from_f32<T>(col < row ? sX[row * LP + col] : (col == row ? 1.f : 0.f));
+        }
+        *reinterpret_cast<u32x4 *>(A + row * 64 + c0) = *reinterpret_cast<const u32x4 *>(vals);
+    }
+}
+
 template <typename T, int DK>
 __global__ __launch_bounds__(256) void intra_kernel(IntraParams p) {
     constexpr int VEC = Vec16<T>::N;
@@ -88,78 +174,214 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraParams p) {
     }
     __syncthreads();
 
-    // ---- inverses of the four 16x16 diagonal blocks: lane c owns column c, row i absorbs rows < i
+    invert_unit_lower(sL, sX);
+    store_unit_lower<T>(sX, static_cast<T *>(p.A) + ((int64_t)ci * p.H_v + h) * 4096);
+}
+
+
+// ------------------------------------------------------------------------------------------
+// Kernel (a), per-channel gates (KDA source walk-through, sections 3-5): per (chunk, value head),
+// with G the chunk-local inclusive cumsum of the [D_k] log-gates (log2 units here),
+//   A_raw[i][j] = beta_i sum_d k_id k_jd 2^(G_id - G_jd)          (j < i)
+//   P[i][j]     = scale sum_d q_id k_jd 2^(G_id - G_jd)            (j <= i)
+//   A = (I + A_raw)^{-1},  Kg = K (.) 2^G,  Qg = Q (.) 2^G,  Kd = K (.) 2^(G_C - G),  decay = 2^G_C
+// (G_C: G at the last valid token; tail rows are zero in every output).  The recurrence kernel
+// then runs the scalar-gate schedule on these operands, with P read instead of formed.  Kd and Qg
+// are stored as hi/lo bf16 pairs like P: rounded once they would move the state and the output by
+// about 1e-2 RMS (the decay factors make them inexact, unlike K and Q themselves); Kg is rounded
+// once, its effect is an order of magnitude smaller.
+//
+// The pairwise factor 2^(G_i - G_j) is split per 16x16 tile at a reference row r between j and i
+// (r = last row of the column block for tiles below the diagonal, the first row of the block on
+// it), so both operand factors are decays over at most 15 tokens or at most 1:
+//   left_i = x_i (.) 2^(G_i - G_r) <= |x_i|,   right_j = k_j (.) 2^(G_r - G_j).
+// P's operands are carried as hi/lo bf16 pairs (three MFMAs per block); A_raw's are rounded once.
+// ------------------------------------------------------------------------------------------
+template <typename T, int DK>
+__global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
+    constexpr int VEC = Vec16<T>::N;
+    constexpr int KP = DK + VEC;   // row stride of the K and Q tiles
+    constexpr int LP = 64 + 4;     // row stride of the fp32 64x64 tiles
+    constexpr int GP = DK + 4;     // row stride of the fp32 G tile
+    constexpr int K_BYTES = 64 * KP * (int)sizeof(T);
+    constexpr int X_BYTES = 64 * LP * 4;
+    constexpr int R0 = K_BYTES > X_BYTES ? K_BYTES : X_BYTES;
+    constexpr int NS = Split<T>::parts;
+    // region 0: K tile, later the inverse X; region 1: Q tile, later P (fp32); region 2: A_raw
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * R0 + X_BYTES];
+    __shared__ __attribute__((aligned(16))) float sG[64 * GP];
+    __shared__ float sB[64];
+    T *sK = reinterpret_cast<T *>(smem);
+    T *sQ = reinterpret_cast<T *>(smem + R0);
+    float *sX = reinterpret_cast<float *>(smem);
+    float *sP = reinterpret_cast<float *>(smem + R0);
+    float *sL = reinterpret_cast<float *>(smem + 2 * R0);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, grp = lane >> 4;
+    const int ci = blockIdx.x / p.H_v, h = blockIdx.x - ci * p.H_v;
+    const int hq = h / (p.H_v / p.H_qk);
+    const ChunkInfo cinfo = chunk_info(p.chunks, ci, p.T);
+    const int t0 = cinfo.tok0, nv = cinfo.nv, last = max(nv - 1, 0);
+    const T *k = static_cast<const T *>(p.k);
+    const T *q = static_cast<const T *>(p.q);
+    const T *g = static_cast<const T *>(p.g);
+    const T *beta = static_cast<const T *>(p.beta);
+
+    // ---- K, Q tiles (clamped rows, tail masked at staging), gate columns, beta
+    constexpr int VPR = DK / VEC;
+    constexpr int NV = 64 * VPR / 256;
+    u32x4 kv[NV], qv[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int idx = tid + 256 * i, row = min(idx / VPR, last), cv = idx % VPR;
+        const int64_t off = ((int64_t)(t0 + row) * p.H_qk + hq) * DK + cv * VEC;
+        kv[i] = *reinterpret_cast<const u32x4 *>(k + off);
+        qv[i] = *reinterpret_cast<const u32x4 *>(q + off);
+    }
+    // thread (d, part) scans NT consecutive tokens of channel d
+    constexpr int NPART = 256 / DK, NT = 64 / NPART;
+    const int d = tid % DK, part = tid / DK;
+    float gs[NT];
     {
-        const float *L = sL + (16 * wave) * LP + 16 * wave;
-        const int c = l16;
-        float x[16];
+        float acc = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float s = (i == c) ? 1.f : 0.f;
-#pragma unroll
-            for (int j = 0; j < i; ++j) s -= L[i * LP + j] * x[j];
-            x[i] = s;
-        }
-        if (grp == 0) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sX[(16 * wave + i) * LP + 16 * wave + c] = x[i];
+        for (int e = 0; e < NT; ++e) {
+            const int t = part * NT + e;
+            const float gv = to_f32(g[((int64_t)(t0 + min(t, last)) * p.H_v + h) * DK + d]);
+            acc += t < nv ? gv : 0.f;
+            gs[e] = acc;
         }
     }
-    __syncthreads();
-
-    // ---- 16 -> 32: Ai[b+1][b] = -D_{b+1} L_{b+1,b} D_b for b = 0 (wave 0) and b = 2 (wave 1)
-    if (wave < 2) {
-        const int b = 2 * wave;
-        f32x4 tt = {0.f, 0.f, 0.f, 0.f}, oo = {0.f, 0.f, 0.f, 0.f};
-        mm16_f32_lds(tt, sL + 16 * (b + 1) * LP + 16 * b, LP, sX + 16 * b * LP + 16 * b, LP);
-        mm16_f32_regB(oo, sX + 16 * (b + 1) * LP + 16 * (b + 1), LP, tt);
+    if (wave == 0) sB[lane] = lane < nv ? to_f32(beta[(int64_t)(t0 + min(lane, last)) * p.H_v + h]) : 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sX[(16 * (b + 1) + 4 * grp + r) * LP + 16 * b + l16] = -oo[r];
+    for (int i = 0; i < NV; ++i) {
+        const int idx = tid + 256 * i, row = idx / VPR, cv = idx % VPR;
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4 *>(sK + row * KP + cv * VEC) = row < nv ? kv[i] : z;
+        *reinterpret_cast<u32x4 *>(sQ + row * KP + cv * VEC) = row < nv ? qv[i] : z;
     }
-    __syncthreads();
-
-    // ---- 32 -> 64: lower-left 32x32 block = -Ai_BB L_BA Ai_AA; wave w builds tile (2 + w/2, w%2)
-    {
-        const int I = 2 + (wave >> 1), J = wave & 1;
-        auto Lt = [&](int a, int b) { return sL + 16 * a * LP + 16 * b; };
-        auto Xt = [&](int a, int b) { return sX + 16 * a * LP + 16 * b; };
-        // T[Ip][J] = L[Ip][0] AiAA[0][J] + L[Ip][1] AiAA[1][J]   (AiAA[0][1] = 0)
-        auto tcalc = [&](int Ip) {
-            f32x4 t = {0.f, 0.f, 0.f, 0.f};
-            if (J == 0) {
-                mm16_f32_lds(t, Lt(Ip, 0), LP, Xt(0, 0), LP);
-                mm16_f32_lds(t, Lt(Ip, 1), LP, Xt(1, 0), LP);
-            } else {
-                mm16_f32_lds(t, Lt(Ip, 1), LP, Xt(1, 1), LP);
-            }
-            return t;
-        };
-        const f32x4 T2 = tcalc(2);
-        f32x4 oo = {0.f, 0.f, 0.f, 0.f};
-        if (I == 2) {
-            mm16_f32_regB(oo, Xt(2, 2), LP, T2);
-        } else {
-            const f32x4 T3 = tcalc(3);
-            mm16_f32_regB(oo, Xt(3, 2), LP, T2);
-            mm16_f32_regB(oo, Xt(3, 3), LP, T3);
-        }
-        // the tiles written here (rows 32..63, cols 0..31) are read by no wave in this step
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sX[(16 * I + 4 * grp + r) * LP + 16 * J + l16] = -oo[r];
-    }
+    for (int e = 0; e < NT; ++e) sG[(part * NT + e) * GP + d] = gs[e];
+    __syncthreads();
+    float base = 0.f;  // totals of the earlier parts of this channel
+    for (int pp = 0; pp < part; ++pp) base += sG[(pp * NT + NT - 1) * GP + d];
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < NT; ++e) sG[(part * NT + e) * GP + d] = (gs[e] + base) * kLog2e;
     __syncthreads();
 
-    // ---- store A (unit lower triangular, zero above the diagonal) in the input dtype
-    T *A = static_cast<T *>(p.A) + ((int64_t)ci * p.H_v + h) * 4096;
-    for (int idx = tid; idx < 64 * 64 / VEC; idx += 256) {
-        const int row = idx / (64 / VEC), c0 = (idx - row * (64 / VEC)) * VEC;
-        T vals[VEC];
+    // ---- gated operands of the recurrence and the per-channel chunk decay
+    const int64_t tile = ((int64_t)ci * p.H_v + h) * 64 * DK;
+    T *kg = static_cast<T *>(p.kg) + tile;
+    T *kd = static_cast<T *>(p.kd) + NS * tile, *qg = static_cast<T *>(p.qg) + NS * tile;  // NS tiles each
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int idx = tid + 256 * i, row = idx / VPR, c0 = (idx % VPR) * VEC;
+        T vk[VEC];
+        float xd[VEC], xq[VEC];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-            const int col = c0 + e;
-            vals[e] = from_f32<T>(col < row ? sX[row * LP + col] : (col == row ? 1.f : 0.f));
+            const float G = sG[row * GP + c0 + e], GC = sG[last * GP + c0 + e];
+            const float kk = to_f32(sK[row * KP + c0 + e]), qq = to_f32(sQ[row * KP + c0 + e]);
+            const float eg = fast_exp2(G);
+            vk[e] = from_f32<T>(kk * eg);
+            xq[e] = qq * eg;
+            xd[e] = kk * fast_exp2(GC - G);
         }
-        *reinterpret_cast<u32x4 *>(A + row * 64 + c0) = *reinterpret_cast<const u32x4 *>(vals);
+        *reinterpret_cast<u32x4 *>(kg + row * DK + c0) = *reinterpret_cast<const u32x4 *>(vk);
+        if constexpr (NS == 2) {
+            Frag<bf16> hi, lo;
+            split8(xq, hi, lo);
+            *reinterpret_cast<bf16x8 *>(qg + row * DK + c0) = hi.v;
+            *reinterpret_cast<bf16x8 *>(qg + 64 * DK + row * DK + c0) = lo.v;
+            split8(xd, hi, lo);
+            *reinterpret_cast<bf16x8 *>(kd + row * DK + c0) = hi.v;
+            *reinterpret_cast<bf16x8 *>(kd + 64 * DK + row * DK + c0) = lo.v;
+        } else {
+            *reinterpret_cast<u32x4 *>(qg + row * DK + c0) = *reinterpret_cast<const u32x4 *>(xq);
+            *reinterpret_cast<u32x4 *>(kd + row * DK + c0) = *reinterpret_cast<const u32x4 *>(xd);
+        }
+    }
+    if (tid < DK) p.decay[((int64_t)ci * p.H_v + h) * DK + tid] = fast_exp2(sG[last * GP + tid]);
+
+    // ---- A_raw (strict lower) and P (lower with diagonal): the 10 lower 16x16 tiles
+    f32x4 pacc[3];
+    int ptile[3] = {-1, -1, -1};
+#pragma unroll
+    for (int n = 0; n < 3; ++n) {
+        const int t = wave + 4 * n;
+        if (t >= 10) break;
+        const int I = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
+        const int J = t - I * (I + 1) / 2;
+        const int r = J < I ? 16 * J + 15 : 16 * I;
+        const int i = 16 * I + l16, j = 16 * J + l16;  // operand rows of this lane
+        f32x4 aa = {0.f, 0.f, 0.f, 0.f}, pa = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb) {
+            const int d0 = 32 * kb + 8 * grp;
+            float kl[8], ql[8], kr[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float gr = sG[r * GP + d0 + e];
+                const float el = fast_exp2(sG[i * GP + d0 + e] - gr), er = fast_exp2(gr - sG[j * GP + d0 + e]);
+                kl[e] = to_f32(sK[i * KP + d0 + e]) * el;
+                ql[e] = to_f32(sQ[i * KP + d0 + e]) * el;
+                kr[e] = to_f32(sK[j * KP + d0 + e]) * er;
+            }
+            Frag<T> fkl, fkr;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                set_elem(fkl, e, from_f32<T>(kl[e]));
+                set_elem(fkr, e, from_f32<T>(kr[e]));
+            }
+            mma(aa, fkl, fkr);
+            Frag<T> qh, qlo, krh, krl;
+            split8(ql, qh, qlo);
+            split8(kr, krh, krl);
+            mma_xx(pa, qh, qlo, krh, krl);
+        }
+        const int jj = 16 * J + l16;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int ii = 16 * I + 4 * grp + rr;
+            sL[ii * LP + jj] = jj < ii ? sB[ii] * aa[rr] : 0.f;
+            pa[rr] = jj <= ii ? p.scale * pa[rr] : 0.f;
+        }
+        pacc[n] = pa;
+        ptile[n] = t;
+    }
+    __syncthreads();  // K and Q tiles are no longer read: their regions now hold X and P
+    // P tiles above the diagonal are zero
+    for (int idx = tid; idx < 64 * 64; idx += 256) {
+        const int row = idx >> 6, col = idx & 63;
+        if ((col >> 4) > (row >> 4)) sP[row * LP + col] = 0.f;
+    }
+#pragma unroll
+    for (int n = 0; n < 3; ++n) {
+        const int t = ptile[n];
+        if (t < 0) continue;
+        const int I = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
+        const int J = t - I * (I + 1) / 2;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) sP[(16 * I + 4 * grp + rr) * LP + 16 * J + l16] = pacc[n][rr];
+    }
+    invert_unit_lower(sL, sX);   // begins and ends with a barrier-complete LDS state
+    store_unit_lower<T>(sX, static_cast<T *>(p.A) + ((int64_t)ci * p.H_v + h) * 4096);
+    // P as NS tiles [64][64] (hi, then lo for bf16)
+    T *P = static_cast<T *>(p.P) + ((int64_t)ci * p.H_v + h) * NS * 4096;
+    for (int idx = tid; idx < 64 * 64 / VEC; idx += 256) {
+        const int row = idx / (64 / VEC), c0 = (idx - row * (64 / VEC)) * VEC;
+        float x[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) x[e] = sP[row * LP + c0 + e];
+        if constexpr (NS == 2) {
+            Frag<bf16> hi, lo;
+            split8(x, hi, lo);
+            *reinterpret_cast<bf16x8 *>(P + row * 64 + c0) = hi.v;
+            *reinterpret_cast<bf16x8 *>(P + 4096 + row * 64 + c0) = lo.v;
+        } else {
+            *reinterpret_cast<u32x4 *>(P + row * 64 + c0) = *reinterpret_cast<const u32x4 *>(x);
+        }
     }
 }
 
@@ -172,6 +394,17 @@ hipError_t launch_intra(int dtype, int D_k, const IntraParams &p, hipStream_t s)
     else if (dtype == 1 && D_k == 64) hipLaunchKernelGGL((intra_kernel<bf16, 64>), grid, block, 0, s, p);
     else if (dtype == 0 && D_k == 128) hipLaunchKernelGGL((intra_kernel<float, 128>), grid, block, 0, s, p);
     else if (dtype == 0 && D_k == 64) hipLaunchKernelGGL((intra_kernel<float, 64>), grid, block, 0, s, p);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_intra_kda(int dtype, int D_k, const IntraKdaParams &p, hipStream_t s) {
+    const dim3 grid((unsigned)p.n_chunks * (unsigned)p.H_v), block(256);
+    if (p.n_chunks == 0) return hipSuccess;
+    if (dtype == 1 && D_k == 128) hipLaunchKernelGGL((intra_kda_kernel<bf16, 128>), grid, block, 0, s, p);
+    else if (dtype == 1 && D_k == 64) hipLaunchKernelGGL((intra_kda_kernel<bf16, 64>), grid, block, 0, s, p);
+    else if (dtype == 0 && D_k == 128) hipLaunchKernelGGL((intra_kda_kernel<float, 128>), grid, block, 0, s, p);
+    else if (dtype == 0 && D_k == 64) hipLaunchKernelGGL((intra_kda_kernel<float, 64>), grid, block, 0, s, p);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }

@@ -131,6 +131,45 @@ def test_longctx_workload_cp_auto_sampled():
     check(x, TOL["bf16"], heads=[1, 2], label="longctx_bf16 CP auto (sampled)", cp_mode="auto")
 
 
+# --------------------------------------------------------------------------- per-channel gates (KDA)
+@pytest.mark.parametrize("T", [64, 200, 700])
+def test_kda_fp32(T):
+    x = _w("tiny_fp32", T=T, B=2, gate="channel", mu=-3.0, h0=True, seed=100 + T)
+    check(x, TOL["fp32"], label=f"KDA fp32 T={T}")
+
+
+def test_kda_fp32_head_dim_128_grouped():
+    x = _w("tiny_fp32", T=333, H=4, H_qk=2, D=128, gate="channel", mu=-3.0, h0=True, seed=110)
+    check(x, TOL["fp32"], label="KDA fp32 D=128 H_v=4 H_qk=2")
+
+
+@pytest.mark.parametrize("T,mu", [(300, -3.0), (1000, -6.0), (777, -1.0)])
+def test_kda_bf16_small(T, mu):
+    x = _w("kda_bf16", B=2, H=3, T=T, mu=mu, h0=True, seed=120 + T)
+    check(x, TOL["bf16"], label=f"KDA bf16 T={T} mu={mu}")
+
+
+def test_kda_bf16_head_dim_64_grouped():
+    x = _w("kda_bf16", B=1, H=4, H_qk=1, D=64, T=500, h0=True, seed=130)
+    check(x, TOL["bf16"], label="KDA bf16 D=64 H_v=4 H_qk=1")
+
+
+def test_kda_packed_ragged():
+    x = _w("kda_bf16", B=1, n_seqs=6, lens=(1, 63, 65, 0, 300, 129), H=2, h0=True, seed=140)
+    check(x, TOL["bf16"], label="KDA bf16 packed")
+
+
+@pytest.mark.parametrize("L", [1, 3])
+def test_kda_cp(L):
+    x = _w("kda_bf16", B=1, H=2, T=64 * 10 + 9, h0=True, seed=150 + L)
+    check(x, TOL["bf16"], label=f"KDA bf16 CP L={L}", cp_mode="on", cp_segment_chunks=L)
+
+
+def test_kda_workload_sampled():
+    x = _w("kda_bf16")
+    check(x, TOL["bf16"], batches=[1], heads=[0, 31], label="kda_bf16 (sampled)")
+
+
 # --------------------------------------------------------------------------- properties
 def test_deterministic():
     x = _w("qwen3next_bf16", B=1, H=4, T=700, h0=True, seed=21)
