@@ -42,7 +42,8 @@ struct Plan {
     int64_t total_segs = 0;
     size_t off_A = 0, off_seq = 0, off_chunks = 0, off_segs = 0, off_order = 0;
     size_t off_sstar = 0, off_m = 0, off_start = 0;
-    size_t off_P = 0, off_kg = 0, off_kd = 0, off_qg = 0, off_dec = 0;  // per-channel gates
+    size_t off_P = 0, off_gates = 0;                              // intra-chunk output matrix, gate blocks
+    size_t off_kg = 0, off_kd = 0, off_qg = 0;                    // per-channel gates
     size_t bytes = 0;
 };
 
@@ -157,13 +158,13 @@ gdn_status validate_and_plan(const gdn_fwd_args *a, Plan *pl) {
     pl->off_chunks = off; off = align_up(off + (size_t)nch * sizeof(gdn::ChunkInfo));
     pl->off_segs = off;   off = align_up(off + (size_t)pl->total_segs * sizeof(gdn::SegInfo));
     pl->off_order = off;  off = align_up(off + (size_t)pl->total_segs * sizeof(int));
+    const size_t tiles = (size_t)nch * a->H_v;
+    pl->off_P = off;       off = align_up(off + tiles * (esz == 2 ? 2 : 1) * 64 * 64 * esz);
+    pl->off_gates = off;   off = align_up(off + tiles * gdn::GB_FLOATS * sizeof(float));
     if (channel) {
-        const size_t tiles = (size_t)nch * a->H_v;
-        pl->off_P = off;   off = align_up(off + tiles * (esz == 2 ? 2 : 1) * 64 * 64 * esz);
         pl->off_kg = off;  off = align_up(off + tiles * 64 * a->D_k * esz);
         pl->off_kd = off;  off = align_up(off + tiles * (esz == 2 ? 2 : 1) * 64 * a->D_k * esz);
         pl->off_qg = off;  off = align_up(off + tiles * (esz == 2 ? 2 : 1) * 64 * a->D_k * esz);
-        pl->off_dec = off; off = align_up(off + tiles * a->D_k * sizeof(float));
     }
     if (cp) {
         pl->off_sstar = off; off = align_up(off + seg_heads * a->D_k * a->D_v * sizeof(float));
@@ -227,10 +228,11 @@ gdn_status run_fwd(const gdn_fwd_args *a, void *workspace, size_t workspace_byte
     if (channel) {
         gdn::IntraKdaParams ip{a->q, a->k, a->g, a->beta, chunks, a->T, (int)pl.total_chunks, a->H_qk, a->H_v,
                                a->scale, ws + pl.off_A, ws + pl.off_P, ws + pl.off_kg, ws + pl.off_kd,
-                               ws + pl.off_qg, reinterpret_cast<float *>(ws + pl.off_dec)};
+                               ws + pl.off_qg, reinterpret_cast<float *>(ws + pl.off_gates)};
         e = gdn::launch_intra_kda(a->dtype, a->D_k, ip, s);
     } else {
-        gdn::IntraParams ip{a->k, a->g, a->beta, chunks, a->T, (int)pl.total_chunks, a->H_qk, a->H_v, ws + pl.off_A};
+        gdn::IntraParams ip{a->q, a->k, a->g, a->beta, chunks, a->T, (int)pl.total_chunks, a->H_qk, a->H_v,
+                            a->scale, ws + pl.off_A, ws + pl.off_P, reinterpret_cast<float *>(ws + pl.off_gates)};
         e = gdn::launch_intra(a->dtype, a->D_k, ip, s);
     }
     if (e != hipSuccess) return done(fail(GDN_ERR_HIP, "intra launch: %s", hipGetErrorString(e)));
@@ -243,9 +245,10 @@ gdn_status run_fwd(const gdn_fwd_args *a, void *workspace, size_t workspace_byte
     cp.T = a->T; cp.N = a->N; cp.H_qk = a->H_qk; cp.H_v = a->H_v; cp.D_v = a->D_v;
     cp.seg_chunks = pl.seg_chunks; cp.total_segs = (int)pl.total_segs;
     cp.scale = a->scale; cp.o_f32 = a->o_dtype == GDN_DTYPE_F32 ? 1 : 0;
+    cp.P = ws + pl.off_P;
+    cp.gates = reinterpret_cast<const float *>(ws + pl.off_gates);
     if (channel) {
-        cp.P = ws + pl.off_P; cp.kg = ws + pl.off_kg; cp.kd = ws + pl.off_kd; cp.qg = ws + pl.off_qg;
-        cp.decay = reinterpret_cast<const float *>(ws + pl.off_dec);
+        cp.kg = ws + pl.off_kg; cp.kd = ws + pl.off_kd; cp.qg = ws + pl.off_qg;
     }
     if (pl.cp) {
         cp.seg_sstar = reinterpret_cast<float *>(ws + pl.off_sstar);

@@ -101,68 +101,47 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanParams p) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Recurrence + output.  One workgroup per (sequence, value head, NSUB slices of 16 value columns);
-// per slice a chain wave (waves 0 .. NSUB-1) and an output wave (waves NSUB .. 2 NSUB-1).
+// Recurrence + output.  One workgroup per (sequence segment, value head, NSUB slices of 16 value
+// columns); per slice a chain wave (waves 0 .. NSUB-1) and an output wave (waves NSUB .. 2 NSUB-1).
 // Per chunk c, two phases separated by one workgroup barrier:
-//   phase 1  chain: hand S_c to the output wave; KS = K S_c; X = diag(beta)(V - diag(gamma) KS);
-//                   V' = A X; hand V' to the output wave; V'' = diag(gamma_C / gamma) V'
-//            output: P = scale Lower(Gamma) (.) Q K^T (registers)
-//   phase 2  chain: S_{c+1} = gamma_C S_c + K^T V''   (K^T read transposed from the K tile)
-//            output: O = scale diag(gamma) Q S_c + P V', stored
-// Accumulator tiles feed the next product directly (pi order, gdn_device.h).  Q, K, A and the V
-// slice of chunk c + 1 stream into the other LDS buffer with direct-to-LDS loads while chunk c
-// computes.  Rows past the end of a chunk are loaded from the last valid row (always in bounds);
-// they meet beta = 0 and g = 0, so X and V' vanish there, and their outputs are not stored.
+//   phase 1  chain: KS = K S_c; X = diag(beta)(V - diag(gamma) KS); V' = A X; hand V' to the
+//                   output wave; V'' = diag(gamma_C / gamma) V'
+//            output: O = scale diag(gamma) Q S_c
+//   phase 2  chain: S_{c+1} = gamma_C S_c + K^T V''   (K^T read transposed from the K tile), then
+//                   hand S_{c+1} to the output waves for the next chunk
+//            output: O += P V' (P = scale Lower(Gamma) (.) Q K^T from the per-chunk kernel), stored
+// The tiles of chunk c + 1 (K, Q, A, P, the V slice and the gate block of per-token gate rows, also
+// from the per-chunk kernel) stream into the other LDS buffer with direct-to-LDS loads meanwhile,
+// issued by the output waves between their Q S products, so the chain waves only compute.  Accumulator tiles
+// feed the next product directly (pi order, gdn_device.h).  Rows past the end of a chunk read as
+// zero (buffer bounds) and carry beta = 0, g = 0, so X and V' vanish there; their outputs are not
+// stored.
 // ------------------------------------------------------------------------------------------
-// Per-token gate rows of one chunk, staged once by wave 0.
-// Scalar gate: log2 gamma, beta, gamma_C/gamma, gamma, scale*gamma.  Per-channel gate: beta and
-// the [D_k] chunk decay 2^G_C.
-enum { GL = 0, BETA = 64, SC = 128, GAM = 192, SGAM = 256, DEC = 320, GROWS = 448 };
 
-template <typename T, int DK, int NSUB, int NBUF, int GATE>
+template <typename T, int DK, int NSUB, int NBUF, int MODE, int GATE>
 struct RecLds {
     static constexpr int ESZ = (int)sizeof(T);
     static constexpr int BV = 16 * NSUB;
     static constexpr int KGPR = DK * ESZ / 16;     // 16-byte granules per Q/K row
-    static constexpr int AGPR = 64 * ESZ / 16;     // per A row
+    static constexpr int AGPR = 64 * ESZ / 16;     // per A (and P) row
     static constexpr int VGPR = BV * ESZ / 16;     // per V-slice row
     static constexpr int KT = 64 * KGPR * 16, AT = 64 * AGPR * 16, VT = 64 * VGPR * 16;  // tile bytes
     static constexpr int NKB = DK / 32;
     static constexpr int NS = Split<T>::parts;
-    static constexpr bool CH = GATE == GDN_GATE_CHANNEL_K;
-    // one tile buffer (byte offsets): K, Q, A, V slice of one chunk.  With per-channel gates K is
-    // K 2^G and Q is Q 2^G (hi part), followed by K 2^(G_C - G) (hi, lo), Q 2^G's lo part and P (hi, lo)
-    static constexpr int K0 = 0, Q0 = KT, A0 = 2 * KT, V0 = 2 * KT + AT, KD0 = V0 + VT;
-    static constexpr int QL0 = KD0 + (CH ? NS * KT : 0), P0 = QL0 + (CH && NS == 2 ? KT : 0);
-    static constexpr int TILES = P0 + (CH ? NS * AT : 0);
+    static constexpr bool CH = GATE == GDN_GATE_CHANNEL_K, OUT = MODE == 0;
+    // one tile buffer (byte offsets): K, Q, A, V slice, P (NS parts) of one chunk.  With per-channel
+    // gates K is K 2^G and Q is Q 2^G (hi part), followed by K 2^(G_C - G) (NS parts) and the lo
+    // part of Q 2^G.  The pre-process (no output) holds no Q and no P.
+    static constexpr int K0 = 0, Q0 = KT, A0 = Q0 + (OUT ? KT : 0), V0 = A0 + AT, P0 = V0 + VT;
+    static constexpr int KD0 = P0 + (OUT ? NS * AT : 0), QL0 = KD0 + (CH ? NS * KT : 0);
+    static constexpr int G0 = QL0 + (CH && OUT && NS == 2 ? KT : 0);   // the chunk's gate block
+    static constexpr int TILES = G0 + GB_FLOATS * 4;
     static constexpr int SXN = NSUB * NKB * NS * 64;   // state fragments handed to the output waves
     static constexpr int VXN = NSUB * 2 * NS * 64;     // V' fragments handed to the output waves
-    static constexpr int PXN = CH ? 1 : 6 * NS * 64;   // P fragments shared by the output waves
-    static constexpr int BYTES = NBUF * TILES + (SXN + VXN + PXN) * (int)sizeof(Frag<T>) + 2 * GROWS * 4;
+    static constexpr int BYTES = NBUF * TILES + (OUT ? (SXN + VXN) * (int)sizeof(Frag<T>) : 0);
     static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
-// 8 consecutive elements (col multiple of 8) of a swizzled tile row.
-template <int GPR>
-__device__ __forceinline__ Frag<bf16> ld8_t(const unsigned char *tile, int row, int col) {
-    Frag<bf16> f;
-    f.v = *reinterpret_cast<const bf16x8 *>(tile + tile_off<GPR, 2>(row, col));
-    return f;
-}
-template <int GPR>
-__device__ __forceinline__ Frag<float> ld8_t_f(const unsigned char *tile, int row, int col) {
-    const float4 a = *reinterpret_cast<const float4 *>(tile + tile_off<GPR, 4>(row, col));
-    const float4 b = *reinterpret_cast<const float4 *>(tile + tile_off<GPR, 4>(row, col + 4));
-    Frag<float> f;
-    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
-    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
-    return f;
-}
-template <typename T, int GPR>
-__device__ __forceinline__ Frag<T> ld8_tile(const unsigned char *tile, int row, int col) {
-    if constexpr (sizeof(T) == 2) return ld8_t<GPR>(tile, row, col);
-    else return ld8_t_f<GPR>(tile, row, col);
-}
 // pi-order operand of a swizzled tile row: elements [32kb + 4grp, +4) and [32kb + 16 + 4grp, +4).
 template <typename T, int GPR>
 __device__ __forceinline__ Frag<T> ldpi_tile(const unsigned char *tile, int row, int kb) {
@@ -181,7 +160,7 @@ __device__ __forceinline__ Frag<T> ldpi_tile(const unsigned char *tile, int row,
     }
     return f;
 }
-// pi-order column operand of the K tile (the K^T operand of the state update): row d, tokens
+// pi-order column operand of a K-shaped tile (the K^T operand of the state update): row d, tokens
 // 32kb + 4grp + r and 32kb + 16 + 4grp + r.
 template <typename T, int GPR>
 __device__ __forceinline__ Frag<T> ldpi_col_tile(const unsigned char *tile, int d0, int kb) {
@@ -203,6 +182,21 @@ __device__ __forceinline__ Frag<T> ldpi_col_tile(const unsigned char *tile, int 
     }
     return f;
 }
+// V[16m + 4grp + r][col], r = 0..3, from the swizzled V-slice tile (col = this lane's column).
+template <typename T, int GPR>
+__device__ __forceinline__ void ld_vcol4(const unsigned char *tile, int m, int col0, float *v) {
+    const int lane = threadIdx.x & 63, grp = lane >> 4, j = lane & 15;
+    if constexpr (sizeof(T) == 2) {
+        // transposed read: lane j = 4e + q points at V[16m + 4grp + e][col0 + 4q .. + 3]
+        const bf16x4 a = lds_read_tr16(tile + tile_off<GPR, 2>(16 * m + 4 * grp + (j >> 2), col0 + 4 * (j & 3)));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = (float)a[r];
+    } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            v[r] = *reinterpret_cast<const float *>(tile + tile_off<GPR, 4>(16 * m + 4 * grp + r, col0 + j));
+    }
+}
 
 // MODE 0: main pass (chain + output waves) over one segment of a sequence, from h0 or from the
 //         segment's fixed-up start state; the last segment writes the final state.
@@ -211,13 +205,12 @@ __device__ __forceinline__ Frag<T> ldpi_col_tile(const unsigned char *tile, int 
 //         the segment's transition matrix M; both are written to the workspace.
 template <typename T, int DK, int NSUB, int NBUF, int MODE, int GATE>
 __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kernel(ChunkParams p) {
-    using L = RecLds<T, DK, NSUB, NBUF, GATE>;
-    constexpr bool OUT = MODE == 0;
-    constexpr bool CH = L::CH;
-    constexpr int NW = OUT ? 2 * NSUB : NSUB;      // waves
+    using L = RecLds<T, DK, NSUB, NBUF, MODE, GATE>;
+    constexpr bool OUT = L::OUT, CH = L::CH;
     constexpr int BV = L::BV, NKB = L::NKB, ESZ = L::ESZ;
     constexpr int EPG = 16 / ESZ;                  // elements per granule
     constexpr int MD = DK / 16;                    // 16-row state tiles
+    constexpr int NL = NSUB;                       // waves sharing each group of tile loads
 
     // Separate LDS objects for the two tile buffers and for the exchange: the chunk loop is
     // unrolled by two, so every LDS access names its buffer at compile time and the compiler can
@@ -227,14 +220,13 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
     __shared__ __attribute__((aligned(16))) unsigned char tiles1[NBUF == 2 ? L::TILES : 16];
     __shared__ __attribute__((aligned(16))) Frag<T> sSx[OUT ? L::SXN : 1];
     __shared__ __attribute__((aligned(16))) Frag<T> sVx[OUT ? L::VXN : 1];
-    __shared__ __attribute__((aligned(16))) Frag<T> sPx[OUT ? L::PXN : 1];
-    __shared__ float sG[2 * GROWS];
 
     // the wave index is uniform across a wave: readfirstlane makes the role branches scalar
     const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool chain = wave < NSUB;
     const int sub = chain ? wave : wave - NSUB;
+    const bool loader = OUT ? !chain : true;       // issues the tile loads
 
     // XCD-aware mapping: the slices of one (segment, head) share blockIdx % 8, i.e. one XCD and
     // its L2, so Q/K/A fetched by one workgroup are L2 hits for the others.
@@ -261,87 +253,102 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
     const T *qb = static_cast<const T *>(p.q) + (int64_t)hq * DK;
     const T *kb_ = static_cast<const T *>(p.k) + (int64_t)hq * DK;
     const T *vb = static_cast<const T *>(p.v) + (int64_t)h * DV + (mcols ? 0 : c0);
-    const float *gb = static_cast<const float *>(p.g) + h;
-    const T *bb = static_cast<const T *>(p.beta) + h;
     const T *Ab = static_cast<const T *>(p.A) + (int64_t)h * 4096;
-    // per-channel gates: gated tiles [chunk][H_v][64][DK] and P [chunk][H_v][NS][64][64]
+    const T *Pb = static_cast<const T *>(p.P) + (int64_t)h * L::NS * 4096;
+    // per-channel gates: gated tiles [chunk][H_v][parts][64][DK]
     const T *kgb = static_cast<const T *>(p.kg) + (int64_t)h * 64 * DK;
     const T *kdb = static_cast<const T *>(p.kd) + (int64_t)h * L::NS * 64 * DK;
     const T *qgb = static_cast<const T *>(p.qg) + (int64_t)h * L::NS * 64 * DK;
-    const T *Pb = static_cast<const T *>(p.P) + (int64_t)h * L::NS * 4096;
-    const float *decb = p.decay + (int64_t)h * DK;
+    const float *Gb = p.gates + (int64_t)h * GB_FLOATS;
     const int64_t qk_stride = (int64_t)p.H_qk * DK, v_stride = (int64_t)p.H_v * DV;
-    const int qks = (int)qk_stride, vs = (int)v_stride, hv = p.H_v;
+    const int qks = (int)qk_stride, vs = (int)v_stride;
     const int nch = sg.nchunks;
     // chunk c of the segment is chunk sg.c0 + c of the sequence
     auto nvalid = [&](int c) { return min(kChunk, si.len - (sg.c0 + c) * kChunk); };
 
-    // ---- direct-to-LDS loads of chunk c into a tile buffer; instruction i of a tile goes to wave i % NW
-    auto issue_loads = [&](int c, unsigned char *tb) __attribute__((always_inline)) {
+    // ---- direct-to-LDS loads of chunk c into a tile buffer.  Instruction i of a tile goes to
+    //      loader wave i % NL; each lane's byte offset within the tile source is fixed, only the
+    //      buffer base moves with the chunk.  The buffer range ends after the chunk's last valid
+    //      row, so rows past the end read as zero.
+    constexpr int NKI = (L::KGPR + NL - 1) / NL, NAI = (L::AGPR + NL - 1) / NL, NVI = (L::VGPR + NL - 1) / NL;
+    const int kst = CH ? DK : qks;   // K and Q row stride (elements): inputs, or the gated tiles
+    int offK[NKI], offA[NAI], offV[NVI];
+#pragma unroll
+    for (int j = 0; j < NKI; ++j) {
+        const int pos = 64 * (sub + NL * j) + lane, row = pos / L::KGPR, g = pos % L::KGPR;
+        offK[j] = (row * kst + (g ^ tile_swz<L::KGPR>(row)) * EPG) * ESZ;
+    }
+#pragma unroll
+    for (int j = 0; j < NAI; ++j) {
+        const int pos = 64 * (sub + NL * j) + lane, row = pos / L::AGPR, g = pos % L::AGPR;
+        offA[j] = (row * 64 + (g ^ tile_swz<L::AGPR>(row)) * EPG) * ESZ;
+    }
+#pragma unroll
+    for (int j = 0; j < NVI; ++j) {
+        const int pos = 64 * (sub + NL * j) + lane, row = pos / L::VGPR, g = pos % L::VGPR;
+        offV[j] = (row * vs + (g ^ tile_swz<L::VGPR>(row)) * EPG) * ESZ;
+    }
+    // Part q of np issues the instructions j with j % np == q of each tile (the output waves spread
+    // their loads over the chunk's Q S products, so the loads never stall them for long).
+    // K and Q (with per-channel gates also K 2^(G_C - G) and Q 2^G's lo part):
+    auto issue_kq = [&](int c, unsigned char *tb, int part_q, int np) __attribute__((always_inline)) {
+        if (!loader) return;
         const int64_t tok = si.tok0 + (int64_t)(sg.c0 + c) * kChunk;
-        const int last = nvalid(c) - 1;
+        const int nvc = nvalid(c);
         const int64_t gci = si.chunk0 + sg.c0 + c;   // global chunk index
-        const T *vc = vb + tok * v_stride;
-        const T *Ac = Ab + gci * p.H_v * 4096;
-        // K and Q rows: the inputs (row stride H_qk DK, clamped into the chunk), or the gated tiles
-        // (row stride DK, tail rows already zero)
         const T *kc = CH ? kgb + gci * p.H_v * 64 * DK : kb_ + tok * qk_stride;
         const T *qc = CH ? qgb + gci * p.H_v * L::NS * 64 * DK : qb + tok * qk_stride;
-        const T *kdc = kdb + gci * p.H_v * L::NS * 64 * DK;
-        const int kst = CH ? DK : qks;
+        const int kbytes = CH ? 64 * DK * ESZ : ((nvc - 1) * qks + DK) * ESZ;
+        const auto rK = make_rsrc(kc, kbytes);
+        const auto rQ = make_rsrc(qc, CH ? L::NS * 64 * DK * ESZ : kbytes);
+        const auto rKd = make_rsrc(kdb + gci * p.H_v * L::NS * 64 * DK, L::NS * 64 * DK * ESZ);
 #pragma unroll
-        for (int i = wave; i < L::KGPR; i += NW) {         // 64 * KGPR granules = KGPR instructions
-            const int pos = 64 * i + lane, row = pos / L::KGPR, g = pos % L::KGPR;
-            const int cv = g ^ tile_swz<L::KGPR>(row), rowc = CH ? row : min(row, last);
-            load_granule_to_lds(kc + rowc * kst + cv * EPG, tb + L::K0 + 1024 * i);
-            if constexpr (OUT) load_granule_to_lds(qc + rowc * kst + cv * EPG, tb + L::Q0 + 1024 * i);
+        for (int j = 0; j < NKI; ++j) {
+            const int i = sub + NL * j;
+            if (j % np != part_q) continue;
+            if (NKI * NL != L::KGPR && i >= L::KGPR) break;
+            buffer_granule_to_lds(rK, tb + L::K0 + 1024 * i, offK[j], 0);
+            if constexpr (OUT) buffer_granule_to_lds(rQ, tb + L::Q0 + 1024 * i, offK[j], 0);
             if constexpr (CH) {
-                load_granule_to_lds(kdc + row * DK + cv * EPG, tb + L::KD0 + 1024 * i);
-                if constexpr (L::NS == 2) {
-                    load_granule_to_lds(kdc + 64 * DK + row * DK + cv * EPG, tb + L::KD0 + L::KT + 1024 * i);
-                    if constexpr (OUT) load_granule_to_lds(qc + 64 * DK + row * DK + cv * EPG, tb + L::QL0 + 1024 * i);
-                }
-            }
-        }
-        if constexpr (CH && OUT) {
-            const T *Pc = Pb + gci * p.H_v * L::NS * 4096;
 #pragma unroll
-            for (int i = wave; i < L::NS * L::AGPR; i += NW) {
-                const int part = i / L::AGPR, ii = i % L::AGPR;
-                const int pos = 64 * ii + lane, row = pos / L::AGPR, g = pos % L::AGPR;
-                const int cv = g ^ tile_swz<L::AGPR>(row);
-                load_granule_to_lds(Pc + part * 4096 + row * 64 + cv * EPG, tb + L::P0 + part * L::AT + 1024 * ii);
-            }
-        }
-#pragma unroll
-        for (int i = wave; i < L::AGPR; i += NW) {
-            const int pos = 64 * i + lane, row = pos / L::AGPR, g = pos % L::AGPR;
-            const int cv = g ^ tile_swz<L::AGPR>(row);
-            load_granule_to_lds(Ac + row * 64 + cv * EPG, tb + L::A0 + 1024 * i);
-        }
-        if (!mcols) {
-#pragma unroll
-            for (int i = wave; i < L::VGPR; i += NW) {
-                const int pos = 64 * i + lane, row = pos / L::VGPR, g = pos % L::VGPR;
-                const int cv = g ^ tile_swz<L::VGPR>(row), rowc = min(row, last);
-                load_granule_to_lds(vc + rowc * vs + cv * EPG, tb + L::V0 + 1024 * i);
+                for (int part = 0; part < L::NS; ++part)
+                    buffer_granule_to_lds(rKd, tb + L::KD0 + part * L::KT + 1024 * i, offK[j], part * 64 * DK * ESZ);
+                if constexpr (OUT && L::NS == 2) buffer_granule_to_lds(rQ, tb + L::QL0 + 1024 * i, offK[j], 64 * DK * ESZ);
             }
         }
     };
-    float rg = 0.f;   // wave 0: gate and (raw) beta of token `lane` of the next chunk; converted
-    T rb = T(0.f);    // only when used, so the loads are not waited for here
-    float rdec[DK / 64];  // per-channel gates: the chunk decay of channels lane, lane + 64
-    auto load_gates = [&](int c) __attribute__((always_inline)) {
+    // A, P, the V slice and the gate block:
+    auto issue_apvg = [&](int c, unsigned char *tb, int part_q, int np) __attribute__((always_inline)) {
+        if (!loader) return;
         const int64_t tok = si.tok0 + (int64_t)(sg.c0 + c) * kChunk;
-        const int tl = min(lane, nvalid(c) - 1);
-        if constexpr (CH) {
-            const float *dc = decb + (si.chunk0 + sg.c0 + c) * (int64_t)p.H_v * DK;
+        const int nvc = nvalid(c);
+        const int64_t gci = si.chunk0 + sg.c0 + c;   // global chunk index
+        const auto rA = make_rsrc(Ab + gci * p.H_v * 4096, 4096 * ESZ);
+        const auto rP = make_rsrc(Pb + gci * p.H_v * L::NS * 4096, L::NS * 4096 * ESZ);
 #pragma unroll
-            for (int u = 0; u < DK / 64; ++u) rdec[u] = dc[lane + 64 * u];
-        } else {
-            rg = (gb + tok * hv)[tl * hv];
+        for (int j = 0; j < NAI; ++j) {
+            const int i = sub + NL * j;
+            if (j % np != part_q) continue;
+            if (NAI * NL != L::AGPR && i >= L::AGPR) break;
+            buffer_granule_to_lds(rA, tb + L::A0 + 1024 * i, offA[j], 0);
+            if constexpr (OUT) {
+#pragma unroll
+                for (int part = 0; part < L::NS; ++part)
+                    buffer_granule_to_lds(rP, tb + L::P0 + part * L::AT + 1024 * i, offA[j], part * 4096 * ESZ);
+            }
         }
-        rb = (bb + tok * hv)[tl * hv];
+        if (!mcols) {
+            const auto rV = make_rsrc(vb + tok * v_stride, ((nvc - 1) * vs + BV) * ESZ);
+#pragma unroll
+            for (int j = 0; j < NVI; ++j) {
+                const int i = sub + NL * j;
+                if (j % np != part_q) continue;
+                if (NVI * NL != L::VGPR && i >= L::VGPR) break;
+                buffer_granule_to_lds(rV, tb + L::V0 + 1024 * i, offV[j], 0);
+            }
+        }
+        if (sub == 0 && part_q == 0)   // the gate block: 64 granules, one instruction
+            buffer_granule_to_lds(make_rsrc(Gb + gci * p.H_v * GB_FLOATS, GB_FLOATS * 4), tb + L::G0, lane * 16, 0);
     };
 
     // ---- chain state: S [DK][16] of this slice in fp32 accumulator tiles (rows 16m + 4grp + r)
@@ -360,6 +367,24 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
             S[m][r] = (chain && s_init) ? s_init[d * DV + col] : (mcols && d == col) ? 1.f : 0.f;
         }
 
+    // ---- the entering state of the next chunk as matrix-core operand pairs (pi order over rows),
+    //      handed to the output waves through LDS.  Formed at the end of each chunk, in the time the
+    //      chain waves would otherwise wait for the output waves.
+    Frag<T> Sh[NKB], Sl[NKB];
+    auto split_state = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            float x[8];
+            pack_pi(S[2 * kb], S[2 * kb + 1], x);
+            split8(x, Sh[kb], Sl[kb]);
+            if constexpr (OUT) {
+                Frag<T> *dst = sSx + ((sub * NKB + kb) * L::NS) * 64 + lane;
+                dst[0] = Sh[kb];
+                if constexpr (L::NS == 2) dst[64] = Sl[kb];
+            }
+        }
+    };
+
     // ---- one chunk; B = tile buffer holding it (compile time)
     auto step = [&]<int B>(int c) __attribute__((always_inline)) {
         unsigned char *tcur = B == 0 ? tiles0 : tiles1;
@@ -367,68 +392,60 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
         if constexpr (NBUF == 1) {
             if (c > 0) {
                 __syncthreads();  // every wave is done with the single buffer
-                issue_loads(c, tiles0);
+                issue_kq(c, tiles0, 0, 1);
+                issue_apvg(c, tiles0, 0, 1);
             }
         }
         const int nv = nvalid(c);
-        float *g3 = sG + B * GROWS;
-        if (wave == 0) {
-            g3[BETA + lane] = lane < nv ? to_f32(rb) : 0.f;
-            if constexpr (CH) {
-#pragma unroll
-                for (int u = 0; u < DK / 64; ++u) g3[DEC + lane + 64 * u] = rdec[u];
-            } else {
-                const float gv = lane < nv ? rg : 0.f;                   // tail tokens carry g = 0
-                const float gl = wave_inclusive_scan(gv) * kLog2e;       // log2 gamma_t
-                const float glC = __shfl(gl, 63, 64);
-                const float gam = fast_exp2(gl);
-                g3[GL + lane] = gl;
-                g3[SC + lane] = fast_exp2(glC - gl);                     // gamma_C / gamma_t
-                g3[GAM + lane] = gam;
-                g3[SGAM + lane] = p.scale * gam;
-            }
-        }
+        const float *g3 = reinterpret_cast<const float *>(tcur + L::G0);
         // vmcnt(0) (gfx9 encoding: vmcnt bits [3:0],[15:14] = 0; expcnt [6:4] and lgkmcnt [11:8]
         // left at their maxima): this wave's direct-to-LDS loads of chunk c have landed
         __builtin_amdgcn_s_waitcnt(0x0f70);
-        __syncthreads();  // tiles and gates of chunk c are visible
-        if constexpr (NBUF == 2) {
-            if (c + 1 < nch) issue_loads(c + 1, tnext);               // stream chunk c + 1 meanwhile
+        __syncthreads();  // tiles, gate rows and S_c of chunk c are visible
+        const bool more = NBUF == 2 && c + 1 < nch;                   // stream chunk c + 1 meanwhile
+        if constexpr (!OUT) {
+            if (more) {
+                issue_kq(c + 1, tnext, 0, 1);
+                issue_apvg(c + 1, tnext, 0, 1);
+            }
         }
-        if (wave == 0) load_gates(min(c + 1, nch - 1));
         const unsigned char *tK = tcur + L::K0, *tQ = tcur + L::Q0, *tA = tcur + L::A0, *tV = tcur + L::V0;
         const unsigned char *tKd = CH ? tcur + L::KD0 : tK, *tP = tcur + L::P0, *tQl = tcur + L::QL0;
         // =========================== phase 1 ===========================
         Frag<T> Wh[2], Wl[2];          // chain: V'' (pi order over tokens)
+        f32x4 o[4];                    // output: O of this wave's 16 columns
         if (chain) {
-            Frag<T> Sh[NKB], Sl[NKB];
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                float x[8];
-                pack_pi(S[2 * kb], S[2 * kb + 1], x);
-                split8(x, Sh[kb], Sl[kb]);
-                if constexpr (OUT) {
-                    Frag<T> *dst = sSx + ((sub * NKB + kb) * L::NS) * 64 + lane;
-                    dst[0] = Sh[kb];
-                    if constexpr (L::NS == 2) dst[64] = Sl[kb];
-                }
-            }
-            f32x4 ks[4];
+            // this lane's V values and gate rows first, so their LDS latency hides behind K S
+            float v[4][4], b4[4][4], ga[4][4];
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                ks[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kb = 0; kb < NKB; ++kb) mma_x(ks[m], ldpi_tile<T, L::KGPR>(tK, 16 * m + l16, kb), Sh[kb], Sl[kb]);
+                for (int r = 0; r < 4; ++r) { v[m][r] = 0.f; ga[m][r] = 1.f; }
+                if (!mcols) ld_vcol4<T, L::VGPR>(tV, m, 16 * sub, v[m]);
+                const float4 be = *reinterpret_cast<const float4 *>(g3 + GB_BETA + 16 * m + 4 * grp);
+                b4[m][0] = be.x; b4[m][1] = be.y; b4[m][2] = be.z; b4[m][3] = be.w;
+                if constexpr (!CH) {
+                    const float4 gg = *reinterpret_cast<const float4 *>(g3 + GB_GAM + 16 * m + 4 * grp);
+                    ga[m][0] = gg.x; ga[m][1] = gg.y; ga[m][2] = gg.z; ga[m][3] = gg.w;
+                }
+            }
+            // K S: contraction block outer, the four row tiles inner (independent accumulators)
+            f32x4 ks[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) ks[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                Frag<T> kf[4];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) kf[m] = ldpi_tile<T, L::KGPR>(tK, 16 * m + l16, kb);
+#pragma unroll
+                for (int m = 0; m < 4; ++m) mma_x(ks[m], kf[m], Sh[kb], Sl[kb]);
             }
             f32x4 xx[4];
 #pragma unroll
             for (int m = 0; m < 4; ++m)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = 16 * m + 4 * grp + r;
-                    const float v = mcols ? 0.f : to_f32(*reinterpret_cast<const T *>(tV + tile_off<L::VGPR, ESZ>(i, 16 * sub + l16)));
-                    xx[m][r] = CH ? g3[BETA + i] * (v - ks[m][r]) : g3[BETA + i] * (v - g3[GAM + i] * ks[m][r]);
-                }
+                for (int r = 0; r < 4; ++r) xx[m][r] = b4[m][r] * (v[m][r] - ga[m][r] * ks[m][r]);
             Frag<T> Xh[2], Xl[2];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
@@ -436,12 +453,17 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
                 pack_pi(xx[2 * kb], xx[2 * kb + 1], x);
                 split8(x, Xh[kb], Xl[kb]);
             }
+            // V' = A X (A lower triangular: row tile m needs contraction blocks kb <= m / 2)
             f32x4 vp[4];
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                vp[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int m = 0; m < 4; ++m) vp[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kb = 0; kb <= m / 2; ++kb) mma_x(vp[m], ldpi_tile<T, L::AGPR>(tA, 16 * m + l16, kb), Xh[kb], Xl[kb]);
+            for (int kb = 0; kb < 2; ++kb) {
+                Frag<T> af[4];
+#pragma unroll
+                for (int m = 2 * kb; m < 4; ++m) af[m] = ldpi_tile<T, L::AGPR>(tA, 16 * m + l16, kb);
+#pragma unroll
+                for (int m = 2 * kb; m < 4; ++m) mma_x(vp[m], af[m], Xh[kb], Xl[kb]);
             }
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
@@ -455,80 +477,24 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
                     if constexpr (L::NS == 2) dst[64] = vl;
                 }
                 if constexpr (!CH) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int t = 32 * kb + (e < 4 ? 4 * grp + e : 16 + 4 * grp + e - 4);
-                        x[e] *= g3[SC + t];
-                    }
+                    const float4 s0 = *reinterpret_cast<const float4 *>(g3 + GB_SC + 32 * kb + 4 * grp);
+                    const float4 s1 = *reinterpret_cast<const float4 *>(g3 + GB_SC + 32 * kb + 16 + 4 * grp);
+                    x[0] *= s0.x; x[1] *= s0.y; x[2] *= s0.z; x[3] *= s0.w;
+                    x[4] *= s1.x; x[5] *= s1.y; x[6] *= s1.z; x[7] *= s1.w;
                 }
                 split8(x, Wh[kb], Wl[kb]);
             }
-        } else if constexpr (OUT && !CH) {
-            // P^T tiles: acc[r] = (Q K^T)[i = 16 ti + l16][j = 16 tj + 4 grp + r], grouped into the six
-            // pi-order fragments (ti, kb); the output waves share the work and the result through LDS.
-#pragma unroll
-            for (int f = 0; f < 6; ++f) {
-                constexpr int FTI[6] = {0, 1, 2, 2, 3, 3}, FKB[6] = {0, 0, 0, 1, 0, 1};
-                // balanced split of the ten tiles: owner of fragment f
-                constexpr int OWN2[6] = {1, 0, 0, 0, 1, 1};
-                const int owner = NSUB == 1 ? 0 : (NSUB == 2 ? OWN2[f] : f % NSUB);
-                if (sub != owner) continue;
-                const int ti = FTI[f], kb = FKB[f];
-                const float gli = g3[GL + 16 * ti + l16];
-                float x[8];
-#pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    const int tj = 2 * kb + half;
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                    if (tj <= ti) {
-#pragma unroll
-                        for (int kd = 0; kd < NKB; ++kd)
-                            mma(acc, ld8_tile<T, L::KGPR>(tK, 16 * tj + l16, 32 * kd + 8 * grp),
-                                ld8_tile<T, L::KGPR>(tQ, 16 * ti + l16, 32 * kd + 8 * grp));
-                    }
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int j = 16 * tj + 4 * grp + r;
-                        const float v = p.scale * fast_exp2(gli - g3[GL + j]) * acc[r];
-                        x[4 * half + r] = tj < ti ? v : (tj == ti && 4 * grp + r <= l16) ? v : 0.f;
-                    }
-                }
-                Frag<T> ph, pl;
-                split8(x, ph, pl);
-                sPx[(f * L::NS) * 64 + lane] = ph;
-                if constexpr (L::NS == 2) sPx[(f * L::NS + 1) * 64 + lane] = pl;
-            }
-        }
-        if constexpr (OUT) lds_only_barrier();  // S_c and V' of chunk c are visible to the output waves
-
-        // =========================== phase 2 ===========================
-        if (chain) {
-            const float gC = g3[GAM + 63];
-#pragma unroll
-            for (int m = 0; m < MD; ++m) {
-                if constexpr (CH) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) S[m][r] *= g3[DEC + 16 * m + 4 * grp + r];
-                } else {
-                    S[m] *= gC;
-                }
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const Frag<T> kdh = ldpi_col_tile<T, L::KGPR>(tKd, 16 * m, kb);
-                    if constexpr (CH && L::NS == 2)
-                        mma_xx(S[m], kdh, ldpi_col_tile<T, L::KGPR>(tKd + L::KT, 16 * m, kb), Wh[kb], Wl[kb]);
-                    else
-                        mma_x(S[m], kdh, Wh[kb], Wl[kb]);
-                }
-            }
         } else if constexpr (OUT) {
+            // inter-chunk part: scale diag(gamma) Q S_c (S_c was handed over before this chunk)
             const Frag<T> *sxs = sSx + (sub * NKB * L::NS) * 64 + lane;
-            const Frag<T> *vxs = sVx + (sub * 2 * L::NS) * 64 + lane;
-            f32x4 o[4];
 #pragma unroll
             for (int m = 0; m < 4; ++m) o[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
+                if (more) {                                   // 1/NKB of the loads per block
+                    issue_kq(c + 1, tnext, kb, NKB);
+                    issue_apvg(c + 1, tnext, kb, NKB);
+                }
                 Frag<T> sh = sxs[kb * L::NS * 64], sl;
                 if constexpr (L::NS == 2) sl = sxs[kb * L::NS * 64 + 64];
 #pragma unroll
@@ -540,6 +506,50 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
                         mma_x(o[m], qh, sh, sl);
                 }
             }
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                if constexpr (CH) {
+                    o[m] *= p.scale;
+                } else {
+                    const float4 sgm = *reinterpret_cast<const float4 *>(g3 + GB_SGAM + 16 * m + 4 * grp);
+                    o[m][0] *= sgm.x; o[m][1] *= sgm.y; o[m][2] *= sgm.z; o[m][3] *= sgm.w;
+                }
+            }
+        }
+        if constexpr (OUT) lds_only_barrier();  // V' of chunk c is visible to the output waves
+
+        // =========================== phase 2 ===========================
+        if (chain) {
+            float4 dec[MD];
+#pragma unroll
+            for (int m = 0; m < MD; ++m) {
+                if constexpr (CH) dec[m] = *reinterpret_cast<const float4 *>(g3 + GB_DEC + 16 * m + 4 * grp);
+                else dec[m] = make_float4(g3[GB_GAM + 63], g3[GB_GAM + 63], g3[GB_GAM + 63], g3[GB_GAM + 63]);
+            }
+#pragma unroll
+            for (int m = 0; m < MD; ++m) {
+                S[m][0] *= dec[m].x; S[m][1] *= dec[m].y; S[m][2] *= dec[m].z; S[m][3] *= dec[m].w;
+            }
+            // S += K^T V'': contraction block outer, the row tiles inner, in groups of four
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int m0 = 0; m0 < MD; m0 += 4) {
+                    Frag<T> kh[4], kl[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        kh[u] = ldpi_col_tile<T, L::KGPR>(tKd, 16 * (m0 + u), kb);
+                        if constexpr (CH && L::NS == 2) kl[u] = ldpi_col_tile<T, L::KGPR>(tKd + L::KT, 16 * (m0 + u), kb);
+                    }
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        if constexpr (CH && L::NS == 2) mma_xx(S[m0 + u], kh[u], kl[u], Wh[kb], Wl[kb]);
+                        else mma_x(S[m0 + u], kh[u], Wh[kb], Wl[kb]);
+                    }
+                }
+            split_state();  // S_{c+1} for the next chunk (the output waves read S_c before the barrier)
+        } else if constexpr (OUT) {
+            const Frag<T> *vxs = sVx + (sub * 2 * L::NS) * 64 + lane;
             Frag<T> Vh[2], Vl[2];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
@@ -547,22 +557,15 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
                 if constexpr (L::NS == 2) Vl[kb] = vxs[kb * L::NS * 64 + 64];
             }
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
+            for (int kb = 0; kb < 2; ++kb) {
+                Frag<T> ph[4], pl[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) o[m][r] *= CH ? p.scale : g3[SGAM + 16 * m + 4 * grp + r];
-#pragma unroll
-                for (int kb = 0; kb <= m / 2; ++kb) {
-                    Frag<T> ph, pl;
-                    if constexpr (CH) {
-                        ph = ldpi_tile<T, L::AGPR>(tP, 16 * m + l16, kb);
-                        if constexpr (L::NS == 2) pl = ldpi_tile<T, L::AGPR>(tP + L::AT, 16 * m + l16, kb);
-                    } else {
-                        const int f = m == 0 ? 0 : m == 1 ? 1 : m == 2 ? 2 + kb : 4 + kb;
-                        ph = sPx[(f * L::NS) * 64 + lane];
-                        if constexpr (L::NS == 2) pl = sPx[(f * L::NS + 1) * 64 + lane];
-                    }
-                    mma_xx(o[m], ph, pl, Vh[kb], Vl[kb]);
+                for (int m = 2 * kb; m < 4; ++m) {
+                    ph[m] = ldpi_tile<T, L::AGPR>(tP, 16 * m + l16, kb);
+                    if constexpr (L::NS == 2) pl[m] = ldpi_tile<T, L::AGPR>(tP + L::AT, 16 * m + l16, kb);
                 }
+#pragma unroll
+                for (int m = 2 * kb; m < 4; ++m) mma_xx(o[m], ph[m], pl[m], Vh[kb], Vl[kb]);
             }
             // buffer stores: the resource covers the chunk's valid rows only (rows past the end are
             // dropped by the bounds check); row offsets are scalar, the lane offset is computed once
@@ -585,8 +588,9 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
     };
 
     if (nch > 0) {
-        issue_loads(0, tiles0);
-        if (wave == 0) load_gates(0);
+        issue_kq(0, tiles0, 0, 1);
+        issue_apvg(0, tiles0, 0, 1);
+        if (chain) split_state();
     }
     for (int c = 0; c < nch; c += 2) {
         step.template operator()<0>(c);
@@ -747,7 +751,7 @@ static hipError_t launch_rec(int dtype, int D_k, int BV, const ChunkParams &p, h
         GDN_CHUNK_CASE(1, bf16, 64, 2, 2)
         GDN_CHUNK_CASE(1, bf16, 64, 1, 2)
         GDN_CHUNK_CASE(0, float, 128, 1, 1)
-        GDN_CHUNK_CASE(0, float, 64, 2, 2)
+        GDN_CHUNK_CASE(0, float, 64, 2, 1)
         GDN_CHUNK_CASE(0, float, 64, 1, 2)
     }
 #undef GDN_CHUNK_CASE

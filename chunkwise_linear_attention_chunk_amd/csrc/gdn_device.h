@@ -190,6 +190,12 @@ typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ void load_granule_to_lds(const void *src, void *lds_base) {
     __builtin_amdgcn_global_load_lds(src, (lds_void *)lds_base, 16, 0, 0);
 }
+// One wave instruction moves 64 granules into LDS positions lds + 16 * lane, lane l reading the
+// buffer at byte voff + soff; lanes out of the resource's range write zeros.  (Layout and zero
+// fill checked on gfx950 with an in-bounds probe.)
+__device__ __forceinline__ void buffer_granule_to_lds(__amdgpu_buffer_rsrc_t r, void *lds_base, int voff, int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_base, 16, voff, soff, 0, 0);
+}
 // Raw buffer resource over [base, base + bytes): out-of-range accesses are dropped (stores) or
 // read as zero (loads).  Word 3 is the gfx9 default descriptor format.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {

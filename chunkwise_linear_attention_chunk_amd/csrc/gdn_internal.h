@@ -9,6 +9,11 @@ namespace gdn {
 constexpr int kChunk = 64;  // tokens per chunk
 constexpr int GDN_GATE_CHANNEL_K = 1;  // gate kind of per-channel (KDA) gates, as in gdn.h
 
+// Per (chunk, head) gate block written by the per-chunk kernel, read by the recurrence: fp32 rows
+// of 64 tokens (scalar gate: beta, gamma_C / gamma, gamma, scale * gamma; per-channel gate: beta
+// and the [D_k] chunk decay 2^G_C).  Tail tokens carry beta = 0 and g = 0.
+enum GateBlock { GB_BETA = 0, GB_SC = 64, GB_GAM = 128, GB_SGAM = 192, GB_DEC = 64, GB_FLOATS = 256 };
+
 // Device-side plan tables (built by the plan kernel from cu_seqlens or the batch shape).
 struct SeqInfo {            // one per sequence
     int tok0;               // first token (row of the [B*T] token axis)
@@ -65,11 +70,14 @@ __device__ __forceinline__ ChunkInfo chunk_info(const ChunkInfo *chunks, int ci,
 }
 
 struct IntraParams {
-    const void *k, *g, *beta;
+    const void *q, *k, *g, *beta;
     const ChunkInfo *chunks;  // nullptr: batched input of T tokens per sequence
     int T;
     int n_chunks, H_qk, H_v;
+    float scale;
     void *A;                // [n_chunks][H_v][64][64] in the input dtype
+    void *P;                // [n_chunks][H_v][parts][64][64]: scale Lower(Gamma) (.) Q K^T, hi (+ lo)
+    float *gates;           // [n_chunks][H_v][GB_FLOATS]
 };
 
 struct IntraKdaParams {       // per-channel gates
@@ -82,7 +90,7 @@ struct IntraKdaParams {       // per-channel gates
     void *P;                // [n_chunks][H_v][parts][64][64]: scale (Lower(2^(G_i - G_j)) (.) Q K^T), hi (+ lo)
     void *kg;               // [n_chunks][H_v][64][D_k]: K 2^G
     void *kd, *qg;          // [n_chunks][H_v][parts][64][D_k]: K 2^(G_C - G), Q 2^G, hi (+ lo)
-    float *decay;           // [n_chunks][H_v][D_k]: 2^G_C
+    float *gates;           // [n_chunks][H_v][GB_FLOATS]: beta and the chunk decay 2^G_C
 };
 
 struct ChunkParams {
@@ -103,9 +111,9 @@ struct ChunkParams {
     float *seg_sstar;       // pre-process output: S* of the segment (cols = D_v)
     float *seg_m;           // pre-process output: transition M of the segment (cols = D_k)
     const float *seg_start; // main pass input for segments j >= 1 (cols = D_v)
-    // per-channel gates (from the per-chunk kernel): gated tiles, P and the chunk decay
+    // from the per-chunk kernel: P, the gate blocks, and the gated tiles of per-channel gates
     const void *kg, *kd, *qg, *P;
-    const float *decay;
+    const float *gates;
 };
 
 struct FixParams {

@@ -1,5 +1,6 @@
 // Kernel (a): per (chunk, value head) -- chunk-local gate cumsum, gated beta*K K^T on the
-// matrix cores, and the exact inverse A = (I + strictLower(diag(beta)(Gamma (.) K K^T)))^{-1}.
+// matrix cores, the exact inverse A = (I + strictLower(diag(beta)(Gamma (.) K K^T)))^{-1}, and
+// the output's intra-chunk matrix P = scale Lower(Gamma) (.) Q K^T.
 //
 // Sources: 06 . Flash Linear Attention, section 3 (chunk-local cumsum of log-gates, exp2 of
 // pre-scaled differences) and section 4 (solve_tril: forward substitution inside 16x16
@@ -8,7 +9,8 @@
 // FlashQLA announcement (Qwen), the first step of the chunk-i forward.
 //
 // The inverse is computed in fp32 throughout (the pages use tf32 dots for the merges; gfx950
-// has no tf32 path, so the merges run on fp32 MFMA).  A is stored in the input dtype.
+// has no tf32 path, so the merges run on fp32 MFMA).  A is stored in the input dtype, P as an
+// operand pair (hi, lo) in bf16 or whole in fp32.
 //
 // One workgroup of 256 threads (4 waves) per (chunk, head); many workgroups per CU hide the
 // latency of the serial 16-step substitutions.
@@ -105,20 +107,47 @@ __device__ __forceinline__ void store_unit_lower(const float *sX, T *A) {
     }
 }
 
+// P (fp32 [64][LP] in LDS, zero above the diagonal) to memory as NS tiles [64][64]: hi, then lo
+// for bf16 (hi the truncation, lo the rounded remainder), or the fp32 values.
+template <typename T>
+__device__ __forceinline__ void store_pair_tiles(const float *sP, T *P) {
+    constexpr int VEC = Vec16<T>::N, LP = 64 + 4;
+    for (int idx = threadIdx.x; idx < 64 * 64 / VEC; idx += 256) {
+        const int row = idx / (64 / VEC), c0 = (idx - row * (64 / VEC)) * VEC;
+        float x[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) x[e] = sP[row * LP + c0 + e];
+        if constexpr (Split<T>::parts == 2) {
+            Frag<bf16> hi, lo;
+            split8(x, hi, lo);
+            *reinterpret_cast<bf16x8 *>(P + row * 64 + c0) = hi.v;
+            *reinterpret_cast<bf16x8 *>(P + 4096 + row * 64 + c0) = lo.v;
+        } else {
+            *reinterpret_cast<u32x4 *>(P + row * 64 + c0) = *reinterpret_cast<const u32x4 *>(x);
+        }
+    }
+}
+
+// Scalar gate.  Besides A, the output's intra-chunk matrix P = scale Lower(Gamma) (.) Q K^T (mask
+// with the diagonal; 06 . Flash Linear Attention, section 3) is formed here once per (chunk,
+// head) and stored as an operand pair, so the recurrence kernel only reads it.
 template <typename T, int DK>
 __global__ __launch_bounds__(256) void intra_kernel(IntraParams p) {
     constexpr int VEC = Vec16<T>::N;
-    constexpr int KP = DK + VEC;   // row stride of the K tile (padded against bank conflicts)
+    constexpr int KP = DK + VEC;   // row stride of the K and Q tiles (padded against bank conflicts)
     constexpr int LP = 64 + 4;     // row stride of the fp32 64x64 tiles
     constexpr int K_BYTES = 64 * KP * (int)sizeof(T);
     constexpr int X_BYTES = 64 * LP * 4;
     constexpr int R0 = K_BYTES > X_BYTES ? K_BYTES : X_BYTES;
-    // region 0 holds the K tile, later (after K K^T) the inverse; region 1 holds A_raw.
-    __shared__ __attribute__((aligned(16))) unsigned char smem[R0 + X_BYTES];
+    constexpr int NS = Split<T>::parts;
+    // region 0: K tile, later the inverse X; region 1: Q tile, later P (fp32); region 2: A_raw
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * R0 + X_BYTES];
     __shared__ float sGl[64], sB[64];
     T *sK = reinterpret_cast<T *>(smem);
+    T *sQ = reinterpret_cast<T *>(smem + R0);
     float *sX = reinterpret_cast<float *>(smem);
-    float *sL = reinterpret_cast<float *>(smem + R0);
+    float *sP = reinterpret_cast<float *>(smem + R0);
+    float *sL = reinterpret_cast<float *>(smem + 2 * R0);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, grp = lane >> 4;
     const int ci = blockIdx.x / p.H_v, h = blockIdx.x - ci * p.H_v;
@@ -126,6 +155,7 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraParams p) {
     const ChunkInfo cinfo = chunk_info(p.chunks, ci, p.T);
     const int t0 = cinfo.tok0, nv = cinfo.nv;
     const T *k = static_cast<const T *>(p.k);
+    const T *q = static_cast<const T *>(p.q);
     const float *g = static_cast<const float *>(p.g);
     const T *beta = static_cast<const T *>(p.beta);
 
@@ -135,49 +165,85 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraParams p) {
     const int last = max(nv - 1, 0);
     constexpr int VPR = DK / VEC;
     constexpr int NV = 64 * VPR / 256;
-    u32x4 kv[NV];
+    u32x4 kv[NV], qv[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int idx = tid + 256 * i, row = min(idx / VPR, last), cv = idx % VPR;
-        kv[i] = *reinterpret_cast<const u32x4 *>(k + ((int64_t)(t0 + row) * p.H_qk + hq) * DK + cv * VEC);
+        const int64_t off = ((int64_t)(t0 + row) * p.H_qk + hq) * DK + cv * VEC;
+        kv[i] = *reinterpret_cast<const u32x4 *>(k + off);
+        qv[i] = *reinterpret_cast<const u32x4 *>(q + off);
     }
     if (wave == 0) {
         const int64_t idx = (int64_t)(t0 + min(lane, last)) * p.H_v + h;
         const float gv = lane < nv ? g[idx] : 0.f;
         const float bv = lane < nv ? to_f32(beta[idx]) : 0.f;
-        sGl[lane] = wave_inclusive_scan(gv) * kLog2e;
+        const float gl = wave_inclusive_scan(gv) * kLog2e;     // log2 gamma_t
+        const float glC = __shfl(gl, 63, 64);                  // at the last valid token
+        sGl[lane] = gl;
         sB[lane] = bv;
+        // gate block of the recurrence
+        float *gbk = p.gates + ((int64_t)ci * p.H_v + h) * GB_FLOATS;
+        const float gam = fast_exp2(gl);
+        gbk[GB_BETA + lane] = bv;
+        gbk[GB_SC + lane] = fast_exp2(glC - gl);
+        gbk[GB_GAM + lane] = gam;
+        gbk[GB_SGAM + lane] = p.scale * gam;
     }
-    // ---- K tile [64][DK] (rows past the chunk end are zero)
+    // ---- K and Q tiles [64][DK] (rows past the chunk end are zero)
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int idx = tid + 256 * i, row = idx / VPR, cv = idx % VPR;
-        *reinterpret_cast<u32x4 *>(sK + row * KP + cv * VEC) = row < nv ? kv[i] : u32x4{0u, 0u, 0u, 0u};
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4 *>(sK + row * KP + cv * VEC) = row < nv ? kv[i] : z;
+        *reinterpret_cast<u32x4 *>(sQ + row * KP + cv * VEC) = row < nv ? qv[i] : z;
     }
     __syncthreads();
 
-    // ---- A_raw = strictLower(diag(beta) (Gamma (.) K K^T)): the 10 lower 16x16 tiles
-    for (int t = wave; t < 10; t += 4) {
+    // ---- the 10 lower 16x16 tiles of A_raw = strictLower(diag(beta) (Gamma (.) K K^T)) and of
+    //      P = scale Lower(Gamma) (.) Q K^T (diagonal included)
+    f32x4 pacc[3];
+#pragma unroll
+    for (int n = 0; n < 3; ++n) {
+        const int t = wave + 4 * n;
+        if (t >= 10) break;
         const int ti = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
         const int tj = t - ti * (ti + 1) / 2;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f}, pa = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < DK / 32; ++kb)
-            mma(acc, ld8(sK + (16 * ti + l16) * KP + 32 * kb + 8 * grp), ld8(sK + (16 * tj + l16) * KP + 32 * kb + 8 * grp));
+        for (int kb = 0; kb < DK / 32; ++kb) {
+            const Frag<T> kj = ld8(sK + (16 * tj + l16) * KP + 32 * kb + 8 * grp);
+            mma(acc, ld8(sK + (16 * ti + l16) * KP + 32 * kb + 8 * grp), kj);
+            mma(pa, ld8(sQ + (16 * ti + l16) * KP + 32 * kb + 8 * grp), kj);
+        }
         const int j = 16 * tj + l16;
         const float glj = sGl[j];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int i = 16 * ti + 4 * grp + r;
-            sL[i * LP + j] = (j < i) ? sB[i] * exp2f(sGl[i] - glj) * acc[r] : 0.f;
+            const float gam = fast_exp2(sGl[i] - glj);
+            sL[i * LP + j] = (j < i) ? sB[i] * gam * acc[r] : 0.f;
+            pa[r] = (j <= i) ? p.scale * gam * pa[r] : 0.f;
         }
+        pacc[n] = pa;
     }
-    __syncthreads();
-
-    invert_unit_lower(sL, sX);
+    __syncthreads();  // the K and Q tiles are no longer read: their regions now hold X and P
+    for (int idx = tid; idx < 64 * 64; idx += 256) {
+        const int row = idx >> 6, col = idx & 63;
+        if ((col >> 4) > (row >> 4)) sP[row * LP + col] = 0.f;   // tiles above the diagonal
+    }
+#pragma unroll
+    for (int n = 0; n < 3; ++n) {
+        const int t = wave + 4 * n;
+        if (t >= 10) break;
+        const int ti = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
+        const int tj = t - ti * (ti + 1) / 2;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sP[(16 * ti + 4 * grp + r) * LP + 16 * tj + l16] = pacc[n][r];
+    }
+    invert_unit_lower(sL, sX);   // its barriers also make P complete
     store_unit_lower<T>(sX, static_cast<T *>(p.A) + ((int64_t)ci * p.H_v + h) * 4096);
+    store_pair_tiles<T>(sP, static_cast<T *>(p.P) + ((int64_t)ci * p.H_v + h) * NS * 4096);
 }
-
 
 // ------------------------------------------------------------------------------------------
 // Kernel (a), per-channel gates (KDA source walk-through, sections 3-5): per (chunk, value head),
@@ -302,7 +368,9 @@ __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
             *reinterpret_cast<u32x4 *>(kd + row * DK + c0) = *reinterpret_cast<const u32x4 *>(xd);
         }
     }
-    if (tid < DK) p.decay[((int64_t)ci * p.H_v + h) * DK + tid] = fast_exp2(sG[last * GP + tid]);
+    float *gbk = p.gates + ((int64_t)ci * p.H_v + h) * GB_FLOATS;
+    if (tid < DK) gbk[GB_DEC + tid] = fast_exp2(sG[last * GP + tid]);
+    if (tid < 64) gbk[GB_BETA + tid] = sB[tid];
 
     // ---- A_raw (strict lower) and P (lower with diagonal): the 10 lower 16x16 tiles
     f32x4 pacc[3];
@@ -367,22 +435,7 @@ __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
     }
     invert_unit_lower(sL, sX);   // begins and ends with a barrier-complete LDS state
     store_unit_lower<T>(sX, static_cast<T *>(p.A) + ((int64_t)ci * p.H_v + h) * 4096);
-    // P as NS tiles [64][64] (hi, then lo for bf16)
-    T *P = static_cast<T *>(p.P) + ((int64_t)ci * p.H_v + h) * NS * 4096;
-    for (int idx = tid; idx < 64 * 64 / VEC; idx += 256) {
-        const int row = idx / (64 / VEC), c0 = (idx - row * (64 / VEC)) * VEC;
-        float x[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) x[e] = sP[row * LP + c0 + e];
-        if constexpr (NS == 2) {
-            Frag<bf16> hi, lo;
-            split8(x, hi, lo);
-            *reinterpret_cast<bf16x8 *>(P + row * 64 + c0) = hi.v;
-            *reinterpret_cast<bf16x8 *>(P + 4096 + row * 64 + c0) = lo.v;
-        } else {
-            *reinterpret_cast<u32x4 *>(P + row * 64 + c0) = *reinterpret_cast<const u32x4 *>(x);
-        }
-    }
+    store_pair_tiles<T>(sP, static_cast<T *>(p.P) + ((int64_t)ci * p.H_v + h) * NS * 4096);
 }
 
 }  // namespace

@@ -118,17 +118,20 @@ def test_packed_needs_single_batch_row_and_host_copy():
 def test_workspace_size_and_checks():
     a = _args()
     n = gdn.workspace_bytes(a)
-    # A: ceil(300/64) = 5 chunks per sequence x 2 sequences x 8 heads x 64 x 64 bf16, plus small tables
-    assert n >= 10 * 8 * 64 * 64 * 2
-    assert n < 10 * 8 * 64 * 64 * 2 + 4096
+    # per chunk-head: A [64][64] bf16, P [64][64] as a bf16 pair and a 1 KiB gate block;
+    # ceil(300/64) = 5 chunks per
+    # sequence x 2 sequences x 8 heads, plus small tables
+    per = 64 * 64 * 2 * 3 + 256 * 4
+    assert n >= 10 * 8 * per
+    assert n < 10 * 8 * per + 4096
     assert _status(a, None, 0) == gdn.GDN_ERR_WORKSPACE
     assert _status(a, ctypes.c_void_p(0x10000), n - 1) == gdn.GDN_ERR_WORKSPACE
     assert _status(a, ctypes.c_void_p(0x10001), n) == gdn.GDN_ERR_WORKSPACE  # misaligned
     assert "aligned" in gdn.lib().gdn_last_error().decode()
     # packed lengths change the chunk count: ceil(1/64) + ceil(64/64) + ceil(65/64) = 4 chunks
     p, keep = _packed([0, 1, 65, 130])
-    assert gdn.workspace_bytes(p) >= 4 * 8 * 64 * 64 * 2
-    assert gdn.workspace_bytes(p) < 4 * 8 * 64 * 64 * 2 + 4096
+    assert gdn.workspace_bytes(p) >= 4 * 8 * per
+    assert gdn.workspace_bytes(p) < 4 * 8 * per + 4096
 
 
 def test_workspace_with_context_parallelism():
@@ -139,7 +142,8 @@ def test_workspace_with_context_parallelism():
     maps = 6 * 8 * 3 * 128 * 128 * 4
     assert maps <= on - base < maps + 4096
     # automatic choice: B*H_v = 4 with 1024 chunks splits the sequence; B*H_v = 64 does not
+    per = 64 * 64 * 2 * 3 + 256 * 4
     long = gdn.workspace_bytes(_args(B=1, N=1, T=65536, H_qk=4, H_v=4))
-    assert long > 1024 * 4 * 64 * 64 * 2 + 4 * 3 * 128 * 128 * 4
+    assert long > 1024 * 4 * per + 4 * 3 * 128 * 128 * 4
     wide = gdn.workspace_bytes(_args(B=4, N=4, T=4096, H_qk=16, H_v=16))
-    assert wide < 4 * 64 * 16 * 64 * 64 * 2 + 4096
+    assert wide < 4 * 64 * 16 * per + 4096
