@@ -24,6 +24,7 @@ METRIC = "GDN chunked-prefill fwd tokens/s at 1 GPU + % of MFMA/HBM roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
 KERNEL_SOURCES = {"chunk": "chunkwise_linear_attention_chunk_amd/csrc/gdn_chunk.hip",
+                  "cp_pre": "chunkwise_linear_attention_chunk_amd/csrc/gdn_chunk.hip",
                   "intra": "chunkwise_linear_attention_chunk_amd/csrc/gdn_intra.hip"}
 
 
@@ -67,6 +68,34 @@ def algorithmic_bytes(x, esz):
     state = x["n_seqs"] * H_v * D_k * D_v * 4
     b += state + (state if x["h0"] is not None else 0)                     # final state, h0
     return b
+
+
+def stage_algorithmic_bytes(stage, x, esz, plan):
+    """Compulsory bytes of one launch of a stage's kernel: the op's inputs it must read (and outputs
+    it must write), each counted once.
+      intra  (per-chunk kernel): q, k, the gate and beta;
+      chunk  (recurrence + output): q, k, v, gate, beta, h0 in; o and the final state out;
+      cp_pre (segment maps): k, v, gate and beta of the tokens in segments that are not a
+             sequence's last (the last segment's maps are never formed)."""
+    q, k, v, g = x["q"], x["k"], x["v"], x["g"]
+    H_qk, D_k, H_v, D_v = q.shape[2], q.shape[3], v.shape[2], v.shape[3]
+    gate_per_token = g.numel() // (q.shape[0] * q.shape[1]) * g.element_size()
+    if stage == "intra":
+        tokens = q.shape[0] * q.shape[1]
+        return tokens * (2 * H_qk * D_k * esz + gate_per_token + H_v * esz)
+    if stage == "cp_pre":
+        sl = plan["segment_chunks"]
+        if x["cu_seqlens"] is None:
+            lens = [q.shape[1]] * q.shape[0]
+        else:
+            cu = x["cu_seqlens"].tolist()
+            lens = [cu[i + 1] - cu[i] for i in range(len(cu) - 1)]
+        tokens = 0
+        for L in lens:
+            ns = max(1, -(-(-(-L // 64)) // sl))
+            tokens += min(L, (ns - 1) * sl * 64)
+        return tokens * (H_qk * D_k * esz + H_v * D_v * esz + gate_per_token + H_v * esz)
+    return algorithmic_bytes(x, esz)
 
 
 def algorithmic_flops(x):
@@ -182,13 +211,10 @@ def main():
             prev = j + 1
         for j in range(n_ev):
             hip.hipEventDestroy(arr[j])
-    dominant = max(("intra", "chunk"), key=lambda s: stage_ms[s])
+    plan = gdn.plan(argv[0])
+    dominant = max(("intra", "cp_pre", "chunk"), key=lambda s: stage_ms[s])
     alg_bytes = algorithmic_bytes(x, esz)
-    if dominant == "intra":  # kernel (a) reads k, g, beta
-        k = x["k"]
-        alg_bytes_dom = k.numel() * esz + x["g"].numel() * x["g"].element_size() + x["beta"].numel() * esz
-    else:                    # kernels (b)+(d) read q, k, v, g, beta (+h0) and write o and the final state
-        alg_bytes_dom = alg_bytes
+    alg_bytes_dom = stage_algorithmic_bytes(dominant, x, esz, plan)
     t_dom = stage_ms[dominant] * 1e-3
     achieved = alg_bytes_dom / t_dom / 1e9
     ms_step = elapsed / a.steps * 1e3
@@ -201,8 +227,11 @@ def main():
         "config": {"workload": w.name, "B": w.B if not w.n_seqs else 1, "T_total": x["tokens"],
                    "seqs": x["n_seqs"], "H_qk": w.hqk, "H_v": w.H, "d_k": w.D, "d_v": w.D,
                    "chunk": 64, "gate": w.gate, "h0": w.h0, "input_copies": len(copies),
-                   "cp": a.cp, "cp_ran": bool((ran[-1] >> gdn.STAGES.index("cp_pre")) & 1)},
-        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                   "cp": a.cp, "cp_ran": bool((ran[-1] >> gdn.STAGES.index("cp_pre")) & 1),
+                   "cp_segment_chunks": plan["segment_chunks"] if plan["cp"] else None,
+                   "value_cols_per_group": plan["value_cols_per_group"]},
+        "roofline": {"bound": "hbm", "kernel": dominant, "alg_bytes": alg_bytes_dom, "achieved": achieved,
+                     "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(dominant, w.name)},
         "stage_ms": stage_ms,
         "whole_op": {"alg_bytes": alg_bytes, "alg_flops": algorithmic_flops(x), "t_bound_ms": t_bound * 1e3,

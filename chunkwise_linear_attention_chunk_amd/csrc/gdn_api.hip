@@ -183,6 +183,25 @@ extern "C" size_t gdn_fwd_workspace_bytes(const gdn_fwd_args *a) {
     return pl.bytes;
 }
 
+extern "C" gdn_status gdn_fwd_plan(const gdn_fwd_args *a, gdn_plan_info *info) {
+    if (!info) return fail(GDN_ERR_INVALID_ARG, "info is NULL");
+    Plan pl;
+    const gdn_status st = validate_and_plan(a, &pl);
+    if (st != GDN_OK) return st;
+    int64_t max_nc = 0;
+    for (int i = 0; i < a->N; ++i) {
+        const int64_t len = a->cu_seqlens_dev ? a->cu_seqlens_host[i + 1] - a->cu_seqlens_host[i] : a->T;
+        max_nc = std::max<int64_t>(max_nc, (len + gdn::kChunk - 1) / gdn::kChunk);
+    }
+    info->cp = pl.cp ? 1 : 0;
+    info->segment_chunks = pl.cp ? pl.seg_chunks : (int32_t)max_nc;
+    info->total_segments = pl.total_segs;
+    info->value_cols_per_group = pl.BV;
+    info->reserved = 0;
+    info->workspace_bytes = pl.bytes;
+    return GDN_OK;
+}
+
 namespace {
 
 gdn_status run_fwd(const gdn_fwd_args *a, void *workspace, size_t workspace_bytes, void *stream,

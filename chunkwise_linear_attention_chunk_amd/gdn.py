@@ -17,7 +17,8 @@ GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP
 DTYPE_F32, DTYPE_BF16 = 0, 1
 GATE_SCALAR, GATE_CHANNEL = 0, 1
 CP_MODES = {"auto": 0, "off": 1, "on": 2}
-EXPORTED = ("gdn_fwd", "gdn_fwd_timed", "gdn_fwd_workspace_bytes", "gdn_status_string", "gdn_last_error")
+EXPORTED = ("gdn_fwd", "gdn_fwd_timed", "gdn_fwd_workspace_bytes", "gdn_fwd_plan", "gdn_status_string",
+            "gdn_last_error")
 STAGES = ("plan", "intra", "cp_pre", "cp_fix", "chunk")  # order of gdn_fwd_timed's stages
 
 
@@ -41,6 +42,13 @@ class FwdArgs(ctypes.Structure):
     ]
 
 
+class PlanInfo(ctypes.Structure):
+    """Mirror of gdn_plan_info."""
+    _fields_ = [("cp", ctypes.c_int32), ("segment_chunks", ctypes.c_int32), ("total_segments", ctypes.c_int64),
+                ("value_cols_per_group", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
 _lib = None
 
 
@@ -58,6 +66,8 @@ def lib():
         L.gdn_fwd_timed.argtypes = [ctypes.POINTER(FwdArgs), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                     ctypes.c_void_p, ctypes.POINTER(ctypes.c_uint32)]
         L.gdn_fwd_timed.restype = ctypes.c_int
+        L.gdn_fwd_plan.argtypes = [ctypes.POINTER(FwdArgs), ctypes.POINTER(PlanInfo)]
+        L.gdn_fwd_plan.restype = ctypes.c_int
         L.gdn_status_string.argtypes = [ctypes.c_int]
         L.gdn_status_string.restype = ctypes.c_char_p
         L.gdn_last_error.argtypes = []
@@ -112,6 +122,14 @@ def _require_gpu(name, t):
 
 def workspace_bytes(args):
     return int(lib().gdn_fwd_workspace_bytes(ctypes.byref(args)))
+
+
+def plan(args):
+    """The schedule gdn_fwd would use: dict(cp, segment_chunks, total_segments, value_cols_per_group,
+    workspace_bytes).  Host-only; raises on invalid arguments."""
+    info = PlanInfo()
+    _check(lib().gdn_fwd_plan(ctypes.byref(args), ctypes.byref(info)))
+    return {f: getattr(info, f) for f, _ in PlanInfo._fields_ if f != "reserved"}
 
 
 def fwd_raw(args, workspace, workspace_bytes_, stream):

@@ -95,6 +95,20 @@ typedef struct {
  * arguments).  Depends on shapes, the packed lengths and the CP decision only. */
 size_t gdn_fwd_workspace_bytes(const gdn_fwd_args *a);
 
+/* The schedule gdn_fwd would use for these arguments (in-GPU context parallelism, section
+ * "key problems of FLA GDN chunked prefill" of the FlashQLA announcement: sequences split into
+ * segments of segment_chunks chunks when too few (sequence, head, column group) chains exist).
+ * Host-only: validates like gdn_fwd, launches nothing.  Returns the same status as validation. */
+typedef struct {
+    int32_t cp;                   /* 1 when sequences are split into segments */
+    int32_t segment_chunks;       /* chunks per segment (the longest sequence's count when cp == 0) */
+    int64_t total_segments;       /* segments over all sequences (N when cp == 0) */
+    int32_t value_cols_per_group; /* D_v columns one recurrence workgroup carries */
+    int32_t reserved;
+    size_t workspace_bytes;       /* as gdn_fwd_workspace_bytes */
+} gdn_plan_info;
+gdn_status gdn_fwd_plan(const gdn_fwd_args *a, gdn_plan_info *info);
+
 /* Validate, plan and enqueue the forward on `stream` (a hipStream_t).  The
  * workspace must be device memory of at least gdn_fwd_workspace_bytes(a)
  * bytes, 256-byte aligned; its contents on entry do not matter. */

@@ -24,7 +24,8 @@ def _declared_functions():
 
 def test_every_declared_function_is_exported():
     names = _declared_functions()
-    assert {"gdn_fwd", "gdn_fwd_timed", "gdn_fwd_workspace_bytes", "gdn_status_string", "gdn_last_error"} <= set(names)
+    assert {"gdn_fwd", "gdn_fwd_timed", "gdn_fwd_workspace_bytes", "gdn_fwd_plan", "gdn_status_string",
+            "gdn_last_error"} <= set(names)
     lib = ctypes.CDLL(gdn.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), f"{n} is declared in gdn.h but not exported"
@@ -147,3 +148,16 @@ def test_workspace_with_context_parallelism():
     assert long > 1024 * 4 * per + 4 * 3 * 128 * 128 * 4
     wide = gdn.workspace_bytes(_args(B=4, N=4, T=4096, H_qk=16, H_v=16))
     assert wide < 4 * 64 * 16 * per + 4096
+
+
+def test_plan_query():
+    # the long-context shape (B * H_v = 4) splits its 1024 chunks into segments
+    a = _args(B=1, N=1, T=65536, H_qk=4, H_v=4)
+    info = gdn.plan(a)
+    assert info["cp"] == 1 and info["value_cols_per_group"] == 32
+    assert info["total_segments"] == -(-1024 // info["segment_chunks"])
+    assert info["workspace_bytes"] == gdn.workspace_bytes(a)
+    off = gdn.plan(_args(B=1, N=1, T=65536, H_qk=4, H_v=4, cp_mode=gdn.CP_MODES["off"]))
+    assert off["cp"] == 0 and off["total_segments"] == 1 and off["segment_chunks"] == 1024
+    with pytest.raises(gdn.GdnError):
+        gdn.plan(_args(chunk_size=48))
