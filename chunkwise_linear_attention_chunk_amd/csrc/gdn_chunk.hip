@@ -413,6 +413,7 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
         const unsigned char *tKd = CH ? tcur + L::KD0 : tK, *tP = tcur + L::P0, *tQl = tcur + L::QL0;
         // =========================== phase 1 ===========================
         Frag<T> Wh[2], Wl[2];          // chain: V'' (pi order over tokens)
+        Frag<T> kt[2][MD];             // chain: the K^T fragments of the state update, read early
         f32x4 o[4];                    // output: O of this wave's 16 columns
         if (chain) {
             // this lane's V values and gate rows first, so their LDS latency hides behind K S
@@ -429,18 +430,26 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
                     ga[m][0] = gg.x; ga[m][1] = gg.y; ga[m][2] = gg.z; ga[m][3] = gg.w;
                 }
             }
+            // every K and A fragment of the chunk's products is read up front, so the reads overlap
+            // each other and the first products instead of each waiting in turn
+            Frag<T> kf[NKB][4], af[6];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) kf[kb][m] = ldpi_tile<T, L::KGPR>(tK, 16 * m + l16, kb);
+#pragma unroll
+            for (int f = 0; f < 6; ++f) {
+                const int m = f < 4 ? f : f - 2, kb = f < 4 ? 0 : 1;   // (m, kb): (0..3, 0), (2, 1), (3, 1)
+                af[f] = ldpi_tile<T, L::AGPR>(tA, 16 * m + l16, kb);
+            }
             // K S: contraction block outer, the four row tiles inner (independent accumulators)
             f32x4 ks[4];
 #pragma unroll
             for (int m = 0; m < 4; ++m) ks[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                Frag<T> kf[4];
+            for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-                for (int m = 0; m < 4; ++m) kf[m] = ldpi_tile<T, L::KGPR>(tK, 16 * m + l16, kb);
-#pragma unroll
-                for (int m = 0; m < 4; ++m) mma_x(ks[m], kf[m], Sh[kb], Sl[kb]);
-            }
+                for (int m = 0; m < 4; ++m) mma_x(ks[m], kf[kb][m], Sh[kb], Sl[kb]);
             f32x4 xx[4];
 #pragma unroll
             for (int m = 0; m < 4; ++m)
@@ -458,12 +467,9 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
 #pragma unroll
             for (int m = 0; m < 4; ++m) vp[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                Frag<T> af[4];
-#pragma unroll
-                for (int m = 2 * kb; m < 4; ++m) af[m] = ldpi_tile<T, L::AGPR>(tA, 16 * m + l16, kb);
-#pragma unroll
-                for (int m = 2 * kb; m < 4; ++m) mma_x(vp[m], af[m], Xh[kb], Xl[kb]);
+            for (int f = 0; f < 6; ++f) {
+                const int m = f < 4 ? f : f - 2, kb = f < 4 ? 0 : 1;
+                mma_x(vp[m], af[f], Xh[kb], Xl[kb]);
             }
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
@@ -484,9 +490,23 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
                 }
                 split8(x, Wh[kb], Wl[kb]);
             }
+            // the state update's K^T fragments, read while the output waves finish phase 1
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int m = 0; m < MD; ++m) kt[kb][m] = ldpi_col_tile<T, L::KGPR>(tKd, 16 * m, kb);
         } else if constexpr (OUT) {
             // inter-chunk part: scale diag(gamma) Q S_c (S_c was handed over before this chunk)
             const Frag<T> *sxs = sSx + (sub * NKB * L::NS) * 64 + lane;
+            // the state and Q fragments first (the Q lo parts of per-channel gates as they are used)
+            Frag<T> sh[NKB], sl[NKB], qf[NKB][4];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                sh[kb] = sxs[kb * L::NS * 64];
+                if constexpr (L::NS == 2) sl[kb] = sxs[kb * L::NS * 64 + 64];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) qf[kb][m] = ldpi_tile<T, L::KGPR>(tQ, 16 * m + l16, kb);
+            }
 #pragma unroll
             for (int m = 0; m < 4; ++m) o[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -495,15 +515,12 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
                     issue_kq(c + 1, tnext, kb, NKB);
                     issue_apvg(c + 1, tnext, kb, NKB);
                 }
-                Frag<T> sh = sxs[kb * L::NS * 64], sl;
-                if constexpr (L::NS == 2) sl = sxs[kb * L::NS * 64 + 64];
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    const Frag<T> qh = ldpi_tile<T, L::KGPR>(tQ, 16 * m + l16, kb);
                     if constexpr (CH && L::NS == 2)
-                        mma_xx(o[m], qh, ldpi_tile<T, L::KGPR>(tQl, 16 * m + l16, kb), sh, sl);
+                        mma_xx(o[m], qf[kb][m], ldpi_tile<T, L::KGPR>(tQl, 16 * m + l16, kb), sh[kb], sl[kb]);
                     else
-                        mma_x(o[m], qh, sh, sl);
+                        mma_x(o[m], qf[kb][m], sh[kb], sl[kb]);
                 }
             }
 #pragma unroll
@@ -530,21 +547,20 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
             for (int m = 0; m < MD; ++m) {
                 S[m][0] *= dec[m].x; S[m][1] *= dec[m].y; S[m][2] *= dec[m].z; S[m][3] *= dec[m].w;
             }
-            // S += K^T V'': contraction block outer, the row tiles inner, in groups of four
+            // S += K^T V'': contraction block outer, the row tiles inner
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int m0 = 0; m0 < MD; m0 += 4) {
-                    Frag<T> kh[4], kl[4];
+                    Frag<T> kl[4];
+                    if constexpr (CH && L::NS == 2) {
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        kh[u] = ldpi_col_tile<T, L::KGPR>(tKd, 16 * (m0 + u), kb);
-                        if constexpr (CH && L::NS == 2) kl[u] = ldpi_col_tile<T, L::KGPR>(tKd + L::KT, 16 * (m0 + u), kb);
+                        for (int u = 0; u < 4; ++u) kl[u] = ldpi_col_tile<T, L::KGPR>(tKd + L::KT, 16 * (m0 + u), kb);
                     }
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
-                        if constexpr (CH && L::NS == 2) mma_xx(S[m0 + u], kh[u], kl[u], Wh[kb], Wl[kb]);
-                        else mma_x(S[m0 + u], kh[u], Wh[kb], Wl[kb]);
+                        if constexpr (CH && L::NS == 2) mma_xx(S[m0 + u], kt[kb][m0 + u], kl[u], Wh[kb], Wl[kb]);
+                        else mma_x(S[m0 + u], kt[kb][m0 + u], Wh[kb], Wl[kb]);
                     }
                 }
             split_state();  // S_{c+1} for the next chunk (the output waves read S_c before the barrier)

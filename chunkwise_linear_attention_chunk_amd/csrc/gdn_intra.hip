@@ -128,26 +128,44 @@ __device__ __forceinline__ void store_pair_tiles(const float *sP, T *P) {
     }
 }
 
+// Store one 16x16 accumulator tile (lane: rows 4 grp + r, column l16) of P into the NS tiles
+// [64][64] at P (hi, then lo for bf16; fp32 whole).
+template <typename T>
+__device__ __forceinline__ void store_p_tile(T *P, int ti, int tj, const f32x4 &acc) {
+    const int lane = threadIdx.x & 63, l16 = lane & 15, grp = lane >> 4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int off = (16 * ti + 4 * grp + r) * 64 + 16 * tj + l16;
+        if constexpr (Split<T>::parts == 2) {
+            const uint32_t bits = __float_as_uint(acc[r]) & 0xffff0000u;
+            P[off] = __builtin_bit_cast(bf16, (unsigned short)(bits >> 16));
+            P[4096 + off] = (bf16)(acc[r] - __uint_as_float(bits));
+        } else {
+            P[off] = from_f32<T>(acc[r]);
+        }
+    }
+}
+
 // Scalar gate.  Besides A, the output's intra-chunk matrix P = scale Lower(Gamma) (.) Q K^T (mask
 // with the diagonal; 06 . Flash Linear Attention, section 3) is formed here once per (chunk,
-// head) and stored as an operand pair, so the recurrence kernel only reads it.
+// head) and stored as an operand pair, so the recurrence kernel only reads it.  Q goes straight
+// from memory into matrix-core operand registers; only K (and later the inverse) and A_raw use LDS.
 template <typename T, int DK>
 __global__ __launch_bounds__(256) void intra_kernel(IntraParams p) {
     constexpr int VEC = Vec16<T>::N;
-    constexpr int KP = DK + VEC;   // row stride of the K and Q tiles (padded against bank conflicts)
+    constexpr int KP = DK + VEC;   // row stride of the K tile (padded against bank conflicts)
     constexpr int LP = 64 + 4;     // row stride of the fp32 64x64 tiles
     constexpr int K_BYTES = 64 * KP * (int)sizeof(T);
     constexpr int X_BYTES = 64 * LP * 4;
     constexpr int R0 = K_BYTES > X_BYTES ? K_BYTES : X_BYTES;
     constexpr int NS = Split<T>::parts;
-    // region 0: K tile, later the inverse X; region 1: Q tile, later P (fp32); region 2: A_raw
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * R0 + X_BYTES];
+    constexpr int NKB = DK / 32;
+    // region 0: K tile, later the inverse X; region 1: A_raw
+    __shared__ __attribute__((aligned(16))) unsigned char smem[R0 + X_BYTES];
     __shared__ float sGl[64], sB[64];
     T *sK = reinterpret_cast<T *>(smem);
-    T *sQ = reinterpret_cast<T *>(smem + R0);
     float *sX = reinterpret_cast<float *>(smem);
-    float *sP = reinterpret_cast<float *>(smem + R0);
-    float *sL = reinterpret_cast<float *>(smem + 2 * R0);
+    float *sL = reinterpret_cast<float *>(smem + R0);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, grp = lane >> 4;
     const int ci = blockIdx.x / p.H_v, h = blockIdx.x - ci * p.H_v;
@@ -159,19 +177,36 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraParams p) {
     const float *g = static_cast<const float *>(p.g);
     const T *beta = static_cast<const T *>(p.beta);
 
-    // ---- chunk-local inclusive cumsum of the log-gate (log2 units) and beta; tail rows are 0
-    // Loads are unconditional from rows clamped into the chunk (always in bounds); the tail is
-    // masked afterwards, so the loads are not serialised behind branches.
+    // this wave's lower tiles t = wave, wave + 4, wave + 8 (< 10): (ti, tj) with tj <= ti
+    constexpr int NT = 3;
+    int TI[NT], TJ[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        const int t = wave + 4 * n;
+        TI[n] = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
+        TJ[n] = t - TI[n] * (TI[n] + 1) / 2;
+    }
+    const int ntiles = wave < 2 ? 3 : 2;
+
+    // ---- loads: K rows into LDS (clamped into the chunk, masked at staging); Q operand fragments
+    //      of this wave's tile rows straight into registers (rows past the end are masked later by
+    //      the zero K rows and the output mask).  All loads are unconditional.
     const int last = max(nv - 1, 0);
     constexpr int VPR = DK / VEC;
     constexpr int NV = 64 * VPR / 256;
-    u32x4 kv[NV], qv[NV];
+    u32x4 kv[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int idx = tid + 256 * i, row = min(idx / VPR, last), cv = idx % VPR;
-        const int64_t off = ((int64_t)(t0 + row) * p.H_qk + hq) * DK + cv * VEC;
-        kv[i] = *reinterpret_cast<const u32x4 *>(k + off);
-        qv[i] = *reinterpret_cast<const u32x4 *>(q + off);
+        kv[i] = *reinterpret_cast<const u32x4 *>(k + ((int64_t)(t0 + row) * p.H_qk + hq) * DK + cv * VEC);
+    }
+    Frag<T> qf[NT][NKB];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        const int row = min(16 * TI[n] + l16, last);
+        const T *qr = q + ((int64_t)(t0 + row) * p.H_qk + hq) * DK + 8 * grp;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) qf[n][kb] = ld8(qr + 32 * kb);
     }
     if (wave == 0) {
         const int64_t idx = (int64_t)(t0 + min(lane, last)) * p.H_v + h;
@@ -189,60 +224,56 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraParams p) {
         gbk[GB_GAM + lane] = gam;
         gbk[GB_SGAM + lane] = p.scale * gam;
     }
-    // ---- K and Q tiles [64][DK] (rows past the chunk end are zero)
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int idx = tid + 256 * i, row = idx / VPR, cv = idx % VPR;
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4 *>(sK + row * KP + cv * VEC) = row < nv ? kv[i] : z;
-        *reinterpret_cast<u32x4 *>(sQ + row * KP + cv * VEC) = row < nv ? qv[i] : z;
+        *reinterpret_cast<u32x4 *>(sK + row * KP + cv * VEC) = row < nv ? kv[i] : u32x4{0u, 0u, 0u, 0u};
     }
     __syncthreads();
 
-    // ---- the 10 lower 16x16 tiles of A_raw = strictLower(diag(beta) (Gamma (.) K K^T)) and of
-    //      P = scale Lower(Gamma) (.) Q K^T (diagonal included)
-    f32x4 pacc[3];
+    // ---- this wave's tiles of A_raw = strictLower(diag(beta) (Gamma (.) K K^T)) and of
+    //      P = scale Lower(Gamma) (.) Q K^T (diagonal included), all accumulators in flight together
+    f32x4 aa[NT], pa[NT];
 #pragma unroll
-    for (int n = 0; n < 3; ++n) {
-        const int t = wave + 4 * n;
-        if (t >= 10) break;
-        const int ti = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
-        const int tj = t - ti * (ti + 1) / 2;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f}, pa = {0.f, 0.f, 0.f, 0.f};
+    for (int n = 0; n < NT; ++n) aa[n] = pa[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < DK / 32; ++kb) {
-            const Frag<T> kj = ld8(sK + (16 * tj + l16) * KP + 32 * kb + 8 * grp);
-            mma(acc, ld8(sK + (16 * ti + l16) * KP + 32 * kb + 8 * grp), kj);
-            mma(pa, ld8(sQ + (16 * ti + l16) * KP + 32 * kb + 8 * grp), kj);
+    for (int kb = 0; kb < NKB; ++kb) {
+        Frag<T> ki[NT], kj[NT];
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            if (n >= ntiles) break;
+            ki[n] = ld8(sK + (16 * TI[n] + l16) * KP + 32 * kb + 8 * grp);
+            kj[n] = ld8(sK + (16 * TJ[n] + l16) * KP + 32 * kb + 8 * grp);
         }
-        const int j = 16 * tj + l16;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            if (n >= ntiles) break;
+            mma(aa[n], ki[n], kj[n]);
+            mma(pa[n], qf[n][kb], kj[n]);
+        }
+    }
+    T *P = static_cast<T *>(p.P) + ((int64_t)ci * p.H_v + h) * NS * 4096;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        if (n >= ntiles) break;
+        const int j = 16 * TJ[n] + l16;
         const float glj = sGl[j];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int i = 16 * ti + 4 * grp + r;
+            const int i = 16 * TI[n] + 4 * grp + r;
             const float gam = fast_exp2(sGl[i] - glj);
-            sL[i * LP + j] = (j < i) ? sB[i] * gam * acc[r] : 0.f;
-            pa[r] = (j <= i) ? p.scale * gam * pa[r] : 0.f;
+            sL[i * LP + j] = (j < i) ? sB[i] * gam * aa[n][r] : 0.f;
+            pa[n][r] = (j <= i) ? p.scale * gam * pa[n][r] : 0.f;
         }
-        pacc[n] = pa;
+        store_p_tile<T>(P, TI[n], TJ[n], pa[n]);
     }
-    __syncthreads();  // the K and Q tiles are no longer read: their regions now hold X and P
-    for (int idx = tid; idx < 64 * 64; idx += 256) {
-        const int row = idx >> 6, col = idx & 63;
-        if ((col >> 4) > (row >> 4)) sP[row * LP + col] = 0.f;   // tiles above the diagonal
-    }
-#pragma unroll
-    for (int n = 0; n < 3; ++n) {
-        const int t = wave + 4 * n;
-        if (t >= 10) break;
-        const int ti = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
-        const int tj = t - ti * (ti + 1) / 2;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sP[(16 * ti + 4 * grp + r) * LP + 16 * tj + l16] = pacc[n][r];
-    }
-    invert_unit_lower(sL, sX);   // its barriers also make P complete
+    // the recurrence reads P row tile 0 over columns 0..31 and row tile 2 over 0..63: the upper
+    // tiles (0, 1) and (2, 3) must hold zeros (the others above the diagonal are never read)
+    if (wave >= 2) store_p_tile<T>(P, wave == 2 ? 0 : 2, wave == 2 ? 1 : 3, f32x4{0.f, 0.f, 0.f, 0.f});
+    __syncthreads();  // A_raw complete; the K tile is no longer read (its region now holds X)
+
+    invert_unit_lower(sL, sX);
     store_unit_lower<T>(sX, static_cast<T *>(p.A) + ((int64_t)ci * p.H_v + h) * 4096);
-    store_pair_tiles<T>(sP, static_cast<T *>(p.P) + ((int64_t)ci * p.H_v + h) * NS * 4096);
 }
 
 // ------------------------------------------------------------------------------------------
