@@ -48,6 +48,7 @@ struct Plan {
 };
 
 constexpr int kNoSegments = 1 << 28;  // segment length meaning "the whole sequence"
+constexpr int kCUs = 256;             // MI355X compute units
 
 int64_t count_segments(const gdn_fwd_args *a, int sl) {
     auto segs = [&](int64_t len) {
@@ -138,8 +139,10 @@ gdn_status validate_and_plan(const gdn_fwd_args *a, Plan *pl) {
     const int seg_env = env_int("GDN_CP_SEG", 0);
     int sl = a->cp_segment_chunks > 0 ? a->cp_segment_chunks : seg_env;
     if (sl <= 0) {
-        // enough segments for about two recurrence workgroups per CU, at least 4 chunks each
-        const int64_t want = std::max<int64_t>(1, (512 + chains - 1) / std::max<int64_t>(chains, 1));
+        // segments so the main pass fills the CUs once (one recurrence workgroup per CU; the
+        // pre-process, with no output waves, then also runs in one round): fewer segments leave
+        // CUs idle, more add rounds to both passes and serial steps to the fix-up
+        const int64_t want = std::max<int64_t>(2, kCUs / std::max<int64_t>(chains, 1));
         sl = (int)std::max<int64_t>(4, (max_nc + want - 1) / want);
     }
     bool cp = false;

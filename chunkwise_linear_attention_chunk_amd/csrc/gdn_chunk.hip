@@ -632,21 +632,22 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
 // Context-parallel fix-up (FlashQLA page, the S_{j,0} update of the CP pre-process): per
 // (sequence, value head, 16 value columns), serially over the sequence's segments,
 //   S_start(0) = h0 (or 0),   S_start(j + 1) = S*_j + M_j S_start(j),
-// writing S_start(j) for j >= 1.  Four waves each produce DK/64 16-row tiles of the product; the
-// new state goes through LDS to become the next step's operand.  M is prefetched one segment
-// ahead into registers and staged in LDS (hi + lo bf16 pairs, or fp32).
+// writing S_start(j) for j >= 1.  One wave per 16-row tile of the product.  Each wave's rows of
+// M_j and its S*_j values come straight from memory into registers, two segments ahead (three
+// register sets), and M_j is split into operand pairs off the serial path; only the new state
+// goes through LDS (two buffers, one barrier per segment).  The column slices of one (sequence,
+// head) share an XCD, so M and S* are L2 hits after the first slice reads them.
 // ------------------------------------------------------------------------------------------
 template <typename T, int DK>
-__global__ __launch_bounds__(256) void cp_fix_kernel(FixParams p) {
-    constexpr int NS = Split<T>::parts, MP = DK + 16 / (int)sizeof(T);  // padded row of M
-    constexpr int MT = DK / 64;                    // 16-row output tiles per wave
-    constexpr int NV = DK * DK / 4 / 256;          // float4 of M per thread
-    __shared__ __attribute__((aligned(16))) T sM[NS][DK * MP];
-    __shared__ __attribute__((aligned(16))) float sS[DK * 17];  // S_start [DK][16], padded
+__global__ __launch_bounds__(DK * 4) void cp_fix_kernel(FixParams p) {
+    constexpr int NKB = DK / 32;                   // contraction blocks
+    constexpr int SP = 17;                         // padded row of the LDS state [DK][16]
+    __shared__ __attribute__((aligned(16))) float sS[2][DK * SP];
     const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int m = __builtin_amdgcn_readfirstlane(tid >> 6);   // this wave's row tile
     const int nsl = p.D_v / 16;
-    const int unit = blockIdx.x / nsl, slice = blockIdx.x - unit * nsl;
+    const int bid = blockIdx.x, xcd = bid & 7, rr = bid >> 3;
+    const int slice = rr % nsl, unit = (rr / nsl) * 8 + xcd;
     if (unit >= p.N * p.H_v) return;
     const int n = unit / p.H_v, h = unit - n * p.H_v;
     const SeqInfo si = seq_info(p.seq, n, p.T);
@@ -658,81 +659,79 @@ __global__ __launch_bounds__(256) void cp_fix_kernel(FixParams p) {
     const int64_t hstride = (int64_t)DK * DV;
 
     // S_start(0): h0 or zero
-    for (int i = tid; i < DK * 16; i += 256) {
+    for (int i = tid; i < DK * 16; i += DK * 4) {
         const int d = i >> 4, c = i & 15;
-        sS[d * 17 + c] = p.h0 ? p.h0[((int64_t)n * p.H_v + h) * hstride + d * DV + c0 + c] : 0.f;
+        sS[0][d * SP + c] = p.h0 ? p.h0[((int64_t)n * p.H_v + h) * hstride + d * DV + c0 + c] : 0.f;
     }
-    float4 mreg[NV];
-    auto load_m = [&](int j) __attribute__((always_inline)) {
-        const float4 *src = reinterpret_cast<const float4 *>(p.seg_m + ((int64_t)(gs0 + j) * p.H_v + h) * DK * DK);
-#pragma unroll
-        for (int i = 0; i < NV; ++i) mreg[i] = src[tid + 256 * i];
+    // raw (fp32) M row 16 m + l16 at the pi-order columns of each block, and the S* values of this
+    // lane's accumulator positions, for one segment
+    struct Raw {
+        float4 m[NKB][2];
+        float sst[4];
     };
-    load_m(0);
-    for (int j = 0; j + 1 < ns; ++j) {
-        __syncthreads();  // the previous step is done with sM and sS
-        // stage M_j
+    auto load_raw = [&](int j, Raw &rw) __attribute__((always_inline)) {
+        const float *row = p.seg_m + ((int64_t)(gs0 + j) * p.H_v + h) * DK * DK + (16 * m + l16) * DK;
+        const float *Sj = p.seg_sstar + ((int64_t)(gs0 + j) * p.H_v + h) * hstride;
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int e = 4 * (tid + 256 * i), row = e / DK, cc = e - row * DK;
-            const float x[4] = {mreg[i].x, mreg[i].y, mreg[i].z, mreg[i].w};
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                if constexpr (NS == 2) {
-                    const bf16 hi = (bf16)x[q];
-                    sM[0][row * MP + cc + q] = hi;
-                    sM[1][row * MP + cc + q] = (bf16)(x[q] - (float)hi);
-                } else {
-                    sM[0][row * MP + cc + q] = from_f32<T>(x[q]);
-                }
-            }
+        for (int kb = 0; kb < NKB; ++kb) {
+            rw.m[kb][0] = *reinterpret_cast<const float4 *>(row + 32 * kb + 4 * grp);
+            rw.m[kb][1] = *reinterpret_cast<const float4 *>(row + 32 * kb + 16 + 4 * grp);
         }
-        if (j + 2 < ns) load_m(j + 1);
-        __syncthreads();
-        // B operand: S_start(j) in pi order over d, as hi/lo fragments
-        Frag<T> Bh[DK / 32], Bl[DK / 32];
 #pragma unroll
-        for (int kb = 0; kb < DK / 32; ++kb) {
+        for (int r = 0; r < 4; ++r) rw.sst[r] = Sj[(16 * m + 4 * grp + r) * DV + c0 + l16];
+    };
+    Raw raw[3];
+    load_raw(0, raw[0]);
+    if (ns > 2) load_raw(1, raw[1]);
+
+    // one segment step; B2 = state buffer (j % 2), B3 = raw register set (j % 3), both compile time
+    auto step = [&]<int B2, int B3>(int j) __attribute__((always_inline)) {
+        // segment j + 2's M and S* (needed only while j + 2 < ns - 1)
+        if (j + 3 < ns) load_raw(j + 2, raw[(B3 + 2) % 3]);
+        // M_j as operand pairs (off the serial path: independent of the state)
+        Frag<T> mh[NKB], ml[NKB];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            const float4 a = raw[B3].m[kb][0], b = raw[B3].m[kb][1];
+            const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+            split8(x, mh[kb], ml[kb]);
+        }
+        __syncthreads();  // S_start(j) is complete in sS[B2]
+        const float *cur = sS[B2];
+        // S_start(j) in pi order over d, as operand pairs
+        Frag<T> bh[NKB], bl[NKB];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
             float x[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int d = 32 * kb + (e < 4 ? 4 * grp + e : 16 + 4 * grp + e - 4);
-                x[e] = sS[d * 17 + l16];
+                x[e] = cur[d * SP + l16];
             }
-            split8(x, Bh[kb], Bl[kb]);
+            split8(x, bh[kb], bl[kb]);
         }
-        // this wave's output tiles: rows 16 (wave * MT + t) ..
-        f32x4 acc[MT];
-        const float *sst = p.seg_sstar + ((int64_t)(gs0 + j) * p.H_v + h) * hstride;
+        f32x4 acc = {raw[B3].sst[0], raw[B3].sst[1], raw[B3].sst[2], raw[B3].sst[3]};
+        if (!(j == 0 && !p.h0)) {   // S_start(0) = 0: M_0 was not computed
 #pragma unroll
-        for (int t = 0; t < MT; ++t) {
-            const int m = wave * MT + t;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[t][r] = sst[(16 * m + 4 * grp + r) * DV + c0 + l16];
-            if (j == 0 && !p.h0) continue;  // S_start(0) = 0 (M_0 was not computed)
-#pragma unroll
-            for (int kb = 0; kb < DK / 32; ++kb) {
-                const Frag<T> ah = ld_pi(&sM[0][(16 * m + l16) * MP], kb);
-                if constexpr (NS == 2) {
-                    const Frag<T> al = ld_pi(&sM[1][(16 * m + l16) * MP], kb);
-                    mma_xx(acc[t], ah, al, Bh[kb], Bl[kb]);
-                } else {
-                    mma(acc[t], ah, Bh[kb]);
-                }
-            }
+            for (int kb = 0; kb < NKB; ++kb) mma_xx(acc, mh[kb], ml[kb], bh[kb], bl[kb]);
         }
-        __syncthreads();  // every wave has read S_start(j)
-        float *dst = const_cast<float *>(p.seg_start) + ((int64_t)(gs0 + j + 1) * p.H_v + h) * hstride;
+        float *nxt = sS[B2 ^ 1];
+        float *dst = p.seg_start + ((int64_t)(gs0 + j + 1) * p.H_v + h) * hstride;
 #pragma unroll
-        for (int t = 0; t < MT; ++t) {
-            const int m = wave * MT + t;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int d = 16 * m + 4 * grp + r;
-                sS[d * 17 + l16] = acc[t][r];
-                dst[d * DV + c0 + l16] = acc[t][r];
-            }
+        for (int r = 0; r < 4; ++r) {
+            const int d = 16 * m + 4 * grp + r;
+            nxt[d * SP + l16] = acc[r];
+            dst[d * DV + c0 + l16] = acc[r];
         }
+    };
+    // steps j = 0 .. ns - 2, unrolled by six so both parities are compile-time constants
+    for (int j = 0; j + 1 < ns; j += 6) {
+        step.template operator()<0, 0>(j);
+        if (j + 2 < ns) step.template operator()<1, 1>(j + 1);
+        if (j + 3 < ns) step.template operator()<0, 2>(j + 2);
+        if (j + 4 < ns) step.template operator()<1, 0>(j + 3);
+        if (j + 5 < ns) step.template operator()<0, 1>(j + 4);
+        if (j + 6 < ns) step.template operator()<1, 2>(j + 5);
     }
 }
 
@@ -783,7 +782,9 @@ hipError_t launch_cp_pre(int dtype, int D_k, int BV, int gate, const ChunkParams
                                       : launch_rec<1, 0>(dtype, D_k, BV, p, s);
 }
 hipError_t launch_cp_fix(int dtype, int D_k, const FixParams &p, hipStream_t s) {
-    const dim3 grid((unsigned)(p.N * p.H_v * (p.D_v / 16))), block(256);
+    // XCD-aware: blockIdx = ((unit / 8) * slices + slice) * 8 + unit % 8
+    const unsigned groups = (unsigned)((p.N * p.H_v + 7) / 8);
+    const dim3 grid(groups * 8u * (unsigned)(p.D_v / 16)), block((unsigned)(D_k * 4));
     if (p.N * p.H_v == 0) return hipSuccess;
     if (dtype == 1 && D_k == 128) hipLaunchKernelGGL((cp_fix_kernel<bf16, 128>), grid, block, 0, s, p);
     else if (dtype == 1 && D_k == 64) hipLaunchKernelGGL((cp_fix_kernel<bf16, 64>), grid, block, 0, s, p);
