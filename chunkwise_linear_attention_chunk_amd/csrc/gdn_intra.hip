@@ -107,27 +107,6 @@ __device__ __forceinline__ void store_unit_lower(const float *sX, T *A) {
     }
 }
 
-// P (fp32 [64][LP] in LDS, zero above the diagonal) to memory as NS tiles [64][64]: hi, then lo
-// for bf16 (hi the truncation, lo the rounded remainder), or the fp32 values.
-template <typename T>
-__device__ __forceinline__ void store_pair_tiles(const float *sP, T *P) {
-    constexpr int VEC = Vec16<T>::N, LP = 64 + 4;
-    for (int idx = threadIdx.x; idx < 64 * 64 / VEC; idx += 256) {
-        const int row = idx / (64 / VEC), c0 = (idx - row * (64 / VEC)) * VEC;
-        float x[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) x[e] = sP[row * LP + c0 + e];
-        if constexpr (Split<T>::parts == 2) {
-            Frag<bf16> hi, lo;
-            split8(x, hi, lo);
-            *reinterpret_cast<bf16x8 *>(P + row * 64 + c0) = hi.v;
-            *reinterpret_cast<bf16x8 *>(P + 4096 + row * 64 + c0) = lo.v;
-        } else {
-            *reinterpret_cast<u32x4 *>(P + row * 64 + c0) = *reinterpret_cast<const u32x4 *>(x);
-        }
-    }
-}
-
 // Store one 16x16 accumulator tile (lane: rows 4 grp + r, column l16) of P into the NS tiles
 // [64][64] at P (hi, then lo for bf16; fp32 whole).
 template <typename T>
@@ -304,15 +283,15 @@ __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
     constexpr int X_BYTES = 64 * LP * 4;
     constexpr int R0 = K_BYTES > X_BYTES ? K_BYTES : X_BYTES;
     constexpr int NS = Split<T>::parts;
-    // region 0: K tile, later the inverse X; region 1: Q tile, later P (fp32); region 2: A_raw
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * R0 + X_BYTES];
+    constexpr int NKB = DK / 32;
+    // region 0: K tile, later the inverse X; region 1: A_raw.  Q stays in registers: each thread's
+    // share for the gated output, and each lane's operand rows for P.
+    __shared__ __attribute__((aligned(16))) unsigned char smem[R0 + X_BYTES];
     __shared__ __attribute__((aligned(16))) float sG[64 * GP];
     __shared__ float sB[64];
     T *sK = reinterpret_cast<T *>(smem);
-    T *sQ = reinterpret_cast<T *>(smem + R0);
     float *sX = reinterpret_cast<float *>(smem);
-    float *sP = reinterpret_cast<float *>(smem + R0);
-    float *sL = reinterpret_cast<float *>(smem + 2 * R0);
+    float *sL = reinterpret_cast<float *>(smem + R0);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, grp = lane >> 4;
     const int ci = blockIdx.x / p.H_v, h = blockIdx.x - ci * p.H_v;
@@ -324,7 +303,16 @@ __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
     const T *g = static_cast<const T *>(p.g);
     const T *beta = static_cast<const T *>(p.beta);
 
-    // ---- K, Q tiles (clamped rows, tail masked at staging), gate columns, beta
+    // this wave's lower tiles t = wave, wave + 4, wave + 8 (< 10): (I, J) with J <= I
+    const int ntiles = wave < 2 ? 3 : 2;
+    int TI[3], TJ[3];
+#pragma unroll
+    for (int n = 0; n < 3; ++n) {
+        const int t = wave + 4 * n;
+        TI[n] = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
+        TJ[n] = t - TI[n] * (TI[n] + 1) / 2;
+    }
+    // ---- K tile (clamped rows, tail masked at staging), Q in registers, gate columns, beta
     constexpr int VPR = DK / VEC;
     constexpr int NV = 64 * VPR / 256;
     u32x4 kv[NV], qv[NV];
@@ -334,6 +322,14 @@ __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
         const int64_t off = ((int64_t)(t0 + row) * p.H_qk + hq) * DK + cv * VEC;
         kv[i] = *reinterpret_cast<const u32x4 *>(k + off);
         qv[i] = *reinterpret_cast<const u32x4 *>(q + off);
+    }
+    // Q operand rows of this lane's P tiles (row 16 I + l16, 8 columns per block)
+    Frag<T> qt[3][NKB];
+#pragma unroll
+    for (int n = 0; n < 3; ++n) {
+        const int row = min(16 * TI[n] + l16, last);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) qt[n][kb] = ld8(q + ((int64_t)(t0 + row) * p.H_qk + hq) * DK + 32 * kb + 8 * grp);
     }
     // thread (d, part) scans NT consecutive tokens of channel d
     constexpr int NPART = 256 / DK, NT = 64 / NPART;
@@ -355,7 +351,7 @@ __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
         const int idx = tid + 256 * i, row = idx / VPR, cv = idx % VPR;
         const u32x4 z = {0u, 0u, 0u, 0u};
         *reinterpret_cast<u32x4 *>(sK + row * KP + cv * VEC) = row < nv ? kv[i] : z;
-        *reinterpret_cast<u32x4 *>(sQ + row * KP + cv * VEC) = row < nv ? qv[i] : z;
+        if (row >= nv) qv[i] = z;
     }
 #pragma unroll
     for (int e = 0; e < NT; ++e) sG[(part * NT + e) * GP + d] = gs[e];
@@ -374,12 +370,13 @@ __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int idx = tid + 256 * i, row = idx / VPR, c0 = (idx % VPR) * VEC;
-        T vk[VEC];
+        T vk[VEC], qs[VEC];
         float xd[VEC], xq[VEC];
+        *reinterpret_cast<u32x4 *>(qs) = qv[i];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             const float G = sG[row * GP + c0 + e], GC = sG[last * GP + c0 + e];
-            const float kk = to_f32(sK[row * KP + c0 + e]), qq = to_f32(sQ[row * KP + c0 + e]);
+            const float kk = to_f32(sK[row * KP + c0 + e]), qq = to_f32(qs[e]);
             const float eg = fast_exp2(G);
             vk[e] = from_f32<T>(kk * eg);
             xq[e] = qq * eg;
@@ -404,19 +401,17 @@ __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
     if (tid < 64) gbk[GB_BETA + tid] = sB[tid];
 
     // ---- A_raw (strict lower) and P (lower with diagonal): the 10 lower 16x16 tiles
-    f32x4 pacc[3];
-    int ptile[3] = {-1, -1, -1};
+    T *P = static_cast<T *>(p.P) + ((int64_t)ci * p.H_v + h) * NS * 4096;
 #pragma unroll
     for (int n = 0; n < 3; ++n) {
-        const int t = wave + 4 * n;
-        if (t >= 10) break;
-        const int I = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
-        const int J = t - I * (I + 1) / 2;
+        if (n >= ntiles) break;
+        const int I = TI[n], J = TJ[n];
         const int r = J < I ? 16 * J + 15 : 16 * I;
         const int i = 16 * I + l16, j = 16 * J + l16;  // operand rows of this lane
+        const float qmask = i < nv ? 1.f : 0.f;
         f32x4 aa = {0.f, 0.f, 0.f, 0.f}, pa = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < DK / 32; ++kb) {
+        for (int kb = 0; kb < NKB; ++kb) {
             const int d0 = 32 * kb + 8 * grp;
             float kl[8], ql[8], kr[8];
 #pragma unroll
@@ -424,7 +419,7 @@ __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
                 const float gr = sG[r * GP + d0 + e];
                 const float el = fast_exp2(sG[i * GP + d0 + e] - gr), er = fast_exp2(gr - sG[j * GP + d0 + e]);
                 kl[e] = to_f32(sK[i * KP + d0 + e]) * el;
-                ql[e] = to_f32(sQ[i * KP + d0 + e]) * el;
+                ql[e] = qmask * to_f32(qt[n][kb].v[e]) * el;
                 kr[e] = to_f32(sK[j * KP + d0 + e]) * er;
             }
             Frag<T> fkl, fkr;
@@ -446,27 +441,14 @@ __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
             sL[ii * LP + jj] = jj < ii ? sB[ii] * aa[rr] : 0.f;
             pa[rr] = jj <= ii ? p.scale * pa[rr] : 0.f;
         }
-        pacc[n] = pa;
-        ptile[n] = t;
+        store_p_tile<T>(P, I, J, pa);
     }
-    __syncthreads();  // K and Q tiles are no longer read: their regions now hold X and P
-    // P tiles above the diagonal are zero
-    for (int idx = tid; idx < 64 * 64; idx += 256) {
-        const int row = idx >> 6, col = idx & 63;
-        if ((col >> 4) > (row >> 4)) sP[row * LP + col] = 0.f;
-    }
-#pragma unroll
-    for (int n = 0; n < 3; ++n) {
-        const int t = ptile[n];
-        if (t < 0) continue;
-        const int I = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
-        const int J = t - I * (I + 1) / 2;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) sP[(16 * I + 4 * grp + rr) * LP + 16 * J + l16] = pacc[n][rr];
-    }
-    invert_unit_lower(sL, sX);   // begins and ends with a barrier-complete LDS state
+    // the recurrence reads P row tile 0 over columns 0..31 and row tile 2 over 0..63: the upper
+    // tiles (0, 1) and (2, 3) must hold zeros (the others above the diagonal are never read)
+    if (wave >= 2) store_p_tile<T>(P, wave == 2 ? 0 : 2, wave == 2 ? 1 : 3, f32x4{0.f, 0.f, 0.f, 0.f});
+    __syncthreads();  // A_raw complete; the K tile is no longer read (its region now holds X)
+    invert_unit_lower(sL, sX);
     store_unit_lower<T>(sX, static_cast<T *>(p.A) + ((int64_t)ci * p.H_v + h) * 4096);
-    store_pair_tiles<T>(sP, static_cast<T *>(p.P) + ((int64_t)ci * p.H_v + h) * NS * 4096);
 }
 
 }  // namespace
