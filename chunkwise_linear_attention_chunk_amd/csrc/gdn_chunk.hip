@@ -100,6 +100,9 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanParams p) {
     }
 }
 
+// tile selections of the recurrence kernel's loads
+enum { LD_A = 1, LD_P = 2, LD_V = 4, LD_G = 8, LD_ALL = 15 };
+
 // ------------------------------------------------------------------------------------------
 // Recurrence + output.  One workgroup per (sequence segment, value head, NSUB slices of 16 value
 // columns); per slice a chain wave (waves 0 .. NSUB-1) and an output wave (waves NSUB .. 2 NSUB-1).
@@ -112,7 +115,8 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanParams p) {
 //            output: O += P V' (P = scale Lower(Gamma) (.) Q K^T from the per-chunk kernel), stored
 // The tiles of chunk c + 1 (K, Q, A, P, the V slice and the gate block of per-token gate rows, also
 // from the per-chunk kernel) stream into the other LDS buffer with direct-to-LDS loads meanwhile,
-// issued by the output waves between their Q S products, so the chain waves only compute.  Accumulator tiles
+// issued by the output waves between their Q S products, so the chain waves only compute (loads
+// issued by the chain waves measured slower: they delay its first products).  Accumulator tiles
 // feed the next product directly (pi order, gdn_device.h).  Rows past the end of a chunk read as
 // zero (buffer bounds) and carry beta = 0, g = 0, so X and V' vanish there; their outputs are not
 // stored.
@@ -138,7 +142,8 @@ struct RecLds {
     static constexpr int TILES = G0 + GB_FLOATS * 4;
     static constexpr int SXN = NSUB * NKB * NS * 64;   // state fragments handed to the output waves
     static constexpr int VXN = NSUB * 2 * NS * 64;     // V' fragments handed to the output waves
-    static constexpr int BYTES = NBUF * TILES + (OUT ? (SXN + VXN) * (int)sizeof(Frag<T>) : 0);
+    static constexpr int SON = OUT && ESZ == 2 ? NSUB * 64 * 16 : 1;   // bf16 output tile per output wave
+    static constexpr int BYTES = NBUF * TILES + (OUT ? (SXN + VXN) * (int)sizeof(Frag<T>) : 0) + SON * 2;
     static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
@@ -220,6 +225,7 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
     __shared__ __attribute__((aligned(16))) unsigned char tiles1[NBUF == 2 ? L::TILES : 16];
     __shared__ __attribute__((aligned(16))) Frag<T> sSx[OUT ? L::SXN : 1];
     __shared__ __attribute__((aligned(16))) Frag<T> sVx[OUT ? L::VXN : 1];
+    __shared__ __attribute__((aligned(16))) bf16 sO[L::SON];   // output rows re-laid for 16-byte stores
 
     // the wave index is uniform across a wave: readfirstlane makes the role branches scalar
     const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
@@ -317,9 +323,8 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
             }
         }
     };
-    // A, P, the V slice and the gate block:
-    auto issue_apvg = [&](int c, unsigned char *tb, int part_q, int np) __attribute__((always_inline)) {
-        if (!loader) return;
+    // A, P, the V slice and the gate block, as selected by `what` (LD_A | LD_P | LD_V | LD_G):
+    auto issue_apvg = [&](int c, unsigned char *tb, int part_q, int np, int what) __attribute__((always_inline)) {
         const int64_t tok = si.tok0 + (int64_t)(sg.c0 + c) * kChunk;
         const int nvc = nvalid(c);
         const int64_t gci = si.chunk0 + sg.c0 + c;   // global chunk index
@@ -330,14 +335,16 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
             const int i = sub + NL * j;
             if (j % np != part_q) continue;
             if (NAI * NL != L::AGPR && i >= L::AGPR) break;
-            buffer_granule_to_lds(rA, tb + L::A0 + 1024 * i, offA[j], 0);
+            if (what & LD_A) buffer_granule_to_lds(rA, tb + L::A0 + 1024 * i, offA[j], 0);
             if constexpr (OUT) {
+                if (what & LD_P) {
 #pragma unroll
-                for (int part = 0; part < L::NS; ++part)
-                    buffer_granule_to_lds(rP, tb + L::P0 + part * L::AT + 1024 * i, offA[j], part * 4096 * ESZ);
+                    for (int part = 0; part < L::NS; ++part)
+                        buffer_granule_to_lds(rP, tb + L::P0 + part * L::AT + 1024 * i, offA[j], part * 4096 * ESZ);
+                }
             }
         }
-        if (!mcols) {
+        if (!mcols && (what & LD_V)) {
             const auto rV = make_rsrc(vb + tok * v_stride, ((nvc - 1) * vs + BV) * ESZ);
 #pragma unroll
             for (int j = 0; j < NVI; ++j) {
@@ -347,7 +354,7 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
                 buffer_granule_to_lds(rV, tb + L::V0 + 1024 * i, offV[j], 0);
             }
         }
-        if (sub == 0 && part_q == 0)   // the gate block: 64 granules, one instruction
+        if ((what & LD_G) && sub == 0 && part_q == 0)   // the gate block: 64 granules, one instruction
             buffer_granule_to_lds(make_rsrc(Gb + gci * p.H_v * GB_FLOATS, GB_FLOATS * 4), tb + L::G0, lane * 16, 0);
     };
 
@@ -393,7 +400,7 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
             if (c > 0) {
                 __syncthreads();  // every wave is done with the single buffer
                 issue_kq(c, tiles0, 0, 1);
-                issue_apvg(c, tiles0, 0, 1);
+                if (loader) issue_apvg(c, tiles0, 0, 1, LD_ALL);
             }
         }
         const int nv = nvalid(c);
@@ -406,7 +413,7 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
         if constexpr (!OUT) {
             if (more) {
                 issue_kq(c + 1, tnext, 0, 1);
-                issue_apvg(c + 1, tnext, 0, 1);
+                issue_apvg(c + 1, tnext, 0, 1, LD_ALL);
             }
         }
         const unsigned char *tK = tcur + L::K0, *tQ = tcur + L::Q0, *tA = tcur + L::A0, *tV = tcur + L::V0;
@@ -513,7 +520,7 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
             for (int kb = 0; kb < NKB; ++kb) {
                 if (more) {                                   // 1/NKB of the loads per block
                     issue_kq(c + 1, tnext, kb, NKB);
-                    issue_apvg(c + 1, tnext, kb, NKB);
+                    issue_apvg(c + 1, tnext, kb, NKB, LD_ALL);
                 }
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
@@ -584,28 +591,47 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
                 for (int m = 2 * kb; m < 4; ++m) mma_xx(o[m], ph[m], pl[m], Vh[kb], Vl[kb]);
             }
             // buffer stores: the resource covers the chunk's valid rows only (rows past the end are
-            // dropped by the bounds check); row offsets are scalar, the lane offset is computed once
+            // dropped by the bounds check)
             const int64_t ebase = (int64_t)(si.tok0 + (sg.c0 + c) * kChunk) * v_stride + (int64_t)h * DV + c0;
             const int oes = p.o_f32 ? 4 : ESZ;
             const __amdgpu_buffer_rsrc_t ors = make_rsrc(static_cast<char *>(p.o) + ebase * oes,
                                                          ((nv - 1) * vs + BV) * oes);
-            const int vlane = ((4 * grp) * vs + 16 * sub + l16) * oes;
+            bool stored = false;
+            if constexpr (ESZ == 2) {
+                if (!p.o_f32) {
+                    // bf16: through this wave's LDS tile [64 rows][16 columns], then two 16-byte stores
+                    // per lane (half a row each); one wave writes and reads it, in order
+                    bf16 *so = sO + sub * 1024;
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
+                    for (int m = 0; m < 4; ++m)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int soff = (16 * m + r) * vs * oes;
-                    if (p.o_f32) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o[m][r]), ors, vlane, soff, 0);
-                    else if constexpr (ESZ == 2)
-                        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (bf16)o[m][r]), ors, vlane, soff, 0);
-                    else __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o[m][r]), ors, vlane, soff, 0);
+                        for (int r = 0; r < 4; ++r) so[(16 * m + 4 * grp + r) * 16 + l16] = (bf16)o[m][r];
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        const int qq = lane + 64 * i, row = qq >> 1, half = qq & 1;
+                        const u32x4 val = *reinterpret_cast<const u32x4 *>(so + row * 16 + 8 * half);
+                        __builtin_amdgcn_raw_buffer_store_b128(val, ors, (row * vs + 16 * sub + 8 * half) * 2, 0, 0);
+                    }
+                    stored = true;
                 }
+            }
+            if (!stored) {
+                // row offsets are scalar, the lane offset is computed once
+                const int vlane = ((4 * grp) * vs + 16 * sub + l16) * oes;
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int soff = (16 * m + r) * vs * oes;
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o[m][r]), ors, vlane, soff, 0);
+                    }
+            }
         }
     };
 
     if (nch > 0) {
         issue_kq(0, tiles0, 0, 1);
-        issue_apvg(0, tiles0, 0, 1);
+        if (loader) issue_apvg(0, tiles0, 0, 1, LD_ALL);
         if (chain) split_state();
     }
     for (int c = 0; c < nch; c += 2) {
