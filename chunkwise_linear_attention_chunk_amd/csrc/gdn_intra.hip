@@ -95,34 +95,63 @@ __device__ __forceinline__ void invert_unit_lower(const float *sL, float *sX) {
 template <typename T>
 __device__ __forceinline__ void store_unit_lower(const float *sX, T *A) {
     constexpr int VEC = Vec16<T>::N, LP = 64 + 4;
-    for (int idx = threadIdx.x; idx < 64 * 64 / VEC; idx += 256) {
+#pragma unroll
+    for (int it = 0; it < 64 * 64 / VEC / 256; ++it) {
+        const int idx = threadIdx.x + 256 * it;
         const int row = idx / (64 / VEC), c0 = (idx - row * (64 / VEC)) * VEC;
+        float x[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; e += 4) {
+            const float4 v = *reinterpret_cast<const float4 *>(sX + row * LP + c0 + e);
+            x[e] = v.x; x[e + 1] = v.y; x[e + 2] = v.z; x[e + 3] = v.w;
+        }
         T vals[VEC];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             const int col = c0 + e;
-            vals[e] = from_f32<T>(col < row ? sX[row * LP + col] : (col == row ? 1.f : 0.f));
+            vals[e] = from_f32<T>(col < row ? x[e] : (col == row ? 1.f : 0.f));
         }
         *reinterpret_cast<u32x4 *>(A + row * 64 + c0) = *reinterpret_cast<const u32x4 *>(vals);
     }
 }
 
-// Store one 16x16 accumulator tile (lane: rows 4 grp + r, column l16) of P into the NS tiles
-// [64][64] at P (hi, then lo for bf16; fp32 whole).
+// Store P from this wave's accumulator tiles (lane: rows 4 grp + r, column l16 of tile (ti, tj)):
+// staged through `stage` (LDS, at least parts * 8 KiB, free from the barrier at entry on) as the NS
+// tiles [64][64] of the output (hi, then lo for bf16; fp32 whole), then written with 16-byte stores.
+// Tiles above the diagonal are written as zeros.  Called by all 256 threads; returns after a
+// barrier, `stage` free again.
 template <typename T>
-__device__ __forceinline__ void store_p_tile(T *P, int ti, int tj, const f32x4 &acc) {
+__device__ __forceinline__ void store_p(void *stage, T *P, const f32x4 *pa, const int *ti, const int *tj, int ntiles) {
+    constexpr int NS = Split<T>::parts, VEC = Vec16<T>::N;
     const int lane = threadIdx.x & 63, l16 = lane & 15, grp = lane >> 4;
+    T *sp = static_cast<T *>(stage);
+    __syncthreads();  // every wave is done with the staging region's previous contents
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int off = (16 * ti + 4 * grp + r) * 64 + 16 * tj + l16;
-        if constexpr (Split<T>::parts == 2) {
-            const uint32_t bits = __float_as_uint(acc[r]) & 0xffff0000u;
-            P[off] = __builtin_bit_cast(bf16, (unsigned short)(bits >> 16));
-            P[4096 + off] = (bf16)(acc[r] - __uint_as_float(bits));
-        } else {
-            P[off] = from_f32<T>(acc[r]);
+    for (int n = 0; n < 3; ++n) {
+        if (n >= ntiles) break;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int off = (16 * ti[n] + 4 * grp + r) * 64 + 16 * tj[n] + l16;
+            const float x = pa[n][r];
+            if constexpr (NS == 2) {
+                const uint32_t bits = __float_as_uint(x) & 0xffff0000u;
+                sp[off] = __builtin_bit_cast(bf16, (unsigned short)(bits >> 16));
+                sp[4096 + off] = (bf16)(x - __uint_as_float(bits));
+            } else {
+                sp[off] = from_f32<T>(x);
+            }
         }
     }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < NS * 4096 / VEC / 256; ++it) {
+        const int idx = threadIdx.x + 256 * it;
+        const int e0 = idx * VEC, row = (e0 & 4095) >> 6, col = e0 & 63;
+        u32x4 v = *reinterpret_cast<const u32x4 *>(sp + e0);
+        if ((col >> 4) > (row >> 4)) v = u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4 *>(P + e0) = v;
+    }
+    __syncthreads();
 }
 
 // Scalar gate.  Besides A, the output's intra-chunk matrix P = scale Lower(Gamma) (.) Q K^T (mask
@@ -244,12 +273,9 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraParams p) {
             sL[i * LP + j] = (j < i) ? sB[i] * gam * aa[n][r] : 0.f;
             pa[n][r] = (j <= i) ? p.scale * gam * pa[n][r] : 0.f;
         }
-        store_p_tile<T>(P, TI[n], TJ[n], pa[n]);
     }
-    // the recurrence reads P row tile 0 over columns 0..31 and row tile 2 over 0..63: the upper
-    // tiles (0, 1) and (2, 3) must hold zeros (the others above the diagonal are never read)
-    if (wave >= 2) store_p_tile<T>(P, wave == 2 ? 0 : 2, wave == 2 ? 1 : 3, f32x4{0.f, 0.f, 0.f, 0.f});
-    __syncthreads();  // A_raw complete; the K tile is no longer read (its region now holds X)
+    // P through the K tile's region (no longer read), then A_raw is complete and the region holds X
+    store_p<T>(smem, P, pa, TI, TJ, ntiles);
 
     invert_unit_lower(sL, sX);
     store_unit_lower<T>(sX, static_cast<T *>(p.A) + ((int64_t)ci * p.H_v + h) * 4096);
@@ -402,6 +428,7 @@ __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
 
     // ---- A_raw (strict lower) and P (lower with diagonal): the 10 lower 16x16 tiles
     T *P = static_cast<T *>(p.P) + ((int64_t)ci * p.H_v + h) * NS * 4096;
+    f32x4 pacc[3];
 #pragma unroll
     for (int n = 0; n < 3; ++n) {
         if (n >= ntiles) break;
@@ -441,12 +468,10 @@ __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
             sL[ii * LP + jj] = jj < ii ? sB[ii] * aa[rr] : 0.f;
             pa[rr] = jj <= ii ? p.scale * pa[rr] : 0.f;
         }
-        store_p_tile<T>(P, I, J, pa);
+        pacc[n] = pa;
     }
-    // the recurrence reads P row tile 0 over columns 0..31 and row tile 2 over 0..63: the upper
-    // tiles (0, 1) and (2, 3) must hold zeros (the others above the diagonal are never read)
-    if (wave >= 2) store_p_tile<T>(P, wave == 2 ? 0 : 2, wave == 2 ? 1 : 3, f32x4{0.f, 0.f, 0.f, 0.f});
-    __syncthreads();  // A_raw complete; the K tile is no longer read (its region now holds X)
+    // P through the K tile's region (no longer read), then A_raw is complete and the region holds X
+    store_p<T>(smem, P, pacc, TI, TJ, ntiles);
     invert_unit_lower(sL, sX);
     store_unit_lower<T>(sX, static_cast<T *>(p.A) + ((int64_t)ci * p.H_v + h) * 4096);
 }
