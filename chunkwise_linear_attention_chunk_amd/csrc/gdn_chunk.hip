@@ -28,12 +28,21 @@ namespace {
 // One workgroup of 256 threads.
 // ------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void plan_kernel(PlanParams p) {
+    constexpr int kSortMax = 1024;   // segments ranked longest first (identity order beyond)
+    constexpr int kSeqMax = 4096;    // sequences whose chunk tables all threads fill together
     __shared__ int sC[256], sS[256];
+    __shared__ int sLen[kSortMax];
+    __shared__ int sChunk0[kSeqMax + 1], sTok0[kSeqMax], sSeqLen[kSeqMax];
     const int tid = threadIdx.x;
+    const bool sort = p.total_segs <= kSortMax;
+    const bool shared_fill = p.N <= kSeqMax;
     // every chunk entry starts empty (nv = 0: the intra kernel then reads nothing), every segment
     // entry empty and not last (it then writes no final state)
     for (int i = tid; i < p.total_chunks; i += 256) p.chunks[i] = ChunkInfo{0, 0};
-    for (int i = tid; i < p.total_segs; i += 256) p.segs[i] = SegInfo{0, 0, 0, 0, 0};
+    for (int i = tid; i < p.total_segs; i += 256) {
+        p.segs[i] = SegInfo{0, 0, 0, 0, 0};
+        if (sort) sLen[i] = 0;
+    }
     __syncthreads();
     int carry_c = 0, carry_s = 0;
     for (int base = 0; base < p.N; base += 256) {
@@ -64,35 +73,53 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanParams p) {
             const int chunk0 = min(carry_c + sC[tid] - nc, p.total_chunks);
             const int ncc = min(nc, p.total_chunks - chunk0);
             const int seg0 = min(carry_s + sS[tid] - ns, p.total_segs);
-            p.seq[n] = SeqInfo{tok0, min(len, ncc * kChunk), chunk0, ncc, seg0};
+            const SeqInfo si{tok0, min(len, ncc * kChunk), chunk0, ncc, seg0};
+            p.seq[n] = si;
+            if (shared_fill) {
+                sChunk0[n] = chunk0;
+                sTok0[n] = si.tok0;
+                sSeqLen[n] = si.len;
+                if (n == p.N - 1) sChunk0[p.N] = chunk0 + ncc;
+            } else {
+                for (int c = 0; c < si.nchunks; ++c) {
+                    const int rem = si.len - c * kChunk;
+                    p.chunks[si.chunk0 + c] = ChunkInfo{si.tok0 + c * kChunk, rem < kChunk ? rem : kChunk};
+                }
+            }
+            const int nseg = max(1, ceil_div(si.nchunks, p.seg_chunks));
+            for (int j = 0; j < nseg && si.seg0 + j < p.total_segs; ++j) {
+                const int c0 = j * p.seg_chunks, segn = max(0, min(p.seg_chunks, si.nchunks - c0));
+                p.segs[si.seg0 + j] = SegInfo{n, j, c0, segn, j == nseg - 1 ? 1 : 0};
+                if (sort) sLen[si.seg0 + j] = segn;
+            }
         }
         carry_c += sC[255];
         carry_s += sS[255];
         __syncthreads();
     }
-    __syncthreads();
-    for (int n = tid; n < p.N; n += 256) {
-        const SeqInfo si = p.seq[n];
-        for (int c = 0; c < si.nchunks; ++c) {
-            const int rem = si.len - c * kChunk;
-            p.chunks[si.chunk0 + c] = ChunkInfo{si.tok0 + c * kChunk, rem < kChunk ? rem : kChunk};
-        }
-        const int ns = max(1, ceil_div(si.nchunks, p.seg_chunks));
-        for (int j = 0; j < ns && si.seg0 + j < p.total_segs; ++j) {
-            const int c0 = j * p.seg_chunks;
-            p.segs[si.seg0 + j] = SegInfo{n, j, c0, max(0, min(p.seg_chunks, si.nchunks - c0)), j == ns - 1 ? 1 : 0};
+    // chunk table, all threads: chunk i belongs to the last sequence whose first chunk is <= i
+    // (empty sequences share their first chunk index with the next one and are skipped)
+    if (shared_fill) {
+        const int nchunks = sChunk0[p.N];
+        for (int i = tid; i < nchunks; i += 256) {
+            int lo = 0, hi = p.N - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (sChunk0[mid] <= i) lo = mid; else hi = mid - 1;
+            }
+            const int c = i - sChunk0[lo];
+            const int rem = sSeqLen[lo] - c * kChunk;
+            p.chunks[i] = ChunkInfo{sTok0[lo] + c * kChunk, rem < kChunk ? rem : kChunk};
         }
     }
-    __syncthreads();
-    // rank sort of the segments (longest first, ties by index); identity past 1024 segments
-    const bool sort = p.total_segs <= 1024;
+    // rank sort of the segments (longest first, ties by index) on the lengths held in LDS
     for (int g = tid; g < p.total_segs; g += 256) {
         int rank = g;
         if (sort) {
-            const int len = p.segs[g].nchunks;
+            const int len = sLen[g];
             rank = 0;
             for (int m = 0; m < p.total_segs; ++m) {
-                const int lm = p.segs[m].nchunks;
+                const int lm = sLen[m];
                 rank += (lm > len) || (lm == len && m < g);
             }
         }
