@@ -170,6 +170,47 @@ def test_kda_workload_sampled():
     check(x, TOL["bf16"], batches=[1], heads=[0, 31], label="kda_bf16 (sampled)")
 
 
+# --------------------------------------------------------------------------- D_k != D_v
+def _dims(x, dk, dv):
+    """Inputs of a D = 128 workload cut to key dim dk and value dim dv (q, k re-normalised over dk,
+    the per-channel gate cut with them); both sides of the comparison take the same tensors."""
+    y = dict(x)
+    for n in ("q", "k"):
+        a = x[n][..., :dk].double()
+        y[n] = (a / a.norm(dim=-1, keepdim=True)).to(x[n].dtype)
+    y["v"] = x["v"][..., :dv].contiguous()
+    if x["gate"] == "channel":
+        y["g"] = x["g"][..., :dk].contiguous()
+    if x["h0"] is not None:
+        y["h0"] = x["h0"][:, :, :dk, :dv].contiguous()
+    y["scale"] = float(dk) ** -0.5
+    return y
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 64), (64, 128)])
+@pytest.mark.parametrize("cp", ["off", "on"])
+def test_bf16_key_and_value_dims_differ(dk, dv, cp):
+    x = _dims(_w("qwen3next_bf16", B=2, H=2, T=64 * 7 + 21, h0=True, mu=-7.0, seed=200 + dk), dk, dv)
+    check(x, TOL["bf16"], label=f"bf16 D_k={dk} D_v={dv} CP {cp}", cp_mode=cp, cp_segment_chunks=2)
+
+
+def test_fp32_key_and_value_dims_differ():
+    x = _dims(_w("tiny_fp32", T=300, H=2, D=128, h0=True, seed=210), 128, 64)
+    check(x, TOL["fp32"], label="fp32 D_k=128 D_v=64")
+
+
+def test_kda_key_and_value_dims_differ():
+    x = _dims(_w("kda_bf16", B=1, H=2, T=400, h0=True, seed=220), 64, 128)
+    check(x, TOL["bf16"], label="KDA bf16 D_k=64 D_v=128")
+
+
+def test_empty_sequence_returns_initial_state():
+    x = _w("qwen3next_bf16", B=2, H=2, T=0, h0=True, seed=230)
+    o, fs = gpu_run(x)
+    assert o.numel() == 0
+    assert torch.equal(fs, x["h0"])
+
+
 # --------------------------------------------------------------------------- properties
 def test_deterministic():
     x = _w("qwen3next_bf16", B=1, H=4, T=700, h0=True, seed=21)
