@@ -386,20 +386,9 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
     };
 
     // ---- chain state: S [DK][16] of this slice in fp32 accumulator tiles (rows 16m + 4grp + r)
-    //      main pass: h0 (first segment) or the fixed-up start state; pre-process: 0 or identity
+    //      main pass: h0 (first segment) or the fixed-up start state; pre-process: 0 or identity.
+    //      Set up by the chain waves only (below).
     f32x4 S[MD];
-    const float *s_init = nullptr;
-    if constexpr (OUT) {
-        s_init = sg.j == 0 ? (p.h0 ? p.h0 + ((int64_t)n * p.H_v + h) * DK * DV : nullptr)
-                           : p.seg_start + ((int64_t)gs * p.H_v + h) * DK * DV;
-    }
-#pragma unroll
-    for (int m = 0; m < MD; ++m)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int d = 16 * m + 4 * grp + r;
-            S[m][r] = (chain && s_init) ? s_init[d * DV + col] : (mcols && d == col) ? 1.f : 0.f;
-        }
 
     // ---- the entering state of the next chunk as matrix-core operand pairs (pi order over rows),
     //      handed to the output waves through LDS.  Formed at the end of each chunk, in the time the
@@ -419,251 +408,298 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
         }
     };
 
-    // ---- one chunk; B = tile buffer holding it (compile time)
-    auto step = [&]<int B>(int c) __attribute__((always_inline)) {
-        unsigned char *tcur = B == 0 ? tiles0 : tiles1;
-        unsigned char *tnext = B == 0 ? tiles1 : tiles0;
+    // ---- the start of chunk c: with one tile buffer, every wave is done with it before the loader
+    //      waves refill it; the loaders wait for their direct-to-LDS loads of chunk c (vmcnt(0), gfx9
+    //      encoding: vmcnt bits [3:0],[15:14] = 0, expcnt [6:4] and lgkmcnt [11:8] at their maxima),
+    //      and the barrier makes the tiles, the gate block and S_c visible to every wave.  Both roles
+    //      below pass the same barriers in the same order.
+    auto chunk_top = [&]<bool LD>(int c) __attribute__((always_inline)) {
         if constexpr (NBUF == 1) {
             if (c > 0) {
-                __syncthreads();  // every wave is done with the single buffer
-                issue_kq(c, tiles0, 0, 1);
-                if (loader) issue_apvg(c, tiles0, 0, 1, LD_ALL);
+                __syncthreads();
+                if constexpr (LD) {
+                    issue_kq(c, tiles0, 0, 1);
+                    issue_apvg(c, tiles0, 0, 1, LD_ALL);
+                }
             }
         }
-        const int nv = nvalid(c);
+        if constexpr (LD) __builtin_amdgcn_s_waitcnt(0x0f70);
+        __syncthreads();
+    };
+
+    // ---- output role (main pass): streams the tiles of the next chunk into LDS and forms
+    //      O = scale diag(gamma) Q S_c + P V' of its 16 columns.  Its own loop, so that none of the
+    //      chain's registers (the state, its operand pairs) are live here and vice versa.
+    if constexpr (OUT) {
+        if (!chain) {
+            auto out_step = [&]<int B>(int c) __attribute__((always_inline)) {
+                unsigned char *tcur = B == 0 ? tiles0 : tiles1;
+                unsigned char *tnext = B == 0 ? tiles1 : tiles0;
+                chunk_top.template operator()<true>(c);
+                const int nv = nvalid(c);
+                const float *g3 = reinterpret_cast<const float *>(tcur + L::G0);
+                const bool more = NBUF == 2 && c + 1 < nch;               // stream chunk c + 1 meanwhile
+                const unsigned char *tQ = tcur + L::Q0, *tP = tcur + L::P0, *tQl = tcur + L::QL0;
+                f32x4 o[4];
+
+                // inter-chunk part: scale diag(gamma) Q S_c (S_c was handed over before this chunk)
+                const Frag<T> *sxs = sSx + (sub * NKB * L::NS) * 64 + lane;
+                // the state and Q fragments first (the Q lo parts of per-channel gates as they are used)
+                Frag<T> sh[NKB], sl[NKB], qf[NKB][4];
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+                    sh[kb] = sxs[kb * L::NS * 64];
+                    if constexpr (L::NS == 2) sl[kb] = sxs[kb * L::NS * 64 + 64];
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) qf[kb][m] = ldpi_tile<T, L::KGPR>(tQ, 16 * m + l16, kb);
+                }
+#pragma unroll
+                for (int m = 0; m < 4; ++m) o[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+                    if (more) {                                   // 1/NKB of the loads per block
+                        issue_kq(c + 1, tnext, kb, NKB);
+                        issue_apvg(c + 1, tnext, kb, NKB, LD_ALL);
+                    }
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        if constexpr (CH && L::NS == 2)
+                            mma_xx(o[m], qf[kb][m], ldpi_tile<T, L::KGPR>(tQl, 16 * m + l16, kb), sh[kb], sl[kb]);
+                        else
+                            mma_x(o[m], qf[kb][m], sh[kb], sl[kb]);
+                    }
+                }
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    if constexpr (CH) {
+                        o[m] *= p.scale;
+                    } else {
+                        const float4 sgm = *reinterpret_cast<const float4 *>(g3 + GB_SGAM + 16 * m + 4 * grp);
+                        o[m][0] *= sgm.x; o[m][1] *= sgm.y; o[m][2] *= sgm.z; o[m][3] *= sgm.w;
+                    }
+                }
+                lds_only_barrier();  // V' of chunk c is visible
+
+                const Frag<T> *vxs = sVx + (sub * 2 * L::NS) * 64 + lane;
+                Frag<T> Vh[2], Vl[2];
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    Vh[kb] = vxs[kb * L::NS * 64];
+                    if constexpr (L::NS == 2) Vl[kb] = vxs[kb * L::NS * 64 + 64];
+                }
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    Frag<T> ph[4], pl[4];
+#pragma unroll
+                    for (int m = 2 * kb; m < 4; ++m) {
+                        ph[m] = ldpi_tile<T, L::AGPR>(tP, 16 * m + l16, kb);
+                        if constexpr (L::NS == 2) pl[m] = ldpi_tile<T, L::AGPR>(tP + L::AT, 16 * m + l16, kb);
+                    }
+#pragma unroll
+                    for (int m = 2 * kb; m < 4; ++m) mma_xx(o[m], ph[m], pl[m], Vh[kb], Vl[kb]);
+                }
+                // buffer stores: the resource covers the chunk's valid rows only (rows past the end are
+                // dropped by the bounds check)
+                const int64_t ebase = (int64_t)(si.tok0 + (sg.c0 + c) * kChunk) * v_stride + (int64_t)h * DV + c0;
+                const int oes = p.o_f32 ? 4 : ESZ;
+                const __amdgpu_buffer_rsrc_t ors = make_rsrc(static_cast<char *>(p.o) + ebase * oes,
+                                                             ((nv - 1) * vs + BV) * oes);
+                bool stored = false;
+                if constexpr (ESZ == 2) {
+                    if (!p.o_f32) {
+                        // bf16: through this wave's LDS tile [64 rows][16 columns], then two 16-byte stores
+                        // per lane (half a row each); one wave writes and reads it, in order
+                        bf16 *so = sO + sub * 1024;
+#pragma unroll
+                        for (int m = 0; m < 4; ++m)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) so[(16 * m + 4 * grp + r) * 16 + l16] = (bf16)o[m][r];
+#pragma unroll
+                        for (int i = 0; i < 2; ++i) {
+                            const int qq = lane + 64 * i, row = qq >> 1, half = qq & 1;
+                            const u32x4 val = *reinterpret_cast<const u32x4 *>(so + row * 16 + 8 * half);
+                            __builtin_amdgcn_raw_buffer_store_b128(val, ors, (row * vs + 16 * sub + 8 * half) * 2, 0, 0);
+                        }
+                        stored = true;
+                    }
+                }
+                if (!stored) {
+                    // row offsets are scalar, the lane offset is computed once
+                    const int vlane = ((4 * grp) * vs + 16 * sub + l16) * oes;
+#pragma unroll
+                    for (int m = 0; m < 4; ++m)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int soff = (16 * m + r) * vs * oes;
+                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o[m][r]), ors, vlane, soff, 0);
+                        }
+                }
+            };
+            if (nch > 0) {
+                issue_kq(0, tiles0, 0, 1);
+                issue_apvg(0, tiles0, 0, 1, LD_ALL);
+            }
+            for (int c = 0; c < nch; c += 2) {
+                out_step.template operator()<0>(c);
+                if (c + 1 < nch) out_step.template operator()<NBUF == 2 ? 1 : 0>(c + 1);
+            }
+            return;
+        }
+    }
+
+    // ---- chain role: the state recurrence (in the pre-process the chain waves also load the tiles)
+    {
+        const float *s_init = nullptr;
+        if constexpr (OUT) {
+            s_init = sg.j == 0 ? (p.h0 ? p.h0 + ((int64_t)n * p.H_v + h) * DK * DV : nullptr)
+                               : p.seg_start + ((int64_t)gs * p.H_v + h) * DK * DV;
+        }
+#pragma unroll
+        for (int m = 0; m < MD; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int d = 16 * m + 4 * grp + r;
+                S[m][r] = s_init ? s_init[d * DV + col] : (mcols && d == col) ? 1.f : 0.f;
+            }
+    }
+    auto chain_step = [&]<int B>(int c) __attribute__((always_inline)) {
+        unsigned char *tcur = B == 0 ? tiles0 : tiles1;
+        unsigned char *tnext = B == 0 ? tiles1 : tiles0;
+        chunk_top.template operator()<!OUT>(c);
         const float *g3 = reinterpret_cast<const float *>(tcur + L::G0);
-        // vmcnt(0) (gfx9 encoding: vmcnt bits [3:0],[15:14] = 0; expcnt [6:4] and lgkmcnt [11:8]
-        // left at their maxima): this wave's direct-to-LDS loads of chunk c have landed
-        __builtin_amdgcn_s_waitcnt(0x0f70);
-        __syncthreads();  // tiles, gate rows and S_c of chunk c are visible
-        const bool more = NBUF == 2 && c + 1 < nch;                   // stream chunk c + 1 meanwhile
+        const bool more = NBUF == 2 && c + 1 < nch;
         if constexpr (!OUT) {
             if (more) {
                 issue_kq(c + 1, tnext, 0, 1);
                 issue_apvg(c + 1, tnext, 0, 1, LD_ALL);
             }
         }
-        const unsigned char *tK = tcur + L::K0, *tQ = tcur + L::Q0, *tA = tcur + L::A0, *tV = tcur + L::V0;
-        const unsigned char *tKd = CH ? tcur + L::KD0 : tK, *tP = tcur + L::P0, *tQl = tcur + L::QL0;
+        const unsigned char *tK = tcur + L::K0, *tA = tcur + L::A0, *tV = tcur + L::V0;
+        const unsigned char *tKd = CH ? tcur + L::KD0 : tK;
         // =========================== phase 1 ===========================
-        Frag<T> Wh[2], Wl[2];          // chain: V'' (pi order over tokens)
-        Frag<T> kt[2][MD];             // chain: the K^T fragments of the state update, read early
-        f32x4 o[4];                    // output: O of this wave's 16 columns
-        if (chain) {
-            // this lane's V values and gate rows first, so their LDS latency hides behind K S
-            float v[4][4], b4[4][4], ga[4][4];
+        Frag<T> Wh[2], Wl[2];          // V'' (pi order over tokens)
+        Frag<T> kt[2][MD];             // the K^T fragments of the state update, read early
+
+        // this lane's V values and gate rows first, so their LDS latency hides behind K S
+        float v[4][4], b4[4][4], ga[4][4];
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
+        for (int m = 0; m < 4; ++m) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) { v[m][r] = 0.f; ga[m][r] = 1.f; }
-                if (!mcols) ld_vcol4<T, L::VGPR>(tV, m, 16 * sub, v[m]);
-                const float4 be = *reinterpret_cast<const float4 *>(g3 + GB_BETA + 16 * m + 4 * grp);
-                b4[m][0] = be.x; b4[m][1] = be.y; b4[m][2] = be.z; b4[m][3] = be.w;
-                if constexpr (!CH) {
-                    const float4 gg = *reinterpret_cast<const float4 *>(g3 + GB_GAM + 16 * m + 4 * grp);
-                    ga[m][0] = gg.x; ga[m][1] = gg.y; ga[m][2] = gg.z; ga[m][3] = gg.w;
-                }
-            }
-            // every K and A fragment of the chunk's products is read up front, so the reads overlap
-            // each other and the first products instead of each waiting in turn
-            Frag<T> kf[NKB][4], af[6];
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int m = 0; m < 4; ++m) kf[kb][m] = ldpi_tile<T, L::KGPR>(tK, 16 * m + l16, kb);
-#pragma unroll
-            for (int f = 0; f < 6; ++f) {
-                const int m = f < 4 ? f : f - 2, kb = f < 4 ? 0 : 1;   // (m, kb): (0..3, 0), (2, 1), (3, 1)
-                af[f] = ldpi_tile<T, L::AGPR>(tA, 16 * m + l16, kb);
-            }
-            // K S: contraction block outer, the four row tiles inner (independent accumulators)
-            f32x4 ks[4];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) ks[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int m = 0; m < 4; ++m) mma_x(ks[m], kf[kb][m], Sh[kb], Sl[kb]);
-            f32x4 xx[4];
-#pragma unroll
-            for (int m = 0; m < 4; ++m)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) xx[m][r] = b4[m][r] * (v[m][r] - ga[m][r] * ks[m][r]);
-            Frag<T> Xh[2], Xl[2];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                float x[8];
-                pack_pi(xx[2 * kb], xx[2 * kb + 1], x);
-                split8(x, Xh[kb], Xl[kb]);
-            }
-            // V' = A X (A lower triangular: row tile m needs contraction blocks kb <= m / 2)
-            f32x4 vp[4];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) vp[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int f = 0; f < 6; ++f) {
-                const int m = f < 4 ? f : f - 2, kb = f < 4 ? 0 : 1;
-                mma_x(vp[m], af[f], Xh[kb], Xl[kb]);
-            }
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                float x[8];
-                pack_pi(vp[2 * kb], vp[2 * kb + 1], x);
-                Frag<T> vh, vl;
-                split8(x, vh, vl);
-                if constexpr (OUT) {
-                    Frag<T> *dst = sVx + ((sub * 2 + kb) * L::NS) * 64 + lane;
-                    dst[0] = vh;
-                    if constexpr (L::NS == 2) dst[64] = vl;
-                }
-                if constexpr (!CH) {
-                    const float4 s0 = *reinterpret_cast<const float4 *>(g3 + GB_SC + 32 * kb + 4 * grp);
-                    const float4 s1 = *reinterpret_cast<const float4 *>(g3 + GB_SC + 32 * kb + 16 + 4 * grp);
-                    x[0] *= s0.x; x[1] *= s0.y; x[2] *= s0.z; x[3] *= s0.w;
-                    x[4] *= s1.x; x[5] *= s1.y; x[6] *= s1.z; x[7] *= s1.w;
-                }
-                split8(x, Wh[kb], Wl[kb]);
-            }
-            // the state update's K^T fragments, read while the output waves finish phase 1
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int m = 0; m < MD; ++m) kt[kb][m] = ldpi_col_tile<T, L::KGPR>(tKd, 16 * m, kb);
-        } else if constexpr (OUT) {
-            // inter-chunk part: scale diag(gamma) Q S_c (S_c was handed over before this chunk)
-            const Frag<T> *sxs = sSx + (sub * NKB * L::NS) * 64 + lane;
-            // the state and Q fragments first (the Q lo parts of per-channel gates as they are used)
-            Frag<T> sh[NKB], sl[NKB], qf[NKB][4];
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                sh[kb] = sxs[kb * L::NS * 64];
-                if constexpr (L::NS == 2) sl[kb] = sxs[kb * L::NS * 64 + 64];
-#pragma unroll
-                for (int m = 0; m < 4; ++m) qf[kb][m] = ldpi_tile<T, L::KGPR>(tQ, 16 * m + l16, kb);
-            }
-#pragma unroll
-            for (int m = 0; m < 4; ++m) o[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                if (more) {                                   // 1/NKB of the loads per block
-                    issue_kq(c + 1, tnext, kb, NKB);
-                    issue_apvg(c + 1, tnext, kb, NKB, LD_ALL);
-                }
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    if constexpr (CH && L::NS == 2)
-                        mma_xx(o[m], qf[kb][m], ldpi_tile<T, L::KGPR>(tQl, 16 * m + l16, kb), sh[kb], sl[kb]);
-                    else
-                        mma_x(o[m], qf[kb][m], sh[kb], sl[kb]);
-                }
-            }
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                if constexpr (CH) {
-                    o[m] *= p.scale;
-                } else {
-                    const float4 sgm = *reinterpret_cast<const float4 *>(g3 + GB_SGAM + 16 * m + 4 * grp);
-                    o[m][0] *= sgm.x; o[m][1] *= sgm.y; o[m][2] *= sgm.z; o[m][3] *= sgm.w;
-                }
+            for (int r = 0; r < 4; ++r) { v[m][r] = 0.f; ga[m][r] = 1.f; }
+            if (!mcols) ld_vcol4<T, L::VGPR>(tV, m, 16 * sub, v[m]);
+            const float4 be = *reinterpret_cast<const float4 *>(g3 + GB_BETA + 16 * m + 4 * grp);
+            b4[m][0] = be.x; b4[m][1] = be.y; b4[m][2] = be.z; b4[m][3] = be.w;
+            if constexpr (!CH) {
+                const float4 gg = *reinterpret_cast<const float4 *>(g3 + GB_GAM + 16 * m + 4 * grp);
+                ga[m][0] = gg.x; ga[m][1] = gg.y; ga[m][2] = gg.z; ga[m][3] = gg.w;
             }
         }
+        // every K and A fragment of the chunk's products is read up front, so the reads overlap
+        // each other and the first products instead of each waiting in turn
+        Frag<T> kf[NKB][4], af[6];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) kf[kb][m] = ldpi_tile<T, L::KGPR>(tK, 16 * m + l16, kb);
+#pragma unroll
+        for (int f = 0; f < 6; ++f) {
+            const int m = f < 4 ? f : f - 2, kb = f < 4 ? 0 : 1;   // (m, kb): (0..3, 0), (2, 1), (3, 1)
+            af[f] = ldpi_tile<T, L::AGPR>(tA, 16 * m + l16, kb);
+        }
+        // K S: contraction block outer, the four row tiles inner (independent accumulators)
+        f32x4 ks[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) ks[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) mma_x(ks[m], kf[kb][m], Sh[kb], Sl[kb]);
+        f32x4 xx[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) xx[m][r] = b4[m][r] * (v[m][r] - ga[m][r] * ks[m][r]);
+        Frag<T> Xh[2], Xl[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            float x[8];
+            pack_pi(xx[2 * kb], xx[2 * kb + 1], x);
+            split8(x, Xh[kb], Xl[kb]);
+        }
+        // V' = A X (A lower triangular: row tile m needs contraction blocks kb <= m / 2)
+        f32x4 vp[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) vp[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int f = 0; f < 6; ++f) {
+            const int m = f < 4 ? f : f - 2, kb = f < 4 ? 0 : 1;
+            mma_x(vp[m], af[f], Xh[kb], Xl[kb]);
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            float x[8];
+            pack_pi(vp[2 * kb], vp[2 * kb + 1], x);
+            Frag<T> vh, vl;
+            split8(x, vh, vl);
+            if constexpr (OUT) {
+                Frag<T> *dst = sVx + ((sub * 2 + kb) * L::NS) * 64 + lane;
+                dst[0] = vh;
+                if constexpr (L::NS == 2) dst[64] = vl;
+            }
+            if constexpr (!CH) {
+                const float4 s0 = *reinterpret_cast<const float4 *>(g3 + GB_SC + 32 * kb + 4 * grp);
+                const float4 s1 = *reinterpret_cast<const float4 *>(g3 + GB_SC + 32 * kb + 16 + 4 * grp);
+                x[0] *= s0.x; x[1] *= s0.y; x[2] *= s0.z; x[3] *= s0.w;
+                x[4] *= s1.x; x[5] *= s1.y; x[6] *= s1.z; x[7] *= s1.w;
+            }
+            split8(x, Wh[kb], Wl[kb]);
+        }
+        // the state update's K^T fragments, read while the output waves finish phase 1
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int m = 0; m < MD; ++m) kt[kb][m] = ldpi_col_tile<T, L::KGPR>(tKd, 16 * m, kb);
         if constexpr (OUT) lds_only_barrier();  // V' of chunk c is visible to the output waves
-
         // =========================== phase 2 ===========================
-        if (chain) {
-            float4 dec[MD];
-#pragma unroll
-            for (int m = 0; m < MD; ++m) {
-                if constexpr (CH) dec[m] = *reinterpret_cast<const float4 *>(g3 + GB_DEC + 16 * m + 4 * grp);
-                else dec[m] = make_float4(g3[GB_GAM + 63], g3[GB_GAM + 63], g3[GB_GAM + 63], g3[GB_GAM + 63]);
-            }
-#pragma unroll
-            for (int m = 0; m < MD; ++m) {
-                S[m][0] *= dec[m].x; S[m][1] *= dec[m].y; S[m][2] *= dec[m].z; S[m][3] *= dec[m].w;
-            }
-            // S += K^T V'': contraction block outer, the row tiles inner
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int m0 = 0; m0 < MD; m0 += 4) {
-                    Frag<T> kl[4];
-                    if constexpr (CH && L::NS == 2) {
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) kl[u] = ldpi_col_tile<T, L::KGPR>(tKd + L::KT, 16 * (m0 + u), kb);
-                    }
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        if constexpr (CH && L::NS == 2) mma_xx(S[m0 + u], kt[kb][m0 + u], kl[u], Wh[kb], Wl[kb]);
-                        else mma_x(S[m0 + u], kt[kb][m0 + u], Wh[kb], Wl[kb]);
-                    }
-                }
-            split_state();  // S_{c+1} for the next chunk (the output waves read S_c before the barrier)
-        } else if constexpr (OUT) {
-            const Frag<T> *vxs = sVx + (sub * 2 * L::NS) * 64 + lane;
-            Frag<T> Vh[2], Vl[2];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                Vh[kb] = vxs[kb * L::NS * 64];
-                if constexpr (L::NS == 2) Vl[kb] = vxs[kb * L::NS * 64 + 64];
-            }
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                Frag<T> ph[4], pl[4];
-#pragma unroll
-                for (int m = 2 * kb; m < 4; ++m) {
-                    ph[m] = ldpi_tile<T, L::AGPR>(tP, 16 * m + l16, kb);
-                    if constexpr (L::NS == 2) pl[m] = ldpi_tile<T, L::AGPR>(tP + L::AT, 16 * m + l16, kb);
-                }
-#pragma unroll
-                for (int m = 2 * kb; m < 4; ++m) mma_xx(o[m], ph[m], pl[m], Vh[kb], Vl[kb]);
-            }
-            // buffer stores: the resource covers the chunk's valid rows only (rows past the end are
-            // dropped by the bounds check)
-            const int64_t ebase = (int64_t)(si.tok0 + (sg.c0 + c) * kChunk) * v_stride + (int64_t)h * DV + c0;
-            const int oes = p.o_f32 ? 4 : ESZ;
-            const __amdgpu_buffer_rsrc_t ors = make_rsrc(static_cast<char *>(p.o) + ebase * oes,
-                                                         ((nv - 1) * vs + BV) * oes);
-            bool stored = false;
-            if constexpr (ESZ == 2) {
-                if (!p.o_f32) {
-                    // bf16: through this wave's LDS tile [64 rows][16 columns], then two 16-byte stores
-                    // per lane (half a row each); one wave writes and reads it, in order
-                    bf16 *so = sO + sub * 1024;
-#pragma unroll
-                    for (int m = 0; m < 4; ++m)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) so[(16 * m + 4 * grp + r) * 16 + l16] = (bf16)o[m][r];
-#pragma unroll
-                    for (int i = 0; i < 2; ++i) {
-                        const int qq = lane + 64 * i, row = qq >> 1, half = qq & 1;
-                        const u32x4 val = *reinterpret_cast<const u32x4 *>(so + row * 16 + 8 * half);
-                        __builtin_amdgcn_raw_buffer_store_b128(val, ors, (row * vs + 16 * sub + 8 * half) * 2, 0, 0);
-                    }
-                    stored = true;
-                }
-            }
-            if (!stored) {
-                // row offsets are scalar, the lane offset is computed once
-                const int vlane = ((4 * grp) * vs + 16 * sub + l16) * oes;
-#pragma unroll
-                for (int m = 0; m < 4; ++m)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int soff = (16 * m + r) * vs * oes;
-                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o[m][r]), ors, vlane, soff, 0);
-                    }
-            }
-        }
-    };
 
+        float4 dec[MD];
+#pragma unroll
+        for (int m = 0; m < MD; ++m) {
+            if constexpr (CH) dec[m] = *reinterpret_cast<const float4 *>(g3 + GB_DEC + 16 * m + 4 * grp);
+            else dec[m] = make_float4(g3[GB_GAM + 63], g3[GB_GAM + 63], g3[GB_GAM + 63], g3[GB_GAM + 63]);
+        }
+#pragma unroll
+        for (int m = 0; m < MD; ++m) {
+            S[m][0] *= dec[m].x; S[m][1] *= dec[m].y; S[m][2] *= dec[m].z; S[m][3] *= dec[m].w;
+        }
+        // S += K^T V'': contraction block outer, the row tiles inner
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int m0 = 0; m0 < MD; m0 += 4) {
+                Frag<T> kl[4];
+                if constexpr (CH && L::NS == 2) {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) kl[u] = ldpi_col_tile<T, L::KGPR>(tKd + L::KT, 16 * (m0 + u), kb);
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    if constexpr (CH && L::NS == 2) mma_xx(S[m0 + u], kt[kb][m0 + u], kl[u], Wh[kb], Wl[kb]);
+                    else mma_x(S[m0 + u], kt[kb][m0 + u], Wh[kb], Wl[kb]);
+                }
+            }
+        split_state();  // S_{c+1} for the next chunk (the output waves read S_c before the barrier)
+    };
     if (nch > 0) {
-        issue_kq(0, tiles0, 0, 1);
-        if (loader) issue_apvg(0, tiles0, 0, 1, LD_ALL);
-        if (chain) split_state();
+        if constexpr (!OUT) {
+            issue_kq(0, tiles0, 0, 1);
+            issue_apvg(0, tiles0, 0, 1, LD_ALL);
+        }
+        split_state();
     }
     for (int c = 0; c < nch; c += 2) {
-        step.template operator()<0>(c);
-        if (c + 1 < nch) step.template operator()<NBUF == 2 ? 1 : 0>(c + 1);
+        chain_step.template operator()<0>(c);
+        if (c + 1 < nch) chain_step.template operator()<NBUF == 2 ? 1 : 0>(c + 1);
     }
 
     // ---- end of the segment: final state (main pass, last segment) or the segment's maps
