@@ -7,9 +7,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgdn.so")
 SOURCES = ["gdn_api.hip", "gdn_intra.hip", "gdn_chunk.hip"]
-# Packed fp32 VALU ops are kept out of the generated code on purpose.
+# Packed fp32 VALU ops are kept out of the generated code on purpose.  Matrix-core results stay in
+# ordinary VGPRs (the recurrence reads and rescales them with vector ALU ops every chunk; the
+# accumulation registers would cost a copy each way).
 HIPFLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC", "-Wall",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             ]
 
 
