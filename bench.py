@@ -73,7 +73,7 @@ def algorithmic_bytes(x, esz):
 def stage_algorithmic_bytes(stage, x, esz, plan):
     """Compulsory bytes of one launch of a stage's kernel: the op's inputs it must read (and outputs
     it must write), each counted once.
-      intra  (per-chunk kernel): q, k, the gate and beta;
+      intra  (per-chunk kernel): k, the gate and beta (and q with per-channel gates, whose P it forms);
       chunk  (recurrence + output): q, k, v, gate, beta, h0 in; o and the final state out;
       cp_pre (segment maps): k, v, gate and beta of the tokens in segments that are not a
              sequence's last (the last segment's maps are never formed)."""
@@ -82,7 +82,8 @@ def stage_algorithmic_bytes(stage, x, esz, plan):
     gate_per_token = g.numel() // (q.shape[0] * q.shape[1]) * g.element_size()
     if stage == "intra":
         tokens = q.shape[0] * q.shape[1]
-        return tokens * (2 * H_qk * D_k * esz + gate_per_token + H_v * esz)
+        qk = 2 if g.dim() == 4 else 1
+        return tokens * (qk * H_qk * D_k * esz + gate_per_token + H_v * esz)
     if stage == "cp_pre":
         sl = plan["segment_chunks"]
         if x["cu_seqlens"] is None:

@@ -162,7 +162,9 @@ gdn_status validate_and_plan(const gdn_fwd_args *a, Plan *pl) {
     pl->off_segs = off;   off = align_up(off + (size_t)pl->total_segs * sizeof(gdn::SegInfo));
     pl->off_order = off;  off = align_up(off + (size_t)pl->total_segs * sizeof(int));
     const size_t tiles = (size_t)nch * a->H_v;
-    pl->off_P = off;       off = align_up(off + tiles * (esz == 2 ? 2 : 1) * 64 * 64 * esz);
+    // P is formed by the recurrence kernel itself with a scalar gate; with per-channel gates the
+    // intra kernel forms it (its exponent factors live inside the contraction)
+    pl->off_P = off;       if (channel) off = align_up(off + tiles * (esz == 2 ? 2 : 1) * 64 * 64 * esz);
     pl->off_gates = off;   off = align_up(off + tiles * gdn::GB_FLOATS * sizeof(float));
     if (channel) {
         pl->off_kg = off;  off = align_up(off + tiles * 64 * a->D_k * esz);

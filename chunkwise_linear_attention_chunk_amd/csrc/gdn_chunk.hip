@@ -128,7 +128,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanParams p) {
 }
 
 // tile selections of the recurrence kernel's loads
-enum { LD_A = 1, LD_P = 2, LD_V = 4, LD_G = 8, LD_ALL = 15 };
+enum { LD_A = 1, LD_P = 2, LD_V = 4, LD_G = 8, LD_K = 16, LD_Q = 32, LD_ALL = 63 };
 
 // ------------------------------------------------------------------------------------------
 // Recurrence + output.  One workgroup per (sequence segment, value head, NSUB slices of 16 value
@@ -160,16 +160,17 @@ struct RecLds {
     static constexpr int NKB = DK / 32;
     static constexpr int NS = Split<T>::parts;
     static constexpr bool CH = GATE == GDN_GATE_CHANNEL_K, OUT = MODE == 0;
-    // one tile buffer (byte offsets): K, Q, A, V slice, P (NS parts) of one chunk.  With per-channel
-    // gates K is K 2^G and Q is Q 2^G (hi part), followed by K 2^(G_C - G) (NS parts) and the lo
-    // part of Q 2^G.  The pre-process (no output) holds no Q and no P.
+    static constexpr bool PL = OUT && CH;          // P loaded with the tiles (else formed in LDS)
+    // one tile buffer (byte offsets): K, Q, A, V slice (and P, NS parts, with per-channel gates) of
+    // one chunk.  With per-channel gates K is K 2^G and Q is Q 2^G (hi part), followed by
+    // K 2^(G_C - G) (NS parts) and the lo part of Q 2^G.  The pre-process (no output) holds no Q.
     static constexpr int K0 = 0, Q0 = KT, A0 = Q0 + (OUT ? KT : 0), V0 = A0 + AT, P0 = V0 + VT;
-    static constexpr int KD0 = P0 + (OUT ? NS * AT : 0), QL0 = KD0 + (CH ? NS * KT : 0);
+    static constexpr int KD0 = P0 + (PL ? NS * AT : 0), QL0 = KD0 + (CH ? NS * KT : 0);
     static constexpr int G0 = QL0 + (CH && OUT && NS == 2 ? KT : 0);   // the chunk's gate block
     static constexpr int TILES = G0 + GB_FLOATS * 4;
     static constexpr int SXN = NSUB * NKB * NS * 64;   // state fragments handed to the output waves
     static constexpr int VXN = NSUB * 2 * NS * 64;     // V' fragments handed to the output waves
-    static constexpr int SON = OUT && ESZ == 2 ? NSUB * 64 * 16 : 1;   // bf16 output tile per output wave
+    static constexpr int SON = OUT && ESZ == 2 ? 64 * BV : 1;   // bf16 output rows of the output waves
     static constexpr int BYTES = NBUF * TILES + (OUT ? (SXN + VXN) * (int)sizeof(Frag<T>) : 0) + SON * 2;
     static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
@@ -243,6 +244,10 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
     constexpr int EPG = 16 / ESZ;                  // elements per granule
     constexpr int MD = DK / 16;                    // 16-row state tiles
     constexpr int NL = NSUB;                       // waves sharing each group of tile loads
+    // main pass with two tile buffers: the chain waves stream the next chunk's K and A tiles, the
+    // output waves the rest
+    constexpr bool CHAIN_LD = MODE == 0 && NBUF == 2;
+    constexpr int OUT_LD = CHAIN_LD ? LD_ALL & ~(LD_K | LD_A) : LD_ALL;
 
     // Separate LDS objects for the two tile buffers and for the exchange: the chunk loop is
     // unrolled by two, so every LDS access names its buffer at compile time and the compiler can
@@ -259,7 +264,6 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool chain = wave < NSUB;
     const int sub = chain ? wave : wave - NSUB;
-    const bool loader = OUT ? !chain : true;       // issues the tile loads
 
     // XCD-aware mapping: the slices of one (segment, head) share blockIdx % 8, i.e. one XCD and
     // its L2, so Q/K/A fetched by one workgroup are L2 hits for the others.
@@ -323,9 +327,9 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
     }
     // Part q of np issues the instructions j with j % np == q of each tile (the output waves spread
     // their loads over the chunk's Q S products, so the loads never stall them for long).
-    // K and Q (with per-channel gates also K 2^(G_C - G) and Q 2^G's lo part):
-    auto issue_kq = [&](int c, unsigned char *tb, int part_q, int np) __attribute__((always_inline)) {
-        if (!loader) return;
+    // K and Q as selected by `what` (LD_K | LD_Q; with per-channel gates K brings K 2^(G_C - G) and
+    // Q brings Q 2^G's lo part):
+    auto issue_kq = [&](int c, unsigned char *tb, int part_q, int np, int what) __attribute__((always_inline)) {
         const int64_t tok = si.tok0 + (int64_t)(sg.c0 + c) * kChunk;
         const int nvc = nvalid(c);
         const int64_t gci = si.chunk0 + sg.c0 + c;   // global chunk index
@@ -340,13 +344,19 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
             const int i = sub + NL * j;
             if (j % np != part_q) continue;
             if (NKI * NL != L::KGPR && i >= L::KGPR) break;
-            buffer_granule_to_lds(rK, tb + L::K0 + 1024 * i, offK[j], 0);
-            if constexpr (OUT) buffer_granule_to_lds(rQ, tb + L::Q0 + 1024 * i, offK[j], 0);
-            if constexpr (CH) {
+            if (what & LD_K) {
+                buffer_granule_to_lds(rK, tb + L::K0 + 1024 * i, offK[j], 0);
+                if constexpr (CH) {
 #pragma unroll
-                for (int part = 0; part < L::NS; ++part)
-                    buffer_granule_to_lds(rKd, tb + L::KD0 + part * L::KT + 1024 * i, offK[j], part * 64 * DK * ESZ);
-                if constexpr (OUT && L::NS == 2) buffer_granule_to_lds(rQ, tb + L::QL0 + 1024 * i, offK[j], 64 * DK * ESZ);
+                    for (int part = 0; part < L::NS; ++part)
+                        buffer_granule_to_lds(rKd, tb + L::KD0 + part * L::KT + 1024 * i, offK[j], part * 64 * DK * ESZ);
+                }
+            }
+            if constexpr (OUT) {
+                if (what & LD_Q) {
+                    buffer_granule_to_lds(rQ, tb + L::Q0 + 1024 * i, offK[j], 0);
+                    if constexpr (CH && L::NS == 2) buffer_granule_to_lds(rQ, tb + L::QL0 + 1024 * i, offK[j], 64 * DK * ESZ);
+                }
             }
         }
     };
@@ -363,7 +373,7 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
             if (j % np != part_q) continue;
             if (NAI * NL != L::AGPR && i >= L::AGPR) break;
             if (what & LD_A) buffer_granule_to_lds(rA, tb + L::A0 + 1024 * i, offA[j], 0);
-            if constexpr (OUT) {
+            if constexpr (L::PL) {
                 if (what & LD_P) {
 #pragma unroll
                     for (int part = 0; part < L::NS; ++part)
@@ -418,7 +428,7 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
             if (c > 0) {
                 __syncthreads();
                 if constexpr (LD) {
-                    issue_kq(c, tiles0, 0, 1);
+                    issue_kq(c, tiles0, 0, 1, LD_ALL);
                     issue_apvg(c, tiles0, 0, 1, LD_ALL);
                 }
             }
@@ -428,10 +438,21 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
     };
 
     // ---- output role (main pass): streams the tiles of the next chunk into LDS and forms
-    //      O = scale diag(gamma) Q S_c + P V' of its 16 columns.  Its own loop, so that none of the
-    //      chain's registers (the state, its operand pairs) are live here and vice versa.
+    //      O = scale diag(gamma) Q S_c + P V' for its token tiles and all BV columns of the slice:
+    //      with two output waves, wave 0 owns tiles 0 and 3 and wave 1 tiles 1 and 2 (which balances
+    //      the causal P work); a single output wave owns all four.  Its own loop, so that none of
+    //      the chain's registers (the state, its operand pairs) are live here and vice versa.
     if constexpr (OUT) {
         if (!chain) {
+            constexpr int NR = 4 / NSUB;                  // token tiles of this wave
+            int mt[NR];
+#pragma unroll
+            for (int i = 0; i < NR; ++i) mt[i] = NSUB == 1 ? i : (i == 0 ? (sub ? 1 : 0) : (sub ? 2 : 3));
+            // the causal blocks of P V': (token tile i, contraction block kb <= m / 2)
+            constexpr int NPB = NSUB == 1 ? 6 : 3;
+            auto pb_tile = [&](int b) { return NSUB == 1 ? (b < 4 ? b : b - 2) : (b == 0 ? 0 : 1); };
+            auto pb_kb = [&](int b) { return NSUB == 1 ? (b < 4 ? 0 : 1) : (b == 2 ? 1 : 0); };
+            // (NSUB == 2: blocks (tile 0, kb 0), (tile 1, kb 0), (tile 1, kb 1); tile 1 is m = 3 or 2)
             auto out_step = [&]<int B>(int c) __attribute__((always_inline)) {
                 unsigned char *tcur = B == 0 ? tiles0 : tiles1;
                 unsigned char *tnext = B == 0 ? tiles1 : tiles0;
@@ -439,67 +460,123 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
                 const int nv = nvalid(c);
                 const float *g3 = reinterpret_cast<const float *>(tcur + L::G0);
                 const bool more = NBUF == 2 && c + 1 < nch;               // stream chunk c + 1 meanwhile
-                const unsigned char *tQ = tcur + L::Q0, *tP = tcur + L::P0, *tQl = tcur + L::QL0;
-                f32x4 o[4];
-
-                // inter-chunk part: scale diag(gamma) Q S_c (S_c was handed over before this chunk)
-                const Frag<T> *sxs = sSx + (sub * NKB * L::NS) * 64 + lane;
+                const unsigned char *tQ = tcur + L::Q0, *tK = tcur + L::K0, *tQl = tcur + L::QL0;
+                // inter-chunk part: scale diag(gamma) Q S_c (S_c was handed over before this chunk);
                 // the state and Q fragments first (the Q lo parts of per-channel gates as they are used)
-                Frag<T> sh[NKB], sl[NKB], qf[NKB][4];
+                Frag<T> sh[NSUB][NKB], sl[NSUB][NKB], qf[NKB][NR];
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb) {
-                    sh[kb] = sxs[kb * L::NS * 64];
-                    if constexpr (L::NS == 2) sl[kb] = sxs[kb * L::NS * 64 + 64];
 #pragma unroll
-                    for (int m = 0; m < 4; ++m) qf[kb][m] = ldpi_tile<T, L::KGPR>(tQ, 16 * m + l16, kb);
+                    for (int g = 0; g < NSUB; ++g) {
+                        const Frag<T> *sxs = sSx + ((g * NKB + kb) * L::NS) * 64 + lane;
+                        sh[g][kb] = sxs[0];
+                        if constexpr (L::NS == 2) sl[g][kb] = sxs[64];
+                    }
+#pragma unroll
+                    for (int i = 0; i < NR; ++i) qf[kb][i] = ldpi_tile<T, L::KGPR>(tQ, 16 * mt[i] + l16, kb);
                 }
+                f32x4 o[NR][NSUB];
 #pragma unroll
-                for (int m = 0; m < 4; ++m) o[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int i = 0; i < NR; ++i)
+#pragma unroll
+                    for (int g = 0; g < NSUB; ++g) o[i][g] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb) {
                     if (more) {                                   // 1/NKB of the loads per block
-                        issue_kq(c + 1, tnext, kb, NKB);
-                        issue_apvg(c + 1, tnext, kb, NKB, LD_ALL);
+                        issue_kq(c + 1, tnext, kb, NKB, OUT_LD);
+                        issue_apvg(c + 1, tnext, kb, NKB, OUT_LD);
                     }
 #pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        if constexpr (CH && L::NS == 2)
-                            mma_xx(o[m], qf[kb][m], ldpi_tile<T, L::KGPR>(tQl, 16 * m + l16, kb), sh[kb], sl[kb]);
-                        else
-                            mma_x(o[m], qf[kb][m], sh[kb], sl[kb]);
+                    for (int i = 0; i < NR; ++i) {
+                        Frag<T> ql;
+                        if constexpr (CH && L::NS == 2) ql = ldpi_tile<T, L::KGPR>(tQl, 16 * mt[i] + l16, kb);
+#pragma unroll
+                        for (int g = 0; g < NSUB; ++g) {
+                            if constexpr (CH && L::NS == 2) mma_xx(o[i][g], qf[kb][i], ql, sh[g][kb], sl[g][kb]);
+                            else mma_x(o[i][g], qf[kb][i], sh[g][kb], sl[g][kb]);
+                        }
                     }
                 }
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
+                for (int i = 0; i < NR; ++i) {
+                    f32x4 f;
                     if constexpr (CH) {
-                        o[m] *= p.scale;
+                        f = f32x4{p.scale, p.scale, p.scale, p.scale};
                     } else {
-                        const float4 sgm = *reinterpret_cast<const float4 *>(g3 + GB_SGAM + 16 * m + 4 * grp);
-                        o[m][0] *= sgm.x; o[m][1] *= sgm.y; o[m][2] *= sgm.z; o[m][3] *= sgm.w;
+                        const float4 gm = *reinterpret_cast<const float4 *>(g3 + GB_GAM + 16 * mt[i] + 4 * grp);
+                        f = f32x4{p.scale * gm.x, p.scale * gm.y, p.scale * gm.z, p.scale * gm.w};
                     }
+#pragma unroll
+                    for (int g = 0; g < NSUB; ++g) o[i][g] *= f;
+                }
+                // P operand pairs of the causal blocks.  Per-channel gates: read from the tile the
+                // per-chunk kernel formed.  Scalar gate: P = scale Lower(Gamma) (.) Q K^T formed here
+                // (06 . Flash Linear Attention, section 3) from the Q fragments above and the K tile,
+                // transposed (C = K Q^T: a lane holds four consecutive key tokens s of one query token
+                // t), which is lane for lane the pi-order row operand of P V' once the two 16-token
+                // halves of a block are packed.
+                Frag<T> ph[NPB], pl[NPB];
+                if constexpr (CH) {
+                    const unsigned char *tP = tcur + L::P0;
+#pragma unroll
+                    for (int b = 0; b < NPB; ++b) {
+                        const int row = 16 * mt[pb_tile(b)] + l16;
+                        ph[b] = ldpi_tile<T, L::AGPR>(tP, row, pb_kb(b));
+                        if constexpr (L::NS == 2) pl[b] = ldpi_tile<T, L::AGPR>(tP + L::AT, row, pb_kb(b));
+                    }
+                }
+                // scalar gate: block b of P, formed in phase 1 (the first NPB1 blocks) or phase 2
+                const float *glr = g3 + GB_GL;
+                const float lsc = __log2f(p.scale);
+                auto form_p = [&](int b) __attribute__((always_inline)) {
+                    const int i = pb_tile(b), kb = pb_kb(b), m = mt[i];
+                    const int t = 16 * m + l16;
+                    const float glt = glr[t] + lsc;
+                    f32x4 pt[2];
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const int nn = 2 * kb + u;             // key tile
+                        pt[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        if (nn > m) continue;                  // above the diagonal: zero
+#pragma unroll
+                        for (int kk = 0; kk < NKB; ++kk) mma(pt[u], ldpi_tile<T, L::KGPR>(tK, 16 * nn + l16, kk), qf[kk][i]);
+                        const int s0 = 16 * nn + 4 * grp;
+                        const float4 gs = *reinterpret_cast<const float4 *>(glr + s0);
+                        const float gsv[4] = {gs.x, gs.y, gs.z, gs.w};
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) pt[u][r] = (s0 + r <= t) ? fast_exp2(glt - gsv[r]) * pt[u][r] : 0.f;
+                    }
+                    float x[8];
+                    pack_pi(pt[0], pt[1], x);
+                    split8(x, ph[b], pl[b]);
+                };
+                // the output waves' two phases are balanced against the chain's: most P blocks here,
+                // the rest after the barrier while V' is read
+                constexpr int NPB1 = NSUB == 2 ? 2 : 4;
+                if constexpr (!CH) {
+#pragma unroll
+                    for (int b = 0; b < NPB1; ++b) form_p(b);
                 }
                 lds_only_barrier();  // V' of chunk c is visible
-
-                const Frag<T> *vxs = sVx + (sub * 2 * L::NS) * 64 + lane;
-                Frag<T> Vh[2], Vl[2];
+                if constexpr (!CH) {
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    Vh[kb] = vxs[kb * L::NS * 64];
-                    if constexpr (L::NS == 2) Vl[kb] = vxs[kb * L::NS * 64 + 64];
+                    for (int b = NPB1; b < NPB; ++b) form_p(b);
                 }
+                // intra-chunk part: P V'
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    Frag<T> ph[4], pl[4];
+                for (int g = 0; g < NSUB; ++g) {
+                    const Frag<T> *vxs = sVx + (g * 2 * L::NS) * 64 + lane;
+                    Frag<T> Vh[2], Vl[2];
 #pragma unroll
-                    for (int m = 2 * kb; m < 4; ++m) {
-                        ph[m] = ldpi_tile<T, L::AGPR>(tP, 16 * m + l16, kb);
-                        if constexpr (L::NS == 2) pl[m] = ldpi_tile<T, L::AGPR>(tP + L::AT, 16 * m + l16, kb);
+                    for (int kb = 0; kb < 2; ++kb) {
+                        Vh[kb] = vxs[kb * L::NS * 64];
+                        if constexpr (L::NS == 2) Vl[kb] = vxs[kb * L::NS * 64 + 64];
                     }
 #pragma unroll
-                    for (int m = 2 * kb; m < 4; ++m) mma_xx(o[m], ph[m], pl[m], Vh[kb], Vl[kb]);
+                    for (int b = 0; b < NPB; ++b) mma_xx(o[pb_tile(b)][g], ph[b], pl[b], Vh[pb_kb(b)], Vl[pb_kb(b)]);
                 }
-                // buffer stores: the resource covers the chunk's valid rows only (rows past the end are
-                // dropped by the bounds check)
+                // buffer stores: the resource covers the chunk's valid rows only (rows past the end
+                // are dropped by the bounds check)
                 const int64_t ebase = (int64_t)(si.tok0 + (sg.c0 + c) * kChunk) * v_stride + (int64_t)h * DV + c0;
                 const int oes = p.o_f32 ? 4 : ESZ;
                 const __amdgpu_buffer_rsrc_t ors = make_rsrc(static_cast<char *>(p.o) + ebase * oes,
@@ -507,36 +584,42 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
                 bool stored = false;
                 if constexpr (ESZ == 2) {
                     if (!p.o_f32) {
-                        // bf16: through this wave's LDS tile [64 rows][16 columns], then two 16-byte stores
-                        // per lane (half a row each); one wave writes and reads it, in order
-                        bf16 *so = sO + sub * 1024;
+                        // bf16: through this wave's LDS tile [16 NR rows][BV columns], then 16-byte
+                        // stores (BV / 8 per row); one wave writes and reads it, in order
+                        bf16 *so = sO + sub * (16 * NR * BV);
 #pragma unroll
-                        for (int m = 0; m < 4; ++m)
+                        for (int i = 0; i < NR; ++i)
 #pragma unroll
-                            for (int r = 0; r < 4; ++r) so[(16 * m + 4 * grp + r) * 16 + l16] = (bf16)o[m][r];
+                            for (int g = 0; g < NSUB; ++g)
 #pragma unroll
-                        for (int i = 0; i < 2; ++i) {
-                            const int qq = lane + 64 * i, row = qq >> 1, half = qq & 1;
-                            const u32x4 val = *reinterpret_cast<const u32x4 *>(so + row * 16 + 8 * half);
-                            __builtin_amdgcn_raw_buffer_store_b128(val, ors, (row * vs + 16 * sub + 8 * half) * 2, 0, 0);
+                                for (int r = 0; r < 4; ++r) so[(16 * i + 4 * grp + r) * BV + 16 * g + l16] = (bf16)o[i][g][r];
+                        constexpr int GPRW = BV / 8;                      // 16-byte pieces per row
+#pragma unroll
+                        for (int it = 0; it < 16 * NR * GPRW / 64; ++it) {
+                            const int qq = lane + 64 * it, lrow = qq / GPRW, piece = qq % GPRW;
+                            const int row = 16 * mt[lrow >> 4] + (lrow & 15);
+                            const u32x4 val = *reinterpret_cast<const u32x4 *>(so + lrow * BV + 8 * piece);
+                            __builtin_amdgcn_raw_buffer_store_b128(val, ors, (row * vs + 8 * piece) * 2, 0, 0);
                         }
                         stored = true;
                     }
                 }
                 if (!stored) {
-                    // row offsets are scalar, the lane offset is computed once
-                    const int vlane = ((4 * grp) * vs + 16 * sub + l16) * oes;
 #pragma unroll
-                    for (int m = 0; m < 4; ++m)
+                    for (int i = 0; i < NR; ++i)
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int soff = (16 * m + r) * vs * oes;
-                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o[m][r]), ors, vlane, soff, 0);
+                        for (int g = 0; g < NSUB; ++g) {
+                            const int vlane = ((4 * grp) * vs + 16 * g + l16) * oes;
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                const int soff = (16 * mt[i] + r) * vs * oes;
+                                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o[i][g][r]), ors, vlane, soff, 0);
+                            }
                         }
                 }
             };
             if (nch > 0) {
-                issue_kq(0, tiles0, 0, 1);
+                issue_kq(0, tiles0, 0, 1, LD_ALL);
                 issue_apvg(0, tiles0, 0, 1, LD_ALL);
             }
             for (int c = 0; c < nch; c += 2) {
@@ -565,12 +648,12 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
     auto chain_step = [&]<int B>(int c) __attribute__((always_inline)) {
         unsigned char *tcur = B == 0 ? tiles0 : tiles1;
         unsigned char *tnext = B == 0 ? tiles1 : tiles0;
-        chunk_top.template operator()<!OUT>(c);
+        chunk_top.template operator()<!OUT || CHAIN_LD>(c);
         const float *g3 = reinterpret_cast<const float *>(tcur + L::G0);
         const bool more = NBUF == 2 && c + 1 < nch;
         if constexpr (!OUT) {
             if (more) {
-                issue_kq(c + 1, tnext, 0, 1);
+                issue_kq(c + 1, tnext, 0, 1, LD_ALL);
                 issue_apvg(c + 1, tnext, 0, 1, LD_ALL);
             }
         }
@@ -659,6 +742,13 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int m = 0; m < MD; ++m) kt[kb][m] = ldpi_col_tile<T, L::KGPR>(tKd, 16 * m, kb);
+        if constexpr (CHAIN_LD) {
+            // the K and A tiles of chunk c + 1 (the chain waves reach this barrier first)
+            if (more) {
+                issue_kq(c + 1, tnext, 0, 1, LD_K);
+                issue_apvg(c + 1, tnext, 0, 1, LD_A);
+            }
+        }
         if constexpr (OUT) lds_only_barrier();  // V' of chunk c is visible to the output waves
         // =========================== phase 2 ===========================
 
@@ -692,7 +782,7 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
     };
     if (nch > 0) {
         if constexpr (!OUT) {
-            issue_kq(0, tiles0, 0, 1);
+            issue_kq(0, tiles0, 0, 1, LD_ALL);
             issue_apvg(0, tiles0, 0, 1, LD_ALL);
         }
         split_state();

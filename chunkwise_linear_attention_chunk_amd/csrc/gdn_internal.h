@@ -10,9 +10,9 @@ constexpr int kChunk = 64;  // tokens per chunk
 constexpr int GDN_GATE_CHANNEL_K = 1;  // gate kind of per-channel (KDA) gates, as in gdn.h
 
 // Per (chunk, head) gate block written by the per-chunk kernel, read by the recurrence: fp32 rows
-// of 64 tokens (scalar gate: beta, gamma_C / gamma, gamma, scale * gamma; per-channel gate: beta
+// of 64 tokens (scalar gate: beta, gamma_C / gamma, gamma, log2 gamma; per-channel gate: beta
 // and the [D_k] chunk decay 2^G_C).  Tail tokens carry beta = 0 and g = 0.
-enum GateBlock { GB_BETA = 0, GB_SC = 64, GB_GAM = 128, GB_SGAM = 192, GB_DEC = 64, GB_FLOATS = 256 };
+enum GateBlock { GB_BETA = 0, GB_SC = 64, GB_GAM = 128, GB_GL = 192, GB_DEC = 64, GB_FLOATS = 256 };
 
 // Device-side plan tables (built by the plan kernel from cu_seqlens or the batch shape).
 struct SeqInfo {            // one per sequence

@@ -1,6 +1,7 @@
 // Kernel (a): per (chunk, value head) -- chunk-local gate cumsum, gated beta*K K^T on the
-// matrix cores, the exact inverse A = (I + strictLower(diag(beta)(Gamma (.) K K^T)))^{-1}, and
-// the output's intra-chunk matrix P = scale Lower(Gamma) (.) Q K^T.
+// matrix cores and the exact inverse A = (I + strictLower(diag(beta)(Gamma (.) K K^T)))^{-1};
+// with per-channel gates also the output's intra-chunk matrix P = scale Lower(Gamma) (.) Q K^T
+// (with a scalar gate the recurrence kernel forms P itself from the Q and K tiles it holds).
 //
 // Sources: 06 . Flash Linear Attention, section 3 (chunk-local cumsum of log-gates, exp2 of
 // pre-scaled differences) and section 4 (solve_tril: forward substitution inside 16x16
@@ -9,8 +10,8 @@
 // FlashQLA announcement (Qwen), the first step of the chunk-i forward.
 //
 // The inverse is computed in fp32 throughout (the pages use tf32 dots for the merges; gfx950
-// has no tf32 path, so the merges run on fp32 MFMA).  A is stored in the input dtype, P as an
-// operand pair (hi, lo) in bf16 or whole in fp32.
+// has no tf32 path, so the merges run on fp32 MFMA).  A is stored in the input dtype, P (per-channel
+// gates) as an operand pair (hi, lo) in bf16 or whole in fp32.
 //
 // One workgroup of 256 threads (4 waves) per (chunk, head); many workgroups per CU hide the
 // latency of the serial 16-step substitutions.
@@ -154,10 +155,7 @@ __device__ __forceinline__ void store_p(void *stage, T *P, const f32x4 *pa, cons
     __syncthreads();
 }
 
-// Scalar gate.  Besides A, the output's intra-chunk matrix P = scale Lower(Gamma) (.) Q K^T (mask
-// with the diagonal; 06 . Flash Linear Attention, section 3) is formed here once per (chunk,
-// head) and stored as an operand pair, so the recurrence kernel only reads it.  Q goes straight
-// from memory into matrix-core operand registers; only K (and later the inverse) and A_raw use LDS.
+// Scalar gate: A and the gate block.  Only K (and later the inverse) and A_raw use LDS.
 template <typename T, int DK>
 __global__ __launch_bounds__(256) void intra_kernel(IntraParams p) {
     constexpr int VEC = Vec16<T>::N;
@@ -166,7 +164,6 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraParams p) {
     constexpr int K_BYTES = 64 * KP * (int)sizeof(T);
     constexpr int X_BYTES = 64 * LP * 4;
     constexpr int R0 = K_BYTES > X_BYTES ? K_BYTES : X_BYTES;
-    constexpr int NS = Split<T>::parts;
     constexpr int NKB = DK / 32;
     // region 0: K tile, later the inverse X; region 1: A_raw
     __shared__ __attribute__((aligned(16))) unsigned char smem[R0 + X_BYTES];
@@ -181,7 +178,6 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraParams p) {
     const ChunkInfo cinfo = chunk_info(p.chunks, ci, p.T);
     const int t0 = cinfo.tok0, nv = cinfo.nv;
     const T *k = static_cast<const T *>(p.k);
-    const T *q = static_cast<const T *>(p.q);
     const float *g = static_cast<const float *>(p.g);
     const T *beta = static_cast<const T *>(p.beta);
 
@@ -196,9 +192,8 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraParams p) {
     }
     const int ntiles = wave < 2 ? 3 : 2;
 
-    // ---- loads: K rows into LDS (clamped into the chunk, masked at staging); Q operand fragments
-    //      of this wave's tile rows straight into registers (rows past the end are masked later by
-    //      the zero K rows and the output mask).  All loads are unconditional.
+    // ---- loads: K rows into LDS (clamped into the chunk, masked at staging).  All loads are
+    //      unconditional.
     const int last = max(nv - 1, 0);
     constexpr int VPR = DK / VEC;
     constexpr int NV = 64 * VPR / 256;
@@ -207,14 +202,6 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraParams p) {
     for (int i = 0; i < NV; ++i) {
         const int idx = tid + 256 * i, row = min(idx / VPR, last), cv = idx % VPR;
         kv[i] = *reinterpret_cast<const u32x4 *>(k + ((int64_t)(t0 + row) * p.H_qk + hq) * DK + cv * VEC);
-    }
-    Frag<T> qf[NT][NKB];
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-        const int row = min(16 * TI[n] + l16, last);
-        const T *qr = q + ((int64_t)(t0 + row) * p.H_qk + hq) * DK + 8 * grp;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) qf[n][kb] = ld8(qr + 32 * kb);
     }
     if (wave == 0) {
         const int64_t idx = (int64_t)(t0 + min(lane, last)) * p.H_v + h;
@@ -230,7 +217,7 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraParams p) {
         gbk[GB_BETA + lane] = bv;
         gbk[GB_SC + lane] = fast_exp2(glC - gl);
         gbk[GB_GAM + lane] = gam;
-        gbk[GB_SGAM + lane] = p.scale * gam;
+        gbk[GB_GL + lane] = gl;
     }
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
@@ -239,11 +226,11 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraParams p) {
     }
     __syncthreads();
 
-    // ---- this wave's tiles of A_raw = strictLower(diag(beta) (Gamma (.) K K^T)) and of
-    //      P = scale Lower(Gamma) (.) Q K^T (diagonal included), all accumulators in flight together
-    f32x4 aa[NT], pa[NT];
+    // ---- this wave's tiles of A_raw = strictLower(diag(beta) (Gamma (.) K K^T)), all accumulators
+    //      in flight together
+    f32x4 aa[NT];
 #pragma unroll
-    for (int n = 0; n < NT; ++n) aa[n] = pa[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int n = 0; n < NT; ++n) aa[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
         Frag<T> ki[NT], kj[NT];
@@ -257,10 +244,8 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraParams p) {
         for (int n = 0; n < NT; ++n) {
             if (n >= ntiles) break;
             mma(aa[n], ki[n], kj[n]);
-            mma(pa[n], qf[n][kb], kj[n]);
         }
     }
-    T *P = static_cast<T *>(p.P) + ((int64_t)ci * p.H_v + h) * NS * 4096;
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
         if (n >= ntiles) break;
@@ -271,11 +256,9 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraParams p) {
             const int i = 16 * TI[n] + 4 * grp + r;
             const float gam = fast_exp2(sGl[i] - glj);
             sL[i * LP + j] = (j < i) ? sB[i] * gam * aa[n][r] : 0.f;
-            pa[n][r] = (j <= i) ? p.scale * gam * pa[n][r] : 0.f;
         }
     }
-    // P through the K tile's region (no longer read), then A_raw is complete and the region holds X
-    store_p<T>(smem, P, pa, TI, TJ, ntiles);
+    __syncthreads();  // A_raw is complete; the K tile's region is free for the inverse X
 
     invert_unit_lower(sL, sX);
     store_unit_lower<T>(sX, static_cast<T *>(p.A) + ((int64_t)ci * p.H_v + h) * 4096);
