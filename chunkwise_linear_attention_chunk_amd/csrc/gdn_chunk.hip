@@ -325,8 +325,8 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
         const int pos = 64 * (sub + NL * j) + lane, row = pos / L::VGPR, g = pos % L::VGPR;
         offV[j] = (row * vs + (g ^ tile_swz<L::VGPR>(row)) * EPG) * ESZ;
     }
-    // Part q of np issues the instructions j with j % np == q of each tile (the output waves spread
-    // their loads over the chunk's Q S products, so the loads never stall them for long).
+    // Part q of np issues the instructions j with j % np == q of each tile (a caller can spread its
+    // loads over other work; issuing them together measured fastest here).
     // K and Q as selected by `what` (LD_K | LD_Q; with per-channel gates K brings K 2^(G_C - G) and
     // Q brings Q 2^G's lo part):
     auto issue_kq = [&](int c, unsigned char *tb, int part_q, int np, int what) __attribute__((always_inline)) {
@@ -463,6 +463,10 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
                 const unsigned char *tQ = tcur + L::Q0, *tK = tcur + L::K0, *tQl = tcur + L::QL0;
                 // inter-chunk part: scale diag(gamma) Q S_c (S_c was handed over before this chunk);
                 // the state and Q fragments first (the Q lo parts of per-channel gates as they are used)
+                if (more) {                                       // the output waves' share, at once
+                    issue_kq(c + 1, tnext, 0, 1, OUT_LD);
+                    issue_apvg(c + 1, tnext, 0, 1, OUT_LD);
+                }
                 Frag<T> sh[NSUB][NKB], sl[NSUB][NKB], qf[NKB][NR];
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb) {
@@ -482,10 +486,6 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
                     for (int g = 0; g < NSUB; ++g) o[i][g] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb) {
-                    if (more) {                                   // 1/NKB of the loads per block
-                        issue_kq(c + 1, tnext, kb, NKB, OUT_LD);
-                        issue_apvg(c + 1, tnext, kb, NKB, OUT_LD);
-                    }
 #pragma unroll
                     for (int i = 0; i < NR; ++i) {
                         Frag<T> ql;
@@ -525,7 +525,7 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
                         if constexpr (L::NS == 2) pl[b] = ldpi_tile<T, L::AGPR>(tP + L::AT, row, pb_kb(b));
                     }
                 }
-                // scalar gate: block b of P, formed in phase 1 (the first NPB1 blocks) or phase 2
+                // scalar gate: block b of P
                 const float *glr = g3 + GB_GL;
                 const float lsc = __log2f(p.scale);
                 auto form_p = [&](int b) __attribute__((always_inline)) {
@@ -550,18 +550,11 @@ __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kern
                     pack_pi(pt[0], pt[1], x);
                     split8(x, ph[b], pl[b]);
                 };
-                // the output waves' two phases are balanced against the chain's: most P blocks here,
-                // the rest after the barrier while V' is read
-                constexpr int NPB1 = NSUB == 2 ? 2 : 4;
                 if constexpr (!CH) {
 #pragma unroll
-                    for (int b = 0; b < NPB1; ++b) form_p(b);
+                    for (int b = 0; b < NPB; ++b) form_p(b);
                 }
                 lds_only_barrier();  // V' of chunk c is visible
-                if constexpr (!CH) {
-#pragma unroll
-                    for (int b = NPB1; b < NPB; ++b) form_p(b);
-                }
                 // intra-chunk part: P V'
 #pragma unroll
                 for (int g = 0; g < NSUB; ++g) {
