@@ -24,7 +24,8 @@ namespace {
 
 // Exact inverse of the unit lower triangular I + L (L strictly lower, fp32 [64][LP] in LDS) into X
 // (same layout, strictly lower part only): forward substitution inside the four 16x16 diagonal
-// blocks (lane = column), then the block-triangular merges 16 -> 32 -> 64 on fp32 MFMA.  Called
+// blocks (lane = column), then the block-triangular merges 16 -> 32 -> 64 on fp32 MFMA.  X may be
+// L itself: each block of X is written only after every read of the L block at its place.  Called
 // by all 256 threads with L complete and visible; returns after a barrier, X complete.
 __device__ __forceinline__ void invert_unit_lower(const float *sL, float *sX) {
     constexpr int LP = 64 + 4;
@@ -84,7 +85,7 @@ __device__ __forceinline__ void invert_unit_lower(const float *sL, float *sX) {
             mm16_f32_regB(oo, Xt(3, 2), LP, T2);
             mm16_f32_regB(oo, Xt(3, 3), LP, T3);
         }
-        // the tiles written here (rows 32..63, cols 0..31) are read by no wave in this step
+        __syncthreads();  // every wave has read L's lower-left blocks (X may overwrite them)
 #pragma unroll
         for (int r = 0; r < 4; ++r) sX[(16 * I + 4 * grp + r) * LP + 16 * J + l16] = -oo[r];
     }
@@ -165,12 +166,13 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraParams p) {
     constexpr int X_BYTES = 64 * LP * 4;
     constexpr int R0 = K_BYTES > X_BYTES ? K_BYTES : X_BYTES;
     constexpr int NKB = DK / 32;
-    // region 0: K tile, later the inverse X; region 1: A_raw
-    __shared__ __attribute__((aligned(16))) unsigned char smem[R0 + X_BYTES];
+    // one region: the K tile, then A_raw, then its inverse X in place (a small footprint keeps
+    // eight workgroups on a CU to hide each one's serial latency)
+    __shared__ __attribute__((aligned(16))) unsigned char smem[R0];
     __shared__ float sGl[64], sB[64];
     T *sK = reinterpret_cast<T *>(smem);
     float *sX = reinterpret_cast<float *>(smem);
-    float *sL = reinterpret_cast<float *>(smem + R0);
+    float *sL = sX;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, grp = lane >> 4;
     const int ci = blockIdx.x / p.H_v, h = blockIdx.x - ci * p.H_v;
@@ -246,6 +248,7 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraParams p) {
             mma(aa[n], ki[n], kj[n]);
         }
     }
+    __syncthreads();  // every wave has read the K tile: A_raw takes its region
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
         if (n >= ntiles) break;
@@ -258,7 +261,7 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraParams p) {
             sL[i * LP + j] = (j < i) ? sB[i] * gam * aa[n][r] : 0.f;
         }
     }
-    __syncthreads();  // A_raw is complete; the K tile's region is free for the inverse X
+    __syncthreads();  // A_raw is complete
 
     invert_unit_lower(sL, sX);
     store_unit_lower<T>(sX, static_cast<T *>(p.A) + ((int64_t)ci * p.H_v + h) * 4096);
