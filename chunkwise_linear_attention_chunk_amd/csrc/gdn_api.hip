@@ -48,7 +48,6 @@ struct Plan {
 };
 
 constexpr int kNoSegments = 1 << 28;  // segment length meaning "the whole sequence"
-constexpr int kCUs = 256;             // MI355X compute units
 
 int64_t count_segments(const gdn_fwd_args *a, int sl) {
     auto segs = [&](int64_t len) {
@@ -142,7 +141,7 @@ gdn_status validate_and_plan(const gdn_fwd_args *a, Plan *pl) {
         // segments so the main pass fills the CUs once (one recurrence workgroup per CU; the
         // pre-process, with no output waves, then also runs in one round): fewer segments leave
         // CUs idle, more add rounds to both passes and serial steps to the fix-up
-        const int64_t want = std::max<int64_t>(2, kCUs / std::max<int64_t>(chains, 1));
+        const int64_t want = std::max<int64_t>(2, gdn::kCUs / std::max<int64_t>(chains, 1));
         sl = (int)std::max<int64_t>(4, (max_nc + want - 1) / want);
     }
     bool cp = false;

@@ -237,7 +237,9 @@ __device__ __forceinline__ void ld_vcol4(const unsigned char *tile, int m, int c
 //         (V as given, S = 0 at the segment start) give S*, identity columns (V = 0, S = I) give
 //         the segment's transition matrix M; both are written to the workspace.
 template <typename T, int DK, int NSUB, int NBUF, int MODE, int GATE>
-__global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB) void chunk_kernel(ChunkParams p) {
+__global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB,
+                             NBUF == 1 && MODE == 0 && GATE == 0 && sizeof(T) == 2 ? 2 : 1)
+void chunk_kernel(ChunkParams p) {
     using L = RecLds<T, DK, NSUB, NBUF, MODE, GATE>;
     constexpr bool OUT = L::OUT, CH = L::CH;
     constexpr int BV = L::BV, NKB = L::NKB, ESZ = L::ESZ;
@@ -933,6 +935,12 @@ static hipError_t launch_rec(int dtype, int D_k, int BV, const ChunkParams &p, h
         GDN_CHUNK_CASE(0, float, 128, 1, 1)
         GDN_CHUNK_CASE(0, float, 64, 1, 1)
     } else {
+        if constexpr (MODE == 0) {
+            // enough workgroups for two per CU (large batches, many packed sequences): the one-buffer
+            // build, whose 75 KiB of LDS and 256 registers per wave let two workgroups share a CU and
+            // fill each other's waits (its own loads then do not overlap its work)
+            if (grid.x >= 2u * (unsigned)kCUs) { GDN_CHUNK_CASE(1, bf16, 128, 2, 1) }
+        }
         GDN_CHUNK_CASE(1, bf16, 128, 2, 2)
         GDN_CHUNK_CASE(1, bf16, 128, 1, 2)
         GDN_CHUNK_CASE(1, bf16, 64, 2, 2)

@@ -7,6 +7,7 @@
 namespace gdn {
 
 constexpr int kChunk = 64;  // tokens per chunk
+constexpr int kCUs = 256;   // MI355X compute units
 constexpr int GDN_GATE_CHANNEL_K = 1;  // gate kind of per-channel (KDA) gates, as in gdn.h
 
 // Per (chunk, head) gate block written by the per-chunk kernel, read by the recurrence: fp32 rows

@@ -64,6 +64,19 @@ def test_bf16_packed_ragged():
     check(x, TOL["bf16"], label="bf16 packed ragged")
 
 
+def test_bf16_two_workgroups_per_cu_build():
+    # 8 sequences x 16 heads x 4 column groups = 512 recurrence workgroups: enough for two per CU,
+    # which selects the one-buffer build of the recurrence; compared in full, ragged last chunk
+    x = _w("qwen3next_bf16", B=8, H=16, T=64 * 3 + 17, h0=True, seed=77)
+    check(x, TOL["bf16"], label="bf16 512 workgroups")
+
+
+def test_packed_two_workgroups_per_cu_build():
+    # packed ragged sequences with the one-buffer build (9 x 16 x 4 = 576 workgroups)
+    x = _w("varlen_bf16", n_seqs=9, lens=(0, 1, 63, 64, 65, 300, 129, 7, 200), H=16, seed=78)
+    check(x, TOL["bf16"], label="bf16 packed, 576 workgroups")
+
+
 def test_qwen3next_workload_sampled():
     x = _w("qwen3next_bf16")
     check(x, TOL["bf16"], batches=[0, 3], heads=[0, 7, 15], label="qwen3next_bf16 (sampled)")
