@@ -87,6 +87,12 @@ gdn_status validate_and_plan(const gdn_fwd_args *a, Plan *pl) {
     if (a->o_dtype != a->dtype && a->o_dtype != GDN_DTYPE_F32)
         return fail(GDN_ERR_INVALID_ARG, "o_dtype %d must equal dtype %d or be fp32", a->o_dtype, a->dtype);
     if (a->cp_mode < GDN_CP_AUTO || a->cp_mode > GDN_CP_ON) return fail(GDN_ERR_INVALID_ARG, "bad cp_mode %d", a->cp_mode);
+    if ((a->qk_l2norm != 0 && a->qk_l2norm != 1) || (a->beta_sigmoid != 0 && a->beta_sigmoid != 1))
+        return fail(GDN_ERR_INVALID_ARG, "qk_l2norm and beta_sigmoid must be 0 or 1");
+    if (!a->A_log && (a->dt_bias || a->gate_lower_bound != 0.f))
+        return fail(GDN_ERR_INVALID_ARG, "dt_bias and gate_lower_bound need A_log");
+    if (!(a->gate_lower_bound <= 0.f) || !std::isfinite(a->gate_lower_bound))
+        return fail(GDN_ERR_INVALID_ARG, "gate_lower_bound must be 0 or a finite negative bound");
     if ((int64_t)a->B * a->T > INT32_MAX / 2) return fail(GDN_ERR_UNSUPPORTED, "too many tokens (%lld)", (long long)a->B * a->T);
 
     const bool packed = a->cu_seqlens_dev != nullptr;
@@ -248,14 +254,15 @@ gdn_status run_fwd(const gdn_fwd_args *a, void *workspace, size_t workspace_byte
     }
 
     const bool channel = a->gate_kind == GDN_GATE_CHANNEL;
+    const gdn::Prologue pro{a->qk_l2norm, a->beta_sigmoid, a->A_log, a->dt_bias, a->gate_lower_bound};
     if (channel) {
         gdn::IntraKdaParams ip{a->q, a->k, a->g, a->beta, chunks, a->T, (int)pl.total_chunks, a->H_qk, a->H_v,
                                a->scale, ws + pl.off_A, ws + pl.off_P, ws + pl.off_kg, ws + pl.off_kd,
-                               ws + pl.off_qg, reinterpret_cast<float *>(ws + pl.off_gates)};
+                               ws + pl.off_qg, reinterpret_cast<float *>(ws + pl.off_gates), pro};
         e = gdn::launch_intra_kda(a->dtype, a->D_k, ip, s);
     } else {
         gdn::IntraParams ip{a->q, a->k, a->g, a->beta, chunks, a->T, (int)pl.total_chunks, a->H_qk, a->H_v,
-                            a->scale, ws + pl.off_A, ws + pl.off_P, reinterpret_cast<float *>(ws + pl.off_gates)};
+                            a->scale, ws + pl.off_A, ws + pl.off_P, reinterpret_cast<float *>(ws + pl.off_gates), pro};
         e = gdn::launch_intra(a->dtype, a->D_k, ip, s);
     }
     if (e != hipSuccess) return done(fail(GDN_ERR_HIP, "intra launch: %s", hipGetErrorString(e)));

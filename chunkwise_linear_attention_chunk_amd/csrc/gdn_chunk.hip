@@ -393,8 +393,11 @@ void chunk_kernel(ChunkParams p) {
                 buffer_granule_to_lds(rV, tb + L::V0 + 1024 * i, offV[j], 0);
             }
         }
-        if ((what & LD_G) && sub == 0 && part_q == 0)   // the gate block: 64 granules, one instruction
-            buffer_granule_to_lds(make_rsrc(Gb + gci * p.H_v * GB_FLOATS, GB_FLOATS * 4), tb + L::G0, lane * 16, 0);
+        if ((what & LD_G) && sub == 0 && part_q == 0) {   // the gate block: 64 granules per instruction
+            const auto rG = make_rsrc(Gb + gci * p.H_v * GB_FLOATS, GB_FLOATS * 4);
+#pragma unroll
+            for (int gi = 0; gi < GB_FLOATS / 256; ++gi) buffer_granule_to_lds(rG, tb + L::G0 + 1024 * gi, lane * 16, 1024 * gi);
+        }
     };
 
     // ---- chain state: S [DK][16] of this slice in fp32 accumulator tiles (rows 16m + 4grp + r)
@@ -505,7 +508,7 @@ void chunk_kernel(ChunkParams p) {
                     if constexpr (CH) {
                         f = f32x4{p.scale, p.scale, p.scale, p.scale};
                     } else {
-                        const float4 gm = *reinterpret_cast<const float4 *>(g3 + GB_GAM + 16 * mt[i] + 4 * grp);
+                        const float4 gm = *reinterpret_cast<const float4 *>(g3 + GB_GAQ + 16 * mt[i] + 4 * grp);
                         f = f32x4{p.scale * gm.x, p.scale * gm.y, p.scale * gm.z, p.scale * gm.w};
                     }
 #pragma unroll
@@ -527,13 +530,13 @@ void chunk_kernel(ChunkParams p) {
                         if constexpr (L::NS == 2) pl[b] = ldpi_tile<T, L::AGPR>(tP + L::AT, row, pb_kb(b));
                     }
                 }
-                // scalar gate: block b of P
-                const float *glr = g3 + GB_GL;
+                // scalar gate: block b of P (query rows' log-gates from GLQ, key rows' from GLK)
+                const float *glq = g3 + GB_GLQ, *glk = g3 + GB_GLK;
                 const float lsc = __log2f(p.scale);
                 auto form_p = [&](int b) __attribute__((always_inline)) {
                     const int i = pb_tile(b), kb = pb_kb(b), m = mt[i];
                     const int t = 16 * m + l16;
-                    const float glt = glr[t] + lsc;
+                    const float glt = glq[t] + lsc;
                     f32x4 pt[2];
 #pragma unroll
                     for (int u = 0; u < 2; ++u) {
@@ -543,7 +546,7 @@ void chunk_kernel(ChunkParams p) {
 #pragma unroll
                         for (int kk = 0; kk < NKB; ++kk) mma(pt[u], ldpi_tile<T, L::KGPR>(tK, 16 * nn + l16, kk), qf[kk][i]);
                         const int s0 = 16 * nn + 4 * grp;
-                        const float4 gs = *reinterpret_cast<const float4 *>(glr + s0);
+                        const float4 gs = *reinterpret_cast<const float4 *>(glk + s0);
                         const float gsv[4] = {gs.x, gs.y, gs.z, gs.w};
 #pragma unroll
                         for (int r = 0; r < 4; ++r) pt[u][r] = (s0 + r <= t) ? fast_exp2(glt - gsv[r]) * pt[u][r] : 0.f;
@@ -668,7 +671,7 @@ void chunk_kernel(ChunkParams p) {
             const float4 be = *reinterpret_cast<const float4 *>(g3 + GB_BETA + 16 * m + 4 * grp);
             b4[m][0] = be.x; b4[m][1] = be.y; b4[m][2] = be.z; b4[m][3] = be.w;
             if constexpr (!CH) {
-                const float4 gg = *reinterpret_cast<const float4 *>(g3 + GB_GAM + 16 * m + 4 * grp);
+                const float4 gg = *reinterpret_cast<const float4 *>(g3 + GB_GAK + 16 * m + 4 * grp);
                 ga[m][0] = gg.x; ga[m][1] = gg.y; ga[m][2] = gg.z; ga[m][3] = gg.w;
             }
         }
@@ -751,7 +754,7 @@ void chunk_kernel(ChunkParams p) {
 #pragma unroll
         for (int m = 0; m < MD; ++m) {
             if constexpr (CH) dec[m] = *reinterpret_cast<const float4 *>(g3 + GB_DEC + 16 * m + 4 * grp);
-            else dec[m] = make_float4(g3[GB_GAM + 63], g3[GB_GAM + 63], g3[GB_GAM + 63], g3[GB_GAM + 63]);
+            else dec[m] = make_float4(g3[GB_GC], g3[GB_GC], g3[GB_GC], g3[GB_GC]);
         }
 #pragma unroll
         for (int m = 0; m < MD; ++m) {

@@ -11,9 +11,35 @@ constexpr int kCUs = 256;   // MI355X compute units
 constexpr int GDN_GATE_CHANNEL_K = 1;  // gate kind of per-channel (KDA) gates, as in gdn.h
 
 // Per (chunk, head) gate block written by the per-chunk kernel, read by the recurrence: fp32 rows
-// of 64 tokens (scalar gate: beta, gamma_C / gamma, gamma, log2 gamma; per-channel gate: beta
-// and the [D_k] chunk decay 2^G_C).  Tail tokens carry beta = 0 and g = 0.
-enum GateBlock { GB_BETA = 0, GB_SC = 64, GB_GAM = 128, GB_GL = 192, GB_DEC = 64, GB_FLOATS = 256 };
+// of 64 tokens.  Scalar gate, with r_k and r_q the key and query rows' L2-norm factors of the
+// in-kernel prologue (else 1) folded in so that the recurrence applies none of them itself:
+//   BETA beta,  SC r_k gamma_C / gamma,  GAK r_k gamma,  GAQ r_q gamma,
+//   GLQ log2 gamma + log2 r_q,  GLK log2 gamma - log2 r_k,  GC gamma_C (one float).
+// Per-channel gate: BETA and the [D_k] chunk decay 2^G_C.  Tail tokens carry beta = 0 and g = 0.
+enum GateBlock {
+    GB_BETA = 0, GB_SC = 64, GB_GAK = 128, GB_GAQ = 192, GB_GLQ = 256, GB_GLK = 320, GB_GC = 384,
+    GB_DEC = 64, GB_FLOATS = 512
+};
+
+// The in-kernel prologue (gdn_fwd_args): raw gate inputs, beta logits, q/k rows to normalise.
+struct Prologue {
+    int qk_l2norm;          // 1: q and k rows used as x / sqrt(sum x^2 + kL2Eps)
+    int beta_sigmoid;       // 1: beta holds logits
+    const float *A_log;     // nullable [H_v]: g holds raw gate inputs
+    const float *dt_bias;   // nullable [H_v] (scalar gate) or [H_v][D_k] (per-channel gate)
+    float lower_bound;      // 0: -exp(A_log) softplus(x + b); < 0: lower_bound sigmoid(exp(A_log) (x + b))
+};
+constexpr float kL2Eps = 1e-6f;
+// log-gate of a raw input x (activation of the gate cumsum kernel on the KDA page, section 2)
+__device__ __forceinline__ float gate_activation(const Prologue &pr, float x, float a_log, float bias) {
+    const float y = x + bias;
+    if (pr.lower_bound < 0.f) return pr.lower_bound / (1.f + expf(-expf(a_log) * y));
+    const float softplus = fmaxf(y, 0.f) + log1pf(expf(-fabsf(y)));
+    return -expf(a_log) * softplus;
+}
+__device__ __forceinline__ float beta_value(const Prologue &pr, float b) {
+    return pr.beta_sigmoid ? 1.f / (1.f + expf(-b)) : b;
+}
 
 // Device-side plan tables (built by the plan kernel from cu_seqlens or the batch shape).
 struct SeqInfo {            // one per sequence
@@ -77,8 +103,9 @@ struct IntraParams {
     int n_chunks, H_qk, H_v;
     float scale;
     void *A;                // [n_chunks][H_v][64][64] in the input dtype
-    void *P;                // [n_chunks][H_v][parts][64][64]: scale Lower(Gamma) (.) Q K^T, hi (+ lo)
+    void *P;                // unused with a scalar gate (the recurrence forms P)
     float *gates;           // [n_chunks][H_v][GB_FLOATS]
+    Prologue pro;
 };
 
 struct IntraKdaParams {       // per-channel gates
@@ -92,6 +119,7 @@ struct IntraKdaParams {       // per-channel gates
     void *kg;               // [n_chunks][H_v][64][D_k]: K 2^G
     void *kd, *qg;          // [n_chunks][H_v][parts][64][D_k]: K 2^(G_C - G), Q 2^G, hi (+ lo)
     float *gates;           // [n_chunks][H_v][GB_FLOATS]: beta and the chunk decay 2^G_C
+    Prologue pro;
 };
 
 struct ChunkParams {

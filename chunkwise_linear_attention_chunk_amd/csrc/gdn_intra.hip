@@ -169,7 +169,7 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraParams p) {
     // one region: the K tile, then A_raw, then its inverse X in place (a small footprint keeps
     // eight workgroups on a CU to hide each one's serial latency)
     __shared__ __attribute__((aligned(16))) unsigned char smem[R0];
-    __shared__ float sGl[64], sB[64];
+    __shared__ float sGl[64], sB[64], sRk[64], sRq[64];
     T *sK = reinterpret_cast<T *>(smem);
     float *sX = reinterpret_cast<float *>(smem);
     float *sL = sX;
@@ -205,21 +205,34 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraParams p) {
         const int idx = tid + 256 * i, row = min(idx / VPR, last), cv = idx % VPR;
         kv[i] = *reinterpret_cast<const u32x4 *>(k + ((int64_t)(t0 + row) * p.H_qk + hq) * DK + cv * VEC);
     }
-    if (wave == 0) {
-        const int64_t idx = (int64_t)(t0 + min(lane, last)) * p.H_v + h;
-        const float gv = lane < nv ? g[idx] : 0.f;
-        const float bv = lane < nv ? to_f32(beta[idx]) : 0.f;
-        const float gl = wave_inclusive_scan(gv) * kLog2e;     // log2 gamma_t
-        const float glC = __shfl(gl, 63, 64);                  // at the last valid token
-        sGl[lane] = gl;
-        sB[lane] = bv;
-        // gate block of the recurrence
-        float *gbk = p.gates + ((int64_t)ci * p.H_v + h) * GB_FLOATS;
-        const float gam = fast_exp2(gl);
-        gbk[GB_BETA + lane] = bv;
-        gbk[GB_SC + lane] = fast_exp2(glC - gl);
-        gbk[GB_GAM + lane] = gam;
-        gbk[GB_GL + lane] = gl;
+    // prologue: the L2-norm factors r = (sum x^2 + eps)^-1/2 of every K and Q row (the VPR threads
+    // holding a row reduce their partial sums), else r = 1.  Q is read only for these factors.
+    if (p.pro.qk_l2norm) {
+        const T *q = static_cast<const T *>(p.q);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int idx = tid + 256 * i, row = min(idx / VPR, last), cv = idx % VPR;
+            u32x4 qv = *reinterpret_cast<const u32x4 *>(q + ((int64_t)(t0 + row) * p.H_qk + hq) * DK + cv * VEC);
+            const T *xk = reinterpret_cast<const T *>(&kv[i]);
+            const T *xq = reinterpret_cast<const T *>(&qv);
+            float sk = 0.f, sq = 0.f;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                sk += to_f32(xk[e]) * to_f32(xk[e]);
+                sq += to_f32(xq[e]) * to_f32(xq[e]);
+            }
+#pragma unroll
+            for (int off = 1; off < VPR; off <<= 1) {
+                sk += __shfl_xor(sk, off, 64);
+                sq += __shfl_xor(sq, off, 64);
+            }
+            if (cv == 0) {
+                sRk[idx / VPR] = 1.f / sqrtf(sk + kL2Eps);
+                sRq[idx / VPR] = 1.f / sqrtf(sq + kL2Eps);
+            }
+        }
+    } else if (tid < 64) {
+        sRk[tid] = sRq[tid] = 1.f;
     }
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
@@ -227,6 +240,26 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraParams p) {
         *reinterpret_cast<u32x4 *>(sK + row * KP + cv * VEC) = row < nv ? kv[i] : u32x4{0u, 0u, 0u, 0u};
     }
     __syncthreads();
+    if (wave == 0) {
+        const int64_t idx = (int64_t)(t0 + min(lane, last)) * p.H_v + h;
+        const float gx = g[idx];
+        const float gv = lane < nv ? (p.pro.A_log ? gate_activation(p.pro, gx, p.pro.A_log[h], p.pro.dt_bias ? p.pro.dt_bias[h] : 0.f) : gx) : 0.f;
+        const float bv = lane < nv ? beta_value(p.pro, to_f32(beta[idx])) : 0.f;
+        const float gl = wave_inclusive_scan(gv) * kLog2e;     // log2 gamma_t
+        const float glC = __shfl(gl, 63, 64);                  // at the last valid token
+        sGl[lane] = gl;
+        sB[lane] = bv;
+        // gate block of the recurrence
+        float *gbk = p.gates + ((int64_t)ci * p.H_v + h) * GB_FLOATS;
+        const float gam = fast_exp2(gl), rk = sRk[lane], rq = sRq[lane];
+        gbk[GB_BETA + lane] = bv;
+        gbk[GB_SC + lane] = fast_exp2(glC - gl) * rk;
+        gbk[GB_GAK + lane] = gam * rk;
+        gbk[GB_GAQ + lane] = gam * rq;
+        gbk[GB_GLQ + lane] = gl + __log2f(rq);
+        gbk[GB_GLK + lane] = gl - __log2f(rk);
+        if (lane == 0) gbk[GB_GC] = fast_exp2(glC);
+    }
 
     // ---- this wave's tiles of A_raw = strictLower(diag(beta) (Gamma (.) K K^T)), all accumulators
     //      in flight together
@@ -258,7 +291,7 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraParams p) {
         for (int r = 0; r < 4; ++r) {
             const int i = 16 * TI[n] + 4 * grp + r;
             const float gam = fast_exp2(sGl[i] - glj);
-            sL[i * LP + j] = (j < i) ? sB[i] * gam * aa[n][r] : 0.f;
+            sL[i * LP + j] = (j < i) ? sB[i] * gam * (sRk[i] * sRk[j]) * aa[n][r] : 0.f;
         }
     }
     __syncthreads();  // A_raw is complete
@@ -285,7 +318,9 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraParams p) {
 //   left_i = x_i (.) 2^(G_i - G_r) <= |x_i|,   right_j = k_j (.) 2^(G_r - G_j).
 // P's operands are carried as hi/lo bf16 pairs (three MFMAs per block); A_raw's are rounded once.
 // ------------------------------------------------------------------------------------------
-template <typename T, int DK>
+// PRO: some part of the prologue is on (q/k L2 norm, gate activation, sigma(beta)); the template
+// flag keeps all of it out of the plain build, whose timing it would otherwise change
+template <typename T, int DK, bool PRO>
 __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
     constexpr int VEC = Vec16<T>::N;
     constexpr int KP = DK + VEC;   // row stride of the K and Q tiles
@@ -300,7 +335,7 @@ __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
     // share for the gated output, and each lane's operand rows for P.
     __shared__ __attribute__((aligned(16))) unsigned char smem[R0 + X_BYTES];
     __shared__ __attribute__((aligned(16))) float sG[64 * GP];
-    __shared__ float sB[64];
+    __shared__ float sB[64], sRq[64], sRk[64];
     T *sK = reinterpret_cast<T *>(smem);
     float *sX = reinterpret_cast<float *>(smem);
     float *sL = reinterpret_cast<float *>(smem + R0);
@@ -347,17 +382,62 @@ __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
     constexpr int NPART = 256 / DK, NT = 64 / NPART;
     const int d = tid % DK, part = tid / DK;
     float gs[NT];
+#pragma unroll
+    for (int e = 0; e < NT; ++e) gs[e] = to_f32(g[((int64_t)(t0 + min(part * NT + e, last)) * p.H_v + h) * DK + d]);
+    if (PRO && p.pro.A_log) {
+        // prologue: raw gate inputs through the gate activation, one rolled loop over this thread's
+        // own cells of the G tile (an unrolled one would double the kernel's code)
+        const float al = p.pro.A_log[h], bias = p.pro.dt_bias ? p.pro.dt_bias[h * DK + d] : 0.f;
+#pragma unroll
+        for (int e = 0; e < NT; ++e) sG[(part * NT + e) * GP + d] = gs[e];
+#pragma unroll 1
+        for (int e = 0; e < NT; ++e) {
+            float *c = sG + (part * NT + e) * GP + d;
+            *c = gate_activation(p.pro, *c, al, bias);
+        }
+#pragma unroll
+        for (int e = 0; e < NT; ++e) gs[e] = sG[(part * NT + e) * GP + d];
+    }
     {
         float acc = 0.f;
 #pragma unroll
         for (int e = 0; e < NT; ++e) {
-            const int t = part * NT + e;
-            const float gv = to_f32(g[((int64_t)(t0 + min(t, last)) * p.H_v + h) * DK + d]);
-            acc += t < nv ? gv : 0.f;
+            acc += part * NT + e < nv ? gs[e] : 0.f;
             gs[e] = acc;
         }
     }
-    if (wave == 0) sB[lane] = lane < nv ? to_f32(beta[(int64_t)(t0 + min(lane, last)) * p.H_v + h]) : 0.f;
+    if (wave == 0) {
+        const float bv = to_f32(beta[(int64_t)(t0 + min(lane, last)) * p.H_v + h]);
+        sB[lane] = lane < nv ? (PRO ? beta_value(p.pro, bv) : bv) : 0.f;
+    }
+    if (PRO && p.pro.qk_l2norm) {
+        // prologue: the q and k rows' L2-norm factors (the VPR threads holding a row reduce their
+        // partial sums); they stay fp32 and scale the rows wherever an operand is formed, since
+        // rounding the normalised rows to the input dtype perturbs the inputs themselves
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const T *xk = reinterpret_cast<const T *>(&kv[i]);
+            const T *xq = reinterpret_cast<const T *>(&qv[i]);
+            float sk = 0.f, sq = 0.f;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                sk += to_f32(xk[e]) * to_f32(xk[e]);
+                sq += to_f32(xq[e]) * to_f32(xq[e]);
+            }
+#pragma unroll
+            for (int off = 1; off < VPR; off <<= 1) {
+                sk += __shfl_xor(sk, off, 64);
+                sq += __shfl_xor(sq, off, 64);
+            }
+            const int idx = tid + 256 * i;
+            if (idx % VPR == 0) {
+                sRk[idx / VPR] = 1.f / sqrtf(sk + kL2Eps);
+                sRq[idx / VPR] = 1.f / sqrtf(sq + kL2Eps);
+            }
+        }
+    } else if (PRO && tid < 64) {
+        sRk[tid] = sRq[tid] = 1.f;
+    }
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int idx = tid + 256 * i, row = idx / VPR, cv = idx % VPR;
@@ -385,10 +465,11 @@ __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
         T vk[VEC], qs[VEC];
         float xd[VEC], xq[VEC];
         *reinterpret_cast<u32x4 *>(qs) = qv[i];
+        const float rk = PRO ? sRk[row] : 1.f, rq = PRO ? sRq[row] : 1.f;   // L2-norm factors (else 1)
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             const float G = sG[row * GP + c0 + e], GC = sG[last * GP + c0 + e];
-            const float kk = to_f32(sK[row * KP + c0 + e]), qq = to_f32(qs[e]);
+            const float kk = to_f32(sK[row * KP + c0 + e]) * rk, qq = to_f32(qs[e]) * rq;
             const float eg = fast_exp2(G);
             vk[e] = from_f32<T>(kk * eg);
             xq[e] = qq * eg;
@@ -421,7 +502,8 @@ __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
         const int I = TI[n], J = TJ[n];
         const int r = J < I ? 16 * J + 15 : 16 * I;
         const int i = 16 * I + l16, j = 16 * J + l16;  // operand rows of this lane
-        const float qmask = i < nv ? 1.f : 0.f;
+        const float qmask = i < nv ? (PRO ? sRq[i] : 1.f) : 0.f;   // with the prologue: Q row i's L2-norm factor
+        const float rki = PRO ? sRk[i] : 1.f, rkj = PRO ? sRk[j] : 1.f;
         f32x4 aa = {0.f, 0.f, 0.f, 0.f}, pa = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
@@ -431,9 +513,9 @@ __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
             for (int e = 0; e < 8; ++e) {
                 const float gr = sG[r * GP + d0 + e];
                 const float el = fast_exp2(sG[i * GP + d0 + e] - gr), er = fast_exp2(gr - sG[j * GP + d0 + e]);
-                kl[e] = to_f32(sK[i * KP + d0 + e]) * el;
+                kl[e] = to_f32(sK[i * KP + d0 + e]) * (rki * el);
                 ql[e] = qmask * to_f32(qt[n][kb].v[e]) * el;
-                kr[e] = to_f32(sK[j * KP + d0 + e]) * er;
+                kr[e] = to_f32(sK[j * KP + d0 + e]) * (rkj * er);
             }
             Frag<T> fkl, fkr;
 #pragma unroll
@@ -478,11 +560,16 @@ hipError_t launch_intra(int dtype, int D_k, const IntraParams &p, hipStream_t s)
 hipError_t launch_intra_kda(int dtype, int D_k, const IntraKdaParams &p, hipStream_t s) {
     const dim3 grid((unsigned)p.n_chunks * (unsigned)p.H_v), block(256);
     if (p.n_chunks == 0) return hipSuccess;
-    if (dtype == 1 && D_k == 128) hipLaunchKernelGGL((intra_kda_kernel<bf16, 128>), grid, block, 0, s, p);
-    else if (dtype == 1 && D_k == 64) hipLaunchKernelGGL((intra_kda_kernel<bf16, 64>), grid, block, 0, s, p);
-    else if (dtype == 0 && D_k == 128) hipLaunchKernelGGL((intra_kda_kernel<float, 128>), grid, block, 0, s, p);
-    else if (dtype == 0 && D_k == 64) hipLaunchKernelGGL((intra_kda_kernel<float, 64>), grid, block, 0, s, p);
+    const bool pro = p.pro.qk_l2norm || p.pro.beta_sigmoid || p.pro.A_log;
+#define GDN_INTRA_KDA_CASE(T, DK)                                                                   \
+    if (pro) hipLaunchKernelGGL((intra_kda_kernel<T, DK, true>), grid, block, 0, s, p);             \
+    else hipLaunchKernelGGL((intra_kda_kernel<T, DK, false>), grid, block, 0, s, p);
+    if (dtype == 1 && D_k == 128) { GDN_INTRA_KDA_CASE(bf16, 128) }
+    else if (dtype == 1 && D_k == 64) { GDN_INTRA_KDA_CASE(bf16, 64) }
+    else if (dtype == 0 && D_k == 128) { GDN_INTRA_KDA_CASE(float, 128) }
+    else if (dtype == 0 && D_k == 64) { GDN_INTRA_KDA_CASE(float, 64) }
     else return hipErrorInvalidValue;
+#undef GDN_INTRA_KDA_CASE
     return hipGetLastError();
 }
 

@@ -39,6 +39,8 @@ class FwdArgs(ctypes.Structure):
         ("cu_seqlens_host", ctypes.c_void_p), ("N", ctypes.c_int32), ("o", ctypes.c_void_p),
         ("final_state", ctypes.c_void_p), ("cp_mode", ctypes.c_int32), ("cp_segment_chunks", ctypes.c_int32),
         ("o_dtype", ctypes.c_int32),
+        ("qk_l2norm", ctypes.c_int32), ("beta_sigmoid", ctypes.c_int32), ("A_log", ctypes.c_void_p),
+        ("dt_bias", ctypes.c_void_p), ("gate_lower_bound", ctypes.c_float),
     ]
 
 
@@ -87,7 +89,8 @@ def _check(status):
 
 
 def make_args(q, k, v, g, beta, scale=None, initial_state=None, cu_seqlens=None, cu_seqlens_cpu=None,
-              chunk_size=64, o=None, final_state=None, cp_mode="auto", cp_segment_chunks=0):
+              chunk_size=64, o=None, final_state=None, cp_mode="auto", cp_segment_chunks=0,
+              qk_l2norm=False, beta_sigmoid=False, A_log=None, dt_bias=None, gate_lower_bound=0.0):
     """Fill a gdn_fwd_args from tensors (shapes are read, nothing is computed)."""
     if q.dim() != 4:
         raise GdnError(GDN_ERR_INVALID_ARG, "q must be [B, T, H_qk, D_k]")
@@ -112,6 +115,9 @@ def make_args(q, k, v, g, beta, scale=None, initial_state=None, cu_seqlens=None,
     a.cp_mode = CP_MODES[cp_mode] if isinstance(cp_mode, str) else int(cp_mode)
     a.cp_segment_chunks = int(cp_segment_chunks)
     a.o_dtype = dt if o is None else {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}[o.dtype]
+    a.qk_l2norm, a.beta_sigmoid = int(bool(qk_l2norm)), int(bool(beta_sigmoid))
+    a.A_log, a.dt_bias = _ptr(A_log), _ptr(dt_bias)
+    a.gate_lower_bound = float(gate_lower_bound)
     return a
 
 
@@ -149,16 +155,21 @@ def fwd_timed_raw(args, workspace, workspace_bytes_, stream, events):
 
 
 def fwd(q, k, v, g, beta, scale=None, initial_state=None, cu_seqlens=None, chunk_size=64,
-        output_final_state=True, cp_mode="auto", cp_segment_chunks=0, workspace=None, out_dtype=None):
+        output_final_state=True, cp_mode="auto", cp_segment_chunks=0, workspace=None, out_dtype=None,
+        qk_l2norm=False, beta_sigmoid=False, A_log=None, dt_bias=None, gate_lower_bound=0.0):
     """Chunked-prefill forward of the gated delta rule on the GPU.
 
     q, k: [B, T, H_qk, D_k]; v: [B, T, H_v, D_v]; g: [B, T, H_v] fp32 log-gates (or
     [B, T, H_v, D_k] per-channel); beta: [B, T, H_v]; initial_state: [N, H_v, D_k, D_v] fp32;
     cu_seqlens: [N + 1] int32 token offsets of packed sequences (B == 1).
     out_dtype: dtype of o (default q's dtype; torch.float32 returns the unrounded fp32 result).
+    In-kernel prologue (gdn_fwd_args in include/gdn.h): qk_l2norm normalises q and k rows, beta_sigmoid
+    takes beta as logits, A_log ([H_v] fp32) with dt_bias ([H_v] or [H_v, D_k] fp32) and
+    gate_lower_bound takes g as raw gate inputs.
     Returns (o [B, T, H_v, D_v], final_state [N, H_v, D_k, D_v] fp32 or None).
     """
-    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("initial_state", initial_state)):
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("initial_state", initial_state),
+                    ("A_log", A_log), ("dt_bias", dt_bias)):
         _require_gpu(name, t)
     cu_dev = cu_host = None
     if cu_seqlens is not None:
@@ -170,7 +181,7 @@ def fwd(q, k, v, g, beta, scale=None, initial_state=None, cu_seqlens=None, chunk
     fs = (torch.empty((N, v.shape[2], k.shape[3], v.shape[3]), dtype=torch.float32, device=q.device)
           if output_final_state else None)
     a = make_args(q, k, v, g, beta, scale, initial_state, cu_dev, cu_host, chunk_size, o, fs, cp_mode,
-                  cp_segment_chunks)
+                  cp_segment_chunks, qk_l2norm, beta_sigmoid, A_log, dt_bias, gate_lower_bound)
     nbytes = workspace_bytes(a)
     if nbytes == 0 and q.numel() > 0:
         _check(lib().gdn_fwd(ctypes.byref(a), None, 0, None))  # reports the validation error

@@ -107,6 +107,33 @@ def make_inputs(w: Workload):
                 tokens=B * T, workload=w)
 
 
+def make_prologue_inputs(w: Workload, lower_bound=0.0, seed_offset=1000):
+    """Raw inputs for the in-kernel prologue, shaped like workload ``w``: q and k rows of random
+    lengths (Gaussian rows times exp(N(0, 0.5))), raw gate inputs ~ N(-1, 1), beta logits ~ N(0, 1),
+    A_log = log U(0.1, 1) per value head and dt_bias ~ N(0, 0.3) ([H] or [H, D]).  v, h0 and the
+    packed lengths are those of make_inputs(w).  Returns (inputs, prologue options)."""
+    x = make_inputs(w)
+    rng = np.random.default_rng(w.seed + seed_offset)
+    dt = x["q"].dtype
+    qs, gs = tuple(x["q"].shape), tuple(x["g"].shape)
+    Hv, D = x["v"].shape[2], x["q"].shape[3]
+
+    def cast(a, to):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(to)
+
+    def rows():
+        return rng.standard_normal(qs) * np.exp(0.5 * rng.standard_normal(qs[:-1] + (1,)))
+
+    x = dict(x, q=cast(rows(), dt), k=cast(rows(), dt),
+             g=cast(rng.standard_normal(gs) - 1.0, torch.float32 if w.gate == "scalar" else dt),
+             beta=cast(rng.standard_normal(tuple(x["beta"].shape)), dt))
+    pro = dict(qk_l2norm=True, beta_sigmoid=True,
+               A_log=cast(np.log(rng.uniform(0.1, 1.0, Hv)), torch.float32),
+               dt_bias=cast(0.3 * rng.standard_normal((Hv,) if w.gate == "scalar" else (Hv, D)), torch.float32),
+               gate_lower_bound=float(lower_bound))
+    return x, pro
+
+
 def to_f64(x):
     """Exact upcast of a (CPU) torch tensor to a numpy fp64 array (None passes through)."""
     return None if x is None else x.detach().to("cpu", torch.float64).numpy()

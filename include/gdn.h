@@ -89,6 +89,24 @@ typedef struct {
     int32_t cp_segment_chunks;        /* segment length L in chunks; 0 = choose */
     int32_t o_dtype;                  /* gdn_dtype of o: equal to dtype, or GDN_DTYPE_F32 to receive
                                          the fp32 result before it is rounded to a bf16 output */
+    /* In-kernel prologue (zero-initialised fields: the inputs are already processed).  Applied
+     * inside the kernels instead of as separate passes over memory (the FLA KDA notes, section
+     * "FlashKDA inference backend": l2-norm, sigma(beta) and the gate activation fused into the
+     * kernel; the gate activation of the chunked gate cumsum kernel, section 2):
+     *   qk_l2norm     1: every q and k row (one token, one head, D_k values) is used as
+     *                 x / sqrt(sum x^2 + 1e-6);
+     *   beta_sigmoid  1: beta holds logits, sigma(beta) = 1 / (1 + exp(-beta)) is used;
+     *   A_log         NULL, or [H_v] fp32: g holds raw gate inputs x and the log-gate is
+     *                   -exp(A_log[h]) * softplus(x + dt_bias)               (gate_lower_bound == 0)
+     *                   gate_lower_bound * sigmoid(exp(A_log[h]) * (x + dt_bias))   (gate_lower_bound < 0)
+     *   dt_bias       NULL (zero) or fp32 [H_v] (scalar gate) / [H_v][D_k] (per-channel gate); only
+     *                 with A_log;
+     *   gate_lower_bound  0, or a negative bound (only with A_log). */
+    int32_t qk_l2norm;
+    int32_t beta_sigmoid;
+    const float *A_log;
+    const float *dt_bias;
+    float gate_lower_bound;
 } gdn_fwd_args;
 
 /* Bytes of device workspace gdn_fwd needs for these arguments (0 on invalid

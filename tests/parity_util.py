@@ -12,6 +12,7 @@ import torch
 
 from chunkwise_linear_attention_chunk_amd import fwd, synth
 from oracle.recurrent import gdn_recurrent
+from oracle.prologue import apply_prologue
 
 TOL = {"fp32": 1e-4, "bf16": 2e-2}
 f64 = synth.to_f64
@@ -23,16 +24,17 @@ def half_ulp_bf16(a):
     return np.where(a == 0, 0.0, np.ldexp(1.0, e - 9))
 
 
-def gpu_run(x, **kw):
+def gpu_run(x, prologue=None, **kw):
     dev = torch.device("cuda:0")
     t = lambda a: None if a is None else a.to(dev)
+    pro = {} if prologue is None else {n: (t(a) if isinstance(a, torch.Tensor) else a) for n, a in prologue.items()}
     o, fs = fwd(t(x["q"]), t(x["k"]), t(x["v"]), t(x["g"]), t(x["beta"]), scale=x["scale"],
-                initial_state=t(x["h0"]), cu_seqlens=x["cu_seqlens"], **kw)
+                initial_state=t(x["h0"]), cu_seqlens=x["cu_seqlens"], **pro, **kw)
     torch.cuda.synchronize()
     return o.cpu(), fs.cpu()
 
 
-def oracle_run(x, batches=None, heads=None, seqs=None):
+def oracle_run(x, batches=None, heads=None, seqs=None, prologue=None):
     """fp64 oracle on all of x, or on the selected batch rows / heads / packed sequences.
 
     Returns (o, final) shaped like the selection, plus a function mapping full GPU outputs to
@@ -40,6 +42,9 @@ def oracle_run(x, batches=None, heads=None, seqs=None):
     q, k, v, g, b = (f64(x[n]) for n in ("q", "k", "v", "g", "beta"))
     h0 = f64(x["h0"])
     gate = x["gate"]
+    if prologue is not None:
+        pro = {n: (f64(a) if isinstance(a, torch.Tensor) else a) for n, a in prologue.items()}
+        q, k, g, b = apply_prologue(q, k, g, b, gate, **pro)
     H = v.shape[2]
     hs = list(range(H)) if heads is None else list(heads)
     G = H // q.shape[2]
@@ -83,13 +88,13 @@ def rel_max_err_rounded(got, ref):
     return max(float(excess.max() / rms), 0.0) if ref.size else 0.0
 
 
-def check(x, tol, batches=None, heads=None, seqs=None, label="", **kw):
-    o_r, f_r, pick = oracle_run(x, batches, heads, seqs)
+def check(x, tol, batches=None, heads=None, seqs=None, label="", prologue=None, **kw):
+    o_r, f_r, pick = oracle_run(x, batches, heads, seqs, prologue)
     bf16 = x["q"].dtype == torch.bfloat16
     runs = [("fp32-out", torch.float32), ("bf16-out", None)] if bf16 else [("", None)]
     worst = (0.0, 0.0)
     for tag, odt in runs:
-        o_g, f_g = gpu_run(x, out_dtype=odt, **kw)
+        o_g, f_g = gpu_run(x, prologue, out_dtype=odt, **kw)
         assert torch.isfinite(o_g.float()).all() and torch.isfinite(f_g).all(), f"{label}: non-finite output"
         o_s, f_s = pick(o_g, f_g)
         eo = rel_max_err_rounded(o_s, o_r) if tag == "bf16-out" else rel_max_err(o_s, o_r)

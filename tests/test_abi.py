@@ -84,6 +84,12 @@ def _status(a, workspace=None, nbytes=0):
     (dict(B=-1), gdn.GDN_ERR_INVALID_ARG, "B=-1"),
     (dict(cp_mode=9), gdn.GDN_ERR_INVALID_ARG, "cp_mode"),
     (dict(scale=float("nan")), gdn.GDN_ERR_INVALID_ARG, "scale"),
+    (dict(qk_l2norm=2), gdn.GDN_ERR_INVALID_ARG, "qk_l2norm"),
+    (dict(beta_sigmoid=-1), gdn.GDN_ERR_INVALID_ARG, "beta_sigmoid"),
+    (dict(dt_bias=ctypes.c_void_p(0x3000)), gdn.GDN_ERR_INVALID_ARG, "need A_log"),
+    (dict(gate_lower_bound=-5.0), gdn.GDN_ERR_INVALID_ARG, "need A_log"),
+    (dict(A_log=ctypes.c_void_p(0x3000), gate_lower_bound=2.0), gdn.GDN_ERR_INVALID_ARG, "gate_lower_bound"),
+    (dict(A_log=ctypes.c_void_p(0x3000), gate_lower_bound=float("-inf")), gdn.GDN_ERR_INVALID_ARG, "gate_lower_bound"),
 ])
 def test_invalid_arguments_are_rejected_before_launch(kw, status, msg):
     a = _args(**kw)
@@ -119,9 +125,9 @@ def test_packed_needs_single_batch_row_and_host_copy():
 def test_workspace_size_and_checks():
     a = _args()
     n = gdn.workspace_bytes(a)
-    # per chunk-head (scalar gate): A [64][64] bf16 and a 1 KiB gate block (the recurrence forms P
+    # per chunk-head (scalar gate): A [64][64] bf16 and a 2 KiB gate block (the recurrence forms P
     # itself); ceil(300/64) = 5 chunks per sequence x 2 sequences x 8 heads, plus small tables
-    per = 64 * 64 * 2 + 256 * 4
+    per = 64 * 64 * 2 + 512 * 4
     assert n >= 10 * 8 * per
     assert n < 10 * 8 * per + 4096
     assert _status(a, None, 0) == gdn.GDN_ERR_WORKSPACE
@@ -142,7 +148,7 @@ def test_workspace_with_context_parallelism():
     maps = 6 * 8 * 3 * 128 * 128 * 4
     assert maps <= on - base < maps + 4096
     # automatic choice: B*H_v = 4 with 1024 chunks splits the sequence; B*H_v = 64 does not
-    per = 64 * 64 * 2 + 256 * 4
+    per = 64 * 64 * 2 + 512 * 4
     long = gdn.workspace_bytes(_args(B=1, N=1, T=65536, H_qk=4, H_v=4))
     assert long > 1024 * 4 * per + 4 * 3 * 128 * 128 * 4
     wide = gdn.workspace_bytes(_args(B=4, N=4, T=4096, H_qk=16, H_v=16))

@@ -224,6 +224,78 @@ def test_empty_sequence_returns_initial_state():
     assert torch.equal(fs, x["h0"])
 
 
+# --------------------------------------------------------------------------- in-kernel prologue
+# Raw inputs (q, k rows of random length, raw gate inputs, beta logits) with the prologue switched on:
+# the oracle applies oracle/prologue.py in fp64, the library inside its kernels.
+def _wp(name, lower_bound=0.0, **kw):
+    return synth.make_prologue_inputs(synth.workload(name, **kw), lower_bound)
+
+
+@pytest.mark.parametrize("T", [64, 300])
+def test_prologue_fp32(T):
+    x, pro = _wp("tiny_fp32", B=2, T=T, h0=True, seed=300 + T)
+    check(x, TOL["fp32"], prologue=pro, label=f"prologue fp32 T={T}")
+
+
+def test_prologue_fp32_head_dim_128():
+    x, pro = _wp("tiny_fp32", B=1, H=2, D=128, T=200, h0=True, seed=305)
+    check(x, TOL["fp32"], prologue=pro, label="prologue fp32 D=128")
+
+
+def test_prologue_bf16():
+    x, pro = _wp("qwen3next_bf16", B=2, H=3, T=700, h0=True, seed=310)
+    check(x, TOL["bf16"], prologue=pro, label="prologue bf16")
+
+
+def test_prologue_lower_bound_grouped_heads():
+    x, pro = _wp("qwen3next_bf16", lower_bound=-5.0, B=1, H=4, H_qk=2, T=333, h0=True, seed=311)
+    check(x, TOL["bf16"], prologue=pro, label="prologue lower bound, H_v=4 H_qk=2")
+
+
+def test_prologue_bf16_head_dim_64():
+    x, pro = _wp("qwen3next_bf16", B=1, H=2, D=64, T=260, h0=True, seed=312)
+    check(x, TOL["bf16"], prologue=pro, label="prologue bf16 D=64")
+
+
+def test_prologue_packed_and_cp():
+    x, pro = _wp("varlen_bf16", n_seqs=5, lens=(1, 65, 300, 0, 700), H=3, h0=True, seed=313)
+    check(x, TOL["bf16"], prologue=pro, label="prologue packed")
+    check(x, TOL["bf16"], prologue=pro, label="prologue packed, CP", cp_mode="on", cp_segment_chunks=2)
+
+
+def test_prologue_two_workgroups_per_cu_build():
+    x, pro = _wp("qwen3next_bf16", B=8, H=16, T=150, seed=314)
+    check(x, TOL["bf16"], prologue=pro, label="prologue, 512 workgroups")
+
+
+def test_prologue_kda():
+    x, pro = _wp("kda_bf16", B=1, H=2, T=400, h0=True, seed=315)
+    check(x, TOL["bf16"], prologue=pro, label="prologue KDA bf16")
+    x, pro = _wp("kda_bf16", lower_bound=-5.0, B=1, n_seqs=3, lens=(65, 0, 200), H=2, seed=316)
+    check(x, TOL["bf16"], prologue=pro, label="prologue KDA bf16 lower bound, packed")
+
+
+@pytest.mark.parametrize("name", ["qwen3next_bf16", "kda_bf16"])
+@pytest.mark.parametrize("part", ["gates", "l2norm"])
+def test_prologue_parts(name, part):
+    """One part of the prologue on, the other inputs already in final form."""
+    w = synth.workload(name, B=1, H=2, T=333, h0=True, seed=320)
+    x0 = synth.make_inputs(w)
+    x, pro = synth.make_prologue_inputs(w)
+    if part == "gates":      # gate activation and sigma(beta); q, k as generated (unit rows)
+        x = dict(x, q=x0["q"], k=x0["k"])
+        pro = dict(pro, qk_l2norm=False)
+    else:                    # q/k L2 norm only; final gates and beta
+        x = dict(x, g=x0["g"], beta=x0["beta"])
+        pro = dict(qk_l2norm=True)
+    check(x, TOL["bf16"], prologue=pro, label=f"prologue {part} only, {name}")
+
+
+def test_prologue_kda_fp32():
+    x, pro = _wp("tiny_fp32", B=2, T=200, gate="channel", h0=True, seed=317)
+    check(x, TOL["fp32"], prologue=pro, label="prologue KDA fp32")
+
+
 # --------------------------------------------------------------------------- properties
 def test_deterministic():
     x = _w("qwen3next_bf16", B=1, H=4, T=700, h0=True, seed=21)
