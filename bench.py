@@ -23,7 +23,8 @@ sys.path.insert(0, ROOT)
 METRIC = "GDN chunked-prefill fwd tokens/s at 1 GPU + % of MFMA/HBM roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
-KERNEL_SOURCES = {"chunk": "chunkwise_linear_attention_chunk_amd/csrc/gdn_chunk.hip",
+KERNEL_SOURCES = {"recurrent": "chunkwise_linear_attention_chunk_amd/csrc/gdn_recurrent.hip",
+                  "chunk": "chunkwise_linear_attention_chunk_amd/csrc/gdn_chunk.hip",
                   "cp_pre": "chunkwise_linear_attention_chunk_amd/csrc/gdn_chunk.hip",
                   "intra": "chunkwise_linear_attention_chunk_amd/csrc/gdn_intra.hip"}
 
@@ -40,6 +41,10 @@ def parse():
     ap.add_argument("--cp-segment-chunks", type=int, default=0, help="CP segment length in chunks (0: automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: all host cores)")
+    ap.add_argument("--path", default="prefill", choices=["prefill", "decode"],
+                    help="prefill: gdn_fwd on --workload; decode: gdn_fwd_recurrent, one token per sequence "
+                         "of a --decode-batch batch with the Qwen3-Next head shape, state updated in place")
+    ap.add_argument("--decode-batch", type=int, default=256)
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 1 GiB device copy (calibrates the HBM byte counters)")
     return ap.parse_args()
@@ -137,6 +142,55 @@ def cpu_baseline(x, threads):
                       f"fp64 token recurrence, {dt:.2f} s wall"}
 
 
+def bench_decode(a, torch, gdn, synth, dev):
+    """Decode steps: one token for each of B sequences (Qwen3-Next heads: H = 16, d = 128, bf16),
+    state read and written in place.  Three state/input copies rotate so the last-level cache
+    cannot hold the previous step's state.  The kernel's compulsory bytes: the state read and
+    written (2 x 4 d^2 per sequence-head) plus q, k, v, o, g, beta of the tokens."""
+    w = synth.workload("qwen3next_bf16", B=a.decode_batch, T=1, h0=True, seed=7)
+    x = synth.make_inputs(w)
+    esz = x["q"].element_size()
+    copies = []
+    for _ in range(max(1, a.copies)):
+        t = {n: x[n].to(dev) for n in ("q", "k", "v", "g", "beta")}
+        t["state"] = x["h0"].to(dev).clone()
+        t["o"] = torch.empty(x["v"].shape, dtype=x["q"].dtype, device=dev)
+        copies.append(t)
+    argv = [gdn.make_args(c["q"], c["k"], c["v"], c["g"], c["beta"], x["scale"], c["state"], None, None, 1,
+                          c["o"], c["state"]) for c in copies]
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    for i in range(a.warmup):
+        gdn.fwd_recurrent_raw(argv[i % len(argv)], stream)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        ev[i][0].record()
+        gdn.fwd_recurrent_raw(argv[i % len(argv)], stream)   # on torch's current stream, as the events
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    k_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / a.steps
+    alg = algorithmic_bytes(x, esz)
+    achieved = alg / (k_ms * 1e-3) / 1e9
+    rec = {
+        "metric": "GDN decode (token-by-token) tokens/s at 1 GPU + % of HBM roofline", "value": x["tokens"] * a.steps / elapsed,
+        "unit": "tokens/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": elapsed / a.steps * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"decode_qwen3next_bf16_b{a.decode_batch}", "B": a.decode_batch, "T": 1,
+                   "H_qk": w.hqk, "H_v": w.H, "d_k": w.D, "d_v": w.D, "gate": w.gate, "state_in_place": True,
+                   "input_copies": len(copies)},
+        "roofline": {"bound": "hbm", "kernel": "recurrent", "alg_bytes": alg, "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic("recurrent", f"decode_qwen3next_bf16_b{a.decode_batch}")},
+        "stage_ms": {"recurrent": k_ms},
+    }
+    if not a.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(x, a.cpu_threads)
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -157,6 +211,8 @@ def main():
         print(json.dumps({"copy_probe_bytes_read": src.numel() * 4, "copy_probe_bytes_written": dst.numel() * 4}))
         return
 
+    if a.path == "decode":
+        return bench_decode(a, torch, gdn, synth, dev)
     w = synth.workload(a.workload)
     x = synth.make_inputs(w)
     esz = x["q"].element_size()

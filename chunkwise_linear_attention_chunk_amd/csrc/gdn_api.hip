@@ -67,7 +67,9 @@ int env_int(const char *name, int dflt) {
     return (s && *s) ? std::atoi(s) : dflt;
 }
 
-gdn_status validate_and_plan(const gdn_fwd_args *a, Plan *pl) {
+// Checks shared by the chunked and the token-by-token entry points (chunk: the chunk_size the
+// entry point requires).
+gdn_status validate_args(const gdn_fwd_args *a, int chunk) {
     g_last_error.clear();
     if (!a) return fail(GDN_ERR_INVALID_ARG, "args is NULL");
     if (a->B < 0 || a->T < 0) return fail(GDN_ERR_INVALID_ARG, "B=%d and T=%d must be >= 0", a->B, a->T);
@@ -79,7 +81,7 @@ gdn_status validate_and_plan(const gdn_fwd_args *a, Plan *pl) {
     if (!(a->D_v == 64 || a->D_v == 128)) return fail(GDN_ERR_UNSUPPORTED, "D_v=%d: supported 64, 128", a->D_v);
     if (a->chunk_size <= 0 || (a->chunk_size & (a->chunk_size - 1)))
         return fail(GDN_ERR_INVALID_ARG, "chunk_size=%d is not a power of two", a->chunk_size);
-    if (a->chunk_size != gdn::kChunk) return fail(GDN_ERR_UNSUPPORTED, "chunk_size=%d: supported 64", a->chunk_size);
+    if (a->chunk_size != chunk) return fail(GDN_ERR_UNSUPPORTED, "chunk_size=%d: this entry point takes %d", a->chunk_size, chunk);
     if (a->dtype != GDN_DTYPE_F32 && a->dtype != GDN_DTYPE_BF16) return fail(GDN_ERR_INVALID_ARG, "bad dtype %d", a->dtype);
     if (a->gate_kind != GDN_GATE_SCALAR && a->gate_kind != GDN_GATE_CHANNEL)
         return fail(GDN_ERR_INVALID_ARG, "bad gate_kind %d", a->gate_kind);
@@ -112,7 +114,13 @@ gdn_status validate_and_plan(const gdn_fwd_args *a, Plan *pl) {
     const int64_t tokens = (int64_t)a->B * a->T;
     if (tokens > 0 && (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->o))
         return fail(GDN_ERR_INVALID_ARG, "q, k, v, g, beta and o are required");
+    return GDN_OK;
+}
 
+gdn_status validate_and_plan(const gdn_fwd_args *a, Plan *pl) {
+    const gdn_status st = validate_args(a, gdn::kChunk);
+    if (st != GDN_OK) return st;
+    const bool packed = a->cu_seqlens_dev != nullptr;
     pl->N = a->N;
     int64_t nch = 0;
     if (packed) {
@@ -312,6 +320,21 @@ extern "C" gdn_status gdn_fwd_timed(const gdn_fwd_args *a, void *workspace, size
                                     void *const *events, uint32_t *stages_run) {
     if (!events) return fail(GDN_ERR_INVALID_ARG, "events is NULL");
     return run_fwd(a, workspace, workspace_bytes, stream, events, stages_run);
+}
+
+extern "C" gdn_status gdn_fwd_recurrent(const gdn_fwd_args *a, void *stream) {
+    const gdn_status st = validate_args(a, 1);
+    if (st != GDN_OK) return st;
+    if (a->N == 0) return GDN_OK;
+    const int64_t blocks = (int64_t)a->N * a->H_v * (a->D_v / 32);
+    if (blocks > INT32_MAX) return fail(GDN_ERR_UNSUPPORTED, "too many (sequence, head) pairs");
+    gdn::RecurrentParams rp{a->q, a->k, a->v, a->g, a->beta, a->h0, a->final_state, a->o, a->cu_seqlens_dev,
+                            a->T, a->N, a->H_qk, a->H_v, a->D_v, a->B * a->T, a->scale,
+                            a->o_dtype == GDN_DTYPE_F32 ? 1 : 0,
+                            gdn::Prologue{a->qk_l2norm, a->beta_sigmoid, a->A_log, a->dt_bias, a->gate_lower_bound}};
+    const hipError_t e = gdn::launch_recurrent(a->dtype, a->D_k, a->gate_kind, rp, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "recurrent launch: %s", hipGetErrorString(e));
+    return GDN_OK;
 }
 
 extern "C" const char *gdn_status_string(gdn_status s) {

@@ -154,6 +154,18 @@ struct FixParams {
     float *seg_start;
 };
 
+struct RecurrentParams {     // token-by-token path (gdn_fwd_recurrent)
+    const void *q, *k, *v, *g, *beta;
+    const float *h0;            // nullable; may alias final_state
+    float *final_state;         // nullable
+    void *o;
+    const int32_t *cu;          // nullable: batched input of T tokens per sequence
+    int T, N, H_qk, H_v, D_v, total_tokens;
+    float scale;
+    int o_f32;                  // 1: o is fp32
+    Prologue pro;
+};
+
 hipError_t launch_plan(const PlanParams &p, hipStream_t s);
 hipError_t launch_intra(int dtype, int D_k, const IntraParams &p, hipStream_t s);
 hipError_t launch_intra_kda(int dtype, int D_k, const IntraKdaParams &p, hipStream_t s);
@@ -161,5 +173,6 @@ hipError_t launch_chunk(int dtype, int D_k, int BV, int gate, const ChunkParams 
 // mode 1: context-parallel pre-process (chain only over value and identity columns)
 hipError_t launch_cp_pre(int dtype, int D_k, int BV, int gate, const ChunkParams &p, hipStream_t s);
 hipError_t launch_cp_fix(int dtype, int D_k, const FixParams &p, hipStream_t s);
+hipError_t launch_recurrent(int dtype, int D_k, int gate, const RecurrentParams &p, hipStream_t s);
 
 }  // namespace gdn

@@ -17,8 +17,8 @@ GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP
 DTYPE_F32, DTYPE_BF16 = 0, 1
 GATE_SCALAR, GATE_CHANNEL = 0, 1
 CP_MODES = {"auto": 0, "off": 1, "on": 2}
-EXPORTED = ("gdn_fwd", "gdn_fwd_timed", "gdn_fwd_workspace_bytes", "gdn_fwd_plan", "gdn_status_string",
-            "gdn_last_error")
+EXPORTED = ("gdn_fwd", "gdn_fwd_timed", "gdn_fwd_workspace_bytes", "gdn_fwd_plan", "gdn_fwd_recurrent",
+            "gdn_status_string", "gdn_last_error")
 STAGES = ("plan", "intra", "cp_pre", "cp_fix", "chunk")  # order of gdn_fwd_timed's stages
 
 
@@ -70,6 +70,8 @@ def lib():
         L.gdn_fwd_timed.restype = ctypes.c_int
         L.gdn_fwd_plan.argtypes = [ctypes.POINTER(FwdArgs), ctypes.POINTER(PlanInfo)]
         L.gdn_fwd_plan.restype = ctypes.c_int
+        L.gdn_fwd_recurrent.argtypes = [ctypes.POINTER(FwdArgs), ctypes.c_void_p]
+        L.gdn_fwd_recurrent.restype = ctypes.c_int
         L.gdn_status_string.argtypes = [ctypes.c_int]
         L.gdn_status_string.restype = ctypes.c_char_p
         L.gdn_last_error.argtypes = []
@@ -190,3 +192,39 @@ def fwd(q, k, v, g, beta, scale=None, initial_state=None, cu_seqlens=None, chunk
     stream = torch.cuda.current_stream(q.device).cuda_stream
     fwd_raw(a, workspace.data_ptr(), workspace.numel(), stream)
     return o, fs
+
+
+def fwd_recurrent(q, k, v, g, beta, scale=None, initial_state=None, cu_seqlens=None, output_final_state=True,
+                  state_in_place=False, out_dtype=None, qk_l2norm=False, beta_sigmoid=False, A_log=None,
+                  dt_bias=None, gate_lower_bound=0.0):
+    """Token-by-token (decode) forward on the GPU: gdn_fwd_recurrent, same arguments as ``fwd``.
+
+    state_in_place: write the final state into ``initial_state`` (which must be given) instead of
+    a new tensor.  Returns (o, final_state or None)."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("initial_state", initial_state),
+                    ("A_log", A_log), ("dt_bias", dt_bias)):
+        _require_gpu(name, t)
+    if state_in_place and initial_state is None:
+        raise GdnError(GDN_ERR_INVALID_ARG, "state_in_place needs initial_state")
+    cu_dev = cu_host = None
+    if cu_seqlens is not None:
+        cu_host = cu_seqlens.detach().to("cpu", torch.int32).contiguous()
+        cu_dev = cu_seqlens if cu_seqlens.is_cuda else cu_host.to(q.device)
+        cu_dev = cu_dev.to(torch.int32).contiguous()
+    N = q.shape[0] if cu_seqlens is None else cu_host.numel() - 1
+    o = torch.empty(v.shape, dtype=q.dtype if out_dtype is None else out_dtype, device=q.device)
+    if state_in_place:
+        fs = initial_state
+    elif output_final_state:
+        fs = torch.empty((N, v.shape[2], k.shape[3], v.shape[3]), dtype=torch.float32, device=q.device)
+    else:
+        fs = None
+    a = make_args(q, k, v, g, beta, scale, initial_state, cu_dev, cu_host, 1, o, fs, "auto", 0,
+                  qk_l2norm, beta_sigmoid, A_log, dt_bias, gate_lower_bound)
+    fwd_recurrent_raw(a, torch.cuda.current_stream(q.device).cuda_stream)
+    return o, fs
+
+
+def fwd_recurrent_raw(args, stream):
+    """Call gdn_fwd_recurrent with a prepared FwdArgs (chunk_size 1) and a stream handle (int)."""
+    _check(lib().gdn_fwd_recurrent(ctypes.byref(args), ctypes.c_void_p(stream)))

@@ -74,7 +74,7 @@ typedef struct {
     int32_t B, T;             /* batch and tokens per batch row (T = total tokens when packed) */
     int32_t H_qk, H_v;        /* query/key heads, value heads (H_v % H_qk == 0) */
     int32_t D_k, D_v;         /* head dims: D_k == D_v in {64, 128} */
-    int32_t chunk_size;       /* must be 64 */
+    int32_t chunk_size;       /* 64 for gdn_fwd, 1 for gdn_fwd_recurrent */
     int32_t dtype;            /* gdn_dtype of q, k, v, beta, o (and a channel gate) */
     int32_t gate_kind;        /* gdn_gate_kind */
     float scale;              /* output scale, usually D_k^-1/2 */
@@ -149,6 +149,20 @@ enum {
  * event to its own.  events must hold GDN_N_STAGES + 1 valid events; stages_run may be NULL. */
 gdn_status gdn_fwd_timed(const gdn_fwd_args *a, void *workspace, size_t workspace_bytes, void *stream,
                          void *const *events, uint32_t *stages_run);
+
+/* Token-by-token forward (the fused recurrent form, chunk size 1; Flash Linear Attention page,
+ * section 8): the decode path, for sequences of a few tokens (a chunked forward of fewer than
+ * about 64 tokens pays its launch and intra-chunk overheads for nothing).  Same operation,
+ * layouts and prologue fields as gdn_fwd; per sequence and value head, token by token,
+ *   S <- alpha_t S (per-channel gate: Diag(alpha_t) S),  w = beta_t (v_t - S^T k_t),
+ *   S <- S + k_t w^T,  o_t = scale S^T q_t,
+ * with the state kept in fp32 and only the final state written.
+ * Differences from gdn_fwd: chunk_size must be 1; cp_mode and cp_segment_chunks are ignored;
+ * no workspace; h0 and final_state may be the same buffer (each state is read whole before it
+ * is written: an in-place decode step).  cu_seqlens_host is still required with cu_seqlens_dev
+ * (validation); the kernel reads the device copy, clamped into [0, B*T].
+ * Errors and ownership as for gdn_fwd; enqueued on `stream`, not synchronised. */
+gdn_status gdn_fwd_recurrent(const gdn_fwd_args *a, void *stream);
 
 /* Static, human-readable name of a status code. */
 const char *gdn_status_string(gdn_status s);

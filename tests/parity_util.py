@@ -10,7 +10,7 @@ The final state is fp32 and is always checked against tol * RMS."""
 import numpy as np
 import torch
 
-from chunkwise_linear_attention_chunk_amd import fwd, synth
+from chunkwise_linear_attention_chunk_amd import fwd, fwd_recurrent, synth
 from oracle.recurrent import gdn_recurrent
 from oracle.prologue import apply_prologue
 
@@ -24,11 +24,13 @@ def half_ulp_bf16(a):
     return np.where(a == 0, 0.0, np.ldexp(1.0, e - 9))
 
 
-def gpu_run(x, prologue=None, **kw):
+def gpu_run(x, prologue=None, recurrent=False, **kw):
+    """The HIP path on x: gdn_fwd (chunked), or gdn_fwd_recurrent (token by token) if recurrent."""
     dev = torch.device("cuda:0")
     t = lambda a: None if a is None else a.to(dev)
     pro = {} if prologue is None else {n: (t(a) if isinstance(a, torch.Tensor) else a) for n, a in prologue.items()}
-    o, fs = fwd(t(x["q"]), t(x["k"]), t(x["v"]), t(x["g"]), t(x["beta"]), scale=x["scale"],
+    run = fwd_recurrent if recurrent else fwd
+    o, fs = run(t(x["q"]), t(x["k"]), t(x["v"]), t(x["g"]), t(x["beta"]), scale=x["scale"],
                 initial_state=t(x["h0"]), cu_seqlens=x["cu_seqlens"], **pro, **kw)
     torch.cuda.synchronize()
     return o.cpu(), fs.cpu()

@@ -24,8 +24,8 @@ def _declared_functions():
 
 def test_every_declared_function_is_exported():
     names = _declared_functions()
-    assert {"gdn_fwd", "gdn_fwd_timed", "gdn_fwd_workspace_bytes", "gdn_fwd_plan", "gdn_status_string",
-            "gdn_last_error"} <= set(names)
+    assert {"gdn_fwd", "gdn_fwd_timed", "gdn_fwd_workspace_bytes", "gdn_fwd_plan", "gdn_fwd_recurrent",
+            "gdn_status_string", "gdn_last_error"} <= set(names)
     lib = ctypes.CDLL(gdn.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), f"{n} is declared in gdn.h but not exported"
@@ -96,6 +96,27 @@ def test_invalid_arguments_are_rejected_before_launch(kw, status, msg):
     assert _status(a) == status
     assert msg in gdn.lib().gdn_last_error().decode()
     assert gdn.workspace_bytes(a) == 0
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(chunk_size=64), gdn.GDN_ERR_UNSUPPORTED, "takes 1"),
+    (dict(D_k=96), gdn.GDN_ERR_UNSUPPORTED, "D_k=96"),
+    (dict(H_v=6), gdn.GDN_ERR_INVALID_ARG, "multiple"),
+    (dict(N=3), gdn.GDN_ERR_INVALID_ARG, "N=3"),
+    (dict(v=None), gdn.GDN_ERR_INVALID_ARG, "required"),
+    (dict(o_dtype=gdn.DTYPE_BF16, dtype=gdn.DTYPE_F32), gdn.GDN_ERR_INVALID_ARG, "o_dtype"),
+    (dict(dt_bias=ctypes.c_void_p(0x3000)), gdn.GDN_ERR_INVALID_ARG, "need A_log"),
+])
+def test_recurrent_entry_validates_before_launch(kw, status, msg):
+    a = _args(**{"chunk_size": 1, **kw})
+    assert gdn.lib().gdn_fwd_recurrent(ctypes.byref(a), None) == status
+    assert msg in gdn.lib().gdn_last_error().decode()
+
+
+def test_chunked_entry_rejects_chunk_size_one():
+    a = _args(chunk_size=1)
+    assert _status(a) == gdn.GDN_ERR_UNSUPPORTED
+    assert "takes 64" in gdn.lib().gdn_last_error().decode()
 
 
 def _packed(cu, **kw):
