@@ -36,7 +36,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen3next_bf16")
     ap.add_argument("--copies", type=int, default=3)
-    ap.add_argument("--cp", default="auto", choices=["auto", "off", "on"],
+    ap.add_argument("--cp", default="auto", choices=["auto", "off", "on", "warmup"],
                     help="in-GPU context parallelism (auto: on when too few (sequence, head) chains fill the chip)")
     ap.add_argument("--cp-segment-chunks", type=int, default=0, help="CP segment length in chunks (0: automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

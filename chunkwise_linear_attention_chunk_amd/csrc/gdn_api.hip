@@ -38,10 +38,11 @@ struct Plan {
     int BV = 32;
     int n_slices = 0;
     bool cp = false;          // in-GPU context parallelism
+    bool warm = false;        // its warmup form (no S*, M, fix-up)
     int seg_chunks = 0;       // segment length in chunks (one segment per sequence without CP)
     int64_t total_segs = 0;
     size_t off_A = 0, off_seq = 0, off_chunks = 0, off_segs = 0, off_order = 0;
-    size_t off_sstar = 0, off_m = 0, off_start = 0;
+    size_t off_sstar = 0, off_m = 0, off_start = 0, off_warm = 0;
     size_t off_P = 0, off_gates = 0;                              // intra-chunk output matrix, gate blocks
     size_t off_kg = 0, off_kd = 0, off_qg = 0;                    // per-channel gates
     size_t bytes = 0;
@@ -88,7 +89,9 @@ gdn_status validate_args(const gdn_fwd_args *a, int chunk) {
     if (!std::isfinite(a->scale)) return fail(GDN_ERR_INVALID_ARG, "scale is not finite");
     if (a->o_dtype != a->dtype && a->o_dtype != GDN_DTYPE_F32)
         return fail(GDN_ERR_INVALID_ARG, "o_dtype %d must equal dtype %d or be fp32", a->o_dtype, a->dtype);
-    if (a->cp_mode < GDN_CP_AUTO || a->cp_mode > GDN_CP_ON) return fail(GDN_ERR_INVALID_ARG, "bad cp_mode %d", a->cp_mode);
+    if (a->cp_mode < GDN_CP_AUTO || a->cp_mode > GDN_CP_WARMUP) return fail(GDN_ERR_INVALID_ARG, "bad cp_mode %d", a->cp_mode);
+    if (!(a->cp_warmup_tol >= 0.f && a->cp_warmup_tol < 1.f))
+        return fail(GDN_ERR_INVALID_ARG, "cp_warmup_tol must be in [0, 1)");
     if ((a->qk_l2norm != 0 && a->qk_l2norm != 1) || (a->beta_sigmoid != 0 && a->beta_sigmoid != 1))
         return fail(GDN_ERR_INVALID_ARG, "qk_l2norm and beta_sigmoid must be 0 or 1");
     if (!a->A_log && (a->dt_bias || a->gate_lower_bound != 0.f))
@@ -159,9 +162,10 @@ gdn_status validate_and_plan(const gdn_fwd_args *a, Plan *pl) {
         sl = (int)std::max<int64_t>(4, (max_nc + want - 1) / want);
     }
     bool cp = false;
-    if (a->cp_mode == GDN_CP_ON) cp = true;
+    if (a->cp_mode == GDN_CP_ON || a->cp_mode == GDN_CP_WARMUP) cp = true;
     else if (a->cp_mode == GDN_CP_AUTO) cp = chains < 128 && max_nc >= 2 * (int64_t)sl;
     pl->cp = cp;
+    pl->warm = cp && a->cp_mode == GDN_CP_WARMUP;
     pl->seg_chunks = cp ? sl : kNoSegments;
     pl->total_segs = count_segments(a, pl->seg_chunks);
     if (pl->total_segs * a->H_v > INT32_MAX / 64) return fail(GDN_ERR_UNSUPPORTED, "too many segments");
@@ -184,7 +188,9 @@ gdn_status validate_and_plan(const gdn_fwd_args *a, Plan *pl) {
         pl->off_kd = off;  off = align_up(off + tiles * (esz == 2 ? 2 : 1) * 64 * a->D_k * esz);
         pl->off_qg = off;  off = align_up(off + tiles * (esz == 2 ? 2 : 1) * 64 * a->D_k * esz);
     }
-    if (cp) {
+    if (pl->warm) {
+        pl->off_warm = off;  off = align_up(off + seg_heads * sizeof(int));
+    } else if (cp) {
         pl->off_sstar = off; off = align_up(off + seg_heads * a->D_k * a->D_v * sizeof(float));
         pl->off_m = off;     off = align_up(off + seg_heads * a->D_k * a->D_k * sizeof(float));
         pl->off_start = off; off = align_up(off + seg_heads * a->D_k * a->D_v * sizeof(float));
@@ -288,7 +294,16 @@ gdn_status run_fwd(const gdn_fwd_args *a, void *workspace, size_t workspace_byte
     if (channel) {
         cp.kg = ws + pl.off_kg; cp.kd = ws + pl.off_kd; cp.qg = ws + pl.off_qg;
     }
-    if (pl.cp) {
+    if (pl.warm) {
+        // warmup CP: each segment's warmup length from the gate statistics, no pre-process maps
+        const float tol = a->cp_warmup_tol > 0.f ? a->cp_warmup_tol : 0x1p-24f;
+        gdn::WarmParams wp{segs, seq, cp.gates, a->T, a->H_v, pl.seg_chunks, (int)pl.total_segs, std::log2(tol),
+                           reinterpret_cast<int *>(ws + pl.off_warm)};
+        e = gdn::launch_warm_stats(wp, s);
+        if (e != hipSuccess) return done(fail(GDN_ERR_HIP, "warmup statistics launch: %s", hipGetErrorString(e)));
+        if ((e = mark(GDN_STAGE_CP_PRE)) != hipSuccess) return done(fail(GDN_ERR_HIP, "event: %s", hipGetErrorString(e)));
+        cp.warm = wp.warm;
+    } else if (pl.cp) {
         cp.seg_sstar = reinterpret_cast<float *>(ws + pl.off_sstar);
         cp.seg_m = reinterpret_cast<float *>(ws + pl.off_m);
         cp.seg_start = reinterpret_cast<float *>(ws + pl.off_start);

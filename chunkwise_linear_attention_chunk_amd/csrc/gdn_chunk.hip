@@ -301,9 +301,12 @@ void chunk_kernel(ChunkParams p) {
     const float *Gb = p.gates + (int64_t)h * GB_FLOATS;
     const int64_t qk_stride = (int64_t)p.H_qk * DK, v_stride = (int64_t)p.H_v * DV;
     const int qks = (int)qk_stride, vs = (int)v_stride;
-    const int nch = sg.nchunks;
-    // chunk c of the segment is chunk sg.c0 + c of the sequence
-    auto nvalid = [&](int c) { return min(kChunk, si.len - (sg.c0 + c) * kChunk); };
+    // warmup CP: the segment starts wup chunks early (from S = 0, or from h0 at the sequence start),
+    // and those chunks write no output
+    const int wup = OUT && p.warm ? p.warm[(int64_t)gs * p.H_v + h] : 0;
+    const int cs = sg.c0 - wup;                  // chunk c of this workgroup is chunk cs + c of the sequence
+    const int nch = sg.nchunks + wup;
+    auto nvalid = [&](int c) { return min(kChunk, si.len - (cs + c) * kChunk); };
 
     // ---- direct-to-LDS loads of chunk c into a tile buffer.  Instruction i of a tile goes to
     //      loader wave i % NL; each lane's byte offset within the tile source is fixed, only the
@@ -332,9 +335,9 @@ void chunk_kernel(ChunkParams p) {
     // K and Q as selected by `what` (LD_K | LD_Q; with per-channel gates K brings K 2^(G_C - G) and
     // Q brings Q 2^G's lo part):
     auto issue_kq = [&](int c, unsigned char *tb, int part_q, int np, int what) __attribute__((always_inline)) {
-        const int64_t tok = si.tok0 + (int64_t)(sg.c0 + c) * kChunk;
+        const int64_t tok = si.tok0 + (int64_t)(cs + c) * kChunk;
         const int nvc = nvalid(c);
-        const int64_t gci = si.chunk0 + sg.c0 + c;   // global chunk index
+        const int64_t gci = si.chunk0 + cs + c;      // global chunk index
         const T *kc = CH ? kgb + gci * p.H_v * 64 * DK : kb_ + tok * qk_stride;
         const T *qc = CH ? qgb + gci * p.H_v * L::NS * 64 * DK : qb + tok * qk_stride;
         const int kbytes = CH ? 64 * DK * ESZ : ((nvc - 1) * qks + DK) * ESZ;
@@ -364,9 +367,9 @@ void chunk_kernel(ChunkParams p) {
     };
     // A, P, the V slice and the gate block, as selected by `what` (LD_A | LD_P | LD_V | LD_G):
     auto issue_apvg = [&](int c, unsigned char *tb, int part_q, int np, int what) __attribute__((always_inline)) {
-        const int64_t tok = si.tok0 + (int64_t)(sg.c0 + c) * kChunk;
+        const int64_t tok = si.tok0 + (int64_t)(cs + c) * kChunk;
         const int nvc = nvalid(c);
-        const int64_t gci = si.chunk0 + sg.c0 + c;   // global chunk index
+        const int64_t gci = si.chunk0 + cs + c;      // global chunk index
         const auto rA = make_rsrc(Ab + gci * p.H_v * 4096, 4096 * ESZ);
         const auto rP = make_rsrc(Pb + gci * p.H_v * L::NS * 4096, L::NS * 4096 * ESZ);
 #pragma unroll
@@ -575,7 +578,8 @@ void chunk_kernel(ChunkParams p) {
                 }
                 // buffer stores: the resource covers the chunk's valid rows only (rows past the end
                 // are dropped by the bounds check)
-                const int64_t ebase = (int64_t)(si.tok0 + (sg.c0 + c) * kChunk) * v_stride + (int64_t)h * DV + c0;
+                if (c < wup) return;                       // warmup chunk: no output
+                const int64_t ebase = (int64_t)(si.tok0 + (cs + c) * kChunk) * v_stride + (int64_t)h * DV + c0;
                 const int oes = p.o_f32 ? 4 : ESZ;
                 const __amdgpu_buffer_rsrc_t ors = make_rsrc(static_cast<char *>(p.o) + ebase * oes,
                                                              ((nv - 1) * vs + BV) * oes);
@@ -632,8 +636,9 @@ void chunk_kernel(ChunkParams p) {
     {
         const float *s_init = nullptr;
         if constexpr (OUT) {
-            s_init = sg.j == 0 ? (p.h0 ? p.h0 + ((int64_t)n * p.H_v + h) * DK * DV : nullptr)
-                               : p.seg_start + ((int64_t)gs * p.H_v + h) * DK * DV;
+            if (cs == 0) s_init = p.h0 ? p.h0 + ((int64_t)n * p.H_v + h) * DK * DV : nullptr;  // sequence start
+            else if (!p.warm) s_init = p.seg_start + ((int64_t)gs * p.H_v + h) * DK * DV;       // fixed-up start
+            // (warmup CP from a later chunk: S = 0)
         }
 #pragma unroll
         for (int m = 0; m < MD; ++m)
@@ -912,6 +917,42 @@ __global__ __launch_bounds__(DK * 4) void cp_fix_kernel(FixParams p) {
     }
 }
 
+// ------------------------------------------------------------------------------------------
+// Warmup CP gate statistics (FlashQLA announcement, section "further optimisation through gate
+// decay": a separate kernel collects the gate statistics that fix each rank's warmup length).
+// One wave per (segment, value head): W = the fewest chunks right before the segment whose decay
+// bounds (gate block GC: the chunk decay, or for per-channel gates the product of each token's
+// largest channel decay) multiply to <= tol, summed in log2 units; the whole prefix (W = c0,
+// which starts from h0 and is exact) when none do.  The wave walks back 64 chunks per step, one
+// chunk per lane, with a running sum across steps.
+__global__ __launch_bounds__(256) void warm_stats_kernel(WarmParams p) {
+    const int lane = threadIdx.x & 63;
+    const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (unit >= p.total_segs * p.H_v) return;
+    const int gs = unit / p.H_v, h = unit - gs * p.H_v;
+    const SegInfo sg = seg_info(p.segs, gs, p.T, p.seg_chunks);
+    const SeqInfo si = seq_info(p.seq, sg.n, p.T);
+    int W = 0;
+    if (sg.j > 0) {
+        W = sg.c0;
+        float carry = 0.f;
+        for (int base = 0; base < sg.c0; base += 64) {
+            const int w = base + lane + 1;           // the warmup length whose oldest chunk this lane adds
+            const bool in = w <= sg.c0;
+            const float lg = in ? __log2f(p.gates[((int64_t)(si.chunk0 + sg.c0 - w) * p.H_v + h) * GB_FLOATS + GB_GC])
+                                : 0.f;               // log2 0 = -inf: a decay that underflowed ends the warmup
+            const float cum = carry + wave_inclusive_scan(lg);
+            const unsigned long long hit = __ballot(in && cum <= p.log2_tol);
+            if (hit) {
+                W = base + __ffsll(hit);             // lowest lane that reaches the bound, plus one
+                break;
+            }
+            carry = __shfl(cum, 63, 64);
+        }
+    }
+    if (lane == 0) p.warm[unit] = W;
+}
+
 }  // namespace
 
 hipError_t launch_plan(const PlanParams &p, hipStream_t s) {
@@ -963,6 +1004,12 @@ hipError_t launch_chunk(int dtype, int D_k, int BV, int gate, const ChunkParams 
 hipError_t launch_cp_pre(int dtype, int D_k, int BV, int gate, const ChunkParams &p, hipStream_t s) {
     return gate == GDN_GATE_CHANNEL_K ? launch_rec<1, GDN_GATE_CHANNEL_K>(dtype, D_k, BV, p, s)
                                       : launch_rec<1, 0>(dtype, D_k, BV, p, s);
+}
+hipError_t launch_warm_stats(const WarmParams &p, hipStream_t s) {
+    const int64_t units = (int64_t)p.total_segs * p.H_v;
+    if (units == 0) return hipSuccess;
+    hipLaunchKernelGGL(warm_stats_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, s, p);
+    return hipGetLastError();
 }
 hipError_t launch_cp_fix(int dtype, int D_k, const FixParams &p, hipStream_t s) {
     // XCD-aware: blockIdx = ((unit / 8) * slices + slice) * 8 + unit % 8

@@ -15,7 +15,9 @@ constexpr int GDN_GATE_CHANNEL_K = 1;  // gate kind of per-channel (KDA) gates, 
 // in-kernel prologue (else 1) folded in so that the recurrence applies none of them itself:
 //   BETA beta,  SC r_k gamma_C / gamma,  GAK r_k gamma,  GAQ r_q gamma,
 //   GLQ log2 gamma + log2 r_q,  GLK log2 gamma - log2 r_k,  GC gamma_C (one float).
-// Per-channel gate: BETA and the [D_k] chunk decay 2^G_C.  Tail tokens carry beta = 0 and g = 0.
+// Per-channel gate: BETA, the [D_k] chunk decay 2^G_C, and at GC the chunk's decay bound for
+// warmup CP (the product over its tokens of each token's largest channel decay).  Tail tokens
+// carry beta = 0 and g = 0.
 enum GateBlock {
     GB_BETA = 0, GB_SC = 64, GB_GAK = 128, GB_GAQ = 192, GB_GLQ = 256, GB_GLK = 320, GB_GC = 384,
     GB_DEC = 64, GB_FLOATS = 512
@@ -143,6 +145,16 @@ struct ChunkParams {
     // from the per-chunk kernel: P, the gate blocks, and the gated tiles of per-channel gates
     const void *kg, *kd, *qg, *P;
     const float *gates;
+    const int *warm;        // warmup CP: [total_segs][H_v] warmup chunks of each segment (nullable)
+};
+
+struct WarmParams {         // warmup CP gate statistics
+    const SegInfo *segs;    // nullptr: batched input
+    const SeqInfo *seq;
+    const float *gates;     // gate blocks (GB_GC: the chunk's decay bound)
+    int T, H_v, seg_chunks, total_segs;
+    float log2_tol;         // -inf: never (whole prefix)
+    int *warm;              // [total_segs][H_v]
 };
 
 struct FixParams {
@@ -173,6 +185,7 @@ hipError_t launch_chunk(int dtype, int D_k, int BV, int gate, const ChunkParams 
 // mode 1: context-parallel pre-process (chain only over value and identity columns)
 hipError_t launch_cp_pre(int dtype, int D_k, int BV, int gate, const ChunkParams &p, hipStream_t s);
 hipError_t launch_cp_fix(int dtype, int D_k, const FixParams &p, hipStream_t s);
+hipError_t launch_warm_stats(const WarmParams &p, hipStream_t s);
 hipError_t launch_recurrent(int dtype, int D_k, int gate, const RecurrentParams &p, hipStream_t s);
 
 }  // namespace gdn

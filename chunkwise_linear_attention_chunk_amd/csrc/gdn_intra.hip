@@ -335,7 +335,7 @@ __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
     // share for the gated output, and each lane's operand rows for P.
     __shared__ __attribute__((aligned(16))) unsigned char smem[R0 + X_BYTES];
     __shared__ __attribute__((aligned(16))) float sG[64 * GP];
-    __shared__ float sB[64], sRq[64], sRk[64];
+    __shared__ float sB[64], sRq[64], sRk[64], sWarm[4];
     T *sK = reinterpret_cast<T *>(smem);
     float *sX = reinterpret_cast<float *>(smem);
     float *sL = reinterpret_cast<float *>(smem + R0);
@@ -492,6 +492,21 @@ __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
     float *gbk = p.gates + ((int64_t)ci * p.H_v + h) * GB_FLOATS;
     if (tid < DK) gbk[GB_DEC + tid] = fast_exp2(sG[last * GP + tid]);
     if (tid < 64) gbk[GB_BETA + tid] = sB[tid];
+    // the chunk's decay bound for warmup CP: the sum over tokens of each token's largest channel
+    // log-decay (G_t - G_{t-1}, zero past the end); four threads per token, one partial per wave
+    {
+        const int t = tid >> 2, d0 = (tid & 3) * (DK / 4);
+        float m = -INFINITY;
+#pragma unroll 8
+        for (int e = 0; e < DK / 4; ++e)
+            m = fmaxf(m, sG[t * GP + d0 + e] - (t > 0 ? sG[(t - 1) * GP + d0 + e] : 0.f));
+        m = fmaxf(m, __shfl_xor(m, 1, 64));
+        m = fmaxf(m, __shfl_xor(m, 2, 64));
+        float x = (tid & 3) == 0 ? m : 0.f;
+#pragma unroll
+        for (int off = 4; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);
+        if (lane == 0) sWarm[wave] = x;
+    }
 
     // ---- A_raw (strict lower) and P (lower with diagonal): the 10 lower 16x16 tiles
     T *P = static_cast<T *>(p.P) + ((int64_t)ci * p.H_v + h) * NS * 4096;
@@ -539,7 +554,8 @@ __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
         pacc[n] = pa;
     }
     // P through the K tile's region (no longer read), then A_raw is complete and the region holds X
-    store_p<T>(smem, P, pacc, TI, TJ, ntiles);
+    store_p<T>(smem, P, pacc, TI, TJ, ntiles);   // (its barriers also publish sWarm)
+    if (tid == 0) gbk[GB_GC] = fast_exp2(sWarm[0] + sWarm[1] + sWarm[2] + sWarm[3]);
     invert_unit_lower(sL, sX);
     store_unit_lower<T>(sX, static_cast<T *>(p.A) + ((int64_t)ci * p.H_v + h) * 4096);
 }

@@ -68,7 +68,16 @@ typedef enum { GDN_GATE_SCALAR = 0, GDN_GATE_CHANNEL = 1 } gdn_gate_kind;
  * pre-process and fix-up): split each sequence into segments of L chunks, run
  * every segment from S = 0 together with its transition matrix M, fix up the
  * segment start states serially, then run all segments in parallel. */
-typedef enum { GDN_CP_AUTO = 0, GDN_CP_OFF = 1, GDN_CP_ON = 2 } gdn_cp_mode;
+/* GDN_CP_WARMUP (FlashQLA announcement, section "further optimisation through gate decay"): the
+ * same segments, but a segment after a sequence's first starts W chunks early from S = 0 instead of
+ * from the exact start state (no S*, no M, no fix-up); its warmup chunks write no output.  W is
+ * chosen per (segment, value head) by a gate-statistics kernel: the fewest whole chunks right
+ * before the segment whose decay bounds multiply to <= cp_warmup_tol (a chunk's bound: the product
+ * of its decays; per-channel gates: of each token's largest channel decay), else the whole prefix
+ * from h0 (exact).  With unit keys and 0 <= beta <= 2 the state error is at most that product
+ * times the norm of the skipped state: an approximation whose error the caller bounds by choosing
+ * cp_warmup_tol.  Never chosen by GDN_CP_AUTO. */
+typedef enum { GDN_CP_AUTO = 0, GDN_CP_OFF = 1, GDN_CP_ON = 2, GDN_CP_WARMUP = 3 } gdn_cp_mode;
 
 typedef struct {
     int32_t B, T;             /* batch and tokens per batch row (T = total tokens when packed) */
@@ -107,6 +116,7 @@ typedef struct {
     const float *A_log;
     const float *dt_bias;
     float gate_lower_bound;
+    float cp_warmup_tol;      /* GDN_CP_WARMUP: decay bound that ends a warmup, in [0, 1); 0 = 2^-24 */
 } gdn_fwd_args;
 
 /* Bytes of device workspace gdn_fwd needs for these arguments (0 on invalid
@@ -136,7 +146,8 @@ gdn_status gdn_fwd(const gdn_fwd_args *a, void *workspace, size_t workspace_byte
 enum {
     GDN_STAGE_PLAN = 0,      /* sequence / chunk tables */
     GDN_STAGE_INTRA = 1,     /* kernel (a): gate cumsum, gated beta*K K^T, inverse */
-    GDN_STAGE_CP_PRE = 2,    /* in-GPU context parallelism: per-segment S* and M */
+    GDN_STAGE_CP_PRE = 2,    /* in-GPU context parallelism: per-segment S* and M (GDN_CP_WARMUP: the
+                                gate statistics that choose each segment's warmup length) */
     GDN_STAGE_CP_FIX = 3,    /* in-GPU context parallelism: serial fix-up of segment starts */
     GDN_STAGE_CHUNK = 4,     /* kernels (b)+(d): state recurrence fused with the output */
     GDN_N_STAGES = 5

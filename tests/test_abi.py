@@ -83,6 +83,9 @@ def _status(a, workspace=None, nbytes=0):
     (dict(q=None), gdn.GDN_ERR_INVALID_ARG, "required"),
     (dict(B=-1), gdn.GDN_ERR_INVALID_ARG, "B=-1"),
     (dict(cp_mode=9), gdn.GDN_ERR_INVALID_ARG, "cp_mode"),
+    (dict(cp_mode=3, cp_warmup_tol=1.0), gdn.GDN_ERR_INVALID_ARG, "cp_warmup_tol"),
+    (dict(cp_warmup_tol=-0.5), gdn.GDN_ERR_INVALID_ARG, "cp_warmup_tol"),
+    (dict(cp_warmup_tol=float("nan")), gdn.GDN_ERR_INVALID_ARG, "cp_warmup_tol"),
     (dict(scale=float("nan")), gdn.GDN_ERR_INVALID_ARG, "scale"),
     (dict(qk_l2norm=2), gdn.GDN_ERR_INVALID_ARG, "qk_l2norm"),
     (dict(beta_sigmoid=-1), gdn.GDN_ERR_INVALID_ARG, "beta_sigmoid"),
@@ -168,6 +171,11 @@ def test_workspace_with_context_parallelism():
     on = gdn.workspace_bytes(_args(cp_mode=gdn.CP_MODES["on"], cp_segment_chunks=2))
     maps = 6 * 8 * 3 * 128 * 128 * 4
     assert maps <= on - base < maps + 4096
+    # warmup CP: no maps, one int (the warmup length) per segment and head
+    warm = gdn.workspace_bytes(_args(cp_mode=gdn.CP_MODES["warmup"], cp_segment_chunks=2))
+    assert 6 * 8 * 4 <= warm - base < 6 * 8 * 4 + 4096
+    info = gdn.plan(_args(cp_mode=gdn.CP_MODES["warmup"], cp_segment_chunks=2))
+    assert info["cp"] == 1 and info["segment_chunks"] == 2 and info["total_segments"] == 6
     # automatic choice: B*H_v = 4 with 1024 chunks splits the sequence; B*H_v = 64 does not
     per = 64 * 64 * 2 + 512 * 4
     long = gdn.workspace_bytes(_args(B=1, N=1, T=65536, H_qk=4, H_v=4))
