@@ -5,4 +5,4 @@ The computation runs in hand-written HIP kernels behind the C ABI declared in
 Importing the package does not load the native library; the first call does,
 and fails loudly if it has not been built.
 """
-from .gdn import GdnError, fwd, fwd_raw, fwd_recurrent, make_args, workspace_bytes  # noqa: F401
+from .gdn import GdnError, bwd, fwd, fwd_raw, fwd_recurrent, make_args, workspace_bytes  # noqa: F401

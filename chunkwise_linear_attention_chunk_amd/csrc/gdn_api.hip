@@ -337,6 +337,98 @@ extern "C" gdn_status gdn_fwd_timed(const gdn_fwd_args *a, void *workspace, size
     return run_fwd(a, workspace, workspace_bytes, stream, events, stages_run);
 }
 
+namespace {
+
+// the forward arguments a backward call implies (for validation and the chunk tables)
+gdn_fwd_args bwd_as_fwd(const gdn_bwd_args *b) {
+    gdn_fwd_args f{};
+    f.B = b->B; f.T = b->T; f.H_qk = b->H_qk; f.H_v = b->H_v; f.D_k = b->D_k; f.D_v = b->D_v;
+    f.chunk_size = b->chunk_size; f.dtype = b->dtype; f.gate_kind = b->gate_kind; f.scale = b->scale;
+    f.q = b->q; f.k = b->k; f.v = b->v; f.g = b->g; f.beta = b->beta; f.h0 = b->h0;
+    f.cu_seqlens_dev = b->cu_seqlens_dev; f.cu_seqlens_host = b->cu_seqlens_host; f.N = b->N;
+    f.o = const_cast<void *>(b->dout); f.cp_mode = GDN_CP_OFF; f.o_dtype = b->dtype;   // (only checked, never written)
+    return f;
+}
+
+struct BwdPlan {
+    Plan fwd;
+    size_t off_states = 0, off_dsn = 0, off_dqv = 0, off_dkv = 0, bytes = 0;
+};
+
+gdn_status validate_and_plan_bwd(const gdn_bwd_args *b, BwdPlan *bp) {
+    if (!b) return fail(GDN_ERR_INVALID_ARG, "args is NULL");
+    const gdn_fwd_args f = bwd_as_fwd(b);
+    gdn_status st = validate_and_plan(&f, &bp->fwd);
+    if (st != GDN_OK) return st;
+    if (b->gate_kind != GDN_GATE_SCALAR) return fail(GDN_ERR_UNSUPPORTED, "the backward takes the scalar gate only");
+    if ((int64_t)b->B * b->T > 0 && (!b->dq || !b->dk || !b->dv || !b->dg || !b->dbeta))
+        return fail(GDN_ERR_INVALID_ARG, "dq, dk, dv, dg and dbeta are required");
+    size_t off = align_up(bp->fwd.bytes);
+    const size_t st_bytes = (size_t)bp->fwd.total_chunks * b->H_v * b->D_k * b->D_v * sizeof(float);
+    bp->off_states = off; off = align_up(off + st_bytes);
+    bp->off_dsn = off;    off = align_up(off + st_bytes);
+    if (b->H_v != b->H_qk) {
+        const size_t g_bytes = (size_t)b->B * b->T * b->H_v * b->D_k * sizeof(float);
+        bp->off_dqv = off; off = align_up(off + g_bytes);
+        bp->off_dkv = off; off = align_up(off + g_bytes);
+    }
+    bp->bytes = off;
+    return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" size_t gdn_bwd_workspace_bytes(const gdn_bwd_args *a) {
+    BwdPlan bp;
+    if (validate_and_plan_bwd(a, &bp) != GDN_OK) return 0;
+    return bp.bytes;
+}
+
+extern "C" gdn_status gdn_bwd(const gdn_bwd_args *a, void *workspace, size_t workspace_bytes, void *stream) {
+    BwdPlan bp;
+    const gdn_status st = validate_and_plan_bwd(a, &bp);
+    if (st != GDN_OK) return st;
+    if (!workspace && bp.bytes) return fail(GDN_ERR_WORKSPACE, "workspace is NULL (needs %zu bytes)", bp.bytes);
+    if (workspace_bytes < bp.bytes)
+        return fail(GDN_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, bp.bytes);
+    if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
+        return fail(GDN_ERR_WORKSPACE, "workspace is not %zu-byte aligned", kAlign);
+    if (a->N == 0) return GDN_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+    const Plan &pl = bp.fwd;
+    const bool packed = a->cu_seqlens_dev != nullptr;
+    gdn::SeqInfo *seq = packed ? reinterpret_cast<gdn::SeqInfo *>(ws + pl.off_seq) : nullptr;
+    gdn::ChunkInfo *chunks = packed ? reinterpret_cast<gdn::ChunkInfo *>(ws + pl.off_chunks) : nullptr;
+    hipError_t e;
+    if (packed) {
+        gdn::PlanParams pp{a->cu_seqlens_dev, a->N, a->T, a->B * a->T, (int)pl.total_chunks, pl.seg_chunks,
+                           (int)pl.total_segs, seq, chunks, reinterpret_cast<gdn::SegInfo *>(ws + pl.off_segs),
+                           reinterpret_cast<int *>(ws + pl.off_order)};
+        if ((e = gdn::launch_plan(pp, s)) != hipSuccess) return fail(GDN_ERR_HIP, "plan launch: %s", hipGetErrorString(e));
+    }
+    // Step 1 of the notes: the chunks' (I + L)^-1, as the forward forms it
+    gdn::IntraParams ip{a->q, a->k, a->g, a->beta, chunks, a->T, (int)pl.total_chunks, a->H_qk, a->H_v,
+                        a->scale, ws + pl.off_A, ws + pl.off_P, reinterpret_cast<float *>(ws + pl.off_gates), gdn::Prologue{}};
+    if ((e = gdn::launch_intra(a->dtype, a->D_k, ip, s)) != hipSuccess)
+        return fail(GDN_ERR_HIP, "intra launch: %s", hipGetErrorString(e));
+    gdn::BwdParams bw{};
+    bw.q = a->q; bw.k = a->k; bw.v = a->v; bw.beta = a->beta; bw.dout = a->dout;
+    bw.g = a->g; bw.h0 = a->h0; bw.dht = a->dht; bw.A = ws + pl.off_A;
+    bw.seq = seq; bw.chunks = chunks;
+    bw.T = a->T; bw.N = a->N; bw.n_chunks = (int)pl.total_chunks; bw.H_qk = a->H_qk; bw.H_v = a->H_v; bw.D_v = a->D_v;
+    bw.T_total = (int64_t)a->B * a->T; bw.scale = a->scale;
+    bw.states = reinterpret_cast<float *>(ws + bp.off_states);
+    bw.dsnext = reinterpret_cast<float *>(ws + bp.off_dsn);
+    bw.dq = a->dq; bw.dk = a->dk; bw.dv = a->dv; bw.dg = a->dg; bw.dbeta = a->dbeta; bw.dh0 = a->dh0;
+    const bool grouped = a->H_v != a->H_qk;
+    bw.dq_v = grouped ? reinterpret_cast<float *>(ws + bp.off_dqv) : a->dq;
+    bw.dk_v = grouped ? reinterpret_cast<float *>(ws + bp.off_dkv) : a->dk;
+    if ((e = gdn::launch_bwd(a->dtype, a->D_k, bw, s)) != hipSuccess)
+        return fail(GDN_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
+    return GDN_OK;
+}
+
 extern "C" gdn_status gdn_fwd_recurrent(const gdn_fwd_args *a, void *stream) {
     const gdn_status st = validate_args(a, 1);
     if (st != GDN_OK) return st;

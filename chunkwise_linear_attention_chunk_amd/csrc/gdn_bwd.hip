@@ -1,0 +1,475 @@
+// Backward of the chunked gated delta rule (scalar gate): GDN-in-FLA notes, backward Steps 1-7,
+// and the Flash Linear Attention page, section 7 (reverse-time state-gradient scan, recomputed
+// chunk states, the gate gradient as a reverse cumsum).  A first, plain form: fp32 arithmetic on
+// LDS tiles, no matrix cores, correctness before speed.
+//
+// Per chunk (tokens i < nv, gl_i the chunk-local cumsum of the log-gates, gamma_i = e^{gl_i},
+// D_i = e^{gl_C - gl_i}, S the state entering the chunk, A the stored (I + L)^-1):
+//   forward:  X = diag(beta)(V - diag(gamma) K S),  V' = A X,
+//             O = scale (diag(gamma) Q S + Pt V'),  Pt_ij = e^{gl_i - gl_j} q_i.k_j  (j <= i),
+//             S_next = gamma_C S + K^T diag(D) V'
+//   backward, given dO and dS_next (the gradient of the state leaving the chunk):
+//     dV' = diag(D) K dS_next + scale Pt^T dO,      dX = A^T dV',     dA = dV' X^T,
+//     dL  = -A^T dA A^T (strictly lower),           dPt = scale dO V'^T (lower with diagonal),
+//     dS  = gamma_C dS_next + scale Q^T diag(gamma) dO - K^T diag(beta gamma) dX,
+//     dQ  = scale diag(gamma) dO S^T + (dPt (.) Gam) K,
+//     dK  = diag(D) V' dS_next^T - diag(beta gamma) dX S^T + (dPt (.) Gam)^T Q + E K + E^T K,
+//           E_ij = dL_ij beta_i e^{gl_i - gl_j}  (j < i),
+//     dV  = diag(beta) dX,   dbeta_i = dX_i.(v_i - gamma_i (K S)_i) + sum_j dL_ij G_ij,
+//           G_ij = e^{gl_i - gl_j} k_i.k_j  (j < i),
+//     d gl_i from every e^{gl} factor (the X, O, Pt, L, D and gamma_C terms), then
+//     dg_t = sum_{i >= t} d gl_i within the chunk (the reverse cumsum of the notes' Step 7).
+#include "gdn_internal.h"
+#include "gdn_device.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kBw = 16;     // value columns per workgroup of the two scans
+constexpr int kBw3 = 8;     // value columns per block of the per-chunk gradient kernel
+
+// chunk-local gates of chunk (tok0, nv) and head h into sgl (cumsum, natural log) and sb (beta);
+// rows past the end carry beta = 0 and the last valid cumsum.  Wave 0 only.
+template <typename T>
+__device__ __forceinline__ void load_gates(const BwdParams &p, int64_t tok0, int nv, int h, float *sgl, float *sb) {
+    const int lane = threadIdx.x & 63;
+    const int64_t t = tok0 + min(lane, max(nv - 1, 0));
+    const float gv = lane < nv ? p.g[t * p.H_v + h] : 0.f;
+    sgl[lane] = wave_inclusive_scan(gv);
+    sb[lane] = lane < nv ? to_f32(static_cast<const T *>(p.beta)[t * p.H_v + h]) : 0.f;
+}
+
+// rows [0, nv) of a [64][cols] tile of x (row stride ld, column offset c0) into fp32 LDS, zero
+// past the end
+template <typename T>
+__device__ __forceinline__ void load_rows(float *dst, int cols, const T *x, int64_t tok0, int nv, int64_t ld,
+                                          int c0) {
+    for (int idx = threadIdx.x; idx < 64 * cols; idx += blockDim.x) {
+        const int i = idx / cols, j = idx - i * cols;
+        dst[idx] = i < nv ? to_f32(x[(tok0 + i) * ld + c0 + j]) : 0.f;
+    }
+}
+
+// ---- recomputed chunk states: S entering every chunk, per (sequence, value head, kBw columns)
+template <typename T, int DK>
+__global__ __launch_bounds__(256) void bwd_states_kernel(BwdParams p) {
+    __shared__ float sK[64][DK], sA[64][64], sS[DK][kBw], sV[64][kBw], sX[64][kBw], sVp[64][kBw];
+    __shared__ float sgl[64], sb[64];
+    const int tid = threadIdx.x;
+    const int ncb = p.D_v / kBw;
+    const int cb = blockIdx.x % ncb, nh = blockIdx.x / ncb, h = nh % p.H_v, n = nh / p.H_v;
+    const int hq = h / (p.H_v / p.H_qk);
+    const SeqInfo si = seq_info(p.seq, n, p.T);
+    const int64_t DV = p.D_v;
+    for (int idx = tid; idx < DK * kBw; idx += 256) {
+        const int d = idx / kBw, j = idx % kBw;
+        sS[d][j] = p.h0 ? p.h0[(((int64_t)n * p.H_v + h) * DK + d) * DV + cb * kBw + j] : 0.f;
+    }
+    for (int c = 0; c < si.nchunks; ++c) {
+        const int64_t gci = si.chunk0 + c, tok0 = si.tok0 + (int64_t)c * kChunk;
+        const int nv = min(kChunk, si.len - c * kChunk);
+        __syncthreads();   // the previous chunk is done with every tile
+        float *st = p.states + ((gci * p.H_v + h) * DK) * DV + cb * kBw;
+        for (int idx = tid; idx < DK * kBw; idx += 256) st[(idx / kBw) * DV + idx % kBw] = sS[idx / kBw][idx % kBw];
+        load_rows<T>(&sK[0][0], DK, static_cast<const T *>(p.k) + (int64_t)hq * DK, tok0, nv, (int64_t)p.H_qk * DK, 0);
+        load_rows<T>(&sV[0][0], kBw, static_cast<const T *>(p.v) + (int64_t)h * DV, tok0, nv, (int64_t)p.H_v * DV, cb * kBw);
+        const T *Ag = static_cast<const T *>(p.A) + (gci * p.H_v + h) * 4096;
+        for (int idx = tid; idx < 4096; idx += 256) sA[idx / 64][idx % 64] = to_f32(Ag[idx]);
+        if (tid < 64) load_gates<T>(p, tok0, nv, h, sgl, sb);
+        __syncthreads();
+        for (int idx = tid; idx < 64 * kBw; idx += 256) {   // X = beta (V - gamma K S)
+            const int i = idx / kBw, j = idx % kBw;
+            float s = 0.f;
+            for (int d = 0; d < DK; ++d) s += sK[i][d] * sS[d][j];
+            sX[i][j] = sb[i] * (sV[i][j] - __expf(sgl[i]) * s);
+        }
+        __syncthreads();
+        for (int idx = tid; idx < 64 * kBw; idx += 256) {   // V' = A X (A lower)
+            const int i = idx / kBw, j = idx % kBw;
+            float s = 0.f;
+            for (int t = 0; t <= i; ++t) s += sA[i][t] * sX[t][j];
+            sVp[i][j] = s;
+        }
+        __syncthreads();
+        const float glC = sgl[63], gC = __expf(glC);
+        for (int idx = tid; idx < DK * kBw; idx += 256) {   // S = gamma_C S + K^T diag(D) V'
+            const int d = idx / kBw, j = idx % kBw;
+            float s = 0.f;
+            for (int i = 0; i < 64; ++i) s += sK[i][d] * __expf(glC - sgl[i]) * sVp[i][j];
+            sS[d][j] = gC * sS[d][j] + s;
+        }
+    }
+}
+
+// ---- reverse scan of the state gradient: dS_next of every chunk, and dh0
+template <typename T, int DK>
+__global__ __launch_bounds__(256) void bwd_dstate_kernel(BwdParams p) {
+    __shared__ float sK[64][DK], sQ[64][DK];
+    __shared__ float sA[64][64], sP[64][64];
+    __shared__ float sdS[DK][kBw], sdO[64][kBw], sKdS[64][kBw], sdVp[64][kBw], sdX[64][kBw];
+    __shared__ float sgl[64], sb[64];
+    const int tid = threadIdx.x;
+    const int ncb = p.D_v / kBw;
+    const int cb = blockIdx.x % ncb, nh = blockIdx.x / ncb, h = nh % p.H_v, n = nh / p.H_v;
+    const int hq = h / (p.H_v / p.H_qk);
+    const SeqInfo si = seq_info(p.seq, n, p.T);
+    const int64_t DV = p.D_v;
+    for (int idx = tid; idx < DK * kBw; idx += 256) {
+        const int d = idx / kBw, j = idx % kBw;
+        sdS[d][j] = p.dht ? p.dht[(((int64_t)n * p.H_v + h) * DK + d) * DV + cb * kBw + j] : 0.f;
+    }
+    for (int c = si.nchunks - 1; c >= 0; --c) {
+        const int64_t gci = si.chunk0 + c, tok0 = si.tok0 + (int64_t)c * kChunk;
+        const int nv = min(kChunk, si.len - c * kChunk);
+        __syncthreads();
+        float *dsn = p.dsnext + ((gci * p.H_v + h) * DK) * DV + cb * kBw;
+        for (int idx = tid; idx < DK * kBw; idx += 256) dsn[(idx / kBw) * DV + idx % kBw] = sdS[idx / kBw][idx % kBw];
+        const int64_t qks = (int64_t)p.H_qk * DK;
+        load_rows<T>(&sK[0][0], DK, static_cast<const T *>(p.k) + (int64_t)hq * DK, tok0, nv, qks, 0);
+        load_rows<T>(&sQ[0][0], DK, static_cast<const T *>(p.q) + (int64_t)hq * DK, tok0, nv, qks, 0);
+        load_rows<T>(&sdO[0][0], kBw, static_cast<const T *>(p.dout) + (int64_t)h * DV, tok0, nv, (int64_t)p.H_v * DV,
+                     cb * kBw);
+        const T *Ag = static_cast<const T *>(p.A) + (gci * p.H_v + h) * 4096;
+        for (int idx = tid; idx < 4096; idx += 256) sA[idx / 64][idx % 64] = to_f32(Ag[idx]);
+        if (tid < 64) load_gates<T>(p, tok0, nv, h, sgl, sb);
+        __syncthreads();
+        for (int idx = tid; idx < 4096; idx += 256) {       // scale Pt (lower with diagonal)
+            const int i = idx / 64, j = idx % 64;
+            float s = 0.f;
+            if (j <= i)
+                for (int d = 0; d < DK; ++d) s += sQ[i][d] * sK[j][d];
+            sP[i][j] = j <= i ? p.scale * __expf(sgl[i] - sgl[j]) * s : 0.f;
+        }
+        for (int idx = tid; idx < 64 * kBw; idx += 256) {   // K dS_next
+            const int i = idx / kBw, j = idx % kBw;
+            float s = 0.f;
+            for (int d = 0; d < DK; ++d) s += sK[i][d] * sdS[d][j];
+            sKdS[i][j] = s;
+        }
+        __syncthreads();
+        const float glC = sgl[63], gC = __expf(glC);
+        for (int idx = tid; idx < 64 * kBw; idx += 256) {   // dV' = D K dS_next + scale Pt^T dO
+            const int i = idx / kBw, j = idx % kBw;
+            float s = __expf(glC - sgl[i]) * sKdS[i][j];
+            for (int t = i; t < 64; ++t) s += sP[t][i] * sdO[t][j];
+            sdVp[i][j] = s;
+        }
+        __syncthreads();
+        for (int idx = tid; idx < 64 * kBw; idx += 256) {   // dX = A^T dV'
+            const int i = idx / kBw, j = idx % kBw;
+            float s = 0.f;
+            for (int t = i; t < 64; ++t) s += sA[t][i] * sdVp[t][j];
+            sdX[i][j] = s;
+        }
+        __syncthreads();
+        for (int idx = tid; idx < DK * kBw; idx += 256) {   // dS = gamma_C dS_next + Q^T(...) - K^T(...)
+            const int d = idx / kBw, j = idx % kBw;
+            float s = 0.f;
+            for (int i = 0; i < 64; ++i) {
+                const float gi = __expf(sgl[i]);
+                s += p.scale * gi * sQ[i][d] * sdO[i][j] - sb[i] * gi * sK[i][d] * sdX[i][j];
+            }
+            sdS[d][j] = gC * sdS[d][j] + s;
+        }
+    }
+    __syncthreads();
+    if (p.dh0) {
+        for (int idx = tid; idx < DK * kBw; idx += 256) {
+            const int d = idx / kBw, j = idx % kBw;
+            p.dh0[(((int64_t)n * p.H_v + h) * DK + d) * DV + cb * kBw + j] = sdS[d][j];
+        }
+    }
+}
+
+// ---- per (chunk, value head): every gradient of the chunk's inputs
+template <typename T, int DK>
+__global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdParams p) {
+    constexpr int EPT = 64 * DK / 256;          // dq / dk elements per thread (rows e * 256 / DK + tid / DK)
+    constexpr int RS = 256 / DK;
+    __shared__ float sK[64][DK], sQ[64][DK];
+    __shared__ float sA[64][64], sdA[64][64], sPt[64][64], sdP[64][64];
+    // per value-column block; after the blocks the same space holds A^T dA, then G
+    constexpr int BLK = 2 * DK * kBw3 + 9 * 64 * kBw3;
+    __shared__ float sBlk[BLK > 4096 ? BLK : 4096];
+    __shared__ float sgl[64], sb[64], sdgl[64], sdb[64], sc[64];
+    __shared__ float sdglC;
+    float (*sS)[kBw3] = reinterpret_cast<float (*)[kBw3]>(sBlk);
+    float (*sdS)[kBw3] = reinterpret_cast<float (*)[kBw3]>(sBlk + DK * kBw3);
+    float (*sV)[kBw3] = reinterpret_cast<float (*)[kBw3]>(sBlk + 2 * DK * kBw3);
+    float (*sdO)[kBw3] = sV + 64;
+    float (*sKS)[kBw3] = sV + 2 * 64;
+    float (*sQS)[kBw3] = sV + 3 * 64;
+    float (*sX)[kBw3] = sV + 4 * 64;
+    float (*sVp)[kBw3] = sV + 5 * 64;
+    float (*sKdS)[kBw3] = sV + 6 * 64;
+    float (*sdVp)[kBw3] = sV + 7 * 64;
+    float (*sdX)[kBw3] = sV + 8 * 64;
+    float (*sT)[64] = reinterpret_cast<float (*)[64]>(sBlk);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int ci = blockIdx.x / p.H_v, h = blockIdx.x - ci * p.H_v;
+    const int hq = h / (p.H_v / p.H_qk);
+    const ChunkInfo cinfo = chunk_info(p.chunks, ci, p.T);
+    const int64_t tok0 = cinfo.tok0;
+    const int nv = cinfo.nv;
+    const int64_t DV = p.D_v, qks = (int64_t)p.H_qk * DK, vs = (int64_t)p.H_v * DV;
+    load_rows<T>(&sK[0][0], DK, static_cast<const T *>(p.k) + (int64_t)hq * DK, tok0, nv, qks, 0);
+    load_rows<T>(&sQ[0][0], DK, static_cast<const T *>(p.q) + (int64_t)hq * DK, tok0, nv, qks, 0);
+    const T *Ag = static_cast<const T *>(p.A) + ((int64_t)ci * p.H_v + h) * 4096;
+    for (int idx = tid; idx < 4096; idx += 256) {
+        sA[idx / 64][idx % 64] = to_f32(Ag[idx]);
+        sdA[idx / 64][idx % 64] = 0.f;
+        sdP[idx / 64][idx % 64] = 0.f;
+    }
+    if (tid < 64) {
+        load_gates<T>(p, tok0, nv, h, sgl, sb);
+        sdgl[tid] = sdb[tid] = sc[tid] = 0.f;
+    }
+    if (tid == 0) sdglC = 0.f;
+    __syncthreads();
+    for (int idx = tid; idx < 4096; idx += 256) {           // Pt (lower with diagonal, no scale)
+        const int i = idx / 64, j = idx % 64;
+        float s = 0.f;
+        if (j <= i)
+            for (int d = 0; d < DK; ++d) s += sQ[i][d] * sK[j][d];
+        sPt[i][j] = j <= i ? __expf(sgl[i] - sgl[j]) * s : 0.f;
+    }
+    const float glC = sgl[63], gC = __expf(glC);
+    float dq[EPT], dk[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) dq[e] = dk[e] = 0.f;
+    const int col = tid % DK;
+
+    const float *St = p.states + (((int64_t)ci * p.H_v + h) * DK) * DV;
+    const float *dSt = p.dsnext + (((int64_t)ci * p.H_v + h) * DK) * DV;
+    for (int c0 = 0; c0 < p.D_v; c0 += kBw3) {
+        __syncthreads();   // Pt is complete; the previous block is done with its tiles
+        for (int idx = tid; idx < DK * kBw3; idx += 256) {
+            const int d = idx / kBw3, j = idx % kBw3;
+            sS[d][j] = St[d * DV + c0 + j];
+            sdS[d][j] = dSt[d * DV + c0 + j];
+        }
+        load_rows<T>(&sV[0][0], kBw3, static_cast<const T *>(p.v) + (int64_t)h * DV, tok0, nv, vs, c0);
+        load_rows<T>(&sdO[0][0], kBw3, static_cast<const T *>(p.dout) + (int64_t)h * DV, tok0, nv, vs, c0);
+        __syncthreads();
+        for (int idx = tid; idx < 64 * kBw3; idx += 256) {  // K S, Q S, K dS_next
+            const int i = idx / kBw3, j = idx % kBw3;
+            float a = 0.f, b = 0.f, e = 0.f;
+            for (int d = 0; d < DK; ++d) {
+                a += sK[i][d] * sS[d][j];
+                b += sQ[i][d] * sS[d][j];
+                e += sK[i][d] * sdS[d][j];
+            }
+            sKS[i][j] = a;
+            sQS[i][j] = b;
+            sKdS[i][j] = e;
+            sX[i][j] = sb[i] * (sV[i][j] - __expf(sgl[i]) * a);
+        }
+        {   // gamma_C <S, dS_next> over this block
+            float s = 0.f;
+            for (int idx = tid; idx < DK * kBw3; idx += 256) s += sS[idx / kBw3][idx % kBw3] * sdS[idx / kBw3][idx % kBw3];
+            for (int off = 1; off < 64; off <<= 1) s += __shfl_xor(s, off, 64);
+            if (lane == 0) atomicAdd(&sdglC, gC * s);
+        }
+        __syncthreads();
+        for (int idx = tid; idx < 64 * kBw3; idx += 256) {  // V' = A X
+            const int i = idx / kBw3, j = idx % kBw3;
+            float s = 0.f;
+            for (int t = 0; t <= i; ++t) s += sA[i][t] * sX[t][j];
+            sVp[i][j] = s;
+        }
+        __syncthreads();
+        for (int idx = tid; idx < 64 * kBw3; idx += 256) {  // dV' = D K dS_next + scale Pt^T dO
+            const int i = idx / kBw3, j = idx % kBw3;
+            float s = __expf(glC - sgl[i]) * sKdS[i][j];
+            float u = 0.f;
+            for (int t = i; t < 64; ++t) u += sPt[t][i] * sdO[t][j];
+            sdVp[i][j] = s + p.scale * u;
+        }
+        if (tid < 64) {    // d gl from the output's gamma and from D; the D terms' sum goes to gl_C
+            const int i = tid;
+            const float gi = __expf(sgl[i]), Di = __expf(glC - sgl[i]);
+            float o = 0.f, cd = 0.f;
+            for (int j = 0; j < kBw3; ++j) {
+                o += sdO[i][j] * sQS[i][j];
+                cd += sKdS[i][j] * sVp[i][j];
+            }
+            sdgl[i] += p.scale * gi * o - Di * cd;
+            sc[i] += Di * cd;
+        }
+        __syncthreads();
+        for (int idx = tid; idx < 64 * kBw3; idx += 256) {  // dX = A^T dV'
+            const int i = idx / kBw3, j = idx % kBw3;
+            float s = 0.f;
+            for (int t = i; t < 64; ++t) s += sA[t][i] * sdVp[t][j];
+            sdX[i][j] = s;
+        }
+        __syncthreads();
+        if (tid < 64) {    // dbeta and d gl from X; dV = diag(beta) dX
+            const int i = tid;
+            const float gi = __expf(sgl[i]);
+            float db = 0.f, dg = 0.f;
+            for (int j = 0; j < kBw3; ++j) {
+                db += sdX[i][j] * (sV[i][j] - gi * sKS[i][j]);
+                dg += sdX[i][j] * sKS[i][j];
+            }
+            sdb[i] += db;
+            sdgl[i] -= sb[i] * gi * dg;
+        }
+        for (int idx = tid; idx < 64 * kBw3; idx += 256) {
+            const int i = idx / kBw3, j = idx % kBw3;
+            if (i < nv) p.dv[(tok0 + i) * vs + (int64_t)h * DV + c0 + j] = sb[i] * sdX[i][j];
+        }
+        for (int idx = tid; idx < 4096; idx += 256) {       // dA += dV' X^T, dPt += scale dO V'^T
+            const int i = idx / 64, t = idx % 64;
+            float a = 0.f, b = 0.f;
+            for (int j = 0; j < kBw3; ++j) {
+                a += sdVp[i][j] * sX[t][j];
+                b += sdO[i][j] * sVp[t][j];
+            }
+            sdA[i][t] += a;
+            sdP[i][t] += p.scale * b;
+        }
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {                      // dq, dk terms through S and dS_next
+            const int row = e * RS + tid / DK;
+            const float gi = __expf(sgl[row]), Di = __expf(glC - sgl[row]);
+            float a = 0.f, b = 0.f, x = 0.f;
+            for (int j = 0; j < kBw3; ++j) {
+                a += sdO[row][j] * sS[col][j];
+                b += sVp[row][j] * sdS[col][j];
+                x += sdX[row][j] * sS[col][j];
+            }
+            dq[e] += p.scale * gi * a;
+            dk[e] += Di * b - sb[row] * gi * x;
+        }
+    }
+    __syncthreads();
+    // dL = -A^T dA A^T (strictly lower), via T = A^T dA in the block space
+    for (int idx = tid; idx < 4096; idx += 256) {
+        const int i = idx / 64, j = idx % 64;
+        float s = 0.f;
+        for (int t = i; t < 64; ++t) s += sA[t][i] * sdA[t][j];
+        sT[i][j] = s;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < 4096; idx += 256) {
+        const int i = idx / 64, j = idx % 64;
+        float s = 0.f;
+        if (j < i)
+            for (int t = 0; t <= j; ++t) s += sT[i][t] * sA[j][t];   // A lower: A[j][t] = 0 past t = j
+        sdA[i][j] = j < i ? -s : 0.f;                        // sdA now holds dL
+    }
+    __syncthreads();
+    for (int idx = tid; idx < 4096; idx += 256) {           // G (gated K K^T, strictly lower) over T
+        const int i = idx / 64, j = idx % 64;
+        float s = 0.f;
+        if (j < i)
+            for (int d = 0; d < DK; ++d) s += sK[i][d] * sK[j][d];
+        sT[i][j] = j < i ? __expf(sgl[i] - sgl[j]) * s : 0.f;
+    }
+    __syncthreads();
+    if (tid < 64) {        // dbeta and d gl from L = diag(beta) G, d gl from Pt
+        const int i = tid;
+        float db = 0.f, dg = 0.f;
+        for (int j = 0; j < 64; ++j) {
+            const float dpij = j <= i ? sdP[i][j] : 0.f, dpji = i <= j ? sdP[j][i] : 0.f;
+            db += sdA[i][j] * sT[i][j];
+            dg += sb[i] * sdA[i][j] * sT[i][j] - sb[j] * sdA[j][i] * sT[j][i];
+            dg += dpij * sPt[i][j] - dpji * sPt[j][i];
+        }
+        sdb[i] += db;
+        sdgl[i] += dg;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < 4096; idx += 256) {           // M1 = dPt (.) Gam over dP, E over dL
+        const int i = idx / 64, j = idx % 64;
+        const float f = __expf(sgl[i] - sgl[j]);
+        sdP[i][j] = j <= i ? sdP[i][j] * f : 0.f;
+        sdA[i][j] = j < i ? sdA[i][j] * sb[i] * f : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+        const int row = e * RS + tid / DK;
+        float a = 0.f, b = 0.f;
+        for (int j = 0; j < 64; ++j) {
+            a += sdP[row][j] * sK[j][col];
+            b += sdP[j][row] * sQ[j][col] + (sdA[row][j] + sdA[j][row]) * sK[j][col];
+        }
+        dq[e] += a;
+        dk[e] += b;
+    }
+    // gl_C: the last valid token; then dg = reverse cumsum of d gl within the chunk
+    if (tid < 64) {
+        float s = tid == 0 ? sdglC : 0.f;
+        for (int j = 0; j < 64; ++j) s += tid == 0 ? sc[j] : 0.f;
+        if (tid == 0) sdgl[max(nv - 1, 0)] += s;
+    }
+    __syncthreads();
+    if (tid < 64) {
+        const float x = tid < nv ? sdgl[tid] : 0.f;
+        const float incl = wave_inclusive_scan(x);
+        const float tot = __shfl(incl, 63, 64);
+        if (tid < nv) {
+            p.dg[(tok0 + tid) * p.H_v + h] = tot - incl + x;
+            p.dbeta[(tok0 + tid) * p.H_v + h] = sdb[tid];
+        }
+    }
+    float *dqo = p.dq_v, *dko = p.dk_v;      // per value head (fp32), reduced over groups later, or final
+    const int hs = p.dq_v == p.dq ? hq : h, hn = p.dq_v == p.dq ? p.H_qk : p.H_v;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+        const int row = e * RS + tid / DK;
+        if (row < nv) {
+            const int64_t o = ((tok0 + row) * hn + hs) * DK + col;
+            dqo[o] = dq[e];
+            dko[o] = dk[e];
+        }
+    }
+}
+
+// dq, dk of a query/key head: the sum over the value heads of its group
+__global__ __launch_bounds__(256) void bwd_group_sum_kernel(BwdParams p, int DK, int64_t n) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= n) return;
+    const int G = p.H_v / p.H_qk;
+    const int64_t d = idx % DK, th = idx / DK, hq = th % p.H_qk, t = th / p.H_qk;
+    float a = 0.f, b = 0.f;
+    for (int g = 0; g < G; ++g) {
+        const int64_t o = (t * p.H_v + hq * G + g) * DK + d;
+        a += p.dq_v[o];
+        b += p.dk_v[o];
+    }
+    p.dq[idx] = a;
+    p.dk[idx] = b;
+}
+
+}  // namespace
+
+hipError_t launch_bwd(int dtype, int D_k, const BwdParams &p, hipStream_t s) {
+    const int64_t scans = (int64_t)p.N * p.H_v * (p.D_v / kBw), chunks = (int64_t)p.n_chunks * p.H_v;
+    if (scans == 0) return hipSuccess;
+#define GDN_BWD(K, T, DK, grid) hipLaunchKernelGGL((K<T, DK>), dim3((unsigned)(grid)), dim3(256), 0, s, p)
+#define GDN_BWD_ALL(T, DK)                                  \
+    GDN_BWD(bwd_states_kernel, T, DK, scans);               \
+    GDN_BWD(bwd_dstate_kernel, T, DK, scans);               \
+    if (chunks) GDN_BWD(bwd_chunk_kernel, T, DK, chunks);
+    if (dtype == 1 && D_k == 128) { GDN_BWD_ALL(bf16, 128) }
+    else if (dtype == 1 && D_k == 64) { GDN_BWD_ALL(bf16, 64) }
+    else if (dtype == 0 && D_k == 128) { GDN_BWD_ALL(float, 128) }
+    else if (dtype == 0 && D_k == 64) { GDN_BWD_ALL(float, 64) }
+    else return hipErrorInvalidValue;
+#undef GDN_BWD_ALL
+#undef GDN_BWD
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (p.dq_v != p.dq) {
+        const int64_t n = (int64_t)p.T_total * p.H_qk * D_k;
+        if (n) hipLaunchKernelGGL(bwd_group_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, D_k, n);
+        e = hipGetLastError();
+    }
+    return e;
+}
+
+}  // namespace gdn

@@ -178,6 +178,20 @@ struct RecurrentParams {     // token-by-token path (gdn_fwd_recurrent)
     Prologue pro;
 };
 
+struct BwdParams {           // backward (gdn_bwd), scalar gate
+    const void *q, *k, *v, *beta, *dout;   // input dtype
+    const float *g, *h0, *dht;             // h0, dht nullable
+    const void *A;                         // (I + L)^-1 of every chunk, from the per-chunk kernel
+    const SeqInfo *seq;                    // nullptr: batched input
+    const ChunkInfo *chunks;
+    int T, N, n_chunks, H_qk, H_v, D_v;
+    int64_t T_total;                       // B * T
+    float scale;
+    float *states, *dsnext;                // [n_chunks][H_v][D_k][D_v]: S entering, dS leaving each chunk
+    float *dq, *dk, *dv, *dg, *dbeta, *dh0;
+    float *dq_v, *dk_v;                    // per value head when H_v > H_qk, else dq / dk
+};
+
 hipError_t launch_plan(const PlanParams &p, hipStream_t s);
 hipError_t launch_intra(int dtype, int D_k, const IntraParams &p, hipStream_t s);
 hipError_t launch_intra_kda(int dtype, int D_k, const IntraKdaParams &p, hipStream_t s);
@@ -186,6 +200,7 @@ hipError_t launch_chunk(int dtype, int D_k, int BV, int gate, const ChunkParams 
 hipError_t launch_cp_pre(int dtype, int D_k, int BV, int gate, const ChunkParams &p, hipStream_t s);
 hipError_t launch_cp_fix(int dtype, int D_k, const FixParams &p, hipStream_t s);
 hipError_t launch_warm_stats(const WarmParams &p, hipStream_t s);
+hipError_t launch_bwd(int dtype, int D_k, const BwdParams &p, hipStream_t s);
 hipError_t launch_recurrent(int dtype, int D_k, int gate, const RecurrentParams &p, hipStream_t s);
 
 }  // namespace gdn

@@ -18,7 +18,7 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 GATE_SCALAR, GATE_CHANNEL = 0, 1
 CP_MODES = {"auto": 0, "off": 1, "on": 2, "warmup": 3}
 EXPORTED = ("gdn_fwd", "gdn_fwd_timed", "gdn_fwd_workspace_bytes", "gdn_fwd_plan", "gdn_fwd_recurrent",
-            "gdn_status_string", "gdn_last_error")
+            "gdn_bwd", "gdn_bwd_workspace_bytes", "gdn_status_string", "gdn_last_error")
 STAGES = ("plan", "intra", "cp_pre", "cp_fix", "chunk")  # order of gdn_fwd_timed's stages
 
 
@@ -41,6 +41,20 @@ class FwdArgs(ctypes.Structure):
         ("o_dtype", ctypes.c_int32),
         ("qk_l2norm", ctypes.c_int32), ("beta_sigmoid", ctypes.c_int32), ("A_log", ctypes.c_void_p),
         ("dt_bias", ctypes.c_void_p), ("gate_lower_bound", ctypes.c_float), ("cp_warmup_tol", ctypes.c_float),
+    ]
+
+
+class BwdArgs(ctypes.Structure):
+    """Mirror of gdn_bwd_args."""
+    _fields_ = [
+        ("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H_qk", ctypes.c_int32), ("H_v", ctypes.c_int32),
+        ("D_k", ctypes.c_int32), ("D_v", ctypes.c_int32), ("chunk_size", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("gate_kind", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("g", ctypes.c_void_p),
+        ("beta", ctypes.c_void_p), ("h0", ctypes.c_void_p), ("cu_seqlens_dev", ctypes.c_void_p),
+        ("cu_seqlens_host", ctypes.c_void_p), ("N", ctypes.c_int32), ("dout", ctypes.c_void_p),
+        ("dht", ctypes.c_void_p), ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
+        ("dg", ctypes.c_void_p), ("dbeta", ctypes.c_void_p), ("dh0", ctypes.c_void_p),
     ]
 
 
@@ -70,6 +84,10 @@ def lib():
         L.gdn_fwd_timed.restype = ctypes.c_int
         L.gdn_fwd_plan.argtypes = [ctypes.POINTER(FwdArgs), ctypes.POINTER(PlanInfo)]
         L.gdn_fwd_plan.restype = ctypes.c_int
+        L.gdn_bwd_workspace_bytes.argtypes = [ctypes.POINTER(BwdArgs)]
+        L.gdn_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.gdn_bwd.argtypes = [ctypes.POINTER(BwdArgs), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.gdn_bwd.restype = ctypes.c_int
         L.gdn_fwd_recurrent.argtypes = [ctypes.POINTER(FwdArgs), ctypes.c_void_p]
         L.gdn_fwd_recurrent.restype = ctypes.c_int
         L.gdn_status_string.argtypes = [ctypes.c_int]
@@ -232,3 +250,44 @@ def fwd_recurrent(q, k, v, g, beta, scale=None, initial_state=None, cu_seqlens=N
 def fwd_recurrent_raw(args, stream):
     """Call gdn_fwd_recurrent with a prepared FwdArgs (chunk_size 1) and a stream handle (int)."""
     _check(lib().gdn_fwd_recurrent(ctypes.byref(args), ctypes.c_void_p(stream)))
+
+
+def make_bwd_args(q, k, v, g, beta, dout, grads, scale=None, initial_state=None, dht=None, cu_seqlens=None,
+                  cu_seqlens_cpu=None):
+    """Fill a gdn_bwd_args; grads: dict of fp32 output tensors dq, dk, dv, dg, dbeta and optional dh0."""
+    f = make_args(q, k, v, g, beta, scale, initial_state, cu_seqlens, cu_seqlens_cpu)
+    a = BwdArgs()
+    for n in ("B", "T", "H_qk", "H_v", "D_k", "D_v", "chunk_size", "dtype", "gate_kind", "scale", "q", "k", "v", "g",
+              "beta", "h0", "cu_seqlens_dev", "cu_seqlens_host", "N"):
+        setattr(a, n, getattr(f, n))
+    a.dout, a.dht = _ptr(dout), _ptr(dht)
+    for n in ("dq", "dk", "dv", "dg", "dbeta", "dh0"):
+        setattr(a, n, _ptr(grads.get(n)))
+    return a
+
+
+def bwd(q, k, v, g, beta, dout, scale=None, initial_state=None, dht=None, cu_seqlens=None, want_dh0=True):
+    """Backward of ``fwd`` (scalar gate): gdn_bwd.  Returns a dict of fp32 gradients dq, dk, dv, dg,
+    dbeta and dh0 (None unless want_dh0), shaped like the inputs."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("dout", dout),
+                    ("initial_state", initial_state), ("dht", dht)):
+        _require_gpu(name, t)
+    cu_dev = cu_host = None
+    if cu_seqlens is not None:
+        cu_host = cu_seqlens.detach().to("cpu", torch.int32).contiguous()
+        cu_dev = cu_seqlens if cu_seqlens.is_cuda else cu_host.to(q.device)
+        cu_dev = cu_dev.to(torch.int32).contiguous()
+    N = q.shape[0] if cu_seqlens is None else cu_host.numel() - 1
+    f32 = dict(dtype=torch.float32, device=q.device)
+    grads = {"dq": torch.empty(q.shape, **f32), "dk": torch.empty(k.shape, **f32), "dv": torch.empty(v.shape, **f32),
+             "dg": torch.empty(beta.shape, **f32), "dbeta": torch.empty(beta.shape, **f32),
+             "dh0": torch.empty((N, v.shape[2], k.shape[3], v.shape[3]), **f32) if want_dh0 else None}
+    a = make_bwd_args(q, k, v, g, beta, dout, grads, scale, initial_state, dht, cu_dev, cu_host)
+    nbytes = int(lib().gdn_bwd_workspace_bytes(ctypes.byref(a)))
+    if nbytes == 0 and q.numel() > 0:
+        _check(lib().gdn_bwd(ctypes.byref(a), None, 0, None))  # reports the validation error
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(lib().gdn_bwd(ctypes.byref(a), ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel()),
+                         ctypes.c_void_p(stream)))
+    return grads

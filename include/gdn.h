@@ -175,6 +175,41 @@ gdn_status gdn_fwd_timed(const gdn_fwd_args *a, void *workspace, size_t workspac
  * Errors and ownership as for gdn_fwd; enqueued on `stream`, not synchronised. */
 gdn_status gdn_fwd_recurrent(const gdn_fwd_args *a, void *stream);
 
+/* Backward of the chunked forward (GDN-in-FLA notes, backward Steps 1-7; Flash Linear Attention
+ * page, section 7): the gradients of a loss through o and the final state, with the chunk states
+ * recomputed (a forward replay), a reverse-time scan of the state gradient, and per chunk the
+ * gradients of q, k, v, beta and the gate (dg as the reverse cumsum of the cumulative log-gate's
+ * gradient within the chunk).  Scalar gate only, no prologue, no context parallelism.
+ * Inputs as for gdn_fwd (same layouts and dtype), plus
+ *   dout   [B, T, H_v, D_v]  dtype   gradient of o
+ *   dht    [N, H_v, D_k, D_v] fp32   gradient of the final state (NULL: zero)
+ * Outputs, all fp32 (written, every token of every sequence):
+ *   dq, dk [B, T, H_qk, D_k] (summed over the value heads of a group), dv [B, T, H_v, D_v],
+ *   dg, dbeta [B, T, H_v], dh0 [N, H_v, D_k, D_v] (NULL: not written).
+ * Workspace: gdn_bwd_workspace_bytes(a) bytes of device memory, 256-byte aligned (it holds the
+ * recomputed chunk states and the state gradients, 2 x 4 D_k D_v bytes per chunk and head).
+ * Errors and ownership as for gdn_fwd. */
+typedef struct {
+    int32_t B, T, H_qk, H_v, D_k, D_v;
+    int32_t chunk_size;               /* 64 */
+    int32_t dtype;                    /* gdn_dtype of q, k, v, beta and dout */
+    int32_t gate_kind;                /* GDN_GATE_SCALAR */
+    float scale;
+    const void *q, *k, *v;
+    const float *g;
+    const void *beta;
+    const float *h0;                  /* nullable */
+    const int32_t *cu_seqlens_dev;    /* nullable, as for gdn_fwd */
+    const int32_t *cu_seqlens_host;
+    int32_t N;
+    const void *dout;
+    const float *dht;                 /* nullable */
+    float *dq, *dk, *dv, *dg, *dbeta;
+    float *dh0;                       /* nullable */
+} gdn_bwd_args;
+size_t gdn_bwd_workspace_bytes(const gdn_bwd_args *a);
+gdn_status gdn_bwd(const gdn_bwd_args *a, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *gdn_status_string(gdn_status s);
 

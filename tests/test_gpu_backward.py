@@ -1,0 +1,73 @@
+"""GPU parity of the backward (gdn_bwd, scalar gate) against the fp64 autograd oracle
+(oracle/backward.py), through the C ABI.
+
+Bound per gradient tensor: max|delta| <= tol * RMS(oracle gradient), tol 1e-4 for fp32 inputs
+and 2e-2 for bf16 inputs (the forward's bounds; the backward keeps every product in fp32 and
+rounds only the stored (I + L)^-1 to the input dtype)."""
+import numpy as np
+import pytest
+import torch
+
+from chunkwise_linear_attention_chunk_amd import bwd, synth
+from oracle.backward import gdn_backward
+from parity_util import rel_max_err
+
+pytestmark = pytest.mark.gpu
+f64 = synth.to_f64
+TOL = {"fp32": 1e-4, "bf16": 2e-2}
+
+
+def _check(x, tol, label, seed=0, dht=True):
+    rng = np.random.default_rng(1000 + seed)
+    dt = x["q"].dtype
+    do = torch.from_numpy(rng.standard_normal(tuple(x["v"].shape)).astype(np.float32)).to(dt)
+    N, H, D, Dv = x["n_seqs"], x["v"].shape[2], x["q"].shape[3], x["v"].shape[3]
+    dh = torch.from_numpy(rng.standard_normal((N, H, D, Dv)).astype(np.float32)) if dht else None
+    dev = torch.device("cuda:0")
+    t = lambda a: None if a is None else a.to(dev)
+    gr = bwd(t(x["q"]), t(x["k"]), t(x["v"]), t(x["g"]), t(x["beta"]), t(do), scale=x["scale"],
+             initial_state=t(x["h0"]), dht=t(dh), cu_seqlens=x["cu_seqlens"])
+    torch.cuda.synchronize()
+    cu = None if x["cu_seqlens"] is None else x["cu_seqlens"].numpy()
+    r = gdn_backward(*(f64(x[n]) for n in ("q", "k", "v", "g", "beta")), x["scale"], f64(do), f64(x["h0"]),
+                     f64(dh), cu_seqlens=cu)
+    for n in ("dq", "dk", "dv", "dg", "dbeta", "dh0"):
+        got = f64(gr[n].cpu())
+        assert np.isfinite(got).all(), f"{label} {n}: non-finite"
+        e = rel_max_err(got, r[n])
+        print(f"[parity] backward {label} {n}: max|d|/rms = {e:.3e} (tol {tol})", flush=True)
+        assert e <= tol, f"{label} {n}: {e:.3e} > {tol}"
+
+
+@pytest.mark.parametrize("T", [1, 64, 150])
+def test_backward_fp32(T):
+    x = synth.make_inputs(synth.workload("tiny_fp32", B=2, H=2, T=T, h0=True, seed=600 + T))
+    _check(x, TOL["fp32"], f"fp32 T={T}", seed=T)
+
+
+def test_backward_fp32_head_dim_128_grouped_heads():
+    x = synth.make_inputs(synth.workload("tiny_fp32", B=1, H=4, H_qk=2, D=128, T=130, h0=True, seed=610))
+    _check(x, TOL["fp32"], "fp32 D=128 H_v=4 H_qk=2", seed=1)
+
+
+def test_backward_fp32_no_initial_state_no_dht():
+    x = synth.make_inputs(synth.workload("tiny_fp32", B=1, H=2, T=100, seed=611))
+    _check(x, TOL["fp32"], "fp32 h0=0 dht=0", seed=2, dht=False)
+
+
+def test_backward_bf16():
+    x = synth.make_inputs(synth.workload("qwen3next_bf16", B=1, H=2, T=300, h0=True, seed=612))
+    _check(x, TOL["bf16"], "bf16", seed=3)
+
+
+def test_backward_packed():
+    x = synth.make_inputs(synth.workload("varlen_bf16", n_seqs=4, lens=(1, 0, 130, 64), H=2, h0=True, seed=613))
+    _check(x, TOL["bf16"], "bf16 packed", seed=4)
+
+
+def test_backward_rejects_per_channel_gate():
+    from chunkwise_linear_attention_chunk_amd.gdn import GdnError
+    x = synth.make_inputs(synth.workload("kda_bf16", B=1, H=2, T=64, seed=614))
+    dev = torch.device("cuda:0")
+    with pytest.raises(GdnError, match="scalar gate"):
+        bwd(*(x[n].to(dev) for n in ("q", "k", "v", "g", "beta")), x["v"].to(dev), scale=x["scale"])
