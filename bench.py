@@ -41,9 +41,10 @@ def parse():
     ap.add_argument("--cp-segment-chunks", type=int, default=0, help="CP segment length in chunks (0: automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: all host cores)")
-    ap.add_argument("--path", default="prefill", choices=["prefill", "decode"],
+    ap.add_argument("--path", default="prefill", choices=["prefill", "decode", "backward"],
                     help="prefill: gdn_fwd on --workload; decode: gdn_fwd_recurrent, one token per sequence "
-                         "of a --decode-batch batch with the Qwen3-Next head shape, state updated in place")
+                         "of a --decode-batch batch with the Qwen3-Next head shape, state updated in place; "
+                         "backward: gdn_bwd on --workload (scalar gate)")
     ap.add_argument("--decode-batch", type=int, default=256)
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 1 GiB device copy (calibrates the HBM byte counters)")
@@ -191,6 +192,63 @@ def bench_decode(a, torch, gdn, synth, dev):
     print(json.dumps(rec), flush=True)
 
 
+def bench_backward(a, torch, gdn, synth, dev):
+    """Backward steps (gdn_bwd) on --workload with a random output gradient and a random final-state
+    gradient.  Compulsory bytes: the forward's inputs and dO (and dht) read once, the fp32 gradients
+    written once."""
+    w = synth.workload(a.workload)
+    x = synth.make_inputs(w)
+    esz = x["q"].element_size()
+    gen = torch.Generator().manual_seed(11)
+    N, H, D, Dv = x["n_seqs"], x["v"].shape[2], x["q"].shape[3], x["v"].shape[3]
+    t = {n: x[n].to(dev) for n in ("q", "k", "v", "g", "beta")}
+    h0 = None if x["h0"] is None else x["h0"].to(dev)
+    do = torch.randn(tuple(x["v"].shape), generator=gen).to(x["q"].dtype).to(dev)
+    dht = torch.randn((N, H, D, Dv), generator=gen).to(dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    grads = {"dq": torch.empty(t["q"].shape, **f32), "dk": torch.empty(t["k"].shape, **f32),
+             "dv": torch.empty(t["v"].shape, **f32), "dg": torch.empty(t["beta"].shape, **f32),
+             "dbeta": torch.empty(t["beta"].shape, **f32), "dh0": torch.empty((N, H, D, Dv), **f32)}
+    cu_host = None if x["cu_seqlens"] is None else x["cu_seqlens"].to(torch.int32)
+    cu_dev = None if cu_host is None else cu_host.to(dev)
+    args = gdn.make_bwd_args(t["q"], t["k"], t["v"], t["g"], t["beta"], do, grads, x["scale"], h0, dht, cu_dev, cu_host)
+    L = gdn.lib()
+    nbytes = int(L.gdn_bwd_workspace_bytes(ctypes.byref(args)))
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    run = lambda: gdn._check(L.gdn_bwd(ctypes.byref(args), ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(nbytes),
+                                       ctypes.c_void_p(stream)))
+    for _ in range(a.warmup):
+        run()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        ev[i][0].record()
+        run()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / a.steps
+    tokens = x["tokens"]
+    H_qk = x["q"].shape[2]
+    alg = algorithmic_bytes(x, esz) + N * H * D * Dv * 4     # q, k, v, dO, beta, g, h0, dht read, dh0 written
+    alg += tokens * (2 * H_qk * D + H * Dv + 2 * H) * 4          # dq, dk, dv, dg, dbeta written (fp32)
+    achieved = alg / (ms * 1e-3) / 1e9
+    rec = {
+        "metric": "GDN chunked backward tokens/s at 1 GPU + % of HBM roofline", "value": tokens * a.steps / elapsed,
+        "unit": "tokens/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": elapsed / a.steps * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": {2: "bf16", 4: "f32"}[esz],
+        "data": "synthetic",
+        "config": {"workload": w.name, "T_total": tokens, "seqs": N, "H_qk": H_qk, "H_v": H, "d_k": D, "d_v": Dv,
+                   "chunk": 64, "gate": w.gate, "h0": w.h0},
+        "roofline": {"bound": "hbm", "kernel": "whole backward", "alg_bytes": alg, "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+        "stage_ms": {"backward": ms},
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -213,6 +271,8 @@ def main():
 
     if a.path == "decode":
         return bench_decode(a, torch, gdn, synth, dev)
+    if a.path == "backward":
+        return bench_backward(a, torch, gdn, synth, dev)
     w = synth.workload(a.workload)
     x = synth.make_inputs(w)
     esz = x["q"].element_size()

@@ -352,7 +352,7 @@ gdn_fwd_args bwd_as_fwd(const gdn_bwd_args *b) {
 
 struct BwdPlan {
     Plan fwd;
-    size_t off_states = 0, off_dsn = 0, off_dqv = 0, off_dkv = 0, bytes = 0;
+    size_t off_states = 0, off_dsn = 0, off_pmat = 0, off_dqv = 0, off_dkv = 0, bytes = 0;
 };
 
 gdn_status validate_and_plan_bwd(const gdn_bwd_args *b, BwdPlan *bp) {
@@ -367,6 +367,7 @@ gdn_status validate_and_plan_bwd(const gdn_bwd_args *b, BwdPlan *bp) {
     const size_t st_bytes = (size_t)bp->fwd.total_chunks * b->H_v * b->D_k * b->D_v * sizeof(float);
     bp->off_states = off; off = align_up(off + st_bytes);
     bp->off_dsn = off;    off = align_up(off + st_bytes);
+    bp->off_pmat = off;   off = align_up(off + (size_t)bp->fwd.total_chunks * b->H_v * 4096 * sizeof(float));
     if (b->H_v != b->H_qk) {
         const size_t g_bytes = (size_t)b->B * b->T * b->H_v * b->D_k * sizeof(float);
         bp->off_dqv = off; off = align_up(off + g_bytes);
@@ -420,6 +421,7 @@ extern "C" gdn_status gdn_bwd(const gdn_bwd_args *a, void *workspace, size_t wor
     bw.T_total = (int64_t)a->B * a->T; bw.scale = a->scale;
     bw.states = reinterpret_cast<float *>(ws + bp.off_states);
     bw.dsnext = reinterpret_cast<float *>(ws + bp.off_dsn);
+    bw.pmat = reinterpret_cast<float *>(ws + bp.off_pmat);
     bw.dq = a->dq; bw.dk = a->dk; bw.dv = a->dv; bw.dg = a->dg; bw.dbeta = a->dbeta; bw.dh0 = a->dh0;
     const bool grouped = a->H_v != a->H_qk;
     bw.dq_v = grouped ? reinterpret_cast<float *>(ws + bp.off_dqv) : a->dq;

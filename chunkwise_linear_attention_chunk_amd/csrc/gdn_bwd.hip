@@ -41,19 +41,43 @@ __device__ __forceinline__ void load_gates(const BwdParams &p, int64_t tok0, int
 
 // rows [0, nv) of a [64][cols] tile of x (row stride ld, column offset c0) into fp32 LDS, zero
 // past the end
-template <typename T>
-__device__ __forceinline__ void load_rows(float *dst, int cols, const T *x, int64_t tok0, int nv, int64_t ld,
+// (256 threads; the element loads of a thread are independent and issued together, rows past
+// the end are clamped to the last valid row and zeroed at the store)
+template <int COLS, typename T>
+__device__ __forceinline__ void load_rows(float *dst, int dst_ld, const T *x, int64_t tok0, int nv, int64_t ld,
                                           int c0) {
-    for (int idx = threadIdx.x; idx < 64 * cols; idx += blockDim.x) {
-        const int i = idx / cols, j = idx - i * cols;
-        dst[idx] = i < nv ? to_f32(x[(tok0 + i) * ld + c0 + j]) : 0.f;
+    constexpr int N = 64 * COLS / 256;
+    float v[N];
+#pragma unroll
+    for (int it = 0; it < N; ++it) {
+        const int idx = threadIdx.x + 256 * it, i = idx / COLS, j = idx - i * COLS;
+        v[it] = to_f32(x[(tok0 + min(i, nv - 1)) * ld + c0 + j]);
+    }
+#pragma unroll
+    for (int it = 0; it < N; ++it) {
+        const int idx = threadIdx.x + 256 * it, i = idx / COLS, j = idx - i * COLS;
+        dst[i * dst_ld + j] = i < nv ? v[it] : 0.f;
+    }
+}
+
+// a [64][64] tile of the input dtype (or fp32) into fp32 LDS rows of stride 65
+template <typename T>
+__device__ __forceinline__ void load_tile64(float (*dst)[65], const T *x) {
+    float v[16];
+#pragma unroll
+    for (int it = 0; it < 16; ++it) v[it] = to_f32(x[threadIdx.x + 256 * it]);
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+        const int idx = threadIdx.x + 256 * it;
+        dst[idx / 64][idx % 64] = v[it];
     }
 }
 
 // ---- recomputed chunk states: S entering every chunk, per (sequence, value head, kBw columns)
 template <typename T, int DK>
 __global__ __launch_bounds__(256) void bwd_states_kernel(BwdParams p) {
-    __shared__ float sK[64][DK], sA[64][64], sS[DK][kBw], sV[64][kBw], sX[64][kBw], sVp[64][kBw];
+    // odd row strides (+1) keep the column walks of these tiles free of LDS bank conflicts
+    __shared__ float sK[64][DK + 1], sA[64][65], sS[DK][kBw + 1], sV[64][kBw + 1], sX[64][kBw + 1], sVp[64][kBw + 1];
     __shared__ float sgl[64], sb[64];
     const int tid = threadIdx.x;
     const int ncb = p.D_v / kBw;
@@ -71,10 +95,9 @@ __global__ __launch_bounds__(256) void bwd_states_kernel(BwdParams p) {
         __syncthreads();   // the previous chunk is done with every tile
         float *st = p.states + ((gci * p.H_v + h) * DK) * DV + cb * kBw;
         for (int idx = tid; idx < DK * kBw; idx += 256) st[(idx / kBw) * DV + idx % kBw] = sS[idx / kBw][idx % kBw];
-        load_rows<T>(&sK[0][0], DK, static_cast<const T *>(p.k) + (int64_t)hq * DK, tok0, nv, (int64_t)p.H_qk * DK, 0);
-        load_rows<T>(&sV[0][0], kBw, static_cast<const T *>(p.v) + (int64_t)h * DV, tok0, nv, (int64_t)p.H_v * DV, cb * kBw);
-        const T *Ag = static_cast<const T *>(p.A) + (gci * p.H_v + h) * 4096;
-        for (int idx = tid; idx < 4096; idx += 256) sA[idx / 64][idx % 64] = to_f32(Ag[idx]);
+        load_rows<DK>(&sK[0][0], DK + 1, static_cast<const T *>(p.k) + (int64_t)hq * DK, tok0, nv, (int64_t)p.H_qk * DK, 0);
+        load_rows<kBw>(&sV[0][0], kBw + 1, static_cast<const T *>(p.v) + (int64_t)h * DV, tok0, nv, (int64_t)p.H_v * DV, cb * kBw);
+        load_tile64(sA, static_cast<const T *>(p.A) + (gci * p.H_v + h) * 4096);
         if (tid < 64) load_gates<T>(p, tok0, nv, h, sgl, sb);
         __syncthreads();
         for (int idx = tid; idx < 64 * kBw; idx += 256) {   // X = beta (V - gamma K S)
@@ -101,12 +124,37 @@ __global__ __launch_bounds__(256) void bwd_states_kernel(BwdParams p) {
     }
 }
 
+// ---- scale Pt of every (chunk, value head), fp32 [64][64], for the reverse scan (which would
+//      otherwise form it once per value-column group)
+template <typename T, int DK>
+__global__ __launch_bounds__(256) void bwd_p_kernel(BwdParams p) {
+    __shared__ float sK[64][DK + 1], sQ[64][DK + 1];
+    __shared__ float sgl[64], sb[64];
+    const int tid = threadIdx.x;
+    const int ci = blockIdx.x / p.H_v, h = blockIdx.x - ci * p.H_v;
+    const int hq = h / (p.H_v / p.H_qk);
+    const ChunkInfo cinfo = chunk_info(p.chunks, ci, p.T);
+    const int64_t qks = (int64_t)p.H_qk * DK;
+    load_rows<DK>(&sK[0][0], DK + 1, static_cast<const T *>(p.k) + (int64_t)hq * DK, cinfo.tok0, cinfo.nv, qks, 0);
+    load_rows<DK>(&sQ[0][0], DK + 1, static_cast<const T *>(p.q) + (int64_t)hq * DK, cinfo.tok0, cinfo.nv, qks, 0);
+    if (tid < 64) load_gates<T>(p, cinfo.tok0, cinfo.nv, h, sgl, sb);
+    __syncthreads();
+    float *P = p.pmat + ((int64_t)ci * p.H_v + h) * 4096;
+    for (int idx = tid; idx < 4096; idx += 256) {
+        const int i = idx / 64, j = idx % 64;
+        float s = 0.f;
+        if (j <= i)
+            for (int d = 0; d < DK; ++d) s += sQ[i][d] * sK[j][d];
+        P[idx] = j <= i ? p.scale * __expf(sgl[i] - sgl[j]) * s : 0.f;
+    }
+}
+
 // ---- reverse scan of the state gradient: dS_next of every chunk, and dh0
 template <typename T, int DK>
 __global__ __launch_bounds__(256) void bwd_dstate_kernel(BwdParams p) {
-    __shared__ float sK[64][DK], sQ[64][DK];
-    __shared__ float sA[64][64], sP[64][64];
-    __shared__ float sdS[DK][kBw], sdO[64][kBw], sKdS[64][kBw], sdVp[64][kBw], sdX[64][kBw];
+    __shared__ float sK[64][DK + 1], sQ[64][DK + 1];
+    __shared__ float sA[64][65], sP[64][65];
+    __shared__ float sdS[DK][kBw + 1], sdO[64][kBw + 1], sKdS[64][kBw + 1], sdVp[64][kBw + 1], sdX[64][kBw + 1];
     __shared__ float sgl[64], sb[64];
     const int tid = threadIdx.x;
     const int ncb = p.D_v / kBw;
@@ -125,21 +173,14 @@ __global__ __launch_bounds__(256) void bwd_dstate_kernel(BwdParams p) {
         float *dsn = p.dsnext + ((gci * p.H_v + h) * DK) * DV + cb * kBw;
         for (int idx = tid; idx < DK * kBw; idx += 256) dsn[(idx / kBw) * DV + idx % kBw] = sdS[idx / kBw][idx % kBw];
         const int64_t qks = (int64_t)p.H_qk * DK;
-        load_rows<T>(&sK[0][0], DK, static_cast<const T *>(p.k) + (int64_t)hq * DK, tok0, nv, qks, 0);
-        load_rows<T>(&sQ[0][0], DK, static_cast<const T *>(p.q) + (int64_t)hq * DK, tok0, nv, qks, 0);
-        load_rows<T>(&sdO[0][0], kBw, static_cast<const T *>(p.dout) + (int64_t)h * DV, tok0, nv, (int64_t)p.H_v * DV,
+        load_rows<DK>(&sK[0][0], DK + 1, static_cast<const T *>(p.k) + (int64_t)hq * DK, tok0, nv, qks, 0);
+        load_rows<DK>(&sQ[0][0], DK + 1, static_cast<const T *>(p.q) + (int64_t)hq * DK, tok0, nv, qks, 0);
+        load_rows<kBw>(&sdO[0][0], kBw + 1, static_cast<const T *>(p.dout) + (int64_t)h * DV, tok0, nv, (int64_t)p.H_v * DV,
                      cb * kBw);
-        const T *Ag = static_cast<const T *>(p.A) + (gci * p.H_v + h) * 4096;
-        for (int idx = tid; idx < 4096; idx += 256) sA[idx / 64][idx % 64] = to_f32(Ag[idx]);
+        load_tile64(sA, static_cast<const T *>(p.A) + (gci * p.H_v + h) * 4096);
+        load_tile64(sP, p.pmat + (gci * p.H_v + h) * 4096);  // scale Pt (lower with diagonal)
         if (tid < 64) load_gates<T>(p, tok0, nv, h, sgl, sb);
         __syncthreads();
-        for (int idx = tid; idx < 4096; idx += 256) {       // scale Pt (lower with diagonal)
-            const int i = idx / 64, j = idx % 64;
-            float s = 0.f;
-            if (j <= i)
-                for (int d = 0; d < DK; ++d) s += sQ[i][d] * sK[j][d];
-            sP[i][j] = j <= i ? p.scale * __expf(sgl[i] - sgl[j]) * s : 0.f;
-        }
         for (int idx = tid; idx < 64 * kBw; idx += 256) {   // K dS_next
             const int i = idx / kBw, j = idx % kBw;
             float s = 0.f;
@@ -186,25 +227,25 @@ template <typename T, int DK>
 __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdParams p) {
     constexpr int EPT = 64 * DK / 256;          // dq / dk elements per thread (rows e * 256 / DK + tid / DK)
     constexpr int RS = 256 / DK;
-    __shared__ float sK[64][DK], sQ[64][DK];
-    __shared__ float sA[64][64], sdA[64][64], sPt[64][64], sdP[64][64];
+    constexpr int W3 = kBw3 + 1;                // odd row strides against LDS bank conflicts
+    __shared__ float sK[64][DK + 1], sQ[64][DK + 1];
+    __shared__ float sA[64][65], sdA[64][65], sPt[64][65], sdP[64][65];
     // per value-column block; after the blocks the same space holds A^T dA, then G
-    constexpr int BLK = 2 * DK * kBw3 + 9 * 64 * kBw3;
-    __shared__ float sBlk[BLK > 4096 ? BLK : 4096];
+    constexpr int BLK = 2 * DK * W3 + 8 * 64 * W3;
+    __shared__ float sBlk[BLK > 64 * 65 ? BLK : 64 * 65];
     __shared__ float sgl[64], sb[64], sdgl[64], sdb[64], sc[64];
     __shared__ float sdglC;
-    float (*sS)[kBw3] = reinterpret_cast<float (*)[kBw3]>(sBlk);
-    float (*sdS)[kBw3] = reinterpret_cast<float (*)[kBw3]>(sBlk + DK * kBw3);
-    float (*sV)[kBw3] = reinterpret_cast<float (*)[kBw3]>(sBlk + 2 * DK * kBw3);
-    float (*sdO)[kBw3] = sV + 64;
-    float (*sKS)[kBw3] = sV + 2 * 64;
-    float (*sQS)[kBw3] = sV + 3 * 64;
-    float (*sX)[kBw3] = sV + 4 * 64;
-    float (*sVp)[kBw3] = sV + 5 * 64;
-    float (*sKdS)[kBw3] = sV + 6 * 64;
-    float (*sdVp)[kBw3] = sV + 7 * 64;
-    float (*sdX)[kBw3] = sV + 8 * 64;
-    float (*sT)[64] = reinterpret_cast<float (*)[64]>(sBlk);
+    float (*sS)[W3] = reinterpret_cast<float (*)[W3]>(sBlk);
+    float (*sdS)[W3] = reinterpret_cast<float (*)[W3]>(sBlk + DK * W3);
+    float (*sV)[W3] = reinterpret_cast<float (*)[W3]>(sBlk + 2 * DK * W3);
+    float (*sdO)[W3] = sV + 64;
+    float (*sKS)[W3] = sV + 2 * 64;
+    float (*sX)[W3] = sV + 3 * 64;
+    float (*sVp)[W3] = sV + 4 * 64;
+    float (*sKdS)[W3] = sV + 5 * 64;
+    float (*sdVp)[W3] = sV + 6 * 64;
+    float (*sdX)[W3] = sV + 7 * 64;
+    float (*sT)[65] = reinterpret_cast<float (*)[65]>(sBlk);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int ci = blockIdx.x / p.H_v, h = blockIdx.x - ci * p.H_v;
@@ -213,11 +254,10 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdParams p) {
     const int64_t tok0 = cinfo.tok0;
     const int nv = cinfo.nv;
     const int64_t DV = p.D_v, qks = (int64_t)p.H_qk * DK, vs = (int64_t)p.H_v * DV;
-    load_rows<T>(&sK[0][0], DK, static_cast<const T *>(p.k) + (int64_t)hq * DK, tok0, nv, qks, 0);
-    load_rows<T>(&sQ[0][0], DK, static_cast<const T *>(p.q) + (int64_t)hq * DK, tok0, nv, qks, 0);
-    const T *Ag = static_cast<const T *>(p.A) + ((int64_t)ci * p.H_v + h) * 4096;
+    load_rows<DK>(&sK[0][0], DK + 1, static_cast<const T *>(p.k) + (int64_t)hq * DK, tok0, nv, qks, 0);
+    load_rows<DK>(&sQ[0][0], DK + 1, static_cast<const T *>(p.q) + (int64_t)hq * DK, tok0, nv, qks, 0);
+    load_tile64(sA, static_cast<const T *>(p.A) + ((int64_t)ci * p.H_v + h) * 4096);
     for (int idx = tid; idx < 4096; idx += 256) {
-        sA[idx / 64][idx % 64] = to_f32(Ag[idx]);
         sdA[idx / 64][idx % 64] = 0.f;
         sdP[idx / 64][idx % 64] = 0.f;
     }
@@ -244,24 +284,33 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdParams p) {
     const float *dSt = p.dsnext + (((int64_t)ci * p.H_v + h) * DK) * DV;
     for (int c0 = 0; c0 < p.D_v; c0 += kBw3) {
         __syncthreads();   // Pt is complete; the previous block is done with its tiles
-        for (int idx = tid; idx < DK * kBw3; idx += 256) {
-            const int d = idx / kBw3, j = idx % kBw3;
-            sS[d][j] = St[d * DV + c0 + j];
-            sdS[d][j] = dSt[d * DV + c0 + j];
+        {
+            constexpr int NE = DK * kBw3 / 256;
+            float a[NE], b[NE];
+#pragma unroll
+            for (int it = 0; it < NE; ++it) {
+                const int idx = tid + 256 * it, d = idx / kBw3, j = idx % kBw3;
+                a[it] = St[d * DV + c0 + j];
+                b[it] = dSt[d * DV + c0 + j];
+            }
+#pragma unroll
+            for (int it = 0; it < NE; ++it) {
+                const int idx = tid + 256 * it, d = idx / kBw3, j = idx % kBw3;
+                sS[d][j] = a[it];
+                sdS[d][j] = b[it];
+            }
         }
-        load_rows<T>(&sV[0][0], kBw3, static_cast<const T *>(p.v) + (int64_t)h * DV, tok0, nv, vs, c0);
-        load_rows<T>(&sdO[0][0], kBw3, static_cast<const T *>(p.dout) + (int64_t)h * DV, tok0, nv, vs, c0);
+        load_rows<kBw3>(&sV[0][0], W3, static_cast<const T *>(p.v) + (int64_t)h * DV, tok0, nv, vs, c0);
+        load_rows<kBw3>(&sdO[0][0], W3, static_cast<const T *>(p.dout) + (int64_t)h * DV, tok0, nv, vs, c0);
         __syncthreads();
-        for (int idx = tid; idx < 64 * kBw3; idx += 256) {  // K S, Q S, K dS_next
+        for (int idx = tid; idx < 64 * kBw3; idx += 256) {  // K S, K dS_next
             const int i = idx / kBw3, j = idx % kBw3;
-            float a = 0.f, b = 0.f, e = 0.f;
+            float a = 0.f, e = 0.f;
             for (int d = 0; d < DK; ++d) {
                 a += sK[i][d] * sS[d][j];
-                b += sQ[i][d] * sS[d][j];
                 e += sK[i][d] * sdS[d][j];
             }
             sKS[i][j] = a;
-            sQS[i][j] = b;
             sKdS[i][j] = e;
             sX[i][j] = sb[i] * (sV[i][j] - __expf(sgl[i]) * a);
         }
@@ -286,15 +335,12 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdParams p) {
             for (int t = i; t < 64; ++t) u += sPt[t][i] * sdO[t][j];
             sdVp[i][j] = s + p.scale * u;
         }
-        if (tid < 64) {    // d gl from the output's gamma and from D; the D terms' sum goes to gl_C
+        if (tid < 64) {    // d gl from D; the D terms' sum goes to gl_C
             const int i = tid;
-            const float gi = __expf(sgl[i]), Di = __expf(glC - sgl[i]);
-            float o = 0.f, cd = 0.f;
-            for (int j = 0; j < kBw3; ++j) {
-                o += sdO[i][j] * sQS[i][j];
-                cd += sKdS[i][j] * sVp[i][j];
-            }
-            sdgl[i] += p.scale * gi * o - Di * cd;
+            const float Di = __expf(glC - sgl[i]);
+            float cd = 0.f;
+            for (int j = 0; j < kBw3; ++j) cd += sKdS[i][j] * sVp[i][j];
+            sdgl[i] -= Di * cd;
             sc[i] += Di * cd;
         }
         __syncthreads();
@@ -343,6 +389,16 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdParams p) {
             dq[e] += p.scale * gi * a;
             dk[e] += Di * b - sb[row] * gi * x;
         }
+    }
+    // d gl from the output's gamma: q_i . (scale gamma_i S dO_i), the inter-chunk dq accumulated so
+    // far; the DK / 64 waves holding a row add their sums
+    __syncthreads();   // the row-owner updates of sdgl above are done
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+        const int row = e * RS + tid / DK;
+        float x = sQ[row][col] * dq[e];
+        for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);
+        if (lane == 0) atomicAdd(&sdgl[row], x);
     }
     __syncthreads();
     // dL = -A^T dA A^T (strictly lower), via T = A^T dA in the block space
@@ -453,6 +509,7 @@ hipError_t launch_bwd(int dtype, int D_k, const BwdParams &p, hipStream_t s) {
 #define GDN_BWD(K, T, DK, grid) hipLaunchKernelGGL((K<T, DK>), dim3((unsigned)(grid)), dim3(256), 0, s, p)
 #define GDN_BWD_ALL(T, DK)                                  \
     GDN_BWD(bwd_states_kernel, T, DK, scans);               \
+    if (chunks) GDN_BWD(bwd_p_kernel, T, DK, chunks);       \
     GDN_BWD(bwd_dstate_kernel, T, DK, scans);               \
     if (chunks) GDN_BWD(bwd_chunk_kernel, T, DK, chunks);
     if (dtype == 1 && D_k == 128) { GDN_BWD_ALL(bf16, 128) }

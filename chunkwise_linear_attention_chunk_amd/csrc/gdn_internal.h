@@ -188,6 +188,7 @@ struct BwdParams {           // backward (gdn_bwd), scalar gate
     int64_t T_total;                       // B * T
     float scale;
     float *states, *dsnext;                // [n_chunks][H_v][D_k][D_v]: S entering, dS leaving each chunk
+    float *pmat;                           // [n_chunks][H_v][64][64]: scale Pt
     float *dq, *dk, *dv, *dg, *dbeta, *dh0;
     float *dq_v, *dk_v;                    // per value head when H_v > H_qk, else dq / dk
 };

@@ -187,7 +187,8 @@ gdn_status gdn_fwd_recurrent(const gdn_fwd_args *a, void *stream);
  *   dq, dk [B, T, H_qk, D_k] (summed over the value heads of a group), dv [B, T, H_v, D_v],
  *   dg, dbeta [B, T, H_v], dh0 [N, H_v, D_k, D_v] (NULL: not written).
  * Workspace: gdn_bwd_workspace_bytes(a) bytes of device memory, 256-byte aligned (it holds the
- * recomputed chunk states and the state gradients, 2 x 4 D_k D_v bytes per chunk and head).
+ * recomputed chunk states, the state gradients and the chunks' intra-chunk output matrices,
+ * 2 x 4 D_k D_v + 16 KiB per chunk and head).
  * Errors and ownership as for gdn_fwd. */
 typedef struct {
     int32_t B, T, H_qk, H_v, D_k, D_v;
