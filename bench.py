@@ -346,7 +346,7 @@ def main():
                    "chunk": 64, "gate": w.gate, "h0": w.h0, "input_copies": len(copies),
                    "cp": a.cp, "cp_ran": bool((ran[-1] >> gdn.STAGES.index("cp_pre")) & 1),
                    "cp_segment_chunks": plan["segment_chunks"] if plan["cp"] else None,
-                   "value_cols_per_group": plan["value_cols_per_group"]},
+                   "value_cols_per_group": plan["value_cols_per_group"], "pieces": plan["pieces"]},
         "roofline": {"bound": "hbm", "kernel": dominant, "alg_bytes": alg_bytes_dom, "achieved": achieved,
                      "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(dominant, w.name)},

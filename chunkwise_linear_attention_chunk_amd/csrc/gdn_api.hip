@@ -9,7 +9,9 @@
 #include <cstdlib>
 #include <cstring>
 #include <algorithm>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/gdn.h"
 #include "gdn_internal.h"
@@ -39,6 +41,8 @@ struct Plan {
     int n_slices = 0;
     bool cp = false;          // in-GPU context parallelism
     bool warm = false;        // its warmup form (no S*, M, fix-up)
+    int pieces = 1;           // batched input without CP: chunk-range pieces (per-chunk kernel of the
+                              // next piece on a side stream while the recurrence runs this one)
     int seg_chunks = 0;       // segment length in chunks (one segment per sequence without CP)
     int64_t total_segs = 0;
     size_t off_A = 0, off_seq = 0, off_chunks = 0, off_segs = 0, off_order = 0;
@@ -49,6 +53,24 @@ struct Plan {
 };
 
 constexpr int kNoSegments = 1 << 28;  // segment length meaning "the whole sequence"
+// Measured on the Qwen3-Next shape: 1 piece 0.212-0.216 ms, 2: 0.239, 4: 0.252, 8: 0.282 ms per
+// step (the latency-bound recurrence slows from ~168 to ~217 us while per-chunk work shares its
+// CUs, and each range adds a launch and a state hand-off), so pieces are off unless GDN_PIECES asks.
+constexpr int kDefaultPieces = 1;
+
+// One side stream per device (default priority), created on first use and kept for the process.
+hipError_t side_stream(hipStream_t *out) {
+    static std::mutex mu;
+    static hipStream_t streams[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!streams[dev] && (e = hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking)) != hipSuccess) return e;
+    *out = streams[dev];
+    return hipSuccess;
+}
 
 int64_t count_segments(const gdn_fwd_args *a, int sl) {
     auto segs = [&](int64_t len) {
@@ -167,6 +189,16 @@ gdn_status validate_and_plan(const gdn_fwd_args *a, Plan *pl) {
     pl->cp = cp;
     pl->warm = cp && a->cp_mode == GDN_CP_WARMUP;
     pl->seg_chunks = cp ? sl : kNoSegments;
+    // pieces: a batched input without CP is cut into P ranges of chunks (segments run one after
+    // another, each from the previous one's end state), so that the per-chunk kernel of range j + 1
+    // overlaps the recurrence over range j; GDN_PIECES overrides P for experiments
+    if (!packed && !cp) {
+        const int want = std::max(1, env_int("GDN_PIECES", kDefaultPieces));
+        if (want > 1 && max_nc >= 2 * (int64_t)want) {
+            pl->seg_chunks = (int)((max_nc + want - 1) / want);
+            pl->pieces = (int)((max_nc + pl->seg_chunks - 1) / pl->seg_chunks);
+        }
+    }
     pl->total_segs = count_segments(a, pl->seg_chunks);
     if (pl->total_segs * a->H_v > INT32_MAX / 64) return fail(GDN_ERR_UNSUPPORTED, "too many segments");
 
@@ -190,6 +222,8 @@ gdn_status validate_and_plan(const gdn_fwd_args *a, Plan *pl) {
     }
     if (pl->warm) {
         pl->off_warm = off;  off = align_up(off + seg_heads * sizeof(int));
+    } else if (pl->pieces > 1) {
+        pl->off_start = off; off = align_up(off + seg_heads * a->D_k * a->D_v * sizeof(float));
     } else if (cp) {
         pl->off_sstar = off; off = align_up(off + seg_heads * a->D_k * a->D_v * sizeof(float));
         pl->off_m = off;     off = align_up(off + seg_heads * a->D_k * a->D_k * sizeof(float));
@@ -221,7 +255,7 @@ extern "C" gdn_status gdn_fwd_plan(const gdn_fwd_args *a, gdn_plan_info *info) {
     info->segment_chunks = pl.cp ? pl.seg_chunks : (int32_t)max_nc;
     info->total_segments = pl.total_segs;
     info->value_cols_per_group = pl.BV;
-    info->reserved = 0;
+    info->pieces = pl.pieces;
     info->workspace_bytes = pl.bytes;
     return GDN_OK;
 }
@@ -269,18 +303,19 @@ gdn_status run_fwd(const gdn_fwd_args *a, void *workspace, size_t workspace_byte
 
     const bool channel = a->gate_kind == GDN_GATE_CHANNEL;
     const gdn::Prologue pro{a->qk_l2norm, a->beta_sigmoid, a->A_log, a->dt_bias, a->gate_lower_bound};
-    if (channel) {
-        gdn::IntraKdaParams ip{a->q, a->k, a->g, a->beta, chunks, a->T, (int)pl.total_chunks, a->H_qk, a->H_v,
-                               a->scale, ws + pl.off_A, ws + pl.off_P, ws + pl.off_kg, ws + pl.off_kd,
-                               ws + pl.off_qg, reinterpret_cast<float *>(ws + pl.off_gates), pro};
-        e = gdn::launch_intra_kda(a->dtype, a->D_k, ip, s);
-    } else {
+    // the per-chunk kernel over every chunk (cnt 0), or over chunks [lo, lo + cnt) of each sequence
+    auto intra = [&](int lo, int cnt, hipStream_t st) -> hipError_t {
+        if (channel) {
+            gdn::IntraKdaParams ip{a->q, a->k, a->g, a->beta, chunks, a->T, (int)pl.total_chunks, a->H_qk, a->H_v,
+                                   a->scale, ws + pl.off_A, ws + pl.off_P, ws + pl.off_kg, ws + pl.off_kd,
+                                   ws + pl.off_qg, reinterpret_cast<float *>(ws + pl.off_gates), pro, a->N, lo, cnt};
+            return gdn::launch_intra_kda(a->dtype, a->D_k, ip, st);
+        }
         gdn::IntraParams ip{a->q, a->k, a->g, a->beta, chunks, a->T, (int)pl.total_chunks, a->H_qk, a->H_v,
-                            a->scale, ws + pl.off_A, ws + pl.off_P, reinterpret_cast<float *>(ws + pl.off_gates), pro};
-        e = gdn::launch_intra(a->dtype, a->D_k, ip, s);
-    }
-    if (e != hipSuccess) return done(fail(GDN_ERR_HIP, "intra launch: %s", hipGetErrorString(e)));
-    if ((e = mark(GDN_STAGE_INTRA)) != hipSuccess) return done(fail(GDN_ERR_HIP, "event: %s", hipGetErrorString(e)));
+                            a->scale, ws + pl.off_A, ws + pl.off_P, reinterpret_cast<float *>(ws + pl.off_gates), pro,
+                            a->N, lo, cnt};
+        return gdn::launch_intra(a->dtype, a->D_k, ip, st);
+    };
 
     gdn::ChunkParams cp{};
     cp.q = a->q; cp.k = a->k; cp.v = a->v; cp.g = a->g; cp.beta = a->beta;
@@ -294,6 +329,55 @@ gdn_status run_fwd(const gdn_fwd_args *a, void *workspace, size_t workspace_byte
     if (channel) {
         cp.kg = ws + pl.off_kg; cp.kd = ws + pl.off_kd; cp.qg = ws + pl.off_qg;
     }
+    cp.n_slices = pl.n_slices;
+
+    if (pl.pieces > 1) {
+        // pieces: the per-chunk kernel of range j runs on a side stream, the recurrence over range
+        // j on `stream` once that range is done (and after range j - 1, whose end state it starts
+        // from).  Timed: the intra stage is range 0 (the part not overlapped), the chunk stage the
+        // rest up to the last range's end.
+        hipStream_t side;
+        if ((e = side_stream(&side)) != hipSuccess) return done(fail(GDN_ERR_HIP, "side stream: %s", hipGetErrorString(e)));
+        const int P = pl.pieces, L = pl.seg_chunks, nc = (a->T + gdn::kChunk - 1) / gdn::kChunk;
+        std::vector<hipEvent_t> ev(P + 1, nullptr);
+        auto release = [&]() {
+            for (hipEvent_t x : ev)
+                if (x) (void)hipEventDestroy(x);
+        };
+        for (auto &x : ev)
+            if ((e = hipEventCreateWithFlags(&x, hipEventDisableTiming)) != hipSuccess) {
+                release();
+                return done(fail(GDN_ERR_HIP, "event: %s", hipGetErrorString(e)));
+            }
+        auto check = [&](hipError_t r, const char *what) {
+            if (r != hipSuccess) fail(GDN_ERR_HIP, "%s: %s", what, hipGetErrorString(r));
+            return r == hipSuccess;
+        };
+        bool ok = check(hipEventRecord(ev[0], s), "event") && check(hipStreamWaitEvent(side, ev[0], 0), "stream wait");
+        for (int j = 0; ok && j < P; ++j) {
+            ok = check(intra(j * L, std::min(L, nc - j * L), side), "intra launch");
+            if (ok && j == 0 && events) {
+                ok = check(hipEventRecord(static_cast<hipEvent_t>(events[GDN_STAGE_INTRA + 1]), side), "event");
+                ran |= 1u << GDN_STAGE_INTRA;
+            }
+            ok = ok && check(hipEventRecord(ev[j + 1], side), "event");
+        }
+        cp.seg_start = cp.seg_next = reinterpret_cast<float *>(ws + pl.off_start);
+        for (int j = 0; ok && j < P; ++j) {
+            cp.seg_only = j + 1;
+            ok = check(hipStreamWaitEvent(s, ev[j + 1], 0), "stream wait") &&
+                 check(gdn::launch_chunk(a->dtype, a->D_k, pl.BV, a->gate_kind, cp, s), "chunk launch");
+        }
+        release();
+        if (!ok) return done(GDN_ERR_HIP);
+        if ((e = mark(GDN_STAGE_CHUNK)) != hipSuccess) return done(fail(GDN_ERR_HIP, "event: %s", hipGetErrorString(e)));
+        return done(GDN_OK);
+    }
+
+    e = intra(0, 0, s);
+    if (e != hipSuccess) return done(fail(GDN_ERR_HIP, "intra launch: %s", hipGetErrorString(e)));
+    if ((e = mark(GDN_STAGE_INTRA)) != hipSuccess) return done(fail(GDN_ERR_HIP, "event: %s", hipGetErrorString(e)));
+
     if (pl.warm) {
         // warmup CP: each segment's warmup length from the gate statistics, no pre-process maps
         const float tol = a->cp_warmup_tol > 0.f ? a->cp_warmup_tol : 0x1p-24f;
@@ -318,7 +402,6 @@ gdn_status run_fwd(const gdn_fwd_args *a, void *workspace, size_t workspace_byte
         if (e != hipSuccess) return done(fail(GDN_ERR_HIP, "cp fix-up launch: %s", hipGetErrorString(e)));
         if ((e = mark(GDN_STAGE_CP_FIX)) != hipSuccess) return done(fail(GDN_ERR_HIP, "event: %s", hipGetErrorString(e)));
     }
-    cp.n_slices = pl.n_slices;
     e = gdn::launch_chunk(a->dtype, a->D_k, pl.BV, a->gate_kind, cp, s);
     if (e != hipSuccess) return done(fail(GDN_ERR_HIP, "chunk launch: %s", hipGetErrorString(e)));
     if ((e = mark(GDN_STAGE_CHUNK)) != hipSuccess) return done(fail(GDN_ERR_HIP, "event: %s", hipGetErrorString(e)));

@@ -271,9 +271,11 @@ void chunk_kernel(ChunkParams p) {
     // its L2, so Q/K/A fetched by one workgroup are L2 hits for the others.
     const int bid = blockIdx.x, xcd = bid & 7, rr = bid >> 3;
     const int slice = rr % p.n_slices, unit = (rr / p.n_slices) * 8 + xcd;
-    if (unit >= p.total_segs * p.H_v) return;
+    if (unit >= (p.seg_only ? p.N : p.total_segs) * p.H_v) return;
     const int gsi = unit / p.H_v, h = unit % p.H_v;
-    const int gs = p.segs ? p.order[gsi] : gsi;
+    // one piece of a batched input: segment seg_only - 1 of sequence gsi
+    const int gs = p.seg_only ? gsi * max(1, ceil_div(ceil_div(p.T, kChunk), p.seg_chunks)) + p.seg_only - 1
+                              : p.segs ? p.order[gsi] : gsi;
     const SegInfo sg = seg_info(p.segs, gs, p.T, p.seg_chunks);
     const int n = sg.n;
     const int hq = h / (p.H_v / p.H_qk);
@@ -799,6 +801,7 @@ void chunk_kernel(ChunkParams p) {
     float *s_end = nullptr;
     if constexpr (OUT) {
         if (sg.last && p.final_state) s_end = p.final_state + ((int64_t)n * p.H_v + h) * DK * DV;
+        else if (!sg.last && p.seg_next) s_end = p.seg_next + ((int64_t)(gs + 1) * p.H_v + h) * DK * DV;
     } else {
         s_end = (mcols ? p.seg_m : p.seg_sstar) + ((int64_t)gs * p.H_v + h) * DK * ccols;
     }
@@ -962,7 +965,7 @@ hipError_t launch_plan(const PlanParams &p, hipStream_t s) {
 
 template <int MODE, int GATE>
 static hipError_t launch_rec(int dtype, int D_k, int BV, const ChunkParams &p, hipStream_t s) {
-    const int units = p.total_segs * p.H_v;
+    const int units = (p.seg_only ? p.N : p.total_segs) * p.H_v;
     const unsigned groups = (unsigned)((units + 7) / 8);
     const dim3 grid(groups * 8u * (unsigned)p.n_slices);
     if (units == 0) return hipSuccess;

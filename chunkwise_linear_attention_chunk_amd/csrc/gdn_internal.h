@@ -108,6 +108,9 @@ struct IntraParams {
     void *P;                // unused with a scalar gate (the recurrence forms P)
     float *gates;           // [n_chunks][H_v][GB_FLOATS]
     Prologue pro;
+    // batched input in pieces: chunks [piece_lo, piece_lo + piece_cnt) of each of the N
+    // sequences (piece_cnt 0: every chunk)
+    int N, piece_lo, piece_cnt;
 };
 
 struct IntraKdaParams {       // per-channel gates
@@ -122,6 +125,7 @@ struct IntraKdaParams {       // per-channel gates
     void *kd, *qg;          // [n_chunks][H_v][parts][64][D_k]: K 2^(G_C - G), Q 2^G, hi (+ lo)
     float *gates;           // [n_chunks][H_v][GB_FLOATS]: beta and the chunk decay 2^G_C
     Prologue pro;
+    int N, piece_lo, piece_cnt;   // as in IntraParams
 };
 
 struct ChunkParams {
@@ -146,7 +150,18 @@ struct ChunkParams {
     const void *kg, *kd, *qg, *P;
     const float *gates;
     const int *warm;        // warmup CP: [total_segs][H_v] warmup chunks of each segment (nullable)
+    // pieces (batched input): seg_only = j + 1 runs segment j of every sequence only (0: all), from
+    // seg_start; seg_next (nullable) receives a non-last segment's end state as the next one's start
+    int seg_only;
+    float *seg_next;
 };
+
+// chunk ci of the per-chunk grid: every chunk, or the chunks of one piece of a batched input
+__device__ __forceinline__ int piece_chunk(int ci, int T, int piece_lo, int piece_cnt) {
+    if (!piece_cnt) return ci;
+    const int nn = ci / piece_cnt;
+    return nn * ((T + kChunk - 1) / kChunk) + piece_lo + (ci - nn * piece_cnt);
+}
 
 struct WarmParams {         // warmup CP gate statistics
     const SegInfo *segs;    // nullptr: batched input

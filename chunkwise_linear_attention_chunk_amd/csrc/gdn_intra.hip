@@ -175,7 +175,8 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraParams p) {
     float *sL = sX;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, grp = lane >> 4;
-    const int ci = blockIdx.x / p.H_v, h = blockIdx.x - ci * p.H_v;
+    const int cg = blockIdx.x / p.H_v, h = blockIdx.x - cg * p.H_v;
+    const int ci = piece_chunk(cg, p.T, p.piece_lo, p.piece_cnt);
     const int hq = h / (p.H_v / p.H_qk);
     const ChunkInfo cinfo = chunk_info(p.chunks, ci, p.T);
     const int t0 = cinfo.tok0, nv = cinfo.nv;
@@ -341,7 +342,8 @@ __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
     float *sL = reinterpret_cast<float *>(smem + R0);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, grp = lane >> 4;
-    const int ci = blockIdx.x / p.H_v, h = blockIdx.x - ci * p.H_v;
+    const int cg = blockIdx.x / p.H_v, h = blockIdx.x - cg * p.H_v;
+    const int ci = piece_chunk(cg, p.T, p.piece_lo, p.piece_cnt);
     const int hq = h / (p.H_v / p.H_qk);
     const ChunkInfo cinfo = chunk_info(p.chunks, ci, p.T);
     const int t0 = cinfo.tok0, nv = cinfo.nv, last = max(nv - 1, 0);
@@ -563,8 +565,9 @@ __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
 }  // namespace
 
 hipError_t launch_intra(int dtype, int D_k, const IntraParams &p, hipStream_t s) {
-    const dim3 grid((unsigned)p.n_chunks * (unsigned)p.H_v), block(256);
-    if (p.n_chunks == 0) return hipSuccess;
+    const int items = p.piece_cnt ? p.N * p.piece_cnt : p.n_chunks;
+    const dim3 grid((unsigned)items * (unsigned)p.H_v), block(256);
+    if (items == 0) return hipSuccess;
     if (dtype == 1 && D_k == 128) hipLaunchKernelGGL((intra_kernel<bf16, 128>), grid, block, 0, s, p);
     else if (dtype == 1 && D_k == 64) hipLaunchKernelGGL((intra_kernel<bf16, 64>), grid, block, 0, s, p);
     else if (dtype == 0 && D_k == 128) hipLaunchKernelGGL((intra_kernel<float, 128>), grid, block, 0, s, p);
@@ -574,8 +577,9 @@ hipError_t launch_intra(int dtype, int D_k, const IntraParams &p, hipStream_t s)
 }
 
 hipError_t launch_intra_kda(int dtype, int D_k, const IntraKdaParams &p, hipStream_t s) {
-    const dim3 grid((unsigned)p.n_chunks * (unsigned)p.H_v), block(256);
-    if (p.n_chunks == 0) return hipSuccess;
+    const int items = p.piece_cnt ? p.N * p.piece_cnt : p.n_chunks;
+    const dim3 grid((unsigned)items * (unsigned)p.H_v), block(256);
+    if (items == 0) return hipSuccess;
     const bool pro = p.pro.qk_l2norm || p.pro.beta_sigmoid || p.pro.A_log;
 #define GDN_INTRA_KDA_CASE(T, DK)                                                                   \
     if (pro) hipLaunchKernelGGL((intra_kda_kernel<T, DK, true>), grid, block, 0, s, p);             \

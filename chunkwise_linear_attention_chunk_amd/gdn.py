@@ -61,7 +61,7 @@ class BwdArgs(ctypes.Structure):
 class PlanInfo(ctypes.Structure):
     """Mirror of gdn_plan_info."""
     _fields_ = [("cp", ctypes.c_int32), ("segment_chunks", ctypes.c_int32), ("total_segments", ctypes.c_int64),
-                ("value_cols_per_group", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("value_cols_per_group", ctypes.c_int32), ("pieces", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_size_t)]
 
 
@@ -154,10 +154,10 @@ def workspace_bytes(args):
 
 def plan(args):
     """The schedule gdn_fwd would use: dict(cp, segment_chunks, total_segments, value_cols_per_group,
-    workspace_bytes).  Host-only; raises on invalid arguments."""
+    pieces, workspace_bytes).  Host-only; raises on invalid arguments."""
     info = PlanInfo()
     _check(lib().gdn_fwd_plan(ctypes.byref(args), ctypes.byref(info)))
-    return {f: getattr(info, f) for f, _ in PlanInfo._fields_ if f != "reserved"}
+    return {f: getattr(info, f) for f, _ in PlanInfo._fields_}
 
 
 def fwd_raw(args, workspace, workspace_bytes_, stream):

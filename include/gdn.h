@@ -132,7 +132,8 @@ typedef struct {
     int32_t segment_chunks;       /* chunks per segment (the longest sequence's count when cp == 0) */
     int64_t total_segments;       /* segments over all sequences (N when cp == 0) */
     int32_t value_cols_per_group; /* D_v columns one recurrence workgroup carries */
-    int32_t reserved;
+    int32_t pieces;               /* chunk ranges of a batched input over which the per-chunk kernel
+                                     (on a side stream) and the recurrence are pipelined; 1: none */
     size_t workspace_bytes;       /* as gdn_fwd_workspace_bytes */
 } gdn_plan_info;
 gdn_status gdn_fwd_plan(const gdn_fwd_args *a, gdn_plan_info *info);

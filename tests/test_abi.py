@@ -182,6 +182,18 @@ def test_workspace_with_context_parallelism():
     assert long > 1024 * 4 * per + 4 * 3 * 128 * 128 * 4
     wide = gdn.workspace_bytes(_args(B=4, N=4, T=4096, H_qk=16, H_v=16))
     assert wide < 4 * 64 * 16 * per + 4096
+    info = gdn.plan(_args(B=4, N=4, T=4096, H_qk=16, H_v=16))
+    assert info["cp"] == 0 and info["pieces"] == 1
+
+
+def test_workspace_with_pieces(monkeypatch):
+    # GDN_PIECES=4 without CP: four ranges of 16 chunks, the start states of ranges 1..3 in fp32
+    monkeypatch.setenv("GDN_PIECES", "4")
+    per = 64 * 64 * 2 + 512 * 4
+    wide = gdn.workspace_bytes(_args(B=4, N=4, T=4096, H_qk=16, H_v=16))
+    pieces = 4 * 4 * 16 * 128 * 128 * 4
+    assert pieces + 4 * 64 * 16 * per <= wide < pieces + 4 * 64 * 16 * per + 4096
+    assert gdn.plan(_args(B=4, N=4, T=4096, H_qk=16, H_v=16))["pieces"] == 4
 
 
 def test_plan_query():
@@ -192,6 +204,6 @@ def test_plan_query():
     assert info["total_segments"] == -(-1024 // info["segment_chunks"])
     assert info["workspace_bytes"] == gdn.workspace_bytes(a)
     off = gdn.plan(_args(B=1, N=1, T=65536, H_qk=4, H_v=4, cp_mode=gdn.CP_MODES["off"]))
-    assert off["cp"] == 0 and off["total_segments"] == 1 and off["segment_chunks"] == 1024
+    assert off["cp"] == 0 and off["pieces"] == 1 and off["total_segments"] == 1 and off["segment_chunks"] == 1024
     with pytest.raises(gdn.GdnError):
         gdn.plan(_args(chunk_size=48))

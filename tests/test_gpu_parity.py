@@ -224,6 +224,37 @@ def test_empty_sequence_returns_initial_state():
     assert torch.equal(fs, x["h0"])
 
 
+# --------------------------------------------------------------------------- pieces
+# Batched input without CP is cut into chunk ranges: the per-chunk kernel of range j + 1 runs on a
+# side stream while the recurrence runs range j from the end state of range j - 1.
+@pytest.mark.parametrize("pieces", [1, 2, 3, 8])
+def test_pieces_bf16(pieces, monkeypatch):
+    monkeypatch.setenv("GDN_PIECES", str(pieces))
+    x = _w("qwen3next_bf16", B=2, H=3, T=64 * 17 + 13, h0=True, seed=700 + pieces)
+    check(x, TOL["bf16"], label=f"pieces={pieces}", cp_mode="off")   # (few chains would pick CP)
+
+
+def test_pieces_fp32_and_kda(monkeypatch):
+    monkeypatch.setenv("GDN_PIECES", "3")
+    check(_w("tiny_fp32", B=2, T=64 * 7 + 5, h0=True, seed=710), TOL["fp32"], label="pieces=3 fp32", cp_mode="off")
+    check(_w("kda_bf16", B=1, H=2, T=64 * 9, h0=True, seed=711), TOL["bf16"], label="pieces=3 KDA", cp_mode="off")
+
+
+def test_pieces_plan_and_repeat_calls(monkeypatch):
+    # the schedule with four pieces, and back-to-back calls that reuse the side stream
+    from chunkwise_linear_attention_chunk_amd import gdn
+    monkeypatch.setenv("GDN_PIECES", "4")
+    x = _w("qwen3next_bf16", B=4, H=16, T=64 * 12, seed=712)
+    o1, f1 = gpu_run(x)
+    o2, f2 = gpu_run(x)
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
+    dev = torch.device("cuda:0")
+    t = {n: x[n].to(dev) for n in ("q", "k", "v", "g", "beta")}
+    o = torch.empty(t["v"].shape, dtype=t["v"].dtype, device=dev)
+    a = gdn.make_args(t["q"], t["k"], t["v"], t["g"], t["beta"], x["scale"], o=o)
+    assert gdn.plan(a)["pieces"] == 4
+
+
 # --------------------------------------------------------------------------- in-kernel prologue
 # Raw inputs (q, k rows of random length, raw gate inputs, beta logits) with the prologue switched on:
 # the oracle applies oracle/prologue.py in fp64, the library inside its kernels.
