@@ -48,6 +48,41 @@ def test_struct_layout_matches_header():
         assert getattr(gdn.FwdArgs, f).offset == off, f"field {f}: ctypes {getattr(gdn.FwdArgs, f).offset} vs C {off}"
 
 
+def test_backward_struct_layout_matches_header():
+    fields = [f[0] for f in gdn.BwdArgs._fields_]
+    src = "#include <stdio.h>\n#include <stddef.h>\n#include \"gdn.h\"\nint main(void){\n"
+    src += 'printf("%zu\\n", sizeof(gdn_bwd_args));\n'
+    src += "".join(f'printf("%zu\\n", offsetof(gdn_bwd_args, {f}));\n' for f in fields)
+    src += "return 0;}\n"
+    with tempfile.TemporaryDirectory() as d:
+        c, exe = os.path.join(d, "probe.c"), os.path.join(d, "probe")
+        open(c, "w").write(src)
+        subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), c, "-o", exe], check=True)
+        out = [int(x) for x in subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split()]
+    assert out[0] == ctypes.sizeof(gdn.BwdArgs)
+    for f, off in zip(fields, out[1:]):
+        assert getattr(gdn.BwdArgs, f).offset == off, f"field {f}"
+
+
+def test_backward_validation():
+    a = gdn.BwdArgs()
+    a.B, a.T, a.H_qk, a.H_v, a.D_k, a.D_v, a.N = 1, 100, 2, 2, 64, 64, 1
+    a.chunk_size, a.dtype, a.gate_kind, a.scale = 64, gdn.DTYPE_F32, gdn.GATE_SCALAR, 0.125
+    fake = ctypes.c_void_p(0x1000)
+    a.q = a.k = a.v = a.g = a.beta = a.dout = fake
+    L = gdn.lib()
+    assert L.gdn_bwd(ctypes.byref(a), None, 0, None) == gdn.GDN_ERR_INVALID_ARG     # no gradient outputs
+    assert "dq, dk, dv" in L.gdn_last_error().decode()
+    a.dq = a.dk = a.dv = a.dg = a.dbeta = fake
+    n = L.gdn_bwd_workspace_bytes(ctypes.byref(a))
+    assert n >= 2 * 2 * 2 * 64 * 64 * 4                                              # states and dS per chunk
+    assert L.gdn_bwd(ctypes.byref(a), None, 0, None) == gdn.GDN_ERR_WORKSPACE
+    a.gate_kind = gdn.GATE_CHANNEL
+    assert L.gdn_bwd(ctypes.byref(a), None, 0, None) == gdn.GDN_ERR_UNSUPPORTED
+    a.gate_kind, a.chunk_size = gdn.GATE_SCALAR, 32
+    assert L.gdn_bwd(ctypes.byref(a), None, 0, None) == gdn.GDN_ERR_UNSUPPORTED
+
+
 def test_status_strings():
     lib = gdn.lib()
     for code, name in enumerate(["GDN_OK", "GDN_ERR_INVALID_ARG", "GDN_ERR_UNSUPPORTED", "GDN_ERR_WORKSPACE",
