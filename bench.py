@@ -246,7 +246,31 @@ def bench_backward(a, torch, gdn, synth, dev):
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None},
         "stage_ms": {"backward": ms},
     }
+    if not a.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_backward(x, do, dht)
     print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline_backward(x, do, dht, T=256, heads=2):
+    """The fp64 autograd backward oracle on a bounded sample: the first T tokens of sequence 0 and
+    its first `heads` value heads (with their query/key heads), scaled to tokens/s at the full head
+    count."""
+    import torch
+    from chunkwise_linear_attention_chunk_amd import synth
+    from oracle.backward import gdn_backward
+    f64 = synth.to_f64
+    H, Hq = x["v"].shape[2], x["q"].shape[2]
+    hq = max(1, heads * Hq // H)
+    sl = lambda a, hh: f64(a[:1, :T, :hh]) if a is not None else None
+    args = [sl(x["q"], hq), sl(x["k"], hq), sl(x["v"], heads), sl(x["g"], heads), sl(x["beta"], heads)]
+    h0 = None if x["h0"] is None else f64(x["h0"][:1, :heads])
+    threads = torch.get_num_threads()
+    t0 = time.perf_counter()
+    gdn_backward(*args, x["scale"], f64(do.cpu()[:1, :T, :heads]), h0, f64(dht.cpu()[:1, :heads]))
+    dt = time.perf_counter() - t0
+    return {"value": T * heads / H / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"sequence 0, first {T} tokens, {heads} of {H} value heads (fp64 autograd through the token "
+                      f"recurrence), scaled to all heads; {dt:.2f} s wall"}
 
 
 def main():

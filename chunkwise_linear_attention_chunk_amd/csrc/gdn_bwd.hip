@@ -25,7 +25,10 @@
 namespace gdn {
 namespace {
 
-constexpr int kBw = 16;     // value columns per workgroup of the two scans
+constexpr int kBw = 16;     // value columns per workgroup of the forward replay
+constexpr int kBwD = 32;    // value columns per workgroup of the reverse scan (measured: 16 columns
+                            // 5.8 ms, 32 columns 5.4 ms on the Qwen3-Next shape; the replay is
+                            // faster at 16: 2.1 against 3.1 ms)
 constexpr int kBw3 = 8;     // value columns per block of the per-chunk gradient kernel
 
 // chunk-local gates of chunk (tok0, nv) and head h into sgl (cumsum, natural log) and sb (beta);
@@ -154,57 +157,57 @@ template <typename T, int DK>
 __global__ __launch_bounds__(256) void bwd_dstate_kernel(BwdParams p) {
     __shared__ float sK[64][DK + 1], sQ[64][DK + 1];
     __shared__ float sA[64][65], sP[64][65];
-    __shared__ float sdS[DK][kBw + 1], sdO[64][kBw + 1], sKdS[64][kBw + 1], sdVp[64][kBw + 1], sdX[64][kBw + 1];
+    __shared__ float sdS[DK][kBwD + 1], sdO[64][kBwD + 1], sKdS[64][kBwD + 1], sdVp[64][kBwD + 1], sdX[64][kBwD + 1];
     __shared__ float sgl[64], sb[64];
     const int tid = threadIdx.x;
-    const int ncb = p.D_v / kBw;
+    const int ncb = p.D_v / kBwD;
     const int cb = blockIdx.x % ncb, nh = blockIdx.x / ncb, h = nh % p.H_v, n = nh / p.H_v;
     const int hq = h / (p.H_v / p.H_qk);
     const SeqInfo si = seq_info(p.seq, n, p.T);
     const int64_t DV = p.D_v;
-    for (int idx = tid; idx < DK * kBw; idx += 256) {
-        const int d = idx / kBw, j = idx % kBw;
-        sdS[d][j] = p.dht ? p.dht[(((int64_t)n * p.H_v + h) * DK + d) * DV + cb * kBw + j] : 0.f;
+    for (int idx = tid; idx < DK * kBwD; idx += 256) {
+        const int d = idx / kBwD, j = idx % kBwD;
+        sdS[d][j] = p.dht ? p.dht[(((int64_t)n * p.H_v + h) * DK + d) * DV + cb * kBwD + j] : 0.f;
     }
     for (int c = si.nchunks - 1; c >= 0; --c) {
         const int64_t gci = si.chunk0 + c, tok0 = si.tok0 + (int64_t)c * kChunk;
         const int nv = min(kChunk, si.len - c * kChunk);
         __syncthreads();
-        float *dsn = p.dsnext + ((gci * p.H_v + h) * DK) * DV + cb * kBw;
-        for (int idx = tid; idx < DK * kBw; idx += 256) dsn[(idx / kBw) * DV + idx % kBw] = sdS[idx / kBw][idx % kBw];
+        float *dsn = p.dsnext + ((gci * p.H_v + h) * DK) * DV + cb * kBwD;
+        for (int idx = tid; idx < DK * kBwD; idx += 256) dsn[(idx / kBwD) * DV + idx % kBwD] = sdS[idx / kBwD][idx % kBwD];
         const int64_t qks = (int64_t)p.H_qk * DK;
         load_rows<DK>(&sK[0][0], DK + 1, static_cast<const T *>(p.k) + (int64_t)hq * DK, tok0, nv, qks, 0);
         load_rows<DK>(&sQ[0][0], DK + 1, static_cast<const T *>(p.q) + (int64_t)hq * DK, tok0, nv, qks, 0);
-        load_rows<kBw>(&sdO[0][0], kBw + 1, static_cast<const T *>(p.dout) + (int64_t)h * DV, tok0, nv, (int64_t)p.H_v * DV,
-                     cb * kBw);
+        load_rows<kBwD>(&sdO[0][0], kBwD + 1, static_cast<const T *>(p.dout) + (int64_t)h * DV, tok0, nv, (int64_t)p.H_v * DV,
+                     cb * kBwD);
         load_tile64(sA, static_cast<const T *>(p.A) + (gci * p.H_v + h) * 4096);
         load_tile64(sP, p.pmat + (gci * p.H_v + h) * 4096);  // scale Pt (lower with diagonal)
         if (tid < 64) load_gates<T>(p, tok0, nv, h, sgl, sb);
         __syncthreads();
-        for (int idx = tid; idx < 64 * kBw; idx += 256) {   // K dS_next
-            const int i = idx / kBw, j = idx % kBw;
+        for (int idx = tid; idx < 64 * kBwD; idx += 256) {   // K dS_next
+            const int i = idx / kBwD, j = idx % kBwD;
             float s = 0.f;
             for (int d = 0; d < DK; ++d) s += sK[i][d] * sdS[d][j];
             sKdS[i][j] = s;
         }
         __syncthreads();
         const float glC = sgl[63], gC = __expf(glC);
-        for (int idx = tid; idx < 64 * kBw; idx += 256) {   // dV' = D K dS_next + scale Pt^T dO
-            const int i = idx / kBw, j = idx % kBw;
+        for (int idx = tid; idx < 64 * kBwD; idx += 256) {   // dV' = D K dS_next + scale Pt^T dO
+            const int i = idx / kBwD, j = idx % kBwD;
             float s = __expf(glC - sgl[i]) * sKdS[i][j];
             for (int t = i; t < 64; ++t) s += sP[t][i] * sdO[t][j];
             sdVp[i][j] = s;
         }
         __syncthreads();
-        for (int idx = tid; idx < 64 * kBw; idx += 256) {   // dX = A^T dV'
-            const int i = idx / kBw, j = idx % kBw;
+        for (int idx = tid; idx < 64 * kBwD; idx += 256) {   // dX = A^T dV'
+            const int i = idx / kBwD, j = idx % kBwD;
             float s = 0.f;
             for (int t = i; t < 64; ++t) s += sA[t][i] * sdVp[t][j];
             sdX[i][j] = s;
         }
         __syncthreads();
-        for (int idx = tid; idx < DK * kBw; idx += 256) {   // dS = gamma_C dS_next + Q^T(...) - K^T(...)
-            const int d = idx / kBw, j = idx % kBw;
+        for (int idx = tid; idx < DK * kBwD; idx += 256) {   // dS = gamma_C dS_next + Q^T(...) - K^T(...)
+            const int d = idx / kBwD, j = idx % kBwD;
             float s = 0.f;
             for (int i = 0; i < 64; ++i) {
                 const float gi = __expf(sgl[i]);
@@ -215,9 +218,9 @@ __global__ __launch_bounds__(256) void bwd_dstate_kernel(BwdParams p) {
     }
     __syncthreads();
     if (p.dh0) {
-        for (int idx = tid; idx < DK * kBw; idx += 256) {
-            const int d = idx / kBw, j = idx % kBw;
-            p.dh0[(((int64_t)n * p.H_v + h) * DK + d) * DV + cb * kBw + j] = sdS[d][j];
+        for (int idx = tid; idx < DK * kBwD; idx += 256) {
+            const int d = idx / kBwD, j = idx % kBwD;
+            p.dh0[(((int64_t)n * p.H_v + h) * DK + d) * DV + cb * kBwD + j] = sdS[d][j];
         }
     }
 }
@@ -504,13 +507,14 @@ __global__ __launch_bounds__(256) void bwd_group_sum_kernel(BwdParams p, int DK,
 }  // namespace
 
 hipError_t launch_bwd(int dtype, int D_k, const BwdParams &p, hipStream_t s) {
-    const int64_t scans = (int64_t)p.N * p.H_v * (p.D_v / kBw), chunks = (int64_t)p.n_chunks * p.H_v;
+    const int64_t scans = (int64_t)p.N * p.H_v * (p.D_v / kBw), rscans = (int64_t)p.N * p.H_v * (p.D_v / kBwD);
+    const int64_t chunks = (int64_t)p.n_chunks * p.H_v;
     if (scans == 0) return hipSuccess;
 #define GDN_BWD(K, T, DK, grid) hipLaunchKernelGGL((K<T, DK>), dim3((unsigned)(grid)), dim3(256), 0, s, p)
 #define GDN_BWD_ALL(T, DK)                                  \
     GDN_BWD(bwd_states_kernel, T, DK, scans);               \
     if (chunks) GDN_BWD(bwd_p_kernel, T, DK, chunks);       \
-    GDN_BWD(bwd_dstate_kernel, T, DK, scans);               \
+    GDN_BWD(bwd_dstate_kernel, T, DK, rscans);              \
     if (chunks) GDN_BWD(bwd_chunk_kernel, T, DK, chunks);
     if (dtype == 1 && D_k == 128) { GDN_BWD_ALL(bf16, 128) }
     else if (dtype == 1 && D_k == 64) { GDN_BWD_ALL(bf16, 64) }
