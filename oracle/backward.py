@@ -2,20 +2,23 @@
 
 The forward is the token recurrence written in plain PyTorch fp64 CPU ops,
     S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,   o_t = scale S_t^T q_t,
-alpha_t = exp(g_t) (scalar gate), S_0 = h0 (FlashQLA announcement, gate-decay section; Flash
-Linear Attention page, section 8), and the gradients of the loss <o, do> + <S_T, dS_T> with
-respect to q, k, v, g, beta and h0 come from torch.autograd (a library primitive standing in for
-the backward's algebra; the GDN-in-FLA notes, backward Steps 1-7, derive the same gradients in
-chunked form).  Pinned by tests/test_oracle_backward.py: the forward equals the C oracle, the
-gradients match central finite differences on tiny inputs, and closed forms at beta = 0.
+alpha_t = exp(g_t) (scalar gate; per-channel gate: Diag(exp(gk_t)) on the rows of S, applied
+before the read and the erase as on the KDA walk-through page, section 3), S_0 = h0 (FlashQLA
+announcement, gate-decay section; Flash Linear Attention page, section 8), and the gradients of
+the loss <o, do> + <S_T, dS_T> with respect to q, k, v, g, beta and h0 come from torch.autograd (a
+library primitive standing in for the backward's algebra; the GDN-in-FLA notes, backward Steps
+1-7, derive the same gradients in chunked form).  Pinned by tests/test_oracle_backward.py: the
+forward equals the C oracle, the gradients match central finite differences of the C oracle on
+tiny inputs (both gate kinds), closed forms at beta = 0, and equal channel gates reduce to the
+scalar gate.
 """
 import numpy as np
 import torch
 
 
 def _recurrence(q, k, v, g, beta, scale, h0, cu):
-    """Token-major fp64 tensors q, k [T, H_qk, D_k], v [T, H_v, D_v], g, beta [T, H_v]; h0
-    [N, H_v, D_k, D_v] or None.  Returns (o [T, H_v, D_v], final [N, H_v, D_k, D_v])."""
+    """Token-major fp64 tensors q, k [T, H_qk, D_k], v [T, H_v, D_v], g [T, H_v] or [T, H_v, D_k],
+    beta [T, H_v]; h0 [N, H_v, D_k, D_v] or None.  Returns (o [T, H_v, D_v], final [N, H_v, D_k, D_v])."""
     T, H_qk, D_k = q.shape
     H_v, D_v = v.shape[1], v.shape[2]
     G = H_v // H_qk
@@ -26,7 +29,8 @@ def _recurrence(q, k, v, g, beta, scale, h0, cu):
         S = h0[n] if h0 is not None else torch.zeros(H_v, D_k, D_v, dtype=torch.float64)
         for t in range(int(cu[n]), int(cu[n + 1])):
             kt, qt, vt = k[t, hq], q[t, hq], v[t]                      # [H_v, D_k], [H_v, D_k], [H_v, D_v]
-            S = torch.exp(g[t])[:, None, None] * S                     # decay
+            a = torch.exp(g[t])
+            S = (a[:, None, None] if a.dim() == 1 else a[:, :, None]) * S   # decay (rows per channel)
             u = torch.einsum("hk,hkv->hv", kt, S)                      # S^T k
             w = beta[t][:, None] * (vt - u)
             S = S + kt[:, :, None] * w[:, None, :]                     # erase and write
@@ -38,8 +42,9 @@ def _recurrence(q, k, v, g, beta, scale, h0, cu):
 
 def gdn_backward(q, k, v, g, beta, scale, do, h0=None, dht=None, cu_seqlens=None):
     """Gradients of <o, do> + <final, dht> (dht None: 0).  Inputs as numpy arrays shaped like the
-    library's ([B, T, H, D] or packed with B = 1 and cu_seqlens).  Returns a dict of numpy fp64
-    arrays dq, dk, dv, dg, dbeta shaped like the inputs, dh0 [N, H_v, D_k, D_v], plus o and final."""
+    library's ([B, T, H, D] or packed with B = 1 and cu_seqlens; g [B, T, H_v] for the scalar gate or
+    [B, T, H_v, D_k] per channel).  Returns a dict of numpy fp64 arrays dq, dk, dv, dg, dbeta shaped
+    like the inputs, dh0 [N, H_v, D_k, D_v], plus o and final."""
     q = np.asarray(q, dtype=np.float64)
     B, T = q.shape[:2]
     cu = (np.arange(B + 1) * T) if cu_seqlens is None else np.asarray(cu_seqlens, dtype=np.int64)

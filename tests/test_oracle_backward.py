@@ -50,6 +50,39 @@ def test_gradients_match_finite_differences(name):
     np.testing.assert_allclose(r[key], fd, rtol=1e-6, atol=1e-8)
 
 
+@pytest.mark.parametrize("name", ["k", "g", "beta", "h0"])
+def test_per_channel_gradients_match_finite_differences(name):
+    q, k, v, g, b, h0, do, dht = _inputs(B=1, T=6, H=2, Hq=1, D=3, seed=7)
+    gk = -np.logaddexp(0.0, np.random.default_rng(8).standard_normal((1, 6, 2, 3)) - 1.0)
+    args = dict(q=q, k=k, v=v, g=gk, beta=b, h0=h0)
+    r = gdn_backward(q, k, v, gk, b, 0.7, do, h0, dht)
+    assert r["dg"].shape == gk.shape
+
+    def loss(a):
+        o, f = gdn_recurrent(a["q"], a["k"], a["v"], a["g"], a["beta"], 0.7, h0=a["h0"], gate="channel")
+        return float((o * do).sum() + (f * dht).sum())
+    x = args[name]
+    fd = np.zeros_like(x)
+    eps = 1e-6
+    for idx in np.ndindex(x.shape):
+        xp, xm = x.copy(), x.copy()
+        xp[idx] += eps
+        xm[idx] -= eps
+        fd[idx] = (loss({**args, name: xp}) - loss({**args, name: xm})) / (2 * eps)
+    key = {"beta": "dbeta", "h0": "dh0"}.get(name, "d" + name)
+    np.testing.assert_allclose(r[key], fd, rtol=1e-6, atol=1e-8)
+
+
+def test_per_channel_gate_with_equal_channels_is_the_scalar_gate():
+    q, k, v, g, b, h0, do, dht = _inputs(B=1, T=9, H=2, D=4, seed=9)
+    gk = np.repeat(g[..., None], 4, axis=-1)
+    r1 = gdn_backward(q, k, v, g, b, 0.5, do, h0, dht)
+    r2 = gdn_backward(q, k, v, gk, b, 0.5, do, h0, dht)
+    for n in ("dq", "dk", "dv", "dbeta", "dh0"):
+        np.testing.assert_allclose(r2[n], r1[n], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(r2["dg"].sum(-1), r1["dg"], rtol=1e-10, atol=1e-12)   # chain rule over copies
+
+
 def test_closed_forms_at_beta_zero():
     # beta = 0: S_t = (prod alpha) h0, o_t = scale S_t^T q_t, so dv = 0, dq_t = scale S_t do_t and
     # dh0 = sum_t scale A_t q_t do_t^T + A_T dht with A_t the decay product through t
