@@ -435,7 +435,7 @@ gdn_fwd_args bwd_as_fwd(const gdn_bwd_args *b) {
 
 struct BwdPlan {
     Plan fwd;
-    size_t off_states = 0, off_dsn = 0, off_pmat = 0, off_dqv = 0, off_dkv = 0, bytes = 0;
+    size_t off_states = 0, off_dsn = 0, off_pmat = 0, off_vp = 0, off_dl = 0, off_dqv = 0, off_dkv = 0, bytes = 0;
 };
 
 gdn_status validate_and_plan_bwd(const gdn_bwd_args *b, BwdPlan *bp) {
@@ -443,7 +443,6 @@ gdn_status validate_and_plan_bwd(const gdn_bwd_args *b, BwdPlan *bp) {
     const gdn_fwd_args f = bwd_as_fwd(b);
     gdn_status st = validate_and_plan(&f, &bp->fwd);
     if (st != GDN_OK) return st;
-    if (b->gate_kind != GDN_GATE_SCALAR) return fail(GDN_ERR_UNSUPPORTED, "the backward takes the scalar gate only");
     if ((int64_t)b->B * b->T > 0 && (!b->dq || !b->dk || !b->dv || !b->dg || !b->dbeta))
         return fail(GDN_ERR_INVALID_ARG, "dq, dk, dv, dg and dbeta are required");
     size_t off = align_up(bp->fwd.bytes);
@@ -451,6 +450,10 @@ gdn_status validate_and_plan_bwd(const gdn_bwd_args *b, BwdPlan *bp) {
     bp->off_states = off; off = align_up(off + st_bytes);
     bp->off_dsn = off;    off = align_up(off + st_bytes);
     bp->off_pmat = off;   off = align_up(off + (size_t)bp->fwd.total_chunks * b->H_v * 4096 * sizeof(float));
+    if (b->gate_kind == GDN_GATE_CHANNEL) {   // V' and dL of every chunk, between the two gradient kernels
+        bp->off_vp = off; off = align_up(off + (size_t)bp->fwd.total_chunks * b->H_v * 64 * b->D_v * sizeof(float));
+        bp->off_dl = off; off = align_up(off + (size_t)bp->fwd.total_chunks * b->H_v * 4096 * sizeof(float));
+    }
     if (b->H_v != b->H_qk) {
         const size_t g_bytes = (size_t)b->B * b->T * b->H_v * b->D_k * sizeof(float);
         bp->off_dqv = off; off = align_up(off + g_bytes);
@@ -492,10 +495,19 @@ extern "C" gdn_status gdn_bwd(const gdn_bwd_args *a, void *workspace, size_t wor
         if ((e = gdn::launch_plan(pp, s)) != hipSuccess) return fail(GDN_ERR_HIP, "plan launch: %s", hipGetErrorString(e));
     }
     // Step 1 of the notes: the chunks' (I + L)^-1, as the forward forms it
-    gdn::IntraParams ip{a->q, a->k, a->g, a->beta, chunks, a->T, (int)pl.total_chunks, a->H_qk, a->H_v,
-                        a->scale, ws + pl.off_A, ws + pl.off_P, reinterpret_cast<float *>(ws + pl.off_gates), gdn::Prologue{}};
-    if ((e = gdn::launch_intra(a->dtype, a->D_k, ip, s)) != hipSuccess)
-        return fail(GDN_ERR_HIP, "intra launch: %s", hipGetErrorString(e));
+    const bool channel = a->gate_kind == GDN_GATE_CHANNEL;
+    if (channel) {
+        gdn::IntraKdaParams ip{a->q, a->k, a->g, a->beta, chunks, a->T, (int)pl.total_chunks, a->H_qk, a->H_v,
+                               a->scale, ws + pl.off_A, ws + pl.off_P, ws + pl.off_kg, ws + pl.off_kd,
+                               ws + pl.off_qg, reinterpret_cast<float *>(ws + pl.off_gates), gdn::Prologue{}};
+        e = gdn::launch_intra_kda(a->dtype, a->D_k, ip, s);
+    } else {
+        gdn::IntraParams ip{a->q, a->k, a->g, a->beta, chunks, a->T, (int)pl.total_chunks, a->H_qk, a->H_v,
+                            a->scale, ws + pl.off_A, ws + pl.off_P, reinterpret_cast<float *>(ws + pl.off_gates),
+                            gdn::Prologue{}};
+        e = gdn::launch_intra(a->dtype, a->D_k, ip, s);
+    }
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "intra launch: %s", hipGetErrorString(e));
     gdn::BwdParams bw{};
     bw.q = a->q; bw.k = a->k; bw.v = a->v; bw.beta = a->beta; bw.dout = a->dout;
     bw.g = a->g; bw.h0 = a->h0; bw.dht = a->dht; bw.A = ws + pl.off_A;
@@ -505,6 +517,9 @@ extern "C" gdn_status gdn_bwd(const gdn_bwd_args *a, void *workspace, size_t wor
     bw.states = reinterpret_cast<float *>(ws + bp.off_states);
     bw.dsnext = reinterpret_cast<float *>(ws + bp.off_dsn);
     bw.pmat = reinterpret_cast<float *>(ws + bp.off_pmat);
+    bw.channel = channel ? 1 : 0;
+    bw.vp = channel ? reinterpret_cast<float *>(ws + bp.off_vp) : nullptr;
+    bw.dlmat = channel ? reinterpret_cast<float *>(ws + bp.off_dl) : nullptr;
     bw.dq = a->dq; bw.dk = a->dk; bw.dv = a->dv; bw.dg = a->dg; bw.dbeta = a->dbeta; bw.dh0 = a->dh0;
     const bool grouped = a->H_v != a->H_qk;
     bw.dq_v = grouped ? reinterpret_cast<float *>(ws + bp.off_dqv) : a->dq;

@@ -37,7 +37,7 @@ template <typename T>
 __device__ __forceinline__ void load_gates(const BwdParams &p, int64_t tok0, int nv, int h, float *sgl, float *sb) {
     const int lane = threadIdx.x & 63;
     const int64_t t = tok0 + min(lane, max(nv - 1, 0));
-    const float gv = lane < nv ? p.g[t * p.H_v + h] : 0.f;
+    const float gv = lane < nv ? static_cast<const float *>(p.g)[t * p.H_v + h] : 0.f;
     sgl[lane] = wave_inclusive_scan(gv);
     sb[lane] = lane < nv ? to_f32(static_cast<const T *>(p.beta)[t * p.H_v + h]) : 0.f;
 }
@@ -488,6 +488,518 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdParams p) {
     }
 }
 
+// ==========================================================================================
+// Per-channel gates (KDA walk-through, sections 3-5): the decay Diag(e^{G_t}) acts on the rows of
+// S, G the chunk-local cumsum of the [D_k] log-gates.  Per chunk, with Kg = K (.) e^G,
+// Kd = K (.) e^{G_C - G}, Qg = Q (.) e^G and the per-channel factors inside P and L,
+//   forward:  X = diag(beta)(V - Kg S),  V' = A X,  O = scale (Qg S + P V'),
+//             P_ij = sum_d q_id k_jd e^{G_id - G_jd} (j <= i),  S_next = Diag(e^{G_C}) S + Kd^T V'
+//   backward: dV' = Kd dS_next + scale P^T dO,  dX = A^T dV',  dA = dV' X^T,  dL = -A^T dA A^T,
+//             dS = Diag(e^{G_C}) dS_next + scale Qg^T dO - Kg^T diag(beta) dX,
+//             dq = scale e^G (.) (dO S^T) + dq_P,  dq_P[i][d] = sum_{j<=i} dP_ij k_jd e^{G_id - G_jd},
+//             dk = -diag(beta) e^G (.) (dX S^T) + e^{G_C - G} (.) (V' dS_next^T) + dk_P + dk_Lrow + dk_Lcol,
+//             dG = q (.) dq + k (.) (dk_X + dk_Lrow) - k (.) (dk_D + dk_P + dk_Lcol), the e^{G_C} terms
+//             on the last valid row, and dgk its reverse cumsum within the chunk per channel.
+// Two kernels per chunk: (a) the products with S and dS_next over value-column blocks, dL; (b) the
+// P and L terms with their per-channel factors.
+
+// chunk-local cumsum of per-channel log-gates: G (fp32 LDS rows of stride ld) holds the raw gates
+// of the chunk (zero past the end) on entry; the first DK threads scan one channel each
+template <int DK>
+__device__ __forceinline__ void cumsum_rows(float *G, int ld) {
+    __syncthreads();
+    if (threadIdx.x < DK) {
+        float acc = 0.f;
+        for (int i = 0; i < 64; ++i) {
+            acc += G[i * ld + threadIdx.x];
+            G[i * ld + threadIdx.x] = acc;
+        }
+    }
+    __syncthreads();
+}
+
+template <typename T>
+__device__ __forceinline__ void load_beta(const BwdParams &p, int64_t tok0, int nv, int h, float *sb) {
+    const int lane = threadIdx.x & 63;
+    sb[lane] = lane < nv ? to_f32(static_cast<const T *>(p.beta)[(tok0 + lane) * p.H_v + h]) : 0.f;
+}
+
+// ---- recomputed chunk states (per-channel gates)
+template <typename T, int DK>
+__global__ __launch_bounds__(256) void bwd_states_kda_kernel(BwdParams p) {
+    __shared__ float sKg[64][DK + 1], sKd[64][DK + 1], sA[64][65];
+    __shared__ float sS[DK][kBw + 1], sV[64][kBw + 1], sX[64][kBw + 1], sVp[64][kBw + 1];
+    __shared__ float sb[64], sgc[DK];
+    const int tid = threadIdx.x;
+    const int ncb = p.D_v / kBw;
+    const int cb = blockIdx.x % ncb, nh = blockIdx.x / ncb, h = nh % p.H_v, n = nh / p.H_v;
+    const int hq = h / (p.H_v / p.H_qk);
+    const SeqInfo si = seq_info(p.seq, n, p.T);
+    const int64_t DV = p.D_v, gks = (int64_t)p.H_v * DK;
+    for (int idx = tid; idx < DK * kBw; idx += 256) {
+        const int d = idx / kBw, j = idx % kBw;
+        sS[d][j] = p.h0 ? p.h0[(((int64_t)n * p.H_v + h) * DK + d) * DV + cb * kBw + j] : 0.f;
+    }
+    for (int c = 0; c < si.nchunks; ++c) {
+        const int64_t gci = si.chunk0 + c, tok0 = si.tok0 + (int64_t)c * kChunk;
+        const int nv = min(kChunk, si.len - c * kChunk);
+        __syncthreads();
+        float *st = p.states + ((gci * p.H_v + h) * DK) * DV + cb * kBw;
+        for (int idx = tid; idx < DK * kBw; idx += 256) st[(idx / kBw) * DV + idx % kBw] = sS[idx / kBw][idx % kBw];
+        load_rows<DK>(&sKg[0][0], DK + 1, static_cast<const T *>(p.k) + (int64_t)hq * DK, tok0, nv, (int64_t)p.H_qk * DK, 0);
+        load_rows<DK>(&sKd[0][0], DK + 1, static_cast<const T *>(p.g) + (int64_t)h * DK, tok0, nv, gks, 0);
+        load_rows<kBw>(&sV[0][0], kBw + 1, static_cast<const T *>(p.v) + (int64_t)h * DV, tok0, nv, (int64_t)p.H_v * DV, cb * kBw);
+        load_tile64(sA, static_cast<const T *>(p.A) + (gci * p.H_v + h) * 4096);
+        if (tid < 64) load_beta<T>(p, tok0, nv, h, sb);
+        cumsum_rows<DK>(&sKd[0][0], DK + 1);                 // sKd holds G
+        if (tid < DK) sgc[tid] = sKd[63][tid];
+        __syncthreads();
+        for (int idx = tid; idx < 64 * DK; idx += 256) {    // Kg = K e^G, Kd = K e^{G_C - G}
+            const int i = idx / DK, d = idx % DK;
+            const float k = sKg[i][d], G = sKd[i][d];
+            sKg[i][d] = k * __expf(G);
+            sKd[i][d] = k * __expf(sgc[d] - G);
+        }
+        __syncthreads();
+        for (int idx = tid; idx < 64 * kBw; idx += 256) {   // X = beta (V - Kg S)
+            const int i = idx / kBw, j = idx % kBw;
+            float s = 0.f;
+            for (int d = 0; d < DK; ++d) s += sKg[i][d] * sS[d][j];
+            sX[i][j] = sb[i] * (sV[i][j] - s);
+        }
+        __syncthreads();
+        for (int idx = tid; idx < 64 * kBw; idx += 256) {   // V' = A X
+            const int i = idx / kBw, j = idx % kBw;
+            float s = 0.f;
+            for (int t = 0; t <= i; ++t) s += sA[i][t] * sX[t][j];
+            sVp[i][j] = s;
+        }
+        __syncthreads();
+        for (int idx = tid; idx < DK * kBw; idx += 256) {   // S = Diag(e^{G_C}) S + Kd^T V'
+            const int d = idx / kBw, j = idx % kBw;
+            float s = 0.f;
+            for (int i = 0; i < 64; ++i) s += sKd[i][d] * sVp[i][j];
+            sS[d][j] = __expf(sgc[d]) * sS[d][j] + s;
+        }
+    }
+}
+
+// ---- scale P of every (chunk, value head), per-channel factors inside the sum
+template <typename T, int DK>
+__global__ __launch_bounds__(256) void bwd_p_kda_kernel(BwdParams p) {
+    __shared__ float sK[64][DK + 1], sQ[64][DK + 1], sG[64][DK + 1];
+    const int tid = threadIdx.x;
+    const int ci = blockIdx.x / p.H_v, h = blockIdx.x - ci * p.H_v;
+    const int hq = h / (p.H_v / p.H_qk);
+    const ChunkInfo cinfo = chunk_info(p.chunks, ci, p.T);
+    const int64_t qks = (int64_t)p.H_qk * DK;
+    load_rows<DK>(&sK[0][0], DK + 1, static_cast<const T *>(p.k) + (int64_t)hq * DK, cinfo.tok0, cinfo.nv, qks, 0);
+    load_rows<DK>(&sQ[0][0], DK + 1, static_cast<const T *>(p.q) + (int64_t)hq * DK, cinfo.tok0, cinfo.nv, qks, 0);
+    load_rows<DK>(&sG[0][0], DK + 1, static_cast<const T *>(p.g) + (int64_t)h * DK, cinfo.tok0, cinfo.nv,
+                  (int64_t)p.H_v * DK, 0);
+    cumsum_rows<DK>(&sG[0][0], DK + 1);
+    float *P = p.pmat + ((int64_t)ci * p.H_v + h) * 4096;
+    for (int idx = tid; idx < 4096; idx += 256) {
+        const int i = idx / 64, j = idx % 64;
+        float s = 0.f;
+        if (j <= i)
+            for (int d = 0; d < DK; ++d) s += sQ[i][d] * sK[j][d] * __expf(sG[i][d] - sG[j][d]);
+        P[idx] = j <= i ? p.scale * s : 0.f;
+    }
+}
+
+// ---- reverse scan of the state gradient (per-channel gates)
+template <typename T, int DK>
+__global__ __launch_bounds__(256) void bwd_dstate_kda_kernel(BwdParams p) {
+    __shared__ float sKd[64][DK + 1], sKg[64][DK + 1], sQg[64][DK + 1];
+    __shared__ float sA[64][65], sP[64][65];
+    __shared__ float sdS[DK][kBw + 1], sdO[64][kBw + 1], sKdS[64][kBw + 1], sdVp[64][kBw + 1], sdX[64][kBw + 1];
+    __shared__ float sb[64], sgc[DK];
+    const int tid = threadIdx.x;
+    const int ncb = p.D_v / kBw;
+    const int cb = blockIdx.x % ncb, nh = blockIdx.x / ncb, h = nh % p.H_v, n = nh / p.H_v;
+    const int hq = h / (p.H_v / p.H_qk);
+    const SeqInfo si = seq_info(p.seq, n, p.T);
+    const int64_t DV = p.D_v;
+    for (int idx = tid; idx < DK * kBw; idx += 256) {
+        const int d = idx / kBw, j = idx % kBw;
+        sdS[d][j] = p.dht ? p.dht[(((int64_t)n * p.H_v + h) * DK + d) * DV + cb * kBw + j] : 0.f;
+    }
+    for (int c = si.nchunks - 1; c >= 0; --c) {
+        const int64_t gci = si.chunk0 + c, tok0 = si.tok0 + (int64_t)c * kChunk;
+        const int nv = min(kChunk, si.len - c * kChunk);
+        __syncthreads();
+        float *dsn = p.dsnext + ((gci * p.H_v + h) * DK) * DV + cb * kBw;
+        for (int idx = tid; idx < DK * kBw; idx += 256) dsn[(idx / kBw) * DV + idx % kBw] = sdS[idx / kBw][idx % kBw];
+        const int64_t qks = (int64_t)p.H_qk * DK;
+        load_rows<DK>(&sKg[0][0], DK + 1, static_cast<const T *>(p.k) + (int64_t)hq * DK, tok0, nv, qks, 0);
+        load_rows<DK>(&sQg[0][0], DK + 1, static_cast<const T *>(p.q) + (int64_t)hq * DK, tok0, nv, qks, 0);
+        load_rows<DK>(&sKd[0][0], DK + 1, static_cast<const T *>(p.g) + (int64_t)h * DK, tok0, nv, (int64_t)p.H_v * DK, 0);
+        load_rows<kBw>(&sdO[0][0], kBw + 1, static_cast<const T *>(p.dout) + (int64_t)h * DV, tok0, nv, (int64_t)p.H_v * DV,
+                       cb * kBw);
+        load_tile64(sA, static_cast<const T *>(p.A) + (gci * p.H_v + h) * 4096);
+        load_tile64(sP, p.pmat + (gci * p.H_v + h) * 4096);
+        if (tid < 64) load_beta<T>(p, tok0, nv, h, sb);
+        cumsum_rows<DK>(&sKd[0][0], DK + 1);                 // sKd holds G
+        if (tid < DK) sgc[tid] = sKd[63][tid];
+        __syncthreads();
+        for (int idx = tid; idx < 64 * DK; idx += 256) {    // Kd, Kg, Qg
+            const int i = idx / DK, d = idx % DK;
+            const float G = sKd[i][d], e = __expf(G), k = sKg[i][d];
+            sKd[i][d] = k * __expf(sgc[d] - G);
+            sKg[i][d] = k * e;
+            sQg[i][d] *= e;
+        }
+        __syncthreads();
+        for (int idx = tid; idx < 64 * kBw; idx += 256) {   // Kd dS_next
+            const int i = idx / kBw, j = idx % kBw;
+            float s = 0.f;
+            for (int d = 0; d < DK; ++d) s += sKd[i][d] * sdS[d][j];
+            sKdS[i][j] = s;
+        }
+        __syncthreads();
+        for (int idx = tid; idx < 64 * kBw; idx += 256) {   // dV' = Kd dS_next + scale P^T dO
+            const int i = idx / kBw, j = idx % kBw;
+            float s = sKdS[i][j];
+            for (int t = i; t < 64; ++t) s += sP[t][i] * sdO[t][j];
+            sdVp[i][j] = s;
+        }
+        __syncthreads();
+        for (int idx = tid; idx < 64 * kBw; idx += 256) {   // dX = A^T dV'
+            const int i = idx / kBw, j = idx % kBw;
+            float s = 0.f;
+            for (int t = i; t < 64; ++t) s += sA[t][i] * sdVp[t][j];
+            sdX[i][j] = s;
+        }
+        __syncthreads();
+        for (int idx = tid; idx < DK * kBw; idx += 256) {   // dS = Diag(e^{G_C}) dS_next + Qg^T(...) - Kg^T(...)
+            const int d = idx / kBw, j = idx % kBw;
+            float s = 0.f;
+            for (int i = 0; i < 64; ++i) s += p.scale * sQg[i][d] * sdO[i][j] - sb[i] * sKg[i][d] * sdX[i][j];
+            sdS[d][j] = __expf(sgc[d]) * sdS[d][j] + s;
+        }
+    }
+    __syncthreads();
+    if (p.dh0) {
+        for (int idx = tid; idx < DK * kBw; idx += 256) {
+            const int d = idx / kBw, j = idx % kBw;
+            p.dh0[(((int64_t)n * p.H_v + h) * DK + d) * DV + cb * kBw + j] = sdS[d][j];
+        }
+    }
+}
+
+// the thread's G values down its column: rows e * RS + tid / DK of the chunk (G_C in *gc)
+template <typename T, int DK, int EPT>
+__device__ __forceinline__ void column_cumsum(const BwdParams &p, int64_t tok0, int nv, int h, float *Gr, float *gc) {
+    constexpr int RS = 256 / DK;
+    const int col = threadIdx.x % DK, r0 = threadIdx.x / DK;
+    const T *g = static_cast<const T *>(p.g) + (int64_t)h * DK + col;
+    float acc = 0.f;
+    int e = 0;
+    for (int t = 0; t < 64; ++t) {
+        if (t < nv) acc += to_f32(g[(tok0 + t) * p.H_v * DK]);
+        if (e < EPT && t == e * RS + r0) Gr[e++] = acc;
+    }
+    *gc = acc;
+}
+
+// ---- (a) per (chunk, value head): the products with S and dS_next, dV, dbeta from X, dL
+template <typename T, int DK>
+__global__ __launch_bounds__(256) void bwd_chunk_kda_a_kernel(BwdParams p) {
+    constexpr int EPT = 64 * DK / 256;
+    constexpr int RS = 256 / DK;
+    constexpr int W3 = kBw3 + 1;
+    __shared__ float sKg[64][DK + 1], sKd[64][DK + 1];
+    __shared__ float sA[64][65], sP[64][65], sdA[64][65];
+    constexpr int BLK = 2 * DK * W3 + 8 * 64 * W3;
+    __shared__ float sBlk[BLK > 64 * 65 ? BLK : 64 * 65];
+    __shared__ float sb[64], sdb[64], sgc[DK], sdgc[DK];
+    float (*sS)[W3] = reinterpret_cast<float (*)[W3]>(sBlk);
+    float (*sdS)[W3] = reinterpret_cast<float (*)[W3]>(sBlk + DK * W3);
+    float (*sV)[W3] = reinterpret_cast<float (*)[W3]>(sBlk + 2 * DK * W3);
+    float (*sdO)[W3] = sV + 64;
+    float (*sKS)[W3] = sV + 2 * 64;
+    float (*sX)[W3] = sV + 3 * 64;
+    float (*sVp)[W3] = sV + 4 * 64;
+    float (*sKdS)[W3] = sV + 5 * 64;
+    float (*sdVp)[W3] = sV + 6 * 64;
+    float (*sdX)[W3] = sV + 7 * 64;
+    float (*sT)[65] = reinterpret_cast<float (*)[65]>(sBlk);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int ci = blockIdx.x / p.H_v, h = blockIdx.x - ci * p.H_v;
+    const int hq = h / (p.H_v / p.H_qk);
+    const ChunkInfo cinfo = chunk_info(p.chunks, ci, p.T);
+    const int64_t tok0 = cinfo.tok0;
+    const int nv = cinfo.nv;
+    const int64_t DV = p.D_v, qks = (int64_t)p.H_qk * DK, vs = (int64_t)p.H_v * DV;
+    load_rows<DK>(&sKg[0][0], DK + 1, static_cast<const T *>(p.k) + (int64_t)hq * DK, tok0, nv, qks, 0);
+    load_rows<DK>(&sKd[0][0], DK + 1, static_cast<const T *>(p.g) + (int64_t)h * DK, tok0, nv, (int64_t)p.H_v * DK, 0);
+    load_tile64(sA, static_cast<const T *>(p.A) + ((int64_t)ci * p.H_v + h) * 4096);
+    load_tile64(sP, p.pmat + ((int64_t)ci * p.H_v + h) * 4096);
+    for (int idx = tid; idx < 4096; idx += 256) sdA[idx / 64][idx % 64] = 0.f;
+    if (tid < 64) {
+        load_beta<T>(p, tok0, nv, h, sb);
+        sdb[tid] = 0.f;
+    }
+    cumsum_rows<DK>(&sKd[0][0], DK + 1);
+    if (tid < DK) {
+        sgc[tid] = sKd[63][tid];
+        sdgc[tid] = 0.f;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < 64 * DK; idx += 256) {
+        const int i = idx / DK, d = idx % DK;
+        const float G = sKd[i][d], k = sKg[i][d];
+        sKd[i][d] = k * __expf(sgc[d] - G);
+        sKg[i][d] = k * __expf(G);
+    }
+    float accQ[EPT], accX[EPT], accD[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) accQ[e] = accX[e] = accD[e] = 0.f;
+    const int col = tid % DK;
+    const float *St = p.states + (((int64_t)ci * p.H_v + h) * DK) * DV;
+    const float *dSt = p.dsnext + (((int64_t)ci * p.H_v + h) * DK) * DV;
+    float *vpw = p.vp + ((int64_t)ci * p.H_v + h) * 64 * DV;
+    for (int c0 = 0; c0 < p.D_v; c0 += kBw3) {
+        __syncthreads();
+        {
+            constexpr int NE = DK * kBw3 / 256;
+            float a[NE], b[NE];
+#pragma unroll
+            for (int it = 0; it < NE; ++it) {
+                const int idx = tid + 256 * it, d = idx / kBw3, j = idx % kBw3;
+                a[it] = St[d * DV + c0 + j];
+                b[it] = dSt[d * DV + c0 + j];
+            }
+#pragma unroll
+            for (int it = 0; it < NE; ++it) {
+                const int idx = tid + 256 * it, d = idx / kBw3, j = idx % kBw3;
+                sS[d][j] = a[it];
+                sdS[d][j] = b[it];
+            }
+        }
+        load_rows<kBw3>(&sV[0][0], W3, static_cast<const T *>(p.v) + (int64_t)h * DV, tok0, nv, vs, c0);
+        load_rows<kBw3>(&sdO[0][0], W3, static_cast<const T *>(p.dout) + (int64_t)h * DV, tok0, nv, vs, c0);
+        __syncthreads();
+        for (int idx = tid; idx < 64 * kBw3; idx += 256) {  // Kg S, Kd dS_next, X
+            const int i = idx / kBw3, j = idx % kBw3;
+            float a = 0.f, e = 0.f;
+            for (int d = 0; d < DK; ++d) {
+                a += sKg[i][d] * sS[d][j];
+                e += sKd[i][d] * sdS[d][j];
+            }
+            sKS[i][j] = a;
+            sKdS[i][j] = e;
+            sX[i][j] = sb[i] * (sV[i][j] - a);
+        }
+        if (tid < DK) {    // e^{G_C} <S, dS_next> per channel (row d of both)
+            float s = 0.f;
+            for (int j = 0; j < kBw3; ++j) s += sS[tid][j] * sdS[tid][j];
+            sdgc[tid] += __expf(sgc[tid]) * s;
+        }
+        __syncthreads();
+        for (int idx = tid; idx < 64 * kBw3; idx += 256) {  // V' = A X
+            const int i = idx / kBw3, j = idx % kBw3;
+            float s = 0.f;
+            for (int t = 0; t <= i; ++t) s += sA[i][t] * sX[t][j];
+            sVp[i][j] = s;
+            vpw[i * DV + c0 + j] = s;
+        }
+        __syncthreads();
+        for (int idx = tid; idx < 64 * kBw3; idx += 256) {  // dV' = Kd dS_next + scale P^T dO
+            const int i = idx / kBw3, j = idx % kBw3;
+            float s = sKdS[i][j];
+            for (int t = i; t < 64; ++t) s += sP[t][i] * sdO[t][j];
+            sdVp[i][j] = s;
+        }
+        __syncthreads();
+        for (int idx = tid; idx < 64 * kBw3; idx += 256) {  // dX = A^T dV'
+            const int i = idx / kBw3, j = idx % kBw3;
+            float s = 0.f;
+            for (int t = i; t < 64; ++t) s += sA[t][i] * sdVp[t][j];
+            sdX[i][j] = s;
+        }
+        __syncthreads();
+        if (tid < 64) {    // dbeta from X
+            float db = 0.f;
+            for (int j = 0; j < kBw3; ++j) db += sdX[tid][j] * (sV[tid][j] - sKS[tid][j]);
+            sdb[tid] += db;
+        }
+        for (int idx = tid; idx < 64 * kBw3; idx += 256) {
+            const int i = idx / kBw3, j = idx % kBw3;
+            if (i < nv) p.dv[(tok0 + i) * vs + (int64_t)h * DV + c0 + j] = sb[i] * sdX[i][j];
+        }
+        for (int idx = tid; idx < 4096; idx += 256) {       // dA += dV' X^T
+            const int i = idx / 64, t = idx % 64;
+            float a = 0.f;
+            for (int j = 0; j < kBw3; ++j) a += sdVp[i][j] * sX[t][j];
+            sdA[i][t] += a;
+        }
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {                      // the raw products with S and dS_next
+            const int row = e * RS + tid / DK;
+            float a = 0.f, b = 0.f, x = 0.f;
+            for (int j = 0; j < kBw3; ++j) {
+                a += sdO[row][j] * sS[col][j];
+                x += sdX[row][j] * sS[col][j];
+                b += sVp[row][j] * sdS[col][j];
+            }
+            accQ[e] += a;
+            accX[e] += x;
+            accD[e] += b;
+        }
+    }
+    __syncthreads();
+    // dL = -A^T dA A^T (strictly lower), to the workspace
+    for (int idx = tid; idx < 4096; idx += 256) {
+        const int i = idx / 64, j = idx % 64;
+        float s = 0.f;
+        for (int t = i; t < 64; ++t) s += sA[t][i] * sdA[t][j];
+        sT[i][j] = s;
+    }
+    __syncthreads();
+    float *dLw = p.dlmat + ((int64_t)ci * p.H_v + h) * 4096;
+    for (int idx = tid; idx < 4096; idx += 256) {
+        const int i = idx / 64, j = idx % 64;
+        float s = 0.f;
+        if (j < i)
+            for (int t = 0; t <= j; ++t) s += sT[i][t] * sA[j][t];
+        dLw[idx] = j < i ? -s : 0.f;
+    }
+    // the gate factors of this thread's elements, then dq, dk and dG of these terms
+    float Gr[EPT], gC;
+    column_cumsum<T, DK, EPT>(p, tok0, nv, h, Gr, &gC);
+    const T *q = static_cast<const T *>(p.q) + (int64_t)hq * DK + col;
+    const T *k = static_cast<const T *>(p.k) + (int64_t)hq * DK + col;
+    float dgcs = 0.f;
+    float dqo[EPT], dko[EPT], dGo[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+        const int row = e * RS + tid / DK;
+        const float qv = row < nv ? to_f32(q[(tok0 + row) * qks]) : 0.f;
+        const float kv = row < nv ? to_f32(k[(tok0 + row) * qks]) : 0.f;
+        const float eg = __expf(Gr[e]);
+        const float dq_o = p.scale * eg * accQ[e];
+        const float dk_x = -sb[row] * eg * accX[e];
+        const float dk_d = __expf(gC - Gr[e]) * accD[e];
+        dqo[e] = dq_o;
+        dko[e] = dk_x + dk_d;
+        dGo[e] = qv * dq_o + kv * dk_x - kv * dk_d;
+        dgcs += kv * dk_d;
+    }
+    atomicAdd(&sdgc[col], dgcs);
+    __syncthreads();
+    const int hs = p.dq_v == p.dq ? hq : h, hn = p.dq_v == p.dq ? p.H_qk : p.H_v;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+        const int row = e * RS + tid / DK;
+        if (row < nv) {
+            const int64_t o = ((tok0 + row) * hn + hs) * DK + col;
+            p.dq_v[o] = dqo[e];
+            p.dk_v[o] = dko[e];
+            p.dg[((tok0 + row) * p.H_v + h) * DK + col] = dGo[e] + (row == nv - 1 ? sdgc[col] : 0.f);
+        }
+    }
+    if (tid < nv) p.dbeta[(tok0 + tid) * p.H_v + h] = sdb[tid];
+}
+
+// ---- (b) per (chunk, value head): the P and L terms with their per-channel factors, then the
+//      per-channel reverse cumsum of dG
+template <typename T, int DK>
+__global__ __launch_bounds__(256) void bwd_chunk_kda_b_kernel(BwdParams p) {
+    constexpr int EPT = 64 * DK / 256;
+    constexpr int RS = 256 / DK;
+    constexpr int W3 = kBw3 + 1;
+    __shared__ float sK[64][DK + 1], sQ[64][DK + 1], sG[64][DK + 1];
+    __shared__ float sdL[64][65], sdP[64][65];
+    __shared__ float sdO[64][W3], sVp[64][W3];
+    __shared__ float sb[64], sdb[64];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int ci = blockIdx.x / p.H_v, h = blockIdx.x - ci * p.H_v;
+    const int hq = h / (p.H_v / p.H_qk);
+    const ChunkInfo cinfo = chunk_info(p.chunks, ci, p.T);
+    const int64_t tok0 = cinfo.tok0;
+    const int nv = cinfo.nv;
+    const int64_t DV = p.D_v, qks = (int64_t)p.H_qk * DK, vs = (int64_t)p.H_v * DV;
+    load_rows<DK>(&sK[0][0], DK + 1, static_cast<const T *>(p.k) + (int64_t)hq * DK, tok0, nv, qks, 0);
+    load_rows<DK>(&sQ[0][0], DK + 1, static_cast<const T *>(p.q) + (int64_t)hq * DK, tok0, nv, qks, 0);
+    load_rows<DK>(&sG[0][0], DK + 1, static_cast<const T *>(p.g) + (int64_t)h * DK, tok0, nv, (int64_t)p.H_v * DK, 0);
+    load_tile64(sdL, p.dlmat + ((int64_t)ci * p.H_v + h) * 4096);
+    for (int idx = tid; idx < 4096; idx += 256) sdP[idx / 64][idx % 64] = 0.f;
+    if (tid < 64) {
+        load_beta<T>(p, tok0, nv, h, sb);
+        sdb[tid] = 0.f;
+    }
+    cumsum_rows<DK>(&sG[0][0], DK + 1);
+    // dP = scale dO V'^T (lower with diagonal), over value-column blocks
+    const float *vpw = p.vp + ((int64_t)ci * p.H_v + h) * 64 * DV;
+    for (int c0 = 0; c0 < p.D_v; c0 += kBw3) {
+        __syncthreads();
+        load_rows<kBw3>(&sdO[0][0], W3, static_cast<const T *>(p.dout) + (int64_t)h * DV, tok0, nv, vs, c0);
+        for (int idx = tid; idx < 64 * kBw3; idx += 256) sVp[idx / kBw3][idx % kBw3] = vpw[(idx / kBw3) * DV + c0 + idx % kBw3];
+        __syncthreads();
+        for (int idx = tid; idx < 4096; idx += 256) {
+            const int i = idx / 64, t = idx % 64;
+            float a = 0.f;
+            for (int j = 0; j < kBw3; ++j) a += sdO[i][j] * sVp[t][j];
+            sdP[i][t] += t <= i ? p.scale * a : 0.f;
+        }
+    }
+    __syncthreads();
+    const int col = tid % DK;
+    float dqp[EPT], dkb[EPT], dGb[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+        const int r = e * RS + tid / DK;
+        const float Gr = sG[r][col], qr = sQ[r][col], kr = sK[r][col];
+        float aq = 0.f, ar = 0.f, ap = 0.f, al = 0.f;
+        for (int t = 0; t < 64; ++t) {
+            if (t <= r) {                                  // r as the row: e^{G_r - G_t}
+                const float f = __expf(Gr - sG[t][col]);
+                aq += sdP[r][t] * sK[t][col] * f;
+                if (t < r) ar += sdL[r][t] * sK[t][col] * f;
+            }
+            if (t >= r) {                                  // r as the column: e^{G_t - G_r}
+                const float f = __expf(sG[t][col] - Gr);
+                ap += sdP[t][r] * sQ[t][col] * f;
+                if (t > r) al += sdL[t][r] * sb[t] * sK[t][col] * f;
+            }
+        }
+        const float dk_lrow = sb[r] * ar;
+        dqp[e] = aq;
+        dkb[e] = ap + dk_lrow + al;
+        dGb[e] = qr * aq + kr * dk_lrow - kr * (ap + al);
+        float x = kr * ar;                                  // dbeta from L: sum_d k_rd R_rd
+        for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);
+        if (lane == 0) atomicAdd(&sdb[r], x);
+    }
+    __syncthreads();
+    // finish dq, dk, dG; dG into the Q tile (every thread is done with Q) for the reverse cumsum
+    const int hs = p.dq_v == p.dq ? hq : h, hn = p.dq_v == p.dq ? p.H_qk : p.H_v;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+        const int r = e * RS + tid / DK;
+        float dG = 0.f;
+        if (r < nv) {
+            const int64_t o = ((tok0 + r) * hn + hs) * DK + col;
+            p.dq_v[o] += dqp[e];
+            p.dk_v[o] += dkb[e];
+            dG = p.dg[((tok0 + r) * p.H_v + h) * DK + col] + dGb[e];
+        }
+        sQ[r][col] = dG;
+    }
+    __syncthreads();
+    if (tid < DK) {
+        float acc = 0.f;
+        for (int t = nv - 1; t >= 0; --t) {
+            acc += sQ[t][tid];
+            p.dg[((tok0 + t) * p.H_v + h) * DK + tid] = acc;
+        }
+    }
+    if (tid < nv) p.dbeta[(tok0 + tid) * p.H_v + h] += sdb[tid];
+}
+
 // dq, dk of a query/key head: the sum over the value heads of its group
 __global__ __launch_bounds__(256) void bwd_group_sum_kernel(BwdParams p, int DK, int64_t n) {
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -507,6 +1019,31 @@ __global__ __launch_bounds__(256) void bwd_group_sum_kernel(BwdParams p, int DK,
 }  // namespace
 
 hipError_t launch_bwd(int dtype, int D_k, const BwdParams &p, hipStream_t s) {
+    if (p.channel) {
+        const int64_t scans = (int64_t)p.N * p.H_v * (p.D_v / kBw), chunks = (int64_t)p.n_chunks * p.H_v;
+        if (scans == 0) return hipSuccess;
+#define GDN_BWDK(K, T, DK, grid) hipLaunchKernelGGL((K<T, DK>), dim3((unsigned)(grid)), dim3(256), 0, s, p)
+#define GDN_BWDK_ALL(T, DK)                                  \
+    GDN_BWDK(bwd_states_kda_kernel, T, DK, scans);           \
+    if (chunks) GDN_BWDK(bwd_p_kda_kernel, T, DK, chunks);   \
+    GDN_BWDK(bwd_dstate_kda_kernel, T, DK, scans);           \
+    if (chunks) {                                            \
+        GDN_BWDK(bwd_chunk_kda_a_kernel, T, DK, chunks);     \
+        GDN_BWDK(bwd_chunk_kda_b_kernel, T, DK, chunks);     \
+    }
+        if (dtype == 1 && D_k == 128) { GDN_BWDK_ALL(bf16, 128) }
+        else if (dtype == 1 && D_k == 64) { GDN_BWDK_ALL(bf16, 64) }
+        else if (dtype == 0 && D_k == 128) { GDN_BWDK_ALL(float, 128) }
+        else if (dtype == 0 && D_k == 64) { GDN_BWDK_ALL(float, 64) }
+        else return hipErrorInvalidValue;
+#undef GDN_BWDK_ALL
+#undef GDN_BWDK
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess || p.dq_v == p.dq) return e;
+        const int64_t n = (int64_t)p.T_total * p.H_qk * D_k;
+        if (n) hipLaunchKernelGGL(bwd_group_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, D_k, n);
+        return hipGetLastError();
+    }
     const int64_t scans = (int64_t)p.N * p.H_v * (p.D_v / kBw), rscans = (int64_t)p.N * p.H_v * (p.D_v / kBwD);
     const int64_t chunks = (int64_t)p.n_chunks * p.H_v;
     if (scans == 0) return hipSuccess;

@@ -195,7 +195,8 @@ struct RecurrentParams {     // token-by-token path (gdn_fwd_recurrent)
 
 struct BwdParams {           // backward (gdn_bwd), scalar gate
     const void *q, *k, *v, *beta, *dout;   // input dtype
-    const float *g, *h0, *dht;             // h0, dht nullable
+    const void *g;                         // fp32 [tokens][H_v] (scalar gate) or [tokens][H_v][D_k] (input dtype)
+    const float *h0, *dht;                 // nullable
     const void *A;                         // (I + L)^-1 of every chunk, from the per-chunk kernel
     const SeqInfo *seq;                    // nullptr: batched input
     const ChunkInfo *chunks;
@@ -204,6 +205,8 @@ struct BwdParams {           // backward (gdn_bwd), scalar gate
     float scale;
     float *states, *dsnext;                // [n_chunks][H_v][D_k][D_v]: S entering, dS leaving each chunk
     float *pmat;                           // [n_chunks][H_v][64][64]: scale Pt
+    int channel;                           // 1: per-channel gates (g is [tokens][H_v][D_k] in the input dtype)
+    float *vp, *dlmat;                     // per-channel gates: V' [n_chunks][H_v][64][D_v], dL [n_chunks][H_v][64][64]
     float *dq, *dk, *dv, *dg, *dbeta, *dh0;
     float *dq_v, *dk_v;                    // per value head when H_v > H_qk, else dq / dk
 };

@@ -267,7 +267,7 @@ def make_bwd_args(q, k, v, g, beta, dout, grads, scale=None, initial_state=None,
 
 
 def bwd(q, k, v, g, beta, dout, scale=None, initial_state=None, dht=None, cu_seqlens=None, want_dh0=True):
-    """Backward of ``fwd`` (scalar gate): gdn_bwd.  Returns a dict of fp32 gradients dq, dk, dv, dg,
+    """Backward of ``fwd`` (both gate kinds): gdn_bwd.  Returns a dict of fp32 gradients dq, dk, dv, dg,
     dbeta and dh0 (None unless want_dh0), shaped like the inputs."""
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("dout", dout),
                     ("initial_state", initial_state), ("dht", dht)):
@@ -280,7 +280,7 @@ def bwd(q, k, v, g, beta, dout, scale=None, initial_state=None, dht=None, cu_seq
     N = q.shape[0] if cu_seqlens is None else cu_host.numel() - 1
     f32 = dict(dtype=torch.float32, device=q.device)
     grads = {"dq": torch.empty(q.shape, **f32), "dk": torch.empty(k.shape, **f32), "dv": torch.empty(v.shape, **f32),
-             "dg": torch.empty(beta.shape, **f32), "dbeta": torch.empty(beta.shape, **f32),
+             "dg": torch.empty(g.shape, **f32), "dbeta": torch.empty(beta.shape, **f32),
              "dh0": torch.empty((N, v.shape[2], k.shape[3], v.shape[3]), **f32) if want_dh0 else None}
     a = make_bwd_args(q, k, v, g, beta, dout, grads, scale, initial_state, dht, cu_dev, cu_host)
     nbytes = int(lib().gdn_bwd_workspace_bytes(ctypes.byref(a)))

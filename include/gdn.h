@@ -180,13 +180,15 @@ gdn_status gdn_fwd_recurrent(const gdn_fwd_args *a, void *stream);
  * page, section 7): the gradients of a loss through o and the final state, with the chunk states
  * recomputed (a forward replay), a reverse-time scan of the state gradient, and per chunk the
  * gradients of q, k, v, beta and the gate (dg as the reverse cumsum of the cumulative log-gate's
- * gradient within the chunk).  Scalar gate only, no prologue, no context parallelism.
+ * gradient within the chunk; per-channel gates: per channel).  Both gate kinds; no prologue, no
+ * context parallelism.
  * Inputs as for gdn_fwd (same layouts and dtype), plus
  *   dout   [B, T, H_v, D_v]  dtype   gradient of o
  *   dht    [N, H_v, D_k, D_v] fp32   gradient of the final state (NULL: zero)
  * Outputs, all fp32 (written, every token of every sequence):
  *   dq, dk [B, T, H_qk, D_k] (summed over the value heads of a group), dv [B, T, H_v, D_v],
- *   dg, dbeta [B, T, H_v], dh0 [N, H_v, D_k, D_v] (NULL: not written).
+ *   dg shaped like g ([B, T, H_v], or [B, T, H_v, D_k] per channel), dbeta [B, T, H_v],
+ *   dh0 [N, H_v, D_k, D_v] (NULL: not written).
  * Workspace: gdn_bwd_workspace_bytes(a) bytes of device memory, 256-byte aligned (it holds the
  * recomputed chunk states, the state gradients and the chunks' intra-chunk output matrices,
  * 2 x 4 D_k D_v + 16 KiB per chunk and head).
@@ -195,10 +197,10 @@ typedef struct {
     int32_t B, T, H_qk, H_v, D_k, D_v;
     int32_t chunk_size;               /* 64 */
     int32_t dtype;                    /* gdn_dtype of q, k, v, beta and dout */
-    int32_t gate_kind;                /* GDN_GATE_SCALAR */
+    int32_t gate_kind;                /* gdn_gate_kind */
     float scale;
     const void *q, *k, *v;
-    const float *g;
+    const void *g;                    /* as for gdn_fwd: fp32 [B, T, H_v] or dtype [B, T, H_v, D_k] */
     const void *beta;
     const float *h0;                  /* nullable */
     const int32_t *cu_seqlens_dev;    /* nullable, as for gdn_fwd */

@@ -77,8 +77,9 @@ def test_backward_validation():
     n = L.gdn_bwd_workspace_bytes(ctypes.byref(a))
     assert n >= 2 * 2 * 2 * 64 * 64 * 4                                              # states and dS per chunk
     assert L.gdn_bwd(ctypes.byref(a), None, 0, None) == gdn.GDN_ERR_WORKSPACE
-    a.gate_kind = gdn.GATE_CHANNEL
-    assert L.gdn_bwd(ctypes.byref(a), None, 0, None) == gdn.GDN_ERR_UNSUPPORTED
+    a.gate_kind = gdn.GATE_CHANNEL                                                   # both gate kinds
+    assert L.gdn_bwd_workspace_bytes(ctypes.byref(a)) > n                            # + V' and dL per chunk
+    assert L.gdn_bwd(ctypes.byref(a), None, 0, None) == gdn.GDN_ERR_WORKSPACE
     a.gate_kind, a.chunk_size = gdn.GATE_SCALAR, 32
     assert L.gdn_bwd(ctypes.byref(a), None, 0, None) == gdn.GDN_ERR_UNSUPPORTED
 

@@ -65,9 +65,23 @@ def test_backward_packed():
     _check(x, TOL["bf16"], "bf16 packed", seed=4)
 
 
-def test_backward_rejects_per_channel_gate():
-    from chunkwise_linear_attention_chunk_amd.gdn import GdnError
-    x = synth.make_inputs(synth.workload("kda_bf16", B=1, H=2, T=64, seed=614))
-    dev = torch.device("cuda:0")
-    with pytest.raises(GdnError, match="scalar gate"):
-        bwd(*(x[n].to(dev) for n in ("q", "k", "v", "g", "beta")), x["v"].to(dev), scale=x["scale"])
+@pytest.mark.parametrize("T", [1, 64, 150])
+def test_backward_per_channel_fp32(T):
+    x = synth.make_inputs(synth.workload("tiny_fp32", B=2, H=2, T=T, gate="channel", h0=True, seed=620 + T))
+    _check(x, TOL["fp32"], f"KDA fp32 T={T}", seed=10 + T)
+
+
+def test_backward_per_channel_fp32_head_dim_128_grouped_heads():
+    x = synth.make_inputs(synth.workload("tiny_fp32", B=1, H=4, H_qk=2, D=128, T=100, gate="channel", h0=True,
+                                         seed=630))
+    _check(x, TOL["fp32"], "KDA fp32 D=128 H_v=4 H_qk=2", seed=11)
+
+
+def test_backward_per_channel_bf16():
+    x = synth.make_inputs(synth.workload("kda_bf16", B=1, H=2, T=200, h0=True, seed=631))
+    _check(x, TOL["bf16"], "KDA bf16", seed=12)
+
+
+def test_backward_per_channel_packed():
+    x = synth.make_inputs(synth.workload("kda_bf16", B=1, n_seqs=4, lens=(1, 0, 130, 64), H=2, h0=True, seed=632))
+    _check(x, TOL["bf16"], "KDA bf16 packed", seed=13, dht=False)
