@@ -207,7 +207,7 @@ def bench_backward(a, torch, gdn, synth, dev):
     dht = torch.randn((N, H, D, Dv), generator=gen).to(dev)
     f32 = dict(dtype=torch.float32, device=dev)
     grads = {"dq": torch.empty(t["q"].shape, **f32), "dk": torch.empty(t["k"].shape, **f32),
-             "dv": torch.empty(t["v"].shape, **f32), "dg": torch.empty(t["beta"].shape, **f32),
+             "dv": torch.empty(t["v"].shape, **f32), "dg": torch.empty(t["g"].shape, **f32),
              "dbeta": torch.empty(t["beta"].shape, **f32), "dh0": torch.empty((N, H, D, Dv), **f32)}
     cu_host = None if x["cu_seqlens"] is None else x["cu_seqlens"].to(torch.int32)
     cu_dev = None if cu_host is None else cu_host.to(dev)

@@ -254,7 +254,17 @@ def fwd_recurrent_raw(args, stream):
 
 def make_bwd_args(q, k, v, g, beta, dout, grads, scale=None, initial_state=None, dht=None, cu_seqlens=None,
                   cu_seqlens_cpu=None):
-    """Fill a gdn_bwd_args; grads: dict of fp32 output tensors dq, dk, dv, dg, dbeta and optional dh0."""
+    """Fill a gdn_bwd_args; grads: dict of fp32 output tensors dq, dk, dv, dg, dbeta and optional dh0
+    (checked here against the shapes the kernels write: the C ABI cannot see buffer sizes)."""
+    N = q.shape[0] if cu_seqlens is None else cu_seqlens.numel() - 1
+    want = {"dq": q.shape, "dk": k.shape, "dv": v.shape, "dg": g.shape, "dbeta": beta.shape,
+            "dh0": (N, v.shape[2], k.shape[3], v.shape[3])}
+    for n, shape in want.items():
+        t = grads.get(n)
+        if t is None and n == "dh0":
+            continue
+        if t is None or tuple(t.shape) != tuple(shape) or t.dtype != torch.float32 or not t.is_contiguous():
+            raise GdnError(GDN_ERR_INVALID_ARG, f"{n} must be a contiguous fp32 tensor of shape {tuple(shape)}")
     f = make_args(q, k, v, g, beta, scale, initial_state, cu_seqlens, cu_seqlens_cpu)
     a = BwdArgs()
     for n in ("B", "T", "H_qk", "H_v", "D_k", "D_v", "chunk_size", "dtype", "gate_kind", "scale", "q", "k", "v", "g",

@@ -243,3 +243,20 @@ def test_plan_query():
     assert off["cp"] == 0 and off["pieces"] == 1 and off["total_segments"] == 1 and off["segment_chunks"] == 1024
     with pytest.raises(gdn.GdnError):
         gdn.plan(_args(chunk_size=48))
+
+
+def test_backward_gradient_shapes_are_checked_on_the_host():
+    # the kernels write dg shaped like g ([B, T, H_v, D_k] per channel): a buffer shaped like beta
+    # must be rejected before anything is launched
+    import torch
+    from chunkwise_linear_attention_chunk_amd import synth
+    x = synth.make_inputs(synth.workload("kda_bf16", B=1, H=2, T=64))
+    t = {n: x[n] for n in ("q", "k", "v", "g", "beta")}
+    f32 = dict(dtype=torch.float32)
+    grads = {"dq": torch.empty(t["q"].shape, **f32), "dk": torch.empty(t["k"].shape, **f32),
+             "dv": torch.empty(t["v"].shape, **f32), "dg": torch.empty(t["g"].shape, **f32),
+             "dbeta": torch.empty(t["beta"].shape, **f32)}
+    gdn.make_bwd_args(t["q"], t["k"], t["v"], t["g"], t["beta"], t["v"], grads, x["scale"])
+    with pytest.raises(gdn.GdnError, match="dg must be"):
+        gdn.make_bwd_args(t["q"], t["k"], t["v"], t["g"], t["beta"], t["v"], dict(grads, dg=torch.empty(t["beta"].shape, **f32)),
+                          x["scale"])
