@@ -170,8 +170,7 @@ struct RecLds {
     static constexpr int TILES = G0 + GB_FLOATS * 4;
     static constexpr int SXN = NSUB * NKB * NS * 64;   // state fragments handed to the output waves
     static constexpr int VXN = NSUB * 2 * NS * 64;     // V' fragments handed to the output waves
-    static constexpr int SON = OUT && ESZ == 2 ? 64 * BV : 1;   // bf16 output rows of the output waves
-    static constexpr int BYTES = NBUF * TILES + (OUT ? (SXN + VXN) * (int)sizeof(Frag<T>) : 0) + SON * 2;
+    static constexpr int BYTES = NBUF * TILES + (OUT ? (SXN + VXN) * (int)sizeof(Frag<T>) : 0);
     static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
@@ -259,7 +258,6 @@ void chunk_kernel(ChunkParams p) {
     __shared__ __attribute__((aligned(16))) unsigned char tiles1[NBUF == 2 ? L::TILES : 16];
     __shared__ __attribute__((aligned(16))) Frag<T> sSx[OUT ? L::SXN : 1];
     __shared__ __attribute__((aligned(16))) Frag<T> sVx[OUT ? L::VXN : 1];
-    __shared__ __attribute__((aligned(16))) bf16 sO[L::SON];   // output rows re-laid for 16-byte stores
 
     // the wave index is uniform across a wave: readfirstlane makes the role branches scalar
     const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
@@ -432,7 +430,8 @@ void chunk_kernel(ChunkParams p) {
     //      waves refill it; the loaders wait for their direct-to-LDS loads of chunk c (vmcnt(0), gfx9
     //      encoding: vmcnt bits [3:0],[15:14] = 0, expcnt [6:4] and lgkmcnt [11:8] at their maxima),
     //      and the barrier makes the tiles, the gate block and S_c visible to every wave.  Both roles
-    //      below pass the same barriers in the same order.
+    //      below pass the same barriers in the same order.  (Waiting for the loads only, with the
+    //      output stores issued after them left in flight, measured no faster.)
     auto chunk_top = [&]<bool LD>(int c) __attribute__((always_inline)) {
         if constexpr (NBUF == 1) {
             if (c > 0) {
@@ -452,6 +451,10 @@ void chunk_kernel(ChunkParams p) {
     //      with two output waves, wave 0 owns tiles 0 and 3 and wave 1 tiles 1 and 2 (which balances
     //      the causal P work); a single output wave owns all four.  Its own loop, so that none of
     //      the chain's registers (the state, its operand pairs) are live here and vice versa.
+    //      It accumulates O^T = scale (S_c^T Q^T diag(gamma) + V'^T P^T): the operand fragments are
+    //      the same with their roles swapped, and a lane then holds four consecutive value columns
+    //      of one token, which it stores straight from registers (one 8-byte bf16 or 16-byte fp32
+    //      store per 16 x 16 tile).
     if constexpr (OUT) {
         if (!chain) {
             constexpr int NR = 4 / NSUB;                  // token tiles of this wave
@@ -502,20 +505,15 @@ void chunk_kernel(ChunkParams p) {
                         if constexpr (CH && L::NS == 2) ql = ldpi_tile<T, L::KGPR>(tQl, 16 * mt[i] + l16, kb);
 #pragma unroll
                         for (int g = 0; g < NSUB; ++g) {
-                            if constexpr (CH && L::NS == 2) mma_xx(o[i][g], qf[kb][i], ql, sh[g][kb], sl[g][kb]);
-                            else mma_x(o[i][g], qf[kb][i], sh[g][kb], sl[g][kb]);
+                            if constexpr (CH && L::NS == 2) mma_xx(o[i][g], sh[g][kb], sl[g][kb], qf[kb][i], ql);
+                            else mma_pair_x(o[i][g], sh[g][kb], sl[g][kb], qf[kb][i]);
                         }
                     }
                 }
 #pragma unroll
                 for (int i = 0; i < NR; ++i) {
-                    f32x4 f;
-                    if constexpr (CH) {
-                        f = f32x4{p.scale, p.scale, p.scale, p.scale};
-                    } else {
-                        const float4 gm = *reinterpret_cast<const float4 *>(g3 + GB_GAQ + 16 * mt[i] + 4 * grp);
-                        f = f32x4{p.scale * gm.x, p.scale * gm.y, p.scale * gm.z, p.scale * gm.w};
-                    }
+                    // this lane's token is 16 mt[i] + l16
+                    const float f = CH ? p.scale : p.scale * g3[GB_GAQ + 16 * mt[i] + l16];
 #pragma unroll
                     for (int g = 0; g < NSUB; ++g) o[i][g] *= f;
                 }
@@ -576,51 +574,31 @@ void chunk_kernel(ChunkParams p) {
                         if constexpr (L::NS == 2) Vl[kb] = vxs[kb * L::NS * 64 + 64];
                     }
 #pragma unroll
-                    for (int b = 0; b < NPB; ++b) mma_xx(o[pb_tile(b)][g], ph[b], pl[b], Vh[pb_kb(b)], Vl[pb_kb(b)]);
+                    for (int b = 0; b < NPB; ++b) mma_xx(o[pb_tile(b)][g], Vh[pb_kb(b)], Vl[pb_kb(b)], ph[b], pl[b]);
                 }
-                // buffer stores: the resource covers the chunk's valid rows only (rows past the end
-                // are dropped by the bounds check)
+                // buffer stores straight from the accumulators: lane (grp, l16) of tile (i, g) holds
+                // O[16 mt[i] + l16][16 g + 4 grp + r], r = 0..3.  The resource covers the chunk's valid
+                // rows only (rows past the end are dropped by the bounds check).
                 if (c < wup) return;                       // warmup chunk: no output
                 const int64_t ebase = (int64_t)(si.tok0 + (cs + c) * kChunk) * v_stride + (int64_t)h * DV + c0;
                 const int oes = p.o_f32 ? 4 : ESZ;
                 const __amdgpu_buffer_rsrc_t ors = make_rsrc(static_cast<char *>(p.o) + ebase * oes,
                                                              ((nv - 1) * vs + BV) * oes);
-                bool stored = false;
-                if constexpr (ESZ == 2) {
-                    if (!p.o_f32) {
-                        // bf16: through this wave's LDS tile [16 NR rows][BV columns], then 16-byte
-                        // stores (BV / 8 per row); one wave writes and reads it, in order
-                        bf16 *so = sO + sub * (16 * NR * BV);
 #pragma unroll
-                        for (int i = 0; i < NR; ++i)
+                for (int i = 0; i < NR; ++i)
 #pragma unroll
-                            for (int g = 0; g < NSUB; ++g)
-#pragma unroll
-                                for (int r = 0; r < 4; ++r) so[(16 * i + 4 * grp + r) * BV + 16 * g + l16] = (bf16)o[i][g][r];
-                        constexpr int GPRW = BV / 8;                      // 16-byte pieces per row
-#pragma unroll
-                        for (int it = 0; it < 16 * NR * GPRW / 64; ++it) {
-                            const int qq = lane + 64 * it, lrow = qq / GPRW, piece = qq % GPRW;
-                            const int row = 16 * mt[lrow >> 4] + (lrow & 15);
-                            const u32x4 val = *reinterpret_cast<const u32x4 *>(so + lrow * BV + 8 * piece);
-                            __builtin_amdgcn_raw_buffer_store_b128(val, ors, (row * vs + 8 * piece) * 2, 0, 0);
+                    for (int g = 0; g < NSUB; ++g) {
+                        const int off = (16 * mt[i] + l16) * vs + 16 * g + 4 * grp;   // elements
+                        const f32x4 &x = o[i][g];
+                        if (ESZ == 2 && !p.o_f32) {
+                            const bf16x4 b = {(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+                            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, b), ors, off * 2, 0, 0);
+                        } else {
+                            const u32x4 w = {__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
+                                             __float_as_uint(x[3])};
+                            __builtin_amdgcn_raw_buffer_store_b128(w, ors, off * 4, 0, 0);
                         }
-                        stored = true;
                     }
-                }
-                if (!stored) {
-#pragma unroll
-                    for (int i = 0; i < NR; ++i)
-#pragma unroll
-                        for (int g = 0; g < NSUB; ++g) {
-                            const int vlane = ((4 * grp) * vs + 16 * g + l16) * oes;
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) {
-                                const int soff = (16 * mt[i] + r) * vs * oes;
-                                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o[i][g][r]), ors, vlane, soff, 0);
-                            }
-                        }
-                }
             };
             if (nch > 0) {
                 issue_kq(0, tiles0, 0, 1, LD_ALL);

@@ -24,6 +24,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // raw 16 bytes (a native vector, so
                                                               // selects and copies stay in registers)
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));  // raw 8 bytes
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -157,6 +158,12 @@ template <typename T>
 __device__ __forceinline__ void mma_x(f32x4 &acc, const Frag<T> &a, const Frag<T> &bh, const Frag<T> &bl) {
     mma(acc, a, bh);
     if constexpr (Split<T>::parts == 2) mma(acc, a, bl);
+}
+// acc += (ah + al) * b            (a hi/lo pair, then an exact operand)
+template <typename T>
+__device__ __forceinline__ void mma_pair_x(f32x4 &acc, const Frag<T> &ah, const Frag<T> &al, const Frag<T> &b) {
+    mma(acc, ah, b);
+    if constexpr (Split<T>::parts == 2) mma(acc, al, b);
 }
 // acc += (ah + al) * (bh + bl)    (lo * lo dropped)
 template <typename T>

@@ -24,15 +24,17 @@ namespace {
 
 // Exact inverse of the unit lower triangular I + L (L strictly lower, fp32 [64][LP] in LDS) into X
 // (same layout, strictly lower part only): forward substitution inside the four 16x16 diagonal
-// blocks (lane = column), then the block-triangular merges 16 -> 32 -> 64 on fp32 MFMA.  X may be
-// L itself: each block of X is written only after every read of the L block at its place.  Called
-// by all 256 threads with L complete and visible; returns after a barrier, X complete.
+// blocks, then the block-triangular merges 16 -> 32 -> 64 on fp32 MFMA.  X may be L itself: each
+// block of X is written only after every read of the L block at its place.  Called by all 256
+// threads with L complete and visible; returns after a barrier, X complete.
 __device__ __forceinline__ void invert_unit_lower(const float *sL, float *sX) {
     constexpr int LP = 64 + 4;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, grp = lane >> 4;
-    // ---- inverses of the four 16x16 diagonal blocks: lane c owns column c, row i absorbs rows < i
-    {
-        const float *L = sL + (16 * wave) * LP + 16 * wave;
+    // ---- inverses of the four 16x16 diagonal blocks, all in wave 0 (the other waves would repeat
+    //      its vector work on idle lanes): lane group grp takes block grp, lane l16 its column c;
+    //      row i absorbs the rows above it.  The lanes of a group read the same L element.
+    if (wave == 0) {
+        const float *L = sL + (16 * grp) * LP + 16 * grp;
         const int c = l16;
         float x[16];
 #pragma unroll
@@ -42,10 +44,8 @@ __device__ __forceinline__ void invert_unit_lower(const float *sL, float *sX) {
             for (int j = 0; j < i; ++j) s -= L[i * LP + j] * x[j];
             x[i] = s;
         }
-        if (grp == 0) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) sX[(16 * wave + i) * LP + 16 * wave + c] = x[i];
-        }
+        for (int i = 0; i < 16; ++i) sX[(16 * grp + i) * LP + 16 * grp + c] = x[i];
     }
     __syncthreads();
 
@@ -200,6 +200,13 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraParams p) {
     const int last = max(nv - 1, 0);
     constexpr int VPR = DK / VEC;
     constexpr int NV = 64 * VPR / 256;
+    // wave 0: this lane's token's log-gate and beta, in flight together with the K rows
+    const int64_t gidx = (int64_t)(t0 + min(lane, last)) * p.H_v + h;
+    float gx = 0.f, bx = 0.f;
+    if (wave == 0) {
+        gx = g[gidx];
+        bx = to_f32(beta[gidx]);
+    }
     u32x4 kv[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
@@ -242,10 +249,8 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraParams p) {
     }
     __syncthreads();
     if (wave == 0) {
-        const int64_t idx = (int64_t)(t0 + min(lane, last)) * p.H_v + h;
-        const float gx = g[idx];
         const float gv = lane < nv ? (p.pro.A_log ? gate_activation(p.pro, gx, p.pro.A_log[h], p.pro.dt_bias ? p.pro.dt_bias[h] : 0.f) : gx) : 0.f;
-        const float bv = lane < nv ? beta_value(p.pro, to_f32(beta[idx])) : 0.f;
+        const float bv = lane < nv ? beta_value(p.pro, bx) : 0.f;
         const float gl = wave_inclusive_scan(gv) * kLog2e;     // log2 gamma_t
         const float glC = __shfl(gl, 63, 64);                  // at the last valid token
         sGl[lane] = gl;
