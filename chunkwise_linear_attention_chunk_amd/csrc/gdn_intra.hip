@@ -92,8 +92,10 @@ __device__ __forceinline__ void invert_unit_lower(const float *sL, float *sX) {
     __syncthreads();
 }
 
-// Store X's strictly lower part as the unit lower triangular A = I + X (zero above the diagonal)
-// in the input dtype, [64][64] row-major at A.
+// Store the inverse as the unit lower triangular A (zero above the diagonal) in the input dtype,
+// [64][64] row-major at A.  X's 16x16 tiles on and below the diagonal are the inverse itself (the
+// diagonal tiles come out of the substitution with exact ones on the diagonal and exact zeros above
+// it); the tiles above the diagonal hold stale data and are written as zeros.
 template <typename T>
 __device__ __forceinline__ void store_unit_lower(const float *sX, T *A) {
     constexpr int VEC = Vec16<T>::N, LP = 64 + 4;
@@ -101,19 +103,18 @@ __device__ __forceinline__ void store_unit_lower(const float *sX, T *A) {
     for (int it = 0; it < 64 * 64 / VEC / 256; ++it) {
         const int idx = threadIdx.x + 256 * it;
         const int row = idx / (64 / VEC), c0 = (idx - row * (64 / VEC)) * VEC;
-        float x[VEC];
+        u32x4 out = {0u, 0u, 0u, 0u};
+        if ((c0 >> 4) <= (row >> 4)) {             // a tile on or below the diagonal
+            T vals[VEC];
 #pragma unroll
-        for (int e = 0; e < VEC; e += 4) {
-            const float4 v = *reinterpret_cast<const float4 *>(sX + row * LP + c0 + e);
-            x[e] = v.x; x[e + 1] = v.y; x[e + 2] = v.z; x[e + 3] = v.w;
+            for (int e = 0; e < VEC; e += 4) {
+                const float4 v = *reinterpret_cast<const float4 *>(sX + row * LP + c0 + e);
+                vals[e] = from_f32<T>(v.x); vals[e + 1] = from_f32<T>(v.y);
+                vals[e + 2] = from_f32<T>(v.z); vals[e + 3] = from_f32<T>(v.w);
+            }
+            out = *reinterpret_cast<const u32x4 *>(vals);
         }
-        T vals[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            const int col = c0 + e;
-            vals[e] = from_f32<T>(col < row ? x[e] : (col == row ? 1.f : 0.f));
-        }
-        *reinterpret_cast<u32x4 *>(A + row * 64 + c0) = *reinterpret_cast<const u32x4 *>(vals);
+        *reinterpret_cast<u32x4 *>(A + row * 64 + c0) = out;
     }
 }
 
@@ -242,10 +243,18 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraParams p) {
     } else if (tid < 64) {
         sRk[tid] = sRq[tid] = 1.f;
     }
+    if (nv == kChunk) {                  // a full chunk (the common case): no row masking
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const int idx = tid + 256 * i, row = idx / VPR, cv = idx % VPR;
-        *reinterpret_cast<u32x4 *>(sK + row * KP + cv * VEC) = row < nv ? kv[i] : u32x4{0u, 0u, 0u, 0u};
+        for (int i = 0; i < NV; ++i) {
+            const int idx = tid + 256 * i, row = idx / VPR, cv = idx % VPR;
+            *reinterpret_cast<u32x4 *>(sK + row * KP + cv * VEC) = kv[i];
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int idx = tid + 256 * i, row = idx / VPR, cv = idx % VPR;
+            *reinterpret_cast<u32x4 *>(sK + row * KP + cv * VEC) = row < nv ? kv[i] : u32x4{0u, 0u, 0u, 0u};
+        }
     }
     __syncthreads();
     if (wave == 0) {
@@ -253,11 +262,12 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraParams p) {
         const float bv = lane < nv ? beta_value(p.pro, bx) : 0.f;
         const float gl = wave_inclusive_scan(gv) * kLog2e;     // log2 gamma_t
         const float glC = __shfl(gl, 63, 64);                  // at the last valid token
+        const float rk = sRk[lane], rq = sRq[lane];
         sGl[lane] = gl;
-        sB[lane] = bv;
+        sB[lane] = bv * rk;                                    // the row factor of A_raw
         // gate block of the recurrence
         float *gbk = p.gates + ((int64_t)ci * p.H_v + h) * GB_FLOATS;
-        const float gam = fast_exp2(gl), rk = sRk[lane], rq = sRq[lane];
+        const float gam = fast_exp2(gl);
         gbk[GB_BETA + lane] = bv;
         gbk[GB_SC + lane] = fast_exp2(glC - gl) * rk;
         gbk[GB_GAK + lane] = gam * rk;
@@ -292,12 +302,13 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraParams p) {
     for (int n = 0; n < NT; ++n) {
         if (n >= ntiles) break;
         const int j = 16 * TJ[n] + l16;
-        const float glj = sGl[j];
+        const float glj = sGl[j], rj = sRk[j];
+        const bool diag = TI[n] == TJ[n];            // only diagonal tiles have entries j >= i
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int i = 16 * TI[n] + 4 * grp + r;
-            const float gam = fast_exp2(sGl[i] - glj);
-            sL[i * LP + j] = (j < i) ? sB[i] * gam * (sRk[i] * sRk[j]) * aa[n][r] : 0.f;
+            const float x = sB[i] * fast_exp2(sGl[i] - glj) * rj * aa[n][r];
+            sL[i * LP + j] = (!diag || j < i) ? x : 0.f;
         }
     }
     __syncthreads();  // A_raw is complete
