@@ -128,7 +128,8 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanParams p) {
 }
 
 // tile selections of the recurrence kernel's loads
-enum { LD_A = 1, LD_P = 2, LD_V = 4, LD_G = 8, LD_K = 16, LD_Q = 32, LD_ALL = 63 };
+// (LD_KD: with per-channel gates, the decayed K tile K 2^(G_C - G) of the state update)
+enum { LD_A = 1, LD_P = 2, LD_V = 4, LD_G = 8, LD_K = 16, LD_Q = 32, LD_KD = 64, LD_ALL = 127 };
 
 // ------------------------------------------------------------------------------------------
 // Recurrence + output.  One workgroup per (sequence segment, value head, NSUB slices of 16 value
@@ -248,7 +249,14 @@ void chunk_kernel(ChunkParams p) {
     // main pass with two tile buffers: the chain waves stream the next chunk's K and A tiles, the
     // output waves the rest
     constexpr bool CHAIN_LD = MODE == 0 && NBUF == 2;
-    constexpr int OUT_LD = CHAIN_LD ? LD_ALL & ~(LD_K | LD_A) : LD_ALL;
+    constexpr int OUT_LD = CHAIN_LD ? LD_ALL & ~(LD_K | LD_KD | LD_A) : LD_ALL;
+    // main pass with one tile buffer and per-channel gates: the tiles that only phase 1 reads
+    // (everything but the gate block and the decayed K tile) are refilled with the next chunk's
+    // right after the mid-chunk barrier, so their loads overlap phase 2; the rest at the chunk top.
+    // (With a scalar gate the one-buffer build runs two workgroups per CU, which already cover
+    // each other's loads; refilling early measured slower there.)
+    constexpr bool EARLY_LD = MODE == 0 && NBUF == 1 && CH;
+    constexpr int LATE_LD = CH ? (LD_KD | LD_G) : LD_G;
 
     // Separate LDS objects for the two tile buffers and for the exchange: the chunk loop is
     // unrolled by two, so every LDS access names its buffer at compile time and the compiler can
@@ -349,9 +357,9 @@ void chunk_kernel(ChunkParams p) {
             const int i = sub + NL * j;
             if (j % np != part_q) continue;
             if (NKI * NL != L::KGPR && i >= L::KGPR) break;
-            if (what & LD_K) {
-                buffer_granule_to_lds(rK, tb + L::K0 + 1024 * i, offK[j], 0);
-                if constexpr (CH) {
+            if (what & LD_K) buffer_granule_to_lds(rK, tb + L::K0 + 1024 * i, offK[j], 0);
+            if constexpr (CH) {
+                if (what & LD_KD) {
 #pragma unroll
                     for (int part = 0; part < L::NS; ++part)
                         buffer_granule_to_lds(rKd, tb + L::KD0 + part * L::KT + 1024 * i, offK[j], part * 64 * DK * ESZ);
@@ -437,8 +445,9 @@ void chunk_kernel(ChunkParams p) {
             if (c > 0) {
                 __syncthreads();
                 if constexpr (LD) {
-                    issue_kq(c, tiles0, 0, 1, LD_ALL);
-                    issue_apvg(c, tiles0, 0, 1, LD_ALL);
+                    constexpr int what = EARLY_LD ? LATE_LD : LD_ALL;
+                    issue_kq(c, tiles0, 0, 1, what);
+                    issue_apvg(c, tiles0, 0, 1, what);
                 }
             }
         }
@@ -562,7 +571,13 @@ void chunk_kernel(ChunkParams p) {
 #pragma unroll
                     for (int b = 0; b < NPB; ++b) form_p(b);
                 }
-                lds_only_barrier();  // V' of chunk c is visible
+                lds_only_barrier();  // V' of chunk c is visible; every wave is done with phase 1
+                if constexpr (EARLY_LD) {
+                    if (c + 1 < nch) {
+                        issue_kq(c + 1, tiles0, 0, 1, LD_ALL & ~LATE_LD);
+                        issue_apvg(c + 1, tiles0, 0, 1, LD_ALL & ~LATE_LD);
+                    }
+                }
                 // intra-chunk part: P V'
 #pragma unroll
                 for (int g = 0; g < NSUB; ++g) {
@@ -728,7 +743,7 @@ void chunk_kernel(ChunkParams p) {
         if constexpr (CHAIN_LD) {
             // the K and A tiles of chunk c + 1 (the chain waves reach this barrier first)
             if (more) {
-                issue_kq(c + 1, tnext, 0, 1, LD_K);
+                issue_kq(c + 1, tnext, 0, 1, LD_K | LD_KD);
                 issue_apvg(c + 1, tnext, 0, 1, LD_A);
             }
         }
