@@ -30,6 +30,8 @@ constexpr int kBwD = 32;    // value columns per workgroup of the reverse scan (
                             // 5.8 ms, 32 columns 5.4 ms on the Qwen3-Next shape; the replay is
                             // faster at 16: 2.1 against 3.1 ms)
 constexpr int kBw3 = 8;     // value columns per block of the per-chunk gradient kernel
+constexpr int kBwT = 512;   // threads of the per-chunk gradient kernel (two waves per SIMD hide its
+                            // LDS latency; 256 threads measured slower)
 
 // chunk-local gates of chunk (tok0, nv) and head h into sgl (cumsum, natural log) and sb (beta);
 // rows past the end carry beta = 0 and the last valid cumsum.  Wave 0 only.
@@ -44,34 +46,36 @@ __device__ __forceinline__ void load_gates(const BwdParams &p, int64_t tok0, int
 
 // rows [0, nv) of a [64][cols] tile of x (row stride ld, column offset c0) into fp32 LDS, zero
 // past the end
-// (256 threads; the element loads of a thread are independent and issued together, rows past
+// (NT threads; the element loads of a thread are independent and issued together, rows past
 // the end are clamped to the last valid row and zeroed at the store)
-template <int COLS, typename T>
+template <int COLS, typename T, int NT = 256>
 __device__ __forceinline__ void load_rows(float *dst, int dst_ld, const T *x, int64_t tok0, int nv, int64_t ld,
                                           int c0) {
-    constexpr int N = 64 * COLS / 256;
+    constexpr int N = 64 * COLS / NT;
+    static_assert(N * NT == 64 * COLS, "whole rows per pass");
     float v[N];
 #pragma unroll
     for (int it = 0; it < N; ++it) {
-        const int idx = threadIdx.x + 256 * it, i = idx / COLS, j = idx - i * COLS;
+        const int idx = threadIdx.x + NT * it, i = idx / COLS, j = idx - i * COLS;
         v[it] = to_f32(x[(tok0 + min(i, nv - 1)) * ld + c0 + j]);
     }
 #pragma unroll
     for (int it = 0; it < N; ++it) {
-        const int idx = threadIdx.x + 256 * it, i = idx / COLS, j = idx - i * COLS;
+        const int idx = threadIdx.x + NT * it, i = idx / COLS, j = idx - i * COLS;
         dst[i * dst_ld + j] = i < nv ? v[it] : 0.f;
     }
 }
 
-// a [64][64] tile of the input dtype (or fp32) into fp32 LDS rows of stride 65
-template <typename T>
+// a [64][64] tile of the input dtype (or fp32) into fp32 LDS rows of stride 65 (NT threads)
+template <typename T, int NT = 256>
 __device__ __forceinline__ void load_tile64(float (*dst)[65], const T *x) {
-    float v[16];
+    constexpr int N = 4096 / NT;
+    float v[N];
 #pragma unroll
-    for (int it = 0; it < 16; ++it) v[it] = to_f32(x[threadIdx.x + 256 * it]);
+    for (int it = 0; it < N; ++it) v[it] = to_f32(x[threadIdx.x + NT * it]);
 #pragma unroll
-    for (int it = 0; it < 16; ++it) {
-        const int idx = threadIdx.x + 256 * it;
+    for (int it = 0; it < N; ++it) {
+        const int idx = threadIdx.x + NT * it;
         dst[idx / 64][idx % 64] = v[it];
     }
 }
@@ -227,9 +231,10 @@ __global__ __launch_bounds__(256) void bwd_dstate_kernel(BwdParams p) {
 
 // ---- per (chunk, value head): every gradient of the chunk's inputs
 template <typename T, int DK>
-__global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdParams p) {
-    constexpr int EPT = 64 * DK / 256;          // dq / dk elements per thread (rows e * 256 / DK + tid / DK)
-    constexpr int RS = 256 / DK;
+__global__ __launch_bounds__(kBwT) void bwd_chunk_kernel(BwdParams p) {
+    constexpr int NT = kBwT;
+    constexpr int EPT = 64 * DK / NT;           // dq / dk elements per thread (rows e * NT / DK + tid / DK)
+    constexpr int RS = NT / DK;
     constexpr int W3 = kBw3 + 1;                // odd row strides against LDS bank conflicts
     __shared__ float sK[64][DK + 1], sQ[64][DK + 1];
     __shared__ float sA[64][65], sdA[64][65], sPt[64][65], sdP[64][65];
@@ -257,10 +262,10 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdParams p) {
     const int64_t tok0 = cinfo.tok0;
     const int nv = cinfo.nv;
     const int64_t DV = p.D_v, qks = (int64_t)p.H_qk * DK, vs = (int64_t)p.H_v * DV;
-    load_rows<DK>(&sK[0][0], DK + 1, static_cast<const T *>(p.k) + (int64_t)hq * DK, tok0, nv, qks, 0);
-    load_rows<DK>(&sQ[0][0], DK + 1, static_cast<const T *>(p.q) + (int64_t)hq * DK, tok0, nv, qks, 0);
-    load_tile64(sA, static_cast<const T *>(p.A) + ((int64_t)ci * p.H_v + h) * 4096);
-    for (int idx = tid; idx < 4096; idx += 256) {
+    load_rows<DK, T, NT>(&sK[0][0], DK + 1, static_cast<const T *>(p.k) + (int64_t)hq * DK, tok0, nv, qks, 0);
+    load_rows<DK, T, NT>(&sQ[0][0], DK + 1, static_cast<const T *>(p.q) + (int64_t)hq * DK, tok0, nv, qks, 0);
+    load_tile64<T, NT>(sA, static_cast<const T *>(p.A) + ((int64_t)ci * p.H_v + h) * 4096);
+    for (int idx = tid; idx < 4096; idx += NT) {
         sdA[idx / 64][idx % 64] = 0.f;
         sdP[idx / 64][idx % 64] = 0.f;
     }
@@ -270,7 +275,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdParams p) {
     }
     if (tid == 0) sdglC = 0.f;
     __syncthreads();
-    for (int idx = tid; idx < 4096; idx += 256) {           // Pt (lower with diagonal, no scale)
+    for (int idx = tid; idx < 4096; idx += NT) {           // Pt (lower with diagonal, no scale)
         const int i = idx / 64, j = idx % 64;
         float s = 0.f;
         if (j <= i)
@@ -288,25 +293,25 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdParams p) {
     for (int c0 = 0; c0 < p.D_v; c0 += kBw3) {
         __syncthreads();   // Pt is complete; the previous block is done with its tiles
         {
-            constexpr int NE = DK * kBw3 / 256;
+            constexpr int NE = DK * kBw3 / NT;
             float a[NE], b[NE];
 #pragma unroll
             for (int it = 0; it < NE; ++it) {
-                const int idx = tid + 256 * it, d = idx / kBw3, j = idx % kBw3;
+                const int idx = tid + NT * it, d = idx / kBw3, j = idx % kBw3;
                 a[it] = St[d * DV + c0 + j];
                 b[it] = dSt[d * DV + c0 + j];
             }
 #pragma unroll
             for (int it = 0; it < NE; ++it) {
-                const int idx = tid + 256 * it, d = idx / kBw3, j = idx % kBw3;
+                const int idx = tid + NT * it, d = idx / kBw3, j = idx % kBw3;
                 sS[d][j] = a[it];
                 sdS[d][j] = b[it];
             }
         }
-        load_rows<kBw3>(&sV[0][0], W3, static_cast<const T *>(p.v) + (int64_t)h * DV, tok0, nv, vs, c0);
-        load_rows<kBw3>(&sdO[0][0], W3, static_cast<const T *>(p.dout) + (int64_t)h * DV, tok0, nv, vs, c0);
+        load_rows<kBw3, T, NT>(&sV[0][0], W3, static_cast<const T *>(p.v) + (int64_t)h * DV, tok0, nv, vs, c0);
+        load_rows<kBw3, T, NT>(&sdO[0][0], W3, static_cast<const T *>(p.dout) + (int64_t)h * DV, tok0, nv, vs, c0);
         __syncthreads();
-        for (int idx = tid; idx < 64 * kBw3; idx += 256) {  // K S, K dS_next
+        for (int idx = tid; idx < 64 * kBw3; idx += NT) {  // K S, K dS_next
             const int i = idx / kBw3, j = idx % kBw3;
             float a = 0.f, e = 0.f;
             for (int d = 0; d < DK; ++d) {
@@ -319,19 +324,19 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdParams p) {
         }
         {   // gamma_C <S, dS_next> over this block
             float s = 0.f;
-            for (int idx = tid; idx < DK * kBw3; idx += 256) s += sS[idx / kBw3][idx % kBw3] * sdS[idx / kBw3][idx % kBw3];
+            for (int idx = tid; idx < DK * kBw3; idx += NT) s += sS[idx / kBw3][idx % kBw3] * sdS[idx / kBw3][idx % kBw3];
             for (int off = 1; off < 64; off <<= 1) s += __shfl_xor(s, off, 64);
             if (lane == 0) atomicAdd(&sdglC, gC * s);
         }
         __syncthreads();
-        for (int idx = tid; idx < 64 * kBw3; idx += 256) {  // V' = A X
+        for (int idx = tid; idx < 64 * kBw3; idx += NT) {  // V' = A X
             const int i = idx / kBw3, j = idx % kBw3;
             float s = 0.f;
             for (int t = 0; t <= i; ++t) s += sA[i][t] * sX[t][j];
             sVp[i][j] = s;
         }
         __syncthreads();
-        for (int idx = tid; idx < 64 * kBw3; idx += 256) {  // dV' = D K dS_next + scale Pt^T dO
+        for (int idx = tid; idx < 64 * kBw3; idx += NT) {  // dV' = D K dS_next + scale Pt^T dO
             const int i = idx / kBw3, j = idx % kBw3;
             float s = __expf(glC - sgl[i]) * sKdS[i][j];
             float u = 0.f;
@@ -347,7 +352,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdParams p) {
             sc[i] += Di * cd;
         }
         __syncthreads();
-        for (int idx = tid; idx < 64 * kBw3; idx += 256) {  // dX = A^T dV'
+        for (int idx = tid; idx < 64 * kBw3; idx += NT) {  // dX = A^T dV'
             const int i = idx / kBw3, j = idx % kBw3;
             float s = 0.f;
             for (int t = i; t < 64; ++t) s += sA[t][i] * sdVp[t][j];
@@ -365,11 +370,11 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdParams p) {
             sdb[i] += db;
             sdgl[i] -= sb[i] * gi * dg;
         }
-        for (int idx = tid; idx < 64 * kBw3; idx += 256) {
+        for (int idx = tid; idx < 64 * kBw3; idx += NT) {
             const int i = idx / kBw3, j = idx % kBw3;
             if (i < nv) p.dv[(tok0 + i) * vs + (int64_t)h * DV + c0 + j] = sb[i] * sdX[i][j];
         }
-        for (int idx = tid; idx < 4096; idx += 256) {       // dA += dV' X^T, dPt += scale dO V'^T
+        for (int idx = tid; idx < 4096; idx += NT) {       // dA += dV' X^T, dPt += scale dO V'^T
             const int i = idx / 64, t = idx % 64;
             float a = 0.f, b = 0.f;
             for (int j = 0; j < kBw3; ++j) {
@@ -405,14 +410,14 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdParams p) {
     }
     __syncthreads();
     // dL = -A^T dA A^T (strictly lower), via T = A^T dA in the block space
-    for (int idx = tid; idx < 4096; idx += 256) {
+    for (int idx = tid; idx < 4096; idx += NT) {
         const int i = idx / 64, j = idx % 64;
         float s = 0.f;
         for (int t = i; t < 64; ++t) s += sA[t][i] * sdA[t][j];
         sT[i][j] = s;
     }
     __syncthreads();
-    for (int idx = tid; idx < 4096; idx += 256) {
+    for (int idx = tid; idx < 4096; idx += NT) {
         const int i = idx / 64, j = idx % 64;
         float s = 0.f;
         if (j < i)
@@ -420,7 +425,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdParams p) {
         sdA[i][j] = j < i ? -s : 0.f;                        // sdA now holds dL
     }
     __syncthreads();
-    for (int idx = tid; idx < 4096; idx += 256) {           // G (gated K K^T, strictly lower) over T
+    for (int idx = tid; idx < 4096; idx += NT) {           // G (gated K K^T, strictly lower) over T
         const int i = idx / 64, j = idx % 64;
         float s = 0.f;
         if (j < i)
@@ -441,7 +446,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdParams p) {
         sdgl[i] += dg;
     }
     __syncthreads();
-    for (int idx = tid; idx < 4096; idx += 256) {           // M1 = dPt (.) Gam over dP, E over dL
+    for (int idx = tid; idx < 4096; idx += NT) {           // M1 = dPt (.) Gam over dP, E over dL
         const int i = idx / 64, j = idx % 64;
         const float f = __expf(sgl[i] - sgl[j]);
         sdP[i][j] = j <= i ? sdP[i][j] * f : 0.f;
@@ -1052,7 +1057,7 @@ hipError_t launch_bwd(int dtype, int D_k, const BwdParams &p, hipStream_t s) {
     GDN_BWD(bwd_states_kernel, T, DK, scans);               \
     if (chunks) GDN_BWD(bwd_p_kernel, T, DK, chunks);       \
     GDN_BWD(bwd_dstate_kernel, T, DK, rscans);              \
-    if (chunks) GDN_BWD(bwd_chunk_kernel, T, DK, chunks);
+    if (chunks) hipLaunchKernelGGL((bwd_chunk_kernel<T, DK>), dim3((unsigned)chunks), dim3(kBwT), 0, s, p);
     if (dtype == 1 && D_k == 128) { GDN_BWD_ALL(bf16, 128) }
     else if (dtype == 1 && D_k == 64) { GDN_BWD_ALL(bf16, 64) }
     else if (dtype == 0 && D_k == 128) { GDN_BWD_ALL(float, 128) }
