@@ -156,20 +156,22 @@ __global__ __launch_bounds__(256) void bwd_p_kernel(BwdParams p) {
     }
 }
 
-// ---- reverse scan of the state gradient: dS_next of every chunk, and dh0
+// ---- reverse scan of the state gradient: dS_next of every chunk, and dh0 (kBwT threads: two
+//      waves per SIMD hide the LDS latency of the products)
 template <typename T, int DK>
-__global__ __launch_bounds__(256) void bwd_dstate_kernel(BwdParams p) {
+__global__ __launch_bounds__(kBwT) void bwd_dstate_kernel(BwdParams p) {
+    constexpr int NT = kBwT;
     __shared__ float sK[64][DK + 1], sQ[64][DK + 1];
     __shared__ float sA[64][65], sP[64][65];
     __shared__ float sdS[DK][kBwD + 1], sdO[64][kBwD + 1], sKdS[64][kBwD + 1], sdVp[64][kBwD + 1], sdX[64][kBwD + 1];
-    __shared__ float sgl[64], sb[64];
+    __shared__ float sgl[64], sb[64], sfq[64], sfk[64], sD[64];
     const int tid = threadIdx.x;
     const int ncb = p.D_v / kBwD;
     const int cb = blockIdx.x % ncb, nh = blockIdx.x / ncb, h = nh % p.H_v, n = nh / p.H_v;
     const int hq = h / (p.H_v / p.H_qk);
     const SeqInfo si = seq_info(p.seq, n, p.T);
     const int64_t DV = p.D_v;
-    for (int idx = tid; idx < DK * kBwD; idx += 256) {
+    for (int idx = tid; idx < DK * kBwD; idx += NT) {
         const int d = idx / kBwD, j = idx % kBwD;
         sdS[d][j] = p.dht ? p.dht[(((int64_t)n * p.H_v + h) * DK + d) * DV + cb * kBwD + j] : 0.f;
     }
@@ -178,51 +180,55 @@ __global__ __launch_bounds__(256) void bwd_dstate_kernel(BwdParams p) {
         const int nv = min(kChunk, si.len - c * kChunk);
         __syncthreads();
         float *dsn = p.dsnext + ((gci * p.H_v + h) * DK) * DV + cb * kBwD;
-        for (int idx = tid; idx < DK * kBwD; idx += 256) dsn[(idx / kBwD) * DV + idx % kBwD] = sdS[idx / kBwD][idx % kBwD];
+        for (int idx = tid; idx < DK * kBwD; idx += NT) dsn[(idx / kBwD) * DV + idx % kBwD] = sdS[idx / kBwD][idx % kBwD];
         const int64_t qks = (int64_t)p.H_qk * DK;
-        load_rows<DK>(&sK[0][0], DK + 1, static_cast<const T *>(p.k) + (int64_t)hq * DK, tok0, nv, qks, 0);
-        load_rows<DK>(&sQ[0][0], DK + 1, static_cast<const T *>(p.q) + (int64_t)hq * DK, tok0, nv, qks, 0);
-        load_rows<kBwD>(&sdO[0][0], kBwD + 1, static_cast<const T *>(p.dout) + (int64_t)h * DV, tok0, nv, (int64_t)p.H_v * DV,
+        load_rows<DK, T, NT>(&sK[0][0], DK + 1, static_cast<const T *>(p.k) + (int64_t)hq * DK, tok0, nv, qks, 0);
+        load_rows<DK, T, NT>(&sQ[0][0], DK + 1, static_cast<const T *>(p.q) + (int64_t)hq * DK, tok0, nv, qks, 0);
+        load_rows<kBwD, T, NT>(&sdO[0][0], kBwD + 1, static_cast<const T *>(p.dout) + (int64_t)h * DV, tok0, nv, (int64_t)p.H_v * DV,
                      cb * kBwD);
-        load_tile64(sA, static_cast<const T *>(p.A) + (gci * p.H_v + h) * 4096);
-        load_tile64(sP, p.pmat + (gci * p.H_v + h) * 4096);  // scale Pt (lower with diagonal)
-        if (tid < 64) load_gates<T>(p, tok0, nv, h, sgl, sb);
+        load_tile64<T, NT>(sA, static_cast<const T *>(p.A) + (gci * p.H_v + h) * 4096);
+        load_tile64<float, NT>(sP, p.pmat + (gci * p.H_v + h) * 4096);  // scale Pt (lower with diagonal)
+        if (tid < 64) {
+            load_gates<T>(p, tok0, nv, h, sgl, sb);
+            // row factors: scale gamma_i (output), beta_i gamma_i (erase), D_i = gamma_C / gamma_i
+            const float gi = __expf(sgl[tid]);
+            sfq[tid] = p.scale * gi;
+            sfk[tid] = sb[tid] * gi;
+            sD[tid] = __expf(__shfl(sgl[tid], 63, 64) - sgl[tid]);
+        }
         __syncthreads();
-        for (int idx = tid; idx < 64 * kBwD; idx += 256) {   // K dS_next
+        for (int idx = tid; idx < 64 * kBwD; idx += NT) {   // K dS_next
             const int i = idx / kBwD, j = idx % kBwD;
             float s = 0.f;
             for (int d = 0; d < DK; ++d) s += sK[i][d] * sdS[d][j];
             sKdS[i][j] = s;
         }
         __syncthreads();
-        const float glC = sgl[63], gC = __expf(glC);
-        for (int idx = tid; idx < 64 * kBwD; idx += 256) {   // dV' = D K dS_next + scale Pt^T dO
+        const float gC = __expf(sgl[63]);
+        for (int idx = tid; idx < 64 * kBwD; idx += NT) {   // dV' = D K dS_next + scale Pt^T dO
             const int i = idx / kBwD, j = idx % kBwD;
-            float s = __expf(glC - sgl[i]) * sKdS[i][j];
+            float s = sD[i] * sKdS[i][j];
             for (int t = i; t < 64; ++t) s += sP[t][i] * sdO[t][j];
             sdVp[i][j] = s;
         }
         __syncthreads();
-        for (int idx = tid; idx < 64 * kBwD; idx += 256) {   // dX = A^T dV'
+        for (int idx = tid; idx < 64 * kBwD; idx += NT) {   // dX = A^T dV'
             const int i = idx / kBwD, j = idx % kBwD;
             float s = 0.f;
             for (int t = i; t < 64; ++t) s += sA[t][i] * sdVp[t][j];
             sdX[i][j] = s;
         }
         __syncthreads();
-        for (int idx = tid; idx < DK * kBwD; idx += 256) {   // dS = gamma_C dS_next + Q^T(...) - K^T(...)
+        for (int idx = tid; idx < DK * kBwD; idx += NT) {   // dS = gamma_C dS_next + Q^T(...) - K^T(...)
             const int d = idx / kBwD, j = idx % kBwD;
             float s = 0.f;
-            for (int i = 0; i < 64; ++i) {
-                const float gi = __expf(sgl[i]);
-                s += p.scale * gi * sQ[i][d] * sdO[i][j] - sb[i] * gi * sK[i][d] * sdX[i][j];
-            }
+            for (int i = 0; i < 64; ++i) s += sfq[i] * sQ[i][d] * sdO[i][j] - sfk[i] * sK[i][d] * sdX[i][j];
             sdS[d][j] = gC * sdS[d][j] + s;
         }
     }
     __syncthreads();
     if (p.dh0) {
-        for (int idx = tid; idx < DK * kBwD; idx += 256) {
+        for (int idx = tid; idx < DK * kBwD; idx += NT) {
             const int d = idx / kBwD, j = idx % kBwD;
             p.dh0[(((int64_t)n * p.H_v + h) * DK + d) * DV + cb * kBwD + j] = sdS[d][j];
         }
@@ -1056,7 +1062,7 @@ hipError_t launch_bwd(int dtype, int D_k, const BwdParams &p, hipStream_t s) {
 #define GDN_BWD_ALL(T, DK)                                  \
     GDN_BWD(bwd_states_kernel, T, DK, scans);               \
     if (chunks) GDN_BWD(bwd_p_kernel, T, DK, chunks);       \
-    GDN_BWD(bwd_dstate_kernel, T, DK, rscans);              \
+    hipLaunchKernelGGL((bwd_dstate_kernel<T, DK>), dim3((unsigned)rscans), dim3(kBwT), 0, s, p); \
     if (chunks) hipLaunchKernelGGL((bwd_chunk_kernel<T, DK>), dim3((unsigned)chunks), dim3(kBwT), 0, s, p);
     if (dtype == 1 && D_k == 128) { GDN_BWD_ALL(bf16, 128) }
     else if (dtype == 1 && D_k == 64) { GDN_BWD_ALL(bf16, 64) }
