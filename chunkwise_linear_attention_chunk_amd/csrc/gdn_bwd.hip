@@ -48,7 +48,7 @@ __device__ __forceinline__ void load_gates(const BwdParams &p, int64_t tok0, int
 // past the end
 // (NT threads; the element loads of a thread are independent and issued together, rows past
 // the end are clamped to the last valid row and zeroed at the store)
-template <int COLS, typename T, int NT = 256>
+template <int COLS, typename T, int NT>
 __device__ __forceinline__ void load_rows(float *dst, int dst_ld, const T *x, int64_t tok0, int nv, int64_t ld,
                                           int c0) {
     constexpr int N = 64 * COLS / NT;
@@ -67,7 +67,7 @@ __device__ __forceinline__ void load_rows(float *dst, int dst_ld, const T *x, in
 }
 
 // a [64][64] tile of the input dtype (or fp32) into fp32 LDS rows of stride 65 (NT threads)
-template <typename T, int NT = 256>
+template <typename T, int NT>
 __device__ __forceinline__ void load_tile64(float (*dst)[65], const T *x) {
     constexpr int N = 4096 / NT;
     float v[N];
@@ -102,9 +102,9 @@ __global__ __launch_bounds__(256) void bwd_states_kernel(BwdParams p) {
         __syncthreads();   // the previous chunk is done with every tile
         float *st = p.states + ((gci * p.H_v + h) * DK) * DV + cb * kBw;
         for (int idx = tid; idx < DK * kBw; idx += 256) st[(idx / kBw) * DV + idx % kBw] = sS[idx / kBw][idx % kBw];
-        load_rows<DK>(&sK[0][0], DK + 1, static_cast<const T *>(p.k) + (int64_t)hq * DK, tok0, nv, (int64_t)p.H_qk * DK, 0);
-        load_rows<kBw>(&sV[0][0], kBw + 1, static_cast<const T *>(p.v) + (int64_t)h * DV, tok0, nv, (int64_t)p.H_v * DV, cb * kBw);
-        load_tile64(sA, static_cast<const T *>(p.A) + (gci * p.H_v + h) * 4096);
+        load_rows<DK, T, 256>(&sK[0][0], DK + 1, static_cast<const T *>(p.k) + (int64_t)hq * DK, tok0, nv, (int64_t)p.H_qk * DK, 0);
+        load_rows<kBw, T, 256>(&sV[0][0], kBw + 1, static_cast<const T *>(p.v) + (int64_t)h * DV, tok0, nv, (int64_t)p.H_v * DV, cb * kBw);
+        load_tile64<T, 256>(sA, static_cast<const T *>(p.A) + (gci * p.H_v + h) * 4096);
         if (tid < 64) load_gates<T>(p, tok0, nv, h, sgl, sb);
         __syncthreads();
         for (int idx = tid; idx < 64 * kBw; idx += 256) {   // X = beta (V - gamma K S)
@@ -142,8 +142,8 @@ __global__ __launch_bounds__(256) void bwd_p_kernel(BwdParams p) {
     const int hq = h / (p.H_v / p.H_qk);
     const ChunkInfo cinfo = chunk_info(p.chunks, ci, p.T);
     const int64_t qks = (int64_t)p.H_qk * DK;
-    load_rows<DK>(&sK[0][0], DK + 1, static_cast<const T *>(p.k) + (int64_t)hq * DK, cinfo.tok0, cinfo.nv, qks, 0);
-    load_rows<DK>(&sQ[0][0], DK + 1, static_cast<const T *>(p.q) + (int64_t)hq * DK, cinfo.tok0, cinfo.nv, qks, 0);
+    load_rows<DK, T, 256>(&sK[0][0], DK + 1, static_cast<const T *>(p.k) + (int64_t)hq * DK, cinfo.tok0, cinfo.nv, qks, 0);
+    load_rows<DK, T, 256>(&sQ[0][0], DK + 1, static_cast<const T *>(p.q) + (int64_t)hq * DK, cinfo.tok0, cinfo.nv, qks, 0);
     if (tid < 64) load_gates<T>(p, cinfo.tok0, cinfo.nv, h, sgl, sb);
     __syncthreads();
     float *P = p.pmat + ((int64_t)ci * p.H_v + h) * 4096;
@@ -557,10 +557,10 @@ __global__ __launch_bounds__(256) void bwd_states_kda_kernel(BwdParams p) {
         __syncthreads();
         float *st = p.states + ((gci * p.H_v + h) * DK) * DV + cb * kBw;
         for (int idx = tid; idx < DK * kBw; idx += 256) st[(idx / kBw) * DV + idx % kBw] = sS[idx / kBw][idx % kBw];
-        load_rows<DK>(&sKg[0][0], DK + 1, static_cast<const T *>(p.k) + (int64_t)hq * DK, tok0, nv, (int64_t)p.H_qk * DK, 0);
-        load_rows<DK>(&sKd[0][0], DK + 1, static_cast<const T *>(p.g) + (int64_t)h * DK, tok0, nv, gks, 0);
-        load_rows<kBw>(&sV[0][0], kBw + 1, static_cast<const T *>(p.v) + (int64_t)h * DV, tok0, nv, (int64_t)p.H_v * DV, cb * kBw);
-        load_tile64(sA, static_cast<const T *>(p.A) + (gci * p.H_v + h) * 4096);
+        load_rows<DK, T, 256>(&sKg[0][0], DK + 1, static_cast<const T *>(p.k) + (int64_t)hq * DK, tok0, nv, (int64_t)p.H_qk * DK, 0);
+        load_rows<DK, T, 256>(&sKd[0][0], DK + 1, static_cast<const T *>(p.g) + (int64_t)h * DK, tok0, nv, gks, 0);
+        load_rows<kBw, T, 256>(&sV[0][0], kBw + 1, static_cast<const T *>(p.v) + (int64_t)h * DV, tok0, nv, (int64_t)p.H_v * DV, cb * kBw);
+        load_tile64<T, 256>(sA, static_cast<const T *>(p.A) + (gci * p.H_v + h) * 4096);
         if (tid < 64) load_beta<T>(p, tok0, nv, h, sb);
         cumsum_rows<DK>(&sKd[0][0], DK + 1);                 // sKd holds G
         if (tid < DK) sgc[tid] = sKd[63][tid];
@@ -604,9 +604,9 @@ __global__ __launch_bounds__(256) void bwd_p_kda_kernel(BwdParams p) {
     const int hq = h / (p.H_v / p.H_qk);
     const ChunkInfo cinfo = chunk_info(p.chunks, ci, p.T);
     const int64_t qks = (int64_t)p.H_qk * DK;
-    load_rows<DK>(&sK[0][0], DK + 1, static_cast<const T *>(p.k) + (int64_t)hq * DK, cinfo.tok0, cinfo.nv, qks, 0);
-    load_rows<DK>(&sQ[0][0], DK + 1, static_cast<const T *>(p.q) + (int64_t)hq * DK, cinfo.tok0, cinfo.nv, qks, 0);
-    load_rows<DK>(&sG[0][0], DK + 1, static_cast<const T *>(p.g) + (int64_t)h * DK, cinfo.tok0, cinfo.nv,
+    load_rows<DK, T, 256>(&sK[0][0], DK + 1, static_cast<const T *>(p.k) + (int64_t)hq * DK, cinfo.tok0, cinfo.nv, qks, 0);
+    load_rows<DK, T, 256>(&sQ[0][0], DK + 1, static_cast<const T *>(p.q) + (int64_t)hq * DK, cinfo.tok0, cinfo.nv, qks, 0);
+    load_rows<DK, T, 256>(&sG[0][0], DK + 1, static_cast<const T *>(p.g) + (int64_t)h * DK, cinfo.tok0, cinfo.nv,
                   (int64_t)p.H_v * DK, 0);
     cumsum_rows<DK>(&sG[0][0], DK + 1);
     float *P = p.pmat + ((int64_t)ci * p.H_v + h) * 4096;
@@ -619,9 +619,10 @@ __global__ __launch_bounds__(256) void bwd_p_kda_kernel(BwdParams p) {
     }
 }
 
-// ---- reverse scan of the state gradient (per-channel gates)
+// ---- reverse scan of the state gradient (per-channel gates; kBwT threads)
 template <typename T, int DK>
-__global__ __launch_bounds__(256) void bwd_dstate_kda_kernel(BwdParams p) {
+__global__ __launch_bounds__(kBwT) void bwd_dstate_kda_kernel(BwdParams p) {
+    constexpr int NT = kBwT;
     __shared__ float sKd[64][DK + 1], sKg[64][DK + 1], sQg[64][DK + 1];
     __shared__ float sA[64][65], sP[64][65];
     __shared__ float sdS[DK][kBw + 1], sdO[64][kBw + 1], sKdS[64][kBw + 1], sdVp[64][kBw + 1], sdX[64][kBw + 1];
@@ -632,7 +633,7 @@ __global__ __launch_bounds__(256) void bwd_dstate_kda_kernel(BwdParams p) {
     const int hq = h / (p.H_v / p.H_qk);
     const SeqInfo si = seq_info(p.seq, n, p.T);
     const int64_t DV = p.D_v;
-    for (int idx = tid; idx < DK * kBw; idx += 256) {
+    for (int idx = tid; idx < DK * kBw; idx += NT) {
         const int d = idx / kBw, j = idx % kBw;
         sdS[d][j] = p.dht ? p.dht[(((int64_t)n * p.H_v + h) * DK + d) * DV + cb * kBw + j] : 0.f;
     }
@@ -641,20 +642,20 @@ __global__ __launch_bounds__(256) void bwd_dstate_kda_kernel(BwdParams p) {
         const int nv = min(kChunk, si.len - c * kChunk);
         __syncthreads();
         float *dsn = p.dsnext + ((gci * p.H_v + h) * DK) * DV + cb * kBw;
-        for (int idx = tid; idx < DK * kBw; idx += 256) dsn[(idx / kBw) * DV + idx % kBw] = sdS[idx / kBw][idx % kBw];
+        for (int idx = tid; idx < DK * kBw; idx += NT) dsn[(idx / kBw) * DV + idx % kBw] = sdS[idx / kBw][idx % kBw];
         const int64_t qks = (int64_t)p.H_qk * DK;
-        load_rows<DK>(&sKg[0][0], DK + 1, static_cast<const T *>(p.k) + (int64_t)hq * DK, tok0, nv, qks, 0);
-        load_rows<DK>(&sQg[0][0], DK + 1, static_cast<const T *>(p.q) + (int64_t)hq * DK, tok0, nv, qks, 0);
-        load_rows<DK>(&sKd[0][0], DK + 1, static_cast<const T *>(p.g) + (int64_t)h * DK, tok0, nv, (int64_t)p.H_v * DK, 0);
-        load_rows<kBw>(&sdO[0][0], kBw + 1, static_cast<const T *>(p.dout) + (int64_t)h * DV, tok0, nv, (int64_t)p.H_v * DV,
+        load_rows<DK, T, NT>(&sKg[0][0], DK + 1, static_cast<const T *>(p.k) + (int64_t)hq * DK, tok0, nv, qks, 0);
+        load_rows<DK, T, NT>(&sQg[0][0], DK + 1, static_cast<const T *>(p.q) + (int64_t)hq * DK, tok0, nv, qks, 0);
+        load_rows<DK, T, NT>(&sKd[0][0], DK + 1, static_cast<const T *>(p.g) + (int64_t)h * DK, tok0, nv, (int64_t)p.H_v * DK, 0);
+        load_rows<kBw, T, NT>(&sdO[0][0], kBw + 1, static_cast<const T *>(p.dout) + (int64_t)h * DV, tok0, nv, (int64_t)p.H_v * DV,
                        cb * kBw);
-        load_tile64(sA, static_cast<const T *>(p.A) + (gci * p.H_v + h) * 4096);
-        load_tile64(sP, p.pmat + (gci * p.H_v + h) * 4096);
+        load_tile64<T, NT>(sA, static_cast<const T *>(p.A) + (gci * p.H_v + h) * 4096);
+        load_tile64<float, NT>(sP, p.pmat + (gci * p.H_v + h) * 4096);
         if (tid < 64) load_beta<T>(p, tok0, nv, h, sb);
         cumsum_rows<DK>(&sKd[0][0], DK + 1);                 // sKd holds G
         if (tid < DK) sgc[tid] = sKd[63][tid];
         __syncthreads();
-        for (int idx = tid; idx < 64 * DK; idx += 256) {    // Kd, Kg, Qg
+        for (int idx = tid; idx < 64 * DK; idx += NT) {    // Kd, Kg, Qg
             const int i = idx / DK, d = idx % DK;
             const float G = sKd[i][d], e = __expf(G), k = sKg[i][d];
             sKd[i][d] = k * __expf(sgc[d] - G);
@@ -662,28 +663,28 @@ __global__ __launch_bounds__(256) void bwd_dstate_kda_kernel(BwdParams p) {
             sQg[i][d] *= e;
         }
         __syncthreads();
-        for (int idx = tid; idx < 64 * kBw; idx += 256) {   // Kd dS_next
+        for (int idx = tid; idx < 64 * kBw; idx += NT) {   // Kd dS_next
             const int i = idx / kBw, j = idx % kBw;
             float s = 0.f;
             for (int d = 0; d < DK; ++d) s += sKd[i][d] * sdS[d][j];
             sKdS[i][j] = s;
         }
         __syncthreads();
-        for (int idx = tid; idx < 64 * kBw; idx += 256) {   // dV' = Kd dS_next + scale P^T dO
+        for (int idx = tid; idx < 64 * kBw; idx += NT) {   // dV' = Kd dS_next + scale P^T dO
             const int i = idx / kBw, j = idx % kBw;
             float s = sKdS[i][j];
             for (int t = i; t < 64; ++t) s += sP[t][i] * sdO[t][j];
             sdVp[i][j] = s;
         }
         __syncthreads();
-        for (int idx = tid; idx < 64 * kBw; idx += 256) {   // dX = A^T dV'
+        for (int idx = tid; idx < 64 * kBw; idx += NT) {   // dX = A^T dV'
             const int i = idx / kBw, j = idx % kBw;
             float s = 0.f;
             for (int t = i; t < 64; ++t) s += sA[t][i] * sdVp[t][j];
             sdX[i][j] = s;
         }
         __syncthreads();
-        for (int idx = tid; idx < DK * kBw; idx += 256) {   // dS = Diag(e^{G_C}) dS_next + Qg^T(...) - Kg^T(...)
+        for (int idx = tid; idx < DK * kBw; idx += NT) {   // dS = Diag(e^{G_C}) dS_next + Qg^T(...) - Kg^T(...)
             const int d = idx / kBw, j = idx % kBw;
             float s = 0.f;
             for (int i = 0; i < 64; ++i) s += p.scale * sQg[i][d] * sdO[i][j] - sb[i] * sKg[i][d] * sdX[i][j];
@@ -692,7 +693,7 @@ __global__ __launch_bounds__(256) void bwd_dstate_kda_kernel(BwdParams p) {
     }
     __syncthreads();
     if (p.dh0) {
-        for (int idx = tid; idx < DK * kBw; idx += 256) {
+        for (int idx = tid; idx < DK * kBw; idx += NT) {
             const int d = idx / kBw, j = idx % kBw;
             p.dh0[(((int64_t)n * p.H_v + h) * DK + d) * DV + cb * kBw + j] = sdS[d][j];
         }
@@ -700,9 +701,9 @@ __global__ __launch_bounds__(256) void bwd_dstate_kda_kernel(BwdParams p) {
 }
 
 // the thread's G values down its column: rows e * RS + tid / DK of the chunk (G_C in *gc)
-template <typename T, int DK, int EPT>
+template <typename T, int DK, int EPT, int NT>
 __device__ __forceinline__ void column_cumsum(const BwdParams &p, int64_t tok0, int nv, int h, float *Gr, float *gc) {
-    constexpr int RS = 256 / DK;
+    constexpr int RS = NT / DK;
     const int col = threadIdx.x % DK, r0 = threadIdx.x / DK;
     const T *g = static_cast<const T *>(p.g) + (int64_t)h * DK + col;
     float acc = 0.f;
@@ -716,9 +717,10 @@ __device__ __forceinline__ void column_cumsum(const BwdParams &p, int64_t tok0, 
 
 // ---- (a) per (chunk, value head): the products with S and dS_next, dV, dbeta from X, dL
 template <typename T, int DK>
-__global__ __launch_bounds__(256) void bwd_chunk_kda_a_kernel(BwdParams p) {
-    constexpr int EPT = 64 * DK / 256;
-    constexpr int RS = 256 / DK;
+__global__ __launch_bounds__(kBwT) void bwd_chunk_kda_a_kernel(BwdParams p) {
+    constexpr int NT = kBwT;
+    constexpr int EPT = 64 * DK / NT;
+    constexpr int RS = NT / DK;
     constexpr int W3 = kBw3 + 1;
     __shared__ float sKg[64][DK + 1], sKd[64][DK + 1];
     __shared__ float sA[64][65], sP[64][65], sdA[64][65];
@@ -737,18 +739,18 @@ __global__ __launch_bounds__(256) void bwd_chunk_kda_a_kernel(BwdParams p) {
     float (*sdX)[W3] = sV + 7 * 64;
     float (*sT)[65] = reinterpret_cast<float (*)[65]>(sBlk);
 
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x;
     const int ci = blockIdx.x / p.H_v, h = blockIdx.x - ci * p.H_v;
     const int hq = h / (p.H_v / p.H_qk);
     const ChunkInfo cinfo = chunk_info(p.chunks, ci, p.T);
     const int64_t tok0 = cinfo.tok0;
     const int nv = cinfo.nv;
     const int64_t DV = p.D_v, qks = (int64_t)p.H_qk * DK, vs = (int64_t)p.H_v * DV;
-    load_rows<DK>(&sKg[0][0], DK + 1, static_cast<const T *>(p.k) + (int64_t)hq * DK, tok0, nv, qks, 0);
-    load_rows<DK>(&sKd[0][0], DK + 1, static_cast<const T *>(p.g) + (int64_t)h * DK, tok0, nv, (int64_t)p.H_v * DK, 0);
-    load_tile64(sA, static_cast<const T *>(p.A) + ((int64_t)ci * p.H_v + h) * 4096);
-    load_tile64(sP, p.pmat + ((int64_t)ci * p.H_v + h) * 4096);
-    for (int idx = tid; idx < 4096; idx += 256) sdA[idx / 64][idx % 64] = 0.f;
+    load_rows<DK, T, NT>(&sKg[0][0], DK + 1, static_cast<const T *>(p.k) + (int64_t)hq * DK, tok0, nv, qks, 0);
+    load_rows<DK, T, NT>(&sKd[0][0], DK + 1, static_cast<const T *>(p.g) + (int64_t)h * DK, tok0, nv, (int64_t)p.H_v * DK, 0);
+    load_tile64<T, NT>(sA, static_cast<const T *>(p.A) + ((int64_t)ci * p.H_v + h) * 4096);
+    load_tile64<float, NT>(sP, p.pmat + ((int64_t)ci * p.H_v + h) * 4096);
+    for (int idx = tid; idx < 4096; idx += NT) sdA[idx / 64][idx % 64] = 0.f;
     if (tid < 64) {
         load_beta<T>(p, tok0, nv, h, sb);
         sdb[tid] = 0.f;
@@ -759,7 +761,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kda_a_kernel(BwdParams p) {
         sdgc[tid] = 0.f;
     }
     __syncthreads();
-    for (int idx = tid; idx < 64 * DK; idx += 256) {
+    for (int idx = tid; idx < 64 * DK; idx += NT) {
         const int i = idx / DK, d = idx % DK;
         const float G = sKd[i][d], k = sKg[i][d];
         sKd[i][d] = k * __expf(sgc[d] - G);
@@ -775,25 +777,25 @@ __global__ __launch_bounds__(256) void bwd_chunk_kda_a_kernel(BwdParams p) {
     for (int c0 = 0; c0 < p.D_v; c0 += kBw3) {
         __syncthreads();
         {
-            constexpr int NE = DK * kBw3 / 256;
+            constexpr int NE = DK * kBw3 / NT;
             float a[NE], b[NE];
 #pragma unroll
             for (int it = 0; it < NE; ++it) {
-                const int idx = tid + 256 * it, d = idx / kBw3, j = idx % kBw3;
+                const int idx = tid + NT * it, d = idx / kBw3, j = idx % kBw3;
                 a[it] = St[d * DV + c0 + j];
                 b[it] = dSt[d * DV + c0 + j];
             }
 #pragma unroll
             for (int it = 0; it < NE; ++it) {
-                const int idx = tid + 256 * it, d = idx / kBw3, j = idx % kBw3;
+                const int idx = tid + NT * it, d = idx / kBw3, j = idx % kBw3;
                 sS[d][j] = a[it];
                 sdS[d][j] = b[it];
             }
         }
-        load_rows<kBw3>(&sV[0][0], W3, static_cast<const T *>(p.v) + (int64_t)h * DV, tok0, nv, vs, c0);
-        load_rows<kBw3>(&sdO[0][0], W3, static_cast<const T *>(p.dout) + (int64_t)h * DV, tok0, nv, vs, c0);
+        load_rows<kBw3, T, NT>(&sV[0][0], W3, static_cast<const T *>(p.v) + (int64_t)h * DV, tok0, nv, vs, c0);
+        load_rows<kBw3, T, NT>(&sdO[0][0], W3, static_cast<const T *>(p.dout) + (int64_t)h * DV, tok0, nv, vs, c0);
         __syncthreads();
-        for (int idx = tid; idx < 64 * kBw3; idx += 256) {  // Kg S, Kd dS_next, X
+        for (int idx = tid; idx < 64 * kBw3; idx += NT) {  // Kg S, Kd dS_next, X
             const int i = idx / kBw3, j = idx % kBw3;
             float a = 0.f, e = 0.f;
             for (int d = 0; d < DK; ++d) {
@@ -810,7 +812,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kda_a_kernel(BwdParams p) {
             sdgc[tid] += __expf(sgc[tid]) * s;
         }
         __syncthreads();
-        for (int idx = tid; idx < 64 * kBw3; idx += 256) {  // V' = A X
+        for (int idx = tid; idx < 64 * kBw3; idx += NT) {  // V' = A X
             const int i = idx / kBw3, j = idx % kBw3;
             float s = 0.f;
             for (int t = 0; t <= i; ++t) s += sA[i][t] * sX[t][j];
@@ -818,14 +820,14 @@ __global__ __launch_bounds__(256) void bwd_chunk_kda_a_kernel(BwdParams p) {
             vpw[i * DV + c0 + j] = s;
         }
         __syncthreads();
-        for (int idx = tid; idx < 64 * kBw3; idx += 256) {  // dV' = Kd dS_next + scale P^T dO
+        for (int idx = tid; idx < 64 * kBw3; idx += NT) {  // dV' = Kd dS_next + scale P^T dO
             const int i = idx / kBw3, j = idx % kBw3;
             float s = sKdS[i][j];
             for (int t = i; t < 64; ++t) s += sP[t][i] * sdO[t][j];
             sdVp[i][j] = s;
         }
         __syncthreads();
-        for (int idx = tid; idx < 64 * kBw3; idx += 256) {  // dX = A^T dV'
+        for (int idx = tid; idx < 64 * kBw3; idx += NT) {  // dX = A^T dV'
             const int i = idx / kBw3, j = idx % kBw3;
             float s = 0.f;
             for (int t = i; t < 64; ++t) s += sA[t][i] * sdVp[t][j];
@@ -837,11 +839,11 @@ __global__ __launch_bounds__(256) void bwd_chunk_kda_a_kernel(BwdParams p) {
             for (int j = 0; j < kBw3; ++j) db += sdX[tid][j] * (sV[tid][j] - sKS[tid][j]);
             sdb[tid] += db;
         }
-        for (int idx = tid; idx < 64 * kBw3; idx += 256) {
+        for (int idx = tid; idx < 64 * kBw3; idx += NT) {
             const int i = idx / kBw3, j = idx % kBw3;
             if (i < nv) p.dv[(tok0 + i) * vs + (int64_t)h * DV + c0 + j] = sb[i] * sdX[i][j];
         }
-        for (int idx = tid; idx < 4096; idx += 256) {       // dA += dV' X^T
+        for (int idx = tid; idx < 4096; idx += NT) {       // dA += dV' X^T
             const int i = idx / 64, t = idx % 64;
             float a = 0.f;
             for (int j = 0; j < kBw3; ++j) a += sdVp[i][j] * sX[t][j];
@@ -863,7 +865,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kda_a_kernel(BwdParams p) {
     }
     __syncthreads();
     // dL = -A^T dA A^T (strictly lower), to the workspace
-    for (int idx = tid; idx < 4096; idx += 256) {
+    for (int idx = tid; idx < 4096; idx += NT) {
         const int i = idx / 64, j = idx % 64;
         float s = 0.f;
         for (int t = i; t < 64; ++t) s += sA[t][i] * sdA[t][j];
@@ -871,7 +873,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kda_a_kernel(BwdParams p) {
     }
     __syncthreads();
     float *dLw = p.dlmat + ((int64_t)ci * p.H_v + h) * 4096;
-    for (int idx = tid; idx < 4096; idx += 256) {
+    for (int idx = tid; idx < 4096; idx += NT) {
         const int i = idx / 64, j = idx % 64;
         float s = 0.f;
         if (j < i)
@@ -880,7 +882,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kda_a_kernel(BwdParams p) {
     }
     // the gate factors of this thread's elements, then dq, dk and dG of these terms
     float Gr[EPT], gC;
-    column_cumsum<T, DK, EPT>(p, tok0, nv, h, Gr, &gC);
+    column_cumsum<T, DK, EPT, NT>(p, tok0, nv, h, Gr, &gC);
     const T *q = static_cast<const T *>(p.q) + (int64_t)hq * DK + col;
     const T *k = static_cast<const T *>(p.k) + (int64_t)hq * DK + col;
     float dgcs = 0.f;
@@ -918,9 +920,10 @@ __global__ __launch_bounds__(256) void bwd_chunk_kda_a_kernel(BwdParams p) {
 // ---- (b) per (chunk, value head): the P and L terms with their per-channel factors, then the
 //      per-channel reverse cumsum of dG
 template <typename T, int DK>
-__global__ __launch_bounds__(256) void bwd_chunk_kda_b_kernel(BwdParams p) {
-    constexpr int EPT = 64 * DK / 256;
-    constexpr int RS = 256 / DK;
+__global__ __launch_bounds__(kBwT) void bwd_chunk_kda_b_kernel(BwdParams p) {
+    constexpr int NT = kBwT;
+    constexpr int EPT = 64 * DK / NT;
+    constexpr int RS = NT / DK;
     constexpr int W3 = kBw3 + 1;
     __shared__ float sK[64][DK + 1], sQ[64][DK + 1], sG[64][DK + 1];
     __shared__ float sdL[64][65], sdP[64][65];
@@ -933,11 +936,11 @@ __global__ __launch_bounds__(256) void bwd_chunk_kda_b_kernel(BwdParams p) {
     const int64_t tok0 = cinfo.tok0;
     const int nv = cinfo.nv;
     const int64_t DV = p.D_v, qks = (int64_t)p.H_qk * DK, vs = (int64_t)p.H_v * DV;
-    load_rows<DK>(&sK[0][0], DK + 1, static_cast<const T *>(p.k) + (int64_t)hq * DK, tok0, nv, qks, 0);
-    load_rows<DK>(&sQ[0][0], DK + 1, static_cast<const T *>(p.q) + (int64_t)hq * DK, tok0, nv, qks, 0);
-    load_rows<DK>(&sG[0][0], DK + 1, static_cast<const T *>(p.g) + (int64_t)h * DK, tok0, nv, (int64_t)p.H_v * DK, 0);
-    load_tile64(sdL, p.dlmat + ((int64_t)ci * p.H_v + h) * 4096);
-    for (int idx = tid; idx < 4096; idx += 256) sdP[idx / 64][idx % 64] = 0.f;
+    load_rows<DK, T, NT>(&sK[0][0], DK + 1, static_cast<const T *>(p.k) + (int64_t)hq * DK, tok0, nv, qks, 0);
+    load_rows<DK, T, NT>(&sQ[0][0], DK + 1, static_cast<const T *>(p.q) + (int64_t)hq * DK, tok0, nv, qks, 0);
+    load_rows<DK, T, NT>(&sG[0][0], DK + 1, static_cast<const T *>(p.g) + (int64_t)h * DK, tok0, nv, (int64_t)p.H_v * DK, 0);
+    load_tile64<float, NT>(sdL, p.dlmat + ((int64_t)ci * p.H_v + h) * 4096);
+    for (int idx = tid; idx < 4096; idx += NT) sdP[idx / 64][idx % 64] = 0.f;
     if (tid < 64) {
         load_beta<T>(p, tok0, nv, h, sb);
         sdb[tid] = 0.f;
@@ -947,10 +950,10 @@ __global__ __launch_bounds__(256) void bwd_chunk_kda_b_kernel(BwdParams p) {
     const float *vpw = p.vp + ((int64_t)ci * p.H_v + h) * 64 * DV;
     for (int c0 = 0; c0 < p.D_v; c0 += kBw3) {
         __syncthreads();
-        load_rows<kBw3>(&sdO[0][0], W3, static_cast<const T *>(p.dout) + (int64_t)h * DV, tok0, nv, vs, c0);
-        for (int idx = tid; idx < 64 * kBw3; idx += 256) sVp[idx / kBw3][idx % kBw3] = vpw[(idx / kBw3) * DV + c0 + idx % kBw3];
+        load_rows<kBw3, T, NT>(&sdO[0][0], W3, static_cast<const T *>(p.dout) + (int64_t)h * DV, tok0, nv, vs, c0);
+        for (int idx = tid; idx < 64 * kBw3; idx += NT) sVp[idx / kBw3][idx % kBw3] = vpw[(idx / kBw3) * DV + c0 + idx % kBw3];
         __syncthreads();
-        for (int idx = tid; idx < 4096; idx += 256) {
+        for (int idx = tid; idx < 4096; idx += NT) {
             const int i = idx / 64, t = idx % 64;
             float a = 0.f;
             for (int j = 0; j < kBw3; ++j) a += sdO[i][j] * sVp[t][j];
@@ -1037,10 +1040,10 @@ hipError_t launch_bwd(int dtype, int D_k, const BwdParams &p, hipStream_t s) {
 #define GDN_BWDK_ALL(T, DK)                                  \
     GDN_BWDK(bwd_states_kda_kernel, T, DK, scans);           \
     if (chunks) GDN_BWDK(bwd_p_kda_kernel, T, DK, chunks);   \
-    GDN_BWDK(bwd_dstate_kda_kernel, T, DK, scans);           \
+    hipLaunchKernelGGL((bwd_dstate_kda_kernel<T, DK>), dim3((unsigned)scans), dim3(kBwT), 0, s, p); \
     if (chunks) {                                            \
-        GDN_BWDK(bwd_chunk_kda_a_kernel, T, DK, chunks);     \
-        GDN_BWDK(bwd_chunk_kda_b_kernel, T, DK, chunks);     \
+        hipLaunchKernelGGL((bwd_chunk_kda_a_kernel<T, DK>), dim3((unsigned)chunks), dim3(kBwT), 0, s, p); \
+        hipLaunchKernelGGL((bwd_chunk_kda_b_kernel<T, DK>), dim3((unsigned)chunks), dim3(kBwT), 0, s, p); \
     }
         if (dtype == 1 && D_k == 128) { GDN_BWDK_ALL(bf16, 128) }
         else if (dtype == 1 && D_k == 64) { GDN_BWDK_ALL(bf16, 64) }
