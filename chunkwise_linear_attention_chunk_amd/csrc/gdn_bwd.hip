@@ -82,17 +82,18 @@ __device__ __forceinline__ void load_tile64(float (*dst)[65], const T *x) {
 
 // ---- recomputed chunk states: S entering every chunk, per (sequence, value head, kBw columns)
 template <typename T, int DK>
-__global__ __launch_bounds__(256) void bwd_states_kernel(BwdParams p) {
+__global__ __launch_bounds__(kBwT) void bwd_states_kernel(BwdParams p) {
+    constexpr int NT = kBwT;
     // odd row strides (+1) keep the column walks of these tiles free of LDS bank conflicts
     __shared__ float sK[64][DK + 1], sA[64][65], sS[DK][kBw + 1], sV[64][kBw + 1], sX[64][kBw + 1], sVp[64][kBw + 1];
-    __shared__ float sgl[64], sb[64];
+    __shared__ float sgl[64], sb[64], sD[64];
     const int tid = threadIdx.x;
     const int ncb = p.D_v / kBw;
     const int cb = blockIdx.x % ncb, nh = blockIdx.x / ncb, h = nh % p.H_v, n = nh / p.H_v;
     const int hq = h / (p.H_v / p.H_qk);
     const SeqInfo si = seq_info(p.seq, n, p.T);
     const int64_t DV = p.D_v;
-    for (int idx = tid; idx < DK * kBw; idx += 256) {
+    for (int idx = tid; idx < DK * kBw; idx += NT) {
         const int d = idx / kBw, j = idx % kBw;
         sS[d][j] = p.h0 ? p.h0[(((int64_t)n * p.H_v + h) * DK + d) * DV + cb * kBw + j] : 0.f;
     }
@@ -101,31 +102,34 @@ __global__ __launch_bounds__(256) void bwd_states_kernel(BwdParams p) {
         const int nv = min(kChunk, si.len - c * kChunk);
         __syncthreads();   // the previous chunk is done with every tile
         float *st = p.states + ((gci * p.H_v + h) * DK) * DV + cb * kBw;
-        for (int idx = tid; idx < DK * kBw; idx += 256) st[(idx / kBw) * DV + idx % kBw] = sS[idx / kBw][idx % kBw];
-        load_rows<DK, T, 256>(&sK[0][0], DK + 1, static_cast<const T *>(p.k) + (int64_t)hq * DK, tok0, nv, (int64_t)p.H_qk * DK, 0);
-        load_rows<kBw, T, 256>(&sV[0][0], kBw + 1, static_cast<const T *>(p.v) + (int64_t)h * DV, tok0, nv, (int64_t)p.H_v * DV, cb * kBw);
-        load_tile64<T, 256>(sA, static_cast<const T *>(p.A) + (gci * p.H_v + h) * 4096);
-        if (tid < 64) load_gates<T>(p, tok0, nv, h, sgl, sb);
+        for (int idx = tid; idx < DK * kBw; idx += NT) st[(idx / kBw) * DV + idx % kBw] = sS[idx / kBw][idx % kBw];
+        load_rows<DK, T, NT>(&sK[0][0], DK + 1, static_cast<const T *>(p.k) + (int64_t)hq * DK, tok0, nv, (int64_t)p.H_qk * DK, 0);
+        load_rows<kBw, T, NT>(&sV[0][0], kBw + 1, static_cast<const T *>(p.v) + (int64_t)h * DV, tok0, nv, (int64_t)p.H_v * DV, cb * kBw);
+        load_tile64<T, NT>(sA, static_cast<const T *>(p.A) + (gci * p.H_v + h) * 4096);
+        if (tid < 64) {
+            load_gates<T>(p, tok0, nv, h, sgl, sb);
+            sD[tid] = __expf(__shfl(sgl[tid], 63, 64) - sgl[tid]);   // D_i = gamma_C / gamma_i
+        }
         __syncthreads();
-        for (int idx = tid; idx < 64 * kBw; idx += 256) {   // X = beta (V - gamma K S)
+        for (int idx = tid; idx < 64 * kBw; idx += NT) {   // X = beta (V - gamma K S)
             const int i = idx / kBw, j = idx % kBw;
             float s = 0.f;
             for (int d = 0; d < DK; ++d) s += sK[i][d] * sS[d][j];
             sX[i][j] = sb[i] * (sV[i][j] - __expf(sgl[i]) * s);
         }
         __syncthreads();
-        for (int idx = tid; idx < 64 * kBw; idx += 256) {   // V' = A X (A lower)
+        for (int idx = tid; idx < 64 * kBw; idx += NT) {   // V' = A X (A lower)
             const int i = idx / kBw, j = idx % kBw;
             float s = 0.f;
             for (int t = 0; t <= i; ++t) s += sA[i][t] * sX[t][j];
             sVp[i][j] = s;
         }
         __syncthreads();
-        const float glC = sgl[63], gC = __expf(glC);
-        for (int idx = tid; idx < DK * kBw; idx += 256) {   // S = gamma_C S + K^T diag(D) V'
+        const float gC = __expf(sgl[63]);
+        for (int idx = tid; idx < DK * kBw; idx += NT) {   // S = gamma_C S + K^T diag(D) V'
             const int d = idx / kBw, j = idx % kBw;
             float s = 0.f;
-            for (int i = 0; i < 64; ++i) s += sK[i][d] * __expf(glC - sgl[i]) * sVp[i][j];
+            for (int i = 0; i < 64; ++i) s += sK[i][d] * sD[i] * sVp[i][j];
             sS[d][j] = gC * sS[d][j] + s;
         }
     }
@@ -537,7 +541,8 @@ __device__ __forceinline__ void load_beta(const BwdParams &p, int64_t tok0, int 
 
 // ---- recomputed chunk states (per-channel gates)
 template <typename T, int DK>
-__global__ __launch_bounds__(256) void bwd_states_kda_kernel(BwdParams p) {
+__global__ __launch_bounds__(kBwT) void bwd_states_kda_kernel(BwdParams p) {
+    constexpr int NT = kBwT;
     __shared__ float sKg[64][DK + 1], sKd[64][DK + 1], sA[64][65];
     __shared__ float sS[DK][kBw + 1], sV[64][kBw + 1], sX[64][kBw + 1], sVp[64][kBw + 1];
     __shared__ float sb[64], sgc[DK];
@@ -547,7 +552,7 @@ __global__ __launch_bounds__(256) void bwd_states_kda_kernel(BwdParams p) {
     const int hq = h / (p.H_v / p.H_qk);
     const SeqInfo si = seq_info(p.seq, n, p.T);
     const int64_t DV = p.D_v, gks = (int64_t)p.H_v * DK;
-    for (int idx = tid; idx < DK * kBw; idx += 256) {
+    for (int idx = tid; idx < DK * kBw; idx += NT) {
         const int d = idx / kBw, j = idx % kBw;
         sS[d][j] = p.h0 ? p.h0[(((int64_t)n * p.H_v + h) * DK + d) * DV + cb * kBw + j] : 0.f;
     }
@@ -556,37 +561,37 @@ __global__ __launch_bounds__(256) void bwd_states_kda_kernel(BwdParams p) {
         const int nv = min(kChunk, si.len - c * kChunk);
         __syncthreads();
         float *st = p.states + ((gci * p.H_v + h) * DK) * DV + cb * kBw;
-        for (int idx = tid; idx < DK * kBw; idx += 256) st[(idx / kBw) * DV + idx % kBw] = sS[idx / kBw][idx % kBw];
-        load_rows<DK, T, 256>(&sKg[0][0], DK + 1, static_cast<const T *>(p.k) + (int64_t)hq * DK, tok0, nv, (int64_t)p.H_qk * DK, 0);
-        load_rows<DK, T, 256>(&sKd[0][0], DK + 1, static_cast<const T *>(p.g) + (int64_t)h * DK, tok0, nv, gks, 0);
-        load_rows<kBw, T, 256>(&sV[0][0], kBw + 1, static_cast<const T *>(p.v) + (int64_t)h * DV, tok0, nv, (int64_t)p.H_v * DV, cb * kBw);
-        load_tile64<T, 256>(sA, static_cast<const T *>(p.A) + (gci * p.H_v + h) * 4096);
+        for (int idx = tid; idx < DK * kBw; idx += NT) st[(idx / kBw) * DV + idx % kBw] = sS[idx / kBw][idx % kBw];
+        load_rows<DK, T, NT>(&sKg[0][0], DK + 1, static_cast<const T *>(p.k) + (int64_t)hq * DK, tok0, nv, (int64_t)p.H_qk * DK, 0);
+        load_rows<DK, T, NT>(&sKd[0][0], DK + 1, static_cast<const T *>(p.g) + (int64_t)h * DK, tok0, nv, gks, 0);
+        load_rows<kBw, T, NT>(&sV[0][0], kBw + 1, static_cast<const T *>(p.v) + (int64_t)h * DV, tok0, nv, (int64_t)p.H_v * DV, cb * kBw);
+        load_tile64<T, NT>(sA, static_cast<const T *>(p.A) + (gci * p.H_v + h) * 4096);
         if (tid < 64) load_beta<T>(p, tok0, nv, h, sb);
         cumsum_rows<DK>(&sKd[0][0], DK + 1);                 // sKd holds G
         if (tid < DK) sgc[tid] = sKd[63][tid];
         __syncthreads();
-        for (int idx = tid; idx < 64 * DK; idx += 256) {    // Kg = K e^G, Kd = K e^{G_C - G}
+        for (int idx = tid; idx < 64 * DK; idx += NT) {    // Kg = K e^G, Kd = K e^{G_C - G}
             const int i = idx / DK, d = idx % DK;
             const float k = sKg[i][d], G = sKd[i][d];
             sKg[i][d] = k * __expf(G);
             sKd[i][d] = k * __expf(sgc[d] - G);
         }
         __syncthreads();
-        for (int idx = tid; idx < 64 * kBw; idx += 256) {   // X = beta (V - Kg S)
+        for (int idx = tid; idx < 64 * kBw; idx += NT) {   // X = beta (V - Kg S)
             const int i = idx / kBw, j = idx % kBw;
             float s = 0.f;
             for (int d = 0; d < DK; ++d) s += sKg[i][d] * sS[d][j];
             sX[i][j] = sb[i] * (sV[i][j] - s);
         }
         __syncthreads();
-        for (int idx = tid; idx < 64 * kBw; idx += 256) {   // V' = A X
+        for (int idx = tid; idx < 64 * kBw; idx += NT) {   // V' = A X
             const int i = idx / kBw, j = idx % kBw;
             float s = 0.f;
             for (int t = 0; t <= i; ++t) s += sA[i][t] * sX[t][j];
             sVp[i][j] = s;
         }
         __syncthreads();
-        for (int idx = tid; idx < DK * kBw; idx += 256) {   // S = Diag(e^{G_C}) S + Kd^T V'
+        for (int idx = tid; idx < DK * kBw; idx += NT) {   // S = Diag(e^{G_C}) S + Kd^T V'
             const int d = idx / kBw, j = idx % kBw;
             float s = 0.f;
             for (int i = 0; i < 64; ++i) s += sKd[i][d] * sVp[i][j];
@@ -1038,7 +1043,7 @@ hipError_t launch_bwd(int dtype, int D_k, const BwdParams &p, hipStream_t s) {
         if (scans == 0) return hipSuccess;
 #define GDN_BWDK(K, T, DK, grid) hipLaunchKernelGGL((K<T, DK>), dim3((unsigned)(grid)), dim3(256), 0, s, p)
 #define GDN_BWDK_ALL(T, DK)                                  \
-    GDN_BWDK(bwd_states_kda_kernel, T, DK, scans);           \
+    hipLaunchKernelGGL((bwd_states_kda_kernel<T, DK>), dim3((unsigned)scans), dim3(kBwT), 0, s, p); \
     if (chunks) GDN_BWDK(bwd_p_kda_kernel, T, DK, chunks);   \
     hipLaunchKernelGGL((bwd_dstate_kda_kernel<T, DK>), dim3((unsigned)scans), dim3(kBwT), 0, s, p); \
     if (chunks) {                                            \
@@ -1063,7 +1068,7 @@ hipError_t launch_bwd(int dtype, int D_k, const BwdParams &p, hipStream_t s) {
     if (scans == 0) return hipSuccess;
 #define GDN_BWD(K, T, DK, grid) hipLaunchKernelGGL((K<T, DK>), dim3((unsigned)(grid)), dim3(256), 0, s, p)
 #define GDN_BWD_ALL(T, DK)                                  \
-    GDN_BWD(bwd_states_kernel, T, DK, scans);               \
+    hipLaunchKernelGGL((bwd_states_kernel<T, DK>), dim3((unsigned)scans), dim3(kBwT), 0, s, p); \
     if (chunks) GDN_BWD(bwd_p_kernel, T, DK, chunks);       \
     hipLaunchKernelGGL((bwd_dstate_kernel<T, DK>), dim3((unsigned)rscans), dim3(kBwT), 0, s, p); \
     if (chunks) hipLaunchKernelGGL((bwd_chunk_kernel<T, DK>), dim3((unsigned)chunks), dim3(kBwT), 0, s, p);
