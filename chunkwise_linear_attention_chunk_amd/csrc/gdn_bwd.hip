@@ -30,8 +30,8 @@ constexpr int kBwD = 32;    // value columns per workgroup of the reverse scan (
                             // 5.8 ms, 32 columns 5.4 ms on the Qwen3-Next shape; the replay is
                             // faster at 16: 2.1 against 3.1 ms)
 constexpr int kBw3 = 8;     // value columns per block of the per-chunk gradient kernel
-constexpr int kBwT = 512;   // threads of the per-chunk gradient kernel (two waves per SIMD hide its
-                            // LDS latency; 256 threads measured slower)
+constexpr int kBwT = 1024;  // threads of the gradient, replay and scan kernels: several waves per
+                            // SIMD hide their LDS latency (256 and 512 threads measured slower)
 
 // chunk-local gates of chunk (tok0, nv) and head h into sgl (cumsum, natural log) and sb (beta);
 // rows past the end carry beta = 0 and the last valid cumsum.  Wave 0 only.
@@ -51,18 +51,17 @@ __device__ __forceinline__ void load_gates(const BwdParams &p, int64_t tok0, int
 template <int COLS, typename T, int NT>
 __device__ __forceinline__ void load_rows(float *dst, int dst_ld, const T *x, int64_t tok0, int nv, int64_t ld,
                                           int c0) {
-    constexpr int N = 64 * COLS / NT;
-    static_assert(N * NT == 64 * COLS, "whole rows per pass");
+    constexpr int N = (64 * COLS + NT - 1) / NT;   // threads past 64 COLS elements idle
     float v[N];
 #pragma unroll
     for (int it = 0; it < N; ++it) {
         const int idx = threadIdx.x + NT * it, i = idx / COLS, j = idx - i * COLS;
-        v[it] = to_f32(x[(tok0 + min(i, nv - 1)) * ld + c0 + j]);
+        v[it] = idx < 64 * COLS ? to_f32(x[(tok0 + min(i, nv - 1)) * ld + c0 + j]) : 0.f;
     }
 #pragma unroll
     for (int it = 0; it < N; ++it) {
         const int idx = threadIdx.x + NT * it, i = idx / COLS, j = idx - i * COLS;
-        dst[i * dst_ld + j] = i < nv ? v[it] : 0.f;
+        if (idx < 64 * COLS) dst[i * dst_ld + j] = i < nv ? v[it] : 0.f;
     }
 }
 
@@ -303,19 +302,21 @@ __global__ __launch_bounds__(kBwT) void bwd_chunk_kernel(BwdParams p) {
     for (int c0 = 0; c0 < p.D_v; c0 += kBw3) {
         __syncthreads();   // Pt is complete; the previous block is done with its tiles
         {
-            constexpr int NE = DK * kBw3 / NT;
+            constexpr int NE = (DK * kBw3 + NT - 1) / NT;   // threads past DK kBw3 elements idle
             float a[NE], b[NE];
 #pragma unroll
             for (int it = 0; it < NE; ++it) {
-                const int idx = tid + NT * it, d = idx / kBw3, j = idx % kBw3;
+                const int idx = min(tid + NT * it, DK * kBw3 - 1), d = idx / kBw3, j = idx % kBw3;
                 a[it] = St[d * DV + c0 + j];
                 b[it] = dSt[d * DV + c0 + j];
             }
 #pragma unroll
             for (int it = 0; it < NE; ++it) {
                 const int idx = tid + NT * it, d = idx / kBw3, j = idx % kBw3;
-                sS[d][j] = a[it];
-                sdS[d][j] = b[it];
+                if (idx < DK * kBw3) {
+                    sS[d][j] = a[it];
+                    sdS[d][j] = b[it];
+                }
             }
         }
         load_rows<kBw3, T, NT>(&sV[0][0], W3, static_cast<const T *>(p.v) + (int64_t)h * DV, tok0, nv, vs, c0);
@@ -782,19 +783,21 @@ __global__ __launch_bounds__(kBwT) void bwd_chunk_kda_a_kernel(BwdParams p) {
     for (int c0 = 0; c0 < p.D_v; c0 += kBw3) {
         __syncthreads();
         {
-            constexpr int NE = DK * kBw3 / NT;
+            constexpr int NE = (DK * kBw3 + NT - 1) / NT;   // threads past DK kBw3 elements idle
             float a[NE], b[NE];
 #pragma unroll
             for (int it = 0; it < NE; ++it) {
-                const int idx = tid + NT * it, d = idx / kBw3, j = idx % kBw3;
+                const int idx = min(tid + NT * it, DK * kBw3 - 1), d = idx / kBw3, j = idx % kBw3;
                 a[it] = St[d * DV + c0 + j];
                 b[it] = dSt[d * DV + c0 + j];
             }
 #pragma unroll
             for (int it = 0; it < NE; ++it) {
                 const int idx = tid + NT * it, d = idx / kBw3, j = idx % kBw3;
-                sS[d][j] = a[it];
-                sdS[d][j] = b[it];
+                if (idx < DK * kBw3) {
+                    sS[d][j] = a[it];
+                    sdS[d][j] = b[it];
+                }
             }
         }
         load_rows<kBw3, T, NT>(&sV[0][0], W3, static_cast<const T *>(p.v) + (int64_t)h * DV, tok0, nv, vs, c0);
