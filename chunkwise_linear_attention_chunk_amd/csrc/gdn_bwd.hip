@@ -30,7 +30,7 @@ constexpr int kBwD = 32;    // value columns per workgroup of the reverse scan (
                             // 5.8 ms, 32 columns 5.4 ms on the Qwen3-Next shape; the replay is
                             // faster at 16: 2.1 against 3.1 ms)
 constexpr int kBw3 = 8;     // value columns per block of the per-chunk gradient kernel
-constexpr int kBwT = 1024;  // threads of the gradient, replay and scan kernels: several waves per
+constexpr int kBwT = 1024;  // threads of the backward kernels (P, replay, scan, gradients): waves per
                             // SIMD hide their LDS latency (256 and 512 threads measured slower)
 
 // chunk-local gates of chunk (tok0, nv) and head h into sgl (cumsum, natural log) and sb (beta);
@@ -137,7 +137,8 @@ __global__ __launch_bounds__(kBwT) void bwd_states_kernel(BwdParams p) {
 // ---- scale Pt of every (chunk, value head), fp32 [64][64], for the reverse scan (which would
 //      otherwise form it once per value-column group)
 template <typename T, int DK>
-__global__ __launch_bounds__(256) void bwd_p_kernel(BwdParams p) {
+__global__ __launch_bounds__(kBwT) void bwd_p_kernel(BwdParams p) {
+    constexpr int NT = kBwT;
     __shared__ float sK[64][DK + 1], sQ[64][DK + 1];
     __shared__ float sgl[64], sb[64];
     const int tid = threadIdx.x;
@@ -145,12 +146,12 @@ __global__ __launch_bounds__(256) void bwd_p_kernel(BwdParams p) {
     const int hq = h / (p.H_v / p.H_qk);
     const ChunkInfo cinfo = chunk_info(p.chunks, ci, p.T);
     const int64_t qks = (int64_t)p.H_qk * DK;
-    load_rows<DK, T, 256>(&sK[0][0], DK + 1, static_cast<const T *>(p.k) + (int64_t)hq * DK, cinfo.tok0, cinfo.nv, qks, 0);
-    load_rows<DK, T, 256>(&sQ[0][0], DK + 1, static_cast<const T *>(p.q) + (int64_t)hq * DK, cinfo.tok0, cinfo.nv, qks, 0);
+    load_rows<DK, T, NT>(&sK[0][0], DK + 1, static_cast<const T *>(p.k) + (int64_t)hq * DK, cinfo.tok0, cinfo.nv, qks, 0);
+    load_rows<DK, T, NT>(&sQ[0][0], DK + 1, static_cast<const T *>(p.q) + (int64_t)hq * DK, cinfo.tok0, cinfo.nv, qks, 0);
     if (tid < 64) load_gates<T>(p, cinfo.tok0, cinfo.nv, h, sgl, sb);
     __syncthreads();
     float *P = p.pmat + ((int64_t)ci * p.H_v + h) * 4096;
-    for (int idx = tid; idx < 4096; idx += 256) {
+    for (int idx = tid; idx < 4096; idx += NT) {
         const int i = idx / 64, j = idx % 64;
         float s = 0.f;
         if (j <= i)
@@ -601,27 +602,48 @@ __global__ __launch_bounds__(kBwT) void bwd_states_kda_kernel(BwdParams p) {
     }
 }
 
-// ---- scale P of every (chunk, value head), per-channel factors inside the sum
+// ---- scale P of every (chunk, value head), per-channel factors inside the sum.  The factor
+//      e^{G_id - G_jd} is split at the first row r of key j's 16-row block (r <= j <= i):
+//      e^{G_id - G_rd} <= 1 goes with q_i, e^{G_rd - G_jd} (a decay over at most 15 tokens) with k_j,
+//      so one exponential per operand element replaces one per term of the sum.
 template <typename T, int DK>
-__global__ __launch_bounds__(256) void bwd_p_kda_kernel(BwdParams p) {
-    __shared__ float sK[64][DK + 1], sQ[64][DK + 1], sG[64][DK + 1];
+__global__ __launch_bounds__(kBwT) void bwd_p_kda_kernel(BwdParams p) {
+    constexpr int NT = kBwT;
+    __shared__ float sK[64][DK + 1], sQ[64][DK + 1], sG[64][DK + 1], sQx[64][DK + 1];
     const int tid = threadIdx.x;
     const int ci = blockIdx.x / p.H_v, h = blockIdx.x - ci * p.H_v;
     const int hq = h / (p.H_v / p.H_qk);
     const ChunkInfo cinfo = chunk_info(p.chunks, ci, p.T);
     const int64_t qks = (int64_t)p.H_qk * DK;
-    load_rows<DK, T, 256>(&sK[0][0], DK + 1, static_cast<const T *>(p.k) + (int64_t)hq * DK, cinfo.tok0, cinfo.nv, qks, 0);
-    load_rows<DK, T, 256>(&sQ[0][0], DK + 1, static_cast<const T *>(p.q) + (int64_t)hq * DK, cinfo.tok0, cinfo.nv, qks, 0);
-    load_rows<DK, T, 256>(&sG[0][0], DK + 1, static_cast<const T *>(p.g) + (int64_t)h * DK, cinfo.tok0, cinfo.nv,
-                  (int64_t)p.H_v * DK, 0);
+    load_rows<DK, T, NT>(&sK[0][0], DK + 1, static_cast<const T *>(p.k) + (int64_t)hq * DK, cinfo.tok0, cinfo.nv, qks, 0);
+    load_rows<DK, T, NT>(&sQ[0][0], DK + 1, static_cast<const T *>(p.q) + (int64_t)hq * DK, cinfo.tok0, cinfo.nv, qks, 0);
+    load_rows<DK, T, NT>(&sG[0][0], DK + 1, static_cast<const T *>(p.g) + (int64_t)h * DK, cinfo.tok0, cinfo.nv,
+                         (int64_t)p.H_v * DK, 0);
     cumsum_rows<DK>(&sG[0][0], DK + 1);
+    for (int idx = tid; idx < 64 * DK; idx += NT) {       // k_j e^{G_r - G_j}, r = 16 floor(j / 16)
+        const int j = idx / DK, d = idx % DK;
+        sK[j][d] *= __expf(sG[j & ~15][d] - sG[j][d]);
+    }
     float *P = p.pmat + ((int64_t)ci * p.H_v + h) * 4096;
-    for (int idx = tid; idx < 4096; idx += 256) {
+    for (int J = 0; J < 4; ++J) {                         // keys of block J: rows i >= 16 J
+        __syncthreads();                                  // sG, sK ready; sQx free
+        for (int idx = tid; idx < (64 - 16 * J) * DK; idx += NT) {
+            const int i = 16 * J + idx / DK, d = idx % DK;
+            sQx[i][d] = sQ[i][d] * __expf(sG[i][d] - sG[16 * J][d]);
+        }
+        __syncthreads();
+        for (int idx = tid; idx < 64 * 16; idx += NT) {
+            const int i = idx / 16, j = 16 * J + idx % 16;
+            if (i < 16 * J) continue;                     // above the diagonal: written below
+            float s = 0.f;
+            if (j <= i)
+                for (int d = 0; d < DK; ++d) s += sQx[i][d] * sK[j][d];
+            P[i * 64 + j] = j <= i ? p.scale * s : 0.f;
+        }
+    }
+    for (int idx = tid; idx < 4096; idx += NT) {          // the blocks above the diagonal
         const int i = idx / 64, j = idx % 64;
-        float s = 0.f;
-        if (j <= i)
-            for (int d = 0; d < DK; ++d) s += sQ[i][d] * sK[j][d] * __expf(sG[i][d] - sG[j][d]);
-        P[idx] = j <= i ? p.scale * s : 0.f;
+        if ((j >> 4) > (i >> 4)) P[idx] = 0.f;
     }
 }
 
@@ -1044,14 +1066,15 @@ hipError_t launch_bwd(int dtype, int D_k, const BwdParams &p, hipStream_t s) {
     if (p.channel) {
         const int64_t scans = (int64_t)p.N * p.H_v * (p.D_v / kBw), chunks = (int64_t)p.n_chunks * p.H_v;
         if (scans == 0) return hipSuccess;
-#define GDN_BWDK(K, T, DK, grid) hipLaunchKernelGGL((K<T, DK>), dim3((unsigned)(grid)), dim3(256), 0, s, p)
+// every kernel of the backward runs kBwT threads per workgroup
+#define GDN_BWDK(K, T, DK, grid) hipLaunchKernelGGL((K<T, DK>), dim3((unsigned)(grid)), dim3(kBwT), 0, s, p)
 #define GDN_BWDK_ALL(T, DK)                                  \
-    hipLaunchKernelGGL((bwd_states_kda_kernel<T, DK>), dim3((unsigned)scans), dim3(kBwT), 0, s, p); \
+    GDN_BWDK(bwd_states_kda_kernel, T, DK, scans);           \
     if (chunks) GDN_BWDK(bwd_p_kda_kernel, T, DK, chunks);   \
-    hipLaunchKernelGGL((bwd_dstate_kda_kernel<T, DK>), dim3((unsigned)scans), dim3(kBwT), 0, s, p); \
+    GDN_BWDK(bwd_dstate_kda_kernel, T, DK, scans);           \
     if (chunks) {                                            \
-        hipLaunchKernelGGL((bwd_chunk_kda_a_kernel<T, DK>), dim3((unsigned)chunks), dim3(kBwT), 0, s, p); \
-        hipLaunchKernelGGL((bwd_chunk_kda_b_kernel<T, DK>), dim3((unsigned)chunks), dim3(kBwT), 0, s, p); \
+        GDN_BWDK(bwd_chunk_kda_a_kernel, T, DK, chunks);     \
+        GDN_BWDK(bwd_chunk_kda_b_kernel, T, DK, chunks);     \
     }
         if (dtype == 1 && D_k == 128) { GDN_BWDK_ALL(bf16, 128) }
         else if (dtype == 1 && D_k == 64) { GDN_BWDK_ALL(bf16, 64) }
@@ -1069,12 +1092,12 @@ hipError_t launch_bwd(int dtype, int D_k, const BwdParams &p, hipStream_t s) {
     const int64_t scans = (int64_t)p.N * p.H_v * (p.D_v / kBw), rscans = (int64_t)p.N * p.H_v * (p.D_v / kBwD);
     const int64_t chunks = (int64_t)p.n_chunks * p.H_v;
     if (scans == 0) return hipSuccess;
-#define GDN_BWD(K, T, DK, grid) hipLaunchKernelGGL((K<T, DK>), dim3((unsigned)(grid)), dim3(256), 0, s, p)
+#define GDN_BWD(K, T, DK, grid) hipLaunchKernelGGL((K<T, DK>), dim3((unsigned)(grid)), dim3(kBwT), 0, s, p)
 #define GDN_BWD_ALL(T, DK)                                  \
-    hipLaunchKernelGGL((bwd_states_kernel<T, DK>), dim3((unsigned)scans), dim3(kBwT), 0, s, p); \
+    GDN_BWD(bwd_states_kernel, T, DK, scans);               \
     if (chunks) GDN_BWD(bwd_p_kernel, T, DK, chunks);       \
-    hipLaunchKernelGGL((bwd_dstate_kernel<T, DK>), dim3((unsigned)rscans), dim3(kBwT), 0, s, p); \
-    if (chunks) hipLaunchKernelGGL((bwd_chunk_kernel<T, DK>), dim3((unsigned)chunks), dim3(kBwT), 0, s, p);
+    GDN_BWD(bwd_dstate_kernel, T, DK, rscans);              \
+    if (chunks) GDN_BWD(bwd_chunk_kernel, T, DK, chunks);
     if (dtype == 1 && D_k == 128) { GDN_BWD_ALL(bf16, 128) }
     else if (dtype == 1 && D_k == 64) { GDN_BWD_ALL(bf16, 64) }
     else if (dtype == 0 && D_k == 128) { GDN_BWD_ALL(float, 128) }
