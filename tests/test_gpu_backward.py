@@ -85,3 +85,13 @@ def test_backward_per_channel_bf16():
 def test_backward_per_channel_packed():
     x = synth.make_inputs(synth.workload("kda_bf16", B=1, n_seqs=4, lens=(1, 0, 130, 64), H=2, h0=True, seed=632))
     _check(x, TOL["bf16"], "KDA bf16 packed", seed=13, dht=False)
+
+
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+@pytest.mark.parametrize("mu", [1.0, -6.0])
+def test_backward_fp32_gate_strengths(gate, mu):
+    # strong decay (about -1.3 per token: a chunk spans ~e^-80) and weak decay (~2.5e-3 per token);
+    # the per-channel P splits its decay factors within 16-token blocks, which strong gates stress
+    x = synth.make_inputs(synth.workload("tiny_fp32", B=1, H=2, T=150, gate=gate, mu=mu, h0=True,
+                                         seed=640 + int(mu) + (10 if gate == "channel" else 0)))
+    _check(x, TOL["fp32"], f"{gate} fp32 mu={mu}", seed=20 + int(mu))
