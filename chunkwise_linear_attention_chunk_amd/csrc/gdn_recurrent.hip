@@ -52,13 +52,14 @@ __global__ __launch_bounds__(256) void recurrent_kernel(RecurrentParams p) {
     const int col = cb * kRecCols + 4 * c4;
     const int64_t sbase = ((int64_t)n * p.H_v + h) * DK * p.D_v;
 
-    // ---- state: h0 or zero
+    // ---- state: h0 or zero.  The state is read once and written once per call: its loads and
+    //      stores carry the non-temporal hint (streamed past the caches' reuse).
     float s[RPT][4];
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
         if (p.h0) {
-            const float4 x = *reinterpret_cast<const float4 *>(p.h0 + sbase + (int64_t)(RPT * rg + r) * p.D_v + col);
-            s[r][0] = x.x; s[r][1] = x.y; s[r][2] = x.z; s[r][3] = x.w;
+            const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p.h0 + sbase + (int64_t)(RPT * rg + r) * p.D_v + col));
+            s[r][0] = x[0]; s[r][1] = x[1]; s[r][2] = x[2]; s[r][3] = x[3];
         } else {
             s[r][0] = s[r][1] = s[r][2] = s[r][3] = 0.f;
         }
@@ -208,8 +209,8 @@ __global__ __launch_bounds__(256) void recurrent_kernel(RecurrentParams p) {
     if (p.final_state) {
 #pragma unroll
         for (int r = 0; r < RPT; ++r)
-            *reinterpret_cast<float4 *>(p.final_state + sbase + (int64_t)(RPT * rg + r) * p.D_v + col) =
-                make_float4(s[r][0], s[r][1], s[r][2], s[r][3]);
+            __builtin_nontemporal_store(f32x4{s[r][0], s[r][1], s[r][2], s[r][3]},
+                                        reinterpret_cast<f32x4 *>(p.final_state + sbase + (int64_t)(RPT * rg + r) * p.D_v + col));
     }
 }
 
