@@ -25,7 +25,8 @@
 namespace gdn {
 namespace {
 
-constexpr int kBw = 16;     // value columns per workgroup of the forward replay
+constexpr int kBw = 16;     // value columns per workgroup of the per-channel reverse scan
+constexpr int kBwR = 32;    // value columns per workgroup of the forward replays
 constexpr int kBwD = 32;    // value columns per workgroup of the reverse scan (measured: 16 columns
                             // 5.8 ms, 32 columns 5.4 ms on the Qwen3-Next shape; the replay is
                             // faster at 16: 2.1 against 3.1 ms)
@@ -79,54 +80,54 @@ __device__ __forceinline__ void load_tile64(float (*dst)[65], const T *x) {
     }
 }
 
-// ---- recomputed chunk states: S entering every chunk, per (sequence, value head, kBw columns)
+// ---- recomputed chunk states: S entering every chunk, per (sequence, value head, kBwR columns)
 template <typename T, int DK>
 __global__ __launch_bounds__(kBwT) void bwd_states_kernel(BwdParams p) {
     constexpr int NT = kBwT;
     // odd row strides (+1) keep the column walks of these tiles free of LDS bank conflicts
-    __shared__ float sK[64][DK + 1], sA[64][65], sS[DK][kBw + 1], sV[64][kBw + 1], sX[64][kBw + 1], sVp[64][kBw + 1];
+    __shared__ float sK[64][DK + 1], sA[64][65], sS[DK][kBwR + 1], sV[64][kBwR + 1], sX[64][kBwR + 1], sVp[64][kBwR + 1];
     __shared__ float sgl[64], sb[64], sD[64];
     const int tid = threadIdx.x;
-    const int ncb = p.D_v / kBw;
+    const int ncb = p.D_v / kBwR;
     const int cb = blockIdx.x % ncb, nh = blockIdx.x / ncb, h = nh % p.H_v, n = nh / p.H_v;
     const int hq = h / (p.H_v / p.H_qk);
     const SeqInfo si = seq_info(p.seq, n, p.T);
     const int64_t DV = p.D_v;
-    for (int idx = tid; idx < DK * kBw; idx += NT) {
-        const int d = idx / kBw, j = idx % kBw;
-        sS[d][j] = p.h0 ? p.h0[(((int64_t)n * p.H_v + h) * DK + d) * DV + cb * kBw + j] : 0.f;
+    for (int idx = tid; idx < DK * kBwR; idx += NT) {
+        const int d = idx / kBwR, j = idx % kBwR;
+        sS[d][j] = p.h0 ? p.h0[(((int64_t)n * p.H_v + h) * DK + d) * DV + cb * kBwR + j] : 0.f;
     }
     for (int c = 0; c < si.nchunks; ++c) {
         const int64_t gci = si.chunk0 + c, tok0 = si.tok0 + (int64_t)c * kChunk;
         const int nv = min(kChunk, si.len - c * kChunk);
         __syncthreads();   // the previous chunk is done with every tile
-        float *st = p.states + ((gci * p.H_v + h) * DK) * DV + cb * kBw;
-        for (int idx = tid; idx < DK * kBw; idx += NT) st[(idx / kBw) * DV + idx % kBw] = sS[idx / kBw][idx % kBw];
+        float *st = p.states + ((gci * p.H_v + h) * DK) * DV + cb * kBwR;
+        for (int idx = tid; idx < DK * kBwR; idx += NT) st[(idx / kBwR) * DV + idx % kBwR] = sS[idx / kBwR][idx % kBwR];
         load_rows<DK, T, NT>(&sK[0][0], DK + 1, static_cast<const T *>(p.k) + (int64_t)hq * DK, tok0, nv, (int64_t)p.H_qk * DK, 0);
-        load_rows<kBw, T, NT>(&sV[0][0], kBw + 1, static_cast<const T *>(p.v) + (int64_t)h * DV, tok0, nv, (int64_t)p.H_v * DV, cb * kBw);
+        load_rows<kBwR, T, NT>(&sV[0][0], kBwR + 1, static_cast<const T *>(p.v) + (int64_t)h * DV, tok0, nv, (int64_t)p.H_v * DV, cb * kBwR);
         load_tile64<T, NT>(sA, static_cast<const T *>(p.A) + (gci * p.H_v + h) * 4096);
         if (tid < 64) {
             load_gates<T>(p, tok0, nv, h, sgl, sb);
             sD[tid] = __expf(__shfl(sgl[tid], 63, 64) - sgl[tid]);   // D_i = gamma_C / gamma_i
         }
         __syncthreads();
-        for (int idx = tid; idx < 64 * kBw; idx += NT) {   // X = beta (V - gamma K S)
-            const int i = idx / kBw, j = idx % kBw;
+        for (int idx = tid; idx < 64 * kBwR; idx += NT) {   // X = beta (V - gamma K S)
+            const int i = idx / kBwR, j = idx % kBwR;
             float s = 0.f;
             for (int d = 0; d < DK; ++d) s += sK[i][d] * sS[d][j];
             sX[i][j] = sb[i] * (sV[i][j] - __expf(sgl[i]) * s);
         }
         __syncthreads();
-        for (int idx = tid; idx < 64 * kBw; idx += NT) {   // V' = A X (A lower)
-            const int i = idx / kBw, j = idx % kBw;
+        for (int idx = tid; idx < 64 * kBwR; idx += NT) {   // V' = A X (A lower)
+            const int i = idx / kBwR, j = idx % kBwR;
             float s = 0.f;
             for (int t = 0; t <= i; ++t) s += sA[i][t] * sX[t][j];
             sVp[i][j] = s;
         }
         __syncthreads();
         const float gC = __expf(sgl[63]);
-        for (int idx = tid; idx < DK * kBw; idx += NT) {   // S = gamma_C S + K^T diag(D) V'
-            const int d = idx / kBw, j = idx % kBw;
+        for (int idx = tid; idx < DK * kBwR; idx += NT) {   // S = gamma_C S + K^T diag(D) V'
+            const int d = idx / kBwR, j = idx % kBwR;
             float s = 0.f;
             for (int i = 0; i < 64; ++i) s += sK[i][d] * sD[i] * sVp[i][j];
             sS[d][j] = gC * sS[d][j] + s;
@@ -546,27 +547,27 @@ template <typename T, int DK>
 __global__ __launch_bounds__(kBwT) void bwd_states_kda_kernel(BwdParams p) {
     constexpr int NT = kBwT;
     __shared__ float sKg[64][DK + 1], sKd[64][DK + 1], sA[64][65];
-    __shared__ float sS[DK][kBw + 1], sV[64][kBw + 1], sX[64][kBw + 1], sVp[64][kBw + 1];
+    __shared__ float sS[DK][kBwR + 1], sV[64][kBwR + 1], sX[64][kBwR + 1], sVp[64][kBwR + 1];
     __shared__ float sb[64], sgc[DK];
     const int tid = threadIdx.x;
-    const int ncb = p.D_v / kBw;
+    const int ncb = p.D_v / kBwR;
     const int cb = blockIdx.x % ncb, nh = blockIdx.x / ncb, h = nh % p.H_v, n = nh / p.H_v;
     const int hq = h / (p.H_v / p.H_qk);
     const SeqInfo si = seq_info(p.seq, n, p.T);
     const int64_t DV = p.D_v, gks = (int64_t)p.H_v * DK;
-    for (int idx = tid; idx < DK * kBw; idx += NT) {
-        const int d = idx / kBw, j = idx % kBw;
-        sS[d][j] = p.h0 ? p.h0[(((int64_t)n * p.H_v + h) * DK + d) * DV + cb * kBw + j] : 0.f;
+    for (int idx = tid; idx < DK * kBwR; idx += NT) {
+        const int d = idx / kBwR, j = idx % kBwR;
+        sS[d][j] = p.h0 ? p.h0[(((int64_t)n * p.H_v + h) * DK + d) * DV + cb * kBwR + j] : 0.f;
     }
     for (int c = 0; c < si.nchunks; ++c) {
         const int64_t gci = si.chunk0 + c, tok0 = si.tok0 + (int64_t)c * kChunk;
         const int nv = min(kChunk, si.len - c * kChunk);
         __syncthreads();
-        float *st = p.states + ((gci * p.H_v + h) * DK) * DV + cb * kBw;
-        for (int idx = tid; idx < DK * kBw; idx += NT) st[(idx / kBw) * DV + idx % kBw] = sS[idx / kBw][idx % kBw];
+        float *st = p.states + ((gci * p.H_v + h) * DK) * DV + cb * kBwR;
+        for (int idx = tid; idx < DK * kBwR; idx += NT) st[(idx / kBwR) * DV + idx % kBwR] = sS[idx / kBwR][idx % kBwR];
         load_rows<DK, T, NT>(&sKg[0][0], DK + 1, static_cast<const T *>(p.k) + (int64_t)hq * DK, tok0, nv, (int64_t)p.H_qk * DK, 0);
         load_rows<DK, T, NT>(&sKd[0][0], DK + 1, static_cast<const T *>(p.g) + (int64_t)h * DK, tok0, nv, gks, 0);
-        load_rows<kBw, T, NT>(&sV[0][0], kBw + 1, static_cast<const T *>(p.v) + (int64_t)h * DV, tok0, nv, (int64_t)p.H_v * DV, cb * kBw);
+        load_rows<kBwR, T, NT>(&sV[0][0], kBwR + 1, static_cast<const T *>(p.v) + (int64_t)h * DV, tok0, nv, (int64_t)p.H_v * DV, cb * kBwR);
         load_tile64<T, NT>(sA, static_cast<const T *>(p.A) + (gci * p.H_v + h) * 4096);
         if (tid < 64) load_beta<T>(p, tok0, nv, h, sb);
         cumsum_rows<DK>(&sKd[0][0], DK + 1);                 // sKd holds G
@@ -579,22 +580,22 @@ __global__ __launch_bounds__(kBwT) void bwd_states_kda_kernel(BwdParams p) {
             sKd[i][d] = k * __expf(sgc[d] - G);
         }
         __syncthreads();
-        for (int idx = tid; idx < 64 * kBw; idx += NT) {   // X = beta (V - Kg S)
-            const int i = idx / kBw, j = idx % kBw;
+        for (int idx = tid; idx < 64 * kBwR; idx += NT) {   // X = beta (V - Kg S)
+            const int i = idx / kBwR, j = idx % kBwR;
             float s = 0.f;
             for (int d = 0; d < DK; ++d) s += sKg[i][d] * sS[d][j];
             sX[i][j] = sb[i] * (sV[i][j] - s);
         }
         __syncthreads();
-        for (int idx = tid; idx < 64 * kBw; idx += NT) {   // V' = A X
-            const int i = idx / kBw, j = idx % kBw;
+        for (int idx = tid; idx < 64 * kBwR; idx += NT) {   // V' = A X
+            const int i = idx / kBwR, j = idx % kBwR;
             float s = 0.f;
             for (int t = 0; t <= i; ++t) s += sA[i][t] * sX[t][j];
             sVp[i][j] = s;
         }
         __syncthreads();
-        for (int idx = tid; idx < DK * kBw; idx += NT) {   // S = Diag(e^{G_C}) S + Kd^T V'
-            const int d = idx / kBw, j = idx % kBw;
+        for (int idx = tid; idx < DK * kBwR; idx += NT) {   // S = Diag(e^{G_C}) S + Kd^T V'
+            const int d = idx / kBwR, j = idx % kBwR;
             float s = 0.f;
             for (int i = 0; i < 64; ++i) s += sKd[i][d] * sVp[i][j];
             sS[d][j] = __expf(sgc[d]) * sS[d][j] + s;
@@ -1065,11 +1066,12 @@ __global__ __launch_bounds__(256) void bwd_group_sum_kernel(BwdParams p, int DK,
 hipError_t launch_bwd(int dtype, int D_k, const BwdParams &p, hipStream_t s) {
     if (p.channel) {
         const int64_t scans = (int64_t)p.N * p.H_v * (p.D_v / kBw), chunks = (int64_t)p.n_chunks * p.H_v;
+        const int64_t replays = (int64_t)p.N * p.H_v * (p.D_v / kBwR);
         if (scans == 0) return hipSuccess;
 // every kernel of the backward runs kBwT threads per workgroup
 #define GDN_BWDK(K, T, DK, grid) hipLaunchKernelGGL((K<T, DK>), dim3((unsigned)(grid)), dim3(kBwT), 0, s, p)
 #define GDN_BWDK_ALL(T, DK)                                  \
-    GDN_BWDK(bwd_states_kda_kernel, T, DK, scans);           \
+    GDN_BWDK(bwd_states_kda_kernel, T, DK, replays);         \
     if (chunks) GDN_BWDK(bwd_p_kda_kernel, T, DK, chunks);   \
     GDN_BWDK(bwd_dstate_kda_kernel, T, DK, scans);           \
     if (chunks) {                                            \
@@ -1089,7 +1091,7 @@ hipError_t launch_bwd(int dtype, int D_k, const BwdParams &p, hipStream_t s) {
         if (n) hipLaunchKernelGGL(bwd_group_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, D_k, n);
         return hipGetLastError();
     }
-    const int64_t scans = (int64_t)p.N * p.H_v * (p.D_v / kBw), rscans = (int64_t)p.N * p.H_v * (p.D_v / kBwD);
+    const int64_t scans = (int64_t)p.N * p.H_v * (p.D_v / kBwR), rscans = (int64_t)p.N * p.H_v * (p.D_v / kBwD);
     const int64_t chunks = (int64_t)p.n_chunks * p.H_v;
     if (scans == 0) return hipSuccess;
 #define GDN_BWD(K, T, DK, grid) hipLaunchKernelGGL((K<T, DK>), dim3((unsigned)(grid)), dim3(kBwT), 0, s, p)
