@@ -276,7 +276,7 @@ def cpu_baseline_backward(x, do, dht, T=256, heads=2):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {a.gpus}); "
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for --gpus {a.gpus}); "
               "heads and sequences would shard across GPUs with no communication.", file=sys.stderr)
         sys.exit(2)
     import torch
