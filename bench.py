@@ -23,10 +23,14 @@ sys.path.insert(0, ROOT)
 METRIC = "GDN chunked-prefill fwd tokens/s at 1 GPU + % of MFMA/HBM roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
-KERNEL_SOURCES = {"recurrent": "chunkwise_linear_attention_chunk_amd/csrc/gdn_recurrent.hip",
-                  "chunk": "chunkwise_linear_attention_chunk_amd/csrc/gdn_chunk.hip",
-                  "cp_pre": "chunkwise_linear_attention_chunk_amd/csrc/gdn_chunk.hip",
-                  "intra": "chunkwise_linear_attention_chunk_amd/csrc/gdn_intra.hip"}
+_CSRC = "chunkwise_linear_attention_chunk_amd/csrc/"
+_HEADERS = [_CSRC + "gdn_device.h", _CSRC + "gdn_internal.h"]
+# each kernel's source file and the headers it includes (the counters of profiles/traffic_*.json
+# are current only while all of them are unchanged)
+KERNEL_SOURCES = {"recurrent": [_CSRC + "gdn_recurrent.hip"] + _HEADERS,
+                  "chunk": [_CSRC + "gdn_chunk.hip"] + _HEADERS,
+                  "cp_pre": [_CSRC + "gdn_chunk.hip"] + _HEADERS,
+                  "intra": [_CSRC + "gdn_intra.hip"] + _HEADERS}
 
 
 def parse():
@@ -40,6 +44,10 @@ def parse():
                     help="in-GPU context parallelism (auto: on when too few (sequence, head) chains fill the chip)")
     ap.add_argument("--cp-segment-chunks", type=int, default=0, help="CP segment length in chunks (0: automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the other configurations (reported by default with the Qwen3-Next-shaped headline)")
+    ap.add_argument("--extra-steps", type=int, default=10)
+    ap.add_argument("--extra-warmup", type=int, default=3)
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: all host cores)")
     ap.add_argument("--path", default="prefill", choices=["prefill", "decode", "backward"],
                     help="prefill: gdn_fwd on --workload; decode: gdn_fwd_recurrent, one token per sequence "
@@ -113,8 +121,11 @@ def algorithmic_flops(x):
 
 
 def source_hash(kernel):
-    with open(os.path.join(ROOT, KERNEL_SOURCES[kernel]), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel, workload):
@@ -233,7 +244,7 @@ def bench_backward(a, torch, gdn, synth, dev):
     tokens = x["tokens"]
     H_qk = x["q"].shape[2]
     alg = algorithmic_bytes(x, esz) + N * H * D * Dv * 4     # q, k, v, dO, beta, g, h0, dht read, dh0 written
-    alg += tokens * (2 * H_qk * D + H * Dv + 2 * H) * 4          # dq, dk, dv, dg, dbeta written (fp32)
+    alg += sum(grads[n].numel() for n in ("dq", "dk", "dv", "dg", "dbeta")) * 4   # gradients written (fp32)
     achieved = alg / (ms * 1e-3) / 1e9
     rec = {
         "metric": "GDN chunked backward tokens/s at 1 GPU + % of HBM roofline", "value": tokens * a.steps / elapsed,
@@ -297,12 +308,49 @@ def main():
         return bench_decode(a, torch, gdn, synth, dev)
     if a.path == "backward":
         return bench_backward(a, torch, gdn, synth, dev)
-    w = synth.workload(a.workload)
+    rec, x = measure_prefill(a.workload, a.steps, a.warmup, a.copies, a.cp, a.cp_segment_chunks, torch, gdn, synth,
+                             dev)
+    if not a.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(x, a.cpu_threads)
+    del x
+    if not a.no_extras and a.workload == "qwen3next_bf16" and a.cp == "auto":
+        rec["extra_configs"] = extra_configs(a, torch, gdn, synth, dev)
+    print(json.dumps(rec), flush=True)
+
+
+# The other configurations of the path, measured in the same run (one line each in extra_configs):
+# (label, workload, cp mode).  The long-context workload is reported with exact context parallelism
+# (the automatic choice) and, labelled, with its warmup form (an approximation with a stated bound).
+EXTRAS = (("tiny_fp32", "tiny_fp32", "auto"), ("longctx_bf16", "longctx_bf16", "auto"),
+          ("longctx_bf16_warmup_cp", "longctx_bf16", "warmup"), ("varlen_bf16", "varlen_bf16", "auto"),
+          ("kda_bf16", "kda_bf16", "auto"))
+
+
+def extra_configs(a, torch, gdn, synth, dev):
+    out = {}
+    for label, name, cp in EXTRAS:
+        print(f"[bench] extra config {label}", file=sys.stderr, flush=True)
+        r, x = measure_prefill(name, a.extra_steps, a.extra_warmup, a.copies, cp, 0, torch, gdn, synth, dev)
+        del x
+        torch.cuda.empty_cache()
+        out[label] = {"workload": name, "cp": cp, "cp_ran": r["config"]["cp_ran"],
+                      "cp_segment_chunks": r["config"]["cp_segment_chunks"], "ms_per_step": r["ms_per_step"],
+                      "tokens_per_s": r["value"], "dtype": r["dtype"],
+                      "whole_op_roofline_frac": r["whole_op"]["roofline_frac"],
+                      "dominant_kernel": r["roofline"]["kernel"], "dominant_kernel_frac": r["roofline"]["frac"],
+                      "stage_ms": r["stage_ms"]}
+    return out
+
+
+def measure_prefill(name, steps, warmup, n_copies, cp, cp_segment_chunks, torch, gdn, synth, dev):
+    """Time `steps` gdn_fwd_timed calls on workload `name` (after `warmup` untimed calls), rotating
+    n_copies input copies.  Returns (record without cpu_baseline, host inputs)."""
+    w = synth.workload(name)
     x = synth.make_inputs(w)
     esz = x["q"].element_size()
     names = ("q", "k", "v", "g", "beta")
     copies = []
-    for _ in range(max(1, a.copies)):
+    for _ in range(max(1, n_copies)):
         t = {n: x[n].to(dev) for n in names}
         t["h0"] = None if x["h0"] is None else x["h0"].to(dev)
         copies.append(t)
@@ -312,7 +360,7 @@ def main():
     fs = torch.empty((x["n_seqs"],) + tuple(x["v"].shape[2:3]) + (x["q"].shape[3], x["v"].shape[3]),
                      dtype=torch.float32, device=dev)
     argv = [gdn.make_args(c["q"], c["k"], c["v"], c["g"], c["beta"], x["scale"], c["h0"], cu_dev, cu_host,
-                          64, o, fs, a.cp, a.cp_segment_chunks) for c in copies]
+                          64, o, fs, cp, cp_segment_chunks) for c in copies]
     nbytes = gdn.workspace_bytes(argv[0])
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
@@ -320,7 +368,7 @@ def main():
     hip = hip_runtime()
     n_ev = len(gdn.STAGES) + 1
     events = []
-    for _ in range(a.steps):
+    for _ in range(steps):
         arr = (ctypes.c_void_p * n_ev)()
         for j in range(n_ev):
             ev = ctypes.c_void_p()
@@ -329,12 +377,12 @@ def main():
             arr[j] = ev.value
         events.append(arr)
 
-    for i in range(a.warmup):
+    for i in range(warmup):
         gdn.fwd_raw(argv[i % len(argv)], ws.data_ptr(), ws.numel(), stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ran = []
-    for i in range(a.steps):
+    for i in range(steps):
         ran.append(gdn.fwd_timed_raw(argv[i % len(argv)], ws.data_ptr(), ws.numel(), stream, events[i]))
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
@@ -348,7 +396,7 @@ def main():
             ms = ctypes.c_float()
             if hip.hipEventElapsedTime(ctypes.byref(ms), arr[prev], arr[j + 1]) != 0:
                 raise RuntimeError("hipEventElapsedTime failed")
-            stage_ms[s] += ms.value / a.steps
+            stage_ms[s] += ms.value / steps
             prev = j + 1
         for j in range(n_ev):
             hip.hipEventDestroy(arr[j])
@@ -358,17 +406,17 @@ def main():
     alg_bytes_dom = stage_algorithmic_bytes(dominant, x, esz, plan)
     t_dom = stage_ms[dominant] * 1e-3
     achieved = alg_bytes_dom / t_dom / 1e9
-    ms_step = elapsed / a.steps * 1e3
-    value = x["tokens"] * a.steps / elapsed
+    ms_step = elapsed / steps * 1e3
+    value = x["tokens"] * steps / elapsed
     t_bound = max(alg_bytes / (HBM_PEAK_GBS * 1e9), algorithmic_flops(x) / (BF16_PEAK_TFLOPS * 1e12))
     rec = {
-        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
-        "warmup": a.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": {2: "bf16", 4: "f32"}[esz], "data": "synthetic",
         "config": {"workload": w.name, "B": w.B if not w.n_seqs else 1, "T_total": x["tokens"],
                    "seqs": x["n_seqs"], "H_qk": w.hqk, "H_v": w.H, "d_k": w.D, "d_v": w.D,
                    "chunk": 64, "gate": w.gate, "h0": w.h0, "input_copies": len(copies),
-                   "cp": a.cp, "cp_ran": bool((ran[-1] >> gdn.STAGES.index("cp_pre")) & 1),
+                   "cp": cp, "cp_ran": bool((ran[-1] >> gdn.STAGES.index("cp_pre")) & 1),
                    "cp_segment_chunks": plan["segment_chunks"] if plan["cp"] else None,
                    "value_cols_per_group": plan["value_cols_per_group"], "pieces": plan["pieces"]},
         "roofline": {"bound": "hbm", "kernel": dominant, "alg_bytes": alg_bytes_dom, "achieved": achieved,
@@ -378,9 +426,8 @@ def main():
         "whole_op": {"alg_bytes": alg_bytes, "alg_flops": algorithmic_flops(x), "t_bound_ms": t_bound * 1e3,
                      "roofline_frac": t_bound / (ms_step * 1e-3)},
     }
-    if not a.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(x, a.cpu_threads)
-    print(json.dumps(rec), flush=True)
+    del copies, argv, ws, o, fs
+    return rec, x
 
 
 if __name__ == "__main__":

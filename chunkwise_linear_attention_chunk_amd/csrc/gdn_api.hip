@@ -72,6 +72,23 @@ hipError_t side_stream(hipStream_t *out) {
     return hipSuccess;
 }
 
+// Compute units of the current device, queried once per device; the MI355X count when no device
+// answers (planning is host-only and also runs where no GPU is present).
+int device_cus() {
+    static std::mutex mu;
+    static int cus[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return gdn::kDefaultCUs;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!cus[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            return gdn::kDefaultCUs;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
 int64_t count_segments(const gdn_fwd_args *a, int sl) {
     auto segs = [&](int64_t len) {
         const int64_t nc = (len + gdn::kChunk - 1) / gdn::kChunk;
@@ -180,7 +197,7 @@ gdn_status validate_and_plan(const gdn_fwd_args *a, Plan *pl) {
         // segments so the main pass fills the CUs once (one recurrence workgroup per CU; the
         // pre-process, with no output waves, then also runs in one round): fewer segments leave
         // CUs idle, more add rounds to both passes and serial steps to the fix-up
-        const int64_t want = std::max<int64_t>(2, gdn::kCUs / std::max<int64_t>(chains, 1));
+        const int64_t want = std::max<int64_t>(2, device_cus() / std::max<int64_t>(chains, 1));
         sl = (int)std::max<int64_t>(4, (max_nc + want - 1) / want);
     }
     bool cp = false;
@@ -330,6 +347,7 @@ gdn_status run_fwd(const gdn_fwd_args *a, void *workspace, size_t workspace_byte
         cp.kg = ws + pl.off_kg; cp.kd = ws + pl.off_kd; cp.qg = ws + pl.off_qg;
     }
     cp.n_slices = pl.n_slices;
+    cp.n_cus = device_cus();
 
     if (pl.pieces > 1) {
         // pieces: the per-chunk kernel of range j runs on a side stream, the recurrence over range

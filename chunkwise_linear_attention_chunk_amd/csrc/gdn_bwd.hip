@@ -603,14 +603,15 @@ __global__ __launch_bounds__(kBwT) void bwd_states_kda_kernel(BwdParams p) {
     }
 }
 
-// ---- scale P of every (chunk, value head), per-channel factors inside the sum.  The factor
-//      e^{G_id - G_jd} is split at the first row r of key j's 16-row block (r <= j <= i):
-//      e^{G_id - G_rd} <= 1 goes with q_i, e^{G_rd - G_jd} (a decay over at most 15 tokens) with k_j,
-//      so one exponential per operand element replaces one per term of the sum.
+// ---- scale P of every (chunk, value head), per-channel factors inside the sum.  For a query below
+//      key j's 16-row block the factor e^{G_id - G_jd} is split at the block's last row r
+//      (j <= r < i), both parts at most 1, so one exponential per operand element replaces one per
+//      term of the sum; pairs inside one block take the whole factor per term.  No factor exceeds 1,
+//      whatever the gates.
 template <typename T, int DK>
 __global__ __launch_bounds__(kBwT) void bwd_p_kda_kernel(BwdParams p) {
     constexpr int NT = kBwT;
-    __shared__ float sK[64][DK + 1], sQ[64][DK + 1], sG[64][DK + 1], sQx[64][DK + 1];
+    __shared__ float sK[64][DK + 1], sQ[64][DK + 1], sG[64][DK + 1], sQx[64][DK + 1], sKx[16][DK + 1];
     const int tid = threadIdx.x;
     const int ci = blockIdx.x / p.H_v, h = blockIdx.x - ci * p.H_v;
     const int hq = h / (p.H_v / p.H_qk);
@@ -621,24 +622,31 @@ __global__ __launch_bounds__(kBwT) void bwd_p_kda_kernel(BwdParams p) {
     load_rows<DK, T, NT>(&sG[0][0], DK + 1, static_cast<const T *>(p.g) + (int64_t)h * DK, cinfo.tok0, cinfo.nv,
                          (int64_t)p.H_v * DK, 0);
     cumsum_rows<DK>(&sG[0][0], DK + 1);
-    for (int idx = tid; idx < 64 * DK; idx += NT) {       // k_j e^{G_r - G_j}, r = 16 floor(j / 16)
-        const int j = idx / DK, d = idx % DK;
-        sK[j][d] *= __expf(sG[j & ~15][d] - sG[j][d]);
-    }
     float *P = p.pmat + ((int64_t)ci * p.H_v + h) * 4096;
     for (int J = 0; J < 4; ++J) {                         // keys of block J: rows i >= 16 J
-        __syncthreads();                                  // sG, sK ready; sQx free
-        for (int idx = tid; idx < (64 - 16 * J) * DK; idx += NT) {
-            const int i = 16 * J + idx / DK, d = idx % DK;
-            sQx[i][d] = sQ[i][d] * __expf(sG[i][d] - sG[16 * J][d]);
+        // Queries below the block and the block's keys are split at its last row r, which lies
+        // between every such pair: q_i e^{G_i - G_r} and k_j e^{G_r - G_j}, both at most their row.
+        // Pairs inside the block have no such row and take their factor e^{G_i - G_j} <= 1 whole.
+        const int r = 16 * J + 15;
+        __syncthreads();                                  // sG ready; sQx, sKx free
+        for (int idx = tid; idx < (48 - 16 * J) * DK; idx += NT) {
+            const int i = 16 * J + 16 + idx / DK, d = idx % DK;
+            sQx[i][d] = sQ[i][d] * __expf(sG[i][d] - sG[r][d]);
+        }
+        for (int idx = tid; idx < 16 * DK; idx += NT) {
+            const int jj = idx / DK, d = idx % DK;
+            sKx[jj][d] = sK[16 * J + jj][d] * __expf(sG[r][d] - sG[16 * J + jj][d]);
         }
         __syncthreads();
         for (int idx = tid; idx < 64 * 16; idx += NT) {
-            const int i = idx / 16, j = 16 * J + idx % 16;
+            const int i = idx / 16, jj = idx % 16, j = 16 * J + jj;
             if (i < 16 * J) continue;                     // above the diagonal: written below
             float s = 0.f;
-            if (j <= i)
-                for (int d = 0; d < DK; ++d) s += sQx[i][d] * sK[j][d];
+            if (i > r) {
+                for (int d = 0; d < DK; ++d) s += sQx[i][d] * sKx[jj][d];
+            } else if (j <= i) {
+                for (int d = 0; d < DK; ++d) s += sQ[i][d] * sK[j][d] * __expf(sG[i][d] - sG[j][d]);
+            }
             P[i * 64 + j] = j <= i ? p.scale * s : 0.f;
         }
     }
@@ -929,8 +937,11 @@ __global__ __launch_bounds__(kBwT) void bwd_chunk_kda_a_kernel(BwdParams p) {
         const float dk_d = __expf(gC - Gr[e]) * accD[e];
         dqo[e] = dq_o;
         dko[e] = dk_x + dk_d;
-        dGo[e] = qv * dq_o + kv * dk_x - kv * dk_d;
-        dgcs += kv * dk_d;
+        // the last valid row's factor e^{G_C - G_C} = 1 has no gate gradient: its - (own row) and
+        // + (G_C) terms would cancel exactly, so neither is added (see the diagonal pairs of (b))
+        const float dgd = row == nv - 1 ? 0.f : kv * dk_d;
+        dGo[e] = qv * dq_o + kv * dk_x - dgd;
+        dgcs += dgd;
     }
     atomicAdd(&sdgc[col], dgcs);
     __syncthreads();
@@ -1000,20 +1011,24 @@ __global__ __launch_bounds__(kBwT) void bwd_chunk_kda_b_kernel(BwdParams p) {
         const float Gr = sG[r][col], qr = sQ[r][col], kr = sK[r][col];
         float aq = 0.f, ar = 0.f, ap = 0.f, al = 0.f;
         for (int t = 0; t < 64; ++t) {
-            if (t <= r) {                                  // r as the row: e^{G_r - G_t}
+            if (t < r) {                                   // r as the row: e^{G_r - G_t}
                 const float f = __expf(Gr - sG[t][col]);
                 aq += sdP[r][t] * sK[t][col] * f;
-                if (t < r) ar += sdL[r][t] * sK[t][col] * f;
+                ar += sdL[r][t] * sK[t][col] * f;
             }
-            if (t >= r) {                                  // r as the column: e^{G_t - G_r}
+            if (t > r) {                                   // r as the column: e^{G_t - G_r}
                 const float f = __expf(sG[t][col] - Gr);
                 ap += sdP[t][r] * sQ[t][col] * f;
-                if (t > r) al += sdL[t][r] * sb[t] * sK[t][col] * f;
+                al += sdL[t][r] * sb[t] * sK[t][col] * f;
             }
         }
+        // the diagonal pair (t = r) has the factor e^0 = 1: it enters dq and dk, but its two gate
+        // terms (+ as the row, - as the column) cancel exactly, so it is left out of dG rather than
+        // added twice with opposite signs (which loses the small dG of steep gates to rounding)
+        const float dpd = sdP[r][r];
         const float dk_lrow = sb[r] * ar;
-        dqp[e] = aq;
-        dkb[e] = ap + dk_lrow + al;
+        dqp[e] = aq + dpd * kr;
+        dkb[e] = ap + dpd * qr + dk_lrow + al;
         dGb[e] = qr * aq + kr * dk_lrow - kr * (ap + al);
         float x = kr * ar;                                  // dbeta from L: sum_d k_rd R_rd
         for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);

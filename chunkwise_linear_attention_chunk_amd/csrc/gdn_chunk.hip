@@ -979,7 +979,7 @@ static hipError_t launch_rec(int dtype, int D_k, int BV, const ChunkParams &p, h
             // enough workgroups for two per CU (large batches, many packed sequences): the one-buffer
             // build, whose 75 KiB of LDS and 256 registers per wave let two workgroups share a CU and
             // fill each other's waits (its own loads then do not overlap its work)
-            if (grid.x >= 2u * (unsigned)kCUs) { GDN_CHUNK_CASE(1, bf16, 128, 2, 1) }
+            if (grid.x >= 2u * (unsigned)p.n_cus) { GDN_CHUNK_CASE(1, bf16, 128, 2, 1) }
         }
         GDN_CHUNK_CASE(1, bf16, 128, 2, 2)
         GDN_CHUNK_CASE(1, bf16, 128, 1, 2)

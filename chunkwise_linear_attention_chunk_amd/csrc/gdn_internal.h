@@ -7,7 +7,7 @@
 namespace gdn {
 
 constexpr int kChunk = 64;  // tokens per chunk
-constexpr int kCUs = 256;   // MI355X compute units
+constexpr int kDefaultCUs = 256;   // MI355X compute units: the plan's assumption when no device answers
 constexpr int GDN_GATE_CHANNEL_K = 1;  // gate kind of per-channel (KDA) gates, as in gdn.h
 
 // Per (chunk, head) gate block written by the per-chunk kernel, read by the recurrence: fp32 rows
@@ -154,6 +154,7 @@ struct ChunkParams {
     // seg_start; seg_next (nullable) receives a non-last segment's end state as the next one's start
     int seg_only;
     float *seg_next;
+    int n_cus;              // compute units of the device the launch goes to
 };
 
 // chunk ci of the per-chunk grid: every chunk, or the chunks of one piece of a batched input

@@ -333,10 +333,17 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraParams p) {
 // (r = last row of the column block for tiles below the diagonal, the first row of the block on
 // it), so both operand factors are decays over at most 15 tokens or at most 1:
 //   left_i = x_i (.) 2^(G_i - G_r) <= |x_i|,   right_j = k_j (.) 2^(G_r - G_j).
+// A diagonal tile whose gates decay by more than 2^-64 across its 16 rows in some channel (where
+// right_j could overflow and left_i underflow) forms each pair's factor 2^(G_i - G_j) <= 1 whole, in
+// fp32 on the vector ALU, so no gate value can produce inf or NaN.
 // P's operands are carried as hi/lo bf16 pairs (three MFMAs per block); A_raw's are rounded once.
 // ------------------------------------------------------------------------------------------
 // PRO: some part of the prologue is on (q/k L2 norm, gate activation, sigma(beta)); the template
 // flag keeps all of it out of the plain build, whose timing it would otherwise change
+// Largest decay (in log2 units) across a diagonal 16-row block for which the split factors of that
+// block are used: the key factor is then at most 2^64 and the query/key factor at least 2^-64.
+constexpr float kMaxRange = 64.f;
+
 template <typename T, int DK, bool PRO>
 __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
     constexpr int VEC = Vec16<T>::N;
@@ -538,8 +545,43 @@ __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
         const float qmask = i < nv ? (PRO ? sRq[i] : 1.f) : 0.f;   // with the prologue: Q row i's L2-norm factor
         const float rki = PRO ? sRk[i] : 1.f, rkj = PRO ? sRk[j] : 1.f;
         f32x4 aa = {0.f, 0.f, 0.f, 0.f}, pa = {0.f, 0.f, 0.f, 0.f};
+        // A tile on the diagonal has no reference row that lies between every pair's two tokens: its
+        // key factor 2^(G_r - G_j) grows across the block.  If some channel decays by more than
+        // 2^-kMaxRange across the block's 16 rows, the split factors could leave the fp32 range
+        // (inf times 0), so every pair's factor 2^(G_i - G_j) <= 1 is then formed whole instead.
+        bool whole = false;
+        if (I == J) {
+            float range = 0.f;
+#pragma unroll
+            for (int d = lane; d < DK; d += 64) range = fmaxf(range, sG[16 * I * GP + d] - sG[(16 * I + 15) * GP + d]);
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) range = fmaxf(range, __shfl_xor(range, off, 64));
+            whole = range > kMaxRange;
+        }
+        if (whole) {
+            // lane: rows i = 16 I + 4 grp + rr, column j = 16 I + l16 (the accumulator layout)
+#pragma unroll 1
+            for (int rr = 0; rr < 4; ++rr) {
+                const int ii = 16 * I + 4 * grp + rr;
+                const T *qi = q + ((int64_t)(t0 + min(ii, last)) * p.H_qk + hq) * DK;
+                float sa = 0.f, sp = 0.f;
+                if (j <= ii) {
+#pragma unroll 4
+                    for (int d = 0; d < DK; ++d) {
+                        const float e = fast_exp2(sG[ii * GP + d] - sG[j * GP + d]);   // <= 1
+                        const float kj = to_f32(sK[j * KP + d]) * e;
+                        sa += to_f32(sK[ii * KP + d]) * kj;
+                        sp += to_f32(qi[d]) * kj;
+                    }
+                }
+                const float qm = ii < nv ? (PRO ? sRq[ii] : 1.f) : 0.f;
+                aa[rr] = sa * (PRO ? sRk[ii] : 1.f) * rkj;
+                pa[rr] = sp * qm * rkj;
+            }
+        }
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
+            if (whole) break;
             const int d0 = 32 * kb + 8 * grp;
             float kl[8], ql[8], kr[8];
 #pragma unroll

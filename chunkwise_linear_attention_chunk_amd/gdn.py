@@ -108,20 +108,62 @@ def _check(status):
         raise GdnError(status, f"{L.gdn_status_string(status).decode()}: {L.gdn_last_error().decode()}")
 
 
+def _expect(name, t, shape, dtype):
+    """Raise GdnError unless tensor t (if given) is contiguous with this shape and dtype: the C ABI
+    takes plain pointers and cannot see sizes or element types."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+        raise GdnError(GDN_ERR_INVALID_ARG, f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} "
+                                            f"(got {t.dtype} {tuple(t.shape)})")
+
+
+def check_inputs(q, k, v, g, beta, initial_state=None, cu_seqlens=None, A_log=None, dt_bias=None, o=None,
+                 final_state=None, dout=None, dht=None):
+    """Host-side shape and dtype checks of every tensor the kernels read or write (include/gdn.h
+    layouts).  Returns (B, T, H_qk, D_k, H_v, D_v, N, gate kind)."""
+    if q.dim() != 4:
+        raise GdnError(GDN_ERR_INVALID_ARG, "q must be [B, T, H_qk, D_k]")
+    if q.dtype not in (torch.float32, torch.bfloat16):
+        raise GdnError(GDN_ERR_UNSUPPORTED, f"dtype {q.dtype} (supported: float32, bfloat16)")
+    B, T, H_qk, D_k = q.shape
+    if v.dim() != 4 or tuple(v.shape[:2]) != (B, T):
+        raise GdnError(GDN_ERR_INVALID_ARG, f"v must be [B={B}, T={T}, H_v, D_v] (got {tuple(v.shape)})")
+    H_v, D_v = v.shape[2], v.shape[3]
+    if g.dim() not in (3, 4):
+        raise GdnError(GDN_ERR_INVALID_ARG, "g must be [B, T, H_v] (scalar gate) or [B, T, H_v, D_k] (per channel)")
+    gate = GATE_SCALAR if g.dim() == 3 else GATE_CHANNEL
+    if cu_seqlens is not None and (cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2
+                                   or cu_seqlens.dtype not in (torch.int32, torch.int64)):
+        raise GdnError(GDN_ERR_INVALID_ARG, "cu_seqlens must be a 1-D integer tensor of N + 1 offsets")
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    _expect("k", k, q.shape, q.dtype)
+    _expect("v", v, v.shape, q.dtype)
+    if gate == GATE_SCALAR:
+        _expect("g", g, (B, T, H_v), torch.float32)
+    else:
+        _expect("g", g, (B, T, H_v, D_k), q.dtype)
+    _expect("beta", beta, (B, T, H_v), q.dtype)
+    state = (N, H_v, D_k, D_v)
+    _expect("initial_state", initial_state, state, torch.float32)
+    _expect("final_state", final_state, state, torch.float32)
+    _expect("A_log", A_log, (H_v,), torch.float32)
+    _expect("dt_bias", dt_bias, (H_v,) if gate == GATE_SCALAR else (H_v, D_k), torch.float32)
+    if o is not None:
+        _expect("o", o, v.shape, o.dtype if o.dtype in (q.dtype, torch.float32) else q.dtype)
+    _expect("dout", dout, v.shape, q.dtype)
+    _expect("dht", dht, state, torch.float32)
+    return B, T, H_qk, D_k, H_v, D_v, N, gate
+
+
 def make_args(q, k, v, g, beta, scale=None, initial_state=None, cu_seqlens=None, cu_seqlens_cpu=None,
               chunk_size=64, o=None, final_state=None, cp_mode="auto", cp_segment_chunks=0,
               qk_l2norm=False, beta_sigmoid=False, A_log=None, dt_bias=None, gate_lower_bound=0.0,
               cp_warmup_tol=0.0):
-    """Fill a gdn_fwd_args from tensors (shapes are read, nothing is computed)."""
-    if q.dim() != 4:
-        raise GdnError(GDN_ERR_INVALID_ARG, "q must be [B, T, H_qk, D_k]")
-    B, T, H_qk, D_k = q.shape
-    H_v, D_v = v.shape[2], v.shape[3]
-    dt = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}.get(q.dtype)
-    if dt is None:
-        raise GdnError(GDN_ERR_UNSUPPORTED, f"dtype {q.dtype} (supported: float32, bfloat16)")
-    gate = GATE_SCALAR if g.dim() == 3 else GATE_CHANNEL
-    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    """Fill a gdn_fwd_args from tensors (shapes and dtypes are checked, nothing is computed)."""
+    B, T, H_qk, D_k, H_v, D_v, N, gate = check_inputs(q, k, v, g, beta, initial_state, cu_seqlens, A_log, dt_bias,
+                                                      o, final_state)
+    dt = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}[q.dtype]
     a = FwdArgs()
     a.B, a.T, a.H_qk, a.H_v, a.D_k, a.D_v = B, T, H_qk, H_v, D_k, D_v
     a.chunk_size, a.dtype, a.gate_kind = chunk_size, dt, gate
@@ -265,6 +307,7 @@ def make_bwd_args(q, k, v, g, beta, dout, grads, scale=None, initial_state=None,
             continue
         if t is None or tuple(t.shape) != tuple(shape) or t.dtype != torch.float32 or not t.is_contiguous():
             raise GdnError(GDN_ERR_INVALID_ARG, f"{n} must be a contiguous fp32 tensor of shape {tuple(shape)}")
+    check_inputs(q, k, v, g, beta, initial_state, cu_seqlens, dout=dout, dht=dht)
     f = make_args(q, k, v, g, beta, scale, initial_state, cu_seqlens, cu_seqlens_cpu)
     a = BwdArgs()
     for n in ("B", "T", "H_qk", "H_v", "D_k", "D_v", "chunk_size", "dtype", "gate_kind", "scale", "q", "k", "v", "g",

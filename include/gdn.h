@@ -82,7 +82,7 @@ typedef enum { GDN_CP_AUTO = 0, GDN_CP_OFF = 1, GDN_CP_ON = 2, GDN_CP_WARMUP = 3
 typedef struct {
     int32_t B, T;             /* batch and tokens per batch row (T = total tokens when packed) */
     int32_t H_qk, H_v;        /* query/key heads, value heads (H_v % H_qk == 0) */
-    int32_t D_k, D_v;         /* head dims: D_k == D_v in {64, 128} */
+    int32_t D_k, D_v;         /* head dims, each 64 or 128 (independently) */
     int32_t chunk_size;       /* 64 for gdn_fwd, 1 for gdn_fwd_recurrent */
     int32_t dtype;            /* gdn_dtype of q, k, v, beta, o (and a channel gate) */
     int32_t gate_kind;        /* gdn_gate_kind */

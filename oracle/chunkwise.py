@@ -57,6 +57,13 @@ def unit_lower_inverse(A_raw):
     return solve_triangular(np.eye(c) + A_raw, np.eye(c), lower=True, unit_diagonal=True)
 
 
+def wy_factors(A, bc, Kw, Vc):
+    """WY form of one chunk: W = A diag(beta) Kw and U = A diag(beta) V, Kw the gated keys
+    (diag(gamma) K, or K (.) exp(G) per channel).  FlashQLA announcement, the second step of the
+    chunk-i forward; KDA source walk-through section 3.3 (u = A (v * beta), w = A (k * beta * exp(g)))."""
+    return A @ (bc[:, None] * Kw), A @ (bc[:, None] * Vc)
+
+
 def intra_scalar(Kc, Vc, bc, gcs, erase=True):
     """One chunk, scalar gate: gcs is the chunk-local cumsum.  Returns dict of intermediates."""
     c = Kc.shape[0]
@@ -66,8 +73,9 @@ def intra_scalar(Kc, Vc, bc, gcs, erase=True):
     Gamma = np.where(lower, np.exp(np.where(lower, diff, 0.0)), 0.0)
     A_raw = np.tril(bc[:, None] * (Gamma * (Kc @ Kc.T)), -1)
     A = unit_lower_inverse(A_raw) if erase else np.eye(c)
-    W = A @ ((bc * gamma)[:, None] * Kc) if erase else np.zeros_like(Kc)
-    U = A @ (bc[:, None] * Vc)
+    W, U = wy_factors(A, bc, gamma[:, None] * Kc, Vc)
+    if not erase:
+        W = np.zeros_like(Kc)
     gC = gamma[-1]
     return dict(A_raw=A_raw, A=A, W=W, U=U, gamma=gamma, Gamma=Gamma,
                 decay=np.full(Kc.shape[1], gC), kd=(gC / gamma)[:, None] * Kc)
@@ -84,8 +92,9 @@ def intra_channel(Qc, Kc, Vc, bc, Gcs, erase=True):
     QK = np.einsum("id,jd,ijd->ij", Qc, Kc, E)
     A_raw = np.tril(bc[:, None] * KK, -1)
     A = unit_lower_inverse(A_raw) if erase else np.eye(c)
-    W = A @ (bc[:, None] * Kc * np.exp(Gcs)) if erase else np.zeros_like(Kc)
-    U = A @ (bc[:, None] * Vc)
+    W, U = wy_factors(A, bc, Kc * np.exp(Gcs), Vc)
+    if not erase:
+        W = np.zeros_like(Kc)
     GC = Gcs[-1]
     return dict(A_raw=A_raw, A=A, W=W, U=U, Aqk=np.tril(QK), qg=Qc * np.exp(Gcs),
                 decay=np.exp(GC), kd=Kc * np.exp(GC[None, :] - Gcs))

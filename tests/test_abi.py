@@ -260,3 +260,53 @@ def test_backward_gradient_shapes_are_checked_on_the_host():
     with pytest.raises(gdn.GdnError, match="dg must be"):
         gdn.make_bwd_args(t["q"], t["k"], t["v"], t["g"], t["beta"], t["v"], dict(grads, dg=torch.empty(t["beta"].shape, **f32)),
                           x["scale"])
+
+
+def _cpu_inputs(gate="scalar"):
+    import torch
+    from chunkwise_linear_attention_chunk_amd import synth
+    name = "qwen3next_bf16" if gate == "scalar" else "kda_bf16"
+    x = synth.make_inputs(synth.workload(name, B=2, H=4, T=70, h0=True, seed=1))
+    return torch, x
+
+
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+def test_binding_rejects_mismatched_inputs_before_any_call(gate):
+    # the C ABI sees only pointers, so the binding checks every tensor's shape and dtype on the host
+    torch, x = _cpu_inputs(gate)
+    q, k, v, g, beta, h0 = (x[n] for n in ("q", "k", "v", "g", "beta", "h0"))
+    gdn.make_args(q, k, v, g, beta, x["scale"], h0)                  # consistent inputs pass
+    bad = {
+        "k": dict(k=k[:, :, :, :64].contiguous()),
+        "v": dict(v=v[:, :50].contiguous()),
+        "g": dict(g=g.to(torch.bfloat16) if gate == "scalar" else g.float()),
+        "beta": dict(beta=beta.float()),
+        "initial_state": dict(h0=h0.to(torch.bfloat16)),
+    }
+    for name, over in bad.items():
+        args = {**dict(q=q, k=k, v=v, g=g, beta=beta, h0=h0), **over}
+        with pytest.raises(gdn.GdnError, match=name):
+            gdn.make_args(args["q"], args["k"], args["v"], args["g"], args["beta"], x["scale"], args["h0"])
+    with pytest.raises(gdn.GdnError, match="initial_state"):
+        gdn.make_args(q, k, v, g, beta, x["scale"], h0[:1].contiguous())
+    with pytest.raises(gdn.GdnError, match="A_log"):
+        gdn.make_args(q, k, v, g, beta, x["scale"], h0, A_log=torch.zeros(3))
+    dtb = torch.zeros(4, 128) if gate == "scalar" else torch.zeros(4)
+    with pytest.raises(gdn.GdnError, match="dt_bias"):
+        gdn.make_args(q, k, v, g, beta, x["scale"], h0, A_log=torch.zeros(4), dt_bias=dtb)
+    with pytest.raises(gdn.GdnError, match="final_state"):
+        gdn.make_args(q, k, v, g, beta, x["scale"], h0, final_state=torch.zeros(2, 4, 128, 64))
+    with pytest.raises(gdn.GdnError, match="o must be"):
+        gdn.make_args(q, k, v, g, beta, x["scale"], h0, o=torch.zeros(v.shape, dtype=torch.float16))
+
+
+def test_binding_checks_backward_inputs():
+    torch, x = _cpu_inputs()
+    q, k, v, g, beta = (x[n] for n in ("q", "k", "v", "g", "beta"))
+    f32 = dict(dtype=torch.float32)
+    grads = {"dq": torch.empty(q.shape, **f32), "dk": torch.empty(k.shape, **f32), "dv": torch.empty(v.shape, **f32),
+             "dg": torch.empty(g.shape, **f32), "dbeta": torch.empty(beta.shape, **f32)}
+    with pytest.raises(gdn.GdnError, match="dout"):
+        gdn.make_bwd_args(q, k, v, g, beta, v.float(), grads, x["scale"])
+    with pytest.raises(gdn.GdnError, match="dht"):
+        gdn.make_bwd_args(q, k, v, g, beta, v, grads, x["scale"], dht=torch.zeros(2, 4, 64, 128))

@@ -143,8 +143,11 @@ def test_wy_derivation_identity():
 def test_golden_u_expansion():
     d = json.load(open(os.path.join(GOLDEN, "wy_u_4x4.json")))
     A, b, v = (np.array(d[x], dtype=float) for x in ("A", "beta", "v"))
-    # U = A diag(beta) V as the chunk evaluator forms it (A given, so no inverse involved)
-    np.testing.assert_array_equal(A @ (b[:, None] * v), np.array(d["expected_u"], dtype=float))
+    # U = A diag(beta) V through the chunk evaluator's WY step (A given, so no inverse involved); the
+    # same step with the values as gated keys gives W, which must equal U then
+    W, U = cw.wy_factors(A, b, v, v)
+    np.testing.assert_array_equal(U, np.array(d["expected_u"], dtype=float))
+    np.testing.assert_array_equal(W, np.array(d["expected_u"], dtype=float))
 
 
 @pytest.mark.parametrize("gate", ["scalar", "channel"])
