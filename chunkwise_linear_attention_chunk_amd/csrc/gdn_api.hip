@@ -159,7 +159,7 @@ gdn_status validate_args(const gdn_fwd_args *a, int chunk) {
     return GDN_OK;
 }
 
-gdn_status validate_and_plan(const gdn_fwd_args *a, Plan *pl) {
+gdn_status validate_and_plan(const gdn_fwd_args *a, Plan *pl, bool allow_pieces = true) {
     const gdn_status st = validate_args(a, gdn::kChunk);
     if (st != GDN_OK) return st;
     const bool packed = a->cu_seqlens_dev != nullptr;
@@ -209,7 +209,7 @@ gdn_status validate_and_plan(const gdn_fwd_args *a, Plan *pl) {
     // pieces: a batched input without CP is cut into P ranges of chunks (segments run one after
     // another, each from the previous one's end state), so that the per-chunk kernel of range j + 1
     // overlaps the recurrence over range j; GDN_PIECES overrides P for experiments
-    if (!packed && !cp) {
+    if (!packed && !cp && allow_pieces) {
         const int want = std::max(1, env_int("GDN_PIECES", kDefaultPieces));
         if (want > 1 && max_nc >= 2 * (int64_t)want) {
             pl->seg_chunks = (int)((max_nc + want - 1) / want);
@@ -280,9 +280,9 @@ extern "C" gdn_status gdn_fwd_plan(const gdn_fwd_args *a, gdn_plan_info *info) {
 namespace {
 
 gdn_status run_fwd(const gdn_fwd_args *a, void *workspace, size_t workspace_bytes, void *stream,
-                   void *const *events, uint32_t *stages_run) {
+                   void *const *events, uint32_t *stages_run, bool allow_pieces = true) {
     Plan pl;
-    const gdn_status st = validate_and_plan(a, &pl);
+    const gdn_status st = validate_and_plan(a, &pl, allow_pieces);
     if (st != GDN_OK) return st;
     if (!workspace && pl.bytes) return fail(GDN_ERR_WORKSPACE, "workspace is NULL (needs %zu bytes)", pl.bytes);
     if (workspace_bytes < pl.bytes)
@@ -430,6 +430,48 @@ gdn_status run_fwd(const gdn_fwd_args *a, void *workspace, size_t workspace_byte
 
 extern "C" gdn_status gdn_fwd(const gdn_fwd_args *a, void *workspace, size_t workspace_bytes, void *stream) {
     return run_fwd(a, workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+// ---- allocation-free entry point: the workspace is a static device array, one copy per GPU.
+// Host code never passes the array's name to a kernel or a copy (on the host it names a host-side
+// stand-in, not device memory): it uses the device address hipGetSymbolAddress returns, looked up
+// once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+hipError_t scratch_address(void **out) {
+    static std::mutex mu;
+    static void *addr[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" gdn_status gdn_fwd_noalloc(const gdn_fwd_args *a, void *stream) {
+    Plan pl;
+    const gdn_status st = validate_and_plan(a, &pl, /*allow_pieces=*/false);
+    if (st != GDN_OK) return st;
+    if (pl.bytes > GDN_NOALLOC_SCRATCH_BYTES)
+        return fail(GDN_ERR_WORKSPACE, "these arguments need %zu bytes of workspace; the allocation-free entry point "
+                    "holds %zu", pl.bytes, (size_t)GDN_NOALLOC_SCRATCH_BYTES);
+    if (a->N == 0) return GDN_OK;
+    void *ws = nullptr;
+    const hipError_t e = scratch_address(&ws);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "scratch address: %s", hipGetErrorString(e));
+    return run_fwd(a, ws, GDN_NOALLOC_SCRATCH_BYTES, stream, nullptr, nullptr, /*allow_pieces=*/false);
 }
 
 extern "C" gdn_status gdn_fwd_timed(const gdn_fwd_args *a, void *workspace, size_t workspace_bytes, void *stream,

@@ -17,8 +17,9 @@ GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP
 DTYPE_F32, DTYPE_BF16 = 0, 1
 GATE_SCALAR, GATE_CHANNEL = 0, 1
 CP_MODES = {"auto": 0, "off": 1, "on": 2, "warmup": 3}
-EXPORTED = ("gdn_fwd", "gdn_fwd_timed", "gdn_fwd_workspace_bytes", "gdn_fwd_plan", "gdn_fwd_recurrent",
-            "gdn_bwd", "gdn_bwd_workspace_bytes", "gdn_status_string", "gdn_last_error")
+EXPORTED = ("gdn_fwd", "gdn_fwd_timed", "gdn_fwd_workspace_bytes", "gdn_fwd_plan", "gdn_fwd_noalloc",
+            "gdn_fwd_recurrent", "gdn_bwd", "gdn_bwd_workspace_bytes", "gdn_status_string", "gdn_last_error")
+NOALLOC_SCRATCH_BYTES = 64 << 20   # GDN_NOALLOC_SCRATCH_BYTES of include/gdn.h
 STAGES = ("plan", "intra", "cp_pre", "cp_fix", "chunk")  # order of gdn_fwd_timed's stages
 
 
@@ -88,6 +89,8 @@ def lib():
         L.gdn_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.gdn_bwd.argtypes = [ctypes.POINTER(BwdArgs), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         L.gdn_bwd.restype = ctypes.c_int
+        L.gdn_fwd_noalloc.argtypes = [ctypes.POINTER(FwdArgs), ctypes.c_void_p]
+        L.gdn_fwd_noalloc.restype = ctypes.c_int
         L.gdn_fwd_recurrent.argtypes = [ctypes.POINTER(FwdArgs), ctypes.c_void_p]
         L.gdn_fwd_recurrent.restype = ctypes.c_int
         L.gdn_status_string.argtypes = [ctypes.c_int]
@@ -206,6 +209,12 @@ def fwd_raw(args, workspace, workspace_bytes_, stream):
     """Call gdn_fwd with a prepared FwdArgs, a workspace pointer (int) and a stream handle (int)."""
     _check(lib().gdn_fwd(ctypes.byref(args), ctypes.c_void_p(workspace), ctypes.c_size_t(workspace_bytes_),
                          ctypes.c_void_p(stream)))
+
+
+def fwd_noalloc_raw(args, stream):
+    """Call gdn_fwd_noalloc (no workspace argument: the library's static device scratch) with a
+    prepared FwdArgs and a stream handle (int)."""
+    _check(lib().gdn_fwd_noalloc(ctypes.byref(args), ctypes.c_void_p(stream)))
 
 
 def fwd_timed_raw(args, workspace, workspace_bytes_, stream, events):

@@ -162,6 +162,23 @@ enum {
 gdn_status gdn_fwd_timed(const gdn_fwd_args *a, void *workspace, size_t workspace_bytes, void *stream,
                          void *const *events, uint32_t *stages_run);
 
+/* Allocation-free form of gdn_fwd, for callers that cannot allocate device memory or call
+ * hipMalloc at the point of the call (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments, validation, results and stream semantics as gdn_fwd, but
+ * no workspace argument: the workspace gdn_fwd would take is a static device array inside the
+ * library of GDN_NOALLOC_SCRATCH_BYTES bytes, one copy per GPU, held from the first call on that
+ * GPU until the process ends (its address is looked up on that first call, with the caller's
+ * device current).  The call allocates nothing: no device or host memory, no streams, no events
+ * (the chunk-range pieces that gdn_fwd may use on a side stream are never used here).
+ * Errors: as gdn_fwd; GDN_ERR_WORKSPACE, with nothing enqueued, when the workspace these arguments
+ * need (gdn_fwd_workspace_bytes(a)) exceeds GDN_NOALLOC_SCRATCH_BYTES.
+ * Concurrency: every call on one GPU uses that GPU's one array, so calls whose work overlaps in
+ * time on one GPU (different streams, or different host threads without ordering) race and give
+ * undefined results; calls ordered on one stream are safe.  The array keeps the last call's
+ * contents; no call depends on them. */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+gdn_status gdn_fwd_noalloc(const gdn_fwd_args *a, void *stream);
+
 /* Token-by-token forward (the fused recurrent form, chunk size 1; Flash Linear Attention page,
  * section 8): the decode path, for sequences of a few tokens (a chunked forward of fewer than
  * about 64 tokens pays its launch and intra-chunk overheads for nothing).  Same operation,

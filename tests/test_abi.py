@@ -262,6 +262,29 @@ def test_backward_gradient_shapes_are_checked_on_the_host():
                           x["scale"])
 
 
+def test_noalloc_entry_validates_and_bounds_its_scratch():
+    # gdn_fwd_noalloc validates like gdn_fwd and rejects work whose workspace exceeds the static
+    # scratch array, before touching the GPU (no launch, no scratch lookup)
+    L = gdn.lib()
+    a = _args(chunk_size=48)
+    assert L.gdn_fwd_noalloc(ctypes.byref(a), None) == gdn.GDN_ERR_INVALID_ARG
+    assert "power of two" in L.gdn_last_error().decode()
+    big = _args(B=16, N=16, T=8192, H_qk=16, H_v=16, cp_mode=gdn.CP_MODES["off"])
+    need = gdn.workspace_bytes(big)
+    assert need > gdn.NOALLOC_SCRATCH_BYTES
+    assert L.gdn_fwd_noalloc(ctypes.byref(big), None) == gdn.GDN_ERR_WORKSPACE
+    msg = L.gdn_last_error().decode()
+    assert str(need) in msg and str(gdn.NOALLOC_SCRATCH_BYTES) in msg
+    # the Qwen3-Next-shaped workload fits
+    assert gdn.workspace_bytes(_args(B=4, N=4, T=4096, H_qk=16, H_v=16)) <= gdn.NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define GDN_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == gdn.NOALLOC_SCRATCH_BYTES
+
+
 def _cpu_inputs(gate="scalar"):
     import torch
     from chunkwise_linear_attention_chunk_amd import synth
