@@ -175,46 +175,6 @@ struct RecLds {
     static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
-// pi-order operand of a swizzled tile row: elements [32kb + 4grp, +4) and [32kb + 16 + 4grp, +4).
-template <typename T, int GPR>
-__device__ __forceinline__ Frag<T> ldpi_tile(const unsigned char *tile, int row, int kb) {
-    const int grp = (threadIdx.x & 63) >> 4;
-    const int c0 = 32 * kb + 4 * grp, c1 = c0 + 16;
-    Frag<T> f;
-    if constexpr (sizeof(T) == 2) {
-        const bf16x4 a = *reinterpret_cast<const bf16x4 *>(tile + tile_off<GPR, 2>(row, c0));
-        const bf16x4 b = *reinterpret_cast<const bf16x4 *>(tile + tile_off<GPR, 2>(row, c1));
-        f.v = bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-    } else {
-        const float4 a = *reinterpret_cast<const float4 *>(tile + tile_off<GPR, 4>(row, c0));
-        const float4 b = *reinterpret_cast<const float4 *>(tile + tile_off<GPR, 4>(row, c1));
-        f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
-        f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
-    }
-    return f;
-}
-// pi-order column operand of a K-shaped tile (the K^T operand of the state update): row d, tokens
-// 32kb + 4grp + r and 32kb + 16 + 4grp + r.
-template <typename T, int GPR>
-__device__ __forceinline__ Frag<T> ldpi_col_tile(const unsigned char *tile, int d0, int kb) {
-    const int lane = threadIdx.x & 63, grp = lane >> 4, j = lane & 15;
-    Frag<T> f;
-    if constexpr (sizeof(T) == 2) {
-        // transposed reads: lane j = 4e + q of the group points at K[t_e][d0 + 4q .. + 3]
-        const int e = j >> 2, q = j & 3;
-        const int t0 = 32 * kb + 4 * grp + e;
-        const bf16x4 a = lds_read_tr16(tile + tile_off<GPR, 2>(t0, d0 + 4 * q));
-        const bf16x4 b = lds_read_tr16(tile + tile_off<GPR, 2>(t0 + 16, d0 + 4 * q));
-        f.v = bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-    } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int t = 32 * kb + (e < 4 ? 4 * grp + e : 16 + 4 * grp + e - 4);
-            f.v[e] = *reinterpret_cast<const float *>(tile + tile_off<GPR, 4>(t, d0 + j));
-        }
-    }
-    return f;
-}
 // V[16m + 4grp + r][col], r = 0..3, from the swizzled V-slice tile (col = this lane's column).
 template <typename T, int GPR>
 __device__ __forceinline__ void ld_vcol4(const unsigned char *tile, int m, int col0, float *v) {
