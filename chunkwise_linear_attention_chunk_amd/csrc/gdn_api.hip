@@ -41,6 +41,7 @@ struct Plan {
     int n_slices = 0;
     bool cp = false;          // in-GPU context parallelism
     bool warm = false;        // its warmup form (no S*, M, fix-up)
+    bool xyz = false;         // exact form: the X/Y/Z pre-process (else the chain form)
     int pieces = 1;           // batched input without CP: chunk-range pieces (per-chunk kernel of the
                               // next piece on a side stream while the recurrence runs this one)
     int seg_chunks = 0;       // segment length in chunks (one segment per sequence without CP)
@@ -129,6 +130,9 @@ gdn_status validate_args(const gdn_fwd_args *a, int chunk) {
     if (a->o_dtype != a->dtype && a->o_dtype != GDN_DTYPE_F32)
         return fail(GDN_ERR_INVALID_ARG, "o_dtype %d must equal dtype %d or be fp32", a->o_dtype, a->dtype);
     if (a->cp_mode < GDN_CP_AUTO || a->cp_mode > GDN_CP_WARMUP) return fail(GDN_ERR_INVALID_ARG, "bad cp_mode %d", a->cp_mode);
+    if (a->cp_form < GDN_CP_FORM_AUTO || a->cp_form > GDN_CP_FORM_XYZ) return fail(GDN_ERR_INVALID_ARG, "bad cp_form %d", a->cp_form);
+    if (a->cp_form == GDN_CP_FORM_XYZ && (a->dtype != GDN_DTYPE_BF16 || a->gate_kind != GDN_GATE_SCALAR))
+        return fail(GDN_ERR_UNSUPPORTED, "cp_form XYZ takes bf16 inputs with a scalar gate");
     if (!(a->cp_warmup_tol >= 0.f && a->cp_warmup_tol < 1.f))
         return fail(GDN_ERR_INVALID_ARG, "cp_warmup_tol must be in [0, 1)");
     if ((a->qk_l2norm != 0 && a->qk_l2norm != 1) || (a->beta_sigmoid != 0 && a->beta_sigmoid != 1))
@@ -217,6 +221,14 @@ gdn_status validate_and_plan(const gdn_fwd_args *a, Plan *pl, bool allow_pieces 
         }
     }
     pl->total_segs = count_segments(a, pl->seg_chunks);
+    // the X/Y/Z pre-process (one workgroup per segment and head, S* and M together) where there
+    // are enough (segment, head) pairs to fill the chip; the chain form (a workgroup per 32
+    // virtual columns) for fewer, longer segments, where it measured faster
+    if (cp && !pl->warm) {
+        const bool can = a->dtype == GDN_DTYPE_BF16 && a->gate_kind == GDN_GATE_SCALAR;
+        pl->xyz = a->cp_form == GDN_CP_FORM_XYZ ||
+                  (a->cp_form == GDN_CP_FORM_AUTO && can && pl->total_segs * a->H_v >= device_cus());
+    }
     if (pl->total_segs * a->H_v > INT32_MAX / 64) return fail(GDN_ERR_UNSUPPORTED, "too many segments");
 
     const size_t esz = a->dtype == GDN_DTYPE_BF16 ? 2 : 4;
@@ -274,6 +286,7 @@ extern "C" gdn_status gdn_fwd_plan(const gdn_fwd_args *a, gdn_plan_info *info) {
     info->value_cols_per_group = pl.BV;
     info->pieces = pl.pieces;
     info->workspace_bytes = pl.bytes;
+    info->cp_form = pl.cp && !pl.warm ? (pl.xyz ? GDN_CP_FORM_XYZ : GDN_CP_FORM_CHAIN) : 0;
     return GDN_OK;
 }
 
@@ -409,14 +422,19 @@ gdn_status run_fwd(const gdn_fwd_args *a, void *workspace, size_t workspace_byte
         cp.seg_sstar = reinterpret_cast<float *>(ws + pl.off_sstar);
         cp.seg_m = reinterpret_cast<float *>(ws + pl.off_m);
         cp.seg_start = reinterpret_cast<float *>(ws + pl.off_start);
-        gdn::ChunkParams pre = cp;
-        pre.n_slices = (a->D_v + a->D_k) / pl.BV;
-        e = gdn::launch_cp_pre(a->dtype, a->D_k, pl.BV, a->gate_kind, pre, s);
+        const bool xyz = pl.xyz;
+        if (xyz) {
+            e = gdn::launch_cp_pre_xyz(a->D_k, cp, s);
+        } else {
+            gdn::ChunkParams pre = cp;
+            pre.n_slices = (a->D_v + a->D_k) / pl.BV;
+            e = gdn::launch_cp_pre(a->dtype, a->D_k, pl.BV, a->gate_kind, pre, s);
+        }
         if (e != hipSuccess) return done(fail(GDN_ERR_HIP, "cp pre-process launch: %s", hipGetErrorString(e)));
         if ((e = mark(GDN_STAGE_CP_PRE)) != hipSuccess) return done(fail(GDN_ERR_HIP, "event: %s", hipGetErrorString(e)));
         gdn::FixParams fp{segs, seq, a->T, a->N, a->H_v, a->D_v, pl.seg_chunks, (int)pl.total_segs, a->h0, cp.seg_sstar, cp.seg_m,
                           reinterpret_cast<float *>(ws + pl.off_start)};
-        e = gdn::launch_cp_fix(a->dtype, a->D_k, fp, s);
+        e = xyz ? gdn::launch_cp_fix_xyz(a->D_k, fp, s) : gdn::launch_cp_fix(a->dtype, a->D_k, fp, s);
         if (e != hipSuccess) return done(fail(GDN_ERR_HIP, "cp fix-up launch: %s", hipGetErrorString(e)));
         if ((e = mark(GDN_STAGE_CP_FIX)) != hipSuccess) return done(fail(GDN_ERR_HIP, "event: %s", hipGetErrorString(e)));
     }

@@ -262,6 +262,44 @@ __device__ __forceinline__ Frag<T> ldpi_col_tile(const unsigned char *tile, int 
     }
     return f;
 }
+// ---- packed operand pairs ---------------------------------------------------------------------
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// two values rounded to nearest-even bf16, packed in one dword (one v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+// hi = bf16(x), lo = bf16(x - hi) for two values, each part packed in one dword
+__device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t &lo) {
+    hi = pk_bf16(a, b);
+    lo = pk_bf16(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
+}
+// the pair of four values (one accumulator run), two per dword
+__device__ __forceinline__ void split4(const f32x4 &x, u32x2 &hi, u32x2 &lo) {
+    uint32_t h0, l0, h1, l1;
+    split2(x[0], x[1], h0, l0);
+    split2(x[2], x[3], h1, l1);
+    hi = u32x2{h0, h1};
+    lo = u32x2{l0, l1};
+}
+// the pair of eight values as operand fragments
+__device__ __forceinline__ void split8_rne(const float *x, Frag<bf16> &h, Frag<bf16> &l) {
+    uint32_t hh[4], ll[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) split2(x[2 * e], x[2 * e + 1], hh[e], ll[e]);
+    h.v = __builtin_bit_cast(bf16x8, u32x4{hh[0], hh[1], hh[2], hh[3]});
+    l.v = __builtin_bit_cast(bf16x8, u32x4{ll[0], ll[1], ll[2], ll[3]});
+}
+
+// s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt in bits [3:0] and [15:14], expcnt and lgkmcnt left at
+// their maxima).  A wave's vector memory loads complete in issue order, so this waits for all but
+// its N most recently issued.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
+}
+
 // 16-byte vector of T: 8 bf16 or 4 fp32.
 template <typename T> struct Vec16 { static constexpr int N = 16 / sizeof(T); };
 

@@ -218,6 +218,10 @@ hipError_t launch_intra_kda(int dtype, int D_k, const IntraKdaParams &p, hipStre
 hipError_t launch_chunk(int dtype, int D_k, int BV, int gate, const ChunkParams &p, hipStream_t s);
 // mode 1: context-parallel pre-process (chain only over value and identity columns)
 hipError_t launch_cp_pre(int dtype, int D_k, int BV, int gate, const ChunkParams &p, hipStream_t s);
+// the same maps in the X/Y/Z form (scalar gate, bf16); hipErrorInvalidValue for other head widths
+// writes M as bf16 pairs in operand order, which launch_cp_fix_xyz reads
+hipError_t launch_cp_pre_xyz(int D_k, const ChunkParams &p, hipStream_t s);
+hipError_t launch_cp_fix_xyz(int D_k, const FixParams &p, hipStream_t s);
 hipError_t launch_cp_fix(int dtype, int D_k, const FixParams &p, hipStream_t s);
 hipError_t launch_warm_stats(const WarmParams &p, hipStream_t s);
 hipError_t launch_bwd(int dtype, int D_k, const BwdParams &p, hipStream_t s);

@@ -17,6 +17,7 @@ GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP
 DTYPE_F32, DTYPE_BF16 = 0, 1
 GATE_SCALAR, GATE_CHANNEL = 0, 1
 CP_MODES = {"auto": 0, "off": 1, "on": 2, "warmup": 3}
+CP_FORMS = {"auto": 0, "chain": 1, "xyz": 2}
 EXPORTED = ("gdn_fwd", "gdn_fwd_timed", "gdn_fwd_workspace_bytes", "gdn_fwd_plan", "gdn_fwd_noalloc",
             "gdn_fwd_recurrent", "gdn_bwd", "gdn_bwd_workspace_bytes", "gdn_status_string", "gdn_last_error")
 NOALLOC_SCRATCH_BYTES = 64 << 20   # GDN_NOALLOC_SCRATCH_BYTES of include/gdn.h
@@ -42,6 +43,7 @@ class FwdArgs(ctypes.Structure):
         ("o_dtype", ctypes.c_int32),
         ("qk_l2norm", ctypes.c_int32), ("beta_sigmoid", ctypes.c_int32), ("A_log", ctypes.c_void_p),
         ("dt_bias", ctypes.c_void_p), ("gate_lower_bound", ctypes.c_float), ("cp_warmup_tol", ctypes.c_float),
+        ("cp_form", ctypes.c_int32),
     ]
 
 
@@ -63,7 +65,7 @@ class PlanInfo(ctypes.Structure):
     """Mirror of gdn_plan_info."""
     _fields_ = [("cp", ctypes.c_int32), ("segment_chunks", ctypes.c_int32), ("total_segments", ctypes.c_int64),
                 ("value_cols_per_group", ctypes.c_int32), ("pieces", ctypes.c_int32),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("cp_form", ctypes.c_int32)]
 
 
 _lib = None
@@ -162,7 +164,7 @@ def check_inputs(q, k, v, g, beta, initial_state=None, cu_seqlens=None, A_log=No
 def make_args(q, k, v, g, beta, scale=None, initial_state=None, cu_seqlens=None, cu_seqlens_cpu=None,
               chunk_size=64, o=None, final_state=None, cp_mode="auto", cp_segment_chunks=0,
               qk_l2norm=False, beta_sigmoid=False, A_log=None, dt_bias=None, gate_lower_bound=0.0,
-              cp_warmup_tol=0.0):
+              cp_warmup_tol=0.0, cp_form="auto"):
     """Fill a gdn_fwd_args from tensors (shapes and dtypes are checked, nothing is computed)."""
     B, T, H_qk, D_k, H_v, D_v, N, gate = check_inputs(q, k, v, g, beta, initial_state, cu_seqlens, A_log, dt_bias,
                                                       o, final_state)
@@ -185,6 +187,7 @@ def make_args(q, k, v, g, beta, scale=None, initial_state=None, cu_seqlens=None,
     a.A_log, a.dt_bias = _ptr(A_log), _ptr(dt_bias)
     a.gate_lower_bound = float(gate_lower_bound)
     a.cp_warmup_tol = float(cp_warmup_tol)
+    a.cp_form = CP_FORMS[cp_form] if isinstance(cp_form, str) else int(cp_form)
     return a
 
 
@@ -230,7 +233,7 @@ def fwd_timed_raw(args, workspace, workspace_bytes_, stream, events):
 def fwd(q, k, v, g, beta, scale=None, initial_state=None, cu_seqlens=None, chunk_size=64,
         output_final_state=True, cp_mode="auto", cp_segment_chunks=0, workspace=None, out_dtype=None,
         qk_l2norm=False, beta_sigmoid=False, A_log=None, dt_bias=None, gate_lower_bound=0.0,
-        cp_warmup_tol=0.0):
+        cp_warmup_tol=0.0, cp_form="auto"):
     """Chunked-prefill forward of the gated delta rule on the GPU.
 
     q, k: [B, T, H_qk, D_k]; v: [B, T, H_v, D_v]; g: [B, T, H_v] fp32 log-gates (or
@@ -240,7 +243,8 @@ def fwd(q, k, v, g, beta, scale=None, initial_state=None, cu_seqlens=None, chunk
     In-kernel prologue (gdn_fwd_args in include/gdn.h): qk_l2norm normalises q and k rows, beta_sigmoid
     takes beta as logits, A_log ([H_v] fp32) with dt_bias ([H_v] or [H_v, D_k] fp32) and
     gate_lower_bound takes g as raw gate inputs.
-    cp_mode "warmup" with cp_warmup_tol: the approximate warmup form of context parallelism (gdn.h).
+    cp_mode "warmup" with cp_warmup_tol: the approximate warmup form of context parallelism (gdn.h);
+    cp_form "chain" or "xyz" picks the form of the exact pre-process (gdn.h, gdn_cp_form).
     Returns (o [B, T, H_v, D_v], final_state [N, H_v, D_k, D_v] fp32 or None).
     """
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("initial_state", initial_state),
@@ -256,7 +260,8 @@ def fwd(q, k, v, g, beta, scale=None, initial_state=None, cu_seqlens=None, chunk
     fs = (torch.empty((N, v.shape[2], k.shape[3], v.shape[3]), dtype=torch.float32, device=q.device)
           if output_final_state else None)
     a = make_args(q, k, v, g, beta, scale, initial_state, cu_dev, cu_host, chunk_size, o, fs, cp_mode,
-                  cp_segment_chunks, qk_l2norm, beta_sigmoid, A_log, dt_bias, gate_lower_bound, cp_warmup_tol)
+                  cp_segment_chunks, qk_l2norm, beta_sigmoid, A_log, dt_bias, gate_lower_bound, cp_warmup_tol,
+                  cp_form)
     nbytes = workspace_bytes(a)
     if nbytes == 0 and q.numel() > 0:
         _check(lib().gdn_fwd(ctypes.byref(a), None, 0, None))  # reports the validation error

@@ -79,6 +79,15 @@ typedef enum { GDN_GATE_SCALAR = 0, GDN_GATE_CHANNEL = 1 } gdn_gate_kind;
  * cp_warmup_tol.  Never chosen by GDN_CP_AUTO. */
 typedef enum { GDN_CP_AUTO = 0, GDN_CP_OFF = 1, GDN_CP_ON = 2, GDN_CP_WARMUP = 3 } gdn_cp_mode;
 
+/* Form of the exact CP pre-process (FlashQLA announcement, step 2.1 of the in-GPU CP pre-process):
+ * CHAIN runs the recurrence's own three products (K S, A X, K^T V'') over virtual value and
+ * identity columns, a workgroup per 32 of them; XYZ forms X^T = -K^T diag(gamma_C / gamma) A
+ * diag(beta) once per chunk and updates S* and M with two products (K S, X^T Y), one workgroup per
+ * (segment, value head); it applies to bf16 inputs with a scalar gate only (GDN_ERR_UNSUPPORTED
+ * otherwise).  AUTO takes XYZ where it applies and the (segment, value head) pairs fill the device's
+ * compute units, else CHAIN. */
+typedef enum { GDN_CP_FORM_AUTO = 0, GDN_CP_FORM_CHAIN = 1, GDN_CP_FORM_XYZ = 2 } gdn_cp_form;
+
 typedef struct {
     int32_t B, T;             /* batch and tokens per batch row (T = total tokens when packed) */
     int32_t H_qk, H_v;        /* query/key heads, value heads (H_v % H_qk == 0) */
@@ -117,6 +126,7 @@ typedef struct {
     const float *dt_bias;
     float gate_lower_bound;
     float cp_warmup_tol;      /* GDN_CP_WARMUP: decay bound that ends a warmup, in [0, 1); 0 = 2^-24 */
+    int32_t cp_form;          /* gdn_cp_form of the exact CP pre-process; 0 = AUTO */
 } gdn_fwd_args;
 
 /* Bytes of device workspace gdn_fwd needs for these arguments (0 on invalid
@@ -135,6 +145,7 @@ typedef struct {
     int32_t pieces;               /* chunk ranges of a batched input over which the per-chunk kernel
                                      (on a side stream) and the recurrence are pipelined; 1: none */
     size_t workspace_bytes;       /* as gdn_fwd_workspace_bytes */
+    int32_t cp_form;              /* gdn_cp_form the exact CP pre-process runs in (0 without it) */
 } gdn_plan_info;
 gdn_status gdn_fwd_plan(const gdn_fwd_args *a, gdn_plan_info *info);
 

@@ -245,6 +245,26 @@ def test_plan_query():
         gdn.plan(_args(chunk_size=48))
 
 
+def test_plan_reports_the_pre_process_form():
+    # the long-context shape: the automatic segment length (64 chunks) leaves 16 x 4 (segment,
+    # head) pairs, fewer than the compute units, so the chain form; 16-chunk segments give 64 x 4,
+    # and the X/Y/Z form (the plan assumes 256 compute units when no device answers)
+    long = dict(B=1, N=1, T=65536, H_qk=4, H_v=4)
+    assert gdn.plan(_args(**long))["cp_form"] == gdn.CP_FORMS["chain"]
+    assert gdn.plan(_args(**long, cp_segment_chunks=16))["cp_form"] == gdn.CP_FORMS["xyz"]
+    assert gdn.plan(_args(**long, cp_segment_chunks=16, cp_form=gdn.CP_FORMS["chain"]))["cp_form"] == gdn.CP_FORMS["chain"]
+    assert gdn.plan(_args(**long, cp_form=gdn.CP_FORMS["xyz"]))["cp_form"] == gdn.CP_FORMS["xyz"]
+    # no exact pre-process: no form
+    assert gdn.plan(_args(**long, cp_mode=gdn.CP_MODES["off"]))["cp_form"] == 0
+    assert gdn.plan(_args(**long, cp_mode=gdn.CP_MODES["warmup"]))["cp_form"] == 0
+    # the X/Y/Z form is bf16 with a scalar gate only; out-of-range forms are invalid
+    for kw in (dict(dtype=gdn.DTYPE_F32, o_dtype=gdn.DTYPE_F32), dict(gate_kind=gdn.GATE_CHANNEL)):
+        assert _status(_args(**long, cp_form=gdn.CP_FORMS["xyz"], **kw)) == gdn.GDN_ERR_UNSUPPORTED
+        assert "XYZ" in gdn.lib().gdn_last_error().decode()
+    assert _status(_args(cp_form=3)) == gdn.GDN_ERR_INVALID_ARG
+    assert "cp_form" in gdn.lib().gdn_last_error().decode()
+
+
 def test_backward_gradient_shapes_are_checked_on_the_host():
     # the kernels write dg shaped like g ([B, T, H_v, D_k] per channel): a buffer shaped like beta
     # must be rejected before anything is launched

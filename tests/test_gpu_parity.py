@@ -96,18 +96,24 @@ def test_varlen_workload_sampled():
 
 # --------------------------------------------------------------------------- context parallelism
 # Sequences split into segments of L chunks: per-segment S* and M, serial fix-up of the segment
-# start states, then the main pass per segment (FlashQLA page, the CP pre-process).
+# start states, then the main pass per segment (FlashQLA page, the CP pre-process).  bf16 with a
+# scalar gate runs either form of the pre-process (the recurrence's chain, or X/Y/Z).
+FORMS = ["chain", "xyz"]
+
+
+@pytest.mark.parametrize("form", FORMS)
 @pytest.mark.parametrize("L", [1, 2, 3, 7])
-def test_cp_bf16_segment_lengths(L):
+def test_cp_bf16_segment_lengths(L, form):
     x = _w("qwen3next_bf16", B=2, H=2, T=64 * 20 + 17, h0=True, seed=40 + L)
-    check(x, TOL["bf16"], label=f"bf16 CP L={L}", cp_mode="on", cp_segment_chunks=L)
+    check(x, TOL["bf16"], label=f"bf16 CP L={L} {form}", cp_mode="on", cp_segment_chunks=L, cp_form=form)
 
 
+@pytest.mark.parametrize("form", FORMS)
 @pytest.mark.parametrize("L", [1, 3])
-def test_cp_without_initial_state(L):
+def test_cp_without_initial_state(L, form):
     # the first segment's M is never formed without h0: the fix-up must not use it
     x = _w("qwen3next_bf16", B=1, H=2, T=64 * 9, mu=-7.0, seed=50 + L)
-    check(x, TOL["bf16"], label=f"bf16 CP no h0 L={L}", cp_mode="on", cp_segment_chunks=L)
+    check(x, TOL["bf16"], label=f"bf16 CP no h0 L={L} {form}", cp_mode="on", cp_segment_chunks=L, cp_form=form)
 
 
 @pytest.mark.parametrize("L", [1, 4])
@@ -118,14 +124,26 @@ def test_cp_fp32(L):
     check(x, TOL["fp32"], label=f"fp32 D=128 CP L={L}", cp_mode="on", cp_segment_chunks=L)
 
 
-def test_cp_packed_ragged():
+@pytest.mark.parametrize("form", FORMS)
+def test_cp_packed_ragged(form):
     x = _w("varlen_bf16", n_seqs=8, lens=(0, 1, 63, 64, 65, 1000, 129, 700), H=3, h0=True, seed=80)
-    check(x, TOL["bf16"], label="bf16 packed CP L=2", cp_mode="on", cp_segment_chunks=2)
+    check(x, TOL["bf16"], label=f"bf16 packed CP L=2 {form}", cp_mode="on", cp_segment_chunks=2, cp_form=form)
 
 
-def test_cp_bf16_head_dim_64():
+@pytest.mark.parametrize("form", FORMS)
+def test_cp_bf16_head_dim_64(form):
     x = _w("qwen3next_bf16", B=1, H=4, H_qk=1, D=64, T=900, h0=True, seed=90)
-    check(x, TOL["bf16"], label="bf16 D=64 CP L=3", cp_mode="on", cp_segment_chunks=3)
+    check(x, TOL["bf16"], label=f"bf16 D=64 CP L=3 {form}", cp_mode="on", cp_segment_chunks=3, cp_form=form)
+
+
+def test_cp_forms_agree():
+    # the two forms of the pre-process compute the same maps; they differ only by rounding order
+    x = _w("qwen3next_bf16", B=1, H=2, T=64 * 40, h0=True, mu=-7.0, seed=92)
+    o1, f1 = gpu_run(x, cp_mode="on", cp_segment_chunks=5, cp_form="chain", out_dtype=torch.float32)
+    o2, f2 = gpu_run(x, cp_mode="on", cp_segment_chunks=5, cp_form="xyz", out_dtype=torch.float32)
+    rms_o, rms_f = o1.double().pow(2).mean().sqrt(), f1.double().pow(2).mean().sqrt()
+    assert (o1 - o2).abs().max() <= 1e-2 * rms_o
+    assert (f1 - f2).abs().max() <= 1e-2 * rms_f
 
 
 def test_cp_matches_serial_pass():
@@ -201,10 +219,11 @@ def _dims(x, dk, dv):
 
 
 @pytest.mark.parametrize("dk,dv", [(128, 64), (64, 128)])
-@pytest.mark.parametrize("cp", ["off", "on"])
+@pytest.mark.parametrize("cp", ["off", "chain", "xyz"])
 def test_bf16_key_and_value_dims_differ(dk, dv, cp):
     x = _dims(_w("qwen3next_bf16", B=2, H=2, T=64 * 7 + 21, h0=True, mu=-7.0, seed=200 + dk), dk, dv)
-    check(x, TOL["bf16"], label=f"bf16 D_k={dk} D_v={dv} CP {cp}", cp_mode=cp, cp_segment_chunks=2)
+    mode = dict(cp_mode="off") if cp == "off" else dict(cp_mode="on", cp_form=cp)
+    check(x, TOL["bf16"], label=f"bf16 D_k={dk} D_v={dv} CP {cp}", cp_segment_chunks=2, **mode)
 
 
 def test_fp32_key_and_value_dims_differ():

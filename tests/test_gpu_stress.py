@@ -4,10 +4,10 @@ The workloads' gates decay fast (about e^-11.7 per chunk for the scalar gate), s
 between chunks, and the transition M of context parallelism, barely reach the output there.  These
 cases take the long-context shape (B = 1, H = 4, d = 128, nonzero h0) with weak decay
 (g = -softplus(N(-7, 1)), about -1e-3 per token) and with no decay at all (g == 0), through the
-serial pass and through context parallelism with segments of 8 (automatic), 16 and 64 chunks, so
-that S* and M accumulate over many slowly decaying chunks and the fix-up runs several steps
-(FlashQLA announcement, the CP pre-process and fix-up).  The full long-context workload runs with
-weak decay on two sampled heads.
+serial pass and through context parallelism with segments of 8 (automatic), 16 and 64 chunks, in
+both forms of the pre-process, so that S* and M accumulate over many slowly decaying chunks and the
+fix-up runs several steps (FlashQLA announcement, the CP pre-process and fix-up).  The full
+long-context workload runs with weak decay on two sampled heads.
 
 Per-channel gates that decay steeply inside a 16-token block (around -8 per token, and around -3
 where only some blocks are steep) exercise the per-pair path of the per-chunk kernel, forward and
@@ -27,15 +27,20 @@ def _w(name, **kw):
 
 
 @pytest.mark.parametrize("mu", [-7.0, None], ids=["weak", "none"])
-@pytest.mark.parametrize("cp,seg", [("off", 0), ("auto", 0), ("on", 16), ("on", 64)])
-def test_longctx_shape_slow_decay(mu, cp, seg):
+@pytest.mark.parametrize("cp,seg,form", [("off", 0, "auto"), ("auto", 0, "auto"), ("on", 16, "chain"),
+                                         ("on", 64, "chain"), ("on", 16, "xyz"), ("on", 64, "xyz")])
+def test_longctx_shape_slow_decay(mu, cp, seg, form):
     x = _w("longctx_bf16", T=8192, mu=mu, seed=800)
-    check(x, TOL["bf16"], label=f"B=1 H=4 T=8192 mu={mu} cp={cp} L={seg}", cp_mode=cp, cp_segment_chunks=seg)
+    check(x, TOL["bf16"], label=f"B=1 H=4 T=8192 mu={mu} cp={cp} L={seg} {form}", cp_mode=cp, cp_segment_chunks=seg,
+          cp_form=form)
 
 
-def test_longctx_workload_weak_decay_cp_auto_sampled():
+@pytest.mark.parametrize("seg,form", [(0, "auto"), (16, "xyz")])
+def test_longctx_workload_weak_decay_cp_sampled(seg, form):
+    # (L = 16: the segment count that makes the automatic choice take the X/Y/Z pre-process)
     x = _w("longctx_bf16", mu=-7.0, seed=801)
-    check(x, TOL["bf16"], heads=[0, 3], label="longctx_bf16 mu=-7 CP auto (sampled)", cp_mode="auto")
+    check(x, TOL["bf16"], heads=[0, 3], label=f"longctx_bf16 mu=-7 CP L={seg} {form} (sampled)", cp_mode="on",
+          cp_segment_chunks=seg, cp_form=form)
 
 
 @pytest.mark.parametrize("mu", [8.0, 3.0], ids=["steep", "mixed"])
