@@ -602,6 +602,28 @@ extern "C" gdn_status gdn_bwd(const gdn_bwd_args *a, void *workspace, size_t wor
     const bool grouped = a->H_v != a->H_qk;
     bw.dq_v = grouped ? reinterpret_cast<float *>(ws + bp.off_dqv) : a->dq;
     bw.dk_v = grouped ? reinterpret_cast<float *>(ws + bp.off_dkv) : a->dk;
+    // Step 2 of the notes (the state entering every chunk): the forward's main pass, with its output
+    // dropped and every chunk's entering state stored
+    gdn::ChunkParams cp{};
+    cp.q = a->q; cp.k = a->k; cp.v = a->v; cp.g = a->g; cp.beta = a->beta;
+    cp.A = ws + pl.off_A; cp.h0 = a->h0; cp.o = nullptr; cp.final_state = nullptr;
+    cp.seq = seq;
+    cp.segs = packed ? reinterpret_cast<gdn::SegInfo *>(ws + pl.off_segs) : nullptr;
+    cp.order = packed ? reinterpret_cast<int *>(ws + pl.off_order) : nullptr;
+    cp.T = a->T; cp.N = a->N; cp.H_qk = a->H_qk; cp.H_v = a->H_v; cp.D_v = a->D_v;
+    cp.seg_chunks = pl.seg_chunks; cp.total_segs = (int)pl.total_segs;
+    cp.scale = a->scale;
+    cp.P = ws + pl.off_P;
+    cp.gates = reinterpret_cast<const float *>(ws + pl.off_gates);
+    if (channel) {
+        cp.kg = ws + pl.off_kg; cp.kd = ws + pl.off_kd; cp.qg = ws + pl.off_qg;
+    }
+    cp.n_slices = pl.n_slices;
+    cp.n_cus = device_cus();
+    cp.chunk_states = bw.states;
+    if ((e = gdn::launch_chunk(a->dtype, a->D_k, pl.BV, a->gate_kind, cp, s)) != hipSuccess)
+        return fail(GDN_ERR_HIP, "state replay launch: %s", hipGetErrorString(e));
+    bw.replayed = 1;
     if ((e = gdn::launch_bwd(a->dtype, a->D_k, bw, s)) != hipSuccess)
         return fail(GDN_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
     return GDN_OK;

@@ -1086,7 +1086,7 @@ hipError_t launch_bwd(int dtype, int D_k, const BwdParams &p, hipStream_t s) {
 // every kernel of the backward runs kBwT threads per workgroup
 #define GDN_BWDK(K, T, DK, grid) hipLaunchKernelGGL((K<T, DK>), dim3((unsigned)(grid)), dim3(kBwT), 0, s, p)
 #define GDN_BWDK_ALL(T, DK)                                  \
-    GDN_BWDK(bwd_states_kda_kernel, T, DK, replays);         \
+    if (!p.replayed) GDN_BWDK(bwd_states_kda_kernel, T, DK, replays); \
     if (chunks) GDN_BWDK(bwd_p_kda_kernel, T, DK, chunks);   \
     GDN_BWDK(bwd_dstate_kda_kernel, T, DK, scans);           \
     if (chunks) {                                            \
@@ -1111,7 +1111,7 @@ hipError_t launch_bwd(int dtype, int D_k, const BwdParams &p, hipStream_t s) {
     if (scans == 0) return hipSuccess;
 #define GDN_BWD(K, T, DK, grid) hipLaunchKernelGGL((K<T, DK>), dim3((unsigned)(grid)), dim3(kBwT), 0, s, p)
 #define GDN_BWD_ALL(T, DK)                                  \
-    GDN_BWD(bwd_states_kernel, T, DK, scans);               \
+    if (!p.replayed) GDN_BWD(bwd_states_kernel, T, DK, scans); \
     if (chunks) GDN_BWD(bwd_p_kernel, T, DK, chunks);       \
     GDN_BWD(bwd_dstate_kernel, T, DK, rscans);              \
     if (chunks) GDN_BWD(bwd_chunk_kernel, T, DK, chunks);

@@ -558,7 +558,7 @@ void chunk_kernel(ChunkParams p) {
                 const int64_t ebase = (int64_t)(si.tok0 + (cs + c) * kChunk) * v_stride + (int64_t)h * DV + c0;
                 const int oes = p.o_f32 ? 4 : ESZ;
                 const __amdgpu_buffer_rsrc_t ors = make_rsrc(static_cast<char *>(p.o) + ebase * oes,
-                                                             ((nv - 1) * vs + BV) * oes);
+                                                             p.o ? ((nv - 1) * vs + BV) * oes : 0);
 #pragma unroll
                 for (int i = 0; i < NR; ++i)
 #pragma unroll
@@ -607,6 +607,15 @@ void chunk_kernel(ChunkParams p) {
         unsigned char *tcur = B == 0 ? tiles0 : tiles1;
         unsigned char *tnext = B == 0 ? tiles1 : tiles0;
         chunk_top.template operator()<!OUT || CHAIN_LD>(c);
+        if constexpr (OUT) {
+            if (p.chunk_states) {   // the state entering this chunk (no CP: segment = sequence)
+                float *st = p.chunk_states + ((int64_t)(si.chunk0 + cs + c) * p.H_v + h) * DK * DV;
+#pragma unroll
+                for (int m = 0; m < MD; ++m)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) st[(16 * m + 4 * grp + r) * DV + col] = S[m][r];
+            }
+        }
         const float *g3 = reinterpret_cast<const float *>(tcur + L::G0);
         const bool more = NBUF == 2 && c + 1 < nch;
         if constexpr (!OUT) {

@@ -155,6 +155,9 @@ struct ChunkParams {
     int seg_only;
     float *seg_next;
     int n_cus;              // compute units of the device the launch goes to
+    // nullable (main pass without CP): receives the state entering every chunk, fp32
+    // [global chunk][H_v][D_k][D_v] (the backward's recomputed chunk states); o may then be null
+    float *chunk_states;
 };
 
 // chunk ci of the per-chunk grid: every chunk, or the chunks of one piece of a batched input
@@ -210,6 +213,7 @@ struct BwdParams {           // backward (gdn_bwd), scalar gate
     float *vp, *dlmat;                     // per-channel gates: V' [n_chunks][H_v][64][D_v], dL [n_chunks][H_v][64][64]
     float *dq, *dk, *dv, *dg, *dbeta, *dh0;
     float *dq_v, *dk_v;                    // per value head when H_v > H_qk, else dq / dk
+    int replayed;                          // 1: states already holds every chunk's entering state
 };
 
 hipError_t launch_plan(const PlanParams &p, hipStream_t s);
@@ -218,8 +222,8 @@ hipError_t launch_intra_kda(int dtype, int D_k, const IntraKdaParams &p, hipStre
 hipError_t launch_chunk(int dtype, int D_k, int BV, int gate, const ChunkParams &p, hipStream_t s);
 // mode 1: context-parallel pre-process (chain only over value and identity columns)
 hipError_t launch_cp_pre(int dtype, int D_k, int BV, int gate, const ChunkParams &p, hipStream_t s);
-// the same maps in the X/Y/Z form (scalar gate, bf16); hipErrorInvalidValue for other head widths
-// writes M as bf16 pairs in operand order, which launch_cp_fix_xyz reads
+// the same maps in the X/Y/Z form (scalar gate, bf16), M written as bf16 pairs in operand order,
+// which launch_cp_fix_xyz reads; hipErrorInvalidValue for other head widths
 hipError_t launch_cp_pre_xyz(int D_k, const ChunkParams &p, hipStream_t s);
 hipError_t launch_cp_fix_xyz(int D_k, const FixParams &p, hipStream_t s);
 hipError_t launch_cp_fix(int dtype, int D_k, const FixParams &p, hipStream_t s);
