@@ -135,8 +135,8 @@ __global__ __launch_bounds__(kBwT) void bwd_states_kernel(BwdParams p) {
     }
 }
 
-// ---- scale Pt of every (chunk, value head), fp32 [64][64], for the reverse scan (which would
-//      otherwise form it once per value-column group)
+// ---- scale Pt of every (chunk, value head), for the reverse scan (which would otherwise form it
+//      once per value-column group): fp32 [64][64], or for bf16 inputs a bf16 pair [2][64][64]
 template <typename T, int DK>
 __global__ __launch_bounds__(kBwT) void bwd_p_kernel(BwdParams p) {
     constexpr int NT = kBwT;
@@ -157,7 +157,16 @@ __global__ __launch_bounds__(kBwT) void bwd_p_kernel(BwdParams p) {
         float s = 0.f;
         if (j <= i)
             for (int d = 0; d < DK; ++d) s += sQ[i][d] * sK[j][d];
-        P[idx] = j <= i ? p.scale * __expf(sgl[i] - sgl[j]) * s : 0.f;
+        const float x = j <= i ? p.scale * __expf(sgl[i] - sgl[j]) * s : 0.f;
+        if constexpr (sizeof(T) == 2) {
+            // bf16 inputs: as the operand pair of the matrix-core reverse scan, hi [64][64] then lo
+            bf16 *Pb = reinterpret_cast<bf16 *>(P);
+            const bf16 hi = (bf16)x;
+            Pb[idx] = hi;
+            Pb[4096 + idx] = (bf16)(x - (float)hi);
+        } else {
+            P[idx] = x;
+        }
     }
 }
 
@@ -237,6 +246,240 @@ __global__ __launch_bounds__(kBwT) void bwd_dstate_kernel(BwdParams p) {
             const int d = idx / kBwD, j = idx % kBwD;
             p.dh0[(((int64_t)n * p.H_v + h) * DK + d) * DV + cb * kBwD + j] = sdS[d][j];
         }
+    }
+}
+
+// ---- reverse scan of the state gradient on the matrix cores (bf16 inputs, scalar gate): the same
+//      quantities as bwd_dstate_kernel.  One workgroup per (sequence, value head, 32 value columns),
+//      two waves; each wave holds dS for its 16 columns and all D_k rows in registers, so K dS and
+//      the update take the state-side operand straight from its accumulators (pi order), and dV'
+//      and dX never leave the wave.  Per chunk, newest first:
+//        store dS (= dS_next of the chunk);  Y = K dS;  dV' = D (.) Y + Pt^T dO;  dX = A^T dV';
+//        dS <- gamma_C dS + Q^T (scale gamma (.) dO) - K^T (beta gamma (.) dX)
+//      K, Q, A, the Pt pair, the dO columns and the gate block of the next-older chunk stream into
+//      the other of two padded LDS stages meanwhile.  Operands that are not inputs are bf16 pairs.
+template <int DK>
+struct DsLayout {
+    static constexpr int NW = 2, WC = 32;             // waves, value columns per workgroup
+    using K = Pad<DK * 2 / 16>;                       // K and Q tiles
+    using A = Pad<8>;                                 // A, and each part of the Pt pair (64 x 64)
+    using O = Pad<WC * 2 / 16>;                       // dO columns of the workgroup
+    static constexpr int GT = GB_FLOATS * 4;
+    static constexpr int K0 = 0, Q0 = K::BYTES, A0 = 2 * K::BYTES, P0 = A0 + A::BYTES, O0 = P0 + 2 * A::BYTES;
+    static constexpr int G0 = O0 + O::BYTES, STAGE = G0 + GT;
+    static constexpr int NLG = GT / 1024;
+    static constexpr int NLOAD = 2 * K::NI + 3 * A::NI + O::NI + NLG;
+    static constexpr int NLW = (NLOAD + NW - 1) / NW;
+    static constexpr int MD = DK / 16, NKB = DK / 32;
+    static_assert(2 * STAGE <= 160 * 1024, "LDS budget");
+};
+
+template <int DK>
+__global__ __launch_bounds__(128, 1) void bwd_dstate_mma_kernel(BwdParams p) {
+    using L = DsLayout<DK>;
+    using KT = typename L::K;
+    using AT = typename L::A;
+    using OT = typename L::O;
+    constexpr int MD = L::MD, NKB = L::NKB, NLW = L::NLW, NW = L::NW;
+    __shared__ __attribute__((aligned(16))) unsigned char stg0[L::STAGE], stg1[L::STAGE];
+    const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ncb = p.D_v / L::WC;
+    const int cb = blockIdx.x % ncb, nh = blockIdx.x / ncb, h = nh % p.H_v, n = nh / p.H_v;
+    if (n >= p.N) return;
+    const int hq = h / (p.H_v / p.H_qk);
+    const SeqInfo si = seq_info(p.seq, n, p.T);
+    const int DV = p.D_v, qks = p.H_qk * DK, vs = p.H_v * DV;
+    const int c0 = cb * L::WC, col = c0 + 16 * wave + l16;
+    const bf16 *kb_ = static_cast<const bf16 *>(p.k) + (int64_t)hq * DK;
+    const bf16 *qb = static_cast<const bf16 *>(p.q) + (int64_t)hq * DK;
+    const bf16 *ob = static_cast<const bf16 *>(p.dout) + (int64_t)h * DV + c0;
+    const bf16 *Ab = static_cast<const bf16 *>(p.A) + (int64_t)h * 4096;
+    const bf16 *Pb = reinterpret_cast<const bf16 *>(p.pmat) + (int64_t)h * 2 * 4096;
+    const float *Gb = p.gates + (int64_t)h * GB_FLOATS;
+
+    // this wave's stage instructions (K, Q, A, Pt hi, Pt lo, dO, gate block; pad granules read zeros)
+    constexpr int kOut = 1 << 30;
+    int soff[NLW], dst[NLW], kind[NLW];
+#pragma unroll
+    for (int j = 0; j < NLW; ++j) {
+        int ii = wave + NW * j;
+        kind[j] = 7;
+        soff[j] = 0;
+        dst[j] = 0;
+        if (ii < 2 * KT::NI) {
+            const int q = ii >= KT::NI, i2 = ii - q * KT::NI, pos = 64 * i2 + lane, row = pos / KT::P, g = pos % KT::P;
+            kind[j] = q;                                     // 0: K, 1: Q
+            soff[j] = g < KT::P - 1 ? row * qks * 2 + 16 * g : kOut;
+            dst[j] = (q ? L::Q0 : L::K0) + 1024 * i2;
+        } else if ((ii -= 2 * KT::NI) < 3 * AT::NI) {
+            const int part = ii / AT::NI, i2 = ii - part * AT::NI, pos = 64 * i2 + lane, row = pos / AT::P, g = pos % AT::P;
+            kind[j] = 2 + part;                              // 2: A, 3: Pt hi, 4: Pt lo
+            soff[j] = g < AT::P - 1 ? row * 128 + 16 * g : kOut;
+            dst[j] = L::A0 + part * AT::BYTES + 1024 * i2;
+        } else if ((ii -= 3 * AT::NI) < OT::NI) {
+            const int pos = 64 * ii + lane, row = pos / OT::P, g = pos % OT::P;
+            kind[j] = 5;
+            soff[j] = g < OT::P - 1 ? row * vs * 2 + 16 * g : kOut;
+            dst[j] = L::O0 + 1024 * ii;
+        } else if ((ii -= OT::NI) < L::NLG) {
+            kind[j] = 6;
+            soff[j] = 1024 * ii + 16 * lane;
+            dst[j] = L::G0 + 1024 * ii;
+        }
+    }
+    auto load_stage = [&](int c, unsigned char *tb) __attribute__((always_inline)) {
+        const int64_t tok = si.tok0 + (int64_t)c * kChunk, gci = si.chunk0 + c;
+        const int nv = min(kChunk, si.len - c * kChunk);
+        const u32x4 rK = rsrc_words(kb_ + tok * qks, ((nv - 1) * qks + DK) * 2);
+        const u32x4 rQ = rsrc_words(qb + tok * qks, ((nv - 1) * qks + DK) * 2);
+        const u32x4 rA = rsrc_words(Ab + gci * p.H_v * 4096, 4096 * 2);
+        const u32x4 rPh = rsrc_words(Pb + gci * p.H_v * 2 * 4096, 4096 * 2);
+        const u32x4 rPl = rsrc_words(Pb + gci * p.H_v * 2 * 4096 + 4096, 4096 * 2);
+        const u32x4 rO = rsrc_words(ob + tok * vs, ((nv - 1) * vs + L::WC) * 2);
+        const u32x4 rG = rsrc_words(Gb + gci * p.H_v * GB_FLOATS, GB_FLOATS * 4);
+#pragma unroll
+        for (int j = 0; j < NLW; ++j) {
+            if (kind[j] == 7) continue;
+            const u32x4 r = kind[j] == 0 ? rK : kind[j] == 1 ? rQ : kind[j] == 2 ? rA : kind[j] == 3 ? rPh
+                          : kind[j] == 4 ? rPl : kind[j] == 5 ? rO : rG;
+            dma_granules(r, tb + dst[j], soff[j]);
+        }
+    };
+
+    f32x4 S[MD];   // dS: rows 16 m + 4 grp + r of column col
+#pragma unroll
+    for (int m = 0; m < MD; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            S[m][r] = p.dht ? p.dht[(((int64_t)n * p.H_v + h) * DK + 16 * m + 4 * grp + r) * DV + col] : 0.f;
+
+    auto step = [&](int c, const unsigned char *st) __attribute__((always_inline)) {
+        const int64_t gci = si.chunk0 + c;
+        const unsigned char *tK = st + L::K0, *tQ = st + L::Q0, *tA = st + L::A0, *tPh = st + L::P0;
+        const unsigned char *tPl = tPh + AT::BYTES, *tO = st + L::O0;
+        const float *g = reinterpret_cast<const float *>(st + L::G0);
+        {   // dS_next of this chunk
+            float *dsn = p.dsnext + (gci * p.H_v + h) * DK * DV;
+#pragma unroll
+            for (int m = 0; m < MD; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dsn[(16 * m + 4 * grp + r) * DV + col] = S[m][r];
+        }
+        // Y = K dS, then dV' = D (.) Y + Pt^T dO
+        f32x4 dv[4];
+        {
+            Frag<bf16> sh[NKB], sl[NKB];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                float x[8];
+                pack_pi(S[2 * kb], S[2 * kb + 1], x);
+                split8_rne(x, sh[kb], sl[kb]);
+            }
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+                    if (kb == 0) dv[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    mma_x(dv[tt], pi_row<KT>(tK, 16 * tt + l16, kb, grp), sh[kb], sl[kb]);
+                }
+                reg_fence();
+            }
+        }
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            const float4 d4 = *reinterpret_cast<const float4 *>(g + GB_SC + 16 * tt + 4 * grp);
+            dv[tt][0] *= d4.x; dv[tt][1] *= d4.y; dv[tt][2] *= d4.z; dv[tt][3] *= d4.w;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                if (32 * kb + 31 < 16 * tt) continue;        // Pt[s][t] = 0 for s < t
+                mma_pair_x(dv[tt], pi_col<AT>(tPh, 16 * tt, kb, grp, l16), pi_col<AT>(tPl, 16 * tt, kb, grp, l16),
+                           pi_col<OT>(tO, 16 * wave, kb, grp, l16));
+            }
+        }
+        // dX = A^T dV'
+        f32x4 dx[4];
+        {
+            Frag<bf16> vh[2], vl[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                float x[8];
+                pack_pi(dv[2 * kb], dv[2 * kb + 1], x);
+                split8_rne(x, vh[kb], vl[kb]);
+            }
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                dx[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    if (32 * kb + 31 < 16 * tt) continue;    // A[s][t] = 0 for s < t
+                    mma_x(dx[tt], pi_col<AT>(tA, 16 * tt, kb, grp, l16), vh[kb], vl[kb]);
+                }
+            }
+        }
+        // dS <- gamma_C dS + Q^T (scale gamma (.) dO) - K^T (beta gamma (.) dX)
+        Frag<bf16> oh[2], ol[2], xh[2], xl[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const int t0 = 32 * kb + 4 * grp;
+            const float4 qa = *reinterpret_cast<const float4 *>(g + GB_GAQ + t0);
+            const float4 qc = *reinterpret_cast<const float4 *>(g + GB_GAQ + t0 + 16);
+            const float4 ba = *reinterpret_cast<const float4 *>(g + GB_BETA + t0);
+            const float4 bc = *reinterpret_cast<const float4 *>(g + GB_BETA + t0 + 16);
+            const float4 ka = *reinterpret_cast<const float4 *>(g + GB_GAK + t0);
+            const float4 kc = *reinterpret_cast<const float4 *>(g + GB_GAK + t0 + 16);
+            const float fq[8] = {qa.x, qa.y, qa.z, qa.w, qc.x, qc.y, qc.z, qc.w};
+            const float fk[8] = {ba.x * ka.x, ba.y * ka.y, ba.z * ka.z, ba.w * ka.w,
+                                 bc.x * kc.x, bc.y * kc.y, bc.z * kc.z, bc.w * kc.w};
+            const Frag<bf16> o = pi_col<OT>(tO, 16 * wave, kb, grp, l16);   // dO[t][col], t in pi order
+            float xo[8], xx[8];
+            pack_pi(dx[2 * kb], dx[2 * kb + 1], xx);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                xo[e] = p.scale * fq[e] * (float)o.v[e];
+                xx[e] = -fk[e] * xx[e];
+            }
+            split8_rne(xo, oh[kb], ol[kb]);
+            split8_rne(xx, xh[kb], xl[kb]);
+        }
+        const float gC = g[GB_GC];
+#pragma unroll
+        for (int m = 0; m < MD; ++m) {
+            S[m] *= gC;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                mma_x(S[m], pi_col<KT>(tQ, 16 * m, kb, grp, l16), oh[kb], ol[kb]);
+                mma_x(S[m], pi_col<KT>(tK, 16 * m, kb, grp, l16), xh[kb], xl[kb]);
+            }
+            if (m & 1) reg_fence();
+        }
+    };
+
+    const int nch = si.nchunks;
+    if (nch > 0) {
+        load_stage(nch - 1, stg0);
+        wait_vm<0>();
+        lds_only_barrier();
+    }
+    // chunks newest first; stage of chunk c: stg0 when (nch - 1 - c) is even
+    for (int k = 0; k < nch; k += 2) {
+        const int c = nch - 1 - k;
+        if (c >= 1) load_stage(c - 1, stg1);
+        step(c, stg0);
+        wait_vm<0>();
+        lds_only_barrier();    // chunk c - 1's stage; every wave is done with stg0
+        if (c >= 1) {
+            if (c >= 2) load_stage(c - 2, stg0);
+            step(c - 1, stg1);
+            wait_vm<0>();
+            lds_only_barrier();
+        }
+    }
+    if (p.dh0) {
+#pragma unroll
+        for (int m = 0; m < MD; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) p.dh0[(((int64_t)n * p.H_v + h) * DK + 16 * m + 4 * grp + r) * DV + col] = S[m][r];
     }
 }
 
@@ -1107,13 +1350,17 @@ hipError_t launch_bwd(int dtype, int D_k, const BwdParams &p, hipStream_t s) {
         return hipGetLastError();
     }
     const int64_t scans = (int64_t)p.N * p.H_v * (p.D_v / kBwR), rscans = (int64_t)p.N * p.H_v * (p.D_v / kBwD);
+    const int64_t mscans = (int64_t)p.N * p.H_v * (p.D_v / 32);
     const int64_t chunks = (int64_t)p.n_chunks * p.H_v;
     if (scans == 0) return hipSuccess;
 #define GDN_BWD(K, T, DK, grid) hipLaunchKernelGGL((K<T, DK>), dim3((unsigned)(grid)), dim3(kBwT), 0, s, p)
-#define GDN_BWD_ALL(T, DK)                                  \
-    if (!p.replayed) GDN_BWD(bwd_states_kernel, T, DK, scans); \
-    if (chunks) GDN_BWD(bwd_p_kernel, T, DK, chunks);       \
-    GDN_BWD(bwd_dstate_kernel, T, DK, rscans);              \
+#define GDN_BWD_ALL(T, DK)                                                                                 \
+    if (!p.replayed) GDN_BWD(bwd_states_kernel, T, DK, scans);                                             \
+    if (chunks) GDN_BWD(bwd_p_kernel, T, DK, chunks);                                                      \
+    if (sizeof(T) == 2)                                                                                    \
+        hipLaunchKernelGGL((bwd_dstate_mma_kernel<DK>), dim3((unsigned)mscans), dim3(128), 0, s, p);      \
+    else                                                                                                   \
+        GDN_BWD(bwd_dstate_kernel, T, DK, rscans);                                                         \
     if (chunks) GDN_BWD(bwd_chunk_kernel, T, DK, chunks);
     if (dtype == 1 && D_k == 128) { GDN_BWD_ALL(bf16, 128) }
     else if (dtype == 1 && D_k == 64) { GDN_BWD_ALL(bf16, 64) }

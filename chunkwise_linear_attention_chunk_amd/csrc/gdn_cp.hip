@@ -37,14 +37,6 @@ namespace gdn {
 
 namespace {
 
-// 64 (or ROWS) rows of G granules, row pitch G + 1 granules; loaded with G + 1 instructions of 64
-// granules each (the pad granules read zeros)
-template <int G, int ROWS = 64>
-struct Pad {
-    static constexpr int P = G + 1, PB = 16 * P, BYTES = ROWS * PB, NI = ROWS * P / 64;
-    __device__ static constexpr int off(int row, int col_bytes) { return row * PB + col_bytes; }
-};
-
 template <int DK, int NW, int CT, int VW>
 struct CpLayout {
     static constexpr int WC = 16 * CT * NW;           // columns per workgroup
@@ -64,50 +56,6 @@ struct CpLayout {
     static_assert(NW == 4 || NW == 8, "four token tiles of X over the waves");
     static_assert(2 * STAGE + 2 * X::BYTES <= 160 * 1024, "LDS budget");
 };
-
-// Buffer resource words over [base, base + bytes) (as make_rsrc builds them), for asm operands.
-__device__ __forceinline__ u32x4 rsrc_words(const void *base, int bytes) {
-    const uint64_t a = reinterpret_cast<uint64_t>(base);
-    return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, (uint32_t)bytes, 0x00020000u};
-}
-// One wave instruction moving 64 granules into LDS at lds + 16 * lane, lane l reading the buffer at
-// byte voff (out of range: zeros), written in asm.  The compiler's wait insertion does not see this
-// load, so reads of the other stage are not made to wait for it (with the builtin, the compiler
-// cannot tell the stages apart and waits for every load in flight before such reads); the kernel
-// waits for it itself (wait_vm) before the barrier that publishes the stage.  M0 carries the LDS
-// base; one wait state separates its write from the load that reads it.
-__device__ __forceinline__ void dma_granules(u32x4 rsrc, const void *lds, int voff) {
-    const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void *)lds);
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :: "s"(m0), "v"(voff), "s"(rsrc) : "memory", "m0");
-}
-
-// pi-order operand of a padded tile row: elements [32kb + 4grp, +4) and [32kb + 16 + 4grp, +4)
-template <typename PT>
-__device__ __forceinline__ Frag<bf16> pi_row(const unsigned char *tile, int row, int kb, int grp) {
-    const unsigned char *p = tile + PT::off(row, (32 * kb + 4 * grp) * 2);
-    const bf16x4 a = *reinterpret_cast<const bf16x4 *>(p);
-    const bf16x4 b = *reinterpret_cast<const bf16x4 *>(p + 32);
-    Frag<bf16> f;
-    f.v = bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-    return f;
-}
-// pi-order column operand of a padded tile: column c0 + l16, rows 32kb + 4grp + r and
-// 32kb + 16 + 4grp + r (transposed reads: lane 4e + q of the group points at row 32kb + 4grp + e,
-// columns c0 + 4q .. + 3)
-template <typename PT>
-__device__ __forceinline__ Frag<bf16> pi_col(const unsigned char *tile, int c0, int kb, int grp, int l16) {
-    const unsigned char *p = tile + PT::off(32 * kb + 4 * grp + (l16 >> 2), (c0 + 4 * (l16 & 3)) * 2);
-    const bf16x4 a = lds_read_tr16(p);
-    const bf16x4 b = lds_read_tr16(p + 16 * PT::PB);
-    Frag<bf16> f;
-    f.v = bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-    return f;
-}
-
-// Keeps the compiler from hoisting LDS operand reads of later iterations above this point: hoisted
-// all at once they would need more registers than a wave has.
-__device__ __forceinline__ void reg_fence() { asm volatile("" ::: "memory"); }
 
 template <int DK, int NW, int CT, int VW>
 __global__ __launch_bounds__(64 * NW, 1) void cp_pre_xyz_kernel(ChunkParams p, int n_blocks) {

@@ -2,8 +2,9 @@
 (oracle/backward.py), through the C ABI.
 
 Bound per gradient tensor: max|delta| <= tol * RMS(oracle gradient), tol 1e-4 for fp32 inputs
-and 2e-2 for bf16 inputs (the forward's bounds; the backward keeps every product in fp32 and
-rounds only the stored (I + L)^-1 to the input dtype)."""
+and 2e-2 for bf16 inputs (the forward's bounds).  The chunk states are recomputed by the forward's
+main pass, the reverse state-gradient scan of bf16 inputs runs on the matrix cores with bf16 operand
+pairs (as the forward), the rest in fp32."""
 import numpy as np
 import pytest
 import torch
@@ -59,6 +60,18 @@ def test_backward_fp32_no_initial_state_no_dht():
 def test_backward_bf16():
     x = synth.make_inputs(synth.workload("qwen3next_bf16", B=1, H=2, T=300, h0=True, seed=612))
     _check(x, TOL["bf16"], "bf16", seed=3)
+
+
+@pytest.mark.parametrize("mu", [-7.0, None], ids=["weak", "none"])
+def test_backward_bf16_many_chunks_slow_decay(mu):
+    # the reverse scan carries dS over 21 chunks with weak decay, or none
+    x = synth.make_inputs(synth.workload("qwen3next_bf16", B=1, H=2, T=64 * 20 + 17, mu=mu, h0=True, seed=614))
+    _check(x, TOL["bf16"], f"bf16 T=1297 mu={mu}", seed=5)
+
+
+def test_backward_bf16_head_dim_64_grouped_heads():
+    x = synth.make_inputs(synth.workload("qwen3next_bf16", B=2, H=4, H_qk=2, D=64, T=200, h0=True, seed=615))
+    _check(x, TOL["bf16"], "bf16 D=64 H_v=4 H_qk=2", seed=6)
 
 
 def test_backward_packed():
