@@ -6,7 +6,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgdn.so")
-SOURCES = ["gdn_api.hip", "gdn_intra.hip", "gdn_chunk.hip", "gdn_cp.hip", "gdn_recurrent.hip", "gdn_bwd.hip"]
+SOURCES = ["gdn_api.hip", "gdn_intra.hip", "gdn_chunk.hip", "gdn_cp.hip", "gdn_recurrent.hip", "gdn_bwd.hip", "gdn_bwd_mma.hip"]
 # Packed fp32 VALU ops are kept out of the generated code on purpose.  Matrix-core results stay in
 # ordinary VGPRs (the recurrence reads and rescales them with vector ALU ops every chunk; the
 # accumulation registers would cost a copy each way).

@@ -1361,7 +1361,14 @@ hipError_t launch_bwd(int dtype, int D_k, const BwdParams &p, hipStream_t s) {
         hipLaunchKernelGGL((bwd_dstate_mma_kernel<DK>), dim3((unsigned)mscans), dim3(128), 0, s, p);      \
     else                                                                                                   \
         GDN_BWD(bwd_dstate_kernel, T, DK, rscans);                                                         \
-    if (chunks) GDN_BWD(bwd_chunk_kernel, T, DK, chunks);
+    if (chunks) {                                                                                          \
+        if (sizeof(T) == 2) {                                                                              \
+            const hipError_t em = launch_bwd_chunk_mma(DK, p, s);                                          \
+            if (em != hipSuccess) return em;                                                               \
+        } else {                                                                                           \
+            GDN_BWD(bwd_chunk_kernel, T, DK, chunks);                                                      \
+        }                                                                                                  \
+    }
     if (dtype == 1 && D_k == 128) { GDN_BWD_ALL(bf16, 128) }
     else if (dtype == 1 && D_k == 64) { GDN_BWD_ALL(bf16, 64) }
     else if (dtype == 0 && D_k == 128) { GDN_BWD_ALL(float, 128) }

@@ -1,0 +1,463 @@
+// Per-chunk gradients of the backward on the matrix cores (bf16 inputs, scalar gate): the same
+// quantities as the plain bwd_chunk_kernel (GDN-in-FLA notes, backward Steps 3-7; the formulas are
+// in gdn_bwd.hip's header), per (chunk, value head) workgroup of eight waves:
+//   value columns in halves of 64:  K S, K dS_next;  X = diag(beta)(V - diag(gamma) K S);
+//     V' = A X;  dV' = diag(D) K dS_next + Pt^T dO;  dX = A^T dV';  dv = diag(beta) dX;
+//     dA += dV' X^T;  dPt += dO V'^T;  dq_S += dO S^T;  dk_D += V' dS_next^T;  dk_X += dX S^T
+//   then:  dq = scale diag(gamma) dq_S,  dk = diag(D) dk_D - diag(beta gamma) dk_X;
+//     T = A^T dA,  dL = -T A^T (strictly lower),  G = Gamma (.) K K^T (strictly lower);
+//     M1 = scale dPt (.) Gamma (lower with the diagonal),  E = diag(beta) dL (.) Gamma;
+//     dq += M1 K,  dk += M1^T Q + E K + E^T K;  dbeta and d gl from every term, dg their reverse
+//     cumsum within the chunk.
+// Operands that are not inputs (the recomputed states, every intermediate) are bf16 hi/lo pairs, as
+// in the forward.  Token-by-column intermediates are kept in LDS transposed ([column][token]), so
+// that both the products over tokens and those over columns read them with 8-byte or transposed
+// reads; the tiles are padded (one granule per row) and filled with direct-to-LDS loads.
+#include "gdn_device.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+
+namespace {
+
+template <int DK>
+struct BcLayout {
+    static constexpr int NW = 8;
+    using K = Pad<DK * 2 / 16>;               // K and Q tiles
+    using S = Pad<8>;                         // every 64 x 64 bf16 tile
+    static constexpr int K0 = 0, Q0 = K::BYTES, A0 = 2 * K::BYTES;
+    static constexpr int PH = A0 + S::BYTES, PL = PH + S::BYTES;     // Pt pair [i][j]
+    static constexpr int V0 = PL + S::BYTES, O0 = V0 + S::BYTES;     // V, dO halves [t][c]
+    static constexpr int X0 = O0 + S::BYTES;                         // X, V', dV', dX pairs [c][t]
+    static constexpr int G0 = X0 + 8 * S::BYTES, BYTES = G0 + GB_FLOATS * 4;
+    static constexpr int MD = DK / 16, NKB = DK / 32, NQT = MD / 2;  // dq/dk tiles per wave
+    static_assert(BYTES <= 160 * 1024 - 1024, "LDS budget");
+};
+
+// rows [row0, row0 + 4) of column col of a tile (transposed read; the row0 / col of lane l16 of
+// group grp must be 16 a + 4 grp and 16 b + l16)
+template <typename PT>
+__device__ __forceinline__ bf16x4 col4(const unsigned char *tile, int r16, int c16, int grp, int l16) {
+    return lds_read_tr16(tile + PT::off(16 * r16 + 4 * grp + (l16 >> 2), (16 * c16 + 4 * (l16 & 3)) * 2));
+}
+// the pair of four accumulator values (rows a .. a + 3 of column b) stored transposed: row b,
+// columns a .. a + 3
+template <typename PT>
+__device__ __forceinline__ void put_t(unsigned char *th, unsigned char *tl, int b, int a, const f32x4 &x) {
+    u32x2 hi, lo;
+    split4(x, hi, lo);
+    *reinterpret_cast<u32x2 *>(th + PT::off(b, a * 2)) = hi;
+    *reinterpret_cast<u32x2 *>(tl + PT::off(b, a * 2)) = lo;
+}
+__device__ __forceinline__ float sum16(float x) {   // over the 16 lanes of a group
+    x += __shfl_xor(x, 1, 64);
+    x += __shfl_xor(x, 2, 64);
+    x += __shfl_xor(x, 4, 64);
+    x += __shfl_xor(x, 8, 64);
+    return x;
+}
+__device__ __forceinline__ float sum_groups(float x) {   // over the 4 groups (same l16)
+    x += __shfl_xor(x, 16, 64);
+    x += __shfl_xor(x, 32, 64);
+    return x;
+}
+
+template <int DK>
+__global__ __launch_bounds__(512, 1) void bwd_chunk_mma_kernel(BwdParams p) {
+    using L = BcLayout<DK>;
+    using KT = typename L::K;
+    using ST = typename L::S;
+    constexpr int NKB = L::NKB, MD = L::MD, NQT = L::NQT, NW = L::NW;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[L::BYTES];
+    __shared__ float rdgl[64], rdb[64], rsc[64], rglc[1];
+    unsigned char *tK = lds + L::K0, *tQ = lds + L::Q0, *tA = lds + L::A0, *tPh = lds + L::PH, *tPl = lds + L::PL;
+    unsigned char *tV = lds + L::V0, *tO = lds + L::O0;
+    unsigned char *tXh = lds + L::X0, *tXl = tXh + ST::BYTES, *tVh = tXl + ST::BYTES, *tVl = tVh + ST::BYTES;
+    unsigned char *tDh = tVl + ST::BYTES, *tDl = tDh + ST::BYTES, *tEh = tDl + ST::BYTES, *tEl = tEh + ST::BYTES;
+    const float *g = reinterpret_cast<const float *>(lds + L::G0);
+
+    const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ci = blockIdx.x / p.H_v, h = blockIdx.x - ci * p.H_v;
+    const int hq = h / (p.H_v / p.H_qk);
+    const ChunkInfo cinfo = chunk_info(p.chunks, ci, p.T);
+    const int64_t tok0 = cinfo.tok0;
+    const int nv = cinfo.nv;
+    const int DV = p.D_v, qks = p.H_qk * DK, vs = p.H_v * DV;
+    const float *St = p.states + ((int64_t)ci * p.H_v + h) * DK * DV;
+    const float *dSt = p.dsnext + ((int64_t)ci * p.H_v + h) * DK * DV;
+
+    // ---- tiles: padded rows through direct-to-LDS loads (pad granules read zeros)
+    auto load = [&]<typename PT>(unsigned char *tile, u32x4 r, int stride) __attribute__((always_inline)) {
+        for (int i = w; i < PT::NI; i += NW) {
+            const int pos = 64 * i + lane, row = pos / PT::P, gg = pos % PT::P;
+            dma_granules(r, tile + 1024 * i, gg < PT::P - 1 ? row * stride + 16 * gg : (1 << 30));
+        }
+    };
+    auto load_half = [&](int hv) __attribute__((always_inline)) {
+        const bf16 *vb = static_cast<const bf16 *>(p.v) + tok0 * vs + (int64_t)h * DV + 64 * hv;
+        const bf16 *ob = static_cast<const bf16 *>(p.dout) + tok0 * vs + (int64_t)h * DV + 64 * hv;
+        load.template operator()<ST>(tV, rsrc_words(vb, ((nv - 1) * vs + 64) * 2), vs * 2);
+        load.template operator()<ST>(tO, rsrc_words(ob, ((nv - 1) * vs + 64) * 2), vs * 2);
+    };
+    {
+        const bf16 *kb_ = static_cast<const bf16 *>(p.k) + tok0 * qks + (int64_t)hq * DK;
+        const bf16 *qb = static_cast<const bf16 *>(p.q) + tok0 * qks + (int64_t)hq * DK;
+        load.template operator()<KT>(tK, rsrc_words(kb_, ((nv - 1) * qks + DK) * 2), qks * 2);
+        load.template operator()<KT>(tQ, rsrc_words(qb, ((nv - 1) * qks + DK) * 2), qks * 2);
+        load.template operator()<ST>(tA, rsrc_words(static_cast<const bf16 *>(p.A) + ((int64_t)ci * p.H_v + h) * 4096, 8192), 128);
+        if (w < GB_FLOATS * 4 / 1024)
+            dma_granules(rsrc_words(p.gates + ((int64_t)ci * p.H_v + h) * GB_FLOATS, GB_FLOATS * 4),
+                         lds + L::G0 + 1024 * w, 1024 * w + 16 * lane);
+        load_half(0);
+    }
+    if (tid < 64) rdgl[tid] = rdb[tid] = rsc[tid] = 0.f;
+    if (tid == 0) rglc[0] = 0.f;
+    wait_vm<0>();
+    __syncthreads();
+
+    // gate rows of this lane's accumulator rows 16 a + 4 grp + r
+    auto rows4 = [&](int off, int a) __attribute__((always_inline)) {
+        return *reinterpret_cast<const float4 *>(g + off + 16 * a + 4 * grp);
+    };
+
+    // ---- Pt = scale Gamma (.) Q K^T (lower with the diagonal), a pair [i][j]; tiles w, w + 8
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int tix = w + 8 * q, ti = tix >> 2, tj = tix & 3;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (tj <= ti) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) mma(acc, pi_row<KT>(tQ, 16 * ti + l16, kb, grp), pi_row<KT>(tK, 16 * tj + l16, kb, grp));
+        }
+        const float4 gq = rows4(GB_GLQ, ti);
+        const float glk = g[GB_GLK + 16 * tj + l16];
+        const float gqv[4] = {gq.x, gq.y, gq.z, gq.w};
+        const int j = 16 * tj + l16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = 16 * ti + 4 * grp + r;
+            const float x = j <= i ? p.scale * fast_exp2(gqv[r] - glk) * acc[r] : 0.f;
+            const bf16 hi = (bf16)x;
+            *reinterpret_cast<bf16 *>(tPh + ST::off(i, j * 2)) = hi;
+            *reinterpret_cast<bf16 *>(tPl + ST::off(i, j * 2)) = (bf16)(x - (float)hi);
+        }
+    }
+
+    // accumulators over both halves
+    f32x4 dA[2], dP[2];                                   // 64 x 64 tiles w, w + 8
+    f32x4 dqS[NQT], dkD[NQT], dkX[NQT];                   // dq / dk tiles (tt, m)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) dA[q] = dP[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < NQT; ++q) dqS[q] = dkD[q] = dkX[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int ct = w & 3, tt0 = 2 * (w >> 2);             // token x column tiles of the half
+    const int m = w % MD, qt0 = (w / MD) * NQT;           // dq / dk tiles: rows 16 m of D_k, tokens
+    const float gC = g[GB_GC];
+
+    const int NH = DV / 64;                               // halves of the value columns
+    for (int hv = 0; hv < NH; ++hv) {
+        __syncthreads();   // the half's V and dO tiles have landed; Pt (first half) is complete
+        const int colg = 64 * hv + 16 * ct + l16;          // this lane's value column (P1 - P3)
+        // ---- P1: K S, K dS_next, X
+        f32x4 ks[2], kd[2];
+        {
+            Frag<bf16> sh[NKB], sl[NKB], dh[NKB], dl[NKB];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                float xs[8], xd[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int d = 32 * kb + (e < 4 ? 4 * grp + e : 16 + 4 * grp + e - 4);
+                    xs[e] = St[d * DV + colg];
+                    xd[e] = dSt[d * DV + colg];
+                }
+                split8_rne(xs, sh[kb], sl[kb]);
+                split8_rne(xd, dh[kb], dl[kb]);
+            }
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int tt = tt0 + q;
+                ks[q] = kd[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+                    const Frag<bf16> kf = pi_row<KT>(tK, 16 * tt + l16, kb, grp);
+                    mma_x(ks[q], kf, sh[kb], sl[kb]);
+                    mma_x(kd[q], kf, dh[kb], dl[kb]);
+                }
+            }
+        }
+        float vv[2][4];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int tt = tt0 + q;
+            const bf16x4 v4 = col4<ST>(tV, tt, ct, grp, l16);
+            const float4 be = rows4(GB_BETA, tt), ga = rows4(GB_GAK, tt);
+            const float bev[4] = {be.x, be.y, be.z, be.w}, gav[4] = {ga.x, ga.y, ga.z, ga.w};
+            f32x4 x;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                vv[q][r] = (float)v4[r];
+                x[r] = bev[r] * (vv[q][r] - gav[r] * ks[q][r]);
+            }
+            put_t<ST>(tXh, tXl, 16 * ct + l16, 16 * tt + 4 * grp, x);
+        }
+        __syncthreads();
+        // ---- P2: V' = A X, dV' = diag(D) K dS_next + Pt^T dO; the D terms of d gl
+        f32x4 vp[2], dvp[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int tt = tt0 + q;
+            vp[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                if (32 * kb > 16 * tt + 15) continue;         // A[t][s] = 0 for s > t
+                mma_x(vp[q], pi_row<ST>(tA, 16 * tt + l16, kb, grp), pi_row<ST>(tXh, 16 * ct + l16, kb, grp),
+                      pi_row<ST>(tXl, 16 * ct + l16, kb, grp));
+            }
+            const float4 d4 = rows4(GB_SC, tt);
+            const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dvp[q][r] = dv4[r] * kd[q][r];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                if (32 * kb + 31 < 16 * tt) continue;         // Pt[s][t] = 0 for s < t
+                mma_pair_x(dvp[q], pi_col<ST>(tPh, 16 * tt, kb, grp, l16), pi_col<ST>(tPl, 16 * tt, kb, grp, l16),
+                           pi_col<ST>(tO, 16 * ct, kb, grp, l16));
+            }
+            put_t<ST>(tVh, tVl, 16 * ct + l16, 16 * tt + 4 * grp, vp[q]);
+            put_t<ST>(tDh, tDl, 16 * ct + l16, 16 * tt + 4 * grp, dvp[q]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float cd = sum16(kd[q][r] * vp[q][r]) * dv4[r];
+                if (l16 == 0) {
+                    atomicAdd(&rdgl[16 * tt + 4 * grp + r], -cd);
+                    atomicAdd(&rsc[16 * tt + 4 * grp + r], cd);
+                }
+            }
+        }
+        __syncthreads();
+        // ---- P3: dX = A^T dV', dv, the X terms of dbeta and d gl
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int tt = tt0 + q;
+            f32x4 dx = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                if (32 * kb + 31 < 16 * tt) continue;         // A[s][t] = 0 for s < t
+                mma_x(dx, pi_col<ST>(tA, 16 * tt, kb, grp, l16), pi_row<ST>(tDh, 16 * ct + l16, kb, grp),
+                      pi_row<ST>(tDl, 16 * ct + l16, kb, grp));
+            }
+            const float4 be = rows4(GB_BETA, tt), ga = rows4(GB_GAK, tt);
+            const float bev[4] = {be.x, be.y, be.z, be.w}, gav[4] = {ga.x, ga.y, ga.z, ga.w};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * tt + 4 * grp + r;
+                if (t < nv) p.dv[(tok0 + t) * vs + (int64_t)h * DV + colg] = bev[r] * dx[r];
+                const float db = sum16(dx[r] * (vv[q][r] - gav[r] * ks[q][r]));
+                const float dg = sum16(dx[r] * ks[q][r]);
+                if (l16 == 0) {
+                    atomicAdd(&rdb[t], db);
+                    atomicAdd(&rdgl[t], -bev[r] * gav[r] * dg);
+                }
+            }
+            put_t<ST>(tEh, tEl, 16 * ct + l16, 16 * tt + 4 * grp, dx);
+        }
+        __syncthreads();
+        // ---- P4: the products over this half's columns
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int tix = w + 8 * q, ti = tix >> 2, tj = tix & 3;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                mma_xx(dA[q], pi_col<ST>(tDh, 16 * ti, kb, grp, l16), pi_col<ST>(tDl, 16 * ti, kb, grp, l16),
+                       pi_col<ST>(tXh, 16 * tj, kb, grp, l16), pi_col<ST>(tXl, 16 * tj, kb, grp, l16));
+                if (tj <= ti)
+                    mma_x(dP[q], pi_row<ST>(tO, 16 * ti + l16, kb, grp), pi_col<ST>(tVh, 16 * tj, kb, grp, l16),
+                          pi_col<ST>(tVl, 16 * tj, kb, grp, l16));
+            }
+        }
+        {
+            // S and dS_next rows 16 m + l16 over this half's columns, in pi order
+            Frag<bf16> sh[2], sl[2], dh[2], dl[2];
+            float fro = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                float xs[8], xd[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int c = 64 * hv + 32 * kb + (e < 4 ? 4 * grp + e : 16 + 4 * grp + e - 4);
+                    xs[e] = St[(16 * m + l16) * DV + c];
+                    xd[e] = dSt[(16 * m + l16) * DV + c];
+                    fro += xs[e] * xd[e];
+                }
+                split8_rne(xs, sh[kb], sl[kb]);
+                split8_rne(xd, dh[kb], dl[kb]);
+            }
+            // gamma_C <S, dS_next> (each element once: the waves past the D_k rows' owners skip it)
+            if (w < MD) {
+                fro = sum_groups(sum16(fro));
+                if (lane == 0) atomicAdd(&rglc[0], gC * fro);
+            }
+#pragma unroll
+            for (int q = 0; q < NQT; ++q) {
+                const int tt = qt0 + q;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    mma_x(dqS[q], pi_row<ST>(tO, 16 * tt + l16, kb, grp), sh[kb], sl[kb]);
+                    mma_xx(dkD[q], pi_col<ST>(tVh, 16 * tt, kb, grp, l16), pi_col<ST>(tVl, 16 * tt, kb, grp, l16), dh[kb], dl[kb]);
+                    mma_xx(dkX[q], pi_col<ST>(tEh, 16 * tt, kb, grp, l16), pi_col<ST>(tEl, 16 * tt, kb, grp, l16), sh[kb], sl[kb]);
+                }
+            }
+        }
+        if (hv + 1 < NH) {
+            __syncthreads();   // every wave is done with the first half's tiles
+            load_half(1);
+            wait_vm<0>();
+        }
+    }
+
+    // ---- dq, dk through the states; the q . dq term of d gl
+    f32x4 dq[NQT], dk[NQT];
+#pragma unroll
+    for (int q = 0; q < NQT; ++q) {
+        const int tt = qt0 + q;
+        const float4 gq = rows4(GB_GAQ, tt), d4 = rows4(GB_SC, tt), be = rows4(GB_BETA, tt), ga = rows4(GB_GAK, tt);
+        const float gqv[4] = {gq.x, gq.y, gq.z, gq.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+        const float bev[4] = {be.x, be.y, be.z, be.w}, gav[4] = {ga.x, ga.y, ga.z, ga.w};
+        const bf16x4 q4 = col4<KT>(tQ, tt, m, grp, l16);   // q[t][16 m + l16]
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            dq[q][r] = p.scale * gqv[r] * dqS[q][r];
+            dk[q][r] = dv4[r] * dkD[q][r] - bev[r] * gav[r] * dkX[q][r];
+            const float e = sum16((float)q4[r] * dq[q][r]);
+            if (l16 == 0) atomicAdd(&rdgl[16 * tt + 4 * grp + r], e);
+        }
+    }
+    __syncthreads();   // every wave is done with the pair buffers
+    // ---- dA transposed ([s][t]) into the X buffers
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int tix = w + 8 * q, ti = tix >> 2, tj = tix & 3;
+        put_t<ST>(tXh, tXl, 16 * tj + l16, 16 * ti + 4 * grp, dA[q]);
+    }
+    __syncthreads();
+    // ---- T = A^T dA, transposed ([t][i]) into the V' buffers
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int tix = w + 8 * q, ti = tix >> 2, tj = tix & 3;
+        f32x4 T = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            if (32 * kb + 31 < 16 * ti) continue;             // A[t][i] = 0 for t < i
+            mma_x(T, pi_col<ST>(tA, 16 * ti, kb, grp, l16), pi_row<ST>(tXh, 16 * tj + l16, kb, grp),
+                  pi_row<ST>(tXl, 16 * tj + l16, kb, grp));
+        }
+        put_t<ST>(tVh, tVl, 16 * tj + l16, 16 * ti + 4 * grp, T);
+    }
+    __syncthreads();
+    // ---- dL, G, the L and Pt terms of dbeta and d gl; M1 and E transposed into the dV' and dX buffers
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int tix = w + 8 * q, ti = tix >> 2, tj = tix & 3;
+        f32x4 dl = {0.f, 0.f, 0.f, 0.f}, gm = {0.f, 0.f, 0.f, 0.f};
+        if (tj <= ti) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                if (32 * kb > 16 * tj + 15) continue;         // A[j][t] = 0 for t > j
+                mma_pair_x(dl, pi_col<ST>(tVh, 16 * ti, kb, grp, l16), pi_col<ST>(tVl, 16 * ti, kb, grp, l16),
+                           pi_row<ST>(tA, 16 * tj + l16, kb, grp));
+            }
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) mma(gm, pi_row<KT>(tK, 16 * ti + l16, kb, grp), pi_row<KT>(tK, 16 * tj + l16, kb, grp));
+        }
+        const bf16x4 ph = col4<ST>(tPh, ti, tj, grp, l16), pl = col4<ST>(tPl, ti, tj, grp, l16);
+        const float4 gq = rows4(GB_GLQ, ti), gk = rows4(GB_GLK, ti), be = rows4(GB_BETA, ti);
+        const float gqv[4] = {gq.x, gq.y, gq.z, gq.w}, gkv[4] = {gk.x, gk.y, gk.z, gk.w}, bev[4] = {be.x, be.y, be.z, be.w};
+        const int j = 16 * tj + l16;
+        const float glkj = g[GB_GLK + j];
+        f32x4 m1, e1;
+        float colsum = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = 16 * ti + 4 * grp + r;
+            const bool lo = j < i, le = j <= i;
+            const float dL = lo ? -dl[r] : 0.f;
+            const float G = lo ? fast_exp2(gkv[r] - glkj) * gm[r] : 0.f;
+            const float a = dL * G;
+            const float f = le ? dP[q][r] * ((float)ph[r] + (float)pl[r]) : 0.f;
+            const float u = bev[r] * a + f;                   // + to d gl_i, - to d gl_j
+            colsum += u;
+            const float db = sum16(a), du = sum16(u);
+            if (l16 == 0) {
+                atomicAdd(&rdb[i], db);
+                atomicAdd(&rdgl[i], du);
+            }
+            const float gam = fast_exp2(gqv[r] - glkj);
+            m1[r] = le ? p.scale * dP[q][r] * gam : 0.f;
+            e1[r] = lo ? dL * bev[r] * fast_exp2(gkv[r] - glkj) : 0.f;
+        }
+        colsum = sum_groups(colsum);
+        if (grp == 0) atomicAdd(&rdgl[j], -colsum);
+        put_t<ST>(tDh, tDl, j, 16 * ti + 4 * grp, m1);
+        put_t<ST>(tEh, tEl, j, 16 * ti + 4 * grp, e1);
+    }
+    __syncthreads();
+    // ---- dq += M1 K, dk += M1^T Q + E K + E^T K; stores
+    const int hs = p.dq_v == p.dq ? hq : h, hn = p.dq_v == p.dq ? p.H_qk : p.H_v;
+#pragma unroll
+    for (int q = 0; q < NQT; ++q) {
+        const int tt = qt0 + q;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const Frag<bf16> kc = pi_col<KT>(tK, 16 * m, kb, grp, l16);     // K[j][16 m + l16]
+            if (32 * kb <= 16 * tt + 15) {                    // M1[t][j], E[t][j]: j <= t
+                mma_pair_x(dq[q], pi_col<ST>(tDh, 16 * tt, kb, grp, l16), pi_col<ST>(tDl, 16 * tt, kb, grp, l16), kc);
+                mma_pair_x(dk[q], pi_col<ST>(tEh, 16 * tt, kb, grp, l16), pi_col<ST>(tEl, 16 * tt, kb, grp, l16), kc);
+            }
+            if (32 * kb + 31 >= 16 * tt) {                    // M1[j][t], E[j][t]: j >= t
+                mma_pair_x(dk[q], pi_row<ST>(tDh, 16 * tt + l16, kb, grp), pi_row<ST>(tDl, 16 * tt + l16, kb, grp),
+                           pi_col<KT>(tQ, 16 * m, kb, grp, l16));
+                mma_pair_x(dk[q], pi_row<ST>(tEh, 16 * tt + l16, kb, grp), pi_row<ST>(tEl, 16 * tt + l16, kb, grp), kc);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * tt + 4 * grp + r;
+            if (t < nv) {
+                const int64_t o = ((tok0 + t) * hn + hs) * DK + 16 * m + l16;
+                p.dq_v[o] = dq[q][r];
+                p.dk_v[o] = dk[q][r];
+            }
+        }
+    }
+    __syncthreads();   // every row term of d gl and dbeta is in
+    if (tid < 64) {
+        float x = tid < nv ? rdgl[tid] : 0.f;
+        if (tid == max(nv - 1, 0)) {
+            float s = rglc[0];
+            for (int j = 0; j < 64; ++j) s += rsc[j];
+            x += s;
+        }
+        const float incl = wave_inclusive_scan(x);
+        const float tot = __shfl(incl, 63, 64);
+        if (tid < nv) {
+            p.dg[(tok0 + tid) * p.H_v + h] = tot - incl + x;
+            p.dbeta[(tok0 + tid) * p.H_v + h] = rdb[tid];
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_bwd_chunk_mma(int D_k, const BwdParams &p, hipStream_t s) {
+    const int64_t chunks = (int64_t)p.n_chunks * p.H_v;
+    if (chunks == 0) return hipSuccess;
+    if (p.D_v != 64 && p.D_v != 128) return hipErrorInvalidValue;
+    if (D_k == 128) hipLaunchKernelGGL((bwd_chunk_mma_kernel<128>), dim3((unsigned)chunks), dim3(512), 0, s, p);
+    else if (D_k == 64) hipLaunchKernelGGL((bwd_chunk_mma_kernel<64>), dim3((unsigned)chunks), dim3(512), 0, s, p);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace gdn

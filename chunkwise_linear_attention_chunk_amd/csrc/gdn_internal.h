@@ -230,6 +230,8 @@ hipError_t launch_cp_fix_xyz(int D_k, const FixParams &p, hipStream_t s);
 hipError_t launch_cp_fix(int dtype, int D_k, const FixParams &p, hipStream_t s);
 hipError_t launch_warm_stats(const WarmParams &p, hipStream_t s);
 hipError_t launch_bwd(int dtype, int D_k, const BwdParams &p, hipStream_t s);
+// the per-chunk gradients on the matrix cores (bf16 inputs, scalar gate)
+hipError_t launch_bwd_chunk_mma(int D_k, const BwdParams &p, hipStream_t s);
 hipError_t launch_recurrent(int dtype, int D_k, int gate, const RecurrentParams &p, hipStream_t s);
 
 }  // namespace gdn
