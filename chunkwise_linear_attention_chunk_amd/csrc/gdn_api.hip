@@ -241,13 +241,14 @@ gdn_status validate_and_plan(const gdn_fwd_args *a, Plan *pl, bool allow_pieces 
     pl->off_order = off;  off = align_up(off + (size_t)pl->total_segs * sizeof(int));
     const size_t tiles = (size_t)nch * a->H_v;
     // P is formed by the recurrence kernel itself with a scalar gate; with per-channel gates the
-    // intra kernel forms it (its exponent factors live inside the contraction)
-    pl->off_P = off;       if (channel) off = align_up(off + tiles * (esz == 2 ? 2 : 1) * 64 * 64 * esz);
+    // intra kernel forms it (its exponent factors live inside the contraction).  The per-channel
+    // operands (P, Kg, Kd, Qg, A) are one part each: fp16 for bf16 inputs, fp32 for fp32 inputs.
+    pl->off_P = off;       if (channel) off = align_up(off + tiles * 64 * 64 * esz);
     pl->off_gates = off;   off = align_up(off + tiles * gdn::GB_FLOATS * sizeof(float));
     if (channel) {
         pl->off_kg = off;  off = align_up(off + tiles * 64 * a->D_k * esz);
-        pl->off_kd = off;  off = align_up(off + tiles * (esz == 2 ? 2 : 1) * 64 * a->D_k * esz);
-        pl->off_qg = off;  off = align_up(off + tiles * (esz == 2 ? 2 : 1) * 64 * a->D_k * esz);
+        pl->off_kd = off;  off = align_up(off + tiles * 64 * a->D_k * esz);
+        pl->off_qg = off;  off = align_up(off + tiles * 64 * a->D_k * esz);
     }
     if (pl->warm) {
         pl->off_warm = off;  off = align_up(off + seg_heads * sizeof(int));

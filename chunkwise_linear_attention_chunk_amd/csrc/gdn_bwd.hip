@@ -762,7 +762,8 @@ __global__ __launch_bounds__(kBwT) void bwd_chunk_kernel(BwdParams p) {
 //             dG = q (.) dq + k (.) (dk_X + dk_Lrow) - k (.) (dk_D + dk_P + dk_Lcol), the e^{G_C} terms
 //             on the last valid row, and dgk its reverse cumsum within the chunk per channel.
 // Two kernels per chunk: (a) the products with S and dS_next over value-column blocks, dL; (b) the
-// P and L terms with their per-channel factors.
+// P and L terms with their per-channel factors.  The inverse A is read as the per-chunk kernel
+// stores it for per-channel gates (fp16 for bf16 inputs).
 
 // chunk-local cumsum of per-channel log-gates: G (fp32 LDS rows of stride ld) holds the raw gates
 // of the chunk (zero past the end) on entry; the first DK threads scan one channel each
@@ -811,7 +812,7 @@ __global__ __launch_bounds__(kBwT) void bwd_states_kda_kernel(BwdParams p) {
         load_rows<DK, T, NT>(&sKg[0][0], DK + 1, static_cast<const T *>(p.k) + (int64_t)hq * DK, tok0, nv, (int64_t)p.H_qk * DK, 0);
         load_rows<DK, T, NT>(&sKd[0][0], DK + 1, static_cast<const T *>(p.g) + (int64_t)h * DK, tok0, nv, gks, 0);
         load_rows<kBwR, T, NT>(&sV[0][0], kBwR + 1, static_cast<const T *>(p.v) + (int64_t)h * DV, tok0, nv, (int64_t)p.H_v * DV, cb * kBwR);
-        load_tile64<T, NT>(sA, static_cast<const T *>(p.A) + (gci * p.H_v + h) * 4096);
+        load_tile64<typename KdaOperand<T>::type, NT>(sA, static_cast<const typename KdaOperand<T>::type *>(p.A) + (gci * p.H_v + h) * 4096);
         if (tid < 64) load_beta<T>(p, tok0, nv, h, sb);
         cumsum_rows<DK>(&sKd[0][0], DK + 1);                 // sKd holds G
         if (tid < DK) sgc[tid] = sKd[63][tid];
@@ -929,7 +930,7 @@ __global__ __launch_bounds__(kBwT) void bwd_dstate_kda_kernel(BwdParams p) {
         load_rows<DK, T, NT>(&sKd[0][0], DK + 1, static_cast<const T *>(p.g) + (int64_t)h * DK, tok0, nv, (int64_t)p.H_v * DK, 0);
         load_rows<kBw, T, NT>(&sdO[0][0], kBw + 1, static_cast<const T *>(p.dout) + (int64_t)h * DV, tok0, nv, (int64_t)p.H_v * DV,
                        cb * kBw);
-        load_tile64<T, NT>(sA, static_cast<const T *>(p.A) + (gci * p.H_v + h) * 4096);
+        load_tile64<typename KdaOperand<T>::type, NT>(sA, static_cast<const typename KdaOperand<T>::type *>(p.A) + (gci * p.H_v + h) * 4096);
         load_tile64<float, NT>(sP, p.pmat + (gci * p.H_v + h) * 4096);
         if (tid < 64) load_beta<T>(p, tok0, nv, h, sb);
         cumsum_rows<DK>(&sKd[0][0], DK + 1);                 // sKd holds G
@@ -1028,7 +1029,7 @@ __global__ __launch_bounds__(kBwT) void bwd_chunk_kda_a_kernel(BwdParams p) {
     const int64_t DV = p.D_v, qks = (int64_t)p.H_qk * DK, vs = (int64_t)p.H_v * DV;
     load_rows<DK, T, NT>(&sKg[0][0], DK + 1, static_cast<const T *>(p.k) + (int64_t)hq * DK, tok0, nv, qks, 0);
     load_rows<DK, T, NT>(&sKd[0][0], DK + 1, static_cast<const T *>(p.g) + (int64_t)h * DK, tok0, nv, (int64_t)p.H_v * DK, 0);
-    load_tile64<T, NT>(sA, static_cast<const T *>(p.A) + ((int64_t)ci * p.H_v + h) * 4096);
+    load_tile64<typename KdaOperand<T>::type, NT>(sA, static_cast<const typename KdaOperand<T>::type *>(p.A) + ((int64_t)ci * p.H_v + h) * 4096);
     load_tile64<float, NT>(sP, p.pmat + ((int64_t)ci * p.H_v + h) * 4096);
     for (int idx = tid; idx < 4096; idx += NT) sdA[idx / 64][idx % 64] = 0.f;
     if (tid < 64) {

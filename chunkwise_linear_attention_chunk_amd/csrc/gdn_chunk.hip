@@ -938,9 +938,10 @@ static hipError_t launch_rec(int dtype, int D_k, int BV, const ChunkParams &p, h
         return hipGetLastError();                                                                         \
     }
     if constexpr (GATE == GDN_GATE_CHANNEL_K) {
-        // the gated and decayed K tiles and P take LDS: one tile buffer for D_k = 128
-        GDN_CHUNK_CASE(1, bf16, 128, 2, 1)
-        GDN_CHUNK_CASE(1, bf16, 64, 2, 2)
+        // bf16 inputs: the per-chunk kernel's gated tiles, P and A are fp16 operands (one part each),
+        // so two tile buffers fit
+        GDN_CHUNK_CASE(1, f16, 128, 2, 2)
+        GDN_CHUNK_CASE(1, f16, 64, 2, 2)
         GDN_CHUNK_CASE(0, float, 128, 1, 1)
         GDN_CHUNK_CASE(0, float, 64, 1, 1)
     } else {

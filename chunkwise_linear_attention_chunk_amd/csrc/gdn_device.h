@@ -20,6 +20,9 @@ namespace gdn {
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // raw 16 bytes (a native vector, so
@@ -30,10 +33,14 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 template <typename T> struct Frag;
 template <> struct Frag<bf16> { bf16x8 v; };
+template <> struct Frag<f16> { f16x8 v; };
 template <> struct Frag<float> { float v[8]; };
 
 __device__ __forceinline__ void mma(f32x4 &c, const Frag<bf16> &a, const Frag<bf16> &b) {
     c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4 &c, const Frag<f16> &a, const Frag<f16> &b) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.v, b.v, c, 0, 0, 0);
 }
 __device__ __forceinline__ void mma(f32x4 &c, const Frag<float> &a, const Frag<float> &b) {
 #pragma unroll
@@ -58,9 +65,11 @@ __device__ __forceinline__ Frag<float> ld8(const float *p) {
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+template <> __device__ __forceinline__ f16 from_f32<f16>(float x) { return (f16)x; }
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(f16 x) { return (float)x; }
 
 // Store 4 consecutive values (one accumulator column run) at p.
 __device__ __forceinline__ void st4(bf16 *p, float a, float b, float c, float d) {
@@ -74,8 +83,14 @@ __device__ __forceinline__ void st4(float *p, float a, float b, float c, float d
 // Precision policy of matrix-core operands that are not exact inputs.  bf16 operands are carried
 // as a pair x = hi + lo (hi = bf16(x), lo = bf16(x - hi)): a product with an exact bf16 operand
 // takes two MFMAs, a product of two such pairs three (lo * lo dropped), for ~16 mantissa bits.
-// fp32 operands need no split.
+// fp16 operands (11 significant bits, rounded to nearest) and fp32 operands need no split.
 template <typename T> struct Split { static constexpr int parts = 1; };
+template <typename T> inline constexpr bool is_f16 = false;
+template <> inline constexpr bool is_f16<f16> = true;
+// Element type of the per-channel-gate operands the per-chunk kernel stores (gated K and Q tiles,
+// P, the inverse A): fp16 for bf16 inputs, fp32 for fp32 inputs.
+template <typename T> struct KdaOperand { using type = T; };
+template <> struct KdaOperand<bf16> { using type = f16; };
 template <> struct Split<bf16> { static constexpr int parts = 2; };
 
 __device__ __forceinline__ void st4_split(bf16 *hi, bf16 *lo, const f32x4 &x) {
@@ -90,6 +105,7 @@ __device__ __forceinline__ void st4_split(float *hi, float *, const f32x4 &x) {
 }
 
 __device__ __forceinline__ void set_elem(Frag<bf16> &f, int e, bf16 x) { f.v[e] = x; }
+__device__ __forceinline__ void set_elem(Frag<f16> &f, int e, f16 x) { f.v[e] = x; }
 __device__ __forceinline__ void set_elem(Frag<float> &f, int e, float x) { f.v[e] = x; }
 
 // ---- operands taken from accumulator registers ----------------------------------------------
@@ -111,6 +127,11 @@ __device__ __forceinline__ void split8(const float *x, Frag<bf16> &h, Frag<bf16>
         h.v[e] = __builtin_bit_cast(bf16, (unsigned short)(bits >> 16));
         l.v[e] = (bf16)(x[e] - __uint_as_float(bits));
     }
+}
+// fp16: one rounding to nearest (v_cvt_pk_f16_f32 per two values), no lo part
+__device__ __forceinline__ void split8(const float *x, Frag<f16> &h, Frag<f16> &) {
+    typedef float f32x8 __attribute__((ext_vector_type(8)));
+    h.v = __builtin_convertvector(f32x8{x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]}, f16x8);
 }
 __device__ __forceinline__ void split8(const float *x, Frag<float> &h, Frag<float> &) {
 #pragma unroll
@@ -228,10 +249,14 @@ __device__ __forceinline__ Frag<T> ldpi_tile(const unsigned char *tile, int row,
     const int grp = (threadIdx.x & 63) >> 4;
     const int c0 = 32 * kb + 4 * grp, c1 = c0 + 16;
     Frag<T> f;
-    if constexpr (sizeof(T) == 2) {
+    if constexpr (sizeof(T) == 2 && !is_f16<T>) {
         const bf16x4 a = *reinterpret_cast<const bf16x4 *>(tile + tile_off<GPR, 2>(row, c0));
         const bf16x4 b = *reinterpret_cast<const bf16x4 *>(tile + tile_off<GPR, 2>(row, c1));
         f.v = bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    } else if constexpr (is_f16<T>) {
+        const f16x4 a = *reinterpret_cast<const f16x4 *>(tile + tile_off<GPR, 2>(row, c0));
+        const f16x4 b = *reinterpret_cast<const f16x4 *>(tile + tile_off<GPR, 2>(row, c1));
+        f.v = f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
     } else {
         const float4 a = *reinterpret_cast<const float4 *>(tile + tile_off<GPR, 4>(row, c0));
         const float4 b = *reinterpret_cast<const float4 *>(tile + tile_off<GPR, 4>(row, c1));
@@ -252,7 +277,8 @@ __device__ __forceinline__ Frag<T> ldpi_col_tile(const unsigned char *tile, int 
         const int t0 = 32 * kb + 4 * grp + e;
         const bf16x4 a = lds_read_tr16(tile + tile_off<GPR, 2>(t0, d0 + 4 * q));
         const bf16x4 b = lds_read_tr16(tile + tile_off<GPR, 2>(t0 + 16, d0 + 4 * q));
-        f.v = bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+        // (the transpose moves 16-bit lanes: fp16 tiles come back bit for bit)
+        f.v = __builtin_bit_cast(decltype(f.v), bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]});
     } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {

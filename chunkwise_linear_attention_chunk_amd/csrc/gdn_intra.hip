@@ -324,10 +324,14 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraParams p) {
 //   P[i][j]     = scale sum_d q_id k_jd 2^(G_id - G_jd)            (j <= i)
 //   A = (I + A_raw)^{-1},  Kg = K (.) 2^G,  Qg = Q (.) 2^G,  Kd = K (.) 2^(G_C - G),  decay = 2^G_C
 // (G_C: G at the last valid token; tail rows are zero in every output).  The recurrence kernel
-// then runs the scalar-gate schedule on these operands, with P read instead of formed.  Kd and Qg
-// are stored as hi/lo bf16 pairs like P: rounded once they would move the state and the output by
-// about 1e-2 RMS (the decay factors make them inexact, unlike K and Q themselves); Kg is rounded
-// once, its effect is an order of magnitude smaller.
+// then runs the scalar-gate schedule on these operands, with P read instead of formed.  The
+// decay factors make Kg, Kd, Qg inexact (unlike K and Q themselves), and bf16 rounding of Kd or Qg
+// would move the state or the output by about 1e-2 RMS; so for bf16 inputs every stored operand
+// (Kg, Kd, Qg, P, A) is fp16, rounded to nearest once (11 significant bits), and the recurrence
+// multiplies them on the fp16 matrix cores.  This needs each stored value below 65504 in
+// magnitude, which holds for L2-normalised q and k rows (the method's convention): decayed
+// entries of unit rows, P of at most scale in size, and the inverse of I plus a strictly lower
+// Gram-like matrix.
 //
 // The pairwise factor 2^(G_i - G_j) is split per 16x16 tile at a reference row r between j and i
 // (r = last row of the column block for tiles below the diagonal, the first row of the block on
@@ -336,7 +340,7 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraParams p) {
 // A diagonal tile whose gates decay by more than 2^-64 across its 16 rows in some channel (where
 // right_j could overflow and left_i underflow) forms each pair's factor 2^(G_i - G_j) <= 1 whole, in
 // fp32 on the vector ALU, so no gate value can produce inf or NaN.
-// P's operands are carried as hi/lo bf16 pairs (three MFMAs per block); A_raw's are rounded once.
+// Inside this kernel P's operands are hi/lo bf16 pairs (three MFMAs per block), A_raw's rounded once.
 // ------------------------------------------------------------------------------------------
 // PRO: some part of the prologue is on (q/k L2 norm, gate activation, sigma(beta)); the template
 // flag keeps all of it out of the plain build, whose timing it would otherwise change
@@ -346,6 +350,8 @@ constexpr float kMaxRange = 64.f;
 
 template <typename T, int DK, bool PRO>
 __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
+    using OT = typename KdaOperand<T>::type;
+    static_assert(sizeof(OT) == sizeof(T), "stored operands keep the input's element size");
     constexpr int VEC = Vec16<T>::N;
     constexpr int KP = DK + VEC;   // row stride of the K and Q tiles
     constexpr int LP = 64 + 4;     // row stride of the fp32 64x64 tiles
@@ -353,7 +359,6 @@ __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
     constexpr int K_BYTES = 64 * KP * (int)sizeof(T);
     constexpr int X_BYTES = 64 * LP * 4;
     constexpr int R0 = K_BYTES > X_BYTES ? K_BYTES : X_BYTES;
-    constexpr int NS = Split<T>::parts;
     constexpr int NKB = DK / 32;
     // region 0: K tile, later the inverse X; region 1: A_raw.  Q stays in registers: each thread's
     // share for the gated output, and each lane's operand rows for P.
@@ -482,13 +487,12 @@ __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
 
     // ---- gated operands of the recurrence and the per-channel chunk decay
     const int64_t tile = ((int64_t)ci * p.H_v + h) * 64 * DK;
-    T *kg = static_cast<T *>(p.kg) + tile;
-    T *kd = static_cast<T *>(p.kd) + NS * tile, *qg = static_cast<T *>(p.qg) + NS * tile;  // NS tiles each
+    OT *kg = static_cast<OT *>(p.kg) + tile, *kd = static_cast<OT *>(p.kd) + tile, *qg = static_cast<OT *>(p.qg) + tile;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int idx = tid + 256 * i, row = idx / VPR, c0 = (idx % VPR) * VEC;
-        T vk[VEC], qs[VEC];
-        float xd[VEC], xq[VEC];
+        T qs[VEC];
+        OT vk[VEC], vq[VEC], vd[VEC];
         *reinterpret_cast<u32x4 *>(qs) = qv[i];
         const float rk = PRO ? sRk[row] : 1.f, rq = PRO ? sRq[row] : 1.f;   // L2-norm factors (else 1)
 #pragma unroll
@@ -496,23 +500,13 @@ __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
             const float G = sG[row * GP + c0 + e], GC = sG[last * GP + c0 + e];
             const float kk = to_f32(sK[row * KP + c0 + e]) * rk, qq = to_f32(qs[e]) * rq;
             const float eg = fast_exp2(G);
-            vk[e] = from_f32<T>(kk * eg);
-            xq[e] = qq * eg;
-            xd[e] = kk * fast_exp2(GC - G);
+            vk[e] = from_f32<OT>(kk * eg);
+            vq[e] = from_f32<OT>(qq * eg);
+            vd[e] = from_f32<OT>(kk * fast_exp2(GC - G));
         }
         *reinterpret_cast<u32x4 *>(kg + row * DK + c0) = *reinterpret_cast<const u32x4 *>(vk);
-        if constexpr (NS == 2) {
-            Frag<bf16> hi, lo;
-            split8(xq, hi, lo);
-            *reinterpret_cast<bf16x8 *>(qg + row * DK + c0) = hi.v;
-            *reinterpret_cast<bf16x8 *>(qg + 64 * DK + row * DK + c0) = lo.v;
-            split8(xd, hi, lo);
-            *reinterpret_cast<bf16x8 *>(kd + row * DK + c0) = hi.v;
-            *reinterpret_cast<bf16x8 *>(kd + 64 * DK + row * DK + c0) = lo.v;
-        } else {
-            *reinterpret_cast<u32x4 *>(qg + row * DK + c0) = *reinterpret_cast<const u32x4 *>(xq);
-            *reinterpret_cast<u32x4 *>(kd + row * DK + c0) = *reinterpret_cast<const u32x4 *>(xd);
-        }
+        *reinterpret_cast<u32x4 *>(qg + row * DK + c0) = *reinterpret_cast<const u32x4 *>(vq);
+        *reinterpret_cast<u32x4 *>(kd + row * DK + c0) = *reinterpret_cast<const u32x4 *>(vd);
     }
     float *gbk = p.gates + ((int64_t)ci * p.H_v + h) * GB_FLOATS;
     if (tid < DK) gbk[GB_DEC + tid] = fast_exp2(sG[last * GP + tid]);
@@ -534,7 +528,7 @@ __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
     }
 
     // ---- A_raw (strict lower) and P (lower with diagonal): the 10 lower 16x16 tiles
-    T *P = static_cast<T *>(p.P) + ((int64_t)ci * p.H_v + h) * NS * 4096;
+    OT *P = static_cast<OT *>(p.P) + ((int64_t)ci * p.H_v + h) * 4096;
     f32x4 pacc[3];
 #pragma unroll
     for (int n = 0; n < 3; ++n) {
@@ -614,10 +608,10 @@ __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
         pacc[n] = pa;
     }
     // P through the K tile's region (no longer read), then A_raw is complete and the region holds X
-    store_p<T>(smem, P, pacc, TI, TJ, ntiles);   // (its barriers also publish sWarm)
+    store_p<OT>(smem, P, pacc, TI, TJ, ntiles);   // (its barriers also publish sWarm)
     if (tid == 0) gbk[GB_GC] = fast_exp2(sWarm[0] + sWarm[1] + sWarm[2] + sWarm[3]);
     invert_unit_lower(sL, sX);
-    store_unit_lower<T>(sX, static_cast<T *>(p.A) + ((int64_t)ci * p.H_v + h) * 4096);
+    store_unit_lower<OT>(sX, static_cast<OT *>(p.A) + ((int64_t)ci * p.H_v + h) * 4096);
 }
 
 }  // namespace
