@@ -10,8 +10,8 @@
 // FlashQLA announcement (Qwen), the first step of the chunk-i forward.
 //
 // The inverse is computed in fp32 throughout (the pages use tf32 dots for the merges; gfx950
-// has no tf32 path, so the merges run on fp32 MFMA).  A is stored in the input dtype, P (per-channel
-// gates) as an operand pair (hi, lo) in bf16 or whole in fp32.
+// has no tf32 path, so the merges run on fp32 MFMA).  With a scalar gate A is stored in the input
+// dtype; with per-channel gates A and P are stored as fp16 for bf16 inputs, fp32 for fp32 inputs.
 //
 // One workgroup of 256 threads (4 waves) per (chunk, head); many workgroups per CU hide the
 // latency of the serial 16-step substitutions.
@@ -116,45 +116,6 @@ __device__ __forceinline__ void store_unit_lower(const float *sX, T *A) {
         }
         *reinterpret_cast<u32x4 *>(A + row * 64 + c0) = out;
     }
-}
-
-// Store P from this wave's accumulator tiles (lane: rows 4 grp + r, column l16 of tile (ti, tj)):
-// staged through `stage` (LDS, at least parts * 8 KiB, free from the barrier at entry on) as the NS
-// tiles [64][64] of the output (hi, then lo for bf16; fp32 whole), then written with 16-byte stores.
-// Tiles above the diagonal are written as zeros.  Called by all 256 threads; returns after a
-// barrier, `stage` free again.
-template <typename T>
-__device__ __forceinline__ void store_p(void *stage, T *P, const f32x4 *pa, const int *ti, const int *tj, int ntiles) {
-    constexpr int NS = Split<T>::parts, VEC = Vec16<T>::N;
-    const int lane = threadIdx.x & 63, l16 = lane & 15, grp = lane >> 4;
-    T *sp = static_cast<T *>(stage);
-    __syncthreads();  // every wave is done with the staging region's previous contents
-#pragma unroll
-    for (int n = 0; n < 3; ++n) {
-        if (n >= ntiles) break;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int off = (16 * ti[n] + 4 * grp + r) * 64 + 16 * tj[n] + l16;
-            const float x = pa[n][r];
-            if constexpr (NS == 2) {
-                const uint32_t bits = __float_as_uint(x) & 0xffff0000u;
-                sp[off] = __builtin_bit_cast(bf16, (unsigned short)(bits >> 16));
-                sp[4096 + off] = (bf16)(x - __uint_as_float(bits));
-            } else {
-                sp[off] = from_f32<T>(x);
-            }
-        }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int it = 0; it < NS * 4096 / VEC / 256; ++it) {
-        const int idx = threadIdx.x + 256 * it;
-        const int e0 = idx * VEC, row = (e0 & 4095) >> 6, col = e0 & 63;
-        u32x4 v = *reinterpret_cast<const u32x4 *>(sp + e0);
-        if ((col >> 4) > (row >> 4)) v = u32x4{0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4 *>(P + e0) = v;
-    }
-    __syncthreads();
 }
 
 // Scalar gate: A and the gate block.  Only K (and later the inverse) and A_raw use LDS.
@@ -345,8 +306,9 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraParams p) {
 // PRO: some part of the prologue is on (q/k L2 norm, gate activation, sigma(beta)); the template
 // flag keeps all of it out of the plain build, whose timing it would otherwise change
 // Largest decay (in log2 units) across a diagonal 16-row block for which the split factors of that
-// block are used: the key factor is then at most 2^64 and the query/key factor at least 2^-64.
-constexpr float kMaxRange = 64.f;
+// block are used: the key factor is then at most 2^64 and the query/key factor at least 2^-64
+// (fp32 operands), or at most 2^12 and at least 2^-12 (fp16 operands: inside their normal range).
+constexpr float kMaxRange = 64.f, kMaxRangeF16 = 12.f;
 
 template <typename T, int DK, bool PRO>
 __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
@@ -527,9 +489,22 @@ __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
         if (lane == 0) sWarm[wave] = x;
     }
 
-    // ---- A_raw (strict lower) and P (lower with diagonal): the 10 lower 16x16 tiles
+    // ---- A_raw (strict lower) and P (lower with diagonal): the 10 lower 16x16 tiles.  The operands
+    //      are rounded once to the stored type (fp16 or fp32).  P is formed transposed (keys as the
+    //      rows of the product), so each lane holds four consecutive key columns of one query row
+    //      and stores them straight from its registers; the two tiles above the diagonal that the
+    //      recurrence reads, (0, 1) and (2, 3), are written as zeros by the waves with two tiles.
     OT *P = static_cast<OT *>(p.P) + ((int64_t)ci * p.H_v + h) * 4096;
-    f32x4 pacc[3];
+    constexpr float range_max = is_f16<OT> ? kMaxRangeF16 : kMaxRange;
+    auto store_p4 = [&](int row, int col, const f32x4 &x) __attribute__((always_inline)) {
+        if constexpr (is_f16<OT>) {
+            const f16x4 v = {(f16)x[0], (f16)x[1], (f16)x[2], (f16)x[3]};
+            *reinterpret_cast<f16x4 *>(P + row * 64 + col) = v;
+        } else {
+            *reinterpret_cast<float4 *>(P + row * 64 + col) = make_float4(x[0], x[1], x[2], x[3]);
+        }
+    };
+    if (ntiles == 2) store_p4(16 * (wave == 2 ? 0 : 2) + l16, 16 * (wave == 2 ? 1 : 3) + 4 * grp, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
     for (int n = 0; n < 3; ++n) {
         if (n >= ntiles) break;
@@ -550,27 +525,33 @@ __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
             for (int d = lane; d < DK; d += 64) range = fmaxf(range, sG[16 * I * GP + d] - sG[(16 * I + 15) * GP + d]);
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) range = fmaxf(range, __shfl_xor(range, off, 64));
-            whole = range > kMaxRange;
+            whole = range > range_max;
         }
         if (whole) {
-            // lane: rows i = 16 I + 4 grp + rr, column j = 16 I + l16 (the accumulator layout)
+            // A_raw: rows ii = 16 I + 4 grp + rr, column j = 16 I + l16 (the accumulator layout);
+            // P: query row i = 16 I + l16, key columns ii (the transposed layout)
+            const T *qi = q + ((int64_t)(t0 + min(i, last)) * p.H_qk + hq) * DK;
 #pragma unroll 1
             for (int rr = 0; rr < 4; ++rr) {
                 const int ii = 16 * I + 4 * grp + rr;
-                const T *qi = q + ((int64_t)(t0 + min(ii, last)) * p.H_qk + hq) * DK;
                 float sa = 0.f, sp = 0.f;
-                if (j <= ii) {
+                if (j < ii) {
 #pragma unroll 4
                     for (int d = 0; d < DK; ++d) {
                         const float e = fast_exp2(sG[ii * GP + d] - sG[j * GP + d]);   // <= 1
-                        const float kj = to_f32(sK[j * KP + d]) * e;
-                        sa += to_f32(sK[ii * KP + d]) * kj;
-                        sp += to_f32(qi[d]) * kj;
+                        sa += to_f32(sK[ii * KP + d]) * to_f32(sK[j * KP + d]) * e;
                     }
                 }
-                const float qm = ii < nv ? (PRO ? sRq[ii] : 1.f) : 0.f;
-                aa[rr] = sa * (PRO ? sRk[ii] : 1.f) * rkj;
-                pa[rr] = sp * qm * rkj;
+                if (ii <= i) {
+#pragma unroll 4
+                    for (int d = 0; d < DK; ++d) {
+                        const float e = fast_exp2(sG[i * GP + d] - sG[ii * GP + d]);   // <= 1
+                        sp += to_f32(qi[d]) * to_f32(sK[ii * KP + d]) * e;
+                    }
+                }
+                const float rkii = PRO ? sRk[ii] : 1.f;
+                aa[rr] = sa * rkii * rkj;
+                pa[rr] = sp * qmask * rkii;
             }
         }
 #pragma unroll
@@ -586,29 +567,26 @@ __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
                 ql[e] = qmask * to_f32(qt[n][kb].v[e]) * el;
                 kr[e] = to_f32(sK[j * KP + d0 + e]) * (rkj * er);
             }
-            Frag<T> fkl, fkr;
+            Frag<OT> fkl, fkr, fql;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                set_elem(fkl, e, from_f32<T>(kl[e]));
-                set_elem(fkr, e, from_f32<T>(kr[e]));
+                set_elem(fkl, e, from_f32<OT>(kl[e]));
+                set_elem(fkr, e, from_f32<OT>(kr[e]));
+                set_elem(fql, e, from_f32<OT>(ql[e]));
             }
             mma(aa, fkl, fkr);
-            Frag<T> qh, qlo, krh, krl;
-            split8(ql, qh, qlo);
-            split8(kr, krh, krl);
-            mma_xx(pa, qh, qlo, krh, krl);
+            mma(pa, fkr, fql);   // P^T: row 4 grp + rr of key block J, column l16 of query block I
         }
         const int jj = 16 * J + l16;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
             const int ii = 16 * I + 4 * grp + rr;
             sL[ii * LP + jj] = jj < ii ? sB[ii] * aa[rr] : 0.f;
-            pa[rr] = jj <= ii ? p.scale * pa[rr] : 0.f;
+            pa[rr] = 16 * J + 4 * grp + rr <= i ? p.scale * pa[rr] : 0.f;
         }
-        pacc[n] = pa;
+        store_p4(i, 16 * J + 4 * grp, pa);
     }
-    // P through the K tile's region (no longer read), then A_raw is complete and the region holds X
-    store_p<OT>(smem, P, pacc, TI, TJ, ntiles);   // (its barriers also publish sWarm)
+    __syncthreads();   // A_raw is complete in sL, the partial decay bounds in sWarm; the K tile is free
     if (tid == 0) gbk[GB_GC] = fast_exp2(sWarm[0] + sWarm[1] + sWarm[2] + sWarm[3]);
     invert_unit_lower(sL, sX);
     store_unit_lower<OT>(sX, static_cast<OT *>(p.A) + ((int64_t)ci * p.H_v + h) * 4096);
