@@ -590,6 +590,9 @@ extern "C" gdn_status gdn_bwd(const gdn_bwd_args *a, void *workspace, size_t wor
     gdn::BwdParams bw{};
     bw.q = a->q; bw.k = a->k; bw.v = a->v; bw.beta = a->beta; bw.dout = a->dout;
     bw.g = a->g; bw.h0 = a->h0; bw.dht = a->dht; bw.A = ws + pl.off_A;
+    if (channel) {
+        bw.P = ws + pl.off_P; bw.kg = ws + pl.off_kg; bw.kd = ws + pl.off_kd; bw.qg = ws + pl.off_qg;
+    }
     bw.gates = reinterpret_cast<const float *>(ws + pl.off_gates);
     bw.seq = seq; bw.chunks = chunks;
     bw.T = a->T; bw.N = a->N; bw.n_chunks = (int)pl.total_chunks; bw.H_qk = a->H_qk; bw.H_v = a->H_v; bw.D_v = a->D_v;

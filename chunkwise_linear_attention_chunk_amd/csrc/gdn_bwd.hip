@@ -483,6 +483,245 @@ __global__ __launch_bounds__(128, 1) void bwd_dstate_mma_kernel(BwdParams p) {
     }
 }
 
+// fp16 view of a 16-bit operand fragment read from an fp16 tile
+__device__ __forceinline__ Frag<f16> as_f16(const Frag<bf16> &f) {
+    Frag<f16> r;
+    r.v = __builtin_bit_cast(f16x8, f.v);
+    return r;
+}
+
+// ---- reverse scan of the state gradient on the matrix cores (per-channel gates, bf16 inputs): the
+//      quantities of bwd_dstate_kda_kernel, from the fp16 operands the per-chunk kernel stores for
+//      every chunk (Kd = K (.) e^{G_C - G}, Kg = K (.) e^G, Qg = Q (.) e^G, scale P, A).  One
+//      workgroup per (sequence, value head, 32 value columns), two waves; each wave holds dS for its
+//      16 columns and all D_k rows in registers.  Per chunk, newest first:
+//        store dS (= dS_next of the chunk);  dV' = Kd dS + (scale P)^T dO;  dX = A^T dV';
+//        dS <- Diag(e^{G_C}) dS + Qg^T (scale dO) - Kg^T (beta (.) dX)
+//      The next-older chunk's tiles stream into the other of two padded LDS stages meanwhile.  The
+//      operands formed here (dS, dV', dO, dX) are fp16, rounded to nearest once.
+template <int DK>
+struct DsKdaLayout {
+    static constexpr int NW = 2, WC = 32;             // waves, value columns per workgroup
+    using K = Pad<DK * 2 / 16>;                       // Kd, Kg, Qg tiles
+    using A = Pad<8>;                                 // A and P (64 x 64)
+    using O = Pad<WC * 2 / 16>;                       // dO columns of the workgroup
+    static constexpr int GT = GB_FLOATS * 4;
+    static constexpr int KD0 = 0, KG0 = K::BYTES, QG0 = 2 * K::BYTES, A0 = 3 * K::BYTES, P0 = A0 + A::BYTES;
+    static constexpr int O0 = P0 + A::BYTES, G0 = O0 + O::BYTES, STAGE = G0 + GT;
+    static constexpr int NLG = GT / 1024;
+    static constexpr int NLOAD = 3 * K::NI + 2 * A::NI + O::NI + NLG;
+    static constexpr int NLW = (NLOAD + NW - 1) / NW;
+    static constexpr int MD = DK / 16, NKB = DK / 32;
+    static_assert(2 * STAGE <= 160 * 1024, "LDS budget");
+};
+
+template <int DK>
+__global__ __launch_bounds__(128, 1) void bwd_dstate_kda_mma_kernel(BwdParams p) {
+    using L = DsKdaLayout<DK>;
+    using KT = typename L::K;
+    using AT = typename L::A;
+    using OT = typename L::O;
+    constexpr int MD = L::MD, NKB = L::NKB, NLW = L::NLW, NW = L::NW;
+    __shared__ __attribute__((aligned(16))) unsigned char stg0[L::STAGE], stg1[L::STAGE];
+    const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ncb = p.D_v / L::WC;
+    const int cb = blockIdx.x % ncb, nh = blockIdx.x / ncb, h = nh % p.H_v, n = nh / p.H_v;
+    if (n >= p.N) return;
+    const SeqInfo si = seq_info(p.seq, n, p.T);
+    const int DV = p.D_v, vs = p.H_v * DV;
+    const int c0 = cb * L::WC, col = c0 + 16 * wave + l16;
+    const f16 *kdb = static_cast<const f16 *>(p.kd) + (int64_t)h * 64 * DK;
+    const f16 *kgb = static_cast<const f16 *>(p.kg) + (int64_t)h * 64 * DK;
+    const f16 *qgb = static_cast<const f16 *>(p.qg) + (int64_t)h * 64 * DK;
+    const f16 *Ab = static_cast<const f16 *>(p.A) + (int64_t)h * 4096;
+    const f16 *Pb = static_cast<const f16 *>(p.P) + (int64_t)h * 4096;
+    const bf16 *ob = static_cast<const bf16 *>(p.dout) + (int64_t)h * DV + c0;
+    const float *Gb = p.gates + (int64_t)h * GB_FLOATS;
+
+    // this wave's stage instructions (Kd, Kg, Qg, A, P, dO, gate block; pad granules read zeros)
+    constexpr int kOut = 1 << 30;
+    int soff[NLW], dst[NLW], kind[NLW];
+#pragma unroll
+    for (int j = 0; j < NLW; ++j) {
+        int ii = wave + NW * j;
+        kind[j] = 7;
+        soff[j] = 0;
+        dst[j] = 0;
+        if (ii < 3 * KT::NI) {
+            const int q = ii / KT::NI, i2 = ii - q * KT::NI, pos = 64 * i2 + lane, row = pos / KT::P, g = pos % KT::P;
+            kind[j] = q;                                     // 0: Kd, 1: Kg, 2: Qg
+            soff[j] = g < KT::P - 1 ? row * DK * 2 + 16 * g : kOut;
+            dst[j] = q * KT::BYTES + 1024 * i2;
+        } else if ((ii -= 3 * KT::NI) < 2 * AT::NI) {
+            const int part = ii / AT::NI, i2 = ii - part * AT::NI, pos = 64 * i2 + lane, row = pos / AT::P, g = pos % AT::P;
+            kind[j] = 3 + part;                              // 3: A, 4: P
+            soff[j] = g < AT::P - 1 ? row * 128 + 16 * g : kOut;
+            dst[j] = L::A0 + part * AT::BYTES + 1024 * i2;
+        } else if ((ii -= 2 * AT::NI) < OT::NI) {
+            const int pos = 64 * ii + lane, row = pos / OT::P, g = pos % OT::P;
+            kind[j] = 5;
+            soff[j] = g < OT::P - 1 ? row * vs * 2 + 16 * g : kOut;
+            dst[j] = L::O0 + 1024 * ii;
+        } else if ((ii -= OT::NI) < L::NLG) {
+            kind[j] = 6;
+            soff[j] = 1024 * ii + 16 * lane;
+            dst[j] = L::G0 + 1024 * ii;
+        }
+    }
+    auto load_stage = [&](int c, unsigned char *tb) __attribute__((always_inline)) {
+        const int64_t tok = si.tok0 + (int64_t)c * kChunk, gci = si.chunk0 + c;
+        const int nv = min(kChunk, si.len - c * kChunk);
+        const int64_t tile = gci * p.H_v * 64 * DK;
+        const u32x4 rKd = rsrc_words(kdb + tile, 64 * DK * 2);
+        const u32x4 rKg = rsrc_words(kgb + tile, 64 * DK * 2);
+        const u32x4 rQg = rsrc_words(qgb + tile, 64 * DK * 2);
+        const u32x4 rA = rsrc_words(Ab + gci * p.H_v * 4096, 4096 * 2);
+        const u32x4 rP = rsrc_words(Pb + gci * p.H_v * 4096, 4096 * 2);
+        const u32x4 rO = rsrc_words(ob + tok * vs, ((nv - 1) * vs + L::WC) * 2);
+        const u32x4 rG = rsrc_words(Gb + gci * p.H_v * GB_FLOATS, GB_FLOATS * 4);
+#pragma unroll
+        for (int j = 0; j < NLW; ++j) {
+            if (kind[j] == 7) continue;
+            const u32x4 r = kind[j] == 0 ? rKd : kind[j] == 1 ? rKg : kind[j] == 2 ? rQg : kind[j] == 3 ? rA
+                          : kind[j] == 4 ? rP : kind[j] == 5 ? rO : rG;
+            dma_granules(r, tb + dst[j], soff[j]);
+        }
+    };
+
+    f32x4 S[MD];   // dS: rows 16 m + 4 grp + r of column col
+#pragma unroll
+    for (int m = 0; m < MD; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            S[m][r] = p.dht ? p.dht[(((int64_t)n * p.H_v + h) * DK + 16 * m + 4 * grp + r) * DV + col] : 0.f;
+
+    auto step = [&](int c, const unsigned char *st) __attribute__((always_inline)) {
+        const int64_t gci = si.chunk0 + c;
+        const unsigned char *tKd = st + L::KD0, *tKg = st + L::KG0, *tQg = st + L::QG0;
+        const unsigned char *tA = st + L::A0, *tP = st + L::P0, *tO = st + L::O0;
+        const float *g = reinterpret_cast<const float *>(st + L::G0);
+        Frag<f16> unused;
+        {   // dS_next of this chunk
+            float *dsn = p.dsnext + (gci * p.H_v + h) * DK * DV;
+#pragma unroll
+            for (int m = 0; m < MD; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dsn[(16 * m + 4 * grp + r) * DV + col] = S[m][r];
+        }
+        // dV' = Kd dS + (scale P)^T dO
+        f32x4 dv[4];
+        {
+            Frag<f16> sf[NKB];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                float x[8];
+                pack_pi(S[2 * kb], S[2 * kb + 1], x);
+                split8(x, sf[kb], unused);
+            }
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                dv[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) mma(dv[tt], as_f16(pi_row<KT>(tKd, 16 * tt + l16, kb, grp)), sf[kb]);
+                reg_fence();
+            }
+        }
+        Frag<f16> of[2], os[2];   // dO[t][col] and scale dO[t][col], t in pi order
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const Frag<bf16> o = pi_col<OT>(tO, 16 * wave, kb, grp, l16);
+            float x[8], y[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                x[e] = (float)o.v[e];
+                y[e] = p.scale * x[e];
+            }
+            split8(x, of[kb], unused);
+            split8(y, os[kb], unused);
+        }
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                if (32 * kb + 31 < 16 * tt) continue;        // P[s][t] = 0 for s < t
+                mma(dv[tt], as_f16(pi_col<AT>(tP, 16 * tt, kb, grp, l16)), of[kb]);
+            }
+        // dX = A^T dV'
+        f32x4 dx[4];
+        {
+            Frag<f16> vf[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                float x[8];
+                pack_pi(dv[2 * kb], dv[2 * kb + 1], x);
+                split8(x, vf[kb], unused);
+            }
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                dx[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    if (32 * kb + 31 < 16 * tt) continue;    // A[s][t] = 0 for s < t
+                    mma(dx[tt], as_f16(pi_col<AT>(tA, 16 * tt, kb, grp, l16)), vf[kb]);
+                }
+            }
+        }
+        // dS <- Diag(e^{G_C}) dS + Qg^T (scale dO) - Kg^T (beta (.) dX)
+        Frag<f16> xf[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const int t0 = 32 * kb + 4 * grp;
+            const float4 ba = *reinterpret_cast<const float4 *>(g + GB_BETA + t0);
+            const float4 bc = *reinterpret_cast<const float4 *>(g + GB_BETA + t0 + 16);
+            const float fb[8] = {ba.x, ba.y, ba.z, ba.w, bc.x, bc.y, bc.z, bc.w};
+            float xx[8];
+            pack_pi(dx[2 * kb], dx[2 * kb + 1], xx);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xx[e] = -fb[e] * xx[e];
+            split8(xx, xf[kb], unused);
+        }
+#pragma unroll
+        for (int m = 0; m < MD; ++m) {
+            const float4 dec = *reinterpret_cast<const float4 *>(g + GB_DEC + 16 * m + 4 * grp);
+            S[m][0] *= dec.x; S[m][1] *= dec.y; S[m][2] *= dec.z; S[m][3] *= dec.w;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                mma(S[m], as_f16(pi_col<KT>(tQg, 16 * m, kb, grp, l16)), os[kb]);
+                mma(S[m], as_f16(pi_col<KT>(tKg, 16 * m, kb, grp, l16)), xf[kb]);
+            }
+            if (m & 1) reg_fence();
+        }
+    };
+
+    const int nch = si.nchunks;
+    if (nch > 0) {
+        load_stage(nch - 1, stg0);
+        wait_vm<0>();
+        lds_only_barrier();
+    }
+    // chunks newest first; stage of chunk c: stg0 when (nch - 1 - c) is even
+    for (int k = 0; k < nch; k += 2) {
+        const int c = nch - 1 - k;
+        if (c >= 1) load_stage(c - 1, stg1);
+        step(c, stg0);
+        wait_vm<0>();
+        lds_only_barrier();    // chunk c - 1's stage; every wave is done with stg0
+        if (c >= 1) {
+            if (c >= 2) load_stage(c - 2, stg0);
+            step(c - 1, stg1);
+            wait_vm<0>();
+            lds_only_barrier();
+        }
+    }
+    if (p.dh0) {
+#pragma unroll
+        for (int m = 0; m < MD; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) p.dh0[(((int64_t)n * p.H_v + h) * DK + 16 * m + 4 * grp + r) * DV + col] = S[m][r];
+    }
+}
+
 // ---- per (chunk, value head): every gradient of the chunk's inputs
 template <typename T, int DK>
 __global__ __launch_bounds__(kBwT) void bwd_chunk_kernel(BwdParams p) {
@@ -1325,14 +1564,17 @@ __global__ __launch_bounds__(256) void bwd_group_sum_kernel(BwdParams p, int DK,
 hipError_t launch_bwd(int dtype, int D_k, const BwdParams &p, hipStream_t s) {
     if (p.channel) {
         const int64_t scans = (int64_t)p.N * p.H_v * (p.D_v / kBw), chunks = (int64_t)p.n_chunks * p.H_v;
-        const int64_t replays = (int64_t)p.N * p.H_v * (p.D_v / kBwR);
+        const int64_t replays = (int64_t)p.N * p.H_v * (p.D_v / kBwR), mscans = (int64_t)p.N * p.H_v * (p.D_v / 32);
         if (scans == 0) return hipSuccess;
 // every kernel of the backward runs kBwT threads per workgroup
 #define GDN_BWDK(K, T, DK, grid) hipLaunchKernelGGL((K<T, DK>), dim3((unsigned)(grid)), dim3(kBwT), 0, s, p)
 #define GDN_BWDK_ALL(T, DK)                                  \
     if (!p.replayed) GDN_BWDK(bwd_states_kda_kernel, T, DK, replays); \
     if (chunks) GDN_BWDK(bwd_p_kda_kernel, T, DK, chunks);   \
-    GDN_BWDK(bwd_dstate_kda_kernel, T, DK, scans);           \
+    if (sizeof(T) == 2)                                      \
+        hipLaunchKernelGGL((bwd_dstate_kda_mma_kernel<DK>), dim3((unsigned)mscans), dim3(128), 0, s, p); \
+    else                                                     \
+        GDN_BWDK(bwd_dstate_kda_kernel, T, DK, scans);       \
     if (chunks) {                                            \
         GDN_BWDK(bwd_chunk_kda_a_kernel, T, DK, chunks);     \
         GDN_BWDK(bwd_chunk_kda_b_kernel, T, DK, chunks);     \

@@ -202,6 +202,7 @@ struct BwdParams {           // backward (gdn_bwd), scalar gate
     const void *g;                         // fp32 [tokens][H_v] (scalar gate) or [tokens][H_v][D_k] (input dtype)
     const float *h0, *dht;                 // nullable
     const void *A;                         // (I + L)^-1 of every chunk, from the per-chunk kernel
+    const void *P, *kg, *kd, *qg;          // per-channel gates: its scale P, K e^G, K e^{G_C - G}, Q e^G
     const float *gates;                    // its gate blocks (GB_*, no prologue factors)
     const SeqInfo *seq;                    // nullptr: batched input
     const ChunkInfo *chunks;
