@@ -1576,7 +1576,12 @@ hipError_t launch_bwd(int dtype, int D_k, const BwdParams &p, hipStream_t s) {
     else                                                     \
         GDN_BWDK(bwd_dstate_kda_kernel, T, DK, scans);       \
     if (chunks) {                                            \
-        GDN_BWDK(bwd_chunk_kda_a_kernel, T, DK, chunks);     \
+        if (sizeof(T) == 2) {                                \
+            const hipError_t em = launch_bwd_chunk_kda_mma(DK, p, s); \
+            if (em != hipSuccess) return em;                 \
+        } else {                                             \
+            GDN_BWDK(bwd_chunk_kda_a_kernel, T, DK, chunks); \
+        }                                                    \
         GDN_BWDK(bwd_chunk_kda_b_kernel, T, DK, chunks);     \
     }
         if (dtype == 1 && D_k == 128) { GDN_BWDK_ALL(bf16, 128) }

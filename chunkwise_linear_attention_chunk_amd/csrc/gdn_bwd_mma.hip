@@ -448,7 +448,417 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_mma_kernel(BwdParams p) {
     }
 }
 
+// ==========================================================================================
+// Per-channel gates, bf16 inputs: the products of the per-chunk gradients with S and dS_next, dA,
+// dL and dv, dbeta's X part and dG's row terms (the quantities of the plain bwd_chunk_kda_a_kernel,
+// whose companion kernel (b) then adds the P and L terms), per (chunk, value head) workgroup of
+// eight waves, from the per-chunk kernel's fp16 operands (Kg = K e^G, Kd = K e^{G_C - G}, A,
+// scale P):
+//   value columns in halves of 64:  Kg S, Kd dS_next;  X = diag(beta)(V - Kg S);  V' = A X;
+//     dV' = Kd dS_next + (scale P)^T dO;  dX = A^T dV';  dv = diag(beta) dX;  dA += dV' X^T;
+//     dq_S += dO S^T;  dk_D += V' dS_next^T;  dk_X += dX S^T;  e^{G_C} <S, dS_next> per channel
+//   then:  dq = scale e^G (.) dq_S,  dk = e^{G_C - G} (.) dk_D - diag(beta) e^G (.) dk_X,
+//     dL = -A^T dA A^T (strictly lower);  dG = q (.) dq + k (.) (dk_X part) - k (.) (dk_D part),
+//     with the e^{G_C} terms on the chunk's last valid row.
+// The operands formed here (S, dS_next, X, V', dV', dX and the dL intermediates) are fp16 hi/lo
+// pairs, hi = fp16(x), lo = fp16(x - hi): with steep gates single terms of a chunk's first or last
+// token are far above the gradients' RMS, and one fp16 rounding of them would not keep those
+// within the bound.  V' and dL go to the workspace in fp32 for kernel (b).
+template <int DK>
+struct KaLayout {
+    static constexpr int NW = 8;
+    using K = Pad<DK * 2 / 16>;               // Kg and Kd tiles
+    using S = Pad<8>;                         // every 64 x 64 16-bit tile
+    static constexpr int KG0 = 0, KD0 = K::BYTES, A0 = 2 * K::BYTES, P0 = A0 + S::BYTES;
+    static constexpr int V0 = P0 + S::BYTES, O0 = V0 + S::BYTES;     // V, dO halves [t][c] (bf16)
+    static constexpr int X0 = O0 + S::BYTES;                         // X, V', dV', dX pairs [c][t] (fp16)
+    static constexpr int G0 = X0 + 8 * S::BYTES, BYTES = G0 + GB_FLOATS * 4;
+    static constexpr int MD = DK / 16, NKB = DK / 32, NQT = MD / 2;  // dq/dk tiles per wave
+    static_assert(BYTES <= 160 * 1024 - 1024, "LDS budget");
+};
+
+// fp16 operand of eight bf16 values (exact inside fp16's normal range)
+__device__ __forceinline__ Frag<f16> bf_to_f16(const Frag<bf16> &f) {
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (float)f.v[e];
+    Frag<f16> r, unused;
+    split8(x, r, unused);
+    return r;
+}
+__device__ __forceinline__ Frag<f16> as_f16(const Frag<bf16> &f) {
+    Frag<f16> r;
+    r.v = __builtin_bit_cast(f16x8, f.v);
+    return r;
+}
+// fp16 pair of eight values: hi = fp16(x), lo = fp16(x - hi), both rounded to nearest
+__device__ __forceinline__ void split8_h2(const float *x, Frag<f16> &h, Frag<f16> &l) {
+    typedef float f32x8 __attribute__((ext_vector_type(8)));
+    const f32x8 v = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
+    h.v = __builtin_convertvector(v, f16x8);
+    l.v = __builtin_convertvector(v - __builtin_convertvector(h.v, f32x8), f16x8);
+}
+// the fp16 pair of four accumulator values (rows a .. a + 3 of column b) stored transposed: row b,
+// columns a .. a + 3 of the hi and lo tiles
+template <typename PT>
+__device__ __forceinline__ void put_t16(unsigned char *th, unsigned char *tl, int b, int a, const f32x4 &x) {
+    f16x4 hv, lv;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        hv[r] = (f16)x[r];
+        lv[r] = (f16)(x[r] - (float)hv[r]);
+    }
+    *reinterpret_cast<f16x4 *>(th + PT::off(b, a * 2)) = hv;
+    *reinterpret_cast<f16x4 *>(tl + PT::off(b, a * 2)) = lv;
+}
+// acc += a (bh + bl);  acc += (ah + al)(bh + bl) without lo * lo
+__device__ __forceinline__ void mma_h1(f32x4 &acc, const Frag<f16> &a, const Frag<f16> &bh, const Frag<f16> &bl) {
+    mma(acc, a, bh);
+    mma(acc, a, bl);
+}
+__device__ __forceinline__ void mma_h2(f32x4 &acc, const Frag<f16> &ah, const Frag<f16> &al, const Frag<f16> &bh,
+                                       const Frag<f16> &bl) {
+    mma(acc, ah, bh);
+    mma(acc, ah, bl);
+    mma(acc, al, bh);
+}
+
+template <int DK>
+__global__ __launch_bounds__(512, 1) void bwd_chunk_kda_mma_kernel(BwdParams p) {
+    using L = KaLayout<DK>;
+    using KT = typename L::K;
+    using ST = typename L::S;
+    constexpr int NKB = L::NKB, MD = L::MD, NQT = L::NQT, NW = L::NW;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[L::BYTES];
+    __shared__ float rdb[64], rdgc[DK];
+    unsigned char *tKg = lds + L::KG0, *tKd = lds + L::KD0, *tA = lds + L::A0, *tP = lds + L::P0;
+    unsigned char *tV = lds + L::V0, *tO = lds + L::O0;
+    unsigned char *tXh = lds + L::X0, *tXl = tXh + ST::BYTES, *tVh = tXl + ST::BYTES, *tVl = tVh + ST::BYTES;
+    unsigned char *tDh = tVl + ST::BYTES, *tDl = tDh + ST::BYTES, *tEh = tDl + ST::BYTES, *tEl = tEh + ST::BYTES;
+    const float *g = reinterpret_cast<const float *>(lds + L::G0);
+
+    const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ci = blockIdx.x / p.H_v, h = blockIdx.x - ci * p.H_v;
+    const int hq = h / (p.H_v / p.H_qk);
+    const ChunkInfo cinfo = chunk_info(p.chunks, ci, p.T);
+    const int64_t tok0 = cinfo.tok0;
+    const int nv = cinfo.nv;
+    const int DV = p.D_v, qks = p.H_qk * DK, vs = p.H_v * DV;
+    const int64_t unit = (int64_t)ci * p.H_v + h;
+    const float *St = p.states + unit * DK * DV;
+    const float *dSt = p.dsnext + unit * DK * DV;
+
+    // ---- tiles: padded rows through direct-to-LDS loads (pad granules read zeros)
+    auto load = [&]<typename PT>(unsigned char *tile, u32x4 r, int stride) __attribute__((always_inline)) {
+        for (int i = w; i < PT::NI; i += NW) {
+            const int pos = 64 * i + lane, row = pos / PT::P, gg = pos % PT::P;
+            dma_granules(r, tile + 1024 * i, gg < PT::P - 1 ? row * stride + 16 * gg : (1 << 30));
+        }
+    };
+    auto load_half = [&](int hv) __attribute__((always_inline)) {
+        const bf16 *vb = static_cast<const bf16 *>(p.v) + tok0 * vs + (int64_t)h * DV + 64 * hv;
+        const bf16 *ob = static_cast<const bf16 *>(p.dout) + tok0 * vs + (int64_t)h * DV + 64 * hv;
+        load.template operator()<ST>(tV, rsrc_words(vb, ((nv - 1) * vs + 64) * 2), vs * 2);
+        load.template operator()<ST>(tO, rsrc_words(ob, ((nv - 1) * vs + 64) * 2), vs * 2);
+    };
+    {
+        load.template operator()<KT>(tKg, rsrc_words(static_cast<const f16 *>(p.kg) + unit * 64 * DK, 64 * DK * 2), DK * 2);
+        load.template operator()<KT>(tKd, rsrc_words(static_cast<const f16 *>(p.kd) + unit * 64 * DK, 64 * DK * 2), DK * 2);
+        load.template operator()<ST>(tA, rsrc_words(static_cast<const f16 *>(p.A) + unit * 4096, 8192), 128);
+        load.template operator()<ST>(tP, rsrc_words(static_cast<const f16 *>(p.P) + unit * 4096, 8192), 128);
+        if (w < GB_FLOATS * 4 / 1024)
+            dma_granules(rsrc_words(p.gates + unit * GB_FLOATS, GB_FLOATS * 4), lds + L::G0 + 1024 * w, 1024 * w + 16 * lane);
+        load_half(0);
+    }
+    if (tid < 64) rdb[tid] = 0.f;
+    if (tid < DK) rdgc[tid] = 0.f;
+    wait_vm<0>();
+    __syncthreads();
+
+    auto rows4 = [&](int off, int a) __attribute__((always_inline)) {
+        return *reinterpret_cast<const float4 *>(g + off + 16 * a + 4 * grp);
+    };
+    // the pi-order pair of eight fp32 values of a state-shaped matrix at (row, column) positions
+    auto state_pair = [&](const float *M, int rowc, bool by_col, int base, int kb, Frag<f16> &hi, Frag<f16> &lo)
+        __attribute__((always_inline)) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int k = base + 32 * kb + (e < 4 ? 4 * grp + e : 16 + 4 * grp + e - 4);
+            x[e] = by_col ? M[k * DV + rowc] : M[rowc * DV + k];
+        }
+        split8_h2(x, hi, lo);
+    };
+
+    f32x4 dA[2];                                          // 64 x 64 tiles w, w + 8
+    f32x4 dqS[NQT], dkD[NQT], dkX[NQT];                   // dq / dk tiles (tt, m)
+    dA[0] = dA[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < NQT; ++q) dqS[q] = dkD[q] = dkX[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int ct = w & 3, tt0 = 2 * (w >> 2);             // token x column tiles of the half
+    const int m = w % MD, qt0 = (w / MD) * NQT;           // dq / dk tiles: rows 16 m of D_k, tokens
+    float *vpw = p.vp + unit * 64 * DV;
+
+    const int NH = DV / 64;                               // halves of the value columns
+    for (int hv = 0; hv < NH; ++hv) {
+        __syncthreads();   // the half's V and dO tiles have landed
+        const int colg = 64 * hv + 16 * ct + l16;          // this lane's value column
+        // ---- P1: Kg S, Kd dS_next, X
+        f32x4 ks[2], kd[2];
+        {
+            Frag<f16> sh[NKB], sl[NKB], dh[NKB], dl[NKB];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                state_pair(St, colg, true, 0, kb, sh[kb], sl[kb]);
+                state_pair(dSt, colg, true, 0, kb, dh[kb], dl[kb]);
+            }
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int tt = tt0 + q;
+                ks[q] = kd[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+                    mma_h1(ks[q], as_f16(pi_row<KT>(tKg, 16 * tt + l16, kb, grp)), sh[kb], sl[kb]);
+                    mma_h1(kd[q], as_f16(pi_row<KT>(tKd, 16 * tt + l16, kb, grp)), dh[kb], dl[kb]);
+                }
+            }
+        }
+        float vk[2][4];                                   // V - Kg S
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int tt = tt0 + q;
+            const bf16x4 v4 = col4<ST>(tV, tt, ct, grp, l16);
+            const float4 be = rows4(GB_BETA, tt);
+            const float bev[4] = {be.x, be.y, be.z, be.w};
+            f32x4 x;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                vk[q][r] = (float)v4[r] - ks[q][r];
+                x[r] = bev[r] * vk[q][r];
+            }
+            put_t16<ST>(tXh, tXl, 16 * ct + l16, 16 * tt + 4 * grp, x);
+        }
+        __syncthreads();
+        // ---- P2: V' = A X, dV' = Kd dS_next + (scale P)^T dO
+        {
+            Frag<f16> of[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) of[kb] = bf_to_f16(pi_col<ST>(tO, 16 * ct, kb, grp, l16));
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int tt = tt0 + q;
+                f32x4 vp = {0.f, 0.f, 0.f, 0.f}, dvp = kd[q];
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    if (32 * kb > 16 * tt + 15) continue;         // A[t][s] = 0 for s > t
+                    mma_h1(vp, as_f16(pi_row<ST>(tA, 16 * tt + l16, kb, grp)), as_f16(pi_row<ST>(tXh, 16 * ct + l16, kb, grp)),
+                           as_f16(pi_row<ST>(tXl, 16 * ct + l16, kb, grp)));
+                }
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    if (32 * kb + 31 < 16 * tt) continue;         // P[s][t] = 0 for s < t
+                    mma(dvp, as_f16(pi_col<ST>(tP, 16 * tt, kb, grp, l16)), of[kb]);
+                }
+                put_t16<ST>(tVh, tVl, 16 * ct + l16, 16 * tt + 4 * grp, vp);
+                put_t16<ST>(tDh, tDl, 16 * ct + l16, 16 * tt + 4 * grp, dvp);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) vpw[(16 * tt + 4 * grp + r) * DV + colg] = vp[r];
+            }
+        }
+        __syncthreads();
+        // ---- P3: dX = A^T dV', dv, the X term of dbeta
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int tt = tt0 + q;
+            f32x4 dx = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                if (32 * kb + 31 < 16 * tt) continue;         // A[s][t] = 0 for s < t
+                mma_h1(dx, as_f16(pi_col<ST>(tA, 16 * tt, kb, grp, l16)), as_f16(pi_row<ST>(tDh, 16 * ct + l16, kb, grp)),
+                       as_f16(pi_row<ST>(tDl, 16 * ct + l16, kb, grp)));
+            }
+            const float4 be = rows4(GB_BETA, tt);
+            const float bev[4] = {be.x, be.y, be.z, be.w};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * tt + 4 * grp + r;
+                if (t < nv) p.dv[(tok0 + t) * vs + (int64_t)h * DV + colg] = bev[r] * dx[r];
+                const float db = sum16(dx[r] * vk[q][r]);
+                if (l16 == 0) atomicAdd(&rdb[t], db);
+            }
+            put_t16<ST>(tEh, tEl, 16 * ct + l16, 16 * tt + 4 * grp, dx);
+        }
+        __syncthreads();
+        // ---- P4: the products over this half's columns
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int tix = w + 8 * q, ti = tix >> 2, tj = tix & 3;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                mma_h2(dA[q], as_f16(pi_col<ST>(tDh, 16 * ti, kb, grp, l16)), as_f16(pi_col<ST>(tDl, 16 * ti, kb, grp, l16)),
+                       as_f16(pi_col<ST>(tXh, 16 * tj, kb, grp, l16)), as_f16(pi_col<ST>(tXl, 16 * tj, kb, grp, l16)));
+        }
+        {
+            // S and dS_next rows 16 m + l16 over this half's columns, in pi order
+            Frag<f16> sh[2], sl[2], dh[2], dl[2];
+            float fro = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                state_pair(St, 16 * m + l16, false, 64 * hv, kb, sh[kb], sl[kb]);
+                state_pair(dSt, 16 * m + l16, false, 64 * hv, kb, dh[kb], dl[kb]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int c = 64 * hv + 32 * kb + (e < 4 ? 4 * grp + e : 16 + 4 * grp + e - 4);
+                    fro += St[(16 * m + l16) * DV + c] * dSt[(16 * m + l16) * DV + c];
+                }
+            }
+            // e^{G_C} <S, dS_next> of channel 16 m + l16 (each row once: the waves past the D_k
+            // rows' owners skip it)
+            if (w < MD) {
+                fro = sum_groups(fro);
+                if (grp == 0) atomicAdd(&rdgc[16 * m + l16], g[GB_DEC + 16 * m + l16] * fro);
+            }
+#pragma unroll
+            for (int q = 0; q < NQT; ++q) {
+                const int tt = qt0 + q;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    mma_h1(dqS[q], bf_to_f16(pi_row<ST>(tO, 16 * tt + l16, kb, grp)), sh[kb], sl[kb]);
+                    mma_h2(dkD[q], as_f16(pi_col<ST>(tVh, 16 * tt, kb, grp, l16)), as_f16(pi_col<ST>(tVl, 16 * tt, kb, grp, l16)),
+                           dh[kb], dl[kb]);
+                    mma_h2(dkX[q], as_f16(pi_col<ST>(tEh, 16 * tt, kb, grp, l16)), as_f16(pi_col<ST>(tEl, 16 * tt, kb, grp, l16)),
+                           sh[kb], sl[kb]);
+                }
+            }
+        }
+        if (hv + 1 < NH) {
+            __syncthreads();   // every wave is done with the first half's tiles
+            load_half(1);
+            wait_vm<0>();
+        }
+    }
+
+    // ---- dq, dk through the states; dG's row terms (the last row's e^{G_C} terms are collected).
+    //      The lane's gate values: the cumsum of its channel d down the chunk, kept at its rows.
+    const int d = 16 * m + l16;
+    float Gt[NQT][4], gC;
+    {
+        const bf16 *gp = static_cast<const bf16 *>(p.g) + tok0 * p.H_v * DK + (int64_t)h * DK + d;
+        float acc = 0.f;
+#pragma unroll
+        for (int t = 0; t < 64; ++t) {
+            if (t < nv) acc += (float)gp[(int64_t)t * p.H_v * DK];
+#pragma unroll
+            for (int q = 0; q < NQT; ++q)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (t == 16 * (qt0 + q) + 4 * grp + r) Gt[q][r] = acc;
+        }
+        gC = acc;
+    }
+    const bf16 *qp = static_cast<const bf16 *>(p.q) + tok0 * qks + (int64_t)hq * DK + d;
+    const bf16 *kp = static_cast<const bf16 *>(p.k) + tok0 * qks + (int64_t)hq * DK + d;
+    f32x4 dq[NQT], dk[NQT], dG[NQT];
+    float dgd_sum = 0.f;
+#pragma unroll
+    for (int q = 0; q < NQT; ++q) {
+        const int tt = qt0 + q;
+        const float4 be = rows4(GB_BETA, tt);
+        const float bev[4] = {be.x, be.y, be.z, be.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * tt + 4 * grp + r;
+            const float G = Gt[q][r], eg = __expf(G);
+            const float qv = t < nv ? (float)qp[(int64_t)t * qks] : 0.f;
+            const float kv = t < nv ? (float)kp[(int64_t)t * qks] : 0.f;
+            const float dq_o = p.scale * eg * dqS[q][r];
+            const float dk_x = -bev[r] * eg * dkX[q][r];
+            const float dk_d = __expf(gC - G) * dkD[q][r];
+            dq[q][r] = dq_o;
+            dk[q][r] = dk_x + dk_d;
+            // the last valid row's factor e^{G_C - G_C} = 1 has no gate gradient: its - (own row) and
+            // + (G_C) terms would cancel exactly, so neither is added
+            const float dgd = t >= nv - 1 ? 0.f : kv * dk_d;
+            dG[q][r] = qv * dq_o + kv * dk_x - dgd;
+            dgd_sum += dgd;
+        }
+    }
+    dgd_sum = sum_groups(dgd_sum);
+    if (grp == 0) atomicAdd(&rdgc[d], dgd_sum);
+    __syncthreads();   // every wave is done with the operand buffers; rdgc and rdb are complete
+    // ---- dA transposed ([s][t]) into the X buffers
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int tix = w + 8 * q, ti = tix >> 2, tj = tix & 3;
+        put_t16<ST>(tXh, tXl, 16 * tj + l16, 16 * ti + 4 * grp, dA[q]);
+    }
+    const int hs = p.dq_v == p.dq ? hq : h, hn = p.dq_v == p.dq ? p.H_qk : p.H_v;
+#pragma unroll
+    for (int q = 0; q < NQT; ++q) {
+        const int tt = qt0 + q;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * tt + 4 * grp + r;
+            if (t < nv) {
+                const int64_t o = ((tok0 + t) * hn + hs) * DK + d;
+                p.dq_v[o] = dq[q][r];
+                p.dk_v[o] = dk[q][r];
+                p.dg[((tok0 + t) * p.H_v + h) * DK + d] = dG[q][r] + (t == nv - 1 ? rdgc[d] : 0.f);
+            }
+        }
+    }
+    if (tid < nv) p.dbeta[(tok0 + tid) * p.H_v + h] = rdb[tid];
+    __syncthreads();
+    // ---- T = A^T dA, transposed ([t][i]) into the V' buffers
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int tix = w + 8 * q, ti = tix >> 2, tj = tix & 3;
+        f32x4 T = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            if (32 * kb + 31 < 16 * ti) continue;             // A[t][i] = 0 for t < i
+            mma_h1(T, as_f16(pi_col<ST>(tA, 16 * ti, kb, grp, l16)), as_f16(pi_row<ST>(tXh, 16 * tj + l16, kb, grp)),
+                   as_f16(pi_row<ST>(tXl, 16 * tj + l16, kb, grp)));
+        }
+        put_t16<ST>(tVh, tVl, 16 * tj + l16, 16 * ti + 4 * grp, T);
+    }
+    __syncthreads();
+    // ---- dL = -T A^T (strictly lower), to the workspace
+    float *dLw = p.dlmat + unit * 4096;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int tix = w + 8 * q, ti = tix >> 2, tj = tix & 3;
+        f32x4 dl = {0.f, 0.f, 0.f, 0.f};
+        if (tj <= ti) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                if (32 * kb > 16 * tj + 15) continue;         // A[j][t] = 0 for t > j
+                const Frag<f16> af = as_f16(pi_row<ST>(tA, 16 * tj + l16, kb, grp));
+                mma(dl, as_f16(pi_col<ST>(tVh, 16 * ti, kb, grp, l16)), af);
+                mma(dl, as_f16(pi_col<ST>(tVl, 16 * ti, kb, grp, l16)), af);
+            }
+        }
+        const int j = 16 * tj + l16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = 16 * ti + 4 * grp + r;
+            dLw[i * 64 + j] = j < i ? -dl[r] : 0.f;
+        }
+    }
+}
+
 }  // namespace
+
+hipError_t launch_bwd_chunk_kda_mma(int D_k, const BwdParams &p, hipStream_t s) {
+    const int64_t chunks = (int64_t)p.n_chunks * p.H_v;
+    if (chunks == 0) return hipSuccess;
+    if (p.D_v != 64 && p.D_v != 128) return hipErrorInvalidValue;
+    if (D_k == 128) hipLaunchKernelGGL((bwd_chunk_kda_mma_kernel<128>), dim3((unsigned)chunks), dim3(512), 0, s, p);
+    else if (D_k == 64) hipLaunchKernelGGL((bwd_chunk_kda_mma_kernel<64>), dim3((unsigned)chunks), dim3(512), 0, s, p);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
 
 hipError_t launch_bwd_chunk_mma(int D_k, const BwdParams &p, hipStream_t s) {
     const int64_t chunks = (int64_t)p.n_chunks * p.H_v;
