@@ -489,6 +489,13 @@ __device__ __forceinline__ Frag<f16> as_f16(const Frag<bf16> &f) {
     r.v = __builtin_bit_cast(f16x8, f.v);
     return r;
 }
+// fp16 pair of eight values: hi = fp16(x), lo = fp16(x - hi), both rounded to nearest
+__device__ __forceinline__ void split8_h2(const float *x, Frag<f16> &h, Frag<f16> &l) {
+    typedef float f32x8 __attribute__((ext_vector_type(8)));
+    const f32x8 v = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
+    h.v = __builtin_convertvector(v, f16x8);
+    l.v = __builtin_convertvector(v - __builtin_convertvector(h.v, f32x8), f16x8);
+}
 
 // ---- reverse scan of the state gradient on the matrix cores (per-channel gates, bf16 inputs): the
 //      quantities of bwd_dstate_kda_kernel, from the fp16 operands the per-chunk kernel stores for
@@ -498,7 +505,9 @@ __device__ __forceinline__ Frag<f16> as_f16(const Frag<bf16> &f) {
 //        store dS (= dS_next of the chunk);  dV' = Kd dS + (scale P)^T dO;  dX = A^T dV';
 //        dS <- Diag(e^{G_C}) dS + Qg^T (scale dO) - Kg^T (beta (.) dX)
 //      The next-older chunk's tiles stream into the other of two padded LDS stages meanwhile.  The
-//      operands formed here (dS, dV', dO, dX) are fp16, rounded to nearest once.
+//      operands formed here (dS, dV', scale dO, dX) are fp16 hi/lo pairs (the steep-gate argument
+//      of the per-chunk gradients: single terms of a chunk's first or last token can be far above
+//      the RMS); dO itself is exact in fp16.
 template <int DK>
 struct DsKdaLayout {
     static constexpr int NW = 2, WC = 32;             // waves, value columns per workgroup
@@ -601,7 +610,6 @@ __global__ __launch_bounds__(128, 1) void bwd_dstate_kda_mma_kernel(BwdParams p)
         const unsigned char *tKd = st + L::KD0, *tKg = st + L::KG0, *tQg = st + L::QG0;
         const unsigned char *tA = st + L::A0, *tP = st + L::P0, *tO = st + L::O0;
         const float *g = reinterpret_cast<const float *>(st + L::G0);
-        Frag<f16> unused;
         {   // dS_next of this chunk
             float *dsn = p.dsnext + (gci * p.H_v + h) * DK * DV;
 #pragma unroll
@@ -612,22 +620,26 @@ __global__ __launch_bounds__(128, 1) void bwd_dstate_kda_mma_kernel(BwdParams p)
         // dV' = Kd dS + (scale P)^T dO
         f32x4 dv[4];
         {
-            Frag<f16> sf[NKB];
+            Frag<f16> sh[NKB], sl[NKB];
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
                 float x[8];
                 pack_pi(S[2 * kb], S[2 * kb + 1], x);
-                split8(x, sf[kb], unused);
+                split8_h2(x, sh[kb], sl[kb]);
             }
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
                 dv[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kb = 0; kb < NKB; ++kb) mma(dv[tt], as_f16(pi_row<KT>(tKd, 16 * tt + l16, kb, grp)), sf[kb]);
+                for (int kb = 0; kb < NKB; ++kb) {
+                    const Frag<f16> kf = as_f16(pi_row<KT>(tKd, 16 * tt + l16, kb, grp));
+                    mma(dv[tt], kf, sh[kb]);
+                    mma(dv[tt], kf, sl[kb]);
+                }
                 reg_fence();
             }
         }
-        Frag<f16> of[2], os[2];   // dO[t][col] and scale dO[t][col], t in pi order
+        Frag<f16> of[2], osh[2], osl[2];   // dO[t][col] and the pair of scale dO[t][col], t in pi order
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             const Frag<bf16> o = pi_col<OT>(tO, 16 * wave, kb, grp, l16);
@@ -637,8 +649,9 @@ __global__ __launch_bounds__(128, 1) void bwd_dstate_kda_mma_kernel(BwdParams p)
                 x[e] = (float)o.v[e];
                 y[e] = p.scale * x[e];
             }
+            Frag<f16> unused;
             split8(x, of[kb], unused);
-            split8(y, os[kb], unused);
+            split8_h2(y, osh[kb], osl[kb]);
         }
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt)
@@ -650,12 +663,12 @@ __global__ __launch_bounds__(128, 1) void bwd_dstate_kda_mma_kernel(BwdParams p)
         // dX = A^T dV'
         f32x4 dx[4];
         {
-            Frag<f16> vf[2];
+            Frag<f16> vh[2], vl[2];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 float x[8];
                 pack_pi(dv[2 * kb], dv[2 * kb + 1], x);
-                split8(x, vf[kb], unused);
+                split8_h2(x, vh[kb], vl[kb]);
             }
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
@@ -663,12 +676,14 @@ __global__ __launch_bounds__(128, 1) void bwd_dstate_kda_mma_kernel(BwdParams p)
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
                     if (32 * kb + 31 < 16 * tt) continue;    // A[s][t] = 0 for s < t
-                    mma(dx[tt], as_f16(pi_col<AT>(tA, 16 * tt, kb, grp, l16)), vf[kb]);
+                    const Frag<f16> af = as_f16(pi_col<AT>(tA, 16 * tt, kb, grp, l16));
+                    mma(dx[tt], af, vh[kb]);
+                    mma(dx[tt], af, vl[kb]);
                 }
             }
         }
         // dS <- Diag(e^{G_C}) dS + Qg^T (scale dO) - Kg^T (beta (.) dX)
-        Frag<f16> xf[2];
+        Frag<f16> xh[2], xl[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             const int t0 = 32 * kb + 4 * grp;
@@ -679,7 +694,7 @@ __global__ __launch_bounds__(128, 1) void bwd_dstate_kda_mma_kernel(BwdParams p)
             pack_pi(dx[2 * kb], dx[2 * kb + 1], xx);
 #pragma unroll
             for (int e = 0; e < 8; ++e) xx[e] = -fb[e] * xx[e];
-            split8(xx, xf[kb], unused);
+            split8_h2(xx, xh[kb], xl[kb]);
         }
 #pragma unroll
         for (int m = 0; m < MD; ++m) {
@@ -687,8 +702,12 @@ __global__ __launch_bounds__(128, 1) void bwd_dstate_kda_mma_kernel(BwdParams p)
             S[m][0] *= dec.x; S[m][1] *= dec.y; S[m][2] *= dec.z; S[m][3] *= dec.w;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                mma(S[m], as_f16(pi_col<KT>(tQg, 16 * m, kb, grp, l16)), os[kb]);
-                mma(S[m], as_f16(pi_col<KT>(tKg, 16 * m, kb, grp, l16)), xf[kb]);
+                const Frag<f16> qf = as_f16(pi_col<KT>(tQg, 16 * m, kb, grp, l16));
+                const Frag<f16> kf = as_f16(pi_col<KT>(tKg, 16 * m, kb, grp, l16));
+                mma(S[m], qf, osh[kb]);
+                mma(S[m], qf, osl[kb]);
+                mma(S[m], kf, xh[kb]);
+                mma(S[m], kf, xl[kb]);
             }
             if (m & 1) reg_fence();
         }
@@ -1570,7 +1589,8 @@ hipError_t launch_bwd(int dtype, int D_k, const BwdParams &p, hipStream_t s) {
 #define GDN_BWDK(K, T, DK, grid) hipLaunchKernelGGL((K<T, DK>), dim3((unsigned)(grid)), dim3(kBwT), 0, s, p)
 #define GDN_BWDK_ALL(T, DK)                                  \
     if (!p.replayed) GDN_BWDK(bwd_states_kda_kernel, T, DK, replays); \
-    if (chunks) GDN_BWDK(bwd_p_kda_kernel, T, DK, chunks);   \
+    /* bf16 inputs read the per-chunk kernel's scale P instead */ \
+    if (chunks && sizeof(T) != 2) GDN_BWDK(bwd_p_kda_kernel, T, DK, chunks); \
     if (sizeof(T) == 2)                                      \
         hipLaunchKernelGGL((bwd_dstate_kda_mma_kernel<DK>), dim3((unsigned)mscans), dim3(128), 0, s, p); \
     else                                                     \
