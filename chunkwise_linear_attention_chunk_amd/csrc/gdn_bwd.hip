@@ -1601,8 +1601,8 @@ hipError_t launch_bwd(int dtype, int D_k, const BwdParams &p, hipStream_t s) {
             if (em != hipSuccess) return em;                 \
         } else {                                             \
             GDN_BWDK(bwd_chunk_kda_a_kernel, T, DK, chunks); \
+            GDN_BWDK(bwd_chunk_kda_b_kernel, T, DK, chunks); \
         }                                                    \
-        GDN_BWDK(bwd_chunk_kda_b_kernel, T, DK, chunks);     \
     }
         if (dtype == 1 && D_k == 128) { GDN_BWDK_ALL(bf16, 128) }
         else if (dtype == 1 && D_k == 64) { GDN_BWDK_ALL(bf16, 64) }

@@ -449,21 +449,35 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_mma_kernel(BwdParams p) {
 }
 
 // ==========================================================================================
-// Per-channel gates, bf16 inputs: the products of the per-chunk gradients with S and dS_next, dA,
-// dL and dv, dbeta's X part and dG's row terms (the quantities of the plain bwd_chunk_kda_a_kernel,
-// whose companion kernel (b) then adds the P and L terms), per (chunk, value head) workgroup of
-// eight waves, from the per-chunk kernel's fp16 operands (Kg = K e^G, Kd = K e^{G_C - G}, A,
-// scale P):
+// Per-channel gates, bf16 inputs: every gradient of a chunk's inputs (the quantities of the plain
+// kernels (a) and (b) together), per (chunk, value head) workgroup of eight waves, from the
+// per-chunk kernel's fp16 operands (Kg = K e^G, Kd = K e^{G_C - G}, A, scale P):
 //   value columns in halves of 64:  Kg S, Kd dS_next;  X = diag(beta)(V - Kg S);  V' = A X;
 //     dV' = Kd dS_next + (scale P)^T dO;  dX = A^T dV';  dv = diag(beta) dX;  dA += dV' X^T;
-//     dq_S += dO S^T;  dk_D += V' dS_next^T;  dk_X += dX S^T;  e^{G_C} <S, dS_next> per channel
+//     dP += dO V'^T;  dq_S += dO S^T;  dk_D += V' dS_next^T;  dk_X += dX S^T;
+//     e^{G_C} <S, dS_next> per channel
 //   then:  dq = scale e^G (.) dq_S,  dk = e^{G_C - G} (.) dk_D - diag(beta) e^G (.) dk_X,
-//     dL = -A^T dA A^T (strictly lower);  dG = q (.) dq + k (.) (dk_X part) - k (.) (dk_D part),
-//     with the e^{G_C} terms on the chunk's last valid row.
-// The operands formed here (S, dS_next, X, V', dV', dX and the dL intermediates) are fp16 hi/lo
-// pairs, hi = fp16(x), lo = fp16(x - hi): with steep gates single terms of a chunk's first or last
-// token are far above the gradients' RMS, and one fp16 rounding of them would not keep those
-// within the bound.  V' and dL go to the workspace in fp32 for kernel (b).
+//     dL = -A^T dA A^T (strictly lower), dP scaled (lower with the diagonal);
+//     the P and L terms with their per-channel factors e^{G_r - G_t}, for the rows r of block R:
+//       aq = sum_{t<r} dP[r][t] k_t e^{G_r - G_t},   ar = sum_{t<r} dL[r][t] k_t e^{G_r - G_t},
+//       ap = sum_{t>r} dP[t][r] q_t e^{G_t - G_r},   al = sum_{t>r} dL[t][r] beta_t k_t e^{G_t - G_r},
+//     each one contraction on the matrix cores with the factor split at one reference row, 16 R - 1
+//     (left sums) or 16 R + 15 (right sums): e^{G_r - G_t} = e^{G_r - G_a} e^{G_a - G_t}, the first
+//     at most 1, the second at most 1 outside block R and at most the block's own decay inside it;
+//     a column whose decay across block R exceeds e^kMaxLn takes that block's pairs whole on the
+//     vector ALU instead;
+//     dq += aq + dP[r][r] k_r,  dk += ap + dP[r][r] q_r + beta_r ar + al,
+//     dG = q (.) dq_S-part + k (.) (dk_X part) - k (.) (dk_D part) + q aq + k beta ar - k (ap + al),
+//     with the e^{G_C} terms on the chunk's last valid row, and dg its reverse cumsum per channel;
+//     dbeta from X and from L (sum_d k_rd ar_rd).
+// The operands formed here (S, dS_next, X, V', dV', dX, dA, dP, dL and the factored K and Q) are
+// fp16 hi/lo pairs, hi = fp16(x), lo = fp16(x - hi): with steep gates single terms of a chunk's
+// first or last token are far above the gradients' RMS, and one fp16 rounding of them would not
+// keep those within the bound.
+// Largest decay (natural log) across a 16-row block for which a column's split factors are used:
+// the factors inside the block then stay below e^kMaxLn (fp16 holds them with room to spare).
+constexpr float kMaxLn = 9.5f;
+
 template <int DK>
 struct KaLayout {
     static constexpr int NW = 8;
@@ -530,7 +544,7 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_kda_mma_kernel(BwdParams p) 
     using ST = typename L::S;
     constexpr int NKB = L::NKB, MD = L::MD, NQT = L::NQT, NW = L::NW;
     __shared__ __attribute__((aligned(16))) unsigned char lds[L::BYTES];
-    __shared__ float rdb[64], rdgc[DK];
+    __shared__ float rdb[64], rdgc[DK], rdpd[64], rtot[512];
     unsigned char *tKg = lds + L::KG0, *tKd = lds + L::KD0, *tA = lds + L::A0, *tP = lds + L::P0;
     unsigned char *tV = lds + L::V0, *tO = lds + L::O0;
     unsigned char *tXh = lds + L::X0, *tXl = tXh + ST::BYTES, *tVh = tXl + ST::BYTES, *tVl = tVh + ST::BYTES;
@@ -591,14 +605,13 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_kda_mma_kernel(BwdParams p) 
         split8_h2(x, hi, lo);
     };
 
-    f32x4 dA[2];                                          // 64 x 64 tiles w, w + 8
+    f32x4 dA[2], dP[2];                                   // 64 x 64 tiles w, w + 8
     f32x4 dqS[NQT], dkD[NQT], dkX[NQT];                   // dq / dk tiles (tt, m)
-    dA[0] = dA[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dA[0] = dA[1] = dP[0] = dP[1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int q = 0; q < NQT; ++q) dqS[q] = dkD[q] = dkX[q] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int ct = w & 3, tt0 = 2 * (w >> 2);             // token x column tiles of the half
     const int m = w % MD, qt0 = (w / MD) * NQT;           // dq / dk tiles: rows 16 m of D_k, tokens
-    float *vpw = p.vp + unit * 64 * DV;
 
     const int NH = DV / 64;                               // halves of the value columns
     for (int hv = 0; hv < NH; ++hv) {
@@ -662,8 +675,6 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_kda_mma_kernel(BwdParams p) 
                 }
                 put_t16<ST>(tVh, tVl, 16 * ct + l16, 16 * tt + 4 * grp, vp);
                 put_t16<ST>(tDh, tDl, 16 * ct + l16, 16 * tt + 4 * grp, dvp);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) vpw[(16 * tt + 4 * grp + r) * DV + colg] = vp[r];
             }
         }
         __syncthreads();
@@ -695,9 +706,13 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_kda_mma_kernel(BwdParams p) 
         for (int q = 0; q < 2; ++q) {
             const int tix = w + 8 * q, ti = tix >> 2, tj = tix & 3;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb) {
                 mma_h2(dA[q], as_f16(pi_col<ST>(tDh, 16 * ti, kb, grp, l16)), as_f16(pi_col<ST>(tDl, 16 * ti, kb, grp, l16)),
                        as_f16(pi_col<ST>(tXh, 16 * tj, kb, grp, l16)), as_f16(pi_col<ST>(tXl, 16 * tj, kb, grp, l16)));
+                if (tj <= ti)
+                    mma_h1(dP[q], bf_to_f16(pi_row<ST>(tO, 16 * ti + l16, kb, grp)), as_f16(pi_col<ST>(tVh, 16 * tj, kb, grp, l16)),
+                           as_f16(pi_col<ST>(tVl, 16 * tj, kb, grp, l16)));
+            }
         }
         {
             // S and dS_next rows 16 m + l16 over this half's columns, in pi order
@@ -739,26 +754,47 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_kda_mma_kernel(BwdParams p) 
         }
     }
 
-    // ---- dq, dk through the states; dG's row terms (the last row's e^{G_C} terms are collected).
-    //      The lane's gate values: the cumsum of its channel d down the chunk, kept at its rows.
-    const int d = 16 * m + l16;
-    float Gt[NQT][4], gC;
-    {
-        const bf16 *gp = static_cast<const bf16 *>(p.g) + tok0 * p.H_v * DK + (int64_t)h * DK + d;
+    // ---- the tail.  G (every channel's inclusive cumsum down the chunk; rows past the end repeat
+    //      the last) goes where the Kg and Kd tiles were, the raw K tile where the V and dO halves
+    //      were, the raw Q tile where the dX pair was; dA^T, then dL, use the X pair's place.
+    static_assert(64 * (DK + 4) * 4 <= 2 * KT::BYTES, "G fits where the Kg and Kd tiles were");
+    static_assert(KT::BYTES <= 2 * ST::BYTES, "K and Q each fit where two 64 x 64 tiles were");
+    float *sG = reinterpret_cast<float *>(lds + L::KG0);
+    unsigned char *tK = tV, *tQ = tEh;
+    constexpr int GP = DK + 4, NPART = 512 / DK, NR = 64 / NPART;
+    __syncthreads();   // every wave is done with the Kg, Kd, V, dO and dX tiles
+    const bf16 *kin = static_cast<const bf16 *>(p.k) + tok0 * qks + (int64_t)hq * DK;
+    const bf16 *qin = static_cast<const bf16 *>(p.q) + tok0 * qks + (int64_t)hq * DK;
+    load.template operator()<KT>(tK, rsrc_words(kin, ((nv - 1) * qks + DK) * 2), qks * 2);
+    load.template operator()<KT>(tQ, rsrc_words(qin, ((nv - 1) * qks + DK) * 2), qks * 2);
+    {   // thread (dd, part) scans NR rows of channel dd; every load issued before any is used
+        const int dd = tid % DK, part = tid / DK;
+        const bf16 *gp = static_cast<const bf16 *>(p.g) + tok0 * p.H_v * DK + (int64_t)h * DK + dd;
+        float v[NR];
+#pragma unroll
+        for (int e = 0; e < NR; ++e) v[e] = (float)gp[(int64_t)min(part * NR + e, nv - 1) * p.H_v * DK];
         float acc = 0.f;
 #pragma unroll
-        for (int t = 0; t < 64; ++t) {
-            if (t < nv) acc += (float)gp[(int64_t)t * p.H_v * DK];
-#pragma unroll
-            for (int q = 0; q < NQT; ++q)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (t == 16 * (qt0 + q) + 4 * grp + r) Gt[q][r] = acc;
+        for (int e = 0; e < NR; ++e) {
+            acc += part * NR + e < nv ? v[e] : 0.f;
+            v[e] = acc;
         }
-        gC = acc;
+        rtot[part * DK + dd] = acc;
+        __syncthreads();
+        float base = 0.f;
+        for (int pp = 0; pp < part; ++pp) base += rtot[pp * DK + dd];
+#pragma unroll
+        for (int e = 0; e < NR; ++e) sG[(part * NR + e) * GP + dd] = v[e] + base;
+        __syncthreads();
     }
-    const bf16 *qp = static_cast<const bf16 *>(p.q) + tok0 * qks + (int64_t)hq * DK + d;
-    const bf16 *kp = static_cast<const bf16 *>(p.k) + tok0 * qks + (int64_t)hq * DK + d;
+    wait_vm<0>();      // this wave's K and Q tile loads
+    __syncthreads();   // both tiles are complete
+    const int d = 16 * m + l16;
+    const float gC = sG[63 * GP + d];
+    auto kq_at = [&](const unsigned char *t, int row) __attribute__((always_inline)) {
+        return (float)*reinterpret_cast<const bf16 *>(t + KT::off(row, d * 2));
+    };
+    // dq, dk through the states and their terms of dG (rows past the end read zero q and k)
     f32x4 dq[NQT], dk[NQT], dG[NQT];
     float dgd_sum = 0.f;
 #pragma unroll
@@ -769,9 +805,8 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_kda_mma_kernel(BwdParams p) 
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = 16 * tt + 4 * grp + r;
-            const float G = Gt[q][r], eg = __expf(G);
-            const float qv = t < nv ? (float)qp[(int64_t)t * qks] : 0.f;
-            const float kv = t < nv ? (float)kp[(int64_t)t * qks] : 0.f;
+            const float G = sG[t * GP + d], eg = __expf(G);
+            const float qv = kq_at(tQ, t), kv = kq_at(tK, t);
             const float dq_o = p.scale * eg * dqS[q][r];
             const float dk_x = -bev[r] * eg * dkX[q][r];
             const float dk_d = __expf(gC - G) * dkD[q][r];
@@ -786,29 +821,20 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_kda_mma_kernel(BwdParams p) 
     }
     dgd_sum = sum_groups(dgd_sum);
     if (grp == 0) atomicAdd(&rdgc[d], dgd_sum);
-    __syncthreads();   // every wave is done with the operand buffers; rdgc and rdb are complete
-    // ---- dA transposed ([s][t]) into the X buffers
+    // ---- dA transposed and scale dP transposed (strictly lower; its diagonal kept apart)
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-        const int tix = w + 8 * q, ti = tix >> 2, tj = tix & 3;
-        put_t16<ST>(tXh, tXl, 16 * tj + l16, 16 * ti + 4 * grp, dA[q]);
-    }
-    const int hs = p.dq_v == p.dq ? hq : h, hn = p.dq_v == p.dq ? p.H_qk : p.H_v;
-#pragma unroll
-    for (int q = 0; q < NQT; ++q) {
-        const int tt = qt0 + q;
+        const int tix = w + 8 * q, ti = tix >> 2, tj = tix & 3, j = 16 * tj + l16;
+        f32x4 x;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int t = 16 * tt + 4 * grp + r;
-            if (t < nv) {
-                const int64_t o = ((tok0 + t) * hn + hs) * DK + d;
-                p.dq_v[o] = dq[q][r];
-                p.dk_v[o] = dk[q][r];
-                p.dg[((tok0 + t) * p.H_v + h) * DK + d] = dG[q][r] + (t == nv - 1 ? rdgc[d] : 0.f);
-            }
+            const int i = 16 * ti + 4 * grp + r;
+            x[r] = j < i ? p.scale * dP[q][r] : 0.f;
+            if (j == i) rdpd[i] = p.scale * dP[q][r];
         }
+        put_t16<ST>(tXh, tXl, j, 16 * ti + 4 * grp, dA[q]);
+        put_t16<ST>(tDh, tDl, j, 16 * ti + 4 * grp, x);
     }
-    if (tid < nv) p.dbeta[(tok0 + tid) * p.H_v + h] = rdb[tid];
     __syncthreads();
     // ---- T = A^T dA, transposed ([t][i]) into the V' buffers
 #pragma unroll
@@ -823,9 +849,8 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_kda_mma_kernel(BwdParams p) 
         }
         put_t16<ST>(tVh, tVl, 16 * tj + l16, 16 * ti + 4 * grp, T);
     }
-    __syncthreads();
-    // ---- dL = -T A^T (strictly lower), to the workspace
-    float *dLw = p.dlmat + unit * 4096;
+    __syncthreads();   // every wave is done with dA^T: dL takes its place
+    // ---- dL = -T A^T (strictly lower), transposed into the X buffers
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         const int tix = w + 8 * q, ti = tix >> 2, tj = tix & 3;
@@ -840,10 +865,134 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_kda_mma_kernel(BwdParams p) 
             }
         }
         const int j = 16 * tj + l16;
+        f32x4 x;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = 16 * ti + 4 * grp + r;
-            dLw[i * 64 + j] = j < i ? -dl[r] : 0.f;
+        for (int r = 0; r < 4; ++r) x[r] = j < 16 * ti + 4 * grp + r ? -dl[r] : 0.f;
+        put_t16<ST>(tXh, tXl, j, 16 * ti + 4 * grp, x);
+    }
+    __syncthreads();   // dP and dL are complete
+    // ---- the P and L terms, block R of rows at a time (the dq / dk tiles of this wave)
+    auto dpair = [&](const unsigned char *th, const unsigned char *tl, int row, int col) __attribute__((always_inline)) {
+        return (float)*reinterpret_cast<const f16 *>(th + ST::off(row, col * 2)) +
+               (float)*reinterpret_cast<const f16 *>(tl + ST::off(row, col * 2));
+    };
+    unsigned char *tLh = tXh, *tLl = tXl;
+#pragma unroll
+    for (int q = 0; q < NQT; ++q) {
+        const int R = qt0 + q;
+        const float Ga = R > 0 ? sG[(16 * R - 1) * GP + d] : 0.f;    // reference rows 16 R - 1, 16 R + 15
+        const float Gb = sG[(16 * R + 15) * GP + d];
+        const bool whole = Ga - Gb > kMaxLn;   // the block's decay in this column: split factors would overflow fp16
+        f32x4 aq = {0.f, 0.f, 0.f, 0.f}, ar = aq, ap = aq, al = aq;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            if (32 * kb > 16 * R + 15) continue;              // left sums: t <= 16 R + 15
+            const Frag<bf16> kc = pi_col<KT>(tK, 16 * m, kb, grp, l16);
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int t = 32 * kb + (e < 4 ? 4 * grp + e : 16 + 4 * grp + e - 4);
+                const bool in = t <= 16 * R + 15 && !(whole && t >= 16 * R);
+                x[e] = in ? (float)kc.v[e] * __expf(Ga - sG[t * GP + d]) : 0.f;
+            }
+            Frag<f16> bh, bl;
+            split8_h2(x, bh, bl);
+            mma_h2(aq, as_f16(pi_col<ST>(tDh, 16 * R, kb, grp, l16)), as_f16(pi_col<ST>(tDl, 16 * R, kb, grp, l16)), bh, bl);
+            mma_h2(ar, as_f16(pi_col<ST>(tLh, 16 * R, kb, grp, l16)), as_f16(pi_col<ST>(tLl, 16 * R, kb, grp, l16)), bh, bl);
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            if (32 * kb + 31 < 16 * R) continue;              // right sums: t >= 16 R
+            const Frag<bf16> qc = pi_col<KT>(tQ, 16 * m, kb, grp, l16), kc = pi_col<KT>(tK, 16 * m, kb, grp, l16);
+            const int t0 = 32 * kb + 4 * grp;
+            const float4 ba = *reinterpret_cast<const float4 *>(g + GB_BETA + t0);
+            const float4 bc = *reinterpret_cast<const float4 *>(g + GB_BETA + t0 + 16);
+            const float fb[8] = {ba.x, ba.y, ba.z, ba.w, bc.x, bc.y, bc.z, bc.w};
+            float xq[8], xk[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int t = 32 * kb + (e < 4 ? 4 * grp + e : 16 + 4 * grp + e - 4);
+                const bool in = t >= 16 * R && !(whole && t <= 16 * R + 15);
+                const float f = in ? __expf(sG[t * GP + d] - Gb) : 0.f;
+                xq[e] = (float)qc.v[e] * f;
+                xk[e] = fb[e] * (float)kc.v[e] * f;
+            }
+            Frag<f16> qh, ql, kh, kl;
+            split8_h2(xq, qh, ql);
+            split8_h2(xk, kh, kl);
+            mma_h2(ap, as_f16(pi_row<ST>(tDh, 16 * R + l16, kb, grp)), as_f16(pi_row<ST>(tDl, 16 * R + l16, kb, grp)), qh, ql);
+            mma_h2(al, as_f16(pi_row<ST>(tLh, 16 * R + l16, kb, grp)), as_f16(pi_row<ST>(tLl, 16 * R + l16, kb, grp)), kh, kl);
+        }
+        const float4 be = rows4(GB_BETA, R);
+        const float bev[4] = {be.x, be.y, be.z, be.w};
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int r = 16 * R + 4 * grp + rr;
+            const float Gr = sG[r * GP + d];
+            float vq = aq[rr] * __expf(Gr - Ga), vr = ar[rr] * __expf(Gr - Ga);
+            float vp = ap[rr] * __expf(Gb - Gr), vl = al[rr] * __expf(Gb - Gr);
+            if (whole) {   // block R's pairs of this column with their whole factors (each at most 1)
+                for (int t = 16 * R; t < r; ++t) {
+                    const float f = __expf(Gr - sG[t * GP + d]), kt = kq_at(tK, t) * f;
+                    vq += dpair(tDh, tDl, t, r) * kt;             // dP[r][t] (tile [t][r])
+                    vr += dpair(tLh, tLl, t, r) * kt;
+                }
+                for (int t = r + 1; t <= 16 * R + 15; ++t) {
+                    const float f = __expf(sG[t * GP + d] - Gr);
+                    vp += dpair(tDh, tDl, r, t) * kq_at(tQ, t) * f;   // dP[t][r] (tile [r][t])
+                    vl += dpair(tLh, tLl, r, t) * g[GB_BETA + t] * kq_at(tK, t) * f;
+                }
+            }
+            const float kr = kq_at(tK, r), qr = kq_at(tQ, r), dpd = rdpd[r];
+            dq[q][rr] += vq + dpd * kr;
+            dk[q][rr] += vp + dpd * qr + bev[rr] * vr + vl;
+            dG[q][rr] += qr * vq + kr * bev[rr] * vr - kr * (vp + vl);
+            const float db = sum16(kr * vr);
+            if (l16 == 0) atomicAdd(&rdb[r], db);
+        }
+        reg_fence();
+    }
+    __syncthreads();   // every wave is done with G; rdb and rdgc are complete
+    // ---- dG (with the last valid row's e^{G_C} terms) into G's place, then its reverse cumsum per
+    //      channel (the notes' Step 7), dq, dk and dbeta
+#pragma unroll
+    for (int q = 0; q < NQT; ++q)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int t = 16 * (qt0 + q) + 4 * grp + rr;
+            sG[t * GP + d] = t < nv ? dG[q][rr] + (t == nv - 1 ? rdgc[d] : 0.f) : 0.f;
+        }
+    const int hs = p.dq_v == p.dq ? hq : h, hn = p.dq_v == p.dq ? p.H_qk : p.H_v;
+#pragma unroll
+    for (int q = 0; q < NQT; ++q)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int t = 16 * (qt0 + q) + 4 * grp + rr;
+            if (t < nv) {
+                const int64_t o = ((tok0 + t) * hn + hs) * DK + d;
+                p.dq_v[o] = dq[q][rr];
+                p.dk_v[o] = dk[q][rr];
+            }
+        }
+    if (tid < nv) p.dbeta[(tok0 + tid) * p.H_v + h] = rdb[tid];
+    __syncthreads();
+    {
+        const int dd = tid % DK, part = tid / DK;
+        float v[NR];
+        float acc = 0.f;
+#pragma unroll
+        for (int e = NR - 1; e >= 0; --e) {
+            acc += sG[(part * NR + e) * GP + dd];
+            v[e] = acc;
+        }
+        rtot[part * DK + dd] = acc;
+        __syncthreads();
+        float later = 0.f;
+        for (int pp = part + 1; pp < NPART; ++pp) later += rtot[pp * DK + dd];
+#pragma unroll
+        for (int e = 0; e < NR; ++e) {
+            const int t = part * NR + e;
+            if (t < nv) p.dg[((tok0 + t) * p.H_v + h) * DK + dd] = v[e] + later;
         }
     }
 }

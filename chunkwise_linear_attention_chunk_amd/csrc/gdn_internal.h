@@ -233,8 +233,8 @@ hipError_t launch_warm_stats(const WarmParams &p, hipStream_t s);
 hipError_t launch_bwd(int dtype, int D_k, const BwdParams &p, hipStream_t s);
 // the per-chunk gradients on the matrix cores (bf16 inputs, scalar gate)
 hipError_t launch_bwd_chunk_mma(int D_k, const BwdParams &p, hipStream_t s);
-// per-channel gates, bf16 inputs: the products with S and dS_next on the matrix cores (the work of
-// the plain kernel (a); kernel (b) then adds the P and L terms)
+// per-channel gates, bf16 inputs: every per-chunk gradient on the matrix cores (the work of the
+// plain kernels (a) and (b))
 hipError_t launch_bwd_chunk_kda_mma(int D_k, const BwdParams &p, hipStream_t s);
 hipError_t launch_recurrent(int dtype, int D_k, int gate, const RecurrentParams &p, hipStream_t s);
 
