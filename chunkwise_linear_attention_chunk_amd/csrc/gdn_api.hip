@@ -528,8 +528,13 @@ gdn_status validate_and_plan_bwd(const gdn_bwd_args *b, BwdPlan *bp) {
     const size_t st_bytes = (size_t)bp->fwd.total_chunks * b->H_v * b->D_k * b->D_v * sizeof(float);
     bp->off_states = off; off = align_up(off + st_bytes);
     bp->off_dsn = off;    off = align_up(off + st_bytes);
-    bp->off_pmat = off;   off = align_up(off + (size_t)bp->fwd.total_chunks * b->H_v * 4096 * sizeof(float));
-    if (b->gate_kind == GDN_GATE_CHANNEL) {   // V' and dL of every chunk, between the two gradient kernels
+    // scale Pt (scalar gate; per-channel gates with fp32 inputs: scale P), and with per-channel gates
+    // and fp32 inputs V' and dL of every chunk, between the two gradient kernels (bf16 inputs take
+    // P from the per-chunk kernel and form every gradient of a chunk in one kernel)
+    const bool kda_plain = b->gate_kind == GDN_GATE_CHANNEL && b->dtype == GDN_DTYPE_F32;
+    bp->off_pmat = off;
+    if (b->gate_kind != GDN_GATE_CHANNEL || kda_plain) off = align_up(off + (size_t)bp->fwd.total_chunks * b->H_v * 4096 * sizeof(float));
+    if (kda_plain) {
         bp->off_vp = off; off = align_up(off + (size_t)bp->fwd.total_chunks * b->H_v * 64 * b->D_v * sizeof(float));
         bp->off_dl = off; off = align_up(off + (size_t)bp->fwd.total_chunks * b->H_v * 4096 * sizeof(float));
     }
@@ -601,8 +606,9 @@ extern "C" gdn_status gdn_bwd(const gdn_bwd_args *a, void *workspace, size_t wor
     bw.dsnext = reinterpret_cast<float *>(ws + bp.off_dsn);
     bw.pmat = reinterpret_cast<float *>(ws + bp.off_pmat);
     bw.channel = channel ? 1 : 0;
-    bw.vp = channel ? reinterpret_cast<float *>(ws + bp.off_vp) : nullptr;
-    bw.dlmat = channel ? reinterpret_cast<float *>(ws + bp.off_dl) : nullptr;
+    const bool kda_plain = channel && a->dtype == GDN_DTYPE_F32;
+    bw.vp = kda_plain ? reinterpret_cast<float *>(ws + bp.off_vp) : nullptr;
+    bw.dlmat = kda_plain ? reinterpret_cast<float *>(ws + bp.off_dl) : nullptr;
     bw.dq = a->dq; bw.dk = a->dk; bw.dv = a->dv; bw.dg = a->dg; bw.dbeta = a->dbeta; bw.dh0 = a->dh0;
     const bool grouped = a->H_v != a->H_qk;
     bw.dq_v = grouped ? reinterpret_cast<float *>(ws + bp.off_dqv) : a->dq;

@@ -96,6 +96,20 @@ def test_backward_per_channel_bf16():
     _check(x, TOL["bf16"], "KDA bf16", seed=12)
 
 
+def test_backward_per_channel_bf16_head_dim_64_grouped_heads():
+    x = synth.make_inputs(synth.workload("kda_bf16", B=2, H=4, H_qk=2, D=64, T=200, h0=True, seed=633))
+    _check(x, TOL["bf16"], "KDA bf16 D=64 H_v=4 H_qk=2", seed=14)
+
+
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+@pytest.mark.parametrize("dk,dv", [(128, 64), (64, 128)])
+def test_backward_bf16_key_and_value_dims_differ(gate, dk, dv):
+    from test_gpu_parity import _dims
+    name = "qwen3next_bf16" if gate == "scalar" else "kda_bf16"
+    x = _dims(synth.make_inputs(synth.workload(name, B=1, H=2, T=64 * 3 + 29, h0=True, seed=634 + dk)), dk, dv)
+    _check(x, TOL["bf16"], f"{gate} bf16 D_k={dk} D_v={dv}", seed=15)
+
+
 def test_backward_per_channel_packed():
     x = synth.make_inputs(synth.workload("kda_bf16", B=1, n_seqs=4, lens=(1, 0, 130, 64), H=2, h0=True, seed=632))
     _check(x, TOL["bf16"], "KDA bf16 packed", seed=13, dht=False)
