@@ -196,7 +196,9 @@ __device__ __forceinline__ void ld_vcol4(const unsigned char *tile, int m, int c
 // MODE 1: context-parallel pre-process (chain waves only) over "virtual" columns: value columns
 //         (V as given, S = 0 at the segment start) give S*, identity columns (V = 0, S = I) give
 //         the segment's transition matrix M; both are written to the workspace.
-template <typename T, int DK, int NSUB, int NBUF, int MODE, int GATE>
+// ST (main pass only): also store the state entering every chunk (the backward's recomputed
+//         states); a separate build, so the forward carries none of it.
+template <typename T, int DK, int NSUB, int NBUF, int MODE, int GATE, bool ST = false>
 __global__ __launch_bounds__(MODE == 0 ? 128 * NSUB : 64 * NSUB,
                              NBUF == 1 && MODE == 0 && GATE == 0 && sizeof(T) == 2 ? 2 : 1)
 void chunk_kernel(ChunkParams p) {
@@ -446,8 +448,18 @@ void chunk_kernel(ChunkParams p) {
                 // inter-chunk part: scale diag(gamma) Q S_c (S_c was handed over before this chunk);
                 // the state and Q fragments first (the Q lo parts of per-channel gates as they are used)
                 if (more) {                                       // the output waves' share, at once
-                    issue_kq(c + 1, tnext, 0, 1, OUT_LD);
+                    issue_kq(c + 1, tnext, 0, 1, ST ? OUT_LD & ~LD_Q : OUT_LD);
                     issue_apvg(c + 1, tnext, 0, 1, OUT_LD);
+                }
+                if constexpr (ST) {   // states only: the loads and the chain's barriers, no output
+                    lds_only_barrier();
+                    if constexpr (EARLY_LD) {
+                        if (c + 1 < nch) {
+                            issue_kq(c + 1, tiles0, 0, 1, LD_ALL & ~LATE_LD & ~LD_Q);
+                            issue_apvg(c + 1, tiles0, 0, 1, LD_ALL & ~LATE_LD);
+                        }
+                    }
+                    return;
                 }
                 Frag<T> sh[NSUB][NKB], sl[NSUB][NKB], qf[NKB][NR];
 #pragma unroll
@@ -607,8 +619,8 @@ void chunk_kernel(ChunkParams p) {
         unsigned char *tcur = B == 0 ? tiles0 : tiles1;
         unsigned char *tnext = B == 0 ? tiles1 : tiles0;
         chunk_top.template operator()<!OUT || CHAIN_LD>(c);
-        if constexpr (OUT) {
-            if (p.chunk_states) {   // the state entering this chunk (no CP: segment = sequence)
+        if constexpr (OUT && ST) {
+            {   // the state entering this chunk (no CP: segment = sequence)
                 float *st = p.chunk_states + ((int64_t)(si.chunk0 + cs + c) * p.H_v + h) * DK * DV;
 #pragma unroll
                 for (int m = 0; m < MD; ++m)
@@ -925,7 +937,7 @@ hipError_t launch_plan(const PlanParams &p, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int MODE, int GATE>
+template <int MODE, int GATE, bool ST = false>
 static hipError_t launch_rec(int dtype, int D_k, int BV, const ChunkParams &p, hipStream_t s) {
     const int units = (p.seg_only ? p.N : p.total_segs) * p.H_v;
     const unsigned groups = (unsigned)((units + 7) / 8);
@@ -933,7 +945,7 @@ static hipError_t launch_rec(int dtype, int D_k, int BV, const ChunkParams &p, h
     if (units == 0) return hipSuccess;
 #define GDN_CHUNK_CASE(DT, T_, DK_, NSUB_, NBUF_)                                                         \
     if (dtype == DT && D_k == DK_ && BV == 16 * NSUB_) {                                                  \
-        hipLaunchKernelGGL((chunk_kernel<T_, DK_, NSUB_, NBUF_, MODE, GATE>), grid, dim3((MODE == 0 ? 128 : 64) * NSUB_), \
+        hipLaunchKernelGGL((chunk_kernel<T_, DK_, NSUB_, NBUF_, MODE, GATE, ST>), grid, dim3((MODE == 0 ? 128 : 64) * NSUB_), \
                            0, s, p);                                                                      \
         return hipGetLastError();                                                                         \
     }
@@ -964,6 +976,9 @@ static hipError_t launch_rec(int dtype, int D_k, int BV, const ChunkParams &p, h
 }
 
 hipError_t launch_chunk(int dtype, int D_k, int BV, int gate, const ChunkParams &p, hipStream_t s) {
+    if (p.chunk_states)
+        return gate == GDN_GATE_CHANNEL_K ? launch_rec<0, GDN_GATE_CHANNEL_K, true>(dtype, D_k, BV, p, s)
+                                          : launch_rec<0, 0, true>(dtype, D_k, BV, p, s);
     return gate == GDN_GATE_CHANNEL_K ? launch_rec<0, GDN_GATE_CHANNEL_K>(dtype, D_k, BV, p, s)
                                       : launch_rec<0, 0>(dtype, D_k, BV, p, s);
 }
