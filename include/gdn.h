@@ -19,7 +19,10 @@
  *
  *   Per-channel gates (KDA; "KDA源码剖析之FLA", sections 3-5): the log-gate is a
  *   [D_k] vector per token, the decay Diag(exp(gk_t)) is applied to the rows of S
- *   before the read and the erase.
+ *   before the read and the erase.  With bf16 inputs the per-channel path multiplies
+ *   fp16 operands (the gated q and k rows, the intra-chunk matrix and the inverse),
+ *   which requires q and k rows of unit scale (L2-normalised, as the method has them,
+ *   or normalised by the prologue's qk_l2norm): larger rows can overflow fp16.
  *
  * Tensor layouts (row-major, contiguous, device memory):
  *   q, k         [B, T, H_qk, D_k]   dtype
