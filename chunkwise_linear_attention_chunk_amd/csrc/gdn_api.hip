@@ -305,18 +305,37 @@ gdn_status run_fwd(const gdn_fwd_args *a, void *workspace, size_t workspace_byte
         return fail(GDN_ERR_WORKSPACE, "workspace is not %zu-byte aligned", kAlign);
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint32_t ran = 0;
-    // records the boundary after `stage` (or the start when stage < 0)
+    // Timed: every stage's kernel carries the boundary events in its own dispatch — the call's
+    // first kernel the start (events[0]), each stage's kernel its end (events[stage + 1]) — armed
+    // just before the stage's launch; a stage that launched nothing records them as plain events.
+    bool first = true;
+    auto arm = [&](int stage) {
+        if (events)
+            gdn::launch_events() = {first ? static_cast<hipEvent_t>(events[0]) : nullptr,
+                                    static_cast<hipEvent_t>(events[stage + 1])};
+    };
     auto mark = [&](int stage) -> hipError_t {
-        if (stage >= 0) ran |= 1u << stage;
-        return events ? hipEventRecord(static_cast<hipEvent_t>(events[stage + 1]), s) : hipSuccess;
+        ran |= 1u << stage;
+        if (!events) return hipSuccess;
+        gdn::LaunchEvents &le = gdn::launch_events();
+        hipError_t r = hipSuccess;
+        if (le.start) r = hipEventRecord(le.start, s);
+        if (r == hipSuccess && le.stop) r = hipEventRecord(le.stop, s);
+        le = gdn::LaunchEvents{nullptr, nullptr};
+        first = false;
+        return r;
     };
     auto done = [&](gdn_status r) {
         if (stages_run) *stages_run = ran;
+        gdn::launch_events() = gdn::LaunchEvents{nullptr, nullptr};
         return r;
     };
-    hipError_t e = mark(-1);
-    if (e != hipSuccess) return done(fail(GDN_ERR_HIP, "event record: %s", hipGetErrorString(e)));
-    if (a->N == 0) return done(GDN_OK);
+    hipError_t e = hipSuccess;
+    if (a->N == 0) {
+        if (events && (e = hipEventRecord(static_cast<hipEvent_t>(events[0]), s)) != hipSuccess)
+            return done(fail(GDN_ERR_HIP, "event record: %s", hipGetErrorString(e)));
+        return done(GDN_OK);
+    }
     char *ws = static_cast<char *>(workspace);
     const bool packed = a->cu_seqlens_dev != nullptr;
     gdn::SeqInfo *seq = packed ? reinterpret_cast<gdn::SeqInfo *>(ws + pl.off_seq) : nullptr;
@@ -327,6 +346,7 @@ gdn_status run_fwd(const gdn_fwd_args *a, void *workspace, size_t workspace_byte
     if (packed) {
         gdn::PlanParams pp{a->cu_seqlens_dev, a->N, a->T, a->B * a->T, (int)pl.total_chunks, pl.seg_chunks,
                            (int)pl.total_segs, seq, chunks, segs, order};
+        arm(GDN_STAGE_PLAN);
         e = gdn::launch_plan(pp, s);
         if (e != hipSuccess) return done(fail(GDN_ERR_HIP, "plan launch: %s", hipGetErrorString(e)));
         if ((e = mark(GDN_STAGE_PLAN)) != hipSuccess) return done(fail(GDN_ERR_HIP, "event: %s", hipGetErrorString(e)));
@@ -386,6 +406,7 @@ gdn_status run_fwd(const gdn_fwd_args *a, void *workspace, size_t workspace_byte
             return r == hipSuccess;
         };
         bool ok = check(hipEventRecord(ev[0], s), "event") && check(hipStreamWaitEvent(side, ev[0], 0), "stream wait");
+        if (ok && events && first) ok = check(hipEventRecord(static_cast<hipEvent_t>(events[0]), s), "event");
         for (int j = 0; ok && j < P; ++j) {
             ok = check(intra(j * L, std::min(L, nc - j * L), side), "intra launch");
             if (ok && j == 0 && events) {
@@ -402,10 +423,13 @@ gdn_status run_fwd(const gdn_fwd_args *a, void *workspace, size_t workspace_byte
         }
         release();
         if (!ok) return done(GDN_ERR_HIP);
-        if ((e = mark(GDN_STAGE_CHUNK)) != hipSuccess) return done(fail(GDN_ERR_HIP, "event: %s", hipGetErrorString(e)));
+        ran |= 1u << GDN_STAGE_CHUNK;
+        if (events && (e = hipEventRecord(static_cast<hipEvent_t>(events[GDN_STAGE_CHUNK + 1]), s)) != hipSuccess)
+            return done(fail(GDN_ERR_HIP, "event: %s", hipGetErrorString(e)));
         return done(GDN_OK);
     }
 
+    arm(GDN_STAGE_INTRA);
     e = intra(0, 0, s);
     if (e != hipSuccess) return done(fail(GDN_ERR_HIP, "intra launch: %s", hipGetErrorString(e)));
     if ((e = mark(GDN_STAGE_INTRA)) != hipSuccess) return done(fail(GDN_ERR_HIP, "event: %s", hipGetErrorString(e)));
@@ -415,6 +439,7 @@ gdn_status run_fwd(const gdn_fwd_args *a, void *workspace, size_t workspace_byte
         const float tol = a->cp_warmup_tol > 0.f ? a->cp_warmup_tol : 0x1p-24f;
         gdn::WarmParams wp{segs, seq, cp.gates, a->T, a->H_v, pl.seg_chunks, (int)pl.total_segs, std::log2(tol),
                            reinterpret_cast<int *>(ws + pl.off_warm)};
+        arm(GDN_STAGE_CP_PRE);
         e = gdn::launch_warm_stats(wp, s);
         if (e != hipSuccess) return done(fail(GDN_ERR_HIP, "warmup statistics launch: %s", hipGetErrorString(e)));
         if ((e = mark(GDN_STAGE_CP_PRE)) != hipSuccess) return done(fail(GDN_ERR_HIP, "event: %s", hipGetErrorString(e)));
@@ -424,6 +449,7 @@ gdn_status run_fwd(const gdn_fwd_args *a, void *workspace, size_t workspace_byte
         cp.seg_m = reinterpret_cast<float *>(ws + pl.off_m);
         cp.seg_start = reinterpret_cast<float *>(ws + pl.off_start);
         const bool xyz = pl.xyz;
+        arm(GDN_STAGE_CP_PRE);
         if (xyz) {
             e = gdn::launch_cp_pre_xyz(a->D_k, cp, s);
         } else {
@@ -435,10 +461,12 @@ gdn_status run_fwd(const gdn_fwd_args *a, void *workspace, size_t workspace_byte
         if ((e = mark(GDN_STAGE_CP_PRE)) != hipSuccess) return done(fail(GDN_ERR_HIP, "event: %s", hipGetErrorString(e)));
         gdn::FixParams fp{segs, seq, a->T, a->N, a->H_v, a->D_v, pl.seg_chunks, (int)pl.total_segs, a->h0, cp.seg_sstar, cp.seg_m,
                           reinterpret_cast<float *>(ws + pl.off_start)};
+        arm(GDN_STAGE_CP_FIX);
         e = xyz ? gdn::launch_cp_fix_xyz(a->D_k, fp, s) : gdn::launch_cp_fix(a->dtype, a->D_k, fp, s);
         if (e != hipSuccess) return done(fail(GDN_ERR_HIP, "cp fix-up launch: %s", hipGetErrorString(e)));
         if ((e = mark(GDN_STAGE_CP_FIX)) != hipSuccess) return done(fail(GDN_ERR_HIP, "event: %s", hipGetErrorString(e)));
     }
+    arm(GDN_STAGE_CHUNK);
     e = gdn::launch_chunk(a->dtype, a->D_k, pl.BV, a->gate_kind, cp, s);
     if (e != hipSuccess) return done(fail(GDN_ERR_HIP, "chunk launch: %s", hipGetErrorString(e)));
     if ((e = mark(GDN_STAGE_CHUNK)) != hipSuccess) return done(fail(GDN_ERR_HIP, "event: %s", hipGetErrorString(e)));
@@ -446,6 +474,13 @@ gdn_status run_fwd(const gdn_fwd_args *a, void *workspace, size_t workspace_byte
 }
 
 }  // namespace
+
+namespace gdn {
+LaunchEvents &launch_events() {
+    static thread_local LaunchEvents le{nullptr, nullptr};
+    return le;
+}
+}  // namespace gdn
 
 extern "C" gdn_status gdn_fwd(const gdn_fwd_args *a, void *workspace, size_t workspace_bytes, void *stream) {
     return run_fwd(a, workspace, workspace_bytes, stream, nullptr, nullptr);

@@ -933,7 +933,7 @@ __global__ __launch_bounds__(256) void warm_stats_kernel(WarmParams p) {
 }  // namespace
 
 hipError_t launch_plan(const PlanParams &p, hipStream_t s) {
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, s, p);
+    launch_k(plan_kernel, dim3(1), dim3(256), s, p);
     return hipGetLastError();
 }
 
@@ -945,8 +945,7 @@ static hipError_t launch_rec(int dtype, int D_k, int BV, const ChunkParams &p, h
     if (units == 0) return hipSuccess;
 #define GDN_CHUNK_CASE(DT, T_, DK_, NSUB_, NBUF_)                                                         \
     if (dtype == DT && D_k == DK_ && BV == 16 * NSUB_) {                                                  \
-        hipLaunchKernelGGL((chunk_kernel<T_, DK_, NSUB_, NBUF_, MODE, GATE, ST>), grid, dim3((MODE == 0 ? 128 : 64) * NSUB_), \
-                           0, s, p);                                                                      \
+        launch_k((chunk_kernel<T_, DK_, NSUB_, NBUF_, MODE, GATE, ST>), grid, dim3((MODE == 0 ? 128 : 64) * NSUB_), s, p);                                                                      \
         return hipGetLastError();                                                                         \
     }
     if constexpr (GATE == GDN_GATE_CHANNEL_K) {
@@ -989,7 +988,7 @@ hipError_t launch_cp_pre(int dtype, int D_k, int BV, int gate, const ChunkParams
 hipError_t launch_warm_stats(const WarmParams &p, hipStream_t s) {
     const int64_t units = (int64_t)p.total_segs * p.H_v;
     if (units == 0) return hipSuccess;
-    hipLaunchKernelGGL(warm_stats_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, s, p);
+    launch_k(warm_stats_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), s, p);
     return hipGetLastError();
 }
 hipError_t launch_cp_fix(int dtype, int D_k, const FixParams &p, hipStream_t s) {
@@ -997,10 +996,10 @@ hipError_t launch_cp_fix(int dtype, int D_k, const FixParams &p, hipStream_t s) 
     const unsigned groups = (unsigned)((p.N * p.H_v + 7) / 8);
     const dim3 grid(groups * 8u * (unsigned)(p.D_v / 16)), block((unsigned)(D_k * 4));
     if (p.N * p.H_v == 0) return hipSuccess;
-    if (dtype == 1 && D_k == 128) hipLaunchKernelGGL((cp_fix_kernel<bf16, 128>), grid, block, 0, s, p);
-    else if (dtype == 1 && D_k == 64) hipLaunchKernelGGL((cp_fix_kernel<bf16, 64>), grid, block, 0, s, p);
-    else if (dtype == 0 && D_k == 128) hipLaunchKernelGGL((cp_fix_kernel<float, 128>), grid, block, 0, s, p);
-    else if (dtype == 0 && D_k == 64) hipLaunchKernelGGL((cp_fix_kernel<float, 64>), grid, block, 0, s, p);
+    if (dtype == 1 && D_k == 128) launch_k(cp_fix_kernel<bf16, 128>, grid, block, s, p);
+    else if (dtype == 1 && D_k == 64) launch_k(cp_fix_kernel<bf16, 64>, grid, block, s, p);
+    else if (dtype == 0 && D_k == 128) launch_k(cp_fix_kernel<float, 128>, grid, block, s, p);
+    else if (dtype == 0 && D_k == 64) launch_k(cp_fix_kernel<float, 64>, grid, block, s, p);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }

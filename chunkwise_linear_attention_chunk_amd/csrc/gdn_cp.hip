@@ -450,10 +450,10 @@ hipError_t launch_cp_pre_xyz(int D_k, const ChunkParams &p, hipStream_t s) {
     const bool one = DV == D_k;
     const int n_blocks = one ? 1 : (DV + D_k) / 64;
     const dim3 grid((unsigned)(((units + 7) / 8) * 8 * n_blocks));
-    if (one && D_k == 128) hipLaunchKernelGGL((cp_pre_xyz_kernel<128, 8, 2, 128>), grid, dim3(512), 0, s, p, n_blocks);
-    else if (one && D_k == 64) hipLaunchKernelGGL((cp_pre_xyz_kernel<64, 8, 1, 64>), grid, dim3(512), 0, s, p, n_blocks);
-    else if (D_k == 128 && DV == 64) hipLaunchKernelGGL((cp_pre_xyz_kernel<128, 4, 1, 64>), grid, dim3(256), 0, s, p, n_blocks);
-    else if (D_k == 64 && DV == 128) hipLaunchKernelGGL((cp_pre_xyz_kernel<64, 4, 1, 64>), grid, dim3(256), 0, s, p, n_blocks);
+    if (one && D_k == 128) launch_k(cp_pre_xyz_kernel<128, 8, 2, 128>, grid, dim3(512), s, p, n_blocks);
+    else if (one && D_k == 64) launch_k(cp_pre_xyz_kernel<64, 8, 1, 64>, grid, dim3(512), s, p, n_blocks);
+    else if (D_k == 128 && DV == 64) launch_k(cp_pre_xyz_kernel<128, 4, 1, 64>, grid, dim3(256), s, p, n_blocks);
+    else if (D_k == 64 && DV == 128) launch_k(cp_pre_xyz_kernel<64, 4, 1, 64>, grid, dim3(256), s, p, n_blocks);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }
@@ -463,8 +463,8 @@ hipError_t launch_cp_fix_xyz(int D_k, const FixParams &p, hipStream_t s) {
     const unsigned groups = (unsigned)((p.N * p.H_v + 7) / 8);
     const dim3 grid(groups * 8u * (unsigned)(p.D_v / 16)), block((unsigned)(D_k * 4));
     if (p.N * p.H_v == 0) return hipSuccess;
-    if (D_k == 128) hipLaunchKernelGGL((cp_fix_xyz_kernel<128>), grid, block, 0, s, p);
-    else if (D_k == 64) hipLaunchKernelGGL((cp_fix_xyz_kernel<64>), grid, block, 0, s, p);
+    if (D_k == 128) launch_k(cp_fix_xyz_kernel<128>, grid, block, s, p);
+    else if (D_k == 64) launch_k(cp_fix_xyz_kernel<64>, grid, block, s, p);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }

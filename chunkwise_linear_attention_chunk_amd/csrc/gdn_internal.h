@@ -1,6 +1,7 @@
 // Internal interface between the C-ABI host code and the kernel launchers.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -217,6 +218,22 @@ struct BwdParams {           // backward (gdn_bwd), scalar gate
     float *dq_v, *dk_v;                    // per value head when H_v > H_qk, else dq / dk
     int replayed;                          // 1: states already holds every chunk's entering state
 };
+
+// Timed forward: when set, the library's next kernel launch on this host thread carries `start`
+// (recorded as the kernel begins) and `stop` (as it ends) in its own dispatch, so no separate
+// event packets sit between the kernels; the launch clears the hook.
+struct LaunchEvents {
+    hipEvent_t start, stop;
+};
+LaunchEvents &launch_events();
+// kernel<<<grid, block, 0, s>>>(args...), with the hook's events if set
+template <typename... KArgs, typename... Args>
+inline void launch_k(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t s, Args... args) {
+    LaunchEvents &le = launch_events();
+    const hipEvent_t a = le.start, b = le.stop;
+    le = LaunchEvents{nullptr, nullptr};
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, a, b, 0, static_cast<KArgs>(args)...);
+}
 
 hipError_t launch_plan(const PlanParams &p, hipStream_t s);
 hipError_t launch_intra(int dtype, int D_k, const IntraParams &p, hipStream_t s);

@@ -598,10 +598,10 @@ hipError_t launch_intra(int dtype, int D_k, const IntraParams &p, hipStream_t s)
     const int items = p.piece_cnt ? p.N * p.piece_cnt : p.n_chunks;
     const dim3 grid((unsigned)items * (unsigned)p.H_v), block(256);
     if (items == 0) return hipSuccess;
-    if (dtype == 1 && D_k == 128) hipLaunchKernelGGL((intra_kernel<bf16, 128>), grid, block, 0, s, p);
-    else if (dtype == 1 && D_k == 64) hipLaunchKernelGGL((intra_kernel<bf16, 64>), grid, block, 0, s, p);
-    else if (dtype == 0 && D_k == 128) hipLaunchKernelGGL((intra_kernel<float, 128>), grid, block, 0, s, p);
-    else if (dtype == 0 && D_k == 64) hipLaunchKernelGGL((intra_kernel<float, 64>), grid, block, 0, s, p);
+    if (dtype == 1 && D_k == 128) launch_k(intra_kernel<bf16, 128>, grid, block, s, p);
+    else if (dtype == 1 && D_k == 64) launch_k(intra_kernel<bf16, 64>, grid, block, s, p);
+    else if (dtype == 0 && D_k == 128) launch_k(intra_kernel<float, 128>, grid, block, s, p);
+    else if (dtype == 0 && D_k == 64) launch_k(intra_kernel<float, 64>, grid, block, s, p);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }
@@ -612,8 +612,8 @@ hipError_t launch_intra_kda(int dtype, int D_k, const IntraKdaParams &p, hipStre
     if (items == 0) return hipSuccess;
     const bool pro = p.pro.qk_l2norm || p.pro.beta_sigmoid || p.pro.A_log;
 #define GDN_INTRA_KDA_CASE(T, DK)                                                                   \
-    if (pro) hipLaunchKernelGGL((intra_kda_kernel<T, DK, true>), grid, block, 0, s, p);             \
-    else hipLaunchKernelGGL((intra_kda_kernel<T, DK, false>), grid, block, 0, s, p);
+    if (pro) launch_k(intra_kda_kernel<T, DK, true>, grid, block, s, p);             \
+    else launch_k(intra_kda_kernel<T, DK, false>, grid, block, s, p);
     if (dtype == 1 && D_k == 128) { GDN_INTRA_KDA_CASE(bf16, 128) }
     else if (dtype == 1 && D_k == 64) { GDN_INTRA_KDA_CASE(bf16, 64) }
     else if (dtype == 0 && D_k == 128) { GDN_INTRA_KDA_CASE(float, 128) }

@@ -169,10 +169,13 @@ enum {
 };
 
 /* Same as gdn_fwd, and also records caller-created hipEvent_t events on `stream` for
- * measurement: events[0] before the first stage and events[i + 1] right after stage i, for the
- * stages that run with these arguments (bit i of *stages_run is set for them); events of stages
- * that do not run are not recorded, so a stage's duration is the time from the previous recorded
- * event to its own.  events must hold GDN_N_STAGES + 1 valid events; stages_run may be NULL. */
+ * measurement: events[0] as the first stage's kernel starts and events[i + 1] as stage i's kernel
+ * ends, for the stages that run with these arguments (bit i of *stages_run is set for them).  The
+ * events ride in the kernels' own dispatches (hipExtLaunchKernel), so no separate event packets
+ * sit between the kernels and the timed call runs as fast as gdn_fwd; a stage that launches no
+ * kernel records its events as plain events.  Events of stages that do not run are not
+ * recorded, so a stage's duration is the time from the previous recorded event to its own.
+ * events must hold GDN_N_STAGES + 1 valid events; stages_run may be NULL. */
 gdn_status gdn_fwd_timed(const gdn_fwd_args *a, void *workspace, size_t workspace_bytes, void *stream,
                          void *const *events, uint32_t *stages_run);
 
