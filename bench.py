@@ -48,6 +48,8 @@ def parse():
                     help="skip the other configurations (reported by default with the Qwen3-Next-shaped headline)")
     ap.add_argument("--extra-steps", type=int, default=10)
     ap.add_argument("--extra-warmup", type=int, default=3)
+    ap.add_argument("--settle-ms", type=float, default=60.0,
+                    help="untimed run of each measured step before its warmup (0: none); see settle()")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: all host cores)")
     ap.add_argument("--path", default="prefill", choices=["prefill", "decode", "backward"],
                     help="prefill: gdn_fwd on --workload; decode: gdn_fwd_recurrent, one token per sequence "
@@ -120,6 +122,24 @@ def algorithmic_flops(x):
     return tokens * x["v"].shape[2] * (6 * d * d + 5 * C * d + C * C / 3)
 
 
+def settle(step, torch, ms):
+    """Run step(i) untimed, in batches of eight, until `ms` of wall time have passed; returns the count.
+
+    After the host has kept the GPU idle (input generation, the CPU baseline), the first tens of steps
+    run at a lower clock: on one MI355X the Qwen3-Next-shaped forward took 0.200 ms per step right
+    after 2 s of idle and 0.165 ms after 200 steps (0.170 after 300 ms of bf16 matrix products).
+    Settling with the measured step itself brings the GPU to the clock that workload sustains; the
+    W warm-up steps and the K timed steps then follow exactly as requested."""
+    n = 0
+    t0 = time.perf_counter()
+    while ms > 0 and (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(8):
+            step(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n
+
+
 def source_hash(kernel):
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[kernel]:
@@ -171,6 +191,7 @@ def bench_decode(a, torch, gdn, synth, dev):
     argv = [gdn.make_args(c["q"], c["k"], c["v"], c["g"], c["beta"], x["scale"], c["state"], None, None, 1,
                           c["o"], c["state"]) for c in copies]
     stream = torch.cuda.current_stream(dev).cuda_stream
+    n_settle = settle(lambda i: gdn.fwd_recurrent_raw(argv[i % len(argv)], stream), torch, a.settle_ms)
     for i in range(a.warmup):
         gdn.fwd_recurrent_raw(argv[i % len(argv)], stream)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
@@ -197,6 +218,7 @@ def bench_decode(a, torch, gdn, synth, dev):
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic("recurrent", f"decode_qwen3next_bf16_b{a.decode_batch}")},
         "stage_ms": {"recurrent": k_ms},
+        "clock_settle": {"ms": a.settle_ms, "untimed_steps": n_settle},
     }
     if not a.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(x, a.cpu_threads)
@@ -229,6 +251,7 @@ def bench_backward(a, torch, gdn, synth, dev):
     stream = torch.cuda.current_stream(dev).cuda_stream
     run = lambda: gdn._check(L.gdn_bwd(ctypes.byref(args), ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(nbytes),
                                        ctypes.c_void_p(stream)))
+    n_settle = settle(lambda i: run(), torch, a.settle_ms)
     for _ in range(a.warmup):
         run()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
@@ -256,6 +279,7 @@ def bench_backward(a, torch, gdn, synth, dev):
         "roofline": {"bound": "hbm", "kernel": "whole backward", "alg_bytes": alg, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None},
         "stage_ms": {"backward": ms},
+        "clock_settle": {"ms": a.settle_ms, "untimed_steps": n_settle},
     }
     if not a.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline_backward(x, do, dht)
@@ -309,7 +333,7 @@ def main():
     if a.path == "backward":
         return bench_backward(a, torch, gdn, synth, dev)
     rec, x = measure_prefill(a.workload, a.steps, a.warmup, a.copies, a.cp, a.cp_segment_chunks, torch, gdn, synth,
-                             dev)
+                             dev, a.settle_ms)
     if not a.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(x, a.cpu_threads)
     del x
@@ -330,7 +354,8 @@ def extra_configs(a, torch, gdn, synth, dev):
     out = {}
     for label, name, cp in EXTRAS:
         print(f"[bench] extra config {label}", file=sys.stderr, flush=True)
-        r, x = measure_prefill(name, a.extra_steps, a.extra_warmup, a.copies, cp, 0, torch, gdn, synth, dev)
+        r, x = measure_prefill(name, a.extra_steps, a.extra_warmup, a.copies, cp, 0, torch, gdn, synth, dev,
+                               a.settle_ms)
         del x
         torch.cuda.empty_cache()
         out[label] = {"workload": name, "cp": cp, "cp_ran": r["config"]["cp_ran"],
@@ -342,9 +367,9 @@ def extra_configs(a, torch, gdn, synth, dev):
     return out
 
 
-def measure_prefill(name, steps, warmup, n_copies, cp, cp_segment_chunks, torch, gdn, synth, dev):
-    """Time `steps` gdn_fwd_timed calls on workload `name` (after `warmup` untimed calls), rotating
-    n_copies input copies.  Returns (record without cpu_baseline, host inputs)."""
+def measure_prefill(name, steps, warmup, n_copies, cp, cp_segment_chunks, torch, gdn, synth, dev, settle_ms=0.0):
+    """Time `steps` gdn_fwd_timed calls on workload `name` (after settling the clock and `warmup`
+    untimed calls), rotating n_copies input copies.  Returns (record without cpu_baseline, host inputs)."""
     w = synth.workload(name)
     x = synth.make_inputs(w)
     esz = x["q"].element_size()
@@ -377,6 +402,7 @@ def measure_prefill(name, steps, warmup, n_copies, cp, cp_segment_chunks, torch,
             arr[j] = ev.value
         events.append(arr)
 
+    n_settle = settle(lambda i: gdn.fwd_raw(argv[i % len(argv)], ws.data_ptr(), ws.numel(), stream), torch, settle_ms)
     for i in range(warmup):
         gdn.fwd_raw(argv[i % len(argv)], ws.data_ptr(), ws.numel(), stream)
     torch.cuda.synchronize()
@@ -425,6 +451,7 @@ def measure_prefill(name, steps, warmup, n_copies, cp, cp_segment_chunks, torch,
         "stage_ms": stage_ms,
         "whole_op": {"alg_bytes": alg_bytes, "alg_flops": algorithmic_flops(x), "t_bound_ms": t_bound * 1e3,
                      "roofline_frac": t_bound / (ms_step * 1e-3)},
+        "clock_settle": {"ms": settle_ms, "untimed_steps": n_settle},
     }
     del copies, argv, ws, o, fs
     return rec, x
