@@ -794,33 +794,6 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_kda_mma_kernel(BwdParams p) 
     auto kq_at = [&](const unsigned char *t, int row) __attribute__((always_inline)) {
         return (float)*reinterpret_cast<const bf16 *>(t + KT::off(row, d * 2));
     };
-    // dq, dk through the states and their terms of dG (rows past the end read zero q and k)
-    f32x4 dq[NQT], dk[NQT], dG[NQT];
-    float dgd_sum = 0.f;
-#pragma unroll
-    for (int q = 0; q < NQT; ++q) {
-        const int tt = qt0 + q;
-        const float4 be = rows4(GB_BETA, tt);
-        const float bev[4] = {be.x, be.y, be.z, be.w};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 16 * tt + 4 * grp + r;
-            const float G = sG[t * GP + d], eg = __expf(G);
-            const float qv = kq_at(tQ, t), kv = kq_at(tK, t);
-            const float dq_o = p.scale * eg * dqS[q][r];
-            const float dk_x = -bev[r] * eg * dkX[q][r];
-            const float dk_d = __expf(gC - G) * dkD[q][r];
-            dq[q][r] = dq_o;
-            dk[q][r] = dk_x + dk_d;
-            // the last valid row's factor e^{G_C - G_C} = 1 has no gate gradient: its - (own row) and
-            // + (G_C) terms would cancel exactly, so neither is added
-            const float dgd = t >= nv - 1 ? 0.f : kv * dk_d;
-            dG[q][r] = qv * dq_o + kv * dk_x - dgd;
-            dgd_sum += dgd;
-        }
-    }
-    dgd_sum = sum_groups(dgd_sum);
-    if (grp == 0) atomicAdd(&rdgc[d], dgd_sum);
     // ---- dA transposed and scale dP transposed (strictly lower; its diagonal kept apart)
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -877,9 +850,38 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_kda_mma_kernel(BwdParams p) 
                (float)*reinterpret_cast<const f16 *>(tl + ST::off(row, col * 2));
     };
     unsigned char *tLh = tXh, *tLl = tXl;
+    // dG of the chunk, fp32 [64][DK]: columns 0..63 where A and P were, 64..127 where T was (both
+    // free now), rows of 68 floats
+    static_assert(64 * 68 * 4 <= 2 * ST::BYTES, "a 64-column half of dG fits in two 64 x 64 tiles");
+    auto dG_at = [&](int row, int col) __attribute__((always_inline)) {
+        return reinterpret_cast<float *>(col < 64 ? tA : tVh) + row * 68 + (col & 63);
+    };
+    const int hs = p.dq_v == p.dq ? hq : h, hn = p.dq_v == p.dq ? p.H_qk : p.H_v;
+    float dgd_sum = 0.f;
 #pragma unroll
     for (int q = 0; q < NQT; ++q) {
         const int R = qt0 + q;
+        const float4 be = rows4(GB_BETA, R);
+        const float bev[4] = {be.x, be.y, be.z, be.w};
+        // dq, dk through the states and their terms of dG (rows past the end read zero q and k)
+        f32x4 dq, dk, dG;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * R + 4 * grp + r;
+            const float G = sG[t * GP + d], eg = __expf(G);
+            const float qv = kq_at(tQ, t), kv = kq_at(tK, t);
+            const float dq_o = p.scale * eg * dqS[q][r];
+            const float dk_x = -bev[r] * eg * dkX[q][r];
+            const float dk_d = __expf(gC - G) * dkD[q][r];
+            dq[r] = dq_o;
+            dk[r] = dk_x + dk_d;
+            // the last valid row's factor e^{G_C - G_C} = 1 has no gate gradient: its - (own row) and
+            // + (G_C) terms would cancel exactly, so neither is added
+            const float dgd = t >= nv - 1 ? 0.f : kv * dk_d;
+            dG[r] = qv * dq_o + kv * dk_x - dgd;
+            dgd_sum += dgd;
+        }
+        // the P and L terms of block R of rows
         const float Ga = R > 0 ? sG[(16 * R - 1) * GP + d] : 0.f;    // reference rows 16 R - 1, 16 R + 15
         const float Gb = sG[(16 * R + 15) * GP + d];
         const bool whole = Ga - Gb > kMaxLn;   // the block's decay in this column: split factors would overflow fp16
@@ -923,8 +925,6 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_kda_mma_kernel(BwdParams p) 
             mma_h2(ap, as_f16(pi_row<ST>(tDh, 16 * R + l16, kb, grp)), as_f16(pi_row<ST>(tDl, 16 * R + l16, kb, grp)), qh, ql);
             mma_h2(al, as_f16(pi_row<ST>(tLh, 16 * R + l16, kb, grp)), as_f16(pi_row<ST>(tLl, 16 * R + l16, kb, grp)), kh, kl);
         }
-        const float4 be = rows4(GB_BETA, R);
-        const float bev[4] = {be.x, be.y, be.z, be.w};
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
             const int r = 16 * R + 4 * grp + rr;
@@ -944,36 +944,26 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_kda_mma_kernel(BwdParams p) 
                 }
             }
             const float kr = kq_at(tK, r), qr = kq_at(tQ, r), dpd = rdpd[r];
-            dq[q][rr] += vq + dpd * kr;
-            dk[q][rr] += vp + dpd * qr + bev[rr] * vr + vl;
-            dG[q][rr] += qr * vq + kr * bev[rr] * vr - kr * (vp + vl);
+            dq[rr] += vq + dpd * kr;
+            dk[rr] += vp + dpd * qr + bev[rr] * vr + vl;
+            dG[rr] += qr * vq + kr * bev[rr] * vr - kr * (vp + vl);
             const float db = sum16(kr * vr);
             if (l16 == 0) atomicAdd(&rdb[r], db);
+            if (r < nv) {
+                const int64_t o = ((tok0 + r) * hn + hs) * DK + d;
+                p.dq_v[o] = dq[rr];
+                p.dk_v[o] = dk[rr];
+            }
+            *dG_at(r, d) = r < nv ? dG[rr] : 0.f;
         }
         reg_fence();
     }
-    __syncthreads();   // every wave is done with G; rdb and rdgc are complete
-    // ---- dG (with the last valid row's e^{G_C} terms) into G's place, then its reverse cumsum per
-    //      channel (the notes' Step 7), dq, dk and dbeta
-#pragma unroll
-    for (int q = 0; q < NQT; ++q)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int t = 16 * (qt0 + q) + 4 * grp + rr;
-            sG[t * GP + d] = t < nv ? dG[q][rr] + (t == nv - 1 ? rdgc[d] : 0.f) : 0.f;
-        }
-    const int hs = p.dq_v == p.dq ? hq : h, hn = p.dq_v == p.dq ? p.H_qk : p.H_v;
-#pragma unroll
-    for (int q = 0; q < NQT; ++q)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int t = 16 * (qt0 + q) + 4 * grp + rr;
-            if (t < nv) {
-                const int64_t o = ((tok0 + t) * hn + hs) * DK + d;
-                p.dq_v[o] = dq[q][rr];
-                p.dk_v[o] = dk[q][rr];
-            }
-        }
+    dgd_sum = sum_groups(dgd_sum);
+    if (grp == 0) atomicAdd(&rdgc[d], dgd_sum);
+    __syncthreads();   // dG, rdb and rdgc are complete
+    // ---- the last valid row's e^{G_C} terms, then dG's reverse cumsum per channel (the notes'
+    //      Step 7) and dbeta
+    if (tid < DK && nv > 0) *dG_at(nv - 1, tid) += rdgc[tid];
     if (tid < nv) p.dbeta[(tok0 + tid) * p.H_v + h] = rdb[tid];
     __syncthreads();
     {
@@ -982,7 +972,7 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_kda_mma_kernel(BwdParams p) 
         float acc = 0.f;
 #pragma unroll
         for (int e = NR - 1; e >= 0; --e) {
-            acc += sG[(part * NR + e) * GP + dd];
+            acc += *dG_at(part * NR + e, dd);
             v[e] = acc;
         }
         rtot[part * DK + dd] = acc;
