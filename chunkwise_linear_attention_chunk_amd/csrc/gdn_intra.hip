@@ -322,14 +322,17 @@ __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
     constexpr int X_BYTES = 64 * LP * 4;
     constexpr int R0 = K_BYTES > X_BYTES ? K_BYTES : X_BYTES;
     constexpr int NKB = DK / 32;
-    // region 0: K tile, later the inverse X; region 1: A_raw.  Q stays in registers: each thread's
-    // share for the gated output, and each lane's operand rows for P.
-    __shared__ __attribute__((aligned(16))) unsigned char smem[R0 + X_BYTES];
+    // region 0: K tile, then the odd waves' P partials, then the inverse X; the G tile, then A_raw
+    // (written only after every wave is done with G).  Q stays in registers: each thread's share for
+    // the gated output, and each lane's operand rows for P.  51 KiB in all at D_k = 128 (bf16), so
+    // three workgroups share a CU.
+    __shared__ __attribute__((aligned(16))) unsigned char smem[R0];
     __shared__ __attribute__((aligned(16))) float sG[64 * GP];
     __shared__ float sB[64], sRq[64], sRk[64], sWarm[4];
+    static_assert(64 * LP <= 64 * GP, "A_raw fits where the G tile was");
     T *sK = reinterpret_cast<T *>(smem);
     float *sX = reinterpret_cast<float *>(smem);
-    float *sL = reinterpret_cast<float *>(smem + R0);
+    float *sL = sG;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, grp = lane >> 4;
     const int cg = blockIdx.x / p.H_v, h = blockIdx.x - cg * p.H_v;
@@ -342,15 +345,11 @@ __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
     const T *g = static_cast<const T *>(p.g);
     const T *beta = static_cast<const T *>(p.beta);
 
-    // this wave's lower tiles t = wave, wave + 4, wave + 8 (< 10): (I, J) with J <= I
-    const int ntiles = wave < 2 ? 3 : 2;
-    int TI[3], TJ[3];
-#pragma unroll
-    for (int n = 0; n < 3; ++n) {
-        const int t = wave + 4 * n;
-        TI[n] = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
-        TJ[n] = t - TI[n] * (TI[n] + 1) / 2;
-    }
+    // the row blocks of this wave's tiles (waves 0, 1: 3 and 0; waves 2, 3: 2 and 1) and its half of
+    // the channel blocks (the even wave of each pair the first half)
+    constexpr int HKB = NKB / 2;
+    const int half = wave & 1, kb0 = HKB * half;
+    const int RB0 = wave < 2 ? 3 : 2, RB1 = wave < 2 ? 0 : 1;
     // ---- K tile (clamped rows, tail masked at staging), Q in registers, gate columns, beta
     constexpr int VPR = DK / VEC;
     constexpr int NV = 64 * VPR / 256;
@@ -362,13 +361,14 @@ __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
         kv[i] = *reinterpret_cast<const u32x4 *>(k + off);
         qv[i] = *reinterpret_cast<const u32x4 *>(q + off);
     }
-    // Q operand rows of this lane's P tiles (row 16 I + l16, 8 columns per block)
-    Frag<T> qt[3][NKB];
+    // Q operand rows of this lane's P tiles (row 16 I + l16 of both row blocks, 8 columns per block)
+    Frag<T> qt[2][HKB];
 #pragma unroll
-    for (int n = 0; n < 3; ++n) {
-        const int row = min(16 * TI[n] + l16, last);
+    for (int b = 0; b < 2; ++b) {
+        const int row = min(16 * (b ? RB1 : RB0) + l16, last);
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) qt[n][kb] = ld8(q + ((int64_t)(t0 + row) * p.H_qk + hq) * DK + 32 * kb + 8 * grp);
+        for (int kk = 0; kk < HKB; ++kk)
+            qt[b][kk] = ld8(q + ((int64_t)(t0 + row) * p.H_qk + hq) * DK + 32 * (kb0 + kk) + 8 * grp);
     }
     // thread (d, part) scans NT consecutive tokens of channel d
     constexpr int NPART = 256 / DK, NT = 64 / NPART;
@@ -490,10 +490,15 @@ __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
     }
 
     // ---- A_raw (strict lower) and P (lower with diagonal): the 10 lower 16x16 tiles.  The operands
-    //      are rounded once to the stored type (fp16 or fp32).  P is formed transposed (keys as the
-    //      rows of the product), so each lane holds four consecutive key columns of one query row
-    //      and stores them straight from its registers; the two tiles above the diagonal that the
-    //      recurrence reads, (0, 1) and (2, 3), are written as zeros by the waves with two tiles.
+    //      are rounded once to the stored type (fp16 or fp32).  Every tile (I, J) of row block I splits
+    //      its pairwise factor at the row r = 16 I - 1 (G_r = 0 for I = 0), so the left operands
+    //      k_i 2^(G_i - G_r) and q_i 2^(G_i - G_r) (at most |x_i|) are formed once per row block and
+    //      channel block, and only the key operand k_j 2^(G_r - G_j) per tile: at most 1 below the
+    //      diagonal, at most the decay across the 17 rows r .. 16 I + 15 on it.  P is formed
+    //      transposed (keys as the rows of the product), so each lane holds four consecutive key
+    //      columns of one query row and stores them straight from its registers.  Each pair of waves
+    //      shares five tiles and splits their channel blocks; the odd wave hands its partial sums to
+    //      the even one through LDS.
     OT *P = static_cast<OT *>(p.P) + ((int64_t)ci * p.H_v + h) * 4096;
     constexpr float range_max = is_f16<OT> ? kMaxRangeF16 : kMaxRange;
     auto store_p4 = [&](int row, int col, const f32x4 &x) __attribute__((always_inline)) {
@@ -504,32 +509,62 @@ __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
             *reinterpret_cast<float4 *>(P + row * 64 + col) = make_float4(x[0], x[1], x[2], x[3]);
         }
     };
-    if (ntiles == 2) store_p4(16 * (wave == 2 ? 0 : 2) + l16, 16 * (wave == 2 ? 1 : 3) + 4 * grp, f32x4{0.f, 0.f, 0.f, 0.f});
+    // accumulator slots: 0 .. 3 tiles (RB0, J), 4 .. 5 tiles (RB1, J)
+    f32x4 aa[6], pa[6];
 #pragma unroll
-    for (int n = 0; n < 3; ++n) {
-        if (n >= ntiles) break;
-        const int I = TI[n], J = TJ[n];
-        const int r = J < I ? 16 * J + 15 : 16 * I;
-        const int i = 16 * I + l16, j = 16 * J + l16;  // operand rows of this lane
+    for (int s = 0; s < 6; ++s) aa[s] = pa[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const int I = b ? RB1 : RB0, r = 16 * I - 1;
+        const int i = 16 * I + l16;                  // this lane's left operand row
+        // the diagonal tile has no reference row between every pair's two tokens: its key factor
+        // 2^(G_r - G_j) grows across the block.  If some channel decays by more than 2^-range_max
+        // across rows r .. 16 I + 15, the split factors could leave the operand type's range, so every
+        // pair's factor 2^(G_i - G_j) <= 1 is then formed whole instead.
+        float range = 0.f;
+#pragma unroll
+        for (int d = lane; d < DK; d += 64) range = fmaxf(range, (I ? sG[r * GP + d] : 0.f) - sG[(16 * I + 15) * GP + d]);
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) range = fmaxf(range, __shfl_xor(range, off, 64));
+        const bool whole = range > range_max;
         const float qmask = i < nv ? (PRO ? sRq[i] : 1.f) : 0.f;   // with the prologue: Q row i's L2-norm factor
-        const float rki = PRO ? sRk[i] : 1.f, rkj = PRO ? sRk[j] : 1.f;
-        f32x4 aa = {0.f, 0.f, 0.f, 0.f}, pa = {0.f, 0.f, 0.f, 0.f};
-        // A tile on the diagonal has no reference row that lies between every pair's two tokens: its
-        // key factor 2^(G_r - G_j) grows across the block.  If some channel decays by more than
-        // 2^-kMaxRange across the block's 16 rows, the split factors could leave the fp32 range
-        // (inf times 0), so every pair's factor 2^(G_i - G_j) <= 1 is then formed whole instead.
-        bool whole = false;
-        if (I == J) {
-            float range = 0.f;
+        const float rki = PRO ? sRk[i] : 1.f;
 #pragma unroll
-            for (int d = lane; d < DK; d += 64) range = fmaxf(range, sG[16 * I * GP + d] - sG[(16 * I + 15) * GP + d]);
+        for (int kk = 0; kk < HKB; ++kk) {
+            const int d0 = 32 * (kb0 + kk) + 8 * grp;
+            float gr[8], kl[8], ql[8];
 #pragma unroll
-            for (int off = 1; off < 64; off <<= 1) range = fmaxf(range, __shfl_xor(range, off, 64));
-            whole = range > range_max;
+            for (int e = 0; e < 8; ++e) {
+                gr[e] = I ? sG[r * GP + d0 + e] : 0.f;
+                const float el = fast_exp2(sG[i * GP + d0 + e] - gr[e]);
+                kl[e] = to_f32(sK[i * KP + d0 + e]) * (rki * el);
+                ql[e] = to_f32(qt[b][kk].v[e]) * (qmask * el);
+            }
+            Frag<OT> fkl, fql;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                set_elem(fkl, e, from_f32<OT>(kl[e]));
+                set_elem(fql, e, from_f32<OT>(ql[e]));
+            }
+#pragma unroll
+            for (int J = 0; J < (b ? 2 : 4); ++J) {
+                if (J > I || (J == I && whole)) continue;
+                const int j = 16 * J + l16, s = b ? 4 + J : J;
+                const float rkj = PRO ? sRk[j] : 1.f;
+                Frag<OT> fkr;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    set_elem(fkr, e, from_f32<OT>(to_f32(sK[j * KP + d0 + e]) * (rkj * fast_exp2(gr[e] - sG[j * GP + d0 + e]))));
+                mma(aa[s], fkl, fkr);
+                mma(pa[s], fkr, fql);   // P^T: row 4 grp + rr of key block J, column l16 of query block I
+            }
         }
         if (whole) {
-            // A_raw: rows ii = 16 I + 4 grp + rr, column j = 16 I + l16 (the accumulator layout);
-            // P: query row i = 16 I + l16, key columns ii (the transposed layout)
+            // this wave's channels of the diagonal tile.  A_raw: rows ii = 16 I + 4 grp + rr, column
+            // j = 16 I + l16 (the accumulator layout); P: query row i, key columns ii (transposed)
+            const int j = i;
+            const float rkj = PRO ? sRk[j] : 1.f;
+            f32x4 wa, wp;
             const T *qi = q + ((int64_t)(t0 + min(i, last)) * p.H_qk + hq) * DK;
 #pragma unroll 1
             for (int rr = 0; rr < 4; ++rr) {
@@ -537,54 +572,66 @@ __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
                 float sa = 0.f, sp = 0.f;
                 if (j < ii) {
 #pragma unroll 4
-                    for (int d = 0; d < DK; ++d) {
+                    for (int d = 32 * kb0; d < 32 * (kb0 + HKB); ++d) {
                         const float e = fast_exp2(sG[ii * GP + d] - sG[j * GP + d]);   // <= 1
                         sa += to_f32(sK[ii * KP + d]) * to_f32(sK[j * KP + d]) * e;
                     }
                 }
                 if (ii <= i) {
 #pragma unroll 4
-                    for (int d = 0; d < DK; ++d) {
+                    for (int d = 32 * kb0; d < 32 * (kb0 + HKB); ++d) {
                         const float e = fast_exp2(sG[i * GP + d] - sG[ii * GP + d]);   // <= 1
                         sp += to_f32(qi[d]) * to_f32(sK[ii * KP + d]) * e;
                     }
                 }
                 const float rkii = PRO ? sRk[ii] : 1.f;
-                aa[rr] = sa * rkii * rkj;
-                pa[rr] = sp * qmask * rkii;
+                wa[rr] = sa * rkii * rkj;
+                wp[rr] = sp * qmask * rkii;
             }
+#pragma unroll
+            for (int J = 0; J < (b ? 2 : 4); ++J)   // the diagonal tile's slot, kept a compile-time index
+                if (J == I) {
+                    aa[b ? 4 + J : J] = wa;
+                    pa[b ? 4 + J : J] = wp;
+                }
         }
+    }
+    __syncthreads();   // every wave has read the K and G tiles: P partials and A_raw take their places
+    float *sPart = reinterpret_cast<float *>(smem) + (wave >> 1) * (6 * 64 * 4);
+    static_assert(2 * 6 * 64 * 4 * 4 <= R0, "the P partials of both wave pairs fit where the K tile was");
+    auto each_tile = [&](auto &&f) __attribute__((always_inline)) {
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            if (whole) break;
-            const int d0 = 32 * kb + 8 * grp;
-            float kl[8], ql[8], kr[8];
+        for (int s = 0; s < 6; ++s) {
+            const int I = s < 4 ? RB0 : RB1, J = s < 4 ? s : s - 4;
+            if (J > I) continue;
+            f(s, I, J);
+        }
+    };
+    if (half) {
+        // A partials straight into their A_raw cells, P partials lane-private; the two tiles above
+        // the diagonal that the recurrence reads, (0, 1) and (2, 3), are written as zeros
+        each_tile([&](int s, int I, int J) __attribute__((always_inline)) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float gr = sG[r * GP + d0 + e];
-                const float el = fast_exp2(sG[i * GP + d0 + e] - gr), er = fast_exp2(gr - sG[j * GP + d0 + e]);
-                kl[e] = to_f32(sK[i * KP + d0 + e]) * (rki * el);
-                ql[e] = qmask * to_f32(qt[n][kb].v[e]) * el;
-                kr[e] = to_f32(sK[j * KP + d0 + e]) * (rkj * er);
+            for (int rr = 0; rr < 4; ++rr) sL[(16 * I + 4 * grp + rr) * LP + 16 * J + l16] = aa[s][rr];
+            *reinterpret_cast<f32x4 *>(sPart + (s * 64 + lane) * 4) = pa[s];
+        });
+        store_p4(16 * (wave == 1 ? 0 : 2) + l16, 16 * (wave == 1 ? 1 : 3) + 4 * grp, f32x4{0.f, 0.f, 0.f, 0.f});
+    }
+    __syncthreads();
+    if (!half) {
+        each_tile([&](int s, int I, int J) __attribute__((always_inline)) {
+            const int i = 16 * I + l16, jj = 16 * J + l16;
+            const f32x4 pp = *reinterpret_cast<const f32x4 *>(sPart + (s * 64 + lane) * 4);
+            f32x4 pv;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int ii = 16 * I + 4 * grp + rr;
+                float *c = sL + ii * LP + jj;
+                *c = jj < ii ? sB[ii] * (aa[s][rr] + *c) : 0.f;
+                pv[rr] = 16 * J + 4 * grp + rr <= i ? p.scale * (pa[s][rr] + pp[rr]) : 0.f;
             }
-            Frag<OT> fkl, fkr, fql;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                set_elem(fkl, e, from_f32<OT>(kl[e]));
-                set_elem(fkr, e, from_f32<OT>(kr[e]));
-                set_elem(fql, e, from_f32<OT>(ql[e]));
-            }
-            mma(aa, fkl, fkr);
-            mma(pa, fkr, fql);   // P^T: row 4 grp + rr of key block J, column l16 of query block I
-        }
-        const int jj = 16 * J + l16;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int ii = 16 * I + 4 * grp + rr;
-            sL[ii * LP + jj] = jj < ii ? sB[ii] * aa[rr] : 0.f;
-            pa[rr] = 16 * J + 4 * grp + rr <= i ? p.scale * pa[rr] : 0.f;
-        }
-        store_p4(i, 16 * J + 4 * grp, pa);
+            store_p4(i, 16 * J + 4 * grp, pv);
+        });
     }
     __syncthreads();   // A_raw is complete in sL, the partial decay bounds in sWarm; the K tile is free
     if (tid == 0) gbk[GB_GC] = fast_exp2(sWarm[0] + sWarm[1] + sWarm[2] + sWarm[3]);
