@@ -219,6 +219,23 @@ void chunk_kernel(ChunkParams p) {
     // each other's loads; refilling early measured slower there.)
     constexpr bool EARLY_LD = MODE == 0 && NBUF == 1 && CH;
     constexpr int LATE_LD = CH ? (LD_KD | LD_G) : LD_G;
+    // L2 prefetch (per-channel main pass with two tile buffers, whose chunk step is otherwise bound
+    // by the latency of its tile loads): the chain waves of a head's column slices together touch
+    // every 128-byte line of chunk c + PF_DIST's tiles right after issuing chunk c + 1's loads, so
+    // the tile loads of that chunk hit L2.  Each chain wave issues exactly NPF such loads per chunk
+    // (and NPF in the prologue): its chunk-top wait then leaves the NPF newest loads in flight,
+    // which, loads returning in order, still covers every tile load issued before them.  The lines
+    // land in a sink that nothing reads.
+    constexpr bool PF = CH && MODE == 0 && NBUF == 2 && !ST;
+    constexpr int NPF = 2;
+#ifndef GDN_PF_DIST
+#define GDN_PF_DIST 2
+#endif
+    constexpr int PF_DIST = GDN_PF_DIST;
+    // the same build stores each chunk's output one step late, after the next step's tile loads are
+    // issued, so the output waves' chunk-top wait does not wait for those stores to land (with a
+    // scalar gate this measured slower: 133 -> 136 us on the Qwen3-Next shape, 523 -> 572 us varlen)
+    constexpr bool DEFER_O = PF;
 
     // Separate LDS objects for the two tile buffers and for the exchange: the chunk loop is
     // unrolled by two, so every LDS access names its buffer at compile time and the compiler can
@@ -228,6 +245,7 @@ void chunk_kernel(ChunkParams p) {
     __shared__ __attribute__((aligned(16))) unsigned char tiles1[NBUF == 2 ? L::TILES : 16];
     __shared__ __attribute__((aligned(16))) Frag<T> sSx[OUT ? L::SXN : 1];
     __shared__ __attribute__((aligned(16))) Frag<T> sVx[OUT ? L::VXN : 1];
+    __shared__ __attribute__((aligned(16))) unsigned char pf_sink[PF ? 1024 : 16];
 
     // the wave index is uniform across a wave: readfirstlane makes the role branches scalar
     const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
@@ -373,6 +391,42 @@ void chunk_kernel(ChunkParams p) {
         }
     };
 
+    // The prefetch units of a chunk: 8 KiB pieces of its Kg, Kd, Qg, P, A tiles and gate block
+    // (one 128-byte line per lane), then this slice's V rows (one row per lane).  Unit u goes to
+    // prefetch slot u of the head's n_slices * NSUB chain waves * NPF slots.
+    auto issue_pf = [&](int c2) __attribute__((always_inline)) {
+        constexpr int UB = 8192;
+        constexpr int UK = (L::KT + UB - 1) / UB, UKN = (L::NS * L::KT + UB - 1) / UB;
+        constexpr int UP = (L::NS * L::AT + UB - 1) / UB, UA = (L::AT + UB - 1) / UB;
+        const bool ok = c2 < nch;
+        const int64_t gci = si.chunk0 + cs + c2;
+        const int pid = slice * NSUB + sub, npf = p.n_slices * NSUB;
+#pragma unroll
+        for (int q = 0; q < NPF; ++q) {
+            const int u = pid + npf * q;
+            const void *base;
+            int bytes, soff, voff = lane * 128;
+            if (u < UK) {
+                base = kgb + gci * p.H_v * 64 * DK; bytes = L::KT; soff = u * UB;
+            } else if (u < UK + UKN) {
+                base = kdb + gci * p.H_v * L::NS * 64 * DK; bytes = L::NS * L::KT; soff = (u - UK) * UB;
+            } else if (u < UK + 2 * UKN) {
+                base = qgb + gci * p.H_v * L::NS * 64 * DK; bytes = L::NS * L::KT; soff = (u - UK - UKN) * UB;
+            } else if (u < UK + 2 * UKN + UP) {
+                base = Pb + gci * p.H_v * L::NS * 4096; bytes = L::NS * L::AT; soff = (u - UK - 2 * UKN) * UB;
+            } else if (u < UK + 2 * UKN + UP + UA) {
+                base = Ab + gci * p.H_v * 4096; bytes = L::AT; soff = (u - UK - 2 * UKN - UP) * UB;
+            } else if (u == UK + 2 * UKN + UP + UA) {
+                base = Gb + gci * p.H_v * GB_FLOATS; bytes = GB_FLOATS * 4; soff = 0;
+            } else {
+                const int64_t tok = si.tok0 + (int64_t)(cs + c2) * kChunk;
+                base = vb + tok * v_stride; soff = 0; voff = lane * vs * ESZ;
+                bytes = ok ? ((nvalid(c2) - 1) * vs + BV) * ESZ : 0;
+            }
+            buffer_granule_to_lds(make_rsrc(base, ok ? bytes : 0), pf_sink, voff, soff);
+        }
+    };
+
     // ---- chain state: S [DK][16] of this slice in fp32 accumulator tiles (rows 16m + 4grp + r)
     //      main pass: h0 (first segment) or the fixed-up start state; pre-process: 0 or identity.
     //      Set up by the chain waves only (below).
@@ -402,7 +456,7 @@ void chunk_kernel(ChunkParams p) {
     //      and the barrier makes the tiles, the gate block and S_c visible to every wave.  Both roles
     //      below pass the same barriers in the same order.  (Waiting for the loads only, with the
     //      output stores issued after them left in flight, measured no faster.)
-    auto chunk_top = [&]<bool LD>(int c) __attribute__((always_inline)) {
+    auto chunk_top = [&]<bool LD, int VM = 0>(int c) __attribute__((always_inline)) {
         if constexpr (NBUF == 1) {
             if (c > 0) {
                 __syncthreads();
@@ -413,7 +467,8 @@ void chunk_kernel(ChunkParams p) {
                 }
             }
         }
-        if constexpr (LD) __builtin_amdgcn_s_waitcnt(0x0f70);
+        static_assert(VM >= 0 && VM < 16, "vmcnt immediate");
+        if constexpr (LD) __builtin_amdgcn_s_waitcnt(0x0f70 | VM);
         __syncthreads();
     };
 
@@ -437,11 +492,38 @@ void chunk_kernel(ChunkParams p) {
             auto pb_tile = [&](int b) { return NSUB == 1 ? (b < 4 ? b : b - 2) : (b == 0 ? 0 : 1); };
             auto pb_kb = [&](int b) { return NSUB == 1 ? (b < 4 ? 0 : 1) : (b == 2 ? 1 : 0); };
             // (NSUB == 2: blocks (tile 0, kb 0), (tile 1, kb 0), (tile 1, kb 1); tile 1 is m = 3 or 2)
+            // the output of a chunk: buffer stores straight from the accumulators (copied to o_prev,
+            // register renames); lane (grp, l16) of tile (i, g) holds
+            // O[16 mt[i] + l16][16 g + 4 grp + r], r = 0..3.  The resource covers the chunk's valid
+            // rows only (rows past the end are dropped by the bounds check).
+            f32x4 o_prev[NR][NSUB];
+            auto store_o = [&](int c) __attribute__((always_inline)) {
+                if (c < wup) return;                       // warmup chunk: no output
+                const int nv = nvalid(c);
+                const int64_t ebase = (int64_t)(si.tok0 + (cs + c) * kChunk) * v_stride + (int64_t)h * DV + c0;
+                const int oes = p.o_f32 ? 4 : ESZ;
+                const __amdgpu_buffer_rsrc_t ors = make_rsrc(static_cast<char *>(p.o) + ebase * oes,
+                                                             p.o ? ((nv - 1) * vs + BV) * oes : 0);
+#pragma unroll
+                for (int i = 0; i < NR; ++i)
+#pragma unroll
+                    for (int g = 0; g < NSUB; ++g) {
+                        const int off = (16 * mt[i] + l16) * vs + 16 * g + 4 * grp;   // elements
+                        const f32x4 &x = o_prev[i][g];
+                        if (ESZ == 2 && !p.o_f32) {
+                            const bf16x4 b = {(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+                            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, b), ors, off * 2, 0, 0);
+                        } else {
+                            const u32x4 w = {__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
+                                             __float_as_uint(x[3])};
+                            __builtin_amdgcn_raw_buffer_store_b128(w, ors, off * 4, 0, 0);
+                        }
+                    }
+            };
             auto out_step = [&]<int B>(int c) __attribute__((always_inline)) {
                 unsigned char *tcur = B == 0 ? tiles0 : tiles1;
                 unsigned char *tnext = B == 0 ? tiles1 : tiles0;
                 chunk_top.template operator()<true>(c);
-                const int nv = nvalid(c);
                 const float *g3 = reinterpret_cast<const float *>(tcur + L::G0);
                 const bool more = NBUF == 2 && c + 1 < nch;               // stream chunk c + 1 meanwhile
                 const unsigned char *tQ = tcur + L::Q0, *tK = tcur + L::K0, *tQl = tcur + L::QL0;
@@ -450,6 +532,9 @@ void chunk_kernel(ChunkParams p) {
                 if (more) {                                       // the output waves' share, at once
                     issue_kq(c + 1, tnext, 0, 1, ST ? OUT_LD & ~LD_Q : OUT_LD);
                     issue_apvg(c + 1, tnext, 0, 1, OUT_LD);
+                }
+                if constexpr (DEFER_O) {
+                    if (c > 0) store_o(c - 1);
                 }
                 if constexpr (ST) {   // states only: the loads and the chain's barriers, no output
                     lds_only_barrier();
@@ -563,29 +648,11 @@ void chunk_kernel(ChunkParams p) {
 #pragma unroll
                     for (int b = 0; b < NPB; ++b) mma_xx(o[pb_tile(b)][g], Vh[pb_kb(b)], Vl[pb_kb(b)], ph[b], pl[b]);
                 }
-                // buffer stores straight from the accumulators: lane (grp, l16) of tile (i, g) holds
-                // O[16 mt[i] + l16][16 g + 4 grp + r], r = 0..3.  The resource covers the chunk's valid
-                // rows only (rows past the end are dropped by the bounds check).
-                if (c < wup) return;                       // warmup chunk: no output
-                const int64_t ebase = (int64_t)(si.tok0 + (cs + c) * kChunk) * v_stride + (int64_t)h * DV + c0;
-                const int oes = p.o_f32 ? 4 : ESZ;
-                const __amdgpu_buffer_rsrc_t ors = make_rsrc(static_cast<char *>(p.o) + ebase * oes,
-                                                             p.o ? ((nv - 1) * vs + BV) * oes : 0);
 #pragma unroll
                 for (int i = 0; i < NR; ++i)
 #pragma unroll
-                    for (int g = 0; g < NSUB; ++g) {
-                        const int off = (16 * mt[i] + l16) * vs + 16 * g + 4 * grp;   // elements
-                        const f32x4 &x = o[i][g];
-                        if (ESZ == 2 && !p.o_f32) {
-                            const bf16x4 b = {(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
-                            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, b), ors, off * 2, 0, 0);
-                        } else {
-                            const u32x4 w = {__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
-                                             __float_as_uint(x[3])};
-                            __builtin_amdgcn_raw_buffer_store_b128(w, ors, off * 4, 0, 0);
-                        }
-                    }
+                    for (int g = 0; g < NSUB; ++g) o_prev[i][g] = o[i][g];
+                if constexpr (!DEFER_O) store_o(c);
             };
             if (nch > 0) {
                 issue_kq(0, tiles0, 0, 1, LD_ALL);
@@ -594,6 +661,9 @@ void chunk_kernel(ChunkParams p) {
             for (int c = 0; c < nch; c += 2) {
                 out_step.template operator()<0>(c);
                 if (c + 1 < nch) out_step.template operator()<NBUF == 2 ? 1 : 0>(c + 1);
+            }
+            if constexpr (DEFER_O) {
+                if (nch > 0) store_o(nch - 1);
             }
             return;
         }
@@ -618,7 +688,7 @@ void chunk_kernel(ChunkParams p) {
     auto chain_step = [&]<int B>(int c) __attribute__((always_inline)) {
         unsigned char *tcur = B == 0 ? tiles0 : tiles1;
         unsigned char *tnext = B == 0 ? tiles1 : tiles0;
-        chunk_top.template operator()<!OUT || CHAIN_LD>(c);
+        chunk_top.template operator()<!OUT || CHAIN_LD, PF ? NPF : 0>(c);
         if constexpr (OUT && ST) {
             {   // the state entering this chunk (no CP: segment = sequence)
                 float *st = p.chunk_states + ((int64_t)(si.chunk0 + cs + c) * p.H_v + h) * DK * DV;
@@ -727,6 +797,7 @@ void chunk_kernel(ChunkParams p) {
                 issue_kq(c + 1, tnext, 0, 1, LD_K | LD_KD);
                 issue_apvg(c + 1, tnext, 0, 1, LD_A);
             }
+            if constexpr (PF) issue_pf(c + PF_DIST);
         }
         if constexpr (OUT) lds_only_barrier();  // V' of chunk c is visible to the output waves
         // =========================== phase 2 ===========================
@@ -764,12 +835,17 @@ void chunk_kernel(ChunkParams p) {
             issue_kq(0, tiles0, 0, 1, LD_ALL);
             issue_apvg(0, tiles0, 0, 1, LD_ALL);
         }
+        if constexpr (PF) {
+#pragma unroll
+            for (int c2 = 1; c2 < PF_DIST; ++c2) issue_pf(c2);
+        }
         split_state();
     }
     for (int c = 0; c < nch; c += 2) {
         chain_step.template operator()<0>(c);
         if (c + 1 < nch) chain_step.template operator()<NBUF == 2 ? 1 : 0>(c + 1);
     }
+    if constexpr (PF) __builtin_amdgcn_s_waitcnt(0x0f70);   // no prefetch into the sink outlives the workgroup
 
     // ---- end of the segment: final state (main pass, last segment) or the segment's maps
     float *s_end = nullptr;
