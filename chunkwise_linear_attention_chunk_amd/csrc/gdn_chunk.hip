@@ -236,6 +236,13 @@ void chunk_kernel(ChunkParams p) {
     // issued, so the output waves' chunk-top wait does not wait for those stores to land (with a
     // scalar gate this measured slower: 133 -> 136 us on the Qwen3-Next shape, 523 -> 572 us varlen)
     constexpr bool DEFER_O = PF;
+    // the scalar-gate main pass with two tile buffers: the output waves hand each chunk's output
+    // to the chain waves through LDS, which store it early in the next chunk (their stores overlap
+    // the first products).  The output waves then issue no stores, so their chunk-top wait for the
+    // next tiles (a vmcnt wait, which counts stores too) no longer waits for output stores to land,
+    // and the chain waves' stores have a whole chunk to land before theirs.
+    constexpr bool SW = MODE == 0 && NBUF == 2 && !ST && !CH;
+    constexpr int NRT = 4 / NSUB;                  // token tiles of each output wave
 
     // Separate LDS objects for the two tile buffers and for the exchange: the chunk loop is
     // unrolled by two, so every LDS access names its buffer at compile time and the compiler can
@@ -246,6 +253,8 @@ void chunk_kernel(ChunkParams p) {
     __shared__ __attribute__((aligned(16))) Frag<T> sSx[OUT ? L::SXN : 1];
     __shared__ __attribute__((aligned(16))) Frag<T> sVx[OUT ? L::VXN : 1];
     __shared__ __attribute__((aligned(16))) unsigned char pf_sink[PF ? 1024 : 16];
+    // outputs handed to the chain waves: [chunk parity][output wave][tile (i, g)][lane], fp32
+    __shared__ __attribute__((aligned(16))) f32x4 sO[SW ? 2 * NSUB * NRT * NSUB * 64 : 1];
 
     // the wave index is uniform across a wave: readfirstlane makes the role branches scalar
     const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
@@ -469,7 +478,10 @@ void chunk_kernel(ChunkParams p) {
         }
         static_assert(VM >= 0 && VM < 16, "vmcnt immediate");
         if constexpr (LD) __builtin_amdgcn_s_waitcnt(0x0f70 | VM);
-        __syncthreads();
+        // (a workgroup barrier with its fence would wait for every memory operation in flight,
+        // vmcnt(0): the prefetches and the chain waves' output stores; each wave's tile loads are covered
+        // by its own wait above, and no wave reads global memory another wave writes here)
+        lds_only_barrier();
     };
 
     // ---- output role (main pass): streams the tiles of the next chunk into LDS and forms
@@ -481,44 +493,50 @@ void chunk_kernel(ChunkParams p) {
     //      the same with their roles swapped, and a lane then holds four consecutive value columns
     //      of one token, which it stores straight from registers (one 8-byte bf16 or 16-byte fp32
     //      store per 16 x 16 tile).
+    // the output tile i of output wave s: token tile; wave 0 owns tiles 0 and 3, wave 1 tiles 1 and
+    // 2 (which balances the causal P work); a single output wave owns all four
+    auto out_tile = [](int s, int i) { return NSUB == 1 ? i : (i == 0 ? (s ? 1 : 0) : (s ? 2 : 3)); };
+    // chunk c's output from registers or LDS: lane (grp, l16) of tile (i, g) of output wave s holds
+    // O[16 out_tile(s, i) + l16][16 g + 4 grp + r], r = 0..3.  The resource covers the chunk's valid
+    // rows only (rows past the end are dropped by the bounds check).
+    auto store_tiles = [&](int c, int s, auto &&tile) __attribute__((always_inline)) {
+        const int nv = nvalid(c);
+        const int64_t ebase = (int64_t)(si.tok0 + (cs + c) * kChunk) * v_stride + (int64_t)h * DV + c0;
+        const int oes = p.o_f32 ? 4 : ESZ;
+        const __amdgpu_buffer_rsrc_t ors = make_rsrc(static_cast<char *>(p.o) + ebase * oes,
+                                                     p.o ? ((nv - 1) * vs + BV) * oes : 0);
+#pragma unroll
+        for (int i = 0; i < NRT; ++i)
+#pragma unroll
+            for (int g = 0; g < NSUB; ++g) {
+                const int off = (16 * out_tile(s, i) + l16) * vs + 16 * g + 4 * grp;   // elements
+                const f32x4 x = tile(i, g);
+                if (ESZ == 2 && !p.o_f32) {
+                    const bf16x4 b = {(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, b), ors, off * 2, 0, 0);
+                } else {
+                    const u32x4 w = {__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
+                                     __float_as_uint(x[3])};
+                    __builtin_amdgcn_raw_buffer_store_b128(w, ors, off * 4, 0, 0);
+                }
+            }
+    };
     if constexpr (OUT) {
         if (!chain) {
-            constexpr int NR = 4 / NSUB;                  // token tiles of this wave
+            constexpr int NR = NRT;                       // token tiles of this wave
             int mt[NR];
 #pragma unroll
-            for (int i = 0; i < NR; ++i) mt[i] = NSUB == 1 ? i : (i == 0 ? (sub ? 1 : 0) : (sub ? 2 : 3));
+            for (int i = 0; i < NR; ++i) mt[i] = out_tile(sub, i);
             // the causal blocks of P V': (token tile i, contraction block kb <= m / 2)
             constexpr int NPB = NSUB == 1 ? 6 : 3;
             auto pb_tile = [&](int b) { return NSUB == 1 ? (b < 4 ? b : b - 2) : (b == 0 ? 0 : 1); };
             auto pb_kb = [&](int b) { return NSUB == 1 ? (b < 4 ? 0 : 1) : (b == 2 ? 1 : 0); };
             // (NSUB == 2: blocks (tile 0, kb 0), (tile 1, kb 0), (tile 1, kb 1); tile 1 is m = 3 or 2)
-            // the output of a chunk: buffer stores straight from the accumulators (copied to o_prev,
-            // register renames); lane (grp, l16) of tile (i, g) holds
-            // O[16 mt[i] + l16][16 g + 4 grp + r], r = 0..3.  The resource covers the chunk's valid
-            // rows only (rows past the end are dropped by the bounds check).
+            // the output of a chunk straight from the accumulators (copied to o_prev: register renames)
             f32x4 o_prev[NR][NSUB];
             auto store_o = [&](int c) __attribute__((always_inline)) {
                 if (c < wup) return;                       // warmup chunk: no output
-                const int nv = nvalid(c);
-                const int64_t ebase = (int64_t)(si.tok0 + (cs + c) * kChunk) * v_stride + (int64_t)h * DV + c0;
-                const int oes = p.o_f32 ? 4 : ESZ;
-                const __amdgpu_buffer_rsrc_t ors = make_rsrc(static_cast<char *>(p.o) + ebase * oes,
-                                                             p.o ? ((nv - 1) * vs + BV) * oes : 0);
-#pragma unroll
-                for (int i = 0; i < NR; ++i)
-#pragma unroll
-                    for (int g = 0; g < NSUB; ++g) {
-                        const int off = (16 * mt[i] + l16) * vs + 16 * g + 4 * grp;   // elements
-                        const f32x4 &x = o_prev[i][g];
-                        if (ESZ == 2 && !p.o_f32) {
-                            const bf16x4 b = {(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
-                            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, b), ors, off * 2, 0, 0);
-                        } else {
-                            const u32x4 w = {__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
-                                             __float_as_uint(x[3])};
-                            __builtin_amdgcn_raw_buffer_store_b128(w, ors, off * 4, 0, 0);
-                        }
-                    }
+                store_tiles(c, sub, [&](int i, int g) { return o_prev[i][g]; });
             };
             auto out_step = [&]<int B>(int c) __attribute__((always_inline)) {
                 unsigned char *tcur = B == 0 ? tiles0 : tiles1;
@@ -648,11 +666,26 @@ void chunk_kernel(ChunkParams p) {
 #pragma unroll
                     for (int b = 0; b < NPB; ++b) mma_xx(o[pb_tile(b)][g], Vh[pb_kb(b)], Vl[pb_kb(b)], ph[b], pl[b]);
                 }
+                if constexpr (!SW) {
 #pragma unroll
-                for (int i = 0; i < NR; ++i)
+                    for (int i = 0; i < NR; ++i)
 #pragma unroll
-                    for (int g = 0; g < NSUB; ++g) o_prev[i][g] = o[i][g];
-                if constexpr (!DEFER_O) store_o(c);
+                        for (int g = 0; g < NSUB; ++g) o_prev[i][g] = o[i][g];
+                }
+                if constexpr (SW) {
+                    if (c < wup) {
+                    } else if (c + 1 == nch) {             // the last chunk: no next chunk stores it
+                        store_tiles(c, sub, [&](int i, int g) { return o[i][g]; });
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < NR; ++i)
+#pragma unroll
+                            for (int g = 0; g < NSUB; ++g)
+                                sO[(((c & 1) * NSUB + sub) * NR * NSUB + i * NSUB + g) * 64 + lane] = o[i][g];
+                    }
+                } else if constexpr (!DEFER_O) {
+                    store_o(c);
+                }
             };
             if (nch > 0) {
                 issue_kq(0, tiles0, 0, 1, LD_ALL);
@@ -700,6 +733,12 @@ void chunk_kernel(ChunkParams p) {
         }
         const float *g3 = reinterpret_cast<const float *>(tcur + L::G0);
         const bool more = NBUF == 2 && c + 1 < nch;
+        if constexpr (SW) {   // chain wave s stores output wave s's tiles of chunk c - 1
+            if (c > 0 && c - 1 >= wup)
+                store_tiles(c - 1, sub, [&](int i, int g) {
+                    return sO[((((c - 1) & 1) * NSUB + sub) * NRT * NSUB + i * NSUB + g) * 64 + lane];
+                });
+        }
         if constexpr (!OUT) {
             if (more) {
                 issue_kq(c + 1, tnext, 0, 1, LD_ALL);
