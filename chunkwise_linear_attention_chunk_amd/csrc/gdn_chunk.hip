@@ -237,10 +237,10 @@ void chunk_kernel(ChunkParams p) {
     // scalar gate this measured slower: 133 -> 136 us on the Qwen3-Next shape, 523 -> 572 us varlen)
     constexpr bool DEFER_O = PF;
     // the scalar-gate main pass with two tile buffers: the output waves hand each chunk's output
-    // to the chain waves through LDS, which store it early in the next chunk (their stores overlap
-    // the first products).  The output waves then issue no stores, so their chunk-top wait for the
-    // next tiles (a vmcnt wait, which counts stores too) no longer waits for output stores to land,
-    // and the chain waves' stores have a whole chunk to land before theirs.
+    // to the chain waves through LDS, which store it in the next chunk.  The output waves then
+    // issue no stores, so their chunk-top wait for the next tiles (a vmcnt wait, which counts
+    // stores too) no longer waits for output stores to land (133.8 -> 128.8 us on the Qwen3-Next
+    // shape); the chain waves' stores have phase 2 to land before their own chunk-top wait.
     constexpr bool SW = MODE == 0 && NBUF == 2 && !ST && !CH;
     constexpr int NRT = 4 / NSUB;                  // token tiles of each output wave
 
@@ -733,12 +733,6 @@ void chunk_kernel(ChunkParams p) {
         }
         const float *g3 = reinterpret_cast<const float *>(tcur + L::G0);
         const bool more = NBUF == 2 && c + 1 < nch;
-        if constexpr (SW) {   // chain wave s stores output wave s's tiles of chunk c - 1
-            if (c > 0 && c - 1 >= wup)
-                store_tiles(c - 1, sub, [&](int i, int g) {
-                    return sO[((((c - 1) & 1) * NSUB + sub) * NRT * NSUB + i * NSUB + g) * 64 + lane];
-                });
-        }
         if constexpr (!OUT) {
             if (more) {
                 issue_kq(c + 1, tnext, 0, 1, LD_ALL);
@@ -837,6 +831,14 @@ void chunk_kernel(ChunkParams p) {
                 issue_apvg(c + 1, tnext, 0, 1, LD_A);
             }
             if constexpr (PF) issue_pf(c + PF_DIST);
+        }
+        if constexpr (SW) {
+            // chain wave s stores output wave s's tiles of chunk c - 1 here, where it would wait for
+            // the output waves at the barrier anyway (at the chunk's start: 1.5 % slower)
+            if (c > 0 && c - 1 >= wup)
+                store_tiles(c - 1, sub, [&](int i, int g) {
+                    return sO[((((c - 1) & 1) * NSUB + sub) * NRT * NSUB + i * NSUB + g) * 64 + lane];
+                });
         }
         if constexpr (OUT) lds_only_barrier();  // V' of chunk c is visible to the output waves
         // =========================== phase 2 ===========================
