@@ -170,6 +170,80 @@ __global__ __launch_bounds__(kBwT) void bwd_p_kernel(BwdParams p) {
     }
 }
 
+// ---- the same scale Pt for bf16 inputs on the matrix cores (the bf16 pair [2][64][64]): 256
+//      threads, wave w forms the lower 16x16 tiles w, w + 4, w + 8 (< 10) of
+//      P_ij = scale e^{gl_i - gl_j} (Q K^T)_ij (j <= i, zero past the chunk's end) from Q and K
+//      fragments read straight from memory (exact bf16 products, fp32 sums), transposed -- keys as
+//      the rows of the product, so a lane holds four consecutive key columns of one query row and
+//      stores them with one 8-byte store per part -- and writes the upper tiles w, w + 4 (< 6) as
+//      zeros.  (bwd_p_kernel's LDS dot products took 237 us per step on the Qwen3-Next shape.)
+template <int DK>
+__global__ __launch_bounds__(256) void bwd_p_mma_kernel(BwdParams p) {
+    constexpr int NKB = DK / 32;
+    __shared__ float sgl[64], sb[64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, grp = lane >> 4;
+    const int ci = blockIdx.x / p.H_v, h = blockIdx.x - ci * p.H_v;
+    const int hq = h / (p.H_v / p.H_qk);
+    const ChunkInfo cinfo = chunk_info(p.chunks, ci, p.T);
+    const int nv = cinfo.nv, last = max(nv - 1, 0);
+    const int64_t qks = (int64_t)p.H_qk * DK;
+    const bf16 *qb = static_cast<const bf16 *>(p.q) + cinfo.tok0 * qks + (int64_t)hq * DK;
+    const bf16 *kb_ = static_cast<const bf16 *>(p.k) + cinfo.tok0 * qks + (int64_t)hq * DK;
+    if (wave == 0) load_gates<bf16>(p, cinfo.tok0, nv, h, sgl, sb);
+    int TI[3], TJ[3];
+#pragma unroll
+    for (int n = 0; n < 3; ++n) {
+        const int t = wave + 4 * n;
+        TI[n] = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
+        TJ[n] = t - TI[n] * (TI[n] + 1) / 2;
+    }
+    const int ntiles = wave < 2 ? 3 : 2;
+    f32x4 acc[3];
+#pragma unroll
+    for (int n = 0; n < 3; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int n = 0; n < 3; ++n) {
+            if (n >= ntiles) break;
+            const Frag<bf16> kf = ld8(kb_ + min(16 * TJ[n] + l16, last) * qks + 32 * kb + 8 * grp);
+            const Frag<bf16> qf = ld8(qb + min(16 * TI[n] + l16, last) * qks + 32 * kb + 8 * grp);
+            mma(acc[n], kf, qf);   // [key 16 TJ + 4 grp + r][query 16 TI + l16]
+        }
+    __syncthreads();   // the gate cumsum
+    bf16 *Pb = reinterpret_cast<bf16 *>(p.pmat + ((int64_t)ci * p.H_v + h) * 4096);
+    auto put = [&](int i, int j0, const float *x) __attribute__((always_inline)) {
+        bf16x4 hi, lo;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            hi[r] = (bf16)x[r];
+            lo[r] = (bf16)(x[r] - (float)hi[r]);
+        }
+        *reinterpret_cast<bf16x4 *>(Pb + i * 64 + j0) = hi;
+        *reinterpret_cast<bf16x4 *>(Pb + 4096 + i * 64 + j0) = lo;
+    };
+#pragma unroll
+    for (int n = 0; n < 3; ++n) {
+        if (n >= ntiles) break;
+        const int i = 16 * TI[n] + l16, j0 = 16 * TJ[n] + 4 * grp;
+        float x[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int j = j0 + r;
+            x[r] = j <= i && i < nv ? p.scale * __expf(sgl[i] - sgl[j]) * acc[n][r] : 0.f;
+        }
+        put(i, j0, x);
+    }
+    const float zero[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        const int u = wave + 4 * m;                       // upper tiles (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
+        if (u >= 6) break;
+        const int I = u < 3 ? 0 : u < 5 ? 1 : 2, J = u < 3 ? u + 1 : u < 5 ? u - 1 : 3;
+        put(16 * I + l16, 16 * J + 4 * grp, zero);
+    }
+}
+
 // ---- reverse scan of the state gradient: dS_next of every chunk, and dh0 (kBwT threads: two
 //      waves per SIMD hide the LDS latency of the products)
 template <typename T, int DK>
@@ -285,7 +359,8 @@ __global__ __launch_bounds__(128, 1) void bwd_dstate_mma_kernel(BwdParams p) {
     const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ncb = p.D_v / L::WC;
-    const int cb = blockIdx.x % ncb, nh = blockIdx.x / ncb, h = nh % p.H_v, n = nh / p.H_v;
+    const int xcd = blockIdx.x & 7, rr = blockIdx.x >> 3;   // XCD-aware, see scan_grid
+    const int cb = rr % ncb, nh = (rr / ncb) * 8 + xcd, h = nh % p.H_v, n = nh / p.H_v;
     if (n >= p.N) return;
     const int hq = h / (p.H_v / p.H_qk);
     const SeqInfo si = seq_info(p.seq, n, p.T);
@@ -535,7 +610,8 @@ __global__ __launch_bounds__(128, 1) void bwd_dstate_kda_mma_kernel(BwdParams p)
     const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ncb = p.D_v / L::WC;
-    const int cb = blockIdx.x % ncb, nh = blockIdx.x / ncb, h = nh % p.H_v, n = nh / p.H_v;
+    const int xcd = blockIdx.x & 7, rr = blockIdx.x >> 3;   // XCD-aware, see scan_grid
+    const int cb = rr % ncb, nh = (rr / ncb) * 8 + xcd, h = nh % p.H_v, n = nh / p.H_v;
     if (n >= p.N) return;
     const SeqInfo si = seq_info(p.seq, n, p.T);
     const int DV = p.D_v, vs = p.H_v * DV;
@@ -1580,10 +1656,19 @@ __global__ __launch_bounds__(256) void bwd_group_sum_kernel(BwdParams p, int DK,
 
 }  // namespace
 
+// Grid of the matrix-core dS scans, one workgroup per (sequence, head, 32 value columns), mapped so
+// that the column blocks of one (sequence, head) share blockIdx % 8, i.e. one XCD and its L2: the
+// K, A, P and gate tiles one block fetches are then L2 hits for the others (with consecutive
+// blocks on different XCDs the per-channel scan read 4.97 GB per step on the KDA shape, four
+// copies of its tiles).
+static int64_t scan_grid(const BwdParams &p) {
+    return ((int64_t)p.N * p.H_v + 7) / 8 * 8 * (p.D_v / 32);
+}
+
 hipError_t launch_bwd(int dtype, int D_k, const BwdParams &p, hipStream_t s) {
     if (p.channel) {
         const int64_t scans = (int64_t)p.N * p.H_v * (p.D_v / kBw), chunks = (int64_t)p.n_chunks * p.H_v;
-        const int64_t replays = (int64_t)p.N * p.H_v * (p.D_v / kBwR), mscans = (int64_t)p.N * p.H_v * (p.D_v / 32);
+        const int64_t replays = (int64_t)p.N * p.H_v * (p.D_v / kBwR), mscans = scan_grid(p);
         if (scans == 0) return hipSuccess;
 // every kernel of the backward runs kBwT threads per workgroup
 #define GDN_BWDK(K, T, DK, grid) hipLaunchKernelGGL((K<T, DK>), dim3((unsigned)(grid)), dim3(kBwT), 0, s, p)
@@ -1618,13 +1703,16 @@ hipError_t launch_bwd(int dtype, int D_k, const BwdParams &p, hipStream_t s) {
         return hipGetLastError();
     }
     const int64_t scans = (int64_t)p.N * p.H_v * (p.D_v / kBwR), rscans = (int64_t)p.N * p.H_v * (p.D_v / kBwD);
-    const int64_t mscans = (int64_t)p.N * p.H_v * (p.D_v / 32);
+    const int64_t mscans = scan_grid(p);
     const int64_t chunks = (int64_t)p.n_chunks * p.H_v;
     if (scans == 0) return hipSuccess;
 #define GDN_BWD(K, T, DK, grid) hipLaunchKernelGGL((K<T, DK>), dim3((unsigned)(grid)), dim3(kBwT), 0, s, p)
 #define GDN_BWD_ALL(T, DK)                                                                                 \
     if (!p.replayed) GDN_BWD(bwd_states_kernel, T, DK, scans);                                             \
-    if (chunks) GDN_BWD(bwd_p_kernel, T, DK, chunks);                                                      \
+    if (chunks) {                                                                                          \
+        if (sizeof(T) == 2) hipLaunchKernelGGL((bwd_p_mma_kernel<DK>), dim3((unsigned)chunks), dim3(256), 0, s, p); \
+        else GDN_BWD(bwd_p_kernel, T, DK, chunks);                                                         \
+    }                                                                                                      \
     if (sizeof(T) == 2)                                                                                    \
         hipLaunchKernelGGL((bwd_dstate_mma_kernel<DK>), dim3((unsigned)mscans), dim3(128), 0, s, p);      \
     else                                                                                                   \
