@@ -231,9 +231,11 @@ def test_fp32_key_and_value_dims_differ():
     check(x, TOL["fp32"], label="fp32 D_k=128 D_v=64")
 
 
-def test_kda_key_and_value_dims_differ():
-    x = _dims(_w("kda_bf16", B=1, H=2, T=400, h0=True, seed=220), 64, 128)
-    check(x, TOL["bf16"], label="KDA bf16 D_k=64 D_v=128")
+@pytest.mark.parametrize("dk,dv", [(64, 128), (128, 64)])
+def test_kda_key_and_value_dims_differ(dk, dv):
+    # (128, 64): two column slices per head, fewer L2-prefetch slots than prefetch units
+    x = _dims(_w("kda_bf16", B=1, H=2, T=400, h0=True, seed=220 + dv), dk, dv)
+    check(x, TOL["bf16"], label=f"KDA bf16 D_k={dk} D_v={dv}")
 
 
 def test_empty_sequence_returns_initial_state():
@@ -241,6 +243,19 @@ def test_empty_sequence_returns_initial_state():
     o, fs = gpu_run(x)
     assert o.numel() == 0
     assert torch.equal(fs, x["h0"])
+
+
+# --------------------------------------------------------------------------- 16-column workgroups
+# GDN_BV=16 selects the recurrence build with one chain and one output wave per workgroup (16 value
+# columns), whose single output wave owns all four token tiles and hands them to its chain wave.
+@pytest.mark.parametrize("dk", [64, 128])
+def test_sixteen_column_workgroups_bf16(dk, monkeypatch):
+    monkeypatch.setenv("GDN_BV", "16")
+    x = _w("qwen3next_bf16", B=2, H=2, D=dk, T=64 * 9 + 21, h0=True, seed=740 + dk)
+    check(x, TOL["bf16"], label=f"BV=16 bf16 D={dk}", cp_mode="off")
+    # with warmup CP: the early chunks of a segment produce no output
+    x = _w("qwen3next_bf16", B=1, H=1, D=dk, T=64 * 40 + 5, seed=750 + dk)
+    check(x, TOL["bf16"], label=f"BV=16 bf16 D={dk} warmup CP", cp_mode="warmup", cp_segment_chunks=8)
 
 
 # --------------------------------------------------------------------------- pieces
