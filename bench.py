@@ -363,8 +363,25 @@ def extra_configs(a, torch, gdn, synth, dev):
                       "tokens_per_s": r["value"], "dtype": r["dtype"],
                       "whole_op_roofline_frac": r["whole_op"]["roofline_frac"],
                       "dominant_kernel": r["roofline"]["kernel"], "dominant_kernel_frac": r["roofline"]["frac"],
-                      "stage_ms": r["stage_ms"]}
+                      "stage_ms": r["stage_ms"], "serial_chain": r["serial_chain"]}
     return out
+
+
+def serial_chain(x, plan, chunk_ms):
+    """The recurrence's serial chain: chunks per chain (a CP segment, else the longest sequence), the
+    chunk step (recurrence time / chunks per chain: the time per chunk when every chain runs at once,
+    an upper bound when the workgroups run in several rounds, as with many packed sequences), and the
+    floor a chain over the longest sequence would take at that step without CP."""
+    if x["cu_seqlens"] is not None:
+        cu = x["cu_seqlens"].tolist()
+        longest = max((b - a for a, b in zip(cu[:-1], cu[1:])), default=0)
+    else:
+        longest = x["q"].shape[1]
+    seq_chunks = -(-longest // 64)
+    chain = min(plan["segment_chunks"], seq_chunks) if plan["cp"] else seq_chunks
+    step_us = chunk_ms * 1e3 / chain if chain else None
+    return {"chunks_per_chain": chain, "chunk_step_us": step_us, "longest_sequence_chunks": seq_chunks,
+            "no_cp_floor_ms": step_us * seq_chunks * 1e-3 if step_us else None}
 
 
 def measure_prefill(name, steps, warmup, n_copies, cp, cp_segment_chunks, torch, gdn, synth, dev, settle_ms=0.0):
@@ -452,6 +469,7 @@ def measure_prefill(name, steps, warmup, n_copies, cp, cp_segment_chunks, torch,
         "whole_op": {"alg_bytes": alg_bytes, "alg_flops": algorithmic_flops(x), "t_bound_ms": t_bound * 1e3,
                      "roofline_frac": t_bound / (ms_step * 1e-3)},
         "clock_settle": {"ms": settle_ms, "untimed_steps": n_settle},
+        "serial_chain": serial_chain(x, plan, stage_ms["chunk"]),
     }
     del copies, argv, ws, o, fs
     return rec, x
