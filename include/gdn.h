@@ -23,6 +23,10 @@
  *   fp16 operands (the gated q and k rows, the intra-chunk matrix and the inverse),
  *   which requires q and k rows of unit scale (L2-normalised, as the method has them,
  *   or normalised by the prologue's qk_l2norm): larger rows can overflow fp16.
+ *   The per-channel log-gates need no lower bound: the pairwise decay factors are split
+ *   at a reference row per 16-token block, and a block whose decay in some channel
+ *   exceeds what the split factors can hold (2^12 for fp16 operands, 2^64 for fp32 ones)
+ *   takes its pairs' factors whole (each at most 1), so no gate value yields inf or NaN.
  *
  * Tensor layouts (row-major, contiguous, device memory):
  *   q, k         [B, T, H_qk, D_k]   dtype
