@@ -236,12 +236,14 @@ void chunk_kernel(ChunkParams p) {
     // issued, so the output waves' chunk-top wait does not wait for those stores to land (with a
     // scalar gate this measured slower: 133 -> 136 us on the Qwen3-Next shape, 523 -> 572 us varlen)
     constexpr bool DEFER_O = PF;
-    // the scalar-gate main pass with two tile buffers: the output waves hand each chunk's output
-    // to the chain waves through LDS, which store it in the next chunk.  The output waves then
-    // issue no stores, so their chunk-top wait for the next tiles (a vmcnt wait, which counts
-    // stores too) no longer waits for output stores to land (133.8 -> 128.8 us on the Qwen3-Next
-    // shape); the chain waves' stores have phase 2 to land before their own chunk-top wait.
-    constexpr bool SW = MODE == 0 && NBUF == 2 && !ST && !CH;
+    // the scalar-gate main pass with two tile buffers: the output waves store each chunk's output
+    // in the next chunk, right after its mid-chunk barrier, where they would otherwise wait for the
+    // chain's state update (phase 2 is the chain's).  Stored at the end of its own chunk, the output
+    // made the output waves' chunk-top wait (a vmcnt wait, which counts stores too) wait for the
+    // stores to land: 133.8 us on the Qwen3-Next shape; handed through LDS to the chain waves, which
+    // stored it before their mid-chunk barrier, 128.0 us; stored this way, 124.2 us (the same as with
+    // the chain waves' stores removed; with no output stores at all 104 us).
+    constexpr bool MIDOUT = MODE == 0 && NBUF == 2 && !ST && !CH;
     constexpr int NRT = 4 / NSUB;                  // token tiles of each output wave
 
     // Separate LDS objects for the two tile buffers and for the exchange: the chunk loop is
@@ -253,8 +255,6 @@ void chunk_kernel(ChunkParams p) {
     __shared__ __attribute__((aligned(16))) Frag<T> sSx[OUT ? L::SXN : 1];
     __shared__ __attribute__((aligned(16))) Frag<T> sVx[OUT ? L::VXN : 1];
     __shared__ __attribute__((aligned(16))) unsigned char pf_sink[PF ? 1024 : 16];
-    // outputs handed to the chain waves: [chunk parity][output wave][tile (i, g)][lane], fp32
-    __shared__ __attribute__((aligned(16))) f32x4 sO[SW ? 2 * NSUB * NRT * NSUB * 64 : 1];
 
     // the wave index is uniform across a wave: readfirstlane makes the role branches scalar
     const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
@@ -496,7 +496,7 @@ void chunk_kernel(ChunkParams p) {
     // the output tile i of output wave s: token tile; wave 0 owns tiles 0 and 3, wave 1 tiles 1 and
     // 2 (which balances the causal P work); a single output wave owns all four
     auto out_tile = [](int s, int i) { return NSUB == 1 ? i : (i == 0 ? (s ? 1 : 0) : (s ? 2 : 3)); };
-    // chunk c's output from registers or LDS: lane (grp, l16) of tile (i, g) of output wave s holds
+    // chunk c's output from the output wave s's registers: lane (grp, l16) of tile (i, g) holds
     // O[16 out_tile(s, i) + l16][16 g + 4 grp + r], r = 0..3.  The resource covers the chunk's valid
     // rows only (rows past the end are dropped by the bounds check).
     auto store_tiles = [&](int c, int s, auto &&tile) __attribute__((always_inline)) {
@@ -532,7 +532,8 @@ void chunk_kernel(ChunkParams p) {
             auto pb_tile = [&](int b) { return NSUB == 1 ? (b < 4 ? b : b - 2) : (b == 0 ? 0 : 1); };
             auto pb_kb = [&](int b) { return NSUB == 1 ? (b < 4 ? 0 : 1) : (b == 2 ? 1 : 0); };
             // (NSUB == 2: blocks (tile 0, kb 0), (tile 1, kb 0), (tile 1, kb 1); tile 1 is m = 3 or 2)
-            // the output of a chunk straight from the accumulators (copied to o_prev: register renames)
+            // the output of a chunk straight from the accumulators (copied to o_prev, register renames,
+            // where it is stored one step late)
             f32x4 o_prev[NR][NSUB];
             auto store_o = [&](int c) __attribute__((always_inline)) {
                 if (c < wup) return;                       // warmup chunk: no output
@@ -647,6 +648,9 @@ void chunk_kernel(ChunkParams p) {
                     for (int b = 0; b < NPB; ++b) form_p(b);
                 }
                 lds_only_barrier();  // V' of chunk c is visible; every wave is done with phase 1
+                if constexpr (MIDOUT) {
+                    if (c > 0) store_o(c - 1);
+                }
                 if constexpr (EARLY_LD) {
                     if (c + 1 < nch) {
                         issue_kq(c + 1, tiles0, 0, 1, LD_ALL & ~LATE_LD);
@@ -666,26 +670,11 @@ void chunk_kernel(ChunkParams p) {
 #pragma unroll
                     for (int b = 0; b < NPB; ++b) mma_xx(o[pb_tile(b)][g], Vh[pb_kb(b)], Vl[pb_kb(b)], ph[b], pl[b]);
                 }
-                if constexpr (!SW) {
 #pragma unroll
-                    for (int i = 0; i < NR; ++i)
+                for (int i = 0; i < NR; ++i)
 #pragma unroll
-                        for (int g = 0; g < NSUB; ++g) o_prev[i][g] = o[i][g];
-                }
-                if constexpr (SW) {
-                    if (c < wup) {
-                    } else if (c + 1 == nch) {             // the last chunk: no next chunk stores it
-                        store_tiles(c, sub, [&](int i, int g) { return o[i][g]; });
-                    } else {
-#pragma unroll
-                        for (int i = 0; i < NR; ++i)
-#pragma unroll
-                            for (int g = 0; g < NSUB; ++g)
-                                sO[(((c & 1) * NSUB + sub) * NR * NSUB + i * NSUB + g) * 64 + lane] = o[i][g];
-                    }
-                } else if constexpr (!DEFER_O) {
-                    store_o(c);
-                }
+                    for (int g = 0; g < NSUB; ++g) o_prev[i][g] = o[i][g];
+                if constexpr (!DEFER_O && !MIDOUT) store_o(c);
             };
             if (nch > 0) {
                 issue_kq(0, tiles0, 0, 1, LD_ALL);
@@ -695,7 +684,7 @@ void chunk_kernel(ChunkParams p) {
                 out_step.template operator()<0>(c);
                 if (c + 1 < nch) out_step.template operator()<NBUF == 2 ? 1 : 0>(c + 1);
             }
-            if constexpr (DEFER_O) {
+            if constexpr (DEFER_O || MIDOUT) {
                 if (nch > 0) store_o(nch - 1);
             }
             return;
@@ -831,14 +820,6 @@ void chunk_kernel(ChunkParams p) {
                 issue_apvg(c + 1, tnext, 0, 1, LD_A);
             }
             if constexpr (PF) issue_pf(c + PF_DIST);
-        }
-        if constexpr (SW) {
-            // chain wave s stores output wave s's tiles of chunk c - 1 here, where it would wait for
-            // the output waves at the barrier anyway (at the chunk's start: 1.5 % slower)
-            if (c > 0 && c - 1 >= wup)
-                store_tiles(c - 1, sub, [&](int i, int g) {
-                    return sO[((((c - 1) & 1) * NSUB + sub) * NRT * NSUB + i * NSUB + g) * 64 + lane];
-                });
         }
         if constexpr (OUT) lds_only_barrier();  // V' of chunk c is visible to the output waves
         // =========================== phase 2 ===========================
