@@ -241,8 +241,8 @@ void chunk_kernel(ChunkParams p) {
     // chain's state update (phase 2 is the chain's).  Stored at the end of its own chunk, the output
     // made the output waves' chunk-top wait (a vmcnt wait, which counts stores too) wait for the
     // stores to land: 133.8 us on the Qwen3-Next shape; handed through LDS to the chain waves, which
-    // stored it before their mid-chunk barrier, 128.0 us; stored this way, 124.2 us (the same as with
-    // the chain waves' stores removed; with no output stores at all 104 us).
+    // stored it before their mid-chunk barrier, 128.0 us; stored this way, 124.2 us (the same as
+    // the hand-over with the chain waves' stores removed).
     constexpr bool MIDOUT = MODE == 0 && NBUF == 2 && !ST && !CH;
     constexpr int NRT = 4 / NSUB;                  // token tiles of each output wave
 

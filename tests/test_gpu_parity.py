@@ -247,7 +247,7 @@ def test_empty_sequence_returns_initial_state():
 
 # --------------------------------------------------------------------------- 16-column workgroups
 # GDN_BV=16 selects the recurrence build with one chain and one output wave per workgroup (16 value
-# columns), whose single output wave owns all four token tiles and hands them to its chain wave.
+# columns), whose single output wave owns all four token tiles and stores them one chunk late.
 @pytest.mark.parametrize("dk", [64, 128])
 def test_sixteen_column_workgroups_bf16(dk, monkeypatch):
     monkeypatch.setenv("GDN_BV", "16")
