@@ -123,3 +123,57 @@ def test_backward_fp32_gate_strengths(gate, mu):
     x = synth.make_inputs(synth.workload("tiny_fp32", B=1, H=2, T=150, gate=gate, mu=mu, h0=True,
                                          seed=640 + int(mu) + (10 if gate == "channel" else 0)))
     _check(x, TOL["fp32"], f"{gate} fp32 mu={mu}", seed=20 + int(mu))
+
+
+# --------------------------------------------------------------------------- full sizes, sampled
+# The backward of the Qwen3-Next-shaped and KDA-shaped workloads at their full sizes, in the
+# launch configuration bench.py times, against the oracle on sampled (sequence, head) slices
+# (heads are independent).  For the KDA shape the oracle takes one head's last `suffix` tokens: the
+# gradients of those tokens depend only on them, on dht and on the state entering them, which the
+# C token recurrence gives from the prefix (dh0 would need the whole reverse pass and is not
+# compared there).
+from oracle.recurrent import gdn_recurrent
+
+
+def _check_sampled(x, tol, label, b, heads, suffix=None, gate="scalar", seed=0):
+    rng = np.random.default_rng(2000 + seed)
+    dt = x["q"].dtype
+    do = torch.from_numpy(rng.standard_normal(tuple(x["v"].shape)).astype(np.float32)).to(dt)
+    B, T, H = x["q"].shape[0], x["q"].shape[1], x["v"].shape[2]
+    D, Dv = x["q"].shape[3], x["v"].shape[3]
+    dh = torch.from_numpy(rng.standard_normal((B, H, D, Dv)).astype(np.float32))
+    dev = torch.device("cuda:0")
+    t = lambda a: None if a is None else a.to(dev)
+    gr = bwd(t(x["q"]), t(x["k"]), t(x["v"]), t(x["g"]), t(x["beta"]), t(do), scale=x["scale"],
+             initial_state=t(x["h0"]), dht=t(dh))
+    torch.cuda.synchronize()
+    gr = {n: v.cpu() for n, v in gr.items()}
+    assert x["q"].shape[2] == H, "sampled slices assume H_qk == H_v"
+    for h in heads:
+        sl = lambda a: f64(a[b:b + 1, :, h:h + 1])
+        q, k, v, g, be, dos = tuple(sl(x[n]) for n in ("q", "k", "v", "g", "beta")) + (sl(do),)
+        h0 = None if x["h0"] is None else f64(x["h0"][b:b + 1, h:h + 1])
+        t0 = 0 if suffix is None else T - suffix
+        if t0 > 0:   # the state entering the suffix, from the C token recurrence over the prefix
+            _, h0 = gdn_recurrent(q[:, :t0], k[:, :t0], v[:, :t0], g[:, :t0], be[:, :t0], x["scale"], h0=h0, gate=gate)
+        cut = lambda a: a[:, t0:]
+        r = gdn_backward(*(cut(a) for a in (q, k, v, g, be)), x["scale"], cut(dos), h0,
+                         f64(dh[b:b + 1, h:h + 1]))
+        names = ("dq", "dk", "dv", "dg", "dbeta") + (("dh0",) if t0 == 0 else ())
+        for n in names:
+            got = f64(gr[n][b:b + 1, h:h + 1]) if n == "dh0" else f64(gr[n][b:b + 1, t0:, h:h + 1])
+            assert np.isfinite(got).all(), f"{label} head {h} {n}: non-finite"
+            e = rel_max_err(got, r[n])
+            print(f"[parity] backward {label} b={b} head {h} {n}: max|d|/rms = {e:.3e} (tol {tol})", flush=True)
+            assert e <= tol, f"{label} head {h} {n}: {e:.3e} > {tol}"
+
+
+def test_backward_qwen3next_shape_full_size_sampled():
+    x = synth.make_inputs(synth.workload("qwen3next_bf16", seed=630))     # B=4, H=16, T=4096, d=128
+    _check_sampled(x, TOL["bf16"], "qwen3next_bf16 full size", b=2, heads=[3, 11], seed=1)
+
+
+def test_backward_kda_shape_full_size_sampled():
+    x = synth.make_inputs(synth.workload("kda_bf16", seed=631))           # B=2, H=32, T=16384, d=128
+    _check_sampled(x, TOL["bf16"], "kda_bf16 full size, last 512 tokens", b=1, heads=[21], suffix=512,
+                   gate="channel", seed=2)
