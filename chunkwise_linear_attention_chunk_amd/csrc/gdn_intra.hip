@@ -370,12 +370,24 @@ __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
         for (int kk = 0; kk < HKB; ++kk)
             qt[b][kk] = ld8(q + ((int64_t)(t0 + row) * p.H_qk + hq) * DK + 32 * (kb0 + kk) + 8 * grp);
     }
-    // thread (d, part) scans NT consecutive tokens of channel d
+    // thread (d, part) scans NT consecutive tokens of channel d.  The gate rows load through a
+    // buffer resource over the chunk's valid rows: the row offset is a scalar, the channel a fixed
+    // lane offset, and rows past the end read as zero (a clamped 64-bit address per element and a
+    // tail mask had cost about a fifth of the kernel's vector instructions)
     constexpr int NPART = 256 / DK, NT = 64 / NPART;
     const int d = tid % DK, part = tid / DK;
+    const int grow = p.H_v * DK * (int)sizeof(T);   // bytes from one token's gate row to the next
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(g + ((int64_t)t0 * p.H_v + h) * DK,
+                                                nv > 0 ? (nv - 1) * grow + DK * (int)sizeof(T) : 0);
     float gs[NT];
 #pragma unroll
-    for (int e = 0; e < NT; ++e) gs[e] = to_f32(g[((int64_t)(t0 + min(part * NT + e, last)) * p.H_v + h) * DK + d]);
+    for (int e = 0; e < NT; ++e) {
+        const int soff = (part * NT + e) * grow;
+        if constexpr (sizeof(T) == 2)
+            gs[e] = __uint_as_float((unsigned)__builtin_amdgcn_raw_buffer_load_b16(rg, d * 2, soff, 0) << 16);
+        else
+            gs[e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, d * 4, soff, 0));
+    }
     if (PRO && p.pro.A_log) {
         // prologue: raw gate inputs through the gate activation, one rolled loop over this thread's
         // own cells of the G tile (an unrolled one would double the kernel's code)
@@ -394,7 +406,8 @@ __global__ __launch_bounds__(256) void intra_kda_kernel(IntraKdaParams p) {
         float acc = 0.f;
 #pragma unroll
         for (int e = 0; e < NT; ++e) {
-            acc += part * NT + e < nv ? gs[e] : 0.f;
+            // rows past the end read zero; with the prologue they went through the activation
+            acc += !PRO || part * NT + e < nv ? gs[e] : 0.f;
             gs[e] = acc;
         }
     }
