@@ -479,8 +479,8 @@ void chunk_kernel(ChunkParams p) {
         static_assert(VM >= 0 && VM < 16, "vmcnt immediate");
         if constexpr (LD) __builtin_amdgcn_s_waitcnt(0x0f70 | VM);
         // (a workgroup barrier with its fence would wait for every memory operation in flight,
-        // vmcnt(0): the prefetches and the chain waves' output stores; each wave's tile loads are covered
-        // by its own wait above, and no wave reads global memory another wave writes here)
+        // vmcnt(0), the prefetches included; each wave's tile loads are covered by its own wait
+        // above, and no wave reads global memory another wave writes here)
         lds_only_barrier();
     };
 
