@@ -78,16 +78,26 @@ def oracle_run(x, batches=None, heads=None, seqs=None, prologue=None):
     return o, fin, pick
 
 
-def rel_max_err(got, ref):
+def _over_rms(err, ref):
+    """err / RMS(ref); an all-zero reference (an empty sequence without h0) allows no error at all."""
+    if ref.size == 0:
+        return 0.0
     rms = np.sqrt(np.mean(ref ** 2))
-    return float(np.abs(got - ref).max() / rms) if ref.size else 0.0
+    if rms == 0.0:
+        return 0.0 if err <= 0.0 else float("inf")
+    return float(err / rms)
+
+
+def rel_max_err(got, ref):
+    return _over_rms(float(np.abs(got - ref).max()) if ref.size else 0.0, ref)
 
 
 def rel_max_err_rounded(got, ref):
     """max_i (|got_i - ref_i| - half_ulp_bf16(max(|got_i|, |ref_i|))) / RMS(ref), floored at 0."""
-    rms = np.sqrt(np.mean(ref ** 2))
+    if ref.size == 0:
+        return 0.0
     excess = np.abs(got - ref) - half_ulp_bf16(np.maximum(np.abs(got), np.abs(ref)))
-    return max(float(excess.max() / rms), 0.0) if ref.size else 0.0
+    return max(_over_rms(float(excess.max()), ref), 0.0)
 
 
 def check(x, tol, batches=None, heads=None, seqs=None, label="", prologue=None, **kw):

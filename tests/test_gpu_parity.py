@@ -238,6 +238,25 @@ def test_kda_key_and_value_dims_differ(dk, dv):
     check(x, TOL["bf16"], label=f"KDA bf16 D_k={dk} D_v={dv}")
 
 
+@pytest.mark.parametrize("gate,dtype", [("scalar", "bf16"), ("channel", "fp32")])
+def test_empty_sequences_without_initial_state(gate, dtype):
+    # packed input whose sequences are all empty, no h0: every final state is zero (written, not left over)
+    x = _w("varlen_bf16", n_seqs=2, lens=(0, 0), H=2, dtype=dtype, gate=gate, seed=231)
+    check(x, TOL[dtype], label=f"empty sequences {gate} {dtype}")
+    dev = torch.device("cuda:0")
+    t = {n: x[n].to(dev) for n in ("q", "k", "v", "g", "beta")}
+    torch.cuda.synchronize()
+    fs = torch.full((2, 2, 128, 128), 7.0, device=dev)
+    o = torch.empty(t["v"].shape, dtype=t["v"].dtype, device=dev)
+    from chunkwise_linear_attention_chunk_amd import gdn
+    cu = x["cu_seqlens"].to(torch.int32)
+    a = gdn.make_args(t["q"], t["k"], t["v"], t["g"], t["beta"], x["scale"], None, cu.to(dev), cu, 64, o, fs)
+    ws = torch.empty(max(gdn.workspace_bytes(a), 1), dtype=torch.uint8, device=dev)
+    gdn.fwd_raw(a, ws.data_ptr(), ws.numel(), torch.cuda.current_stream(dev).cuda_stream)
+    torch.cuda.synchronize()
+    assert bool((fs == 0).all()), "the final states of empty sequences must be written as zeros"
+
+
 def test_empty_sequence_returns_initial_state():
     x = _w("qwen3next_bf16", B=2, H=2, T=0, h0=True, seed=230)
     o, fs = gpu_run(x)
