@@ -73,3 +73,40 @@ def test_random_configuration(c, monkeypatch):
         w = synth.workload("qwen3next_bf16", B=c["B"], T=c["T"], **common)
     x = _dims(synth.make_inputs(w), c["dk"], c["dv"])
     check(x, TOL[c["dtype"]], label=_id(c), **c["kw"])
+
+
+def _decode_cases(seed=20261204, n=16):
+    r = random.Random(seed)
+    out = []
+    for i in range(n):
+        c = dict(i=i, gate=r.choice(["scalar", "channel"]), dtype=r.choice(["bf16", "fp32"]))
+        c["Hv"] = r.choice([1, 2, 4, 6])
+        c["Hq"] = r.choice([d for d in (1, 2, 3, 6) if c["Hv"] % d == 0])
+        c["dk"], c["dv"] = r.choice([64, 128]), r.choice([64, 128])
+        c["mu"] = r.choice([None, -3.0, -2.0, 0.0])
+        c["h0"] = r.random() < 0.7
+        if r.random() < 0.4:
+            c["lens"] = tuple(r.choice([0, 1, 2, r.randint(1, 40)]) for _ in range(r.randint(1, 8)))
+        else:
+            c["B"], c["T"] = r.randint(1, 8), r.choice([1, 1, 2, r.randint(1, 40)])
+        out.append(c)
+    return out
+
+
+def _decode_id(c):
+    shape = ("lens" + "_".join(str(n) for n in c["lens"])) if "lens" in c else f"B{c['B']}T{c['T']}"
+    return (f"{c['i']}-{c['gate']}-{c['dtype']}-Hv{c['Hv']}Hq{c['Hq']}-dk{c['dk']}dv{c['dv']}-mu{c['mu']}-"
+            f"h0{int(c['h0'])}-{shape}")
+
+
+@pytest.mark.parametrize("c", _decode_cases(), ids=_decode_id)
+def test_random_decode_configuration(c):
+    # gdn_fwd_recurrent (token by token) on a random configuration
+    common = dict(H=c["Hv"], H_qk=c["Hq"], D=128, dtype=c["dtype"], gate=c["gate"], mu=c["mu"], h0=c["h0"],
+                  seed=9800 + c["i"])
+    if "lens" in c:
+        w = synth.workload("varlen_bf16", n_seqs=len(c["lens"]), lens=c["lens"], **common)
+    else:
+        w = synth.workload("qwen3next_bf16", B=c["B"], T=c["T"], **common)
+    x = _dims(synth.make_inputs(w), c["dk"], c["dv"])
+    check(x, TOL[c["dtype"]], label=_decode_id(c), recurrent=True)
