@@ -24,6 +24,7 @@ METRIC = "GDN chunked-prefill fwd tokens/s at 1 GPU + % of MFMA/HBM roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
 _CSRC = "chunkwise_linear_attention_chunk_amd/csrc/"
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000   # hipEventDisableSystemFence
 _HEADERS = [_CSRC + "gdn_device.h", _CSRC + "gdn_internal.h"]
 # each kernel's source file and the headers it includes (the counters of profiles/traffic_*.json
 # are current only while all of them are unchanged)
@@ -409,13 +410,19 @@ def measure_prefill(name, steps, warmup, n_copies, cp, cp_segment_chunks, torch,
 
     hip = hip_runtime()
     n_ev = len(gdn.STAGES) + 1
+    # The stage-end events only, without the system-scope fence (they serve timing alone): a start
+    # event in each call's first dispatch cost about 5 us per step, so each step's first stage is
+    # timed from the previous step's last event (the gap between the calls included) and the first
+    # step's first stage is not timed.
+    hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
     events = []
     for _ in range(steps):
         arr = (ctypes.c_void_p * n_ev)()
-        for j in range(n_ev):
+        arr[0] = None
+        for j in range(1, n_ev):
             ev = ctypes.c_void_p()
-            if hip.hipEventCreate(ctypes.byref(ev)) != 0:
-                raise RuntimeError("hipEventCreate failed")
+            if hip.hipEventCreateWithFlags(ctypes.byref(ev), HIP_EVENT_DISABLE_SYSTEM_FENCE) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
             arr[j] = ev.value
         events.append(arr)
 
@@ -431,17 +438,23 @@ def measure_prefill(name, steps, warmup, n_copies, cp, cp_segment_chunks, torch,
     elapsed = time.perf_counter() - t0
 
     stage_ms = {s: 0.0 for s in gdn.STAGES}
+    counts = {s: 0 for s in gdn.STAGES}
+    prev = None  # the last recorded boundary (the previous step's last event at a step's start)
     for arr, mask in zip(events, ran):
-        prev = 0  # last recorded boundary
         for j, s in enumerate(gdn.STAGES):
             if not (mask >> j) & 1:
                 continue
-            ms = ctypes.c_float()
-            if hip.hipEventElapsedTime(ctypes.byref(ms), arr[prev], arr[j + 1]) != 0:
-                raise RuntimeError("hipEventElapsedTime failed")
-            stage_ms[s] += ms.value / steps
-            prev = j + 1
-        for j in range(n_ev):
+            if prev is not None:
+                ms = ctypes.c_float()
+                if hip.hipEventElapsedTime(ctypes.byref(ms), prev, arr[j + 1]) != 0:
+                    raise RuntimeError("hipEventElapsedTime failed")
+                stage_ms[s] += ms.value
+                counts[s] += 1
+            prev = arr[j + 1]
+    for s in gdn.STAGES:
+        stage_ms[s] = stage_ms[s] / counts[s] if counts[s] else 0.0
+    for arr in events:
+        for j in range(1, n_ev):
             hip.hipEventDestroy(arr[j])
     plan = gdn.plan(argv[0])
     dominant = max(("intra", "cp_pre", "chunk"), key=lambda s: stage_ms[s])

@@ -332,7 +332,7 @@ gdn_status run_fwd(const gdn_fwd_args *a, void *workspace, size_t workspace_byte
     };
     hipError_t e = hipSuccess;
     if (a->N == 0) {
-        if (events && (e = hipEventRecord(static_cast<hipEvent_t>(events[0]), s)) != hipSuccess)
+        if (events && events[0] && (e = hipEventRecord(static_cast<hipEvent_t>(events[0]), s)) != hipSuccess)
             return done(fail(GDN_ERR_HIP, "event record: %s", hipGetErrorString(e)));
         return done(GDN_OK);
     }
@@ -406,11 +406,12 @@ gdn_status run_fwd(const gdn_fwd_args *a, void *workspace, size_t workspace_byte
             return r == hipSuccess;
         };
         bool ok = check(hipEventRecord(ev[0], s), "event") && check(hipStreamWaitEvent(side, ev[0], 0), "stream wait");
-        if (ok && events && first) ok = check(hipEventRecord(static_cast<hipEvent_t>(events[0]), s), "event");
+        if (ok && events && first && events[0]) ok = check(hipEventRecord(static_cast<hipEvent_t>(events[0]), s), "event");
         for (int j = 0; ok && j < P; ++j) {
             ok = check(intra(j * L, std::min(L, nc - j * L), side), "intra launch");
-            if (ok && j == 0 && events) {
-                ok = check(hipEventRecord(static_cast<hipEvent_t>(events[GDN_STAGE_INTRA + 1]), side), "event");
+            if (ok && j == 0) {
+                if (events && events[GDN_STAGE_INTRA + 1])
+                    ok = check(hipEventRecord(static_cast<hipEvent_t>(events[GDN_STAGE_INTRA + 1]), side), "event");
                 ran |= 1u << GDN_STAGE_INTRA;
             }
             ok = ok && check(hipEventRecord(ev[j + 1], side), "event");
@@ -424,7 +425,8 @@ gdn_status run_fwd(const gdn_fwd_args *a, void *workspace, size_t workspace_byte
         release();
         if (!ok) return done(GDN_ERR_HIP);
         ran |= 1u << GDN_STAGE_CHUNK;
-        if (events && (e = hipEventRecord(static_cast<hipEvent_t>(events[GDN_STAGE_CHUNK + 1]), s)) != hipSuccess)
+        if (events && events[GDN_STAGE_CHUNK + 1] &&
+            (e = hipEventRecord(static_cast<hipEvent_t>(events[GDN_STAGE_CHUNK + 1]), s)) != hipSuccess)
             return done(fail(GDN_ERR_HIP, "event: %s", hipGetErrorString(e)));
         return done(GDN_OK);
     }

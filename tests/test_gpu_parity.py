@@ -399,3 +399,42 @@ def test_continuation():
     rms = o_full.double().pow(2).mean().sqrt()
     assert (torch.cat([o1, o2], 1) - o_full).abs().max() <= 1e-4 * rms
     assert (f2 - f_full).abs().max() <= 1e-4 * f_full.double().pow(2).mean().sqrt()
+
+
+# --------------------------------------------------------------------------- timed entry point
+@pytest.mark.parametrize("pieces", [1, 2])
+def test_timed_call_with_null_events_matches_untimed(pieces, monkeypatch):
+    # gdn_fwd_timed with only some events given (NULL entries are not recorded): same results as
+    # gdn_fwd, and the recorded events give the recurrence's time
+    import ctypes
+    from chunkwise_linear_attention_chunk_amd import gdn
+    monkeypatch.setenv("GDN_PIECES", str(pieces))
+    x = _w("qwen3next_bf16", B=2, H=2, T=64 * 6 + 9, h0=True, seed=760 + pieces)
+    dev = torch.device("cuda:0")
+    t = {n: x[n].to(dev) for n in ("q", "k", "v", "g", "beta", "h0")}
+    outs = []
+    for timed in (False, True):
+        o = torch.empty(t["v"].shape, dtype=t["v"].dtype, device=dev)
+        fs = torch.empty(t["h0"].shape, dtype=torch.float32, device=dev)
+        a = gdn.make_args(t["q"], t["k"], t["v"], t["g"], t["beta"], x["scale"], t["h0"], None, None, 64, o, fs,
+                          cp_mode="off")
+        ws = torch.empty(max(gdn.workspace_bytes(a), 1), dtype=torch.uint8, device=dev)
+        s = torch.cuda.current_stream(dev).cuda_stream
+        if timed:
+            # torch's timing events (hipEvent_t handles underneath), created by a first record
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            for e in evs:
+                e.record()
+            torch.cuda.synchronize()
+            arr = (ctypes.c_void_p * (len(gdn.STAGES) + 1))()   # every entry NULL but these two
+            arr[gdn.STAGES.index("intra") + 1] = evs[0].cuda_event
+            arr[gdn.STAGES.index("chunk") + 1] = evs[1].cuda_event
+            mask = gdn.fwd_timed_raw(a, ws.data_ptr(), ws.numel(), s, arr)
+            torch.cuda.synchronize()
+            assert (mask >> gdn.STAGES.index("intra")) & 1 and (mask >> gdn.STAGES.index("chunk")) & 1
+            assert evs[0].elapsed_time(evs[1]) > 0.0
+        else:
+            gdn.fwd_raw(a, ws.data_ptr(), ws.numel(), s)
+            torch.cuda.synchronize()
+        outs.append((o.cpu(), fs.cpu()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
