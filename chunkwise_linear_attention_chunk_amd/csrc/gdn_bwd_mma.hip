@@ -13,6 +13,8 @@
 // in the forward.  Token-by-column intermediates are kept in LDS transposed ([column][token]), so
 // that both the products over tokens and those over columns read them with 8-byte or transposed
 // reads; the tiles are padded (one granule per row) and filled with direct-to-LDS loads.
+// The phase barriers wait for LDS traffic only (explicit waits cover the tile loads): the gradient
+// stores and the state values read ahead for the next phase stay in flight across them.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -111,10 +113,40 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_mma_kernel(BwdParams p) {
                          lds + L::G0 + 1024 * w, 1024 * w + 16 * lane);
         load_half(0);
     }
+    // S and dS_next values of P1 (this lane's value column, D_k rows in pi order), read from memory
+    // ahead of the barrier that precedes their use, together with the tile loads
+    const int ct = w & 3, tt0 = 2 * (w >> 2);             // token x column tiles of the half
+    float ps[NKB][8], pd[NKB][8];
+    auto ld_p1 = [&](int hv) __attribute__((always_inline)) {
+        const int cg = 64 * hv + 16 * ct + l16;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int d = 32 * kb + (e < 4 ? 4 * grp + e : 16 + 4 * grp + e - 4);
+                ps[kb][e] = St[d * DV + cg];
+                pd[kb][e] = dSt[d * DV + cg];
+            }
+    };
+    // S and dS_next values of P4 (rows 16 m + l16, this half's columns in pi order), read at the
+    // start of P3
+    const int m = w % MD;
+    float qs[2][8], qd[2][8];
+    auto ld_p4 = [&](int hv) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int c = 64 * hv + 32 * kb + (e < 4 ? 4 * grp + e : 16 + 4 * grp + e - 4);
+                qs[kb][e] = St[(16 * m + l16) * DV + c];
+                qd[kb][e] = dSt[(16 * m + l16) * DV + c];
+            }
+    };
+    ld_p1(0);
     if (tid < 64) rdgl[tid] = rdb[tid] = rsc[tid] = 0.f;
     if (tid == 0) rglc[0] = 0.f;
     wait_vm<0>();
-    __syncthreads();
+    lds_only_barrier();
 
     // gate rows of this lane's accumulator rows 16 a + 4 grp + r
     auto rows4 = [&](int off, int a) __attribute__((always_inline)) {
@@ -151,13 +183,14 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_mma_kernel(BwdParams p) {
     for (int q = 0; q < 2; ++q) dA[q] = dP[q] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int q = 0; q < NQT; ++q) dqS[q] = dkD[q] = dkX[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int ct = w & 3, tt0 = 2 * (w >> 2);             // token x column tiles of the half
-    const int m = w % MD, qt0 = (w / MD) * NQT;           // dq / dk tiles: rows 16 m of D_k, tokens
+    const int qt0 = (w / MD) * NQT;                       // dq / dk tiles: rows 16 m of D_k, tokens
     const float gC = g[GB_GC];
 
     const int NH = DV / 64;                               // halves of the value columns
-    for (int hv = 0; hv < NH; ++hv) {
-        __syncthreads();   // the half's V and dO tiles have landed; Pt (first half) is complete
+    // one half of the value columns; the second half is a separate inlined copy, so that the state
+    // values read ahead for its P1 are not carried around a loop
+    auto half = [&](int hv) __attribute__((always_inline)) {
+        lds_only_barrier();   // the half's V and dO tiles have landed; Pt (first half) is complete
         const int colg = 64 * hv + 16 * ct + l16;          // this lane's value column (P1 - P3)
         // ---- P1: K S, K dS_next, X
         f32x4 ks[2], kd[2];
@@ -165,15 +198,8 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_mma_kernel(BwdParams p) {
             Frag<bf16> sh[NKB], sl[NKB], dh[NKB], dl[NKB];
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
-                float xs[8], xd[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int d = 32 * kb + (e < 4 ? 4 * grp + e : 16 + 4 * grp + e - 4);
-                    xs[e] = St[d * DV + colg];
-                    xd[e] = dSt[d * DV + colg];
-                }
-                split8_rne(xs, sh[kb], sl[kb]);
-                split8_rne(xd, dh[kb], dl[kb]);
+                split8_rne(ps[kb], sh[kb], sl[kb]);
+                split8_rne(pd[kb], dh[kb], dl[kb]);
             }
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
@@ -202,7 +228,7 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_mma_kernel(BwdParams p) {
             }
             put_t<ST>(tXh, tXl, 16 * ct + l16, 16 * tt + 4 * grp, x);
         }
-        __syncthreads();
+        lds_only_barrier();
         // ---- P2: V' = A X, dV' = diag(D) K dS_next + Pt^T dO; the D terms of d gl
         f32x4 vp[2], dvp[2];
 #pragma unroll
@@ -236,8 +262,9 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_mma_kernel(BwdParams p) {
                 }
             }
         }
-        __syncthreads();
+        lds_only_barrier();
         // ---- P3: dX = A^T dV', dv, the X terms of dbeta and d gl
+        ld_p4(hv);
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             const int tt = tt0 + q;
@@ -263,7 +290,7 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_mma_kernel(BwdParams p) {
             }
             put_t<ST>(tEh, tEl, 16 * ct + l16, 16 * tt + 4 * grp, dx);
         }
-        __syncthreads();
+        lds_only_barrier();
         // ---- P4: the products over this half's columns
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
@@ -283,16 +310,10 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_mma_kernel(BwdParams p) {
             float fro = 0.f;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                float xs[8], xd[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int c = 64 * hv + 32 * kb + (e < 4 ? 4 * grp + e : 16 + 4 * grp + e - 4);
-                    xs[e] = St[(16 * m + l16) * DV + c];
-                    xd[e] = dSt[(16 * m + l16) * DV + c];
-                    fro += xs[e] * xd[e];
-                }
-                split8_rne(xs, sh[kb], sl[kb]);
-                split8_rne(xd, dh[kb], dl[kb]);
+                for (int e = 0; e < 8; ++e) fro += qs[kb][e] * qd[kb][e];
+                split8_rne(qs[kb], sh[kb], sl[kb]);
+                split8_rne(qd[kb], dh[kb], dl[kb]);
             }
             // gamma_C <S, dS_next> (each element once: the waves past the D_k rows' owners skip it)
             if (w < MD) {
@@ -310,11 +331,14 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_mma_kernel(BwdParams p) {
                 }
             }
         }
-        if (hv + 1 < NH) {
-            __syncthreads();   // every wave is done with the first half's tiles
-            load_half(1);
-            wait_vm<0>();
-        }
+    };
+    half(0);
+    if (NH > 1) {
+        lds_only_barrier();   // every wave is done with the first half's tiles
+        load_half(1);
+        ld_p1(1);
+        wait_vm<0>();
+        half(1);
     }
 
     // ---- dq, dk through the states; the q . dq term of d gl
@@ -334,14 +358,14 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_mma_kernel(BwdParams p) {
             if (l16 == 0) atomicAdd(&rdgl[16 * tt + 4 * grp + r], e);
         }
     }
-    __syncthreads();   // every wave is done with the pair buffers
+    lds_only_barrier();   // every wave is done with the pair buffers
     // ---- dA transposed ([s][t]) into the X buffers
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         const int tix = w + 8 * q, ti = tix >> 2, tj = tix & 3;
         put_t<ST>(tXh, tXl, 16 * tj + l16, 16 * ti + 4 * grp, dA[q]);
     }
-    __syncthreads();
+    lds_only_barrier();
     // ---- T = A^T dA, transposed ([t][i]) into the V' buffers
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -355,7 +379,7 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_mma_kernel(BwdParams p) {
         }
         put_t<ST>(tVh, tVl, 16 * tj + l16, 16 * ti + 4 * grp, T);
     }
-    __syncthreads();
+    lds_only_barrier();
     // ---- dL, G, the L and Pt terms of dbeta and d gl; M1 and E transposed into the dV' and dX buffers
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -402,7 +426,7 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_mma_kernel(BwdParams p) {
         put_t<ST>(tDh, tDl, j, 16 * ti + 4 * grp, m1);
         put_t<ST>(tEh, tEl, j, 16 * ti + 4 * grp, e1);
     }
-    __syncthreads();
+    lds_only_barrier();
     // ---- dq += M1 K, dk += M1^T Q + E K + E^T K; stores
     const int hs = p.dq_v == p.dq ? hq : h, hn = p.dq_v == p.dq ? p.H_qk : p.H_v;
 #pragma unroll
@@ -431,7 +455,7 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_mma_kernel(BwdParams p) {
             }
         }
     }
-    __syncthreads();   // every row term of d gl and dbeta is in
+    lds_only_barrier();   // every row term of d gl and dbeta is in
     if (tid < 64) {
         float x = tid < nv ? rdgl[tid] : 0.f;
         if (tid == max(nv - 1, 0)) {
@@ -585,24 +609,43 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_kda_mma_kernel(BwdParams p) 
             dma_granules(rsrc_words(p.gates + unit * GB_FLOATS, GB_FLOATS * 4), lds + L::G0 + 1024 * w, 1024 * w + 16 * lane);
         load_half(0);
     }
+    // S and dS_next values of P1 (this lane's value column, D_k rows in pi order), read from memory
+    // ahead of the barrier that precedes their use, together with the tile loads
+    const int ct = w & 3, tt0 = 2 * (w >> 2);             // token x column tiles of the half
+    float ps[NKB][8], pd[NKB][8];
+    auto ld_p1 = [&](int hv) __attribute__((always_inline)) {
+        const int cg = 64 * hv + 16 * ct + l16;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int d = 32 * kb + (e < 4 ? 4 * grp + e : 16 + 4 * grp + e - 4);
+                ps[kb][e] = St[d * DV + cg];
+                pd[kb][e] = dSt[d * DV + cg];
+            }
+    };
+    // S and dS_next values of P4 (rows 16 m + l16, this half's columns in pi order), read at the
+    // start of P3
+    const int m = w % MD;
+    float qs[2][8], qd[2][8];
+    auto ld_p4 = [&](int hv) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int c = 64 * hv + 32 * kb + (e < 4 ? 4 * grp + e : 16 + 4 * grp + e - 4);
+                qs[kb][e] = St[(16 * m + l16) * DV + c];
+                qd[kb][e] = dSt[(16 * m + l16) * DV + c];
+            }
+    };
+    ld_p1(0);
     if (tid < 64) rdb[tid] = 0.f;
     if (tid < DK) rdgc[tid] = 0.f;
     wait_vm<0>();
-    __syncthreads();
+    lds_only_barrier();
 
     auto rows4 = [&](int off, int a) __attribute__((always_inline)) {
         return *reinterpret_cast<const float4 *>(g + off + 16 * a + 4 * grp);
-    };
-    // the pi-order pair of eight fp32 values of a state-shaped matrix at (row, column) positions
-    auto state_pair = [&](const float *M, int rowc, bool by_col, int base, int kb, Frag<f16> &hi, Frag<f16> &lo)
-        __attribute__((always_inline)) {
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int k = base + 32 * kb + (e < 4 ? 4 * grp + e : 16 + 4 * grp + e - 4);
-            x[e] = by_col ? M[k * DV + rowc] : M[rowc * DV + k];
-        }
-        split8_h2(x, hi, lo);
     };
 
     f32x4 dA[2], dP[2];                                   // 64 x 64 tiles w, w + 8
@@ -610,12 +653,13 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_kda_mma_kernel(BwdParams p) 
     dA[0] = dA[1] = dP[0] = dP[1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int q = 0; q < NQT; ++q) dqS[q] = dkD[q] = dkX[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int ct = w & 3, tt0 = 2 * (w >> 2);             // token x column tiles of the half
-    const int m = w % MD, qt0 = (w / MD) * NQT;           // dq / dk tiles: rows 16 m of D_k, tokens
+    const int qt0 = (w / MD) * NQT;                       // dq / dk tiles: rows 16 m of D_k, tokens
 
     const int NH = DV / 64;                               // halves of the value columns
-    for (int hv = 0; hv < NH; ++hv) {
-        __syncthreads();   // the half's V and dO tiles have landed
+    // one half of the value columns; the second half is a separate inlined copy, so that the state
+    // values read ahead for its P1 are not carried around a loop
+    auto half = [&](int hv) __attribute__((always_inline)) {
+        lds_only_barrier();   // the half's V and dO tiles have landed
         const int colg = 64 * hv + 16 * ct + l16;          // this lane's value column
         // ---- P1: Kg S, Kd dS_next, X
         f32x4 ks[2], kd[2];
@@ -623,8 +667,8 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_kda_mma_kernel(BwdParams p) 
             Frag<f16> sh[NKB], sl[NKB], dh[NKB], dl[NKB];
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
-                state_pair(St, colg, true, 0, kb, sh[kb], sl[kb]);
-                state_pair(dSt, colg, true, 0, kb, dh[kb], dl[kb]);
+                split8_h2(ps[kb], sh[kb], sl[kb]);
+                split8_h2(pd[kb], dh[kb], dl[kb]);
             }
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
@@ -652,7 +696,7 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_kda_mma_kernel(BwdParams p) 
             }
             put_t16<ST>(tXh, tXl, 16 * ct + l16, 16 * tt + 4 * grp, x);
         }
-        __syncthreads();
+        lds_only_barrier();
         // ---- P2: V' = A X, dV' = Kd dS_next + (scale P)^T dO
         {
             Frag<f16> of[2];
@@ -677,8 +721,9 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_kda_mma_kernel(BwdParams p) 
                 put_t16<ST>(tDh, tDl, 16 * ct + l16, 16 * tt + 4 * grp, dvp);
             }
         }
-        __syncthreads();
+        lds_only_barrier();
         // ---- P3: dX = A^T dV', dv, the X term of dbeta
+        ld_p4(hv);
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             const int tt = tt0 + q;
@@ -700,7 +745,7 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_kda_mma_kernel(BwdParams p) 
             }
             put_t16<ST>(tEh, tEl, 16 * ct + l16, 16 * tt + 4 * grp, dx);
         }
-        __syncthreads();
+        lds_only_barrier();
         // ---- P4: the products over this half's columns
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
@@ -720,13 +765,10 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_kda_mma_kernel(BwdParams p) 
             float fro = 0.f;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                state_pair(St, 16 * m + l16, false, 64 * hv, kb, sh[kb], sl[kb]);
-                state_pair(dSt, 16 * m + l16, false, 64 * hv, kb, dh[kb], dl[kb]);
+                split8_h2(qs[kb], sh[kb], sl[kb]);
+                split8_h2(qd[kb], dh[kb], dl[kb]);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int c = 64 * hv + 32 * kb + (e < 4 ? 4 * grp + e : 16 + 4 * grp + e - 4);
-                    fro += St[(16 * m + l16) * DV + c] * dSt[(16 * m + l16) * DV + c];
-                }
+                for (int e = 0; e < 8; ++e) fro += qs[kb][e] * qd[kb][e];
             }
             // e^{G_C} <S, dS_next> of channel 16 m + l16 (each row once: the waves past the D_k
             // rows' owners skip it)
@@ -747,11 +789,14 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_kda_mma_kernel(BwdParams p) 
                 }
             }
         }
-        if (hv + 1 < NH) {
-            __syncthreads();   // every wave is done with the first half's tiles
-            load_half(1);
-            wait_vm<0>();
-        }
+    };
+    half(0);
+    if (NH > 1) {
+        lds_only_barrier();   // every wave is done with the first half's tiles
+        load_half(1);
+        ld_p1(1);
+        wait_vm<0>();
+        half(1);
     }
 
     // ---- the tail.  G (every channel's inclusive cumsum down the chunk; rows past the end repeat
@@ -762,7 +807,7 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_kda_mma_kernel(BwdParams p) 
     float *sG = reinterpret_cast<float *>(lds + L::KG0);
     unsigned char *tK = tV, *tQ = tEh;
     constexpr int GP = DK + 4, NPART = 512 / DK, NR = 64 / NPART;
-    __syncthreads();   // every wave is done with the Kg, Kd, V, dO and dX tiles
+    lds_only_barrier();   // every wave is done with the Kg, Kd, V, dO and dX tiles
     const bf16 *kin = static_cast<const bf16 *>(p.k) + tok0 * qks + (int64_t)hq * DK;
     const bf16 *qin = static_cast<const bf16 *>(p.q) + tok0 * qks + (int64_t)hq * DK;
     load.template operator()<KT>(tK, rsrc_words(kin, ((nv - 1) * qks + DK) * 2), qks * 2);
@@ -780,15 +825,15 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_kda_mma_kernel(BwdParams p) 
             v[e] = acc;
         }
         rtot[part * DK + dd] = acc;
-        __syncthreads();
+        lds_only_barrier();
         float base = 0.f;
         for (int pp = 0; pp < part; ++pp) base += rtot[pp * DK + dd];
 #pragma unroll
         for (int e = 0; e < NR; ++e) sG[(part * NR + e) * GP + dd] = v[e] + base;
-        __syncthreads();
+        lds_only_barrier();
     }
     wait_vm<0>();      // this wave's K and Q tile loads
-    __syncthreads();   // both tiles are complete
+    lds_only_barrier();   // both tiles are complete
     const int d = 16 * m + l16;
     const float gC = sG[63 * GP + d];
     auto kq_at = [&](const unsigned char *t, int row) __attribute__((always_inline)) {
@@ -808,7 +853,7 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_kda_mma_kernel(BwdParams p) 
         put_t16<ST>(tXh, tXl, j, 16 * ti + 4 * grp, dA[q]);
         put_t16<ST>(tDh, tDl, j, 16 * ti + 4 * grp, x);
     }
-    __syncthreads();
+    lds_only_barrier();
     // ---- T = A^T dA, transposed ([t][i]) into the V' buffers
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -822,7 +867,7 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_kda_mma_kernel(BwdParams p) 
         }
         put_t16<ST>(tVh, tVl, 16 * tj + l16, 16 * ti + 4 * grp, T);
     }
-    __syncthreads();   // every wave is done with dA^T: dL takes its place
+    lds_only_barrier();   // every wave is done with dA^T: dL takes its place
     // ---- dL = -T A^T (strictly lower), transposed into the X buffers
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -843,7 +888,7 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_kda_mma_kernel(BwdParams p) 
         for (int r = 0; r < 4; ++r) x[r] = j < 16 * ti + 4 * grp + r ? -dl[r] : 0.f;
         put_t16<ST>(tXh, tXl, j, 16 * ti + 4 * grp, x);
     }
-    __syncthreads();   // dP and dL are complete
+    lds_only_barrier();   // dP and dL are complete
     // ---- the P and L terms, block R of rows at a time (the dq / dk tiles of this wave)
     auto dpair = [&](const unsigned char *th, const unsigned char *tl, int row, int col) __attribute__((always_inline)) {
         return (float)*reinterpret_cast<const f16 *>(th + ST::off(row, col * 2)) +
@@ -960,12 +1005,12 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_kda_mma_kernel(BwdParams p) 
     }
     dgd_sum = sum_groups(dgd_sum);
     if (grp == 0) atomicAdd(&rdgc[d], dgd_sum);
-    __syncthreads();   // dG, rdb and rdgc are complete
+    lds_only_barrier();   // dG, rdb and rdgc are complete
     // ---- the last valid row's e^{G_C} terms, then dG's reverse cumsum per channel (the notes'
     //      Step 7) and dbeta
     if (tid < DK && nv > 0) *dG_at(nv - 1, tid) += rdgc[tid];
     if (tid < nv) p.dbeta[(tok0 + tid) * p.H_v + h] = rdb[tid];
-    __syncthreads();
+    lds_only_barrier();
     {
         const int dd = tid % DK, part = tid / DK;
         float v[NR];
@@ -976,7 +1021,7 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_kda_mma_kernel(BwdParams p) 
             v[e] = acc;
         }
         rtot[part * DK + dd] = acc;
-        __syncthreads();
+        lds_only_barrier();
         float later = 0.f;
         for (int pp = part + 1; pp < NPART; ++pp) later += rtot[pp * DK + dd];
 #pragma unroll
