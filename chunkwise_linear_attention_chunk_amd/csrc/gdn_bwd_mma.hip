@@ -51,11 +51,20 @@ __device__ __forceinline__ void put_t(unsigned char *th, unsigned char *tl, int 
     *reinterpret_cast<u32x2 *>(th + PT::off(b, a * 2)) = hi;
     *reinterpret_cast<u32x2 *>(tl + PT::off(b, a * 2)) = lo;
 }
-__device__ __forceinline__ float sum16(float x) {   // over the 16 lanes of a group
-    x += __shfl_xor(x, 1, 64);
-    x += __shfl_xor(x, 2, 64);
-    x += __shfl_xor(x, 4, 64);
-    x += __shfl_xor(x, 8, 64);
+// x from the lane the DPP control picks within this lane's row of 16 (all lanes active)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+// over the 16 lanes of a group, on the DPP crossbar instead of LDS permutes: quad_perm [1,0,3,2]
+// and [2,3,0,1] (lane xor 1, xor 2), then row_half_mirror and row_mirror, which pair the quads and
+// the halves of the row as xor 4 and xor 8 would; every lane ends with the same total, added in the
+// same order as the xor butterfly.  Call with the whole wave active.
+__device__ __forceinline__ float sum16(float x) {
+    x += dpp_f32<0xb1>(x);
+    x += dpp_f32<0x4e>(x);
+    x += dpp_f32<0x141>(x);
+    x += dpp_f32<0x140>(x);
     return x;
 }
 __device__ __forceinline__ float sum_groups(float x) {   // over the 4 groups (same l16)
