@@ -354,7 +354,7 @@ __global__ __launch_bounds__(128, 1) void bwd_dstate_mma_kernel(BwdParams p) {
     using KT = typename L::K;
     using AT = typename L::A;
     using OT = typename L::O;
-    constexpr int MD = L::MD, NKB = L::NKB, NLW = L::NLW, NW = L::NW;
+    constexpr int MD = L::MD, NKB = L::NKB, NW = L::NW;
     __shared__ __attribute__((aligned(16))) unsigned char stg0[L::STAGE], stg1[L::STAGE];
     const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -373,35 +373,25 @@ __global__ __launch_bounds__(128, 1) void bwd_dstate_mma_kernel(BwdParams p) {
     const bf16 *Pb = reinterpret_cast<const bf16 *>(p.pmat) + (int64_t)h * 2 * 4096;
     const float *Gb = p.gates + (int64_t)h * GB_FLOATS;
 
-    // this wave's stage instructions (K, Q, A, Pt hi, Pt lo, dO, gate block; pad granules read zeros)
+    // this wave's stage instructions: instruction i = wave + NW j of each tile (the K-shaped tiles
+    // share their lane offsets, as do the 64 x 64 ones); pad granules read zeros
     constexpr int kOut = 1 << 30;
-    int soff[NLW], dst[NLW], kind[NLW];
+    constexpr int JK = (KT::NI + NW - 1) / NW, JA = (AT::NI + NW - 1) / NW, JO = (OT::NI + NW - 1) / NW;
+    int offK[JK], offA[JA], offO[JO];
 #pragma unroll
-    for (int j = 0; j < NLW; ++j) {
-        int ii = wave + NW * j;
-        kind[j] = 7;
-        soff[j] = 0;
-        dst[j] = 0;
-        if (ii < 2 * KT::NI) {
-            const int q = ii >= KT::NI, i2 = ii - q * KT::NI, pos = 64 * i2 + lane, row = pos / KT::P, g = pos % KT::P;
-            kind[j] = q;                                     // 0: K, 1: Q
-            soff[j] = g < KT::P - 1 ? row * qks * 2 + 16 * g : kOut;
-            dst[j] = (q ? L::Q0 : L::K0) + 1024 * i2;
-        } else if ((ii -= 2 * KT::NI) < 3 * AT::NI) {
-            const int part = ii / AT::NI, i2 = ii - part * AT::NI, pos = 64 * i2 + lane, row = pos / AT::P, g = pos % AT::P;
-            kind[j] = 2 + part;                              // 2: A, 3: Pt hi, 4: Pt lo
-            soff[j] = g < AT::P - 1 ? row * 128 + 16 * g : kOut;
-            dst[j] = L::A0 + part * AT::BYTES + 1024 * i2;
-        } else if ((ii -= 3 * AT::NI) < OT::NI) {
-            const int pos = 64 * ii + lane, row = pos / OT::P, g = pos % OT::P;
-            kind[j] = 5;
-            soff[j] = g < OT::P - 1 ? row * vs * 2 + 16 * g : kOut;
-            dst[j] = L::O0 + 1024 * ii;
-        } else if ((ii -= OT::NI) < L::NLG) {
-            kind[j] = 6;
-            soff[j] = 1024 * ii + 16 * lane;
-            dst[j] = L::G0 + 1024 * ii;
-        }
+    for (int j = 0; j < JK; ++j) {
+        const int pos = 64 * (wave + NW * j) + lane, row = pos / KT::P, g = pos % KT::P;
+        offK[j] = g < KT::P - 1 ? row * qks * 2 + 16 * g : kOut;
+    }
+#pragma unroll
+    for (int j = 0; j < JA; ++j) {
+        const int pos = 64 * (wave + NW * j) + lane, row = pos / AT::P, g = pos % AT::P;
+        offA[j] = g < AT::P - 1 ? row * 128 + 16 * g : kOut;
+    }
+#pragma unroll
+    for (int j = 0; j < JO; ++j) {
+        const int pos = 64 * (wave + NW * j) + lane, row = pos / OT::P, g = pos % OT::P;
+        offO[j] = g < OT::P - 1 ? row * vs * 2 + 16 * g : kOut;
     }
     auto load_stage = [&](int c, unsigned char *tb) __attribute__((always_inline)) {
         const int64_t tok = si.tok0 + (int64_t)c * kChunk, gci = si.chunk0 + c;
@@ -414,12 +404,28 @@ __global__ __launch_bounds__(128, 1) void bwd_dstate_mma_kernel(BwdParams p) {
         const u32x4 rO = rsrc_words(ob + tok * vs, ((nv - 1) * vs + L::WC) * 2);
         const u32x4 rG = rsrc_words(Gb + gci * p.H_v * GB_FLOATS, GB_FLOATS * 4);
 #pragma unroll
-        for (int j = 0; j < NLW; ++j) {
-            if (kind[j] == 7) continue;
-            const u32x4 r = kind[j] == 0 ? rK : kind[j] == 1 ? rQ : kind[j] == 2 ? rA : kind[j] == 3 ? rPh
-                          : kind[j] == 4 ? rPl : kind[j] == 5 ? rO : rG;
-            dma_granules(r, tb + dst[j], soff[j]);
+        for (int j = 0; j < JK; ++j) {
+            const int i = wave + NW * j;
+            if (i < KT::NI) {
+                dma_granules(rK, tb + L::K0 + 1024 * i, offK[j]);
+                dma_granules(rQ, tb + L::Q0 + 1024 * i, offK[j]);
+            }
         }
+#pragma unroll
+        for (int j = 0; j < JA; ++j) {
+            const int i = wave + NW * j;
+            if (i < AT::NI) {
+                dma_granules(rA, tb + L::A0 + 1024 * i, offA[j]);
+                dma_granules(rPh, tb + L::A0 + AT::BYTES + 1024 * i, offA[j]);
+                dma_granules(rPl, tb + L::A0 + 2 * AT::BYTES + 1024 * i, offA[j]);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < JO; ++j) {
+            const int i = wave + NW * j;
+            if (i < OT::NI) dma_granules(rO, tb + L::O0 + 1024 * i, offO[j]);
+        }
+        for (int i = wave; i < L::NLG; i += NW) dma_granules(rG, tb + L::G0 + 1024 * i, 1024 * i + 16 * lane);
     };
 
     f32x4 S[MD];   // dS: rows 16 m + 4 grp + r of column col
@@ -605,7 +611,7 @@ __global__ __launch_bounds__(128, 1) void bwd_dstate_kda_mma_kernel(BwdParams p)
     using KT = typename L::K;
     using AT = typename L::A;
     using OT = typename L::O;
-    constexpr int MD = L::MD, NKB = L::NKB, NLW = L::NLW, NW = L::NW;
+    constexpr int MD = L::MD, NKB = L::NKB, NW = L::NW;
     __shared__ __attribute__((aligned(16))) unsigned char stg0[L::STAGE], stg1[L::STAGE];
     const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -624,35 +630,25 @@ __global__ __launch_bounds__(128, 1) void bwd_dstate_kda_mma_kernel(BwdParams p)
     const bf16 *ob = static_cast<const bf16 *>(p.dout) + (int64_t)h * DV + c0;
     const float *Gb = p.gates + (int64_t)h * GB_FLOATS;
 
-    // this wave's stage instructions (Kd, Kg, Qg, A, P, dO, gate block; pad granules read zeros)
+    // this wave's stage instructions: instruction i = wave + NW j of each tile (the K-shaped tiles
+    // share their lane offsets, as do the 64 x 64 ones); pad granules read zeros
     constexpr int kOut = 1 << 30;
-    int soff[NLW], dst[NLW], kind[NLW];
+    constexpr int JK = (KT::NI + NW - 1) / NW, JA = (AT::NI + NW - 1) / NW, JO = (OT::NI + NW - 1) / NW;
+    int offK[JK], offA[JA], offO[JO];
 #pragma unroll
-    for (int j = 0; j < NLW; ++j) {
-        int ii = wave + NW * j;
-        kind[j] = 7;
-        soff[j] = 0;
-        dst[j] = 0;
-        if (ii < 3 * KT::NI) {
-            const int q = ii / KT::NI, i2 = ii - q * KT::NI, pos = 64 * i2 + lane, row = pos / KT::P, g = pos % KT::P;
-            kind[j] = q;                                     // 0: Kd, 1: Kg, 2: Qg
-            soff[j] = g < KT::P - 1 ? row * DK * 2 + 16 * g : kOut;
-            dst[j] = q * KT::BYTES + 1024 * i2;
-        } else if ((ii -= 3 * KT::NI) < 2 * AT::NI) {
-            const int part = ii / AT::NI, i2 = ii - part * AT::NI, pos = 64 * i2 + lane, row = pos / AT::P, g = pos % AT::P;
-            kind[j] = 3 + part;                              // 3: A, 4: P
-            soff[j] = g < AT::P - 1 ? row * 128 + 16 * g : kOut;
-            dst[j] = L::A0 + part * AT::BYTES + 1024 * i2;
-        } else if ((ii -= 2 * AT::NI) < OT::NI) {
-            const int pos = 64 * ii + lane, row = pos / OT::P, g = pos % OT::P;
-            kind[j] = 5;
-            soff[j] = g < OT::P - 1 ? row * vs * 2 + 16 * g : kOut;
-            dst[j] = L::O0 + 1024 * ii;
-        } else if ((ii -= OT::NI) < L::NLG) {
-            kind[j] = 6;
-            soff[j] = 1024 * ii + 16 * lane;
-            dst[j] = L::G0 + 1024 * ii;
-        }
+    for (int j = 0; j < JK; ++j) {
+        const int pos = 64 * (wave + NW * j) + lane, row = pos / KT::P, g = pos % KT::P;
+        offK[j] = g < KT::P - 1 ? row * DK * 2 + 16 * g : kOut;
+    }
+#pragma unroll
+    for (int j = 0; j < JA; ++j) {
+        const int pos = 64 * (wave + NW * j) + lane, row = pos / AT::P, g = pos % AT::P;
+        offA[j] = g < AT::P - 1 ? row * 128 + 16 * g : kOut;
+    }
+#pragma unroll
+    for (int j = 0; j < JO; ++j) {
+        const int pos = 64 * (wave + NW * j) + lane, row = pos / OT::P, g = pos % OT::P;
+        offO[j] = g < OT::P - 1 ? row * vs * 2 + 16 * g : kOut;
     }
     auto load_stage = [&](int c, unsigned char *tb) __attribute__((always_inline)) {
         const int64_t tok = si.tok0 + (int64_t)c * kChunk, gci = si.chunk0 + c;
@@ -666,12 +662,28 @@ __global__ __launch_bounds__(128, 1) void bwd_dstate_kda_mma_kernel(BwdParams p)
         const u32x4 rO = rsrc_words(ob + tok * vs, ((nv - 1) * vs + L::WC) * 2);
         const u32x4 rG = rsrc_words(Gb + gci * p.H_v * GB_FLOATS, GB_FLOATS * 4);
 #pragma unroll
-        for (int j = 0; j < NLW; ++j) {
-            if (kind[j] == 7) continue;
-            const u32x4 r = kind[j] == 0 ? rKd : kind[j] == 1 ? rKg : kind[j] == 2 ? rQg : kind[j] == 3 ? rA
-                          : kind[j] == 4 ? rP : kind[j] == 5 ? rO : rG;
-            dma_granules(r, tb + dst[j], soff[j]);
+        for (int j = 0; j < JK; ++j) {
+            const int i = wave + NW * j;
+            if (i < KT::NI) {
+                dma_granules(rKd, tb + L::KD0 + 1024 * i, offK[j]);
+                dma_granules(rKg, tb + L::KG0 + 1024 * i, offK[j]);
+                dma_granules(rQg, tb + L::QG0 + 1024 * i, offK[j]);
+            }
         }
+#pragma unroll
+        for (int j = 0; j < JA; ++j) {
+            const int i = wave + NW * j;
+            if (i < AT::NI) {
+                dma_granules(rA, tb + L::A0 + 1024 * i, offA[j]);
+                dma_granules(rP, tb + L::P0 + 1024 * i, offA[j]);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < JO; ++j) {
+            const int i = wave + NW * j;
+            if (i < OT::NI) dma_granules(rO, tb + L::O0 + 1024 * i, offO[j]);
+        }
+        for (int i = wave; i < L::NLG; i += NW) dma_granules(rG, tb + L::G0 + 1024 * i, 1024 * i + 16 * lane);
     };
 
     f32x4 S[MD];   // dS: rows 16 m + 4 grp + r of column col
