@@ -712,12 +712,13 @@ void chunk_kernel(ChunkParams p) {
         unsigned char *tnext = B == 0 ? tiles1 : tiles0;
         chunk_top.template operator()<!OUT || CHAIN_LD, PF ? NPF : 0>(c);
         if constexpr (OUT && ST) {
-            {   // the state entering this chunk (no CP: segment = sequence)
+            {   // the state entering this chunk (no CP: segment = sequence); non-temporal: another
+                // kernel reads it, well after this one has moved on
                 float *st = p.chunk_states + ((int64_t)(si.chunk0 + cs + c) * p.H_v + h) * DK * DV;
 #pragma unroll
                 for (int m = 0; m < MD; ++m)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) st[(16 * m + 4 * grp + r) * DV + col] = S[m][r];
+                    for (int r = 0; r < 4; ++r) __builtin_nontemporal_store(S[m][r], &st[(16 * m + 4 * grp + r) * DV + col]);
             }
         }
         const float *g3 = reinterpret_cast<const float *>(tcur + L::G0);
@@ -953,7 +954,7 @@ __global__ __launch_bounds__(DK * 4) void cp_fix_kernel(FixParams p) {
             const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
             split8(x, mh[kb], ml[kb]);
         }
-        __syncthreads();  // S_start(j) is complete in sS[B2]
+        lds_only_barrier();  // S_start(j) is complete in sS[B2] (the loads of later segments stay in flight)
         const float *cur = sS[B2];
         // S_start(j) in pi order over d, as operand pairs
         Frag<T> bh[NKB], bl[NKB];
