@@ -325,16 +325,17 @@ __global__ __launch_bounds__(kBwT) void bwd_dstate_kernel(BwdParams p) {
 
 // ---- reverse scan of the state gradient on the matrix cores (bf16 inputs, scalar gate): the same
 //      quantities as bwd_dstate_kernel.  One workgroup per (sequence, value head, 32 value columns),
-//      two waves; each wave holds dS for its 16 columns and all D_k rows in registers, so K dS and
-//      the update take the state-side operand straight from its accumulators (pi order), and dV'
-//      and dX never leave the wave.  Per chunk, newest first:
+//      four waves: two groups of 16 columns times two halves of the D_k rows.  Each wave holds dS for
+//      its columns and rows in registers, so K dS and the update take the state-side operand straight
+//      from its accumulators (pi order); the two halves' partial K dS are summed through LDS, and
+//      both waves of a column group then form the same dV' and dX.  Per chunk, newest first:
 //        store dS (= dS_next of the chunk);  Y = K dS;  dV' = D (.) Y + Pt^T dO;  dX = A^T dV';
 //        dS <- gamma_C dS + Q^T (scale gamma (.) dO) - K^T (beta gamma (.) dX)
 //      K, Q, A, the Pt pair, the dO columns and the gate block of the next-older chunk stream into
 //      the other of two padded LDS stages meanwhile.  Operands that are not inputs are bf16 pairs.
 template <int DK>
 struct DsLayout {
-    static constexpr int NW = 2, WC = 32;             // waves, value columns per workgroup
+    static constexpr int NW = 4, WC = 32;             // waves, value columns per workgroup
     using K = Pad<DK * 2 / 16>;                       // K and Q tiles
     using A = Pad<8>;                                 // A, and each part of the Pt pair (64 x 64)
     using O = Pad<WC * 2 / 16>;                       // dO columns of the workgroup
@@ -342,20 +343,21 @@ struct DsLayout {
     static constexpr int K0 = 0, Q0 = K::BYTES, A0 = 2 * K::BYTES, P0 = A0 + A::BYTES, O0 = P0 + 2 * A::BYTES;
     static constexpr int G0 = O0 + O::BYTES, STAGE = G0 + GT;
     static constexpr int NLG = GT / 1024;
-    static constexpr int NLOAD = 2 * K::NI + 3 * A::NI + O::NI + NLG;
-    static constexpr int NLW = (NLOAD + NW - 1) / NW;
-    static constexpr int MD = DK / 16, NKB = DK / 32;
-    static_assert(2 * STAGE <= 160 * 1024, "LDS budget");
+    static constexpr int XCH = NW * 4 * 64 * 16;      // each wave's partial K dS (four f32x4 per lane)
+    static constexpr int MD = DK / 16, NKB = DK / 32;   // over all D_k rows
+    static constexpr int MH = MD / 2, KH = NKB / 2;     // over one wave's half of them
+    static_assert(2 * STAGE + XCH <= 160 * 1024, "LDS budget");
 };
 
 template <int DK>
-__global__ __launch_bounds__(128, 1) void bwd_dstate_mma_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, 1) void bwd_dstate_mma_kernel(BwdParams p) {
     using L = DsLayout<DK>;
     using KT = typename L::K;
     using AT = typename L::A;
     using OT = typename L::O;
-    constexpr int MD = L::MD, NKB = L::NKB, NW = L::NW;
+    constexpr int MH = L::MH, KH = L::KH, NW = L::NW;
     __shared__ __attribute__((aligned(16))) unsigned char stg0[L::STAGE], stg1[L::STAGE];
+    __shared__ f32x4 xch[NW][4][64];
     const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ncb = p.D_v / L::WC;
@@ -365,7 +367,8 @@ __global__ __launch_bounds__(128, 1) void bwd_dstate_mma_kernel(BwdParams p) {
     const int hq = h / (p.H_v / p.H_qk);
     const SeqInfo si = seq_info(p.seq, n, p.T);
     const int DV = p.D_v, qks = p.H_qk * DK, vs = p.H_v * DV;
-    const int c0 = cb * L::WC, col = c0 + 16 * wave + l16;
+    const int cg = wave & 1, rh = wave >> 1, RB = rh * (DK / 2);   // column group, first D_k row
+    const int c0 = cb * L::WC, col = c0 + 16 * cg + l16;
     const bf16 *kb_ = static_cast<const bf16 *>(p.k) + (int64_t)hq * DK;
     const bf16 *qb = static_cast<const bf16 *>(p.q) + (int64_t)hq * DK;
     const bf16 *ob = static_cast<const bf16 *>(p.dout) + (int64_t)h * DV + c0;
@@ -428,12 +431,12 @@ __global__ __launch_bounds__(128, 1) void bwd_dstate_mma_kernel(BwdParams p) {
         for (int i = wave; i < L::NLG; i += NW) dma_granules(rG, tb + L::G0 + 1024 * i, 1024 * i + 16 * lane);
     };
 
-    f32x4 S[MD];   // dS: rows 16 m + 4 grp + r of column col
+    f32x4 S[MH];   // dS: rows RB + 16 m + 4 grp + r of column col
 #pragma unroll
-    for (int m = 0; m < MD; ++m)
+    for (int m = 0; m < MH; ++m)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            S[m][r] = p.dht ? p.dht[(((int64_t)n * p.H_v + h) * DK + 16 * m + 4 * grp + r) * DV + col] : 0.f;
+            S[m][r] = p.dht ? p.dht[(((int64_t)n * p.H_v + h) * DK + RB + 16 * m + 4 * grp + r) * DV + col] : 0.f;
 
     auto step = [&](int c, const unsigned char *st) __attribute__((always_inline)) {
         const int64_t gci = si.chunk0 + c;
@@ -443,16 +446,17 @@ __global__ __launch_bounds__(128, 1) void bwd_dstate_mma_kernel(BwdParams p) {
         {   // dS_next of this chunk
             float *dsn = p.dsnext + (gci * p.H_v + h) * DK * DV;
 #pragma unroll
-            for (int m = 0; m < MD; ++m)
+            for (int m = 0; m < MH; ++m)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) dsn[(16 * m + 4 * grp + r) * DV + col] = S[m][r];
+                for (int r = 0; r < 4; ++r) dsn[(RB + 16 * m + 4 * grp + r) * DV + col] = S[m][r];
         }
-        // Y = K dS, then dV' = D (.) Y + Pt^T dO
+        // Y = K dS (this wave's half of the D_k rows, then the other half's partial from LDS: both
+        // waves of the column group add the same two partials), then dV' = D (.) Y + Pt^T dO
         f32x4 dv[4];
         {
-            Frag<bf16> sh[NKB], sl[NKB];
+            Frag<bf16> sh[KH], sl[KH];
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
+            for (int kb = 0; kb < KH; ++kb) {
                 float x[8];
                 pack_pi(S[2 * kb], S[2 * kb + 1], x);
                 split8_rne(x, sh[kb], sl[kb]);
@@ -460,13 +464,16 @@ __global__ __launch_bounds__(128, 1) void bwd_dstate_mma_kernel(BwdParams p) {
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
 #pragma unroll
-                for (int kb = 0; kb < NKB; ++kb) {
+                for (int kb = 0; kb < KH; ++kb) {
                     if (kb == 0) dv[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    mma_x(dv[tt], pi_row<KT>(tK, 16 * tt + l16, kb, grp), sh[kb], sl[kb]);
+                    mma_x(dv[tt], pi_row<KT>(tK, 16 * tt + l16, rh * KH + kb, grp), sh[kb], sl[kb]);
                 }
-                reg_fence();
+                xch[wave][tt][lane] = dv[tt];
             }
         }
+        lds_only_barrier();   // both halves' partials are in
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) dv[tt] += xch[wave ^ 2][tt][lane];
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
             const float4 d4 = *reinterpret_cast<const float4 *>(g + GB_SC + 16 * tt + 4 * grp);
@@ -475,7 +482,7 @@ __global__ __launch_bounds__(128, 1) void bwd_dstate_mma_kernel(BwdParams p) {
             for (int kb = 0; kb < 2; ++kb) {
                 if (32 * kb + 31 < 16 * tt) continue;        // Pt[s][t] = 0 for s < t
                 mma_pair_x(dv[tt], pi_col<AT>(tPh, 16 * tt, kb, grp, l16), pi_col<AT>(tPl, 16 * tt, kb, grp, l16),
-                           pi_col<OT>(tO, 16 * wave, kb, grp, l16));
+                           pi_col<OT>(tO, 16 * cg, kb, grp, l16));
             }
         }
         // dX = A^T dV'
@@ -512,7 +519,7 @@ __global__ __launch_bounds__(128, 1) void bwd_dstate_mma_kernel(BwdParams p) {
             const float fq[8] = {qa.x, qa.y, qa.z, qa.w, qc.x, qc.y, qc.z, qc.w};
             const float fk[8] = {ba.x * ka.x, ba.y * ka.y, ba.z * ka.z, ba.w * ka.w,
                                  bc.x * kc.x, bc.y * kc.y, bc.z * kc.z, bc.w * kc.w};
-            const Frag<bf16> o = pi_col<OT>(tO, 16 * wave, kb, grp, l16);   // dO[t][col], t in pi order
+            const Frag<bf16> o = pi_col<OT>(tO, 16 * cg, kb, grp, l16);   // dO[t][col], t in pi order
             float xo[8], xx[8];
             pack_pi(dx[2 * kb], dx[2 * kb + 1], xx);
 #pragma unroll
@@ -525,12 +532,12 @@ __global__ __launch_bounds__(128, 1) void bwd_dstate_mma_kernel(BwdParams p) {
         }
         const float gC = g[GB_GC];
 #pragma unroll
-        for (int m = 0; m < MD; ++m) {
+        for (int m = 0; m < MH; ++m) {
             S[m] *= gC;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                mma_x(S[m], pi_col<KT>(tQ, 16 * m, kb, grp, l16), oh[kb], ol[kb]);
-                mma_x(S[m], pi_col<KT>(tK, 16 * m, kb, grp, l16), xh[kb], xl[kb]);
+                mma_x(S[m], pi_col<KT>(tQ, RB + 16 * m, kb, grp, l16), oh[kb], ol[kb]);
+                mma_x(S[m], pi_col<KT>(tK, RB + 16 * m, kb, grp, l16), xh[kb], xl[kb]);
             }
             if (m & 1) reg_fence();
         }
@@ -558,9 +565,9 @@ __global__ __launch_bounds__(128, 1) void bwd_dstate_mma_kernel(BwdParams p) {
     }
     if (p.dh0) {
 #pragma unroll
-        for (int m = 0; m < MD; ++m)
+        for (int m = 0; m < MH; ++m)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) p.dh0[(((int64_t)n * p.H_v + h) * DK + 16 * m + 4 * grp + r) * DV + col] = S[m][r];
+            for (int r = 0; r < 4; ++r) p.dh0[(((int64_t)n * p.H_v + h) * DK + RB + 16 * m + 4 * grp + r) * DV + col] = S[m][r];
     }
 }
 
@@ -1726,7 +1733,7 @@ hipError_t launch_bwd(int dtype, int D_k, const BwdParams &p, hipStream_t s) {
         else GDN_BWD(bwd_p_kernel, T, DK, chunks);                                                         \
     }                                                                                                      \
     if (sizeof(T) == 2)                                                                                    \
-        hipLaunchKernelGGL((bwd_dstate_mma_kernel<DK>), dim3((unsigned)mscans), dim3(128), 0, s, p);      \
+        hipLaunchKernelGGL((bwd_dstate_mma_kernel<DK>), dim3((unsigned)mscans), dim3(256), 0, s, p);      \
     else                                                                                                   \
         GDN_BWD(bwd_dstate_kernel, T, DK, rscans);                                                         \
     if (chunks) {                                                                                          \
