@@ -588,8 +588,11 @@ __device__ __forceinline__ void split8_h2(const float *x, Frag<f16> &h, Frag<f16
 // ---- reverse scan of the state gradient on the matrix cores (per-channel gates, bf16 inputs): the
 //      quantities of bwd_dstate_kda_kernel, from the fp16 operands the per-chunk kernel stores for
 //      every chunk (Kd = K (.) e^{G_C - G}, Kg = K (.) e^G, Qg = Q (.) e^G, scale P, A).  One
-//      workgroup per (sequence, value head, 32 value columns), two waves; each wave holds dS for its
-//      16 columns and all D_k rows in registers.  Per chunk, newest first:
+//      workgroup per (sequence, value head, 32 value columns), four waves: two groups of 16 columns
+//      times two halves of the D_k rows, each holding dS for its columns and rows in registers; the
+//      halves' partial Kd dS are summed through LDS (with D_k = 128 in the chunk's Kd tile, which
+//      nothing reads after them), and both waves of a column group form the same dV' and dX.  Per
+//      chunk, newest first:
 //        store dS (= dS_next of the chunk);  dV' = Kd dS + (scale P)^T dO;  dX = A^T dV';
 //        dS <- Diag(e^{G_C}) dS + Qg^T (scale dO) - Kg^T (beta (.) dX)
 //      The next-older chunk's tiles stream into the other of two padded LDS stages meanwhile.  The
@@ -598,7 +601,7 @@ __device__ __forceinline__ void split8_h2(const float *x, Frag<f16> &h, Frag<f16
 //      the RMS); dO itself is exact in fp16.
 template <int DK>
 struct DsKdaLayout {
-    static constexpr int NW = 2, WC = 32;             // waves, value columns per workgroup
+    static constexpr int NW = 4, WC = 32;             // waves, value columns per workgroup
     using K = Pad<DK * 2 / 16>;                       // Kd, Kg, Qg tiles
     using A = Pad<8>;                                 // A and P (64 x 64)
     using O = Pad<WC * 2 / 16>;                       // dO columns of the workgroup
@@ -608,18 +611,25 @@ struct DsKdaLayout {
     static constexpr int NLG = GT / 1024;
     static constexpr int NLOAD = 3 * K::NI + 2 * A::NI + O::NI + NLG;
     static constexpr int NLW = (NLOAD + NW - 1) / NW;
-    static constexpr int MD = DK / 16, NKB = DK / 32;
+    static constexpr int MD = DK / 16, NKB = DK / 32;   // over all D_k rows
+    static constexpr int MH = MD / 2, KH = NKB / 2;     // over one wave's half of them
+    // the partial Kd dS of every wave: in a buffer of their own where it fits (D_k = 64), else in the
+    // stage's Kd tile once every wave has read it
+    static constexpr int XCH = NW * 4 * 64 * 16;
+    static constexpr bool OWN_XCH = 2 * STAGE + XCH <= 160 * 1024;
+    static_assert(OWN_XCH || XCH <= K::BYTES, "the partials fit in the Kd tile");
     static_assert(2 * STAGE <= 160 * 1024, "LDS budget");
 };
 
 template <int DK>
-__global__ __launch_bounds__(128, 1) void bwd_dstate_kda_mma_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, 1) void bwd_dstate_kda_mma_kernel(BwdParams p) {
     using L = DsKdaLayout<DK>;
     using KT = typename L::K;
     using AT = typename L::A;
     using OT = typename L::O;
-    constexpr int MD = L::MD, NKB = L::NKB, NW = L::NW;
+    constexpr int MH = L::MH, KH = L::KH, NW = L::NW;
     __shared__ __attribute__((aligned(16))) unsigned char stg0[L::STAGE], stg1[L::STAGE];
+    __shared__ f32x4 xbuf[L::OWN_XCH ? L::XCH / 16 : 1];
     const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ncb = p.D_v / L::WC;
@@ -628,7 +638,8 @@ __global__ __launch_bounds__(128, 1) void bwd_dstate_kda_mma_kernel(BwdParams p)
     if (n >= p.N) return;
     const SeqInfo si = seq_info(p.seq, n, p.T);
     const int DV = p.D_v, vs = p.H_v * DV;
-    const int c0 = cb * L::WC, col = c0 + 16 * wave + l16;
+    const int cg = wave & 1, rh = wave >> 1, RB = rh * (DK / 2);   // column group, first D_k row
+    const int c0 = cb * L::WC, col = c0 + 16 * cg + l16;
     const f16 *kdb = static_cast<const f16 *>(p.kd) + (int64_t)h * 64 * DK;
     const f16 *kgb = static_cast<const f16 *>(p.kg) + (int64_t)h * 64 * DK;
     const f16 *qgb = static_cast<const f16 *>(p.qg) + (int64_t)h * 64 * DK;
@@ -693,14 +704,14 @@ __global__ __launch_bounds__(128, 1) void bwd_dstate_kda_mma_kernel(BwdParams p)
         for (int i = wave; i < L::NLG; i += NW) dma_granules(rG, tb + L::G0 + 1024 * i, 1024 * i + 16 * lane);
     };
 
-    f32x4 S[MD];   // dS: rows 16 m + 4 grp + r of column col
+    f32x4 S[MH];   // dS: rows RB + 16 m + 4 grp + r of column col
 #pragma unroll
-    for (int m = 0; m < MD; ++m)
+    for (int m = 0; m < MH; ++m)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            S[m][r] = p.dht ? p.dht[(((int64_t)n * p.H_v + h) * DK + 16 * m + 4 * grp + r) * DV + col] : 0.f;
+            S[m][r] = p.dht ? p.dht[(((int64_t)n * p.H_v + h) * DK + RB + 16 * m + 4 * grp + r) * DV + col] : 0.f;
 
-    auto step = [&](int c, const unsigned char *st) __attribute__((always_inline)) {
+    auto step = [&](int c, unsigned char *st) __attribute__((always_inline)) {
         const int64_t gci = si.chunk0 + c;
         const unsigned char *tKd = st + L::KD0, *tKg = st + L::KG0, *tQg = st + L::QG0;
         const unsigned char *tA = st + L::A0, *tP = st + L::P0, *tO = st + L::O0;
@@ -708,16 +719,17 @@ __global__ __launch_bounds__(128, 1) void bwd_dstate_kda_mma_kernel(BwdParams p)
         {   // dS_next of this chunk
             float *dsn = p.dsnext + (gci * p.H_v + h) * DK * DV;
 #pragma unroll
-            for (int m = 0; m < MD; ++m)
+            for (int m = 0; m < MH; ++m)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) dsn[(16 * m + 4 * grp + r) * DV + col] = S[m][r];
+                for (int r = 0; r < 4; ++r) dsn[(RB + 16 * m + 4 * grp + r) * DV + col] = S[m][r];
         }
-        // dV' = Kd dS + (scale P)^T dO
+        // dV' = Kd dS (this wave's half of the D_k rows, then the other half's partial through the
+        // Kd tile: both waves of the column group add the same two partials) + (scale P)^T dO
         f32x4 dv[4];
         {
-            Frag<f16> sh[NKB], sl[NKB];
+            Frag<f16> sh[KH], sl[KH];
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
+            for (int kb = 0; kb < KH; ++kb) {
                 float x[8];
                 pack_pi(S[2 * kb], S[2 * kb + 1], x);
                 split8_h2(x, sh[kb], sl[kb]);
@@ -726,18 +738,24 @@ __global__ __launch_bounds__(128, 1) void bwd_dstate_kda_mma_kernel(BwdParams p)
             for (int tt = 0; tt < 4; ++tt) {
                 dv[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kb = 0; kb < NKB; ++kb) {
-                    const Frag<f16> kf = as_f16(pi_row<KT>(tKd, 16 * tt + l16, kb, grp));
+                for (int kb = 0; kb < KH; ++kb) {
+                    const Frag<f16> kf = as_f16(pi_row<KT>(tKd, 16 * tt + l16, rh * KH + kb, grp));
                     mma(dv[tt], kf, sh[kb]);
                     mma(dv[tt], kf, sl[kb]);
                 }
-                reg_fence();
             }
         }
+        f32x4 *xch = L::OWN_XCH ? xbuf : reinterpret_cast<f32x4 *>(st + L::KD0);
+        if constexpr (!L::OWN_XCH) lds_only_barrier();   // every wave is done with the Kd tile
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) xch[(wave * 4 + tt) * 64 + lane] = dv[tt];
+        lds_only_barrier();   // both halves' partials are in
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) dv[tt] += xch[((wave ^ 2) * 4 + tt) * 64 + lane];
         Frag<f16> of[2], osh[2], osl[2];   // dO[t][col] and the pair of scale dO[t][col], t in pi order
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            const Frag<bf16> o = pi_col<OT>(tO, 16 * wave, kb, grp, l16);
+            const Frag<bf16> o = pi_col<OT>(tO, 16 * cg, kb, grp, l16);
             float x[8], y[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -792,13 +810,13 @@ __global__ __launch_bounds__(128, 1) void bwd_dstate_kda_mma_kernel(BwdParams p)
             split8_h2(xx, xh[kb], xl[kb]);
         }
 #pragma unroll
-        for (int m = 0; m < MD; ++m) {
-            const float4 dec = *reinterpret_cast<const float4 *>(g + GB_DEC + 16 * m + 4 * grp);
+        for (int m = 0; m < MH; ++m) {
+            const float4 dec = *reinterpret_cast<const float4 *>(g + GB_DEC + RB + 16 * m + 4 * grp);
             S[m][0] *= dec.x; S[m][1] *= dec.y; S[m][2] *= dec.z; S[m][3] *= dec.w;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                const Frag<f16> qf = as_f16(pi_col<KT>(tQg, 16 * m, kb, grp, l16));
-                const Frag<f16> kf = as_f16(pi_col<KT>(tKg, 16 * m, kb, grp, l16));
+                const Frag<f16> qf = as_f16(pi_col<KT>(tQg, RB + 16 * m, kb, grp, l16));
+                const Frag<f16> kf = as_f16(pi_col<KT>(tKg, RB + 16 * m, kb, grp, l16));
                 mma(S[m], qf, osh[kb]);
                 mma(S[m], qf, osl[kb]);
                 mma(S[m], kf, xh[kb]);
@@ -830,9 +848,9 @@ __global__ __launch_bounds__(128, 1) void bwd_dstate_kda_mma_kernel(BwdParams p)
     }
     if (p.dh0) {
 #pragma unroll
-        for (int m = 0; m < MD; ++m)
+        for (int m = 0; m < MH; ++m)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) p.dh0[(((int64_t)n * p.H_v + h) * DK + 16 * m + 4 * grp + r) * DV + col] = S[m][r];
+            for (int r = 0; r < 4; ++r) p.dh0[(((int64_t)n * p.H_v + h) * DK + RB + 16 * m + 4 * grp + r) * DV + col] = S[m][r];
     }
 }
 
@@ -1696,7 +1714,7 @@ hipError_t launch_bwd(int dtype, int D_k, const BwdParams &p, hipStream_t s) {
     /* bf16 inputs read the per-chunk kernel's scale P instead */ \
     if (chunks && sizeof(T) != 2) GDN_BWDK(bwd_p_kda_kernel, T, DK, chunks); \
     if (sizeof(T) == 2)                                      \
-        hipLaunchKernelGGL((bwd_dstate_kda_mma_kernel<DK>), dim3((unsigned)mscans), dim3(128), 0, s, p); \
+        hipLaunchKernelGGL((bwd_dstate_kda_mma_kernel<DK>), dim3((unsigned)mscans), dim3(256), 0, s, p); \
     else                                                     \
         GDN_BWDK(bwd_dstate_kda_kernel, T, DK, scans);       \
     if (chunks) {                                            \
