@@ -225,8 +225,10 @@ void chunk_kernel(ChunkParams p) {
     // the tile loads of that chunk hit L2.  Each chain wave issues exactly NPF such loads per chunk
     // (and NPF in the prologue): its chunk-top wait then leaves the NPF newest loads in flight,
     // which, loads returning in order, still covers every tile load issued before them.  The lines
-    // land in a sink that nothing reads.
-    constexpr bool PF = CH && MODE == 0 && NBUF == 2 && !ST;
+    // land in a sink that nothing reads.  In the state-storing replay the chain waves' state stores
+    // come before their loads of a chunk; the wait still covers every tile load (stores only add to
+    // the count it waits through).
+    constexpr bool PF = CH && MODE == 0 && NBUF == 2;
     constexpr int NPF = 2;
 #ifndef GDN_PF_DIST
 #define GDN_PF_DIST 2
@@ -235,7 +237,7 @@ void chunk_kernel(ChunkParams p) {
     // the same build stores each chunk's output one step late, after the next step's tile loads are
     // issued, so the output waves' chunk-top wait does not wait for those stores to land (with a
     // scalar gate this measured slower: 133 -> 136 us on the Qwen3-Next shape, 523 -> 572 us varlen)
-    constexpr bool DEFER_O = PF;
+    constexpr bool DEFER_O = PF && !ST;
     // the scalar-gate main pass with two tile buffers: the output waves store each chunk's output
     // in the next chunk, right after its mid-chunk barrier, where they would otherwise wait for the
     // chain's state update (phase 2 is the chain's).  Stored at the end of its own chunk, the output
