@@ -669,6 +669,7 @@ extern "C" gdn_status gdn_bwd(const gdn_bwd_args *a, void *workspace, size_t wor
     cp.n_slices = pl.n_slices;
     cp.n_cus = device_cus();
     cp.chunk_states = bw.states;
+    cp.pmat = bw.pmat;   // the scalar-gate bf16 replay forms the scan's scale P on the way
     if ((e = gdn::launch_chunk(a->dtype, a->D_k, pl.BV, a->gate_kind, cp, s)) != hipSuccess)
         return fail(GDN_ERR_HIP, "state replay launch: %s", hipGetErrorString(e));
     bw.replayed = 1;

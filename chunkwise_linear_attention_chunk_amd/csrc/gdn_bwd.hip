@@ -177,6 +177,9 @@ __global__ __launch_bounds__(kBwT) void bwd_p_kernel(BwdParams p) {
 //      the rows of the product, so a lane holds four consecutive key columns of one query row and
 //      stores them with one 8-byte store per part -- and writes the upper tiles w, w + 4 (< 6) as
 //      zeros.  (bwd_p_kernel's LDS dot products took 237 us per step on the Qwen3-Next shape.)
+//      Used when the states were not replayed: the replay (chunk_kernel's state-storing build)
+//      forms the same pair from the tiles it holds (71 us less per step on the Qwen3-Next shape,
+//      the replay ~50 us more).
 template <int DK>
 __global__ __launch_bounds__(256) void bwd_p_mma_kernel(BwdParams p) {
     constexpr int NKB = DK / 32;
@@ -1747,7 +1750,8 @@ hipError_t launch_bwd(int dtype, int D_k, const BwdParams &p, hipStream_t s) {
 #define GDN_BWD_ALL(T, DK)                                                                                 \
     if (!p.replayed) GDN_BWD(bwd_states_kernel, T, DK, scans);                                             \
     if (chunks) {                                                                                          \
-        if (sizeof(T) == 2) hipLaunchKernelGGL((bwd_p_mma_kernel<DK>), dim3((unsigned)chunks), dim3(256), 0, s, p); \
+        /* bf16: the replay (chunk_kernel's state-storing build) has formed scale P already */           \
+        if (sizeof(T) == 2) { if (!p.replayed) hipLaunchKernelGGL((bwd_p_mma_kernel<DK>), dim3((unsigned)chunks), dim3(256), 0, s, p); } \
         else GDN_BWD(bwd_p_kernel, T, DK, chunks);                                                         \
     }                                                                                                      \
     if (sizeof(T) == 2)                                                                                    \

@@ -246,6 +246,8 @@ void chunk_kernel(ChunkParams p) {
     // stored it before their mid-chunk barrier, 128.0 us; stored this way, 124.2 us (the same as
     // the hand-over with the chain waves' stores removed).
     constexpr bool MIDOUT = MODE == 0 && NBUF == 2 && !ST && !CH;
+    // the state-storing build with a scalar gate and bf16 inputs also forms the backward scan's scale P
+    constexpr bool PSTORE = ST && !CH && sizeof(T) == 2;
     constexpr int NRT = 4 / NSUB;                  // token tiles of each output wave
 
     // Separate LDS objects for the two tile buffers and for the exchange: the chunk loop is
@@ -551,13 +553,53 @@ void chunk_kernel(ChunkParams p) {
                 // inter-chunk part: scale diag(gamma) Q S_c (S_c was handed over before this chunk);
                 // the state and Q fragments first (the Q lo parts of per-channel gates as they are used)
                 if (more) {                                       // the output waves' share, at once
-                    issue_kq(c + 1, tnext, 0, 1, ST ? OUT_LD & ~LD_Q : OUT_LD);
+                    issue_kq(c + 1, tnext, 0, 1, ST && !PSTORE ? OUT_LD & ~LD_Q : OUT_LD);
                     issue_apvg(c + 1, tnext, 0, 1, OUT_LD);
                 }
                 if constexpr (DEFER_O) {
                     if (c > 0) store_o(c - 1);
                 }
                 if constexpr (ST) {   // states only: the loads and the chain's barriers, no output
+                    if constexpr (PSTORE) {
+                        // scale P of the chunk for the backward's scan, once per head (the first
+                        // column slice): the blocks of P V' below, stored as a bf16 pair per row
+                        if (slice == 0 && p.pmat) {
+                            Frag<T> qf[NKB][NR];
+#pragma unroll
+                            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                                for (int i = 0; i < NR; ++i) qf[kb][i] = ldpi_tile<T, L::KGPR>(tQ, 16 * mt[i] + l16, kb);
+                            bf16 *Pb = static_cast<bf16 *>(p.pmat) + ((int64_t)(si.chunk0 + cs + c) * p.H_v + h) * 2 * 4096;
+                            const float lsc = __log2f(p.scale);
+#pragma unroll
+                            for (int b = 0; b < NPB; ++b) {
+                                const int i = pb_tile(b), kb = pb_kb(b), m = mt[i], t = 16 * m + l16;
+                                const float glt = g3[GB_GLQ + t] + lsc;
+#pragma unroll
+                                for (int u = 0; u < 2; ++u) {
+                                    const int nn = 2 * kb + u, s0 = 16 * nn + 4 * grp;   // key tile, first key
+                                    f32x4 pt = {0.f, 0.f, 0.f, 0.f};                      // P[t][s0 .. s0 + 3]
+                                    if (nn <= m) {
+#pragma unroll
+                                        for (int kk = 0; kk < NKB; ++kk)
+                                            mma(pt, ldpi_tile<T, L::KGPR>(tK, 16 * nn + l16, kk), qf[kk][i]);
+                                        const float4 gs = *reinterpret_cast<const float4 *>(g3 + GB_GLK + s0);
+                                        const float gsv[4] = {gs.x, gs.y, gs.z, gs.w};
+#pragma unroll
+                                        for (int r = 0; r < 4; ++r) pt[r] = s0 + r <= t ? fast_exp2(glt - gsv[r]) * pt[r] : 0.f;
+                                    }
+                                    bf16x4 hi, lo;
+#pragma unroll
+                                    for (int r = 0; r < 4; ++r) {
+                                        hi[r] = (bf16)pt[r];
+                                        lo[r] = (bf16)(pt[r] - (float)hi[r]);
+                                    }
+                                    *reinterpret_cast<bf16x4 *>(Pb + t * 64 + s0) = hi;
+                                    *reinterpret_cast<bf16x4 *>(Pb + 4096 + t * 64 + s0) = lo;
+                                }
+                            }
+                        }
+                    }
                     lds_only_barrier();
                     if constexpr (EARLY_LD) {
                         if (c + 1 < nch) {

@@ -159,6 +159,10 @@ struct ChunkParams {
     // nullable (main pass without CP): receives the state entering every chunk, fp32
     // [global chunk][H_v][D_k][D_v] (the backward's recomputed chunk states); o may then be null
     float *chunk_states;
+    // nullable (that build, scalar gate, bf16): receives scale P = scale Lower(Gamma) (.) Q K^T of
+    // every chunk as a bf16 pair, [global chunk][H_v] x (hi [64][64], lo [64][64]) row-major; the
+    // tiles above the diagonal that the backward's scan reads, (0, 1) and (2, 3), are zeros
+    void *pmat;
 };
 
 // chunk ci of the per-chunk grid: every chunk, or the chunks of one piece of a batched input
