@@ -612,8 +612,6 @@ struct DsKdaLayout {
     static constexpr int KD0 = 0, KG0 = K::BYTES, QG0 = 2 * K::BYTES, A0 = 3 * K::BYTES, P0 = A0 + A::BYTES;
     static constexpr int O0 = P0 + A::BYTES, G0 = O0 + O::BYTES, STAGE = G0 + GT;
     static constexpr int NLG = GT / 1024;
-    static constexpr int NLOAD = 3 * K::NI + 2 * A::NI + O::NI + NLG;
-    static constexpr int NLW = (NLOAD + NW - 1) / NW;
     static constexpr int MD = DK / 16, NKB = DK / 32;   // over all D_k rows
     static constexpr int MH = MD / 2, KH = NKB / 2;     // over one wave's half of them
     // the partial Kd dS of every wave: in a buffer of their own where it fits (D_k = 64), else in the
