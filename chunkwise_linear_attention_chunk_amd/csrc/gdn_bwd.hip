@@ -823,7 +823,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dstate_kda_mma_kernel(BwdParams p)
                 mma(S[m], kf, xh[kb]);
                 mma(S[m], kf, xl[kb]);
             }
-            if (m & 1) reg_fence();
         }
     };
 
